@@ -1,0 +1,322 @@
+"""CPU reference (oracle) for the calibration-Hessian GPTQ path.
+
+TEST INFRASTRUCTURE ONLY: imported by the tests, the smoke check and the
+benchmark's CPU-baseline leg.  The product library never imports it, and it
+shares no code with the HIP path.  The arithmetic lives in `gq_oracle.c`
+(plain fp64 C, OpenMP over independent rows); this file only marshals numpy
+arrays through ctypes and builds the shared object with gcc.
+
+Parity is pinned for every function by the CPU tests (tests/test_oracle_*.py)
+against brute force, closed forms, invariants, library special cases and the
+values the pages print.  GPTQ codes on correlated Hessians at K >= 1024 are
+"parity unpinned" beyond those invariants: the pages publish no golden codes.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "gq_oracle.c")
+_LIB = os.path.join(_HERE, "libgq_oracle.so")
+
+OK, ERR_INVALID_ARG, ERR_NOT_PD, ERR_NONFINITE, ERR_NO_CALIBRATION = 0, 1, 2, 3, 4
+ERR_NO_CONVERGENCE = 6
+
+
+def build(force: bool = False) -> str:
+    """Compile gq_oracle.c into libgq_oracle.so (portable x86-64, no FP contraction)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp"
+        cmd = ["gcc", "-O3", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-ffp-contract=off",
+               "-fno-fast-math", _SRC, "-o", tmp, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def build_mutant(mutant: int, outdir: str) -> str:
+    """Compile a deliberately wrong variant (-DORC_MUTANT=n) for the mutation tests."""
+    out = os.path.join(outdir, f"libgq_oracle_mutant{mutant}.so")
+    cmd = ["gcc", "-O3", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-ffp-contract=off",
+           "-fno-fast-math", f"-DORC_MUTANT={mutant}", _SRC, "-o", out, "-lm"]
+    subprocess.run(cmd, check=True)
+    return out
+
+
+_lib = None
+
+
+def use_library(path):
+    """Point this module at another build of gq_oracle.c (mutation tests); None restores."""
+    global _lib
+    _lib = None if path is None else _load(path)
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        build()
+        _lib = _load(_LIB)
+    return _lib
+
+
+def _load(path):
+    L = ctypes.CDLL(path)
+    P = ctypes.c_void_p
+    I64 = ctypes.c_int64
+    D = ctypes.c_double
+    I = ctypes.c_int
+    sig = {
+        "orc_num_threads": (I, []),
+        "orc_gram_accumulate": (None, [P, P, I64, I64]),
+        "orc_gram_entries": (None, [P, P, I64, I64, P, P, I64]),
+        "orc_tril_bytes": (I64, [I64]),
+        "orc_pack_tril": (None, [P, P, I64]),
+        "orc_unpack_tril": (None, [P, P, I64]),
+        "orc_eigh_jacobi": (I, [P, P, P, I64, I]),
+        "orc_eigh_tridiag": (I, [P, P, P, I64]),
+        "orc_eigh": (I, [P, P, P, I64, I]),
+        "orc_eigvalsh": (I, [P, P, I64]),
+        "orc_eigvalsh_f64": (I, [P, P, I64]),
+        "orc_psd_project": (I, [P, P, P, I64, I]),
+        "orc_cholesky_lower": (I, [P, I64]),
+        "orc_diag_mean": (D, [P, I64]),
+        "orc_gptq_U": (I, [P, P, I64, D, P]),
+        "orc_gptq_sweep": (None, [P, P, P, P, I64, I64, P, I64]),
+        "orc_rtn": (None, [P, P, P, I64, I64, I64]),
+        "orc_qerr": (D, [P, P, P, P, I64, I64, I64, P]),
+        "orc_pack_codes": (None, [P, P, I64, I64]),
+        "orc_unpack_codes": (None, [P, P, I64, I64]),
+        "orc_gptq": (I, [P, P, P, P, P, P, I64, I64, I64, D]),
+        "orc_gptq_replay": (None, [P, P, P, P, P, P, I64, I64, P, I64, D, D]),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(L, name)
+        f.restype = res
+        f.argtypes = args
+    return L
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c(a, dtype):
+    return np.ascontiguousarray(np.asarray(a, dtype=dtype))
+
+
+def _np(x, dtype):
+    """Accept numpy arrays or torch tensors (CPU; bf16 is widened exactly to fp32)."""
+    try:
+        import torch
+        if isinstance(x, torch.Tensor):
+            x = x.detach().cpu()
+            if x.dtype == torch.bfloat16:
+                x = x.to(torch.float32)
+            x = x.numpy()
+    except ImportError:  # pragma: no cover
+        pass
+    return _c(x, dtype)
+
+
+class OracleError(RuntimeError):
+    def __init__(self, status, what):
+        super().__init__(f"{what}: oracle status {status}")
+        self.status = status
+
+
+def num_threads() -> int:
+    return lib().orc_num_threads()
+
+
+# ------------------------------------------------------------------ Gram
+def gram(X, H=None):
+    """fp64 H (+)= X^T X for X (T x K, fp32 or bf16 values)."""
+    X = _np(X, np.float32)
+    T, K = X.shape
+    if H is None:
+        H = np.zeros((K, K), np.float64)
+    lib().orc_gram_accumulate(_p(H), _p(X), T, K)
+    return H
+
+
+def gram_entries(X, I, J):
+    X = _np(X, np.float32)
+    T, K = X.shape
+    I = _c(I, np.int64)
+    J = _c(J, np.int64)
+    out = np.zeros(len(I), np.float64)
+    lib().orc_gram_entries(_p(out), _p(X), T, K, _p(I), _p(J), len(I))
+    return out
+
+
+# ------------------------------------------------------------------ tril storage
+def tril_bytes(K: int) -> int:
+    return int(lib().orc_tril_bytes(K))
+
+
+def pack_tril(H):
+    H = _np(H, np.float32)
+    K = H.shape[0]
+    blob = np.zeros(tril_bytes(K), np.uint8)
+    lib().orc_pack_tril(_p(blob), _p(H), K)
+    return blob
+
+
+def unpack_tril(blob, K: int):
+    blob = _c(blob, np.uint8)
+    assert blob.size == tril_bytes(K)
+    H = np.zeros((K, K), np.float32)
+    lib().orc_unpack_tril(_p(H), _p(blob), K)
+    return H
+
+
+# ------------------------------------------------------------------ eigen / PSD
+def eigh(H, method: int = 1):
+    """(w, V) with V[:, k] the eigenvector of w[k]; method 0 Jacobi, 1 tridiagonal QR."""
+    H = _np(H, np.float32)
+    K = H.shape[0]
+    w = np.zeros(K, np.float64)
+    Vt = np.zeros((K, K), np.float64)
+    st = lib().orc_eigh(_p(w), _p(Vt), _p(H), K, method)
+    if st:
+        raise OracleError(st, "eigh")
+    return w, Vt.T.copy()
+
+
+def eigvalsh(H):
+    H = _np(H, np.float32)
+    K = H.shape[0]
+    w = np.zeros(K, np.float64)
+    st = lib().orc_eigvalsh(_p(w), _p(H), K)
+    if st:
+        raise OracleError(st, "eigvalsh")
+    return np.sort(w)
+
+
+def eigvalsh_f64(S):
+    S = _c(S, np.float64)
+    K = S.shape[0]
+    w = np.zeros(K, np.float64)
+    st = lib().orc_eigvalsh_f64(_p(w), _p(S), K)
+    if st:
+        raise OracleError(st, "eigvalsh_f64")
+    return np.sort(w)
+
+
+def psd_project(H, method: int = 1, return_f64: bool = False):
+    H = _np(H, np.float32)
+    K = H.shape[0]
+    P = np.zeros((K, K), np.float32)
+    P64 = np.zeros((K, K), np.float64) if return_f64 else None
+    st = lib().orc_psd_project(_p(P), _p(P64), _p(H), K, method)
+    if st:
+        raise OracleError(st, "psd_project")
+    return (P, P64) if return_f64 else P
+
+
+# ------------------------------------------------------------------ GPTQ
+def cholesky_lower(A):
+    A = _c(A, np.float64).copy()
+    st = lib().orc_cholesky_lower(_p(A), A.shape[0])
+    return st, A
+
+
+def diag_mean(H) -> float:
+    H = _np(H, np.float32)
+    return float(lib().orc_diag_mean(_p(H), H.shape[0]))
+
+
+def gptq_U(H, damp: float = 0.01):
+    """(status, U fp64 upper, mu) with (H + damp*mu*I)^-1 = U^T U."""
+    H = _np(H, np.float32)
+    K = H.shape[0]
+    U = np.zeros((K, K), np.float64)
+    mu = ctypes.c_double(0.0)
+    st = lib().orc_gptq_U(_p(U), _p(H), K, damp, ctypes.byref(mu))
+    return st, U, mu.value
+
+
+def gptq_sweep(W, U, G: int, rows=None):
+    """Codes (len(rows) x K int8) and scales of the GPTQ sweep of W's rows under U."""
+    W = _np(W, np.float32)
+    U = _c(U, np.float64)
+    N, K = W.shape
+    rows = np.arange(N, dtype=np.int64) if rows is None else _c(rows, np.int64)
+    codes = np.zeros((len(rows), K), np.int8)
+    scales = np.zeros((len(rows), K // G), np.float32)
+    lib().orc_gptq_sweep(_p(codes), _p(scales), _p(W), _p(U), K, G, _p(rows), len(rows))
+    return codes, scales
+
+
+def rtn(W, G: int):
+    W = _np(W, np.float32)
+    N, K = W.shape
+    codes = np.zeros((N, K), np.int8)
+    scales = np.zeros((N, K // G), np.float32)
+    lib().orc_rtn(_p(codes), _p(scales), _p(W), N, K, G)
+    return codes, scales
+
+
+def qerr(codes, scales, W, imp=None, return_sums: bool = False):
+    W = _np(W, np.float32)
+    N, K = W.shape
+    codes = _c(codes, np.int8)
+    scales = _c(scales, np.float32)
+    G = K // scales.shape[1]
+    imp = None if imp is None else _np(imp, np.float32)
+    nd = np.zeros(2, np.float64)
+    q = float(lib().orc_qerr(_p(codes), _p(scales), _p(W), _p(imp), N, K, G, _p(nd)))
+    return (q, nd) if return_sums else q
+
+
+def pack_codes(codes):
+    codes = _c(codes, np.int8)
+    N, K = codes.shape
+    out = np.zeros((N, K // 2), np.uint8)
+    lib().orc_pack_codes(_p(out), _p(codes), N, K)
+    return out
+
+
+def unpack_codes(packed, K: int):
+    packed = _c(packed, np.uint8)
+    N = packed.shape[0]
+    codes = np.zeros((N, K), np.int8)
+    lib().orc_unpack_codes(_p(codes), _p(packed), N, K)
+    return codes
+
+
+def gptq(W, H, G: int, damp: float = 0.01, imp=None, want_qerr: bool = True):
+    """(status, codes int8 N x K, scales N x K/G, qerr or None)."""
+    W = _np(W, np.float32)
+    H = _np(H, np.float32)
+    N, K = W.shape
+    imp = None if imp is None else _np(imp, np.float32)
+    codes = np.zeros((N, K), np.int8)
+    scales = np.zeros((N, max(1, K // max(G, 1))), np.float32)
+    q = ctypes.c_double(0.0)
+    st = lib().orc_gptq(_p(codes), _p(scales), ctypes.byref(q) if want_qerr else None,
+                        _p(W), _p(H), _p(imp), N, K, G, damp)
+    return st, codes, scales, (q.value if want_qerr else None)
+
+
+def gptq_replay(cand_codes, cand_scales, W, U, G: int, rows=None, delta: float = 1e-3,
+                scale_tol: float = 1e-5):
+    """Admissibility of candidate codes/scales for W's listed rows (see gq_oracle.c)."""
+    W = _np(W, np.float32)
+    U = _c(U, np.float64)
+    N, K = W.shape
+    rows = np.arange(N, dtype=np.int64) if rows is None else _c(rows, np.int64)
+    cc = _c(cand_codes, np.int8)
+    cs = _c(cand_scales, np.float32)
+    assert cc.shape == (len(rows), K) and cs.shape == (len(rows), K // G)
+    stats = np.zeros(4, np.int64)
+    mrel = ctypes.c_double(0.0)
+    lib().orc_gptq_replay(_p(stats), ctypes.byref(mrel), _p(cc), _p(cs), _p(W), _p(U), K, G,
+                          _p(rows), len(rows), delta, scale_tol)
+    return {"exact": int(stats[0]), "tie_flips": int(stats[1]), "inadmissible": int(stats[2]),
+            "scale_mismatch": int(stats[3]), "max_scale_rel": mrel.value}
