@@ -1,0 +1,195 @@
+/*
+ * gq.h -- C ABI of the calibration-Hessian GPTQ int4 library for AMD MI355X
+ * (gfx950).  Everything runs in hand-written HIP kernels on the stream the
+ * caller passes; the library never allocates or frees device memory: the
+ * caller owns every buffer and workspace.
+ *
+ * Conventions shared by every call
+ *   - Pointers are DEVICE pointers unless marked "host".  Device buffers must be
+ *     4-byte aligned; 16-byte alignment (what hipMalloc and PyTorch give) enables
+ *     the vectorised paths.
+ *   - Matrices are row-major.  H is K x K fp32.  A symmetric input is read from
+ *     its lower triangle (row >= column) only.
+ *   - Calls return a gq_status.  GQ_OK is 0; the detail of any other status is
+ *     in gq_last_error() (thread-local, valid until the next call on the same
+ *     host thread).  On an error the outputs are undefined.
+ *   - hessian_* calls are asynchronous: they validate arguments, enqueue kernels
+ *     and return; they report argument and launch errors only.  psd_project,
+ *     gptq_factor, gptq_sweep and gptq_quantize synchronise their stream before
+ *     returning, to report data-dependent status (and qerr).
+ *   - Calls that share a workspace must not overlap on different streams.
+ *   - New behaviour is added as new symbols that the old ones forward to, never
+ *     by changing a signature (the extension rule of the ork-driver wiki page
+ *     "Exp 2026-08-18 GPTQ Int4", qerr section).
+ */
+#ifndef GQ_H
+#define GQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GQ_ABI_VERSION 1
+
+typedef enum gq_status {
+    GQ_OK = 0,
+    GQ_ERR_INVALID_ARG = 1,    /* bad size, null required pointer, short workspace   */
+    GQ_ERR_NOT_PD = 2,         /* a Cholesky pivot of the damped Hessian was <= 0     */
+    GQ_ERR_NONFINITE = 3,      /* NaN or Inf in W, in the lower triangle of H, or imp */
+    GQ_ERR_NO_CALIBRATION = 4, /* mean(diag H) <= 0: refuse rather than guess         */
+    GQ_ERR_HIP = 5             /* a HIP runtime call failed                           */
+} gq_status;
+
+typedef enum gq_dtype { GQ_F32 = 0, GQ_BF16 = 1 } gq_dtype;
+
+/* ABI version of the loaded library (GQ_ABI_VERSION of its build). */
+int gq_abi_version(void);
+
+/* Detail of the last non-OK status returned on this host thread ("" if none). */
+const char *gq_last_error(void);
+
+/*
+ * hessian_accumulate -- H_lower += X^T X for one activation chunk.
+ *
+ * The calibration Hessian is the full Gram matrix of the activations
+ * (hipfire-calib-data dataset card, "Hessian storage": full Hessians, not
+ * diagonals), and it is a sum over token chunks, so chunks accumulated in any
+ * split add up to the single-pass statistic (AtomicChat Qwen3.8-27B GGUF page,
+ * "The importance matrix").
+ *
+ *   H       K x K fp32, row-major.  Entries with row >= column are updated in
+ *           place; the strict upper triangle is not touched.  The caller zeroes
+ *           H before the first chunk.  Each call adds its chunk's sum, formed in
+ *           fp32 accumulators, to H once.
+ *   X       T x K row-major activations, fp32 (x_dtype GQ_F32) or bf16
+ *           (GQ_BF16).  Not modified.
+ *   T, K    tokens in this chunk (T >= 0; T == 0 is a no-op) and channels (K >= 1).
+ *   stream  HIP stream for the launch.
+ * Errors: GQ_ERR_INVALID_ARG for null pointers, K < 1, T < 0 or an unknown dtype.
+ */
+int hessian_accumulate(float *H, const void *X, int x_dtype, int64_t T, int64_t K,
+                       hipStream_t stream);
+
+/* Bytes of a Bf16TrilDiagF32 blob: K*4 + K*(K-1)/2*2 (hipfire-calib-data,
+ * "Hessian storage: Bf16TrilDiagF32"). 0 for K < 1. */
+size_t hessian_tril_bytes(int64_t K);
+
+/*
+ * hessian_pack_tril -- H -> Bf16TrilDiagF32 blob (hipfire-calib-data, "Hessian
+ * storage: Bf16TrilDiagF32 (quant_type 130)"): K little-endian f32 words holding
+ * the exact diagonal, then K*(K-1)/2 little-endian u16 words; word i*(i-1)/2 + j
+ * (i > j) holds the top 16 bits of H[i][j] (truncation, f32_bits >> 16, not
+ * rounding).  Only the lower triangle of H is read.
+ *   blob  hessian_tril_bytes(K) bytes, written.    H  K x K fp32, read.
+ * Errors: GQ_ERR_INVALID_ARG for null pointers or K < 1.
+ */
+int hessian_pack_tril(void *blob, const float *H, int64_t K, hipStream_t stream);
+
+/*
+ * hessian_unpack_tril -- Bf16TrilDiagF32 blob -> full symmetric H: H[i][i] is the
+ * stored f32, H[i][j] = H[j][i] = f32(u16 << 16) (mirrored on read, same section).
+ *   H     K x K fp32, written in full.    blob  hessian_tril_bytes(K) bytes, read.
+ * Errors: GQ_ERR_INVALID_ARG for null pointers or K < 1.
+ */
+int hessian_unpack_tril(float *H, const void *blob, int64_t K, hipStream_t stream);
+
+/* Workspace bytes psd_project needs for size K. */
+size_t psd_project_workspace_size(int64_t K);
+
+/* Floating-point operations psd_project executes for size K (the method's cost;
+ * the dataset card's "The fix" prices the eigendecomposition at O(K^3)): each
+ * symmetric K x K product of the sign iteration counts K*K*(K+1) (the lower
+ * triangle it computes), plus the final rebuild.  Host-only query. */
+double psd_project_flops(int64_t K);
+
+/* Number of symmetric products psd_project launches for any K. Host-only query. */
+int psd_project_products(void);
+
+/*
+ * psd_project -- H <- nearest positive-semidefinite matrix in Frobenius norm:
+ * eigenvalues clipped at zero, rebuilt, symmetrised (hipfire-calib-data, "The
+ * fix"; required before Cholesky on stored Hessians).  Computed on the device
+ * without an eigendecomposition, as P = (H + sign(H) H) / 2 with sign(H) from a
+ * scaled Newton-Schulz iteration run in fp64 on the matrix cores.
+ *   H   K x K fp32; the lower triangle is read, the full symmetric result is
+ *       written in place.
+ *   ws  device workspace of at least psd_project_workspace_size(K) bytes.
+ * Synchronises `stream`.
+ * Errors: GQ_ERR_INVALID_ARG (null pointer, K < 1, short workspace),
+ *         GQ_ERR_NONFINITE (NaN/Inf in the lower triangle of H).  An all-zero H
+ *         returns all zeros.
+ */
+int psd_project(float *H, int64_t K, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Workspace bytes gptq_factor needs for size K. */
+size_t gptq_factor_workspace_size(int64_t K);
+
+/*
+ * gptq_factor -- the Cholesky-based inverse GPTQ sweeps with (ork-driver wiki,
+ * "Exp 2026-08-18 GPTQ Int4": Cholesky-based Hessian inverse).
+ * mu = mean(diag H); H_d = H + damp * mu * I (damping in units of mean(diag H),
+ * hipfire-calib-data, "The fix"); U is the upper-triangular factor with
+ * H_d^{-1} = U^T U.  Computed in fp64 as U = R^{-1} where H_d = R R^T with R
+ * upper triangular (the Cholesky factor of the order-reversed H_d, reversed back).
+ *   U     K x K fp32 row-major, written (zeros below the diagonal).
+ *   H     K x K fp32, lower triangle read.    damp  >= 0 (0.01 on the pages).
+ *   ws    at least gptq_factor_workspace_size(K) bytes.
+ * Synchronises `stream`.
+ * Errors: GQ_ERR_INVALID_ARG, GQ_ERR_NONFINITE (H lower triangle),
+ *         GQ_ERR_NO_CALIBRATION (mu <= 0), GQ_ERR_NOT_PD (pivot <= 0).
+ */
+int gptq_factor(float *U, const float *H, int64_t K, float damp, void *ws, size_t ws_bytes,
+                hipStream_t stream);
+
+/* Workspace bytes gptq_sweep needs for an N x K weight with group size `group`. */
+size_t gptq_sweep_workspace_size(int64_t N, int64_t K, int64_t group);
+
+/*
+ * gptq_sweep -- GPTQ error-feedback sweep of W under a given factor U (from
+ * gptq_factor), emitting uniform symmetric int4 codes in [-8, 7] with one scale
+ * absmax/7 per (row, group), so that w ~ code * scale (ork-driver wiki, "Exp
+ * 2026-08-18 GPTQ Int4").  Columns are taken in natural order; a group's scale is
+ * fixed at the group's first column from the group's current error-updated
+ * values; code = clamp(rint(w / scale), -8, 7) with ties to even; the error
+ * e = (w - code*scale) / U[i][i] is fed back into the later columns through row
+ * i of U.  Updates are batched lazily over blocks of 128 columns.
+ *   codes     N x K/2 bytes: column 2m in the low nibble of byte m of its row,
+ *             two's complement.
+ *   scales    N x (K/group) fp32.
+ *   qerr_out  host pointer or NULL.  When non-NULL it receives
+ *             sqrt(sum_n sum_k imp[k] (w - code*scale)^2 / sum_n sum_k imp[k] w^2)
+ *             over the original W (0 when the denominator is 0) -- the qerr of the
+ *             same wiki page.  Codes and scales are identical either way.
+ *   W         N x K fp32, not modified.    U  K x K fp32 from gptq_factor.
+ *   imp       K fp32 importance weights, or NULL for all ones.
+ *   N >= 1; K even, K >= 2; 1 <= group <= 128, group divides 128 and K.
+ *   ws        at least gptq_sweep_workspace_size(N, K, group) bytes.
+ * Synchronises `stream`.
+ * Errors: GQ_ERR_INVALID_ARG, GQ_ERR_NONFINITE (W or imp).
+ */
+int gptq_sweep(uint8_t *codes, float *scales, double *qerr_out, const float *W, const float *U,
+               const float *imp, int64_t N, int64_t K, int64_t group, void *ws, size_t ws_bytes,
+               hipStream_t stream);
+
+/* Workspace bytes gptq_quantize needs. */
+size_t gptq_quantize_workspace_size(int64_t N, int64_t K, int64_t group);
+
+/*
+ * gptq_quantize -- damping, blocked Cholesky, U, and the lazy-batch sweep in one
+ * call: gptq_factor into the workspace, then gptq_sweep.  Arguments as above;
+ * H is K x K fp32 (lower triangle read), damp the damping fraction (0.01).
+ * Synchronises `stream`.
+ */
+int gptq_quantize(uint8_t *codes, float *scales, double *qerr_out, const float *W,
+                  const float *H, const float *imp, int64_t N, int64_t K, int64_t group,
+                  float damp, void *ws, size_t ws_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GQ_H */

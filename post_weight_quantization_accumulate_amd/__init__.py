@@ -1,0 +1,214 @@
+"""Python binding of libgq.so, the calibration-Hessian GPTQ int4 library for MI355X.
+
+Thin ctypes marshalling over the C ABI declared in include/gq.h: each function
+takes torch tensors that already live on the GPU, passes their device pointers
+and the current HIP stream, and raises GQError on a non-zero status.  Every step
+of the path runs in the library's HIP kernels; nothing here computes.  PyTorch
+supplies device memory and streams only.  The library must be built
+(``python -m post_weight_quantization_accumulate_amd.build``); there is no
+fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgq.so")
+
+GQ_OK, GQ_ERR_INVALID_ARG, GQ_ERR_NOT_PD, GQ_ERR_NONFINITE, GQ_ERR_NO_CALIBRATION, GQ_ERR_HIP = range(6)
+GQ_F32, GQ_BF16 = 0, 1
+
+EXPORTS = (
+    "gq_abi_version", "gq_last_error", "hessian_accumulate", "hessian_tril_bytes",
+    "hessian_pack_tril", "hessian_unpack_tril", "psd_project_workspace_size", "psd_project",
+    "psd_project_flops", "psd_project_products",
+    "gptq_factor_workspace_size", "gptq_factor", "gptq_sweep_workspace_size", "gptq_sweep",
+    "gptq_quantize_workspace_size", "gptq_quantize",
+)
+
+
+class GQError(RuntimeError):
+    def __init__(self, status: int, what: str, detail: str):
+        super().__init__(f"{what} failed with status {status}: {detail}")
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libgq.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m post_weight_quantization_accumulate_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I64, I, SZ, F, D = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t,
+                               ctypes.c_float, ctypes.c_double)
+        sig = {
+            "gq_abi_version": (I, []),
+            "gq_last_error": (ctypes.c_char_p, []),
+            "hessian_accumulate": (I, [P, P, I, I64, I64, P]),
+            "hessian_tril_bytes": (SZ, [I64]),
+            "hessian_pack_tril": (I, [P, P, I64, P]),
+            "hessian_unpack_tril": (I, [P, P, I64, P]),
+            "psd_project_workspace_size": (SZ, [I64]),
+            "psd_project": (I, [P, I64, P, SZ, P]),
+            "psd_project_flops": (D, [I64]),
+            "psd_project_products": (I, []),
+            "gptq_factor_workspace_size": (SZ, [I64]),
+            "gptq_factor": (I, [P, P, I64, F, P, SZ, P]),
+            "gptq_sweep_workspace_size": (SZ, [I64, I64, I64]),
+            "gptq_sweep": (I, [P, P, P, P, P, P, I64, I64, I64, P, SZ, P]),
+            "gptq_quantize_workspace_size": (SZ, [I64, I64, I64]),
+            "gptq_quantize": (I, [P, P, P, P, P, P, I64, I64, I64, F, P, SZ, P]),
+        }
+        for name, (res, args) in sig.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _need(t: torch.Tensor, name: str, dtype, numel=None):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a CUDA (HIP) tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must have dtype {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if numel is not None and t.numel() < numel:
+        raise ValueError(f"{name} holds {t.numel()} elements, needs {numel}")
+
+
+def _check(status: int, what: str):
+    if status != GQ_OK:
+        raise GQError(status, what, lib().gq_last_error().decode(errors="replace"))
+
+
+def abi_version() -> int:
+    return lib().gq_abi_version()
+
+
+def workspace(nbytes: int, device) -> torch.Tensor:
+    """A byte buffer to pass as `ws` (the library itself never allocates)."""
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+def hessian_accumulate(H: torch.Tensor, X: torch.Tensor) -> None:
+    """H[i][j] += sum_t X[t][i] X[t][j] for i >= j (fp32 H, fp32 or bf16 X)."""
+    T, K = X.shape
+    _need(H, "H", torch.float32, K * K)
+    _need(X, "X", None)
+    if X.dtype == torch.bfloat16:
+        dt = GQ_BF16
+    elif X.dtype == torch.float32:
+        dt = GQ_F32
+    else:
+        raise ValueError("X must be fp32 or bf16")
+    _check(lib().hessian_accumulate(_ptr(H), _ptr(X), dt, T, K, _stream(H)), "hessian_accumulate")
+
+
+def hessian_tril_bytes(K: int) -> int:
+    return int(lib().hessian_tril_bytes(K))
+
+
+def hessian_pack_tril(blob: torch.Tensor, H: torch.Tensor) -> None:
+    K = H.shape[0]
+    _need(H, "H", torch.float32, K * K)
+    _need(blob, "blob", torch.uint8, hessian_tril_bytes(K))
+    _check(lib().hessian_pack_tril(_ptr(blob), _ptr(H), K, _stream(H)), "hessian_pack_tril")
+
+
+def hessian_unpack_tril(H: torch.Tensor, blob: torch.Tensor) -> None:
+    K = H.shape[0]
+    _need(H, "H", torch.float32, K * K)
+    _need(blob, "blob", torch.uint8, hessian_tril_bytes(K))
+    _check(lib().hessian_unpack_tril(_ptr(H), _ptr(blob), K, _stream(H)), "hessian_unpack_tril")
+
+
+def psd_project_workspace_size(K: int) -> int:
+    return int(lib().psd_project_workspace_size(K))
+
+
+def psd_project_flops(K: int) -> float:
+    return float(lib().psd_project_flops(K))
+
+
+def psd_project_products() -> int:
+    return int(lib().psd_project_products())
+
+
+def psd_project(H: torch.Tensor, ws: torch.Tensor) -> None:
+    K = H.shape[0]
+    _need(H, "H", torch.float32, K * K)
+    _need(ws, "ws", torch.uint8)
+    _check(lib().psd_project(_ptr(H), K, _ptr(ws), ws.numel(), _stream(H)), "psd_project")
+
+
+def gptq_factor_workspace_size(K: int) -> int:
+    return int(lib().gptq_factor_workspace_size(K))
+
+
+def gptq_factor(U: torch.Tensor, H: torch.Tensor, damp: float, ws: torch.Tensor) -> None:
+    K = H.shape[0]
+    _need(U, "U", torch.float32, K * K)
+    _need(H, "H", torch.float32, K * K)
+    _need(ws, "ws", torch.uint8)
+    _check(lib().gptq_factor(_ptr(U), _ptr(H), K, float(damp), _ptr(ws), ws.numel(), _stream(H)),
+           "gptq_factor")
+
+
+def gptq_sweep_workspace_size(N: int, K: int, group: int) -> int:
+    return int(lib().gptq_sweep_workspace_size(N, K, group))
+
+
+def gptq_sweep(codes, scales, W, U, imp, group: int, ws, want_qerr: bool = True):
+    """Codes/scales of the GPTQ sweep of W under U; returns qerr (or None)."""
+    N, K = W.shape
+    _need(W, "W", torch.float32)
+    _need(U, "U", torch.float32, K * K)
+    _need(codes, "codes", torch.uint8, N * (K // 2))
+    _need(scales, "scales", torch.float32, N * (K // max(group, 1)))
+    if imp is not None:
+        _need(imp, "imp", torch.float32, K)
+    _need(ws, "ws", torch.uint8)
+    q = ctypes.c_double(0.0)
+    _check(lib().gptq_sweep(_ptr(codes), _ptr(scales), ctypes.byref(q) if want_qerr else None,
+                            _ptr(W), _ptr(U), _ptr(imp), N, K, group, _ptr(ws), ws.numel(),
+                            _stream(W)), "gptq_sweep")
+    return q.value if want_qerr else None
+
+
+def gptq_quantize_workspace_size(N: int, K: int, group: int) -> int:
+    return int(lib().gptq_quantize_workspace_size(N, K, group))
+
+
+def gptq_quantize(codes, scales, W, H, imp, group: int, damp: float, ws, want_qerr: bool = True):
+    """Damping, Cholesky, U and the sweep in one call; returns qerr (or None)."""
+    N, K = W.shape
+    _need(W, "W", torch.float32)
+    _need(H, "H", torch.float32, K * K)
+    _need(codes, "codes", torch.uint8, N * (K // 2))
+    _need(scales, "scales", torch.float32, N * (K // max(group, 1)))
+    if imp is not None:
+        _need(imp, "imp", torch.float32, K)
+    _need(ws, "ws", torch.uint8)
+    q = ctypes.c_double(0.0)
+    _check(lib().gptq_quantize(_ptr(codes), _ptr(scales), ctypes.byref(q) if want_qerr else None,
+                               _ptr(W), _ptr(H), _ptr(imp), N, K, group, float(damp), _ptr(ws),
+                               ws.numel(), _stream(W)), "gptq_quantize")
+    return q.value if want_qerr else None

@@ -1,0 +1,510 @@
+// api.hip -- the C ABI (include/gq.h): argument validation, workspace carving,
+// launch order, and the single end-of-call read of the device status word.
+// The library allocates nothing; every buffer comes from the caller.
+#include <string>
+#include <cmath>
+#include <vector>
+
+#include "gq.h"
+#include "gq_internal.h"
+
+using namespace gq;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const std::string &msg)
+{
+    g_last_error = msg;
+    return status;
+}
+
+int hip_fail(hipError_t e, const char *where)
+{
+    return fail(GQ_ERR_HIP, std::string(where) + ": " + hipGetErrorString(e));
+}
+
+#define GQ_HIP(call, where)                        \
+    do {                                           \
+        hipError_t e_ = (call);                    \
+        if (e_ != hipSuccess) return hip_fail(e_, where); \
+    } while (0)
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// Carves aligned sub-buffers out of a caller workspace, in a fixed order, so
+// the *_workspace_size functions and the calls agree by construction.
+struct Carver {
+    char *base;
+    size_t off = 0;
+    explicit Carver(void *b) : base((char *)b) {}
+    template <typename T> T *take(size_t count)
+    {
+        T *p = base ? (T *)(base + off) : nullptr;
+        off += align_up(count * sizeof(T));
+        return p;
+    }
+};
+
+// Scalars at the front of every workspace.
+struct Scalars {
+    unsigned *status;     // 4 words
+    double *d;            // 8 doubles
+    double *partials;     // 2048 doubles
+};
+
+Scalars carve_scalars(Carver &c)
+{
+    Scalars s;
+    s.status = c.take<unsigned>(4);
+    s.d = c.take<double>(8);
+    s.partials = c.take<double>(2048);
+    return s;
+}
+
+int read_status(const unsigned *dev_status, hipStream_t stream, unsigned *out)
+{
+    unsigned h = 0;
+    GQ_HIP(hipMemcpyAsync(&h, dev_status, sizeof(unsigned), hipMemcpyDeviceToHost, stream),
+           "status readback");
+    GQ_HIP(hipStreamSynchronize(stream), "stream synchronize");
+    *out = h;
+    return GQ_OK;
+}
+
+int status_to_code(unsigned st)
+{
+    if (st & ST_NONFINITE) return fail(GQ_ERR_NONFINITE, "non-finite value in an input");
+    if (st & ST_NO_CALIB) return fail(GQ_ERR_NO_CALIBRATION, "mean(diag H) is not positive: no calibration data");
+    if (st & ST_NOT_PD) return fail(GQ_ERR_NOT_PD, "damped Hessian is not positive definite (Cholesky pivot <= 0)");
+    return GQ_OK;
+}
+
+GemmDesc gemm(const void *A, int64_t lda, const void *B, int64_t ldb, int64_t M, int64_t N, int64_t Kd,
+              void *out, int64_t ldo)
+{
+    GemmDesc d{};
+    d.A = A; d.lda = lda; d.B = B; d.ldb = ldb;
+    d.M = M; d.N = N; d.Kd = Kd;
+    d.out = out; d.ldo = ldo;
+    d.out_t = nullptr; d.cin = nullptr; d.ldc = ldo;
+    d.alpha = 1.0; d.beta = 0.0;
+    d.alpha_dev = nullptr; d.alpha_pow = 0; d.beta_dev = nullptr; d.beta_pow = 0;
+    d.tri = 0; d.mode = TILE_RECT;
+    return d;
+}
+
+constexpr int kPanel = 64;             // Cholesky / inverse panel width
+
+// ------------------------------------------------------------- sign iteration
+// Scaled Newton-Schulz for sign(X), X symmetric with spectrum in [-1, 1]:
+//   X <- a_k X + b_k X^3,  a_k = 1.5 alpha_k, b_k = -0.5 alpha_k^3,
+//   alpha_k = sqrt(3 / (1 + l + l^2)),  l <- a_k l + b_k l^3.
+// alpha_k maps [l, 1] onto [l', 1] with equal values at both ends, so every
+// eigenvalue with |lambda| >= l_0 (relative to the bound) converges to +-1.
+constexpr double kSignL0 = 3e-7;
+constexpr double kSignTol = 1e-9;
+
+std::vector<double> sign_schedule()
+{
+    std::vector<double> alphas;
+    double l = kSignL0;
+    while (l < 1.0 - kSignTol && alphas.size() < 64) {
+        const double a = std::sqrt(3.0 / (1.0 + l + l * l));
+        alphas.push_back(a);
+        l = 1.5 * a * l - 0.5 * a * a * a * l * l * l;
+    }
+    return alphas;
+}
+
+struct PsdWs {
+    Scalars sc;
+    double *H64, *X, *Y, *Xn;
+};
+
+PsdWs carve_psd(Carver &c, int64_t K)
+{
+    PsdWs w;
+    w.sc = carve_scalars(c);
+    const size_t n = (size_t)K * (size_t)K;
+    w.H64 = c.take<double>(n);
+    w.X = c.take<double>(n);
+    w.Y = c.take<double>(n);
+    w.Xn = c.take<double>(n);
+    return w;
+}
+
+struct FactorWs {
+    Scalars sc;
+    double *M, *X, *Dinv, *DinvT;
+};
+
+FactorWs carve_factor(Carver &c, int64_t K)
+{
+    FactorWs w;
+    w.sc = carve_scalars(c);
+    const size_t n = (size_t)K * (size_t)K;
+    const size_t nblk = (size_t)((K + kPanel - 1) / kPanel);
+    w.M = c.take<double>(n);
+    w.X = c.take<double>(n);
+    w.Dinv = c.take<double>(nblk * kPanel * kPanel);
+    w.DinvT = c.take<double>(nblk * kPanel * kPanel);
+    return w;
+}
+
+struct SweepWs {
+    Scalars sc;
+    float *Wk, *ET;
+};
+
+SweepWs carve_sweep(Carver &c, int64_t N, int64_t K)
+{
+    SweepWs w;
+    w.sc = carve_scalars(c);
+    w.Wk = c.take<float>((size_t)N * (size_t)K);
+    w.ET = c.take<float>((size_t)kSweepBlock * (size_t)N);
+    return w;
+}
+
+size_t psd_bytes(int64_t K)
+{
+    Carver c(nullptr);
+    carve_psd(c, K);
+    return c.off;
+}
+
+size_t factor_bytes(int64_t K)
+{
+    Carver c(nullptr);
+    carve_factor(c, K);
+    return c.off;
+}
+
+size_t sweep_bytes(int64_t N, int64_t K)
+{
+    Carver c(nullptr);
+    carve_sweep(c, N, K);
+    return c.off;
+}
+
+bool valid_group(int64_t G, int64_t K)
+{
+    if (G < 1 || G > 128) return false;
+    if ((G & (G - 1)) != 0) return false;       // divides 128 <=> power of two <= 128
+    return K % G == 0;
+}
+
+int check_sweep_args(const void *codes, const void *scales, const void *W, const void *U, int64_t N,
+                     int64_t K, int64_t G)
+{
+    if (!codes || !scales || !W || !U) return fail(GQ_ERR_INVALID_ARG, "null required pointer");
+    if (N < 1) return fail(GQ_ERR_INVALID_ARG, "N must be >= 1");
+    if (K < 2 || (K & 1)) return fail(GQ_ERR_INVALID_ARG, "K must be even and >= 2 (two codes per byte)");
+    if (!valid_group(G, K))
+        return fail(GQ_ERR_INVALID_ARG, "group must be a power of two <= 128 that divides K");
+    return GQ_OK;
+}
+
+// Upper Cholesky of the reversed, damped H, then the inverse; writes U (fp32).
+int run_factor(float *U, const float *H, int64_t K, float damp, FactorWs &w, hipStream_t s)
+{
+    GQ_HIP(launch_fill_u32(w.sc.status, 4, 0u, s), "fill");
+    double *mu = w.sc.d;
+    GQ_HIP(launch_diag_mean_check(mu, H, K, w.sc.status, s), "diag mean");
+    GQ_HIP(launch_damp_reverse(w.M, H, K, (double)damp, mu, s), "damp/reverse");
+    const int64_t nblk = (K + kPanel - 1) / kPanel;
+    for (int64_t p = 0; p < nblk; ++p) {
+        const int64_t p0 = p * kPanel;
+        const int nbp = (int)((K - p0) < kPanel ? (K - p0) : kPanel);
+        const int64_t p1 = p0 + nbp;
+        double *Dinv = w.Dinv + p * kPanel * kPanel;
+        double *DinvT = w.DinvT + p * kPanel * kPanel;
+        GQ_HIP(launch_potrf_diag(w.M, K, p0, nbp, Dinv, DinvT, w.sc.status, s), "potrf diag");
+        if (p1 < K) {
+            // panel rows: R_{p,rest} = R_pp^{-T} A_{p,rest}, mirrored below the diagonal
+            GemmDesc t = gemm(Dinv, nbp, w.M + p0 * K + p1, K, nbp, K - p1, nbp, w.M + p0 * K + p1, K);
+            t.out_t = w.M + p1 * K + p0;
+            GQ_HIP(gemm_tn_f64(t, s), "trsm");
+            // trailing update of the upper triangle: A_rest -= R_{p,rest}^T R_{p,rest}
+            GemmDesc u = gemm(w.M + p0 * K + p1, K, w.M + p0 * K + p1, K, K - p1, K - p1, nbp,
+                              w.M + p1 * K + p1, K);
+            u.cin = w.M + p1 * K + p1;
+            u.alpha = -1.0;
+            u.beta = 1.0;
+            u.mode = TILE_UPPER;
+            u.tri = 2;
+            GQ_HIP(gemm_tn_f64(u, s), "syrk");
+        }
+    }
+    // X = R^{-1}, block rows from the bottom up
+    GQ_HIP(launch_set_identity_f64(w.X, K, s), "identity");
+    for (int64_t p = nblk - 1; p >= 0; --p) {
+        const int64_t q0 = p * kPanel;
+        const int nbq = (int)((K - q0) < kPanel ? (K - q0) : kPanel);
+        const double *DinvT = w.DinvT + p * kPanel * kPanel;
+        GemmDesc a = gemm(DinvT, nbq, w.X + q0 * K + q0, K, nbq, K - q0, nbq, w.X + q0 * K + q0, K);
+        GQ_HIP(gemm_tn_f64(a, s), "trtri row");
+        if (q0 > 0) {
+            GemmDesc b = gemm(w.M + q0 * K, K, w.X + q0 * K + q0, K, q0, K - q0, nbq, w.X + q0, K);
+            b.cin = w.X + q0;
+            b.alpha = -1.0;
+            b.beta = 1.0;
+            GQ_HIP(gemm_tn_f64(b, s), "trtri update");
+        }
+    }
+    GQ_HIP(launch_flip_transpose(U, w.X, K, s), "flip transpose");
+    return GQ_OK;
+}
+
+int run_sweep(uint8_t *codes, float *scales, double *qerr_out, const float *W, const float *U,
+              const float *imp, int64_t N, int64_t K, int64_t G, SweepWs &w, hipStream_t s)
+{
+    GQ_HIP(launch_fill_u32(w.sc.status, 4, 0u, s), "fill");
+    GQ_HIP(launch_copy_check(w.Wk, W, N * K, w.sc.status, s), "copy W");
+    if (imp) GQ_HIP(launch_check_finite(imp, K, w.sc.status, s), "check imp");
+    for (int64_t b0 = 0; b0 < K; b0 += kSweepBlock) {
+        const int64_t bw = (K - b0) < kSweepBlock ? (K - b0) : kSweepBlock;
+        GQ_HIP(launch_sweep_block(w.Wk, w.ET, codes, scales, U, N, K, G, b0, s), "sweep block");
+        const int64_t e = b0 + bw;
+        if (e < K) {
+            GemmDesc d = gemm(w.ET, N, U + b0 * K + e, K, N, K - e, bw, w.Wk + e, K);
+            d.cin = w.Wk + e;
+            d.alpha = -1.0;
+            d.beta = 1.0;
+            GQ_HIP(gemm_tn_f32(d, s), "block update");
+        }
+    }
+    if (qerr_out) {
+        GQ_HIP(launch_qerr(w.sc.partials, W, codes, scales, imp, N, K, G, s), "qerr");
+        GQ_HIP(launch_qerr_reduce(w.sc.d, w.sc.partials, qerr_partials(N), s), "qerr reduce");
+    }
+    unsigned st = 0;
+    int rc = read_status(w.sc.status, s, &st);
+    if (rc) return rc;
+    rc = status_to_code(st);
+    if (rc) return rc;
+    if (qerr_out) {
+        double nd[2] = {0.0, 0.0};
+        GQ_HIP(hipMemcpyAsync(nd, w.sc.d, sizeof(nd), hipMemcpyDeviceToHost, s), "qerr readback");
+        GQ_HIP(hipStreamSynchronize(s), "stream synchronize");
+        *qerr_out = nd[1] > 0.0 ? std::sqrt(nd[0] / nd[1]) : 0.0;
+    }
+    return GQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gq_abi_version(void) { return GQ_ABI_VERSION; }
+
+const char *gq_last_error(void) { return g_last_error.c_str(); }
+
+int hessian_accumulate(float *H, const void *X, int x_dtype, int64_t T, int64_t K, hipStream_t stream)
+{
+    g_last_error.clear();
+    if (!H || (!X && T > 0)) return fail(GQ_ERR_INVALID_ARG, "null required pointer");
+    if (K < 1 || T < 0) return fail(GQ_ERR_INVALID_ARG, "need K >= 1 and T >= 0");
+    if (x_dtype != GQ_F32 && x_dtype != GQ_BF16) return fail(GQ_ERR_INVALID_ARG, "unknown x_dtype");
+    if (T == 0) return GQ_OK;
+    if (x_dtype == GQ_BF16) {
+        GQ_HIP(launch_gram_bf16(H, (const uint16_t *)X, T, K, stream), "gram bf16");
+    } else {
+        GemmDesc d = gemm(X, K, X, K, K, K, T, H, K);
+        d.cin = H;
+        d.beta = 1.0;
+        d.mode = TILE_LOWER;
+        d.tri = 1;
+        GQ_HIP(gemm_tn_f32(d, stream), "gram f32");
+    }
+    return GQ_OK;
+}
+
+size_t hessian_tril_bytes(int64_t K)
+{
+    if (K < 1) return 0;
+    return (size_t)K * 4 + (size_t)K * (size_t)(K - 1) / 2 * 2;
+}
+
+int hessian_pack_tril(void *blob, const float *H, int64_t K, hipStream_t stream)
+{
+    g_last_error.clear();
+    if (!blob || !H) return fail(GQ_ERR_INVALID_ARG, "null required pointer");
+    if (K < 1) return fail(GQ_ERR_INVALID_ARG, "K must be >= 1");
+    GQ_HIP(launch_tril_pack((uint8_t *)blob, H, K, stream), "tril pack");
+    return GQ_OK;
+}
+
+int hessian_unpack_tril(float *H, const void *blob, int64_t K, hipStream_t stream)
+{
+    g_last_error.clear();
+    if (!blob || !H) return fail(GQ_ERR_INVALID_ARG, "null required pointer");
+    if (K < 1) return fail(GQ_ERR_INVALID_ARG, "K must be >= 1");
+    GQ_HIP(launch_tril_unpack(H, (const uint8_t *)blob, K, stream), "tril unpack");
+    return GQ_OK;
+}
+
+size_t psd_project_workspace_size(int64_t K) { return K < 1 ? 0 : psd_bytes(K); }
+
+// One square for the bound, then (square, step) per iteration except the first,
+// whose square is the bound's, then the rebuild: 2 * iterations + 1.
+int psd_project_products(void) { return 2 * (int)sign_schedule().size() + 1; }
+
+double psd_project_flops(int64_t K)
+{
+    if (K < 1) return 0.0;
+    const double k = (double)K;
+    return (double)psd_project_products() * k * k * (k + 1.0);
+}
+
+int psd_project(float *H, int64_t K, void *ws, size_t ws_bytes, hipStream_t stream)
+{
+    g_last_error.clear();
+    if (!H || !ws) return fail(GQ_ERR_INVALID_ARG, "null required pointer");
+    if (K < 1) return fail(GQ_ERR_INVALID_ARG, "K must be >= 1");
+    if (ws_bytes < psd_bytes(K)) return fail(GQ_ERR_INVALID_ARG, "workspace too small");
+    Carver cv(ws);
+    PsdWs w = carve_psd(cv, K);
+    const int64_t n = K * K;
+    unsigned *status = w.sc.status;
+    double *fro = w.sc.d + 0, *inv = w.sc.d + 1, *yfro = w.sc.d + 2, *c = w.sc.d + 3;
+    double *c1inv = w.sc.d + 4, *c3inv = w.sc.d + 5;
+    GQ_HIP(launch_fill_u32(status, 4, 0u, stream), "fill");
+    GQ_HIP(launch_sym_lower_to_f64(w.H64, H, K, status, stream), "symmetrise");
+    GQ_HIP(launch_frobenius(fro, w.H64, n, w.sc.partials, stream), "norm");
+    GQ_HIP(launch_scalar_combine(inv, fro, -1.0, nullptr, 0.0, stream), "inverse norm");
+
+    // X0 = H / ||H||_F;  Y0 = X0^2;  c = ||Y0||_F^(-1/2) tightens the bound
+    // (||H||_2 <= ||H^2||_F^(1/2)), so the spectrum of c X0 lies in [-1, 1].
+    GemmDesc sq = gemm(w.H64, K, w.H64, K, K, K, K, w.Y, K);
+    sq.alpha_dev = inv;
+    sq.alpha_pow = 2;
+    sq.mode = TILE_LOWER;
+    sq.tri = 1;
+    sq.out_t = w.Y;
+    GQ_HIP(gemm_tn_f64(sq, stream), "sign square");
+    GQ_HIP(launch_frobenius(yfro, w.Y, n, w.sc.partials, stream), "norm");
+    GQ_HIP(launch_scalar_combine(c, yfro, -0.5, nullptr, 0.0, stream), "bound");
+    GQ_HIP(launch_scalar_combine(c1inv, c, 1.0, inv, 1.0, stream), "scalars");
+    GQ_HIP(launch_scalar_combine(c3inv, c, 3.0, inv, 1.0, stream), "scalars");
+    const std::vector<double> al = sign_schedule();
+    double *X = w.X, *Xn = w.Xn;
+    for (size_t k = 0; k < al.size(); ++k) {
+        const double a = 1.5 * al[k], b = -0.5 * al[k] * al[k] * al[k];
+        if (k == 0) {
+            // X0 = inv H, so X1 = a (c inv) H + b (c^3 inv) H Y0
+            GemmDesc st = gemm(w.H64, K, w.Y, K, K, K, K, X, K);
+            st.cin = w.H64;
+            st.alpha = b;
+            st.alpha_dev = c3inv;
+            st.alpha_pow = 1;
+            st.beta = a;
+            st.beta_dev = c1inv;
+            st.beta_pow = 1;
+            st.mode = TILE_LOWER;
+            st.tri = 1;
+            st.out_t = X;
+            GQ_HIP(gemm_tn_f64(st, stream), "sign step");
+            continue;
+        }
+        GemmDesc y = gemm(X, K, X, K, K, K, K, w.Y, K);
+        y.mode = TILE_LOWER;
+        y.tri = 1;
+        y.out_t = w.Y;
+        GQ_HIP(gemm_tn_f64(y, stream), "sign square");
+        GemmDesc st = gemm(X, K, w.Y, K, K, K, K, Xn, K);
+        st.cin = X;
+        st.alpha = b;
+        st.beta = a;
+        st.mode = TILE_LOWER;
+        st.tri = 1;
+        st.out_t = Xn;
+        GQ_HIP(gemm_tn_f64(st, stream), "sign step");
+        double *t = X;
+        X = Xn;
+        Xn = t;
+    }
+    // P = (H + sign(H) H) / 2, written to H as fp32 (both triangles)
+    GemmDesc fin = gemm(X, K, w.H64, K, K, K, K, H, K);
+    fin.cin = w.H64;
+    fin.alpha = 0.5;
+    fin.beta = 0.5;
+    fin.mode = TILE_LOWER;
+    fin.tri = 1;
+    fin.out_t = H;
+    GQ_HIP(gemm_tn_f64_out_f32(fin, stream), "projection");
+    unsigned st = 0;
+    int rc = read_status(status, stream, &st);
+    if (rc) return rc;
+    return status_to_code(st);
+}
+
+size_t gptq_factor_workspace_size(int64_t K) { return K < 1 ? 0 : factor_bytes(K); }
+
+int gptq_factor(float *U, const float *H, int64_t K, float damp, void *ws, size_t ws_bytes,
+                hipStream_t stream)
+{
+    g_last_error.clear();
+    if (!U || !H || !ws) return fail(GQ_ERR_INVALID_ARG, "null required pointer");
+    if (K < 1) return fail(GQ_ERR_INVALID_ARG, "K must be >= 1");
+    if (!(damp >= 0.0f) || !std::isfinite(damp)) return fail(GQ_ERR_INVALID_ARG, "damp must be finite and >= 0");
+    if (ws_bytes < factor_bytes(K)) return fail(GQ_ERR_INVALID_ARG, "workspace too small");
+    Carver cv(ws);
+    FactorWs w = carve_factor(cv, K);
+    int rc = run_factor(U, H, K, damp, w, stream);
+    if (rc) return rc;
+    unsigned st = 0;
+    rc = read_status(w.sc.status, stream, &st);
+    if (rc) return rc;
+    return status_to_code(st);
+}
+
+size_t gptq_sweep_workspace_size(int64_t N, int64_t K, int64_t group)
+{
+    (void)group;
+    if (N < 1 || K < 1) return 0;
+    return sweep_bytes(N, K);
+}
+
+int gptq_sweep(uint8_t *codes, float *scales, double *qerr_out, const float *W, const float *U,
+               const float *imp, int64_t N, int64_t K, int64_t group, void *ws, size_t ws_bytes,
+               hipStream_t stream)
+{
+    g_last_error.clear();
+    int rc = check_sweep_args(codes, scales, W, U, N, K, group);
+    if (rc) return rc;
+    if (!ws) return fail(GQ_ERR_INVALID_ARG, "null workspace");
+    if (ws_bytes < sweep_bytes(N, K)) return fail(GQ_ERR_INVALID_ARG, "workspace too small");
+    Carver cv(ws);
+    SweepWs w = carve_sweep(cv, N, K);
+    return run_sweep(codes, scales, qerr_out, W, U, imp, N, K, group, w, stream);
+}
+
+size_t gptq_quantize_workspace_size(int64_t N, int64_t K, int64_t group)
+{
+    (void)group;
+    if (N < 1 || K < 1) return 0;
+    return factor_bytes(K) + align_up((size_t)K * (size_t)K * sizeof(float)) + sweep_bytes(N, K);
+}
+
+int gptq_quantize(uint8_t *codes, float *scales, double *qerr_out, const float *W, const float *H,
+                  const float *imp, int64_t N, int64_t K, int64_t group, float damp, void *ws,
+                  size_t ws_bytes, hipStream_t stream)
+{
+    g_last_error.clear();
+    int rc = check_sweep_args(codes, scales, W, H, N, K, group);
+    if (rc) return rc;
+    if (!ws) return fail(GQ_ERR_INVALID_ARG, "null workspace");
+    if (ws_bytes < gptq_quantize_workspace_size(N, K, group)) return fail(GQ_ERR_INVALID_ARG, "workspace too small");
+    char *base = (char *)ws;
+    const size_t fb = factor_bytes(K);
+    float *U = (float *)(base + fb);
+    void *sweep_ws = base + fb + align_up((size_t)K * (size_t)K * sizeof(float));
+    rc = gptq_factor(U, H, K, damp, base, fb, stream);
+    if (rc) return rc;
+    return gptq_sweep(codes, scales, qerr_out, W, U, imp, N, K, group, sweep_ws, sweep_bytes(N, K), stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,297 @@
+// gptq.hip -- the GPTQ error-feedback sweep over one lazy block of 128 columns,
+// and the qerr reduction (ork-driver wiki, "Exp 2026-08-18 GPTQ Int4": error-
+// compensated column-sequential int4 rounding emitting symmetric codes in
+// [-8, 7] with a per-(row, group) scale absmax/7; qerr definition).
+//
+// Sweep layout: rows are independent given U, so a wave holds 4 rows, 16 lanes
+// per row, 8 consecutive columns per lane (the whole 128-column block of a row
+// lives in registers).  Column i of the block is owned by lane i/8 of each
+// 16-lane row group; one __shfl broadcasts its current value to the row group,
+// every lane takes the same rounding decision, and each lane then applies the
+// error to its own 8 columns with one 32-byte LDS read of U's row i (the 128 x
+// 128 block of U sits in LDS; zeros below its diagonal make the update a no-op
+// for columns already done).  Group maxima are a 16-lane xor-shuffle reduction.
+// The per-column errors leave the kernel transposed (k-major) through LDS, as
+// the A operand of the matrix-core block update that follows.
+#include "gq_internal.h"
+
+namespace gq {
+namespace {
+
+constexpr int BW = kSweepBlock;        // 128
+constexpr int SW_NT = 512;             // 8 waves
+constexpr int ROWS_WG = 32;            // 4 rows per wave
+constexpr int UPITCH = BW + 4;
+
+__global__ __launch_bounds__(SW_NT) void sweep_block_kernel(float *__restrict__ Wk, float *__restrict__ ET,
+                                                           uint8_t *__restrict__ codes,
+                                                           float *__restrict__ scales,
+                                                           const float *__restrict__ U, int64_t N,
+                                                           int64_t K, int64_t G, int64_t b0)
+{
+    __shared__ __attribute__((aligned(16))) float Us[BW * UPITCH];
+    const int tid = threadIdx.x;
+    const int bw = (int)((K - b0) < BW ? (K - b0) : BW);
+
+    for (int e = tid; e < BW * BW; e += SW_NT) {
+        const int r = e / BW, c = e % BW;
+        Us[r * UPITCH + c] = (r < bw && c < bw) ? U[(b0 + r) * K + b0 + c] : 0.0f;
+    }
+    __syncthreads();
+
+    const int lane = tid & 63, wave = tid >> 6;
+    const int g16 = lane & 15;
+    const int rloc = wave * 4 + (lane >> 4);
+    const int64_t row = (int64_t)blockIdx.x * ROWS_WG + rloc;
+    const bool rv = row < N;
+    const int cb = g16 * 8;
+    const int src = lane & ~15;
+    const int64_t ngroups = K / G;
+    const int gmask = (int)G - 1;          // G is a power of two dividing 128
+
+    float w[8];
+    int cd[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+        const int col = cb + t;
+        w[t] = (rv && col < bw) ? Wk[row * K + b0 + col] : 0.0f;
+        cd[t] = 0;
+    }
+
+    float s = 0.0f;
+    for (int q = 0; q < 16; ++q) {
+        if (q * 8 >= bw) break;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            const int i = q * 8 + t;
+            if (i >= bw) break;
+            const float wi = __shfl(w[t], src + q, 64);
+            if ((i & gmask) == 0) {
+                float m = 0.0f;
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const int col = cb + u;
+                    if (col >= i && col < i + G) m = fmaxf(m, fabsf(w[u]));
+                }
+                m = fmaxf(m, __shfl_xor(m, 1, 16));
+                m = fmaxf(m, __shfl_xor(m, 2, 16));
+                m = fmaxf(m, __shfl_xor(m, 4, 16));
+                m = fmaxf(m, __shfl_xor(m, 8, 16));
+                s = m / 7.0f;
+                if (g16 == 0 && rv) scales[row * ngroups + (b0 + i) / G] = s;
+            }
+            float c = 0.0f;
+            if (s != 0.0f) {
+                c = rintf(wi / s);
+                c = fminf(fmaxf(c, -8.0f), 7.0f);
+            }
+            const float e = fmaf(-c, s, wi) / Us[i * UPITCH + i];
+            const float4 u0 = *(const float4 *)&Us[i * UPITCH + cb];
+            const float4 u1 = *(const float4 *)&Us[i * UPITCH + cb + 4];
+            w[0] = fmaf(-e, u0.x, w[0]);
+            w[1] = fmaf(-e, u0.y, w[1]);
+            w[2] = fmaf(-e, u0.z, w[2]);
+            w[3] = fmaf(-e, u0.w, w[3]);
+            w[4] = fmaf(-e, u1.x, w[4]);
+            w[5] = fmaf(-e, u1.y, w[5]);
+            w[6] = fmaf(-e, u1.z, w[6]);
+            w[7] = fmaf(-e, u1.w, w[7]);
+            if (g16 == q) {
+                w[t] = e;
+                cd[t] = (int)c;
+            }
+        }
+    }
+
+    // codes: two per byte, column 2m in the low nibble
+    if (rv) {
+        uint8_t *crow = codes + row * (K / 2) + (b0 + cb) / 2;
+        unsigned packed = 0;
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+            packed |= (((unsigned)cd[2 * m] & 0xFu) | (((unsigned)cd[2 * m + 1] & 0xFu) << 4)) << (8 * m);
+        if (cb + 8 <= bw && (((uintptr_t)crow & 3) == 0)) {
+            *(unsigned *)crow = packed;
+        } else {
+            for (int m = 0; m < 4; ++m)
+                if (cb + 2 * m < bw) crow[m] = (uint8_t)(packed >> (8 * m));
+        }
+    }
+
+    // errors, transposed through LDS: ET[k][n] for the block's k = 0..bw-1
+    __syncthreads();
+    float *Es = Us;                        // reuse: [BW][ROWS_WG + 1]
+#pragma unroll
+    for (int t = 0; t < 8; ++t) Es[(cb + t) * (ROWS_WG + 1) + rloc] = w[t];
+    __syncthreads();
+    const int64_t n0 = (int64_t)blockIdx.x * ROWS_WG;
+    for (int e = tid; e < BW * ROWS_WG; e += SW_NT) {
+        const int k = e / ROWS_WG, r = e % ROWS_WG;
+        if (k < bw && n0 + r < N) ET[k * N + n0 + r] = Es[k * (ROWS_WG + 1) + r];
+    }
+}
+
+__global__ __launch_bounds__(256) void copy_check_kernel(float *__restrict__ dst, const float *__restrict__ src,
+                                                        int64_t n, unsigned *status)
+{
+    bool bad = false;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    const int64_t n4 = n / 4;
+    const bool al = ((((uintptr_t)dst) | ((uintptr_t)src)) & 15) == 0;
+    if (al) {
+        for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n4; i += stride) {
+            const float4 v = ((const float4 *)src)[i];
+            if (!isfinite(v.x) || !isfinite(v.y) || !isfinite(v.z) || !isfinite(v.w)) bad = true;
+            ((float4 *)dst)[i] = v;
+        }
+        for (int64_t i = 4 * n4 + blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += stride) {
+            const float v = src[i];
+            if (!isfinite(v)) bad = true;
+            dst[i] = v;
+        }
+    } else {
+        for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += stride) {
+            const float v = src[i];
+            if (!isfinite(v)) bad = true;
+            dst[i] = v;
+        }
+    }
+    if (bad) atomicOr(status, ST_NONFINITE);
+}
+
+__global__ __launch_bounds__(256) void check_finite_kernel(const float *__restrict__ x, int64_t n,
+                                                          unsigned *status)
+{
+    bool bad = false;
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n;
+         i += (int64_t)gridDim.x * blockDim.x)
+        if (!isfinite(x[i])) bad = true;
+    if (bad) atomicOr(status, ST_NONFINITE);
+}
+
+constexpr int QNT = 256;
+constexpr int64_t QPARTS = 1024;
+
+__device__ void block_sum2(double &a, double &b, double *sh)
+{
+    const int t = threadIdx.x;
+    sh[t] = a;
+    sh[QNT + t] = b;
+    __syncthreads();
+    for (int s = QNT / 2; s > 0; s >>= 1) {
+        if (t < s) {
+            sh[t] += sh[t + s];
+            sh[QNT + t] += sh[QNT + t + s];
+        }
+        __syncthreads();
+    }
+    a = sh[0];
+    b = sh[QNT];
+}
+
+// Partial sums over a fixed row range per workgroup: sum imp (w - c s)^2, sum imp w^2.
+__global__ __launch_bounds__(QNT) void qerr_kernel(double *__restrict__ partials, const float *__restrict__ W,
+                                                  const uint8_t *__restrict__ codes,
+                                                  const float *__restrict__ scales,
+                                                  const float *__restrict__ imp, int64_t N, int64_t K,
+                                                  int64_t G, int64_t rows_per)
+{
+    __shared__ double sh[2 * QNT];
+    const int64_t r0 = blockIdx.x * rows_per;
+    const int64_t r1 = (r0 + rows_per < N) ? r0 + rows_per : N;
+    const int64_t half = K / 2, ng = K / G;
+    double num = 0.0, den = 0.0;
+    for (int64_t n = r0; n < r1; ++n) {
+        for (int64_t m = threadIdx.x; m < half; m += QNT) {
+            const unsigned b = codes[n * half + m];
+            const int c0 = (int)(b & 0xFu) - ((b & 0x8u) ? 16 : 0);
+            const int c1 = (int)(b >> 4) - ((b & 0x80u) ? 16 : 0);
+            const int64_t k0 = 2 * m, k1 = 2 * m + 1;
+            const float w0 = W[n * K + k0], w1 = W[n * K + k1];
+            const float s0 = scales[n * ng + k0 / G], s1 = scales[n * ng + k1 / G];
+            const double i0 = imp ? (double)imp[k0] : 1.0, i1 = imp ? (double)imp[k1] : 1.0;
+            const double d0 = (double)fmaf(-(float)c0, s0, w0), d1 = (double)fmaf(-(float)c1, s1, w1);
+            num += i0 * d0 * d0 + i1 * d1 * d1;
+            den += i0 * (double)w0 * (double)w0 + i1 * (double)w1 * (double)w1;
+        }
+    }
+    block_sum2(num, den, sh);
+    if (threadIdx.x == 0) {
+        partials[2 * blockIdx.x] = num;
+        partials[2 * blockIdx.x + 1] = den;
+    }
+}
+
+__global__ __launch_bounds__(QNT) void qerr_reduce_kernel(double *out2, const double *partials, int64_t nparts)
+{
+    __shared__ double sh[2 * QNT];
+    double a = 0.0, b = 0.0;
+    for (int64_t i = threadIdx.x; i < nparts; i += QNT) {
+        a += partials[2 * i];
+        b += partials[2 * i + 1];
+    }
+    block_sum2(a, b, sh);
+    if (threadIdx.x == 0) {
+        out2[0] = a;
+        out2[1] = b;
+    }
+}
+
+unsigned grid_for(int64_t n)
+{
+    int64_t g = (n + 255) / 256;
+    if (g > 16384) g = 16384;
+    if (g < 1) g = 1;
+    return (unsigned)g;
+}
+
+}  // namespace
+
+int64_t qerr_partials(int64_t N)
+{
+    const int64_t np = N < QPARTS ? N : QPARTS;
+    const int64_t rows_per = (N + np - 1) / np;
+    return (N + rows_per - 1) / rows_per;
+}
+
+hipError_t launch_copy_check(float *dst, const float *src, int64_t n, unsigned *status, hipStream_t s)
+{
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(copy_check_kernel, dim3(grid_for(n / 4 + 1)), dim3(256), 0, s, dst, src, n, status);
+    return hipGetLastError();
+}
+
+hipError_t launch_check_finite(const float *x, int64_t n, unsigned *status, hipStream_t s)
+{
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(check_finite_kernel, dim3(grid_for(n)), dim3(256), 0, s, x, n, status);
+    return hipGetLastError();
+}
+
+hipError_t launch_sweep_block(float *Wk, float *ET, uint8_t *codes, float *scales, const float *U,
+                              int64_t N, int64_t K, int64_t G, int64_t b0, hipStream_t s)
+{
+    const int64_t nwg = (N + ROWS_WG - 1) / ROWS_WG;
+    hipLaunchKernelGGL(sweep_block_kernel, dim3((unsigned)nwg), dim3(SW_NT), 0, s, Wk, ET, codes, scales,
+                       U, N, K, G, b0);
+    return hipGetLastError();
+}
+
+hipError_t launch_qerr(double *partials, const float *W, const uint8_t *codes, const float *scales,
+                       const float *imp, int64_t N, int64_t K, int64_t G, hipStream_t s)
+{
+    const int64_t np = N < QPARTS ? N : QPARTS;
+    const int64_t rows_per = (N + np - 1) / np;
+    const int64_t nwg = qerr_partials(N);
+    hipLaunchKernelGGL(qerr_kernel, dim3((unsigned)nwg), dim3(QNT), 0, s, partials, W, codes, scales, imp,
+                       N, K, G, rows_per);
+    return hipGetLastError();
+}
+
+hipError_t launch_qerr_reduce(double *out2, const double *partials, int64_t nparts, hipStream_t s)
+{
+    hipLaunchKernelGGL(qerr_reduce_kernel, dim3(1), dim3(QNT), 0, s, out2, partials, nparts);
+    return hipGetLastError();
+}
+
+}  // namespace gq

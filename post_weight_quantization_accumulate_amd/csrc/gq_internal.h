@@ -1,0 +1,102 @@
+// gq_internal.h -- shared declarations of the HIP implementation (gfx950).
+//
+// Device status word bits, the TN matrix-core GEMM interface used by every dense
+// contraction of the path (Gram in fp32, Cholesky/inverse and the sign iteration
+// in fp64, GPTQ lazy-block update in fp32), and the launchers of the other
+// kernels.  Host code in api.hip orchestrates them.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+namespace gq {
+
+// Bits of the device status word (OR-ed by kernels, read once per call).
+enum : unsigned {
+    ST_NOT_PD = 1u,      // a Cholesky pivot was not > 0
+    ST_NONFINITE = 2u,   // NaN / Inf in an input
+    ST_NO_CALIB = 4u,    // mean(diag H) <= 0 (or not finite)
+};
+
+// Which output tiles a GEMM launch computes.
+enum TileMode : int { TILE_RECT = 0, TILE_LOWER = 1, TILE_UPPER = 2 };
+
+// C(i, j) for i < M, j < N of
+//     out = alpha * sum_{k < Kd} A[k*lda + i] * B[k*ldb + j] + beta * cin[i*ldc + j]
+// Both operands are "k-major": row k of A holds the i-range, row k of B the
+// j-range (the transposed-A, normal-B product A^T B).  alpha and beta are the
+// host values times (*alpha_dev)^alpha_pow (resp. beta) when the device pointer
+// is set.  tri = 1 keeps only i >= j, tri = 2 only i <= j.  When out_t is set,
+// each kept (i, j) is also written at out_t[j*ldo + i] (the mirror; out_t is the
+// origin of the transposed block, which for a symmetric output is out itself).
+struct GemmDesc {
+    const void *A; int64_t lda;
+    const void *B; int64_t ldb;
+    int64_t M, N, Kd;
+    void *out; int64_t ldo;
+    void *out_t;              // mirror base (may equal out), or nullptr
+    const void *cin; int64_t ldc;   // same element type as A/B; may alias out
+    double alpha, beta;
+    const double *alpha_dev; int alpha_pow;
+    const double *beta_dev; int beta_pow;
+    int tri;
+    int mode;                 // TileMode
+};
+
+// T = float or double; OutT = T, or float for a double product written as fp32.
+hipError_t gemm_tn_f32(const GemmDesc &d, hipStream_t s);
+hipError_t gemm_tn_f64(const GemmDesc &d, hipStream_t s);
+hipError_t gemm_tn_f64_out_f32(const GemmDesc &d, hipStream_t s);
+
+// bf16 Gram: H_lower += X^T X, X T x K bf16 row-major.
+hipError_t launch_gram_bf16(float *H, const uint16_t *X, int64_t T, int64_t K, hipStream_t s);
+
+// Bf16TrilDiagF32 storage.
+hipError_t launch_tril_pack(uint8_t *blob, const float *H, int64_t K, hipStream_t s);
+hipError_t launch_tril_unpack(float *H, const uint8_t *blob, int64_t K, hipStream_t s);
+
+// Small helpers (factor.hip).
+hipError_t launch_fill_f64(double *p, int64_t n, double v, hipStream_t s);
+hipError_t launch_fill_u32(unsigned *p, int64_t n, unsigned v, hipStream_t s);
+hipError_t launch_set_identity_f64(double *X, int64_t K, hipStream_t s);
+// D = sym(lower(H)) in fp64; status |= NONFINITE on a non-finite lower entry.
+hipError_t launch_sym_lower_to_f64(double *D, const float *H, int64_t K, unsigned *status,
+                                   hipStream_t s);
+// out[0] = sqrt(sum of squares of a[0..n)), deterministic two-stage tree;
+// partials holds kFrobParts doubles.
+constexpr int64_t kFrobParts = 1024;
+hipError_t launch_frobenius(double *out, const double *a, int64_t n, double *partials, hipStream_t s);
+// out[0] = x[0]^px * y[0]^py (y optional), or 0 unless x[0] (and y[0]) are finite and > 0.
+hipError_t launch_scalar_combine(double *out, const double *x, double px, const double *y, double py,
+                                 hipStream_t s);
+// mu[0] = mean(diag H); status |= NO_CALIB if !(mu > 0); NONFINITE if the lower
+// triangle of H holds NaN/Inf.
+hipError_t launch_diag_mean_check(double *mu, const float *H, int64_t K, unsigned *status,
+                                  hipStream_t s);
+// M[i][j] = H[K-1-i][K-1-j] (i <= j, fp64) + (i == j) * damp * mu[0].
+hipError_t launch_damp_reverse(double *M, const float *H, int64_t K, double damp,
+                               const double *mu, hipStream_t s);
+// Factor the nb x nb diagonal block at (p0, p0) of M (upper Cholesky, in place,
+// mirrored below), write its inverse to Dinv and the transpose to DinvT.
+hipError_t launch_potrf_diag(double *M, int64_t K, int64_t p0, int nb, double *Dinv,
+                             double *DinvT, unsigned *status, hipStream_t s);
+// U[i][j] = X[K-1-j][K-1-i] for i <= j (as fp32), 0 below the diagonal.
+hipError_t launch_flip_transpose(float *U, const double *X, int64_t K, hipStream_t s);
+
+// GPTQ (gptq.hip).
+constexpr int kSweepBlock = 128;      // lazy-batch block width (columns)
+hipError_t launch_copy_check(float *dst, const float *src, int64_t n, unsigned *status,
+                             hipStream_t s);
+hipError_t launch_check_finite(const float *x, int64_t n, unsigned *status, hipStream_t s);
+hipError_t launch_sweep_block(float *Wk, float *ET, uint8_t *codes, float *scales,
+                              const float *U, int64_t N, int64_t K, int64_t G, int64_t b0,
+                              hipStream_t s);
+hipError_t launch_qerr(double *partials, const float *W, const uint8_t *codes,
+                       const float *scales, const float *imp, int64_t N, int64_t K, int64_t G,
+                       hipStream_t s);
+hipError_t launch_qerr_reduce(double *out2, const double *partials, int64_t nparts,
+                              hipStream_t s);
+int64_t qerr_partials(int64_t N);
+
+}  // namespace gq

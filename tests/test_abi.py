@@ -1,0 +1,46 @@
+"""CPU checks of the C ABI library: it loads without a GPU and exports every
+symbol include/gq.h declares (no compute calls: there is no GPU here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import post_weight_quantization_accumulate_amd as gq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    text = open(os.path.join(ROOT, "include", "gq.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", text)) - {"if", "while", "for", "sizeof"})
+
+
+def test_header_declares_the_binding_exports():
+    assert _declared() == sorted(gq.EXPORTS)
+
+
+@pytest.mark.skipif(not os.path.exists(gq.LIB_PATH), reason="libgq.so not built")
+def test_library_loads_and_exports_every_symbol():
+    L = ctypes.CDLL(gq.LIB_PATH)
+    for name in _declared():
+        assert hasattr(L, name), name
+    assert gq.abi_version() == 1
+
+
+@pytest.mark.skipif(not os.path.exists(gq.LIB_PATH), reason="libgq.so not built")
+def test_size_queries_are_host_only():
+    # Bf16TrilDiagF32 size: K*4 + K*(K-1)/2*2 (hipfire-calib-data, "Hessian storage")
+    for K, n in [(128, 16768), (1024, 1051648), (5120, 26229760), (17408, 303090688)]:
+        assert gq.hessian_tril_bytes(K) == n
+    assert gq.hessian_tril_bytes(0) == 0
+    assert gq.psd_project_workspace_size(1024) >= 4 * 1024 * 1024 * 8
+    assert gq.gptq_quantize_workspace_size(64, 128, 32) > gq.gptq_sweep_workspace_size(64, 128, 32)
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(gq, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(gq, "_lib", None)
+    with pytest.raises(RuntimeError, match="missing"):
+        gq.lib()
