@@ -51,9 +51,9 @@ def cpu_baseline(wl, X, W):
     N*K^2, qerr N*K)."""
     import numpy as np
     import oracle
-    Ks = min(wl.K, 1024)
-    Ts = min(wl.T, 2048)
-    Ns = min(wl.N[0], 256)
+    Ks = min(wl.K, 2560)
+    Ts = wl.T
+    Ns = min(wl.N[0], 2560)
     Xs = X[:Ts, :Ks].float().cpu().numpy()
     Ws = W[:Ns, :Ks].cpu().numpy()
     G = wl.group

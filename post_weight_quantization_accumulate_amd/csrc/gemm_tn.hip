@@ -69,18 +69,67 @@ __device__ inline double ipow(double x, int p)
     return r;
 }
 
-// Linear index of a lower-triangular tile list -> (ti >= tj).
-__device__ inline void tri_index(int64_t id, int64_t &ti, int64_t &tj)
+// Tile order.  Workgroup w runs on XCD w % 8 (round-robin dispatch), and each
+// XCD has its own L2.  The j-th workgroup of XCD x is given logical tile
+// base_x + j, so each XCD walks a contiguous stretch of the logical order; the
+// logical order visits tiles in groups of kGroup tile rows, column by column, so
+// the workgroups resident on one XCD at a time cover a compact block of tiles
+// and read the same A and B panels through its L2.
+constexpr int kXcd = 8;
+constexpr int64_t kGroup = 8;
+
+__device__ inline int64_t xcd_logical(int64_t w, int64_t n)
 {
-    int64_t t = (int64_t)((sqrt(8.0 * (double)id + 1.0) - 1.0) * 0.5);
-    while (t * (t + 1) / 2 > id) --t;
-    while ((t + 1) * (t + 2) / 2 <= id) ++t;
-    ti = t;
-    tj = id - t * (t + 1) / 2;
+    const int64_t x = w % kXcd, j = w / kXcd;
+    int64_t base = 0;
+    for (int64_t y = 0; y < x; ++y) base += (n - y + kXcd - 1) / kXcd;
+    return base + j;
+}
+
+// Rectangular tm x tn grid, grouped by kGroup tile rows.
+__device__ inline void rect_tile(int64_t l, int64_t tm, int64_t tn, int64_t &ti, int64_t &tj)
+{
+    const int64_t per = kGroup * tn;
+    const int64_t g = l / per, r = l % per;
+    const int64_t rows = (tm - g * kGroup) < kGroup ? (tm - g * kGroup) : kGroup;
+    tj = r / rows;
+    ti = g * kGroup + r % rows;
+}
+
+// Lower triangle (ti >= tj) of an nt x nt grid, grouped by kGroup tile rows:
+// group g holds rows [g*G, g*G+G); within it, column tj lists rows max(tj, g*G)..
+// All full groups before g hold sum over their rows of (row+1) tiles.
+__device__ inline void lower_tile(int64_t l, int64_t nt, int64_t &ti, int64_t &tj)
+{
+    int64_t g = 0, start = 0;
+    for (;;) {
+        const int64_t r0 = g * kGroup;
+        const int64_t r1 = (r0 + kGroup < nt) ? r0 + kGroup : nt;
+        const int64_t cnt = (r1 * (r1 + 1) - r0 * (r0 + 1)) / 2;   // tiles in rows [r0, r1)
+        if (l < start + cnt) {
+            int64_t off = l - start;
+            // columns 0 .. r0-1 have (r1 - r0) rows each
+            const int64_t full = r0 * (r1 - r0);
+            if (off < full) {
+                tj = off / (r1 - r0);
+                ti = r0 + off % (r1 - r0);
+            } else {
+                off -= full;           // columns r0 .. r1-1: column c has rows c .. r1-1
+                int64_t c = r0;
+                while (off >= r1 - c) { off -= r1 - c; ++c; }
+                tj = c;
+                ti = c + off;
+            }
+            return;
+        }
+        start += cnt;
+        ++g;
+    }
 }
 
 template <typename T, typename OutT>
-__global__ __launch_bounds__(NT) void gemm_tn_kernel(GemmDesc d, int64_t tiles_n, int vecA, int vecB)
+__global__ __launch_bounds__(NT) void gemm_tn_kernel(GemmDesc d, int64_t tiles_m, int64_t tiles_n, int vecA,
+                                                    int vecB)
 {
     using MF = Mfma<T>;
     constexpr int V = 16 / (int)sizeof(T);          // elements per 16-byte vector
@@ -93,43 +142,68 @@ __global__ __launch_bounds__(NT) void gemm_tn_kernel(GemmDesc d, int64_t tiles_n
     __shared__ __attribute__((aligned(16))) T Bs[2][BK][LDP];
 
     int64_t ti, tj;
-    const int64_t bid = blockIdx.x;
+    const int64_t l = xcd_logical(blockIdx.x, gridDim.x);
     if (d.mode == TILE_RECT) {
-        ti = bid / tiles_n;
-        tj = bid % tiles_n;
+        rect_tile(l, tiles_m, tiles_n, ti, tj);
     } else {
-        tri_index(bid, ti, tj);
+        lower_tile(l, tiles_m, ti, tj);
         if (d.mode == TILE_UPPER) { int64_t t = ti; ti = tj; tj = t; }
     }
     const int64_t i0 = ti * BM, j0 = tj * BN;
+    const bool full_i = vecA && (i0 + BM <= d.M);      // uniform across the workgroup
+    const bool full_j = vecB && (j0 + BN <= d.N);
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wr = wave >> 1, wc = wave & 1;
     const T *A = (const T *)d.A;
     const T *B = (const T *)d.B;
 
+    // Interior stages load whole 16-byte vectors unconditionally; edge stages
+    // load element by element from clamped (always valid) addresses and zero
+    // the out-of-range elements with a select, so no lane ever branches.
     vec_t ra[NV], rb[NV];
     auto gload = [&](int64_t kb) {
+        const bool full_k = kb + BK <= d.Kd;
+        if (full_i && full_k) {
 #pragma unroll
-        for (int v = 0; v < NV; ++v) {
-            const int lin = tid + NT * v;
-            const int kr = lin / VPR;
-            const int cc = (lin % VPR) * V;
-            const int64_t k = kb + kr;
-            const int64_t gi = i0 + cc, gj = j0 + cc;
-            if (k < d.Kd && vecA && gi + V <= d.M) {
-                ra[v] = *(const vec_t *)(A + k * d.lda + gi);
-            } else {
-#pragma unroll
-                for (int e = 0; e < V; ++e)
-                    ra[v][e] = (k < d.Kd && gi + e < d.M) ? A[k * d.lda + gi + e] : (T)0;
+            for (int v = 0; v < NV; ++v) {
+                const int lin = tid + NT * v;
+                const int kr = lin / VPR, cc = (lin % VPR) * V;
+                ra[v] = *(const vec_t *)(A + (kb + kr) * d.lda + i0 + cc);
             }
-            if (k < d.Kd && vecB && gj + V <= d.N) {
-                rb[v] = *(const vec_t *)(B + k * d.ldb + gj);
-            } else {
+        } else {
 #pragma unroll
-                for (int e = 0; e < V; ++e)
-                    rb[v][e] = (k < d.Kd && gj + e < d.N) ? B[k * d.ldb + gj + e] : (T)0;
+            for (int v = 0; v < NV; ++v) {
+                const int lin = tid + NT * v;
+                const int kr = lin / VPR, cc = (lin % VPR) * V;
+                const int64_t k = kb + kr;
+#pragma unroll
+                for (int e = 0; e < V; ++e) {
+                    const bool ok = k < d.Kd && i0 + cc + e < d.M;
+                    const T x = A[ok ? k * d.lda + i0 + cc + e : 0];
+                    ra[v][e] = ok ? x : (T)0;
+                }
+            }
+        }
+        if (full_j && full_k) {
+#pragma unroll
+            for (int v = 0; v < NV; ++v) {
+                const int lin = tid + NT * v;
+                const int kr = lin / VPR, cc = (lin % VPR) * V;
+                rb[v] = *(const vec_t *)(B + (kb + kr) * d.ldb + j0 + cc);
+            }
+        } else {
+#pragma unroll
+            for (int v = 0; v < NV; ++v) {
+                const int lin = tid + NT * v;
+                const int kr = lin / VPR, cc = (lin % VPR) * V;
+                const int64_t k = kb + kr;
+#pragma unroll
+                for (int e = 0; e < V; ++e) {
+                    const bool ok = k < d.Kd && j0 + cc + e < d.N;
+                    const T x = B[ok ? k * d.ldb + j0 + cc + e : 0];
+                    rb[v][e] = ok ? x : (T)0;
+                }
             }
         }
     };
@@ -218,7 +292,7 @@ hipError_t launch(const GemmDesc &d, hipStream_t s)
     }
     const int vecA = (d.lda % V == 0) && (((uintptr_t)d.A & 15) == 0);
     const int vecB = (d.ldb % V == 0) && (((uintptr_t)d.B & 15) == 0);
-    hipLaunchKernelGGL((gemm_tn_kernel<T, OutT>), dim3((unsigned)ntiles), dim3(NT), 0, s, d, tn,
+    hipLaunchKernelGGL((gemm_tn_kernel<T, OutT>), dim3((unsigned)ntiles), dim3(NT), 0, s, d, tm, tn,
                        vecA, vecB);
     return hipGetLastError();
 }

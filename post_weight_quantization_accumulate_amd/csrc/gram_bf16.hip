@@ -60,22 +60,28 @@ __global__ __launch_bounds__(NT) void gram_bf16_kernel(float *__restrict__ H,
     const int64_t cbase = (panel ? j0 : i0) + 8 * o;
     const bool loader = !(diag && panel == 1);
 
+    // Interior tiles and full token stages take unconditional 16-byte loads; the
+    // ragged edges load 16-bit elements from clamped addresses and zero the
+    // out-of-range ones with a select (no divergent branches around loads).
+    const bool full_c = vec && (i0 + BM <= K) && (j0 + BM <= K);
     u32x4 v[4];
     auto gload = [&](int64_t t0) {
         if (!loader) return;
+        if (full_c && t0 + BKT <= T) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int64_t t = t0 + 4 * q + r;
-            if (t < T && vec && cbase + 8 <= K) {
-                v[r] = *(const u32x4 *)(X + t * K + cbase);
-            } else {
+            for (int r = 0; r < 4; ++r) v[r] = *(const u32x4 *)(X + (t0 + 4 * q + r) * K + cbase);
+        } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int64_t t = t0 + 4 * q + r;
                 unsigned w[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int64_t c0 = cbase + 2 * e;
-                    unsigned lo = (t < T && c0 < K) ? X[t * K + c0] : 0u;
-                    unsigned hi = (t < T && c0 + 1 < K) ? X[t * K + c0 + 1] : 0u;
-                    w[e] = lo | (hi << 16);
+                    const bool ok0 = t < T && c0 < K, ok1 = t < T && c0 + 1 < K;
+                    const unsigned lo = X[ok0 ? t * K + c0 : 0];
+                    const unsigned hi = X[ok1 ? t * K + c0 + 1 : 0];
+                    w[e] = (ok0 ? lo : 0u) | ((ok1 ? hi : 0u) << 16);
                 }
                 v[r] = u32x4{w[0], w[1], w[2], w[3]};
             }
