@@ -127,8 +127,11 @@ __device__ inline void lower_tile(int64_t l, int64_t nt, int64_t &ti, int64_t &t
     }
 }
 
+// Two waves per SIMD: without the hint the fp64 instance keeps its 64-double
+// accumulator in AGPRs next to 238 VGPRs, one wave per SIMD, and every stage
+// stalls on its own loads; with it, 250 VGPRs and no AGPR copies.
 template <typename T, typename OutT>
-__global__ __launch_bounds__(NT) void gemm_tn_kernel(GemmDesc d, int64_t tiles_m, int64_t tiles_n, int vecA,
+__global__ __launch_bounds__(NT, 2) void gemm_tn_kernel(GemmDesc d, int64_t tiles_m, int64_t tiles_n, int vecA,
                                                     int vecB)
 {
     using MF = Mfma<T>;
