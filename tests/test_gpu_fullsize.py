@@ -1,0 +1,307 @@
+"""GPU parity at the workloads' full sizes, in the launch configuration the
+benchmark times: the attention-projection shape (T=8192, K=5120, N=10240,
+bf16 X), the MLP down-projection shape (T=8192, K=17408, N=5120, heavy-tailed
+bf16 X) and the streamed accumulation (8192-token chunks at K=5120).
+
+Where the oracle finishes in seconds it checks every output (Gram, storage,
+GPTQ codes/scales/qerr at K=5120).  Where it cannot, it checks outputs it can
+compute one by one (sampled Gram entries at K=17408; a block-diagonal Hessian of
+the full size whose U the oracle builds block by block) or properties that hold
+at any size: the projection onto the PSD cone is characterised by P >= 0,
+P - H >= 0 and <P, P - H> = 0, and is at least as close to H as the PSD Gram
+matrix it was stored from.
+"""
+import numpy as np
+import pytest
+import torch
+
+import synthgen as g
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module")
+def gq():
+    import post_weight_quantization_accumulate_amd as m
+    m.lib()
+    return m
+
+
+def _relF(a, b):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    return np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300)
+
+
+def _sym64(A):
+    A = np.asarray(A, np.float64)
+    return np.tril(A) + np.tril(A, -1).T
+
+
+def _stored_path(gq, wl, X):
+    """GPU: Gram of one chunk -> blob -> unpacked -> projected (all in HBM)."""
+    K = wl.K
+    H = torch.zeros(K, K, dtype=torch.float32, device=DEV)
+    gq.hessian_accumulate(H, X.to(DEV))
+    blob = torch.empty(gq.hessian_tril_bytes(K), dtype=torch.uint8, device=DEV)
+    gq.hessian_pack_tril(blob, H)
+    Hs = torch.empty(K, K, dtype=torch.float32, device=DEV)
+    gq.hessian_unpack_tril(Hs, blob)
+    P = Hs.clone()
+    gq.psd_project(P, gq.workspace(gq.psd_project_workspace_size(K), DEV))
+    torch.cuda.synchronize()
+    return H, blob, Hs, P
+
+
+def _kkt_certificates(P, Hs, eps):
+    """Cholesky certificates (LAPACK through torch, fp64, a library check) for
+    P + eps*mu*I >= 0 and (P - Hs) + eps*mu*I >= 0, plus the complementarity
+    <P, P - Hs> relative to ||P|| ||P - Hs||."""
+    P64 = P.to(torch.float64)
+    H64 = Hs.to(torch.float64)
+    H64 = torch.tril(H64) + torch.tril(H64, -1).T
+    K = P.shape[0]
+    mu = float(torch.diagonal(H64).mean())
+    I = torch.eye(K, dtype=torch.float64, device=P.device)
+    ok1 = int(torch.linalg.cholesky_ex(P64 + eps * mu * I).info) == 0
+    N = P64 - H64
+    ok2 = int(torch.linalg.cholesky_ex(N + eps * mu * I).info) == 0
+    comp = float((P64 * N).sum() / (torch.linalg.norm(P64) * torch.linalg.norm(N)).clamp_min(1e-300))
+    return ok1, ok2, comp, float(torch.linalg.norm(N) / torch.linalg.norm(H64))
+
+
+# ------------------------------------------------------------------ K = 5120
+@pytest.fixture(scope="module")
+def attn(gq, orc):
+    wl = g.WORKLOADS["attn5120"]
+    X = g.x_chunk(wl)
+    W = g.weights(wl)
+    H, blob, Hs, P = _stored_path(gq, wl, X)
+    return wl, X, W, H, blob, Hs, P
+
+
+def test_attn_gram_full(gq, orc, attn):
+    wl, X, W, H, blob, Hs, P = attn
+    ref = orc.gram(X)
+    low = np.tril_indices(wl.K)
+    Hg = H.cpu().numpy()
+    assert _relF(Hg[low], ref[low]) < 1e-5
+    # mean(diag H) about 1, as on the dataset card's K=5120 tensor (by construction of the recipe)
+    assert abs(np.diag(ref).mean() - 1.0) < 0.05
+
+
+def test_attn_storage_bitexact(gq, orc, attn):
+    wl, X, W, H, blob, Hs, P = attn
+    ref = orc.pack_tril(H.cpu().numpy())
+    assert np.array_equal(blob.cpu().numpy(), ref)
+    assert np.array_equal(Hs.cpu().numpy().view(np.uint32), orc.unpack_tril(ref, wl.K).view(np.uint32))
+
+
+def test_attn_projection_certificates(gq, orc, attn):
+    wl, X, W, H, blob, Hs, P = attn
+    Pn = P.cpu().numpy()
+    assert np.array_equal(Pn, Pn.T)
+    ok1, ok2, comp, change = _kkt_certificates(P, Hs, 1e-5)
+    assert ok1 and ok2 and abs(comp) < 1e-3
+    # no farther from the stored matrix than the pre-storage PSD Gram (a feasible point)
+    Hs64 = _sym64(Hs.cpu().numpy())
+    H32 = _sym64(H.cpu().numpy())
+    assert np.linalg.norm(Pn.astype(np.float64) - Hs64) <= np.linalg.norm(H32 - Hs64) * (1 + 1e-6)
+    assert change < 0.00391          # below bf16's step (dataset card, "The fix")
+
+
+def test_attn_gptq_full(gq, orc, attn):
+    """All 10240 rows: codes, scales and qerr against the oracle run on the same
+    projected Hessian, with the stored diagonal as importance."""
+    wl, X, W, H, blob, Hs, P = attn
+    N, K, G = wl.N[0], wl.K, wl.group
+    imp = blob[: 4 * K].view(torch.float32)
+    codes = torch.empty(N, K // 2, dtype=torch.uint8, device=DEV)
+    scales = torch.empty(N, K // G, dtype=torch.float32, device=DEV)
+    q = gq.gptq_quantize(codes, scales, W.to(DEV), P, imp, G, wl.damp,
+                         gq.workspace(gq.gptq_quantize_workspace_size(N, K, G), DEV))
+    Pn, Wn, impn = P.cpu().numpy(), W.numpy(), imp.cpu().numpy().copy()
+    st, U, mu = orc.gptq_U(Pn, wl.damp)
+    assert st == orc.OK
+    cg = orc.unpack_codes(codes.cpu().numpy(), K)
+    sg = scales.cpu().numpy()
+    oc, os_ = orc.gptq_sweep(Wn, U, G)
+    ident = float((cg == oc).mean())
+    rep = orc.gptq_replay(cg, sg, Wn, U, G)
+    print(f"K=5120 code identity {ident:.6f}, replay {rep}")
+    assert rep["inadmissible"] == 0 and rep["scale_mismatch"] == 0
+    assert ident >= 0.999
+    qo = orc.qerr(oc, os_, Wn, impn)
+    assert abs(q - qo) / qo < 1e-4
+
+
+def test_attn_raw_stored_hessian_needs_projection(gq, orc, attn):
+    """The dataset card: a stored Hessian fails Cholesky at small damping on about
+    half the K=5120 tensors, and succeeds at damp 0.01 once projected.  On this
+    synthetic recipe the raw stored matrix's outcome is reported, not assumed;
+    the projected one must factor."""
+    wl, X, W, H, blob, Hs, P = attn
+    K = wl.K
+    U = torch.empty(K, K, dtype=torch.float32, device=DEV)
+    ws = gq.workspace(gq.gptq_factor_workspace_size(K), DEV)
+    gq.gptq_factor(U, P, 0.01, ws)
+    try:
+        gq.gptq_factor(U, Hs, 0.01, ws)
+        raw = "factors"
+    except gq.GQError as e:
+        assert e.status == gq.GQ_ERR_NOT_PD
+        raw = "NOT_PD"
+    print(f"raw stored K=5120 Hessian at damp 0.01: {raw}")
+
+
+# ------------------------------------------------------------------ K = 17408
+@pytest.fixture(scope="module")
+def mlp(gq):
+    wl = g.WORKLOADS["mlpdown17408"]
+    X = g.x_chunk(wl)
+    H, blob, Hs, P = _stored_path(gq, wl, X)
+    return wl, X, H, blob, Hs, P
+
+
+@pytest.fixture(scope="module")
+def mlp_w():
+    return g.weights(g.WORKLOADS["mlpdown17408"])
+
+
+def test_mlp_gram_sampled_entries(gq, orc, mlp):
+    wl, X, H, blob, Hs, P = mlp
+    K = wl.K
+    rng = np.random.default_rng(0)
+    I = np.concatenate([rng.integers(0, K, 200), [0, K - 1, K - 1, 5000, 17407]])
+    J = np.concatenate([rng.integers(0, K, 200), [0, 0, K - 1, 4999, 128]])
+    I, J = np.maximum(I, J), np.minimum(I, J)
+    ref = orc.gram_entries(X, I, J)
+    got = H.cpu().numpy()[I, J]
+    assert _relF(got, ref) < 1e-5
+
+
+def test_mlp_storage_bitexact(gq, orc, mlp):
+    wl, X, H, blob, Hs, P = mlp
+    ref = orc.pack_tril(H.cpu().numpy())
+    assert np.array_equal(blob.cpu().numpy(), ref)
+    assert np.array_equal(Hs.cpu().numpy().view(np.uint32), orc.unpack_tril(ref, wl.K).view(np.uint32))
+
+
+def test_mlp_projection_certificates(gq, mlp):
+    wl, X, H, blob, Hs, P = mlp
+    Pc = P.cpu()
+    assert torch.equal(Pc, Pc.T)
+    ok1, ok2, comp, change = _kkt_certificates(P, Hs, 1e-5)
+    assert ok1 and ok2 and abs(comp) < 1e-3
+    Hs64 = Hs.to(torch.float64)
+    H64 = H.to(torch.float64)
+    Hsym = torch.tril(H64) + torch.tril(H64, -1).T          # the GPU Gram fills the lower triangle
+    assert float(torch.linalg.norm(P.to(torch.float64) - Hs64)) <= float(
+        torch.linalg.norm(Hsym - Hs64)) * (1 + 1e-6)
+    assert change < 0.00391
+
+
+def test_mlp_gptq_blockdiag_hessian(gq, orc, mlp_w):
+    """Full K=17408 launch configuration (N=5120, G=128) on a block-diagonal
+    Hessian with ragged 300-column blocks, so coupling crosses the 128-column
+    lazy blocks; the oracle builds U block by block and sweeps sampled rows."""
+    wl = g.WORKLOADS["mlpdown17408"]
+    K, N, G = wl.K, wl.N[0], wl.group
+    W = mlp_w
+    edges = list(range(0, K, 300)) + [K]
+    Hd = np.zeros((K, K), np.float32)
+    U = np.zeros((K, K), np.float64)
+    for a, b in zip(edges[:-1], edges[1:]):
+        Xb = g.normal_matrix(a + 7, g.S_X, 2 * (b - a), b - a).numpy()
+        Hb = orc.gram(Xb).astype(np.float32)
+        Hd[a:b, a:b] = Hb
+    mu = float(np.trace(Hd.astype(np.float64)) / K)
+    for a, b in zip(edges[:-1], edges[1:]):
+        # the damping is in units of the whole matrix's mean diagonal
+        blk = Hd[a:b, a:b].astype(np.float64) + 0.01 * mu * np.eye(b - a)
+        st, Ub, _ = orc.gptq_U(blk.astype(np.float32), 0.0)
+        assert st == orc.OK
+        U[a:b, a:b] = Ub
+    codes = torch.empty(N, K // 2, dtype=torch.uint8, device=DEV)
+    scales = torch.empty(N, K // G, dtype=torch.float32, device=DEV)
+    q = gq.gptq_quantize(codes, scales, W.to(DEV), torch.from_numpy(Hd).to(DEV), None, G, 0.01,
+                         gq.workspace(gq.gptq_quantize_workspace_size(N, K, G), DEV))
+    rows = np.array([0, 1, 777, 2500, N - 1])
+    cg = orc.unpack_codes(codes.cpu().numpy()[rows], K)
+    sg = scales.cpu().numpy()[rows]
+    Wn = W.numpy()
+    rep = orc.gptq_replay(cg, sg, Wn, U, G, rows=rows)
+    oc, os_ = orc.gptq_sweep(Wn, U, G, rows=rows)
+    ident = float((cg == oc).mean())
+    print(f"K=17408 block-diagonal: identity {ident:.6f}, replay {rep}")
+    assert rep["inadmissible"] == 0 and rep["scale_mismatch"] == 0 and ident >= 0.999
+    assert 0.0 < q < 1.0
+
+
+def test_mlp_gptq_diagonal_is_rtn(gq, orc, mlp_w):
+    wl = g.WORKLOADS["mlpdown17408"]
+    K, N, G = wl.K, wl.N[0], wl.group
+    W = mlp_w
+    d = np.exp(g.normal_tensor(1, g.S_S, (K,)).numpy()).astype(np.float32)
+    codes = torch.empty(N, K // 2, dtype=torch.uint8, device=DEV)
+    scales = torch.empty(N, K // G, dtype=torch.float32, device=DEV)
+    gq.gptq_quantize(codes, scales, W.to(DEV), torch.diag(torch.from_numpy(d)).to(DEV), None, G, 0.01,
+                     gq.workspace(gq.gptq_quantize_workspace_size(N, K, G), DEV), want_qerr=False)
+    rc, rs = orc.rtn(W.numpy(), G)
+    assert np.array_equal(orc.unpack_codes(codes.cpu().numpy(), K), rc)
+    assert np.array_equal(scales.cpu().numpy(), rs)
+
+
+def test_mlp_gptq_projected_beats_rtn_on_output(gq, orc, mlp, mlp_w):
+    """GPTQ with the projected K=17408 Hessian at damp 0.01 (which the dataset
+    card says needs the projection) factors, and its output error ||(W - Q) X||
+    on a row sample is below round-to-nearest's."""
+    wl, X, H, blob, Hs, P = mlp
+    K, N, G = wl.K, wl.N[0], wl.group
+    W = mlp_w
+    imp = blob[: 4 * K].view(torch.float32)
+    codes = torch.empty(N, K // 2, dtype=torch.uint8, device=DEV)
+    scales = torch.empty(N, K // G, dtype=torch.float32, device=DEV)
+    q = gq.gptq_quantize(codes, scales, W.to(DEV), P, imp, G, wl.damp,
+                         gq.workspace(gq.gptq_quantize_workspace_size(N, K, G), DEV))
+    rows = np.arange(0, N, 40)
+    cg = orc.unpack_codes(codes.cpu().numpy()[rows], K).astype(np.float64)
+    sg = scales.cpu().numpy()[rows].astype(np.float64)
+    Wr = W.numpy()[rows].astype(np.float64)
+    Qg = (cg.reshape(len(rows), -1, G) * sg[:, :, None]).reshape(len(rows), K)
+    rc, rs = orc.rtn(W.numpy()[rows], G)
+    Qr = (rc.astype(np.float64).reshape(len(rows), -1, G) * rs[:, :, None]).reshape(len(rows), K)
+    Xd = X.to(DEV).to(torch.float64)
+    eg = float(torch.linalg.norm(torch.from_numpy(Wr - Qg).to(DEV) @ Xd.T))
+    er = float(torch.linalg.norm(torch.from_numpy(Wr - Qr).to(DEV) @ Xd.T))
+    print(f"K=17408 qerr {q:.5f}; output error GPTQ/RTN = {eg / er:.4f}")
+    assert eg < er
+
+
+# ------------------------------------------------------------------ streaming
+def test_stream_chunks_full_width(gq, orc):
+    """8 chunks of 8192 tokens at K=5120 (the streamed recipe), accumulated in
+    two halves with a host round trip of H in between: bitwise equal to the
+    uninterrupted run, and equal to the oracle's sum on sampled entries."""
+    wl = g.WORKLOADS["stream5120"]
+    small = g.Workload("stream5120", wl.T, wl.K, wl.N, wl.group, wl.damp, "bf16", True, 8, wl.seed)
+    K = wl.K
+    chunks = [g.x_chunk(small, c) for c in range(small.chunks)]
+    H = torch.zeros(K, K, dtype=torch.float32, device=DEV)
+    for X in chunks:
+        gq.hessian_accumulate(H, X.to(DEV))
+    H2 = torch.zeros(K, K, dtype=torch.float32, device=DEV)
+    for X in chunks[:4]:
+        gq.hessian_accumulate(H2, X.to(DEV))
+    H3 = H2.cpu().to(DEV)
+    for X in chunks[4:]:
+        gq.hessian_accumulate(H3, X.to(DEV))
+    torch.cuda.synchronize()
+    assert torch.equal(H.cpu(), H3.cpu())
+    rng = np.random.default_rng(1)
+    I = rng.integers(0, K, 64)
+    J = rng.integers(0, K, 64)
+    I, J = np.maximum(I, J), np.minimum(I, J)
+    ref = sum(orc.gram_entries(X, I, J) for X in chunks)
+    assert _relF(H.cpu().numpy()[I, J], ref) < 1e-5
