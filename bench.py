@@ -176,6 +176,7 @@ def main():
         "stages_ms": {k: round(v, 4) for k, v in stage_ms.items()},
         "hessian_tflops": gram_tflops,
         "hessian_frac_of_bf16_peak": gram_tflops / PEAK_TFLOPS["bf16"],
+        "tensors_per_s": 1e3 / ms_step,
         "gptq_weights_per_s": N * K / (gptq_ms * 1e-3),
         "sweep_update_tflops": upd_flops / (stage_ms["sweep"] * 1e-3) / 1e12,
         "qerr": qerr[0],

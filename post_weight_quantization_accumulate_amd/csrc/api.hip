@@ -96,7 +96,6 @@ GemmDesc gemm(const void *A, int64_t lda, const void *B, int64_t ldb, int64_t M,
     return d;
 }
 
-constexpr int kPanel = 64;             // Cholesky / inverse panel width
 
 // ------------------------------------------------------------- sign iteration
 // Scaled Newton-Schulz for sign(X), X symmetric with spectrum in [-1, 1]:

@@ -136,61 +136,276 @@ __global__ __launch_bounds__(NT) void damp_reverse_kernel(double *__restrict__ M
     }
 }
 
-// Upper Cholesky (A = R^T R) of one nb x nb diagonal block in LDS, then its
-// triangular inverse.  Writes R (upper) and R^T (lower) back into M, and the
-// inverse / transposed inverse into Dinv / DinvT (nb x nb, row-major, ld = nb).
-constexpr int NBMAX = 64;
+// Upper Cholesky (A = R^T R) of one nb x nb diagonal block (nb <= 128) and its
+// triangular inverse, blocked by 32 so that the sequential part runs in one wave
+// without workgroup barriers:
+//   - one wave factors and inverts each 32 x 32 diagonal sub-block D in its
+//     registers (each lane a 4 x 4 tile), publishing the pivot row (column) of
+//     each step through LDS;
+//   - all 8 waves then apply it: the strip solve R[D, rest] = R_DD^-T A[D, rest]
+//     and the trailing update A[rest, rest] -= R[D, rest]^T R[D, rest];
+//   - the inverse of the whole block is built by block back substitution,
+//     X[i, rest] = -X_ii R[i, rest] X[rest, rest].
+// The block lives in LDS: R in the upper triangle, the inverse transposed in the
+// lower triangle (its diagonal apart).  Writes R (upper) and R^T (lower) back
+// into M, and the inverse and its transpose to Dinv / DinvT (nb x nb, ld = nb).
+// Rows and columns beyond nb are padded with the identity, which decouples them.
+constexpr int NBMAX = kPanel;
+constexpr int SB = 32;
+constexpr int PNT = 512;
 
-__global__ __launch_bounds__(NT) void potrf_diag_kernel(double *__restrict__ M, int64_t K, int64_t p0,
-                                                       int nb, double *__restrict__ Dinv,
-                                                       double *__restrict__ DinvT, unsigned *status)
+// One wave: Cholesky and inverse of the 32 x 32 block at (o, o) of A.  Lane l
+// owns rows 4 (l / 8) + i and columns 4 (l % 8) + k.  A wave's LDS operations
+// complete in issue order, so a value published to LDS is visible to the reads
+// that follow it; the wave barriers only stop the compiler from reordering them.
+// Writes R (upper) into A, the inverse dense into XD and transposed into the
+// sub-block's strict lower triangle (diagonal into xdiag).  Returns true if a
+// pivot of a real (not padded) row was not positive.
+__device__ bool wave_factor32(double (*A)[NBMAX + 1], double *xdiag, double (*XD)[SB + 1],
+                              double *rowj, double *colj, int o, int nb, int lane)
 {
-    __shared__ double a[NBMAX][NBMAX + 1];
-    __shared__ double x[NBMAX][NBMAX + 1];
+    const int br = lane >> 3, bc = lane & 7;
+    double a[4][4], x[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int r = 4 * br + i, c = 4 * bc + k;
+            a[i][k] = (c >= r) ? A[o + r][o + c] : 0.0;
+            x[i][k] = (r == c) ? 1.0 : 0.0;
+        }
+    bool badp = false;
+#pragma unroll 1
+    for (int j = 0; j < SB; ++j) {
+        if (br == (j >> 2)) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)                 // static register indices
+                if (i == (j & 3)) {
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) rowj[4 * bc + k] = a[i][k];
+                }
+        }
+        __builtin_amdgcn_wave_barrier();
+        double piv = rowj[j];
+        if (!(piv > 0.0)) {
+            if (o + j < nb) badp = true;
+            piv = 1.0;
+        }
+        const double rjj = sqrt(piv), inv = 1.0 / rjj;
+        double vr[4], vc[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) vr[i] = rowj[4 * br + i] * inv;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) vc[k] = rowj[4 * bc + k] * inv;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {          // branch-free: every lane computes both
+                const int r = 4 * br + i, c = 4 * bc + k;
+                const double v = a[i][k];
+                const double scl = (c == j) ? rjj : ((c > j) ? v * inv : v);
+                const double upd = fma(-vr[i], vc[k], v);
+                a[i][k] = (r == j) ? scl : ((r > j && c >= r) ? upd : v);
+            }
+        __builtin_amdgcn_wave_barrier();
+    }
+    // X = R^{-1}: for j = 31 .. 0: X[j][:] /= R[j][j]; X[r][:] -= R[r][j] X[j][:] (r < j)
+#pragma unroll 1
+    for (int j = SB - 1; j >= 0; --j) {
+        if (bc == (j >> 2)) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                if (k == (j & 3)) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) colj[4 * br + i] = a[i][k];
+                }
+        }
+        __builtin_amdgcn_wave_barrier();
+        const double inv = 1.0 / colj[j];
+        if (br == (j >> 2)) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (i == (j & 3)) {
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        x[i][k] *= inv;
+                        rowj[4 * bc + k] = x[i][k];
+                    }
+                }
+        }
+        __builtin_amdgcn_wave_barrier();
+        double vr[4], vc[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) vr[i] = colj[4 * br + i];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) vc[k] = rowj[4 * bc + k];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const double v = x[i][k];
+                x[i][k] = (4 * br + i < j) ? fma(-vr[i], vc[k], v) : v;
+            }
+        __builtin_amdgcn_wave_barrier();
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int r = 4 * br + i, c = 4 * bc + k;
+            if (c >= r) A[o + r][o + c] = a[i][k];
+            XD[r][c] = x[i][k];
+            if (r < c) A[o + c][o + r] = x[i][k];
+            if (r == c) xdiag[o + r] = x[i][k];
+        }
+    return badp;
+}
+
+// X[k][c] of the inverse for k, c in the finished lower-right part: stored
+// transposed below the diagonal, diagonal apart, zero for k > c.
+__device__ inline double xval(double (*A)[NBMAX + 1], const double *xdiag, int k, int c)
+{
+    const double lo = A[c][k];
+    const double dg = xdiag[c];
+    return (k < c) ? lo : ((k == c) ? dg : 0.0);
+}
+
+__global__ __launch_bounds__(PNT) void potrf_diag_kernel(double *__restrict__ M, int64_t K, int64_t p0,
+                                                        int nb, double *__restrict__ Dinv,
+                                                        double *__restrict__ DinvT, unsigned *status)
+{
+    __shared__ double A[NBMAX][NBMAX + 1];
+    __shared__ double XD[SB][SB + 1];
+    __shared__ double xdiag[NBMAX];
+    __shared__ double rowj[SB], colj[SB];
     __shared__ int bad;
-    const int t = threadIdx.x;
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+
+    for (int e = t; e < NBMAX * NBMAX; e += PNT) {
+        const int r = e >> 7, c = e & 127;
+        const bool in = r < nb && c < nb;
+        A[r][c] = (in && c >= r) ? M[(p0 + r) * K + p0 + c] : ((r == c) ? 1.0 : 0.0);
+    }
     if (t == 0) bad = 0;
-    for (int e = t; e < nb * nb; e += NT) {
-        const int r = e / nb, c = e % nb;
-        a[r][c] = (c >= r) ? M[(p0 + r) * K + p0 + c] : 0.0;
-        x[r][c] = 0.0;
+    __syncthreads();
+
+    const int cc = t & 127, rg = t >> 7;             // strip mapping: one column, 8 rows
+    const int ty = t >> 5, tx = t & 31;              // trailing mapping: 16 x 32 grid
+#pragma unroll 1
+    for (int s = 0; s < NBMAX / SB; ++s) {
+        const int o = s * SB;
+        if (wave == 0) {
+            const bool b = wave_factor32(A, xdiag, XD, rowj, colj, o, nb, lane);
+            if (b && lane == 0) bad = 1;
+        }
+        __syncthreads();
+        if (o + SB >= NBMAX) break;
+        // strip: R[o+rr][c] = sum_k XD[k][rr] A[o+k][c]  (XD is zero below its diagonal)
+        const int c = o + SB + cc;
+        double out[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) out[q] = 0.0;
+        if (c < NBMAX) {
+#pragma unroll 4
+            for (int k = 0; k < SB; ++k) {
+                const double ak = A[o + k][c];
+#pragma unroll
+                for (int q = 0; q < 8; ++q) out[q] += XD[k][rg * 8 + q] * ak;
+            }
+        }
+        __syncthreads();
+        if (c < NBMAX) {
+#pragma unroll
+            for (int q = 0; q < 8; ++q) A[o + rg * 8 + q][c] = out[q];
+        }
+        __syncthreads();
+        // trailing: A[r][c] -= sum_k R[o+k][r] R[o+k][c], r <= c in [o+32, 128)
+        const int base = o + SB;
+        double acc[6][3];
+#pragma unroll
+        for (int i = 0; i < 6; ++i)
+#pragma unroll
+            for (int kk = 0; kk < 3; ++kk) acc[i][kk] = 0.0;
+#pragma unroll 2
+        for (int k = 0; k < SB; ++k) {
+            double vr[6], vc[3];
+#pragma unroll
+            for (int i = 0; i < 6; ++i) {
+                const int r = base + ty + 16 * i;
+                vr[i] = A[o + k][r < NBMAX ? r : NBMAX - 1];
+            }
+#pragma unroll
+            for (int kk = 0; kk < 3; ++kk) {
+                const int c2 = base + tx + 32 * kk;
+                vc[kk] = A[o + k][c2 < NBMAX ? c2 : NBMAX - 1];
+            }
+#pragma unroll
+            for (int i = 0; i < 6; ++i)
+#pragma unroll
+                for (int kk = 0; kk < 3; ++kk) acc[i][kk] += vr[i] * vc[kk];
+        }
+#pragma unroll
+        for (int i = 0; i < 6; ++i)
+#pragma unroll
+            for (int kk = 0; kk < 3; ++kk) {
+                const int r = base + ty + 16 * i, c2 = base + tx + 32 * kk;
+                if (r < NBMAX && c2 < NBMAX && r <= c2) A[r][c2] -= acc[i][kk];
+            }
+        __syncthreads();
+    }
+
+    // R is final: write it (upper) and R^T (lower) back, before the upper
+    // triangle is reused as scratch by the inverse
+    for (int e = t; e < NBMAX * NBMAX; e += PNT) {
+        const int r = e >> 7, c = e & 127;
+        if (r < nb && c < nb) M[(p0 + r) * K + p0 + c] = (c >= r) ? A[r][c] : A[c][r];
     }
     __syncthreads();
-    for (int j = 0; j < nb; ++j) {
-        if (t == 0) {
-            double d = a[j][j];
-            if (!(d > 0.0)) { bad = 1; d = 1.0; }
-            a[j][j] = sqrt(d);
+
+    // ---- inverse, block rows from the bottom: X[i, rest] = -X_ii (R[i, rest] X[rest, rest])
+#pragma unroll 1
+    for (int i = NBMAX / SB - 2; i >= 0; --i) {
+        const int o = i * SB;
+        const int c = o + SB + cc;
+        double tv[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) tv[q] = 0.0;
+        if (c < NBMAX) {
+            for (int k = o + SB; k <= c; ++k) {
+                const double xk = xval(A, xdiag, k, c);
+#pragma unroll
+                for (int q = 0; q < 8; ++q) tv[q] += A[o + rg * 8 + q][k] * xk;
+            }
         }
         __syncthreads();
-        const double rjj = a[j][j];
-        for (int c = j + 1 + t; c < nb; c += NT) a[j][c] /= rjj;
+        if (c < NBMAX) {                      // T replaces R[i, rest] (already written out)
+#pragma unroll
+            for (int q = 0; q < 8; ++q) A[o + rg * 8 + q][c] = tv[q];
+        }
         __syncthreads();
-        // trailing update of the upper triangle: a[r][c] -= a[j][r] * a[j][c], j < r <= c
-        const int m = nb - j - 1;
-        for (int e = t; e < m * m; e += NT) {
-            const int r = j + 1 + e / m, c = j + 1 + e % m;
-            if (c >= r) a[r][c] -= a[j][r] * a[j][c];
+        if (c < NBMAX) {
+            double xo[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) xo[q] = 0.0;
+#pragma unroll 2
+            for (int m = 0; m < SB; ++m) {
+                const double tm = A[o + m][c];
+#pragma unroll
+                for (int q = 0; q < 8; ++q) xo[q] -= xval(A, xdiag, o + rg * 8 + q, o + m) * tm;
+            }
+#pragma unroll
+            for (int q = 0; q < 8; ++q) A[c][o + rg * 8 + q] = xo[q];     // X[o+rr][c], transposed
         }
         __syncthreads();
     }
-    // inverse of the upper triangular R by back substitution, one column per thread
-    if (t < nb) {
-        const int c = t;
-        x[c][c] = 1.0 / a[c][c];
-        for (int r = c - 1; r >= 0; --r) {
-            double s = 0.0;
-            for (int m2 = r + 1; m2 <= c; ++m2) s += a[r][m2] * x[m2][c];
-            x[r][c] = -s / a[r][r];
+
+    for (int e = t; e < NBMAX * NBMAX; e += PNT) {
+        const int r = e >> 7, c = e & 127;
+        if (r < nb && c < nb) {
+            const double xv = (c > r) ? A[c][r] : ((c == r) ? xdiag[r] : 0.0);
+            Dinv[r * nb + c] = xv;
+            DinvT[c * nb + r] = xv;
         }
-    }
-    __syncthreads();
-    for (int e = t; e < nb * nb; e += NT) {
-        const int r = e / nb, c = e % nb;
-        const double rv = (c >= r) ? a[r][c] : a[c][r];     // R above, R^T below
-        M[(p0 + r) * K + p0 + c] = rv;
-        Dinv[r * nb + c] = x[r][c];
-        DinvT[c * nb + r] = x[r][c];
     }
     if (t == 0 && bad) atomicOr(status, ST_NOT_PD);
 }
@@ -289,7 +504,7 @@ hipError_t launch_potrf_diag(double *M, int64_t K, int64_t p0, int nb, double *D
                              unsigned *status, hipStream_t s)
 {
     if (nb < 1 || nb > NBMAX) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(potrf_diag_kernel, dim3(1), dim3(NT), 0, s, M, K, p0, nb, Dinv, DinvT, status);
+    hipLaunchKernelGGL(potrf_diag_kernel, dim3(1), dim3(PNT), 0, s, M, K, p0, nb, Dinv, DinvT, status);
     return hipGetLastError();
 }
 

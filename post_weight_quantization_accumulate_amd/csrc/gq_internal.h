@@ -77,6 +77,9 @@ hipError_t launch_diag_mean_check(double *mu, const float *H, int64_t K, unsigne
 // M[i][j] = H[K-1-i][K-1-j] (i <= j, fp64) + (i == j) * damp * mu[0].
 hipError_t launch_damp_reverse(double *M, const float *H, int64_t K, double damp,
                                const double *mu, hipStream_t s);
+// Cholesky / inverse panel width: the diagonal blocks are factored in one
+// workgroup, and every trailing and inverse update is a GEMM of depth kPanel.
+constexpr int kPanel = 128;
 // Factor the nb x nb diagonal block at (p0, p0) of M (upper Cholesky, in place,
 // mirrored below), write its inverse to Dinv and the transpose to DinvT.
 hipError_t launch_potrf_diag(double *M, int64_t K, int64_t p0, int nb, double *Dinv,
