@@ -121,6 +121,7 @@ std::vector<double> sign_schedule()
 struct PsdWs {
     Scalars sc;
     double *H64, *X, *Y, *Xn;
+    double *partials;          // stream-K split-tile accumulators (large K only)
 };
 
 PsdWs carve_psd(Carver &c, int64_t K)
@@ -132,6 +133,8 @@ PsdWs carve_psd(Carver &c, int64_t K)
     w.X = c.take<double>(n);
     w.Y = c.take<double>(n);
     w.Xn = c.take<double>(n);
+    w.partials = streamk_lower_worthwhile(K) ? c.take<double>(streamk_partials_bytes(sizeof(double)) / sizeof(double))
+                                             : nullptr;
     return w;
 }
 
@@ -383,7 +386,7 @@ int psd_project(float *H, int64_t K, void *ws, size_t ws_bytes, hipStream_t stre
     sq.mode = TILE_LOWER;
     sq.tri = 1;
     sq.out_t = w.Y;
-    GQ_HIP(gemm_tn_f64(sq, stream), "sign square");
+    GQ_HIP(gemm_tn_f64_streamk(sq, w.partials, stream), "sign square");
     GQ_HIP(launch_frobenius(yfro, w.Y, n, w.sc.partials, stream), "norm");
     GQ_HIP(launch_scalar_combine(c, yfro, -0.5, nullptr, 0.0, stream), "bound");
     GQ_HIP(launch_scalar_combine(c1inv, c, 1.0, inv, 1.0, stream), "scalars");
@@ -405,14 +408,14 @@ int psd_project(float *H, int64_t K, void *ws, size_t ws_bytes, hipStream_t stre
             st.mode = TILE_LOWER;
             st.tri = 1;
             st.out_t = X;
-            GQ_HIP(gemm_tn_f64(st, stream), "sign step");
+            GQ_HIP(gemm_tn_f64_streamk(st, w.partials, stream), "sign step");
             continue;
         }
         GemmDesc y = gemm(X, K, X, K, K, K, K, w.Y, K);
         y.mode = TILE_LOWER;
         y.tri = 1;
         y.out_t = w.Y;
-        GQ_HIP(gemm_tn_f64(y, stream), "sign square");
+        GQ_HIP(gemm_tn_f64_streamk(y, w.partials, stream), "sign square");
         GemmDesc st = gemm(X, K, w.Y, K, K, K, K, Xn, K);
         st.cin = X;
         st.alpha = b;
@@ -420,7 +423,7 @@ int psd_project(float *H, int64_t K, void *ws, size_t ws_bytes, hipStream_t stre
         st.mode = TILE_LOWER;
         st.tri = 1;
         st.out_t = Xn;
-        GQ_HIP(gemm_tn_f64(st, stream), "sign step");
+        GQ_HIP(gemm_tn_f64_streamk(st, w.partials, stream), "sign step");
         double *t = X;
         X = Xn;
         Xn = t;
@@ -433,7 +436,7 @@ int psd_project(float *H, int64_t K, void *ws, size_t ws_bytes, hipStream_t stre
     fin.mode = TILE_LOWER;
     fin.tri = 1;
     fin.out_t = H;
-    GQ_HIP(gemm_tn_f64_out_f32(fin, stream), "projection");
+    GQ_HIP(gemm_tn_f64_out_f32_streamk(fin, w.partials, stream), "projection");
     unsigned st = 0;
     int rc = read_status(status, stream, &st);
     if (rc) return rc;

@@ -17,6 +17,8 @@
 // flight while the matrix cores work on stage k.
 //   fp32: v_mfma_f32_32x32x2f32, 2 x 2 blocks of 32 x 32 per wave.
 //   fp64: v_mfma_f64_16x16x4f64, 4 x 4 blocks of 16 x 16 per wave.
+#include <algorithm>
+
 #include "gq_internal.h"
 
 namespace gq {
@@ -127,157 +129,277 @@ __device__ inline void lower_tile(int64_t l, int64_t nt, int64_t &ti, int64_t &t
     }
 }
 
-// Two waves per SIMD: without the hint the fp64 instance keeps its 64-double
-// accumulator in AGPRs next to 238 VGPRs, one wave per SIMD, and every stage
-// stalls on its own loads; with it, 250 VGPRs and no AGPR copies.
-template <typename T, typename OutT>
-__global__ __launch_bounds__(NT, 2) void gemm_tn_kernel(GemmDesc d, int64_t tiles_m, int64_t tiles_n, int vecA,
-                                                    int vecB)
-{
+// Operand loading, the MFMA main loop over a range of k stages, and the
+// epilogue of one 128 x 128 tile, shared by the tile-per-workgroup kernel and
+// the stream-K kernels below.
+template <typename T> struct Tile {
     using MF = Mfma<T>;
-    constexpr int V = 16 / (int)sizeof(T);          // elements per 16-byte vector
-    constexpr int LDP = BM + V;                      // padded LDS row (elements)
-    constexpr int VPR = BM / V;                      // vectors per tile row
-    constexpr int NV = BK * VPR / NT;                // vectors per thread per operand
+    static constexpr int V = 16 / (int)sizeof(T);       // elements per 16-byte vector
+    static constexpr int LDP = BM + V;                   // padded LDS row (elements)
+    static constexpr int VPR = BM / V;                   // vectors per tile row
+    static constexpr int NV = BK * VPR / NT;             // vectors per thread per operand
     typedef T vec_t __attribute__((ext_vector_type(V)));
+    typedef typename MF::acc_t acc_t;
+    struct Smem {
+        T As[2][BK][LDP];
+        T Bs[2][BK][LDP];
+    };
 
-    __shared__ __attribute__((aligned(16))) T As[2][BK][LDP];
-    __shared__ __attribute__((aligned(16))) T Bs[2][BK][LDP];
-
-    int64_t ti, tj;
-    const int64_t l = xcd_logical(blockIdx.x, gridDim.x);
-    if (d.mode == TILE_RECT) {
-        rect_tile(l, tiles_m, tiles_n, ti, tj);
-    } else {
-        lower_tile(l, tiles_m, ti, tj);
-        if (d.mode == TILE_UPPER) { int64_t t = ti; ti = tj; tj = t; }
-    }
-    const int64_t i0 = ti * BM, j0 = tj * BN;
-    const bool full_i = vecA && (i0 + BM <= d.M);      // uniform across the workgroup
-    const bool full_j = vecB && (j0 + BN <= d.N);
-
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wr = wave >> 1, wc = wave & 1;
-    const T *A = (const T *)d.A;
-    const T *B = (const T *)d.B;
-
+    // acc = sum over k stages [s0, s1) of A[k][i0 + i] * B[k][j0 + j].
     // Interior stages load whole 16-byte vectors unconditionally; edge stages
-    // load element by element from clamped (always valid) addresses and zero
-    // the out-of-range elements with a select, so no lane ever branches.
-    vec_t ra[NV], rb[NV];
-    auto gload = [&](int64_t kb) {
-        const bool full_k = kb + BK <= d.Kd;
-        if (full_i && full_k) {
+    // load element by element from clamped (always valid) addresses and zero the
+    // out-of-range elements with a select, so no lane ever branches.
+    __device__ static void mainloop(const GemmDesc &d, int64_t i0, int64_t j0, int64_t s0, int64_t s1,
+                                    int vecA, int vecB, Smem &sm, acc_t (&acc)[MF::NB][MF::NB])
+    {
+        const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+        const int wr = wave >> 1, wc = wave & 1;
+        const T *A = (const T *)d.A;
+        const T *B = (const T *)d.B;
+        const bool full_i = vecA && (i0 + BM <= d.M);
+        const bool full_j = vecB && (j0 + BN <= d.N);
 #pragma unroll
-            for (int v = 0; v < NV; ++v) {
-                const int lin = tid + NT * v;
-                const int kr = lin / VPR, cc = (lin % VPR) * V;
-                ra[v] = *(const vec_t *)(A + (kb + kr) * d.lda + i0 + cc);
-            }
-        } else {
+        for (int bi = 0; bi < MF::NB; ++bi)
 #pragma unroll
-            for (int v = 0; v < NV; ++v) {
-                const int lin = tid + NT * v;
-                const int kr = lin / VPR, cc = (lin % VPR) * V;
-                const int64_t k = kb + kr;
+            for (int bj = 0; bj < MF::NB; ++bj)
 #pragma unroll
-                for (int e = 0; e < V; ++e) {
-                    const bool ok = k < d.Kd && i0 + cc + e < d.M;
-                    const T x = A[ok ? k * d.lda + i0 + cc + e : 0];
-                    ra[v][e] = ok ? x : (T)0;
+                for (int r = 0; r < MF::NACC; ++r) acc[bi][bj][r] = (T)0;
+        if (s1 <= s0) return;
+
+        vec_t ra[NV], rb[NV];
+        auto gload = [&](int64_t kb) {
+            const bool full_k = kb + BK <= d.Kd;
+            if (full_i && full_k) {
+#pragma unroll
+                for (int v = 0; v < NV; ++v) {
+                    const int lin = tid + NT * v;
+                    const int kr = lin / VPR, cc = (lin % VPR) * V;
+                    ra[v] = *(const vec_t *)(A + (kb + kr) * d.lda + i0 + cc);
+                }
+            } else {
+#pragma unroll
+                for (int v = 0; v < NV; ++v) {
+                    const int lin = tid + NT * v;
+                    const int kr = lin / VPR, cc = (lin % VPR) * V;
+                    const int64_t k = kb + kr;
+#pragma unroll
+                    for (int e = 0; e < V; ++e) {
+                        const bool ok = k < d.Kd && i0 + cc + e < d.M;
+                        const T x = A[ok ? k * d.lda + i0 + cc + e : 0];
+                        ra[v][e] = ok ? x : (T)0;
+                    }
                 }
             }
-        }
-        if (full_j && full_k) {
+            if (full_j && full_k) {
 #pragma unroll
-            for (int v = 0; v < NV; ++v) {
-                const int lin = tid + NT * v;
-                const int kr = lin / VPR, cc = (lin % VPR) * V;
-                rb[v] = *(const vec_t *)(B + (kb + kr) * d.ldb + j0 + cc);
-            }
-        } else {
+                for (int v = 0; v < NV; ++v) {
+                    const int lin = tid + NT * v;
+                    const int kr = lin / VPR, cc = (lin % VPR) * V;
+                    rb[v] = *(const vec_t *)(B + (kb + kr) * d.ldb + j0 + cc);
+                }
+            } else {
 #pragma unroll
-            for (int v = 0; v < NV; ++v) {
-                const int lin = tid + NT * v;
-                const int kr = lin / VPR, cc = (lin % VPR) * V;
-                const int64_t k = kb + kr;
+                for (int v = 0; v < NV; ++v) {
+                    const int lin = tid + NT * v;
+                    const int kr = lin / VPR, cc = (lin % VPR) * V;
+                    const int64_t k = kb + kr;
 #pragma unroll
-                for (int e = 0; e < V; ++e) {
-                    const bool ok = k < d.Kd && j0 + cc + e < d.N;
-                    const T x = B[ok ? k * d.ldb + j0 + cc + e : 0];
-                    rb[v][e] = ok ? x : (T)0;
+                    for (int e = 0; e < V; ++e) {
+                        const bool ok = k < d.Kd && j0 + cc + e < d.N;
+                        const T x = B[ok ? k * d.ldb + j0 + cc + e : 0];
+                        rb[v][e] = ok ? x : (T)0;
+                    }
                 }
             }
-        }
-    };
-    auto sstore = [&](int buf) {
+        };
+        auto sstore = [&](int buf) {
 #pragma unroll
-        for (int v = 0; v < NV; ++v) {
-            const int lin = tid + NT * v;
-            const int kr = lin / VPR;
-            const int cc = (lin % VPR) * V;
-            *(vec_t *)&As[buf][kr][cc] = ra[v];
-            *(vec_t *)&Bs[buf][kr][cc] = rb[v];
-        }
-    };
+            for (int v = 0; v < NV; ++v) {
+                const int lin = tid + NT * v;
+                const int kr = lin / VPR, cc = (lin % VPR) * V;
+                *(vec_t *)&sm.As[buf][kr][cc] = ra[v];
+                *(vec_t *)&sm.Bs[buf][kr][cc] = rb[v];
+            }
+        };
 
-    typename MF::acc_t acc[MF::NB][MF::NB];
-#pragma unroll
-    for (int bi = 0; bi < MF::NB; ++bi)
-#pragma unroll
-        for (int bj = 0; bj < MF::NB; ++bj)
-#pragma unroll
-            for (int r = 0; r < MF::NACC; ++r) acc[bi][bj][r] = (T)0;
-
-    const int64_t nk = (d.Kd + BK - 1) / BK;
-    if (nk > 0) {
-        gload(0);
+        gload(s0 * BK);
         sstore(0);
         __syncthreads();
-        for (int64_t kt = 0; kt < nk; ++kt) {
-            const int buf = (int)(kt & 1);
-            if (kt + 1 < nk) gload((kt + 1) * BK);
+        for (int64_t kt = s0; kt < s1; ++kt) {
+            const int buf = (int)((kt - s0) & 1);
+            if (kt + 1 < s1) gload((kt + 1) * BK);
             const int m = lane % MF::LPK;
 #pragma unroll
             for (int kk = 0; kk < BK; kk += MF::KSTEP) {
                 const int kr = kk + lane / MF::LPK;
                 T a[MF::NB], b[MF::NB];
 #pragma unroll
-                for (int bi = 0; bi < MF::NB; ++bi) a[bi] = As[buf][kr][wr * 64 + bi * MF::BLK + m];
+                for (int bi = 0; bi < MF::NB; ++bi) a[bi] = sm.As[buf][kr][wr * 64 + bi * MF::BLK + m];
 #pragma unroll
-                for (int bj = 0; bj < MF::NB; ++bj) b[bj] = Bs[buf][kr][wc * 64 + bj * MF::BLK + m];
+                for (int bj = 0; bj < MF::NB; ++bj) b[bj] = sm.Bs[buf][kr][wc * 64 + bj * MF::BLK + m];
 #pragma unroll
                 for (int bi = 0; bi < MF::NB; ++bi)
 #pragma unroll
                     for (int bj = 0; bj < MF::NB; ++bj) acc[bi][bj] = MF::mma(a[bi], b[bj], acc[bi][bj]);
             }
-            if (kt + 1 < nk) sstore(buf ^ 1);
+            if (kt + 1 < s1) sstore(buf ^ 1);
             __syncthreads();
         }
     }
 
-    double alpha = d.alpha, beta = d.beta;
-    if (d.alpha_dev) alpha *= ipow(*d.alpha_dev, d.alpha_pow);
-    if (d.beta_dev) beta *= ipow(*d.beta_dev, d.beta_pow);
-    OutT *out = (OutT *)d.out;
-    OutT *out_t = (OutT *)d.out_t;
-    const T *cin = (const T *)d.cin;
+    template <typename OutT>
+    __device__ static void epilogue(const GemmDesc &d, int64_t i0, int64_t j0, const acc_t (&acc)[MF::NB][MF::NB])
+    {
+        const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+        const int wr = wave >> 1, wc = wave & 1;
+        double alpha = d.alpha, beta = d.beta;
+        if (d.alpha_dev) alpha *= ipow(*d.alpha_dev, d.alpha_pow);
+        if (d.beta_dev) beta *= ipow(*d.beta_dev, d.beta_pow);
+        OutT *out = (OutT *)d.out;
+        OutT *out_t = (OutT *)d.out_t;
+        const T *cin = (const T *)d.cin;
 #pragma unroll
-    for (int bi = 0; bi < MF::NB; ++bi)
+        for (int bi = 0; bi < MF::NB; ++bi)
 #pragma unroll
-        for (int bj = 0; bj < MF::NB; ++bj)
+            for (int bj = 0; bj < MF::NB; ++bj)
 #pragma unroll
-            for (int r = 0; r < MF::NACC; ++r) {
-                const int64_t gi = i0 + wr * 64 + bi * MF::BLK + MF::row(lane, r);
-                const int64_t gj = j0 + wc * 64 + bj * MF::BLK + MF::col(lane, r);
-                if (gi >= d.M || gj >= d.N) continue;
-                if (d.tri == 1 && gi < gj) continue;
-                if (d.tri == 2 && gi > gj) continue;
-                double v = alpha * (double)acc[bi][bj][r];
-                if (beta != 0.0) v += beta * (double)cin[gi * d.ldc + gj];
-                out[gi * d.ldo + gj] = (OutT)v;
-                if (out_t) out_t[gj * d.ldo + gi] = (OutT)v;
+                for (int r = 0; r < MF::NACC; ++r) {
+                    const int64_t gi = i0 + wr * 64 + bi * MF::BLK + MF::row(lane, r);
+                    const int64_t gj = j0 + wc * 64 + bj * MF::BLK + MF::col(lane, r);
+                    if (gi >= d.M || gj >= d.N) continue;
+                    if (d.tri == 1 && gi < gj) continue;
+                    if (d.tri == 2 && gi > gj) continue;
+                    double v = alpha * (double)acc[bi][bj][r];
+                    if (beta != 0.0) v += beta * (double)cin[gi * d.ldc + gj];
+                    out[gi * d.ldo + gj] = (OutT)v;
+                    if (out_t) out_t[gj * d.ldo + gi] = (OutT)v;
+                }
+    }
+};
+
+__device__ inline void tile_coords(const GemmDesc &d, int64_t l, int64_t tiles_m, int64_t tiles_n,
+                                   int64_t &i0, int64_t &j0)
+{
+    int64_t ti, tj;
+    if (d.mode == TILE_RECT) {
+        rect_tile(l, tiles_m, tiles_n, ti, tj);
+    } else {
+        lower_tile(l, tiles_m, ti, tj);
+        if (d.mode == TILE_UPPER) { int64_t t = ti; ti = tj; tj = t; }
+    }
+    i0 = ti * BM;
+    j0 = tj * BN;
+}
+
+// Two waves per SIMD: without the hint the fp64 instance keeps its 64-double
+// accumulator in AGPRs next to 238 VGPRs, one wave per SIMD, and every stage
+// stalls on its own loads; with it, 250 VGPRs and no AGPR copies.
+template <typename T, typename OutT>
+__global__ __launch_bounds__(NT, 2) void gemm_tn_kernel(GemmDesc d, int64_t tiles_m, int64_t tiles_n, int vecA,
+                                                       int vecB)
+{
+    using TL = Tile<T>;
+    __shared__ __attribute__((aligned(16))) typename TL::Smem sm;
+    int64_t i0, j0;
+    tile_coords(d, xcd_logical(blockIdx.x, gridDim.x), tiles_m, tiles_n, i0, j0);
+    typename TL::acc_t acc[TL::MF::NB][TL::MF::NB];
+    TL::mainloop(d, i0, j0, 0, (d.Kd + BK - 1) / BK, vecA, vecB, sm, acc);
+    TL::template epilogue<OutT>(d, i0, j0, acc);
+}
+
+// Stream-K with a data-parallel head: a persistent grid of exactly the
+// resident workgroups.  The first dp_tiles tiles (whole waves) go one per
+// worker per round in the grouped order, so the workgroups resident on one XCD
+// share panels through its L2 as in the plain kernel.  The (tile, k-stage)
+// iteration space of the remaining tiles (one to two waves' worth) is cut into
+// equal contiguous shares, one per worker, so the last waves keep every CU
+// equally busy whatever the tile count.  A worker finishes the tiles its share
+// covers entirely; for a tile that a share boundary cuts (each share spans at
+// least one tile, so a tile has at most one cut), the two sides store their
+// partial accumulators in the slot of that boundary and the fix-up kernel adds
+// them, in a fixed order, before the epilogue.
+struct StreamK {
+    int64_t tiles_m, tiles_n, ntiles, nstage, workers, dp_tiles;
+    // first iteration of worker w's share; w = workers gives the end
+    __device__ int64_t share_begin(int64_t w) const
+    {
+        return dp_tiles * nstage + w * ((ntiles - dp_tiles) * nstage) / workers;
+    }
+};
+
+template <typename T, typename OutT>
+__global__ __launch_bounds__(NT, 2) void gemm_tn_streamk_kernel(GemmDesc d, StreamK k, int vecA, int vecB,
+                                                               T *partials)
+{
+    using TL = Tile<T>;
+    __shared__ __attribute__((aligned(16))) typename TL::Smem sm;
+    const int64_t w = xcd_logical(blockIdx.x, gridDim.x);
+    typename TL::acc_t acc[TL::MF::NB][TL::MF::NB];
+    int64_t dp = w;                                     // next data-parallel tile
+    int64_t it = k.share_begin(w);                      // next stream-K iteration
+    const int64_t end = k.share_begin(w + 1);
+    // one loop for both phases keeps a single copy of the main loop and epilogue
+    for (;;) {
+        int64_t tile, s0, s1;
+        if (dp < k.dp_tiles) {
+            tile = dp;
+            s0 = 0;
+            s1 = k.nstage;
+            dp += k.workers;
+        } else if (it < end) {
+            tile = it / k.nstage;
+            s0 = it - tile * k.nstage;
+            s1 = (end - tile * k.nstage) < k.nstage ? (end - tile * k.nstage) : k.nstage;
+            it = tile * k.nstage + s1;
+        } else {
+            break;
+        }
+        int64_t i0, j0;
+        tile_coords(d, tile, k.tiles_m, k.tiles_n, i0, j0);
+        TL::mainloop(d, i0, j0, s0, s1, vecA, vecB, sm, acc);
+        if (s0 == 0 && s1 == k.nstage) {
+            TL::template epilogue<OutT>(d, i0, j0, acc);
+        } else {
+            // boundary b cuts this tile: the head part ends at b (this worker is
+            // b - 1), the tail part starts at b (this worker is b)
+            const bool head = (s0 == 0);
+            const int64_t b = head ? w + 1 : w;
+            T *slot = partials + ((b - 1) * 2 + (head ? 0 : 1)) * (int64_t)(BM * BN);
+            const int tid = threadIdx.x;
+#pragma unroll
+            for (int bi = 0; bi < TL::MF::NB; ++bi)
+#pragma unroll
+                for (int bj = 0; bj < TL::MF::NB; ++bj)
+#pragma unroll
+                    for (int r = 0; r < TL::MF::NACC; ++r)
+                        slot[((bi * TL::MF::NB + bj) * TL::MF::NACC + r) * NT + tid] = acc[bi][bj][r];
+        }
+    }
+}
+
+template <typename T, typename OutT>
+__global__ __launch_bounds__(NT) void gemm_tn_fixup_kernel(GemmDesc d, StreamK k, const T *partials)
+{
+    using TL = Tile<T>;
+    const int64_t b = blockIdx.x + 1;                   // boundary between workers b-1 and b
+    const int64_t cut = k.share_begin(b);
+    if (cut % k.nstage == 0) return;                    // falls between tiles
+    int64_t i0, j0;
+    tile_coords(d, cut / k.nstage, k.tiles_m, k.tiles_n, i0, j0);
+    const T *h = partials + ((b - 1) * 2 + 0) * (int64_t)(BM * BN);
+    const T *t = partials + ((b - 1) * 2 + 1) * (int64_t)(BM * BN);
+    const int tid = threadIdx.x;
+    typename TL::acc_t acc[TL::MF::NB][TL::MF::NB];
+#pragma unroll
+    for (int bi = 0; bi < TL::MF::NB; ++bi)
+#pragma unroll
+        for (int bj = 0; bj < TL::MF::NB; ++bj)
+#pragma unroll
+            for (int r = 0; r < TL::MF::NACC; ++r) {
+                const int64_t o = ((bi * TL::MF::NB + bj) * TL::MF::NACC + r) * NT + tid;
+                acc[bi][bj][r] = h[o] + t[o];
             }
+    TL::template epilogue<OutT>(d, i0, j0, acc);
 }
 
 template <typename T, typename OutT>
@@ -300,10 +422,55 @@ hipError_t launch(const GemmDesc &d, hipStream_t s)
     return hipGetLastError();
 }
 
+int resident_workers()
+{
+    static int w = 0;
+    if (w == 0) {
+        int dev = 0, cus = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+            cus = 256;
+        w = 2 * cus;                                    // two workgroups per CU (occupancy hint)
+    }
+    return w;
+}
+
+template <typename T, typename OutT>
+hipError_t launch_streamk(const GemmDesc &d, void *partials, hipStream_t s)
+{
+    if (d.M <= 0 || d.N <= 0) return hipSuccess;
+    constexpr int V = 16 / (int)sizeof(T);
+    if (d.mode != TILE_RECT && d.M != d.N) return hipErrorInvalidValue;
+    StreamK k;
+    k.tiles_m = (d.M + BM - 1) / BM;
+    k.tiles_n = (d.N + BN - 1) / BN;
+    k.ntiles = (d.mode == TILE_RECT) ? k.tiles_m * k.tiles_n : k.tiles_m * (k.tiles_m + 1) / 2;
+    k.nstage = (d.Kd + BK - 1) / BK;
+    k.workers = std::min<int64_t>(resident_workers(), kStreamKMaxWorkers);
+    if (!partials || k.ntiles < k.workers || k.nstage < 1) return launch<T, OutT>(d, s);
+    // all but the last one to two waves run data-parallel
+    k.dp_tiles = (k.ntiles / k.workers - 1) * k.workers;
+    const int vecA = (d.lda % V == 0) && (((uintptr_t)d.A & 15) == 0);
+    const int vecB = (d.ldb % V == 0) && (((uintptr_t)d.B & 15) == 0);
+    hipLaunchKernelGGL((gemm_tn_streamk_kernel<T, OutT>), dim3((unsigned)k.workers), dim3(NT), 0, s, d, k, vecA,
+                       vecB, (T *)partials);
+    hipLaunchKernelGGL((gemm_tn_fixup_kernel<T, OutT>), dim3((unsigned)(k.workers - 1)), dim3(NT), 0, s, d, k,
+                       (const T *)partials);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t gemm_tn_f32(const GemmDesc &d, hipStream_t s) { return launch<float, float>(d, s); }
 hipError_t gemm_tn_f64(const GemmDesc &d, hipStream_t s) { return launch<double, double>(d, s); }
 hipError_t gemm_tn_f64_out_f32(const GemmDesc &d, hipStream_t s) { return launch<double, float>(d, s); }
+hipError_t gemm_tn_f64_streamk(const GemmDesc &d, void *partials, hipStream_t s)
+{
+    return launch_streamk<double, double>(d, partials, s);
+}
+hipError_t gemm_tn_f64_out_f32_streamk(const GemmDesc &d, void *partials, hipStream_t s)
+{
+    return launch_streamk<double, float>(d, partials, s);
+}
 
 }  // namespace gq
