@@ -33,6 +33,32 @@ PEAK_TFLOPS = {"bf16": 2516.6, "f32": 157.3, "f64": 78.6}
 PEAK_HBM_GBS = 8000.0
 SWEEP_BLOCK = 128          # lazy-batch width of gptq_sweep (include/gq.h)
 
+# HBM bytes per launch of the dominant kernel, from two rocprofv3 --pmc passes
+# (FETCH_SIZE, WRITE_SIZE) scaled by what the same counters read for the copy
+# kernel of known size in the same run (profiles/gemm_tn_streamk_attn5120_traffic.md).
+# Valid only for the kernel sources they were taken on: any change to those
+# files makes the figure stale and it is reported as null.
+TRAFFIC = {
+    "attn5120": {"fetch_bytes": 3277930.2 * 1.99969 * 1024, "write_bytes": 271987.1 * 1024,
+                 "sources_sha256_16": "d77d081e206798fd"},
+}
+TRAFFIC_SOURCES = ("post_weight_quantization_accumulate_amd/csrc/gemm_tn.hip",
+                   "post_weight_quantization_accumulate_amd/csrc/gq_internal.h")
+
+
+def traffic_for(workload):
+    import hashlib
+    t = TRAFFIC.get(workload)
+    if t is None:
+        return None, None
+    h = hashlib.sha256()
+    for f in TRAFFIC_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    if h.hexdigest()[:16] != t["sources_sha256_16"]:
+        return None, "kernel sources changed since the counters were taken"
+    return t["fetch_bytes"] + t["write_bytes"], {"fetch_bytes": t["fetch_bytes"], "write_bytes": t["write_bytes"]}
+
 
 def parse():
     p = argparse.ArgumentParser()
@@ -51,9 +77,9 @@ def cpu_baseline(wl, X, W):
     N*K^2, qerr N*K)."""
     import numpy as np
     import oracle
-    Ks = min(wl.K, 2560)
+    Ks = min(wl.K, 3072)
     Ts = wl.T
-    Ns = min(wl.N[0], 2560)
+    Ns = min(wl.N[0], 3072)
     Xs = X[:Ts, :Ks].float().cpu().numpy()
     Ws = W[:Ns, :Ks].cpu().numpy()
     G = wl.group
@@ -155,6 +181,7 @@ def main():
     upd_flops = sum(2 * N * min(SWEEP_BLOCK, K - b0) * (K - b0 - min(SWEEP_BLOCK, K - b0))
                     for b0 in range(0, K, SWEEP_BLOCK))
     gptq_ms = stage_ms["factor"] + stage_ms["sweep"]
+    traffic, traffic_detail = traffic_for(wl.name)
 
     out = {
         "metric": METRIC,
@@ -182,12 +209,17 @@ def main():
         "qerr": qerr[0],
         "roofline": {
             "bound": "mfma",
-            "kernel": "gemm_tn_kernel<double,double> (sign-iteration symmetric product)",
+            "kernel": ("gemm_tn_streamk_kernel<double,double> (sign-iteration symmetric product); "
+                       "launch time = psd_project time / products, so it also carries the norm and "
+                       "symmetrisation kernels"),
             "achieved": prod_tflops,
             "peak": PEAK_TFLOPS["f64"],
             "unit": "TFLOP/s",
             "frac": prod_tflops / PEAK_TFLOPS["f64"],
-            "traffic": None,
+            "traffic": traffic,
+            "traffic_detail": traffic_detail,
+            "algorithmic_bytes_per_launch": {"read_AB": 2 * K * K * 8, "read_cin_step_products": K * K * 8,
+                                             "write_lower_and_mirror": K * K * 8},
             "per_launch_flops": prod_flops,
             "avg_launch_ms": prod_ms,
             "launches_per_step": n_prod,

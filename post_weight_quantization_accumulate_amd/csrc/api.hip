@@ -122,6 +122,7 @@ struct PsdWs {
     Scalars sc;
     double *H64, *X, *Y, *Xn;
     double *partials;          // stream-K split-tile accumulators (large K only)
+    unsigned *flags;           // stream-K boundary counters
 };
 
 PsdWs carve_psd(Carver &c, int64_t K)
@@ -133,8 +134,9 @@ PsdWs carve_psd(Carver &c, int64_t K)
     w.X = c.take<double>(n);
     w.Y = c.take<double>(n);
     w.Xn = c.take<double>(n);
-    w.partials = streamk_lower_worthwhile(K) ? c.take<double>(streamk_partials_bytes(sizeof(double)) / sizeof(double))
-                                             : nullptr;
+    const bool sk = streamk_lower_worthwhile(K);
+    w.partials = sk ? c.take<double>(streamk_partials_bytes(sizeof(double)) / sizeof(double)) : nullptr;
+    w.flags = sk ? c.take<unsigned>(kStreamKMaxWorkers) : nullptr;
     return w;
 }
 
@@ -374,6 +376,7 @@ int psd_project(float *H, int64_t K, void *ws, size_t ws_bytes, hipStream_t stre
     double *fro = w.sc.d + 0, *inv = w.sc.d + 1, *yfro = w.sc.d + 2, *c = w.sc.d + 3;
     double *c1inv = w.sc.d + 4, *c3inv = w.sc.d + 5;
     GQ_HIP(launch_fill_u32(status, 4, 0u, stream), "fill");
+    if (w.flags) GQ_HIP(launch_fill_u32(w.flags, kStreamKMaxWorkers, 0u, stream), "fill");
     GQ_HIP(launch_sym_lower_to_f64(w.H64, H, K, status, stream), "symmetrise");
     GQ_HIP(launch_frobenius(fro, w.H64, n, w.sc.partials, stream), "norm");
     GQ_HIP(launch_scalar_combine(inv, fro, -1.0, nullptr, 0.0, stream), "inverse norm");
@@ -386,7 +389,7 @@ int psd_project(float *H, int64_t K, void *ws, size_t ws_bytes, hipStream_t stre
     sq.mode = TILE_LOWER;
     sq.tri = 1;
     sq.out_t = w.Y;
-    GQ_HIP(gemm_tn_f64_streamk(sq, w.partials, stream), "sign square");
+    GQ_HIP(gemm_tn_f64_streamk(sq, w.partials, w.flags, stream), "sign square");
     GQ_HIP(launch_frobenius(yfro, w.Y, n, w.sc.partials, stream), "norm");
     GQ_HIP(launch_scalar_combine(c, yfro, -0.5, nullptr, 0.0, stream), "bound");
     GQ_HIP(launch_scalar_combine(c1inv, c, 1.0, inv, 1.0, stream), "scalars");
@@ -408,14 +411,14 @@ int psd_project(float *H, int64_t K, void *ws, size_t ws_bytes, hipStream_t stre
             st.mode = TILE_LOWER;
             st.tri = 1;
             st.out_t = X;
-            GQ_HIP(gemm_tn_f64_streamk(st, w.partials, stream), "sign step");
+            GQ_HIP(gemm_tn_f64_streamk(st, w.partials, w.flags, stream), "sign step");
             continue;
         }
         GemmDesc y = gemm(X, K, X, K, K, K, K, w.Y, K);
         y.mode = TILE_LOWER;
         y.tri = 1;
         y.out_t = w.Y;
-        GQ_HIP(gemm_tn_f64_streamk(y, w.partials, stream), "sign square");
+        GQ_HIP(gemm_tn_f64_streamk(y, w.partials, w.flags, stream), "sign square");
         GemmDesc st = gemm(X, K, w.Y, K, K, K, K, Xn, K);
         st.cin = X;
         st.alpha = b;
@@ -423,7 +426,7 @@ int psd_project(float *H, int64_t K, void *ws, size_t ws_bytes, hipStream_t stre
         st.mode = TILE_LOWER;
         st.tri = 1;
         st.out_t = Xn;
-        GQ_HIP(gemm_tn_f64_streamk(st, w.partials, stream), "sign step");
+        GQ_HIP(gemm_tn_f64_streamk(st, w.partials, w.flags, stream), "sign step");
         double *t = X;
         X = Xn;
         Xn = t;
@@ -436,7 +439,7 @@ int psd_project(float *H, int64_t K, void *ws, size_t ws_bytes, hipStream_t stre
     fin.mode = TILE_LOWER;
     fin.tri = 1;
     fin.out_t = H;
-    GQ_HIP(gemm_tn_f64_out_f32_streamk(fin, w.partials, stream), "projection");
+    GQ_HIP(gemm_tn_f64_out_f32_streamk(fin, w.partials, w.flags, stream), "projection");
     unsigned st = 0;
     int rc = read_status(status, stream, &st);
     if (rc) return rc;

@@ -314,10 +314,14 @@ __global__ __launch_bounds__(NT, 2) void gemm_tn_kernel(GemmDesc d, int64_t tile
 // iteration space of the remaining tiles (one to two waves' worth) is cut into
 // equal contiguous shares, one per worker, so the last waves keep every CU
 // equally busy whatever the tile count.  A worker finishes the tiles its share
-// covers entirely; for a tile that a share boundary cuts (each share spans at
-// least one tile, so a tile has at most one cut), the two sides store their
-// partial accumulators in the slot of that boundary and the fix-up kernel adds
-// them, in a fixed order, before the epilogue.
+// covers entirely.  A tile that a share boundary cuts (each share spans at
+// least one tile, so a tile has at most one cut) has a head part, which ends
+// the share of the worker before the boundary, and a tail part, which begins
+// the share of the worker after it.  Whichever side finishes second adds the
+// other's partial accumulator to its own and runs the epilogue; a counter per
+// boundary decides which side that is, so no workgroup ever waits for another.
+// The sum is head + tail whichever side forms it (floating-point addition is
+// commutative), so results do not depend on timing.
 struct StreamK {
     int64_t tiles_m, tiles_n, ntiles, nstage, workers, dp_tiles;
     // first iteration of worker w's share; w = workers gives the end
@@ -329,7 +333,7 @@ struct StreamK {
 
 template <typename T, typename OutT>
 __global__ __launch_bounds__(NT, 2) void gemm_tn_streamk_kernel(GemmDesc d, StreamK k, int vecA, int vecB,
-                                                               T *partials)
+                                                               T *partials, unsigned *flags)
 {
     using TL = Tile<T>;
     __shared__ __attribute__((aligned(16))) typename TL::Smem sm;
@@ -357,49 +361,57 @@ __global__ __launch_bounds__(NT, 2) void gemm_tn_streamk_kernel(GemmDesc d, Stre
         int64_t i0, j0;
         tile_coords(d, tile, k.tiles_m, k.tiles_n, i0, j0);
         TL::mainloop(d, i0, j0, s0, s1, vecA, vecB, sm, acc);
-        if (s0 == 0 && s1 == k.nstage) {
-            TL::template epilogue<OutT>(d, i0, j0, acc);
-        } else {
+        bool epi = (s0 == 0 && s1 == k.nstage);
+        unsigned *flag = nullptr;
+        if (!epi) {
             // boundary b cuts this tile: the head part ends at b (this worker is
             // b - 1), the tail part starts at b (this worker is b)
             const bool head = (s0 == 0);
             const int64_t b = head ? w + 1 : w;
-            T *slot = partials + ((b - 1) * 2 + (head ? 0 : 1)) * (int64_t)(BM * BN);
+            flag = flags + (b - 1);
+            T *mine = partials + ((b - 1) * 2 + (head ? 0 : 1)) * (int64_t)(BM * BN);
+            const T *other = partials + ((b - 1) * 2 + (head ? 1 : 0)) * (int64_t)(BM * BN);
             const int tid = threadIdx.x;
+            __shared__ unsigned s_prev;
+            // The head part usually finishes last (it ends a share); if the tail
+            // has already posted, skip storing the head part.
+            if (tid == 0)
+                s_prev = head ? __hip_atomic_load(flag, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) : 0u;
+            __syncthreads();
+            epi = (s_prev == 1u);
+            __syncthreads();
+            if (!epi) {
 #pragma unroll
-            for (int bi = 0; bi < TL::MF::NB; ++bi)
+                for (int bi = 0; bi < TL::MF::NB; ++bi)
 #pragma unroll
-                for (int bj = 0; bj < TL::MF::NB; ++bj)
+                    for (int bj = 0; bj < TL::MF::NB; ++bj)
 #pragma unroll
-                    for (int r = 0; r < TL::MF::NACC; ++r)
-                        slot[((bi * TL::MF::NB + bj) * TL::MF::NACC + r) * NT + tid] = acc[bi][bj][r];
+                        for (int r = 0; r < TL::MF::NACC; ++r)
+                            mine[((bi * TL::MF::NB + bj) * TL::MF::NACC + r) * NT + tid] = acc[bi][bj][r];
+                __threadfence();                        // publish the partial device-wide
+                __syncthreads();
+                if (tid == 0) s_prev = atomicAdd(flag, 1u);
+                __syncthreads();
+                epi = (s_prev == 1u);
+                __syncthreads();
+            }
+            if (epi) {
+                __threadfence();                        // see the other side's partial
+#pragma unroll
+                for (int bi = 0; bi < TL::MF::NB; ++bi)
+#pragma unroll
+                    for (int bj = 0; bj < TL::MF::NB; ++bj)
+#pragma unroll
+                        for (int r = 0; r < TL::MF::NACC; ++r)
+                            acc[bi][bj][r] += other[((bi * TL::MF::NB + bj) * TL::MF::NACC + r) * NT + tid];
+            }
+        }
+        if (epi) {
+            TL::template epilogue<OutT>(d, i0, j0, acc);
+            // the side that finished a split tile re-arms its counter
+            if (flag && threadIdx.x == 0) __hip_atomic_store(flag, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
-}
-
-template <typename T, typename OutT>
-__global__ __launch_bounds__(NT) void gemm_tn_fixup_kernel(GemmDesc d, StreamK k, const T *partials)
-{
-    using TL = Tile<T>;
-    const int64_t b = blockIdx.x + 1;                   // boundary between workers b-1 and b
-    const int64_t cut = k.share_begin(b);
-    if (cut % k.nstage == 0) return;                    // falls between tiles
-    int64_t i0, j0;
-    tile_coords(d, cut / k.nstage, k.tiles_m, k.tiles_n, i0, j0);
-    const T *h = partials + ((b - 1) * 2 + 0) * (int64_t)(BM * BN);
-    const T *t = partials + ((b - 1) * 2 + 1) * (int64_t)(BM * BN);
-    const int tid = threadIdx.x;
-    typename TL::acc_t acc[TL::MF::NB][TL::MF::NB];
-#pragma unroll
-    for (int bi = 0; bi < TL::MF::NB; ++bi)
-#pragma unroll
-        for (int bj = 0; bj < TL::MF::NB; ++bj)
-#pragma unroll
-            for (int r = 0; r < TL::MF::NACC; ++r) {
-                const int64_t o = ((bi * TL::MF::NB + bj) * TL::MF::NACC + r) * NT + tid;
-                acc[bi][bj][r] = h[o] + t[o];
-            }
-    TL::template epilogue<OutT>(d, i0, j0, acc);
 }
 
 template <typename T, typename OutT>
@@ -436,7 +448,7 @@ int resident_workers()
 }
 
 template <typename T, typename OutT>
-hipError_t launch_streamk(const GemmDesc &d, void *partials, hipStream_t s)
+hipError_t launch_streamk(const GemmDesc &d, void *partials, unsigned *flags, hipStream_t s)
 {
     if (d.M <= 0 || d.N <= 0) return hipSuccess;
     constexpr int V = 16 / (int)sizeof(T);
@@ -447,15 +459,13 @@ hipError_t launch_streamk(const GemmDesc &d, void *partials, hipStream_t s)
     k.ntiles = (d.mode == TILE_RECT) ? k.tiles_m * k.tiles_n : k.tiles_m * (k.tiles_m + 1) / 2;
     k.nstage = (d.Kd + BK - 1) / BK;
     k.workers = std::min<int64_t>(resident_workers(), kStreamKMaxWorkers);
-    if (!partials || k.ntiles < k.workers || k.nstage < 1) return launch<T, OutT>(d, s);
+    if (!partials || !flags || k.ntiles < k.workers || k.nstage < 1) return launch<T, OutT>(d, s);
     // all but the last one to two waves run data-parallel
     k.dp_tiles = (k.ntiles / k.workers - 1) * k.workers;
     const int vecA = (d.lda % V == 0) && (((uintptr_t)d.A & 15) == 0);
     const int vecB = (d.ldb % V == 0) && (((uintptr_t)d.B & 15) == 0);
     hipLaunchKernelGGL((gemm_tn_streamk_kernel<T, OutT>), dim3((unsigned)k.workers), dim3(NT), 0, s, d, k, vecA,
-                       vecB, (T *)partials);
-    hipLaunchKernelGGL((gemm_tn_fixup_kernel<T, OutT>), dim3((unsigned)(k.workers - 1)), dim3(NT), 0, s, d, k,
-                       (const T *)partials);
+                       vecB, (T *)partials, flags);
     return hipGetLastError();
 }
 
@@ -464,13 +474,13 @@ hipError_t launch_streamk(const GemmDesc &d, void *partials, hipStream_t s)
 hipError_t gemm_tn_f32(const GemmDesc &d, hipStream_t s) { return launch<float, float>(d, s); }
 hipError_t gemm_tn_f64(const GemmDesc &d, hipStream_t s) { return launch<double, double>(d, s); }
 hipError_t gemm_tn_f64_out_f32(const GemmDesc &d, hipStream_t s) { return launch<double, float>(d, s); }
-hipError_t gemm_tn_f64_streamk(const GemmDesc &d, void *partials, hipStream_t s)
+hipError_t gemm_tn_f64_streamk(const GemmDesc &d, void *partials, unsigned *flags, hipStream_t s)
 {
-    return launch_streamk<double, double>(d, partials, s);
+    return launch_streamk<double, double>(d, partials, flags, s);
 }
-hipError_t gemm_tn_f64_out_f32_streamk(const GemmDesc &d, void *partials, hipStream_t s)
+hipError_t gemm_tn_f64_out_f32_streamk(const GemmDesc &d, void *partials, unsigned *flags, hipStream_t s)
 {
-    return launch_streamk<double, float>(d, partials, s);
+    return launch_streamk<double, float>(d, partials, flags, s);
 }
 
 }  // namespace gq

@@ -51,8 +51,9 @@ hipError_t gemm_tn_f64_out_f32(const GemmDesc &d, hipStream_t s);
 // Stream-K variants for products with at least as many tiles as resident
 // workgroups (at most kStreamKMaxWorkers of them); with fewer tiles, or with no
 // partials buffer, they run one tile per workgroup.  partials holds
-// streamk_partials_bytes(sizeof element) bytes of scratch.  out must not alias
-// A, B or cin.
+// streamk_partials_bytes(sizeof element) bytes of scratch and flags
+// kStreamKMaxWorkers counters, which must be zero before the first call and
+// are left zero by every call.  out must not alias A, B or cin.
 constexpr int64_t kStreamKMaxWorkers = 512;
 constexpr size_t streamk_partials_bytes(size_t elem) { return (size_t)2 * kStreamKMaxWorkers * 128 * 128 * elem; }
 // True when a lower-triangle product of order K has enough tiles for stream-K.
@@ -60,8 +61,8 @@ constexpr bool streamk_lower_worthwhile(int64_t K)
 {
     return ((K + 127) / 128) * ((K + 127) / 128 + 1) / 2 >= kStreamKMaxWorkers;
 }
-hipError_t gemm_tn_f64_streamk(const GemmDesc &d, void *partials, hipStream_t s);
-hipError_t gemm_tn_f64_out_f32_streamk(const GemmDesc &d, void *partials, hipStream_t s);
+hipError_t gemm_tn_f64_streamk(const GemmDesc &d, void *partials, unsigned *flags, hipStream_t s);
+hipError_t gemm_tn_f64_out_f32_streamk(const GemmDesc &d, void *partials, unsigned *flags, hipStream_t s);
 
 // bf16 Gram: H_lower += X^T X, X T x K bf16 row-major.
 hipError_t launch_gram_bf16(float *H, const uint16_t *X, int64_t T, int64_t K, hipStream_t s);

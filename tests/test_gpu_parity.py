@@ -142,6 +142,33 @@ def test_psd_random_indefinite(gq, orc, K):
     assert _relF(P, P64) < 1e-5
 
 
+def test_psd_stream_k_path_ragged(gq):
+    """K=4100: 33 tile rows (the last one 4 wide), 561 lower tiles, more than
+    the resident workgroups, so the products run the stream-K kernel with split
+    tiles.  The oracle's eigendecomposition takes minutes at this size, so the
+    input has a known spectrum instead: H = Q diag(lam) Q^T with Q orthogonal
+    (Householder QR of a Gaussian matrix, LAPACK through numpy) and lam spread
+    over [-1, 1], whose projection is Q diag(max(lam, 0)) Q^T exactly.
+    Rounding H to fp32 moves the projection by at most ||H32 - H||_F (projection
+    onto a convex set is non-expansive), about 6e-8 of ||P||_F here.  A second
+    call on the same input must give the same bits (split tiles are summed in a
+    fixed order whichever side finishes last)."""
+    K = 4100
+    rng = np.random.default_rng(4100)
+    Q, _ = np.linalg.qr(rng.standard_normal((K, K)))
+    lam = np.linspace(-1.0, 1.0, K)
+    rng.shuffle(lam)
+    H64 = (Q * lam) @ Q.T
+    H64 = (H64 + H64.T) / 2
+    P_exact = (Q * np.maximum(lam, 0.0)) @ Q.T
+    H = H64.astype(np.float32)
+    assert np.linalg.norm(H - H64) / np.linalg.norm(P_exact) < 1e-7
+    P = _gpu_psd(gq, H)
+    assert np.array_equal(P, P.T)
+    assert _relF(P, P_exact) < 1e-5
+    assert np.array_equal(_gpu_psd(gq, H).view(np.uint32), P.view(np.uint32))
+
+
 def test_psd_stored_hessian_full_size(gq, orc):
     """The stored-Hessian workload at its full size (K=1024): Gram -> bf16 tril
     storage -> unpack -> projection, both sides from the same stored matrix."""
