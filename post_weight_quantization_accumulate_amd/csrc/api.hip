@@ -168,7 +168,7 @@ SweepWs carve_sweep(Carver &c, int64_t N, int64_t K)
     SweepWs w;
     w.sc = carve_scalars(c);
     w.Wk = c.take<float>((size_t)N * (size_t)K);
-    w.ET = c.take<float>((size_t)kSweepBlock * (size_t)N);
+    w.ET = c.take<float>((size_t)kSweepSuper * (size_t)N);
     return w;
 }
 
@@ -268,16 +268,31 @@ int run_sweep(uint8_t *codes, float *scales, double *qerr_out, const float *W, c
     GQ_HIP(launch_fill_u32(w.sc.status, 4, 0u, s), "fill");
     GQ_HIP(launch_copy_check(w.Wk, W, N * K, w.sc.status, s), "copy W");
     if (imp) GQ_HIP(launch_check_finite(imp, K, w.sc.status, s), "check imp");
-    for (int64_t b0 = 0; b0 < K; b0 += kSweepBlock) {
-        const int64_t bw = (K - b0) < kSweepBlock ? (K - b0) : kSweepBlock;
-        GQ_HIP(launch_sweep_block(w.Wk, w.ET, codes, scales, U, N, K, G, b0, s), "sweep block");
-        const int64_t e = b0 + bw;
-        if (e < K) {
-            GemmDesc d = gemm(w.ET, N, U + b0 * K + e, K, N, K - e, bw, w.Wk + e, K);
-            d.cin = w.Wk + e;
+    // Column order as in the unblocked sweep; every column receives the
+    // feedback of all earlier columns before it is quantised: from its own
+    // block inside the sweep kernel, from earlier blocks of its group through
+    // the per-block products, and from earlier groups through the group products.
+    for (int64_t g0 = 0; g0 < K; g0 += kSweepSuper) {
+        const int64_t g1 = (K - g0) < kSweepSuper ? K : g0 + kSweepSuper;
+        for (int64_t b0 = g0; b0 < g1; b0 += kSweepBlock) {
+            const int64_t bw = (g1 - b0) < kSweepBlock ? (g1 - b0) : kSweepBlock;
+            float *ETb = w.ET + (b0 - g0) * N;          // this block's rows of the group's E^T
+            GQ_HIP(launch_sweep_block(w.Wk, ETb, codes, scales, U, N, K, G, b0, s), "sweep block");
+            const int64_t e = b0 + bw;
+            if (e < g1) {
+                GemmDesc d = gemm(ETb, N, U + b0 * K + e, K, N, g1 - e, bw, w.Wk + e, K);
+                d.cin = w.Wk + e;
+                d.alpha = -1.0;
+                d.beta = 1.0;
+                GQ_HIP(gemm_tn_f32(d, s), "block update");
+            }
+        }
+        if (g1 < K) {
+            GemmDesc d = gemm(w.ET, N, U + g0 * K + g1, K, N, K - g1, g1 - g0, w.Wk + g1, K);
+            d.cin = w.Wk + g1;
             d.alpha = -1.0;
             d.beta = 1.0;
-            GQ_HIP(gemm_tn_f32(d, s), "block update");
+            GQ_HIP(gemm_tn_f32(d, s), "group update");
         }
     }
     if (qerr_out) {

@@ -6,13 +6,17 @@
 // Sweep layout: rows are independent given U, so a wave holds 4 rows, 16 lanes
 // per row, 8 consecutive columns per lane (the whole 128-column block of a row
 // lives in registers).  Column i of the block is owned by lane i/8 of each
-// 16-lane row group; one __shfl broadcasts its current value to the row group,
-// every lane takes the same rounding decision, and each lane then applies the
-// error to its own 8 columns with one 32-byte LDS read of U's row i (the 128 x
-// 128 block of U sits in LDS; zeros below its diagonal make the update a no-op
-// for columns already done).  Group maxima are a 16-lane xor-shuffle reduction.
+// 16-lane row group; a DPP row broadcast hands its current value to the row
+// group, every lane takes the same rounding decision, and each lane then
+// applies the error to its own 8 columns with one 32-byte LDS read of U's row i
+// (the 128 x 128 block of U sits in LDS; zeros below its diagonal make the
+// update a no-op for columns already done).  The 128 columns are unrolled with
+// the group size fixed at compile time, so the column loop is straight-line code
+// the scheduler can overlap.  Group maxima are a 16-lane xor-shuffle reduction.
 // The per-column errors leave the kernel transposed (k-major) through LDS, as
 // the A operand of the matrix-core block update that follows.
+#include <utility>
+
 #include "gq_internal.h"
 
 namespace gq {
@@ -23,20 +27,38 @@ constexpr int SW_NT = 512;             // 8 waves
 constexpr int ROWS_WG = 32;            // 4 rows per wave
 constexpr int UPITCH = BW + 4;
 
-__global__ __launch_bounds__(SW_NT) void sweep_block_kernel(float *__restrict__ Wk, float *__restrict__ ET,
+// Value of register x in lane `src` of each 16-lane row, to every lane of it.
+template <int src> __device__ inline float row_bcast(float x)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x150 + src, 0xF, 0xF, false));
+}
+
+template <typename F, int... I> __device__ inline void unroll_columns(F &f, std::integer_sequence<int, I...>)
+{
+    (f(std::integral_constant<int, I>{}), ...);
+}
+
+// Four waves per SIMD (two workgroups per CU): the grid has one workgroup per
+// 32 rows, which for ten thousand rows is just over one per CU.
+template <int G>
+__global__ __launch_bounds__(SW_NT, 4) void sweep_block_kernel(float *__restrict__ Wk, float *__restrict__ ET,
                                                            uint8_t *__restrict__ codes,
                                                            float *__restrict__ scales,
                                                            const float *__restrict__ U, int64_t N,
-                                                           int64_t K, int64_t G, int64_t b0)
+                                                           int64_t K, int64_t b0)
 {
     __shared__ __attribute__((aligned(16))) float Us[BW * UPITCH];
+    __shared__ float rdiag[BW];
     const int tid = threadIdx.x;
     const int bw = (int)((K - b0) < BW ? (K - b0) : BW);
 
+    // U's block, zero outside the bw x bw corner; past bw the reciprocal
+    // diagonal is 0, so padded columns carry zero error and change nothing.
     for (int e = tid; e < BW * BW; e += SW_NT) {
         const int r = e / BW, c = e % BW;
         Us[r * UPITCH + c] = (r < bw && c < bw) ? U[(b0 + r) * K + b0 + c] : 0.0f;
     }
+    if (tid < BW) rdiag[tid] = tid < bw ? 1.0f / U[(b0 + tid) * K + b0 + tid] : 0.0f;
     __syncthreads();
 
     const int lane = tid & 63, wave = tid >> 6;
@@ -45,71 +67,78 @@ __global__ __launch_bounds__(SW_NT) void sweep_block_kernel(float *__restrict__ 
     const int64_t row = (int64_t)blockIdx.x * ROWS_WG + rloc;
     const bool rv = row < N;
     const int cb = g16 * 8;
-    const int src = lane & ~15;
     const int64_t ngroups = K / G;
-    const int gmask = (int)G - 1;          // G is a power of two dividing 128
 
     float w[8];
-    int cd[8];
+    unsigned cdw = 0;          // the lane's 8 codes, column cb + t in nibble t
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
         const int col = cb + t;
         w[t] = (rv && col < bw) ? Wk[row * K + b0 + col] : 0.0f;
-        cd[t] = 0;
     }
 
-    float s = 0.0f;
-    for (int q = 0; q < 16; ++q) {
-        if (q * 8 >= bw) break;
+    float s = 1.0f, y = 1.0f;  // the group's scale (1 for an all-zero group) and RN(1/s)
+    float4 nu0 = *(const float4 *)&Us[cb], nu1 = *(const float4 *)&Us[cb + 4];
+    // one column: the static index lets the broadcast source and the group test
+    // be immediates
+    auto column = [&](auto I) {
+        constexpr int i = decltype(I)::value;
+        constexpr int q = i / 8, t = i % 8;
+        const float wi = row_bcast<q>(w[t]);
+        if constexpr (i % G == 0) {
+            float m = 0.0f;
 #pragma unroll
-        for (int t = 0; t < 8; ++t) {
-            const int i = q * 8 + t;
-            if (i >= bw) break;
-            const float wi = __shfl(w[t], src + q, 64);
-            if ((i & gmask) == 0) {
-                float m = 0.0f;
-#pragma unroll
-                for (int u = 0; u < 8; ++u) {
-                    const int col = cb + u;
-                    if (col >= i && col < i + G) m = fmaxf(m, fabsf(w[u]));
-                }
-                m = fmaxf(m, __shfl_xor(m, 1, 16));
-                m = fmaxf(m, __shfl_xor(m, 2, 16));
-                m = fmaxf(m, __shfl_xor(m, 4, 16));
-                m = fmaxf(m, __shfl_xor(m, 8, 16));
-                s = m / 7.0f;
-                if (g16 == 0 && rv) scales[row * ngroups + (b0 + i) / G] = s;
+            for (int u = 0; u < 8; ++u) {
+                const int col = cb + u;
+                m = (col >= i && col < i + G) ? fmaxf(m, fabsf(w[u])) : m;
             }
-            float c = 0.0f;
-            if (s != 0.0f) {
-                c = rintf(wi / s);
-                c = fminf(fmaxf(c, -8.0f), 7.0f);
-            }
-            const float e = fmaf(-c, s, wi) / Us[i * UPITCH + i];
-            const float4 u0 = *(const float4 *)&Us[i * UPITCH + cb];
-            const float4 u1 = *(const float4 *)&Us[i * UPITCH + cb + 4];
-            w[0] = fmaf(-e, u0.x, w[0]);
-            w[1] = fmaf(-e, u0.y, w[1]);
-            w[2] = fmaf(-e, u0.z, w[2]);
-            w[3] = fmaf(-e, u0.w, w[3]);
-            w[4] = fmaf(-e, u1.x, w[4]);
-            w[5] = fmaf(-e, u1.y, w[5]);
-            w[6] = fmaf(-e, u1.z, w[6]);
-            w[7] = fmaf(-e, u1.w, w[7]);
-            if (g16 == q) {
-                w[t] = e;
-                cd[t] = (int)c;
-            }
+            m = fmaxf(m, __shfl_xor(m, 1, 16));
+            m = fmaxf(m, __shfl_xor(m, 2, 16));
+            m = fmaxf(m, __shfl_xor(m, 4, 16));
+            m = fmaxf(m, __shfl_xor(m, 8, 16));
+            const float sc = m / 7.0f;
+            if (g16 == 0 && rv && i < bw) scales[row * ngroups + (b0 + i) / G] = sc;
+            // A group whose scale is 0 is all zeros at its start, and its
+            // columns feed back nothing to each other, so every value met in it
+            // is 0; dividing by 1 there gives code 0 without a branch.
+            s = sc != 0.0f ? sc : 1.0f;
+            y = 1.0f / s;
         }
-    }
+        // q = RN(wi / s) by Markstein's correction step (Markstein 1990; Muller
+        // et al., Handbook of Floating-Point Arithmetic, division via FMA): with
+        // y = RN(1/s) and q0 = RN(wi y), r = wi - s q0 is exact and RN(q0 + r y)
+        // is the correctly rounded quotient (normal range), so the code is the
+        // same as from an IEEE division, in three dependent operations instead
+        // of the division's dozen.
+        const float q0 = wi * y;
+        const float rr = fmaf(-s, q0, wi);
+        const float c = fminf(fmaxf(rintf(fmaf(rr, y, q0)), -8.0f), 7.0f);
+        const float e = fmaf(-c, s, wi) * rdiag[i];       // s = 1 only where c = wi = 0
+        // U's row i was read one column ahead; read row i + 1 now
+        const float4 u0 = nu0, u1 = nu1;
+        if constexpr (i + 1 < BW) {
+            nu0 = *(const float4 *)&Us[(i + 1) * UPITCH + cb];
+            nu1 = *(const float4 *)&Us[(i + 1) * UPITCH + cb + 4];
+        }
+        w[0] = fmaf(-e, u0.x, w[0]);
+        w[1] = fmaf(-e, u0.y, w[1]);
+        w[2] = fmaf(-e, u0.z, w[2]);
+        w[3] = fmaf(-e, u0.w, w[3]);
+        w[4] = fmaf(-e, u1.x, w[4]);
+        w[5] = fmaf(-e, u1.y, w[5]);
+        w[6] = fmaf(-e, u1.z, w[6]);
+        w[7] = fmaf(-e, u1.w, w[7]);
+        const bool own = (g16 == q);
+        w[t] = own ? e : w[t];
+        cdw |= own ? ((unsigned)(int)c & 0xFu) << (4 * t) : 0u;
+        asm("" : "+v"(cdw));       // pack now: sunk to the end, the 128 codes would all stay live
+    };
+    unroll_columns(column, std::make_integer_sequence<int, BW>{});
 
     // codes: two per byte, column 2m in the low nibble
     if (rv) {
         uint8_t *crow = codes + row * (K / 2) + (b0 + cb) / 2;
-        unsigned packed = 0;
-#pragma unroll
-        for (int m = 0; m < 4; ++m)
-            packed |= (((unsigned)cd[2 * m] & 0xFu) | (((unsigned)cd[2 * m + 1] & 0xFu) << 4)) << (8 * m);
+        const unsigned packed = cdw;
         if (cb + 8 <= bw && (((uintptr_t)crow & 3) == 0)) {
             *(unsigned *)crow = packed;
         } else {
@@ -272,8 +301,18 @@ hipError_t launch_sweep_block(float *Wk, float *ET, uint8_t *codes, float *scale
                               int64_t N, int64_t K, int64_t G, int64_t b0, hipStream_t s)
 {
     const int64_t nwg = (N + ROWS_WG - 1) / ROWS_WG;
-    hipLaunchKernelGGL(sweep_block_kernel, dim3((unsigned)nwg), dim3(SW_NT), 0, s, Wk, ET, codes, scales,
-                       U, N, K, G, b0);
+    const dim3 grid((unsigned)nwg), block(SW_NT);
+    switch (G) {
+    case 1: hipLaunchKernelGGL(sweep_block_kernel<1>, grid, block, 0, s, Wk, ET, codes, scales, U, N, K, b0); break;
+    case 2: hipLaunchKernelGGL(sweep_block_kernel<2>, grid, block, 0, s, Wk, ET, codes, scales, U, N, K, b0); break;
+    case 4: hipLaunchKernelGGL(sweep_block_kernel<4>, grid, block, 0, s, Wk, ET, codes, scales, U, N, K, b0); break;
+    case 8: hipLaunchKernelGGL(sweep_block_kernel<8>, grid, block, 0, s, Wk, ET, codes, scales, U, N, K, b0); break;
+    case 16: hipLaunchKernelGGL(sweep_block_kernel<16>, grid, block, 0, s, Wk, ET, codes, scales, U, N, K, b0); break;
+    case 32: hipLaunchKernelGGL(sweep_block_kernel<32>, grid, block, 0, s, Wk, ET, codes, scales, U, N, K, b0); break;
+    case 64: hipLaunchKernelGGL(sweep_block_kernel<64>, grid, block, 0, s, Wk, ET, codes, scales, U, N, K, b0); break;
+    case 128: hipLaunchKernelGGL(sweep_block_kernel<128>, grid, block, 0, s, Wk, ET, codes, scales, U, N, K, b0); break;
+    default: return hipErrorInvalidValue;      // the API admits powers of two up to 128 only
+    }
     return hipGetLastError();
 }
 

@@ -104,6 +104,10 @@ hipError_t launch_flip_transpose(float *U, const double *X, int64_t K, hipStream
 
 // GPTQ (gptq.hip).
 constexpr int kSweepBlock = 128;      // lazy-batch block width (columns)
+// Two-level lazy batch: blocks are grouped kSweepSuper columns at a time.  A
+// block's errors update the rest of its group at once; the columns beyond the
+// group receive the whole group's errors in one product of depth kSweepSuper.
+constexpr int kSweepSuper = 512;
 hipError_t launch_copy_check(float *dst, const float *src, int64_t n, unsigned *status,
                              hipStream_t s);
 hipError_t launch_check_finite(const float *x, int64_t n, unsigned *status, hipStream_t s);
