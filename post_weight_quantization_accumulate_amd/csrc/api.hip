@@ -14,6 +14,34 @@ namespace {
 
 thread_local std::string g_last_error;
 
+// A second stream per (thread, device) on which gptq_factor runs each next
+// diagonal block while the trailing update of the current panel runs on the
+// caller's stream, and two events that order the two.  Created on first use at
+// the default priority and kept until the process ends.
+struct Lookahead {
+    int dev = -1;
+    hipStream_t side = nullptr;
+    hipEvent_t to_side = nullptr, to_main = nullptr;
+};
+thread_local std::vector<Lookahead> g_lookahead;
+
+hipError_t lookahead_for_current_device(Lookahead **out)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    for (auto &l : g_lookahead)
+        if (l.dev == dev) { *out = &l; return hipSuccess; }
+    Lookahead l;
+    l.dev = dev;
+    if ((e = hipStreamCreateWithFlags(&l.side, hipStreamNonBlocking)) != hipSuccess) return e;
+    if ((e = hipEventCreateWithFlags(&l.to_side, hipEventDisableTiming)) != hipSuccess) return e;
+    if ((e = hipEventCreateWithFlags(&l.to_main, hipEventDisableTiming)) != hipSuccess) return e;
+    g_lookahead.push_back(l);
+    *out = &g_lookahead.back();
+    return hipSuccess;
+}
+
 int fail(int status, const std::string &msg)
 {
     g_last_error = msg;
@@ -219,22 +247,47 @@ int run_factor(float *U, const float *H, int64_t K, float damp, FactorWs &w, hip
     GQ_HIP(launch_diag_mean_check(mu, H, K, w.sc.status, s), "diag mean");
     GQ_HIP(launch_damp_reverse(w.M, H, K, (double)damp, mu, s), "damp/reverse");
     const int64_t nblk = (K + kPanel - 1) / kPanel;
+    Lookahead *la = nullptr;
+    GQ_HIP(lookahead_for_current_device(&la), "lookahead stream");
+    // Right-looking blocked Cholesky with a look-ahead of one panel: once the
+    // block row of panel p+1 has its update from panel p, the diagonal block
+    // p+1 is factored on the side stream while the rest of the trailing update
+    // of panel p runs on the caller's stream.
+    GQ_HIP(launch_potrf_diag(w.M, K, 0, (int)(K < kPanel ? K : kPanel), w.Dinv, w.DinvT, w.sc.status, s),
+           "potrf diag");
     for (int64_t p = 0; p < nblk; ++p) {
         const int64_t p0 = p * kPanel;
         const int nbp = (int)((K - p0) < kPanel ? (K - p0) : kPanel);
         const int64_t p1 = p0 + nbp;
-        double *Dinv = w.Dinv + p * kPanel * kPanel;
-        double *DinvT = w.DinvT + p * kPanel * kPanel;
-        GQ_HIP(launch_potrf_diag(w.M, K, p0, nbp, Dinv, DinvT, w.sc.status, s), "potrf diag");
-        if (p1 < K) {
-            // panel rows: R_{p,rest} = R_pp^{-T} A_{p,rest}, mirrored below the diagonal
-            GemmDesc t = gemm(Dinv, nbp, w.M + p0 * K + p1, K, nbp, K - p1, nbp, w.M + p0 * K + p1, K);
-            t.out_t = w.M + p1 * K + p0;
-            GQ_HIP(gemm_tn_f64(t, s), "trsm");
-            // trailing update of the upper triangle: A_rest -= R_{p,rest}^T R_{p,rest}
-            GemmDesc u = gemm(w.M + p0 * K + p1, K, w.M + p0 * K + p1, K, K - p1, K - p1, nbp,
-                              w.M + p1 * K + p1, K);
-            u.cin = w.M + p1 * K + p1;
+        const double *Dinv = w.Dinv + p * kPanel * kPanel;
+        if (p > 0) GQ_HIP(hipStreamWaitEvent(s, la->to_main, 0), "wait diagonal block");
+        if (p1 >= K) break;
+        // panel rows: R_{p,rest} = R_pp^{-T} A_{p,rest}, mirrored below the diagonal
+        GemmDesc t = gemm(Dinv, nbp, w.M + p0 * K + p1, K, nbp, K - p1, nbp, w.M + p0 * K + p1, K);
+        t.out_t = w.M + p1 * K + p0;
+        GQ_HIP(gemm_tn_f64(t, s), "trsm");
+        // trailing update of the upper triangle, A_rest -= R_{p,rest}^T R_{p,rest}:
+        // first the block row of panel p+1 ...
+        const int nbn = (int)((K - p1) < kPanel ? (K - p1) : kPanel);
+        const int64_t p2 = p1 + nbn;
+        GemmDesc un = gemm(w.M + p0 * K + p1, K, w.M + p0 * K + p1, K, nbn, K - p1, nbp, w.M + p1 * K + p1, K);
+        un.cin = w.M + p1 * K + p1;
+        un.alpha = -1.0;
+        un.beta = 1.0;
+        un.tri = 2;
+        GQ_HIP(gemm_tn_f64(un, s), "syrk next row");
+        // ... then its diagonal block on the side stream ...
+        GQ_HIP(hipEventRecord(la->to_side, s), "record");
+        GQ_HIP(hipStreamWaitEvent(la->side, la->to_side, 0), "wait trailing row");
+        GQ_HIP(launch_potrf_diag(w.M, K, p1, nbn, w.Dinv + (p + 1) * kPanel * kPanel,
+                                 w.DinvT + (p + 1) * kPanel * kPanel, w.sc.status, la->side),
+               "potrf diag");
+        GQ_HIP(hipEventRecord(la->to_main, la->side), "record");
+        // ... while the rest of the trailing update runs here
+        if (p2 < K) {
+            GemmDesc u = gemm(w.M + p0 * K + p2, K, w.M + p0 * K + p2, K, K - p2, K - p2, nbp,
+                              w.M + p2 * K + p2, K);
+            u.cin = w.M + p2 * K + p2;
             u.alpha = -1.0;
             u.beta = 1.0;
             u.mode = TILE_UPPER;

@@ -161,8 +161,8 @@ constexpr int PNT = 512;
 // Writes R (upper) into A, the inverse dense into XD and transposed into the
 // sub-block's strict lower triangle (diagonal into xdiag).  Returns true if a
 // pivot of a real (not padded) row was not positive.
-__device__ bool wave_factor32(double (*A)[NBMAX + 1], double *xdiag, double (*XD)[SB + 1],
-                              double *rowj, double *colj, int o, int nb, int lane)
+__device__ __attribute__((noinline)) bool wave_factor32(double (*A)[NBMAX + 1], double *xdiag, double (*XD)[SB + 1],
+                              double *rowj, double *colj, double *invd, int o, int nb, int lane)
 {
     const int br = lane >> 3, bc = lane & 7;
     double a[4][4], x[4][4];
@@ -175,23 +175,28 @@ __device__ bool wave_factor32(double (*A)[NBMAX + 1], double *xdiag, double (*XD
             x[i][k] = (r == c) ? 1.0 : 0.0;
         }
     bool badp = false;
-#pragma unroll 1
-    for (int j = 0; j < SB; ++j) {
+    // Step j with j a compile-time constant: row and column tests against j fold
+    // wherever the lane's static tile index decides them.
+    static_for<SB>([&](auto J) {
+        constexpr int j = decltype(J)::value;
         if (br == (j >> 2)) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i)                 // static register indices
-                if (i == (j & 3)) {
-#pragma unroll
-                    for (int k = 0; k < 4; ++k) rowj[4 * bc + k] = a[i][k];
-                }
+            for (int k = 0; k < 4; ++k) rowj[4 * bc + k] = a[j & 3][k];
         }
         __builtin_amdgcn_wave_barrier();
-        double piv = rowj[j];
-        if (!(piv > 0.0)) {
-            if (o + j < nb) badp = true;
-            piv = 1.0;
-        }
-        const double rjj = sqrt(piv), inv = 1.0 / rjj;
+        const double piv0 = rowj[j];
+        badp = badp || (!(piv0 > 0.0) && o + j < nb);
+        const double piv = piv0 > 0.0 ? piv0 : 1.0;
+        // 1/sqrt(piv) from the hardware estimate and two Newton steps
+        // y <- y + y (1/2 - (piv/2) y^2) (quadratic convergence to full double
+        // precision), then sqrt(piv) = piv y: a short dependent chain in place of
+        // a square root and a division
+        double inv = __builtin_amdgcn_rsq(piv);
+        const double hp = 0.5 * piv;
+        inv = fma(inv, fma(-hp * inv, inv, 0.5), inv);
+        inv = fma(inv, fma(-hp * inv, inv, 0.5), inv);
+        const double rjj = piv * inv;
+        if (lane == 0) invd[j] = inv;
         double vr[4], vc[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) vr[i] = rowj[4 * br + i] * inv;
@@ -208,30 +213,22 @@ __device__ bool wave_factor32(double (*A)[NBMAX + 1], double *xdiag, double (*XD
                 a[i][k] = (r == j) ? scl : ((r > j && c >= r) ? upd : v);
             }
         __builtin_amdgcn_wave_barrier();
-    }
+    });
     // X = R^{-1}: for j = 31 .. 0: X[j][:] /= R[j][j]; X[r][:] -= R[r][j] X[j][:] (r < j)
-#pragma unroll 1
-    for (int j = SB - 1; j >= 0; --j) {
+    static_for<SB>([&](auto JJ) {
+        constexpr int j = SB - 1 - decltype(JJ)::value;
         if (bc == (j >> 2)) {
 #pragma unroll
-            for (int k = 0; k < 4; ++k)
-                if (k == (j & 3)) {
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) colj[4 * br + i] = a[i][k];
-                }
+            for (int i = 0; i < 4; ++i) colj[4 * br + i] = a[i][j & 3];
         }
         __builtin_amdgcn_wave_barrier();
-        const double inv = 1.0 / colj[j];
+        const double inv = invd[j];                   // 1 / R_jj from the factor steps
         if (br == (j >> 2)) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                if (i == (j & 3)) {
-#pragma unroll
-                    for (int k = 0; k < 4; ++k) {
-                        x[i][k] *= inv;
-                        rowj[4 * bc + k] = x[i][k];
-                    }
-                }
+            for (int k = 0; k < 4; ++k) {
+                x[j & 3][k] *= inv;
+                rowj[4 * bc + k] = x[j & 3][k];
+            }
         }
         __builtin_amdgcn_wave_barrier();
         double vr[4], vc[4];
@@ -247,7 +244,7 @@ __device__ bool wave_factor32(double (*A)[NBMAX + 1], double *xdiag, double (*XD
                 x[i][k] = (4 * br + i < j) ? fma(-vr[i], vc[k], v) : v;
             }
         __builtin_amdgcn_wave_barrier();
-    }
+    });
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -277,14 +274,27 @@ __global__ __launch_bounds__(PNT) void potrf_diag_kernel(double *__restrict__ M,
     __shared__ double A[NBMAX][NBMAX + 1];
     __shared__ double XD[SB][SB + 1];
     __shared__ double xdiag[NBMAX];
-    __shared__ double rowj[SB], colj[SB];
+    __shared__ double rowj[SB], colj[SB], invd[SB];
     __shared__ int bad;
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
 
-    for (int e = t; e < NBMAX * NBMAX; e += PNT) {
-        const int r = e >> 7, c = e & 127;
-        const bool in = r < nb && c < nb;
-        A[r][c] = (in && c >= r) ? M[(p0 + r) * K + p0 + c] : ((r == c) ? 1.0 : 0.0);
+    {
+        // every thread's loads are issued before any LDS store (clamped
+        // addresses, selects after), so they overlap instead of round-tripping
+        constexpr int PER = NBMAX * NBMAX / PNT;
+        double v[PER];
+#pragma unroll
+        for (int m = 0; m < PER; ++m) {
+            const int e = t + PNT * m, r = e >> 7, c = e & 127;
+            const bool in = r < nb && c < nb && c >= r;
+            v[m] = M[in ? (p0 + r) * K + p0 + c : p0 * K + p0];
+        }
+#pragma unroll
+        for (int m = 0; m < PER; ++m) {
+            const int e = t + PNT * m, r = e >> 7, c = e & 127;
+            const bool in = r < nb && c < nb && c >= r;
+            A[r][c] = in ? v[m] : ((r == c) ? 1.0 : 0.0);
+        }
     }
     if (t == 0) bad = 0;
     __syncthreads();
@@ -295,7 +305,7 @@ __global__ __launch_bounds__(PNT) void potrf_diag_kernel(double *__restrict__ M,
     for (int s = 0; s < NBMAX / SB; ++s) {
         const int o = s * SB;
         if (wave == 0) {
-            const bool b = wave_factor32(A, xdiag, XD, rowj, colj, o, nb, lane);
+            const bool b = wave_factor32(A, xdiag, XD, rowj, colj, invd, o, nb, lane);
             if (b && lane == 0) bad = 1;
         }
         __syncthreads();
@@ -370,11 +380,15 @@ __global__ __launch_bounds__(PNT) void potrf_diag_kernel(double *__restrict__ M,
         double tv[8];
 #pragma unroll
         for (int q = 0; q < 8; ++q) tv[q] = 0.0;
-        if (c < NBMAX) {
-            for (int k = o + SB; k <= c; ++k) {
-                const double xk = xval(A, xdiag, k, c);
+        {
+            // the same trip count on every lane (xval is 0 for k > c), so the
+            // loop unrolls and its LDS reads overlap
+            const int cs = c < NBMAX ? c : NBMAX - 1;
+#pragma unroll 4
+            for (int k = o + SB; k < NBMAX; ++k) {
+                const double xk = xval(A, xdiag, k, cs);
 #pragma unroll
-                for (int q = 0; q < 8; ++q) tv[q] += A[o + rg * 8 + q][k] * xk;
+                for (int q = 0; q < 8; ++q) tv[q] = fma(A[o + rg * 8 + q][k], xk, tv[q]);
             }
         }
         __syncthreads();
@@ -383,15 +397,21 @@ __global__ __launch_bounds__(PNT) void potrf_diag_kernel(double *__restrict__ M,
             for (int q = 0; q < 8; ++q) A[o + rg * 8 + q][c] = tv[q];
         }
         __syncthreads();
+        // X_ii dense in XD (zero below its diagonal) for the product below
+        for (int e = t; e < SB * SB; e += PNT) {
+            const int rr = e / SB, m = e % SB;
+            XD[rr][m] = xval(A, xdiag, o + rr, o + m);
+        }
+        __syncthreads();
         if (c < NBMAX) {
             double xo[8];
 #pragma unroll
             for (int q = 0; q < 8; ++q) xo[q] = 0.0;
-#pragma unroll 2
+#pragma unroll 4
             for (int m = 0; m < SB; ++m) {
                 const double tm = A[o + m][c];
 #pragma unroll
-                for (int q = 0; q < 8; ++q) xo[q] -= xval(A, xdiag, o + rg * 8 + q, o + m) * tm;
+                for (int q = 0; q < 8; ++q) xo[q] = fma(-XD[rg * 8 + q][m], tm, xo[q]);
             }
 #pragma unroll
             for (int q = 0; q < 8; ++q) A[c][o + rg * 8 + q] = xo[q];     // X[o+rr][c], transposed
@@ -399,13 +419,14 @@ __global__ __launch_bounds__(PNT) void potrf_diag_kernel(double *__restrict__ M,
         __syncthreads();
     }
 
+    // X[r][c] (upper) is kept transposed below A's diagonal, its diagonal in xdiag
     for (int e = t; e < NBMAX * NBMAX; e += PNT) {
         const int r = e >> 7, c = e & 127;
-        if (r < nb && c < nb) {
-            const double xv = (c > r) ? A[c][r] : ((c == r) ? xdiag[r] : 0.0);
-            Dinv[r * nb + c] = xv;
-            DinvT[c * nb + r] = xv;
-        }
+        if (r < nb && c < nb) Dinv[r * nb + c] = (c > r) ? A[c][r] : ((c == r) ? xdiag[r] : 0.0);
+    }
+    for (int e = t; e < NBMAX * NBMAX; e += PNT) {
+        const int c = e >> 7, r = e & 127;        // DinvT[c][r] = X[r][c], written row by row
+        if (r < nb && c < nb) DinvT[c * nb + r] = (c > r) ? A[c][r] : ((c == r) ? xdiag[r] : 0.0);
     }
     if (t == 0 && bad) atomicOr(status, ST_NOT_PD);
 }

@@ -15,8 +15,6 @@
 // the scheduler can overlap.  Group maxima are a 16-lane xor-shuffle reduction.
 // The per-column errors leave the kernel transposed (k-major) through LDS, as
 // the A operand of the matrix-core block update that follows.
-#include <utility>
-
 #include "gq_internal.h"
 
 namespace gq {
@@ -31,11 +29,6 @@ constexpr int UPITCH = BW + 4;
 template <int src> __device__ inline float row_bcast(float x)
 {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x150 + src, 0xF, 0xF, false));
-}
-
-template <typename F, int... I> __device__ inline void unroll_columns(F &f, std::integer_sequence<int, I...>)
-{
-    (f(std::integral_constant<int, I>{}), ...);
 }
 
 // Four waves per SIMD (two workgroups per CU): the grid has one workgroup per
@@ -133,7 +126,7 @@ __global__ __launch_bounds__(SW_NT, 4) void sweep_block_kernel(float *__restrict
         cdw |= own ? ((unsigned)(int)c & 0xFu) << (4 * t) : 0u;
         asm("" : "+v"(cdw));       // pack now: sunk to the end, the 128 codes would all stay live
     };
-    unroll_columns(column, std::make_integer_sequence<int, BW>{});
+    static_for<BW>(column);
 
     // codes: two per byte, column 2m in the low nibble
     if (rv) {

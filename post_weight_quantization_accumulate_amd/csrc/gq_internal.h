@@ -7,10 +7,22 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <utility>
 #include <stdint.h>
 #include <stddef.h>
 
 namespace gq {
+
+// Calls f(std::integral_constant<int, I>{}) for I = 0, 1, ..., N-1: a loop whose
+// index is a compile-time constant in the body.
+template <typename F, int... I> __device__ inline void static_for_impl(F &f, std::integer_sequence<int, I...>)
+{
+    (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F> __device__ inline void static_for(F &&f)
+{
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
 
 // Bits of the device status word (OR-ed by kernels, read once per call).
 enum : unsigned {
