@@ -247,6 +247,103 @@ template <typename T> struct Tile {
         }
     }
 
+    // The same sum with the operands copied by the DMA path (global_load_lds:
+    // each wave instruction lands 64 x 16 bytes, one 128-element row, straight
+    // in LDS, with no registers held for it), in sub-stages of SUB rows through
+    // a ring of RING buffers that keeps three sub-stages in flight.  It uses the
+    // same LDS as the two 16-row buffers of mainloop, so two workgroups still
+    // share a CU.  Preconditions, checked by the launcher: every row of A and B
+    // starts 16-byte aligned, M and N are even (so the last 16-byte column pair
+    // of a row exists: columns past M or N read their clamped neighbours, whose
+    // products land only in discarded outputs) and Kd is a multiple of 16 (no
+    // partial k rows, which would have to be zero).  Stage indices count 16-row
+    // stages, as in mainloop.
+    static constexpr int SUB = 8, RING = 4;
+    // One DMA row copy: each lane's 16 bytes at gptr land at LDS byte address
+    // lds + 16 * lane.  Issued from asm so that the compiler, which cannot tell
+    // the ring's slots apart, adds no waits of its own; every wait is explicit
+    // below.  No register is written by the instruction.
+    __device__ static void dma_row(const T *gptr, const T *lds)
+    {
+        typedef __attribute__((address_space(3))) const void lds_cvoid;
+        const unsigned addr = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)(lds_cvoid *)lds);
+        asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                     :
+                     : "v"(gptr), "s"(addr)
+                     : "memory", "m0");
+    }
+    __device__ static void mainloop_dma(const GemmDesc &d, int64_t i0, int64_t j0, int64_t s0, int64_t s1,
+                                        Smem &sm, acc_t (&acc)[MF::NB][MF::NB])
+    {
+        static_assert(sizeof(T) == 8 && RING * SUB == 2 * BK, "the DMA ring is laid out for fp64 in Smem");
+        T(*As)[LDP] = &sm.As[0][0];                     // RING * SUB rows of the same storage
+        T(*Bs)[LDP] = &sm.Bs[0][0];
+        const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+        const int wr = wave >> 1, wc = wave & 1;
+#pragma unroll
+        for (int bi = 0; bi < MF::NB; ++bi)
+#pragma unroll
+            for (int bj = 0; bj < MF::NB; ++bj)
+#pragma unroll
+                for (int r = 0; r < MF::NACC; ++r) acc[bi][bj][r] = (T)0;
+        if (s1 <= s0) return;
+        const int64_t q0 = 2 * s0, q1 = 2 * s1;
+        // this wave copies rows 2 wave and 2 wave + 1 of each sub-stage of A and B
+        const int64_t ca = (i0 + 2 * lane) < d.M - 2 ? i0 + 2 * lane : d.M - 2;
+        const int64_t cb = (j0 + 2 * lane) < d.N - 2 ? j0 + 2 * lane : d.N - 2;
+        const T *pa = (const T *)d.A + ca + (int64_t)(2 * wave) * d.lda;
+        const T *pb = (const T *)d.B + cb + (int64_t)(2 * wave) * d.ldb;
+        auto issue = [&](int64_t q, int slot) {
+            const int64_t kb = q * SUB;
+            const T *la = As[slot * SUB + 2 * wave];
+            const T *lb = Bs[slot * SUB + 2 * wave];
+            dma_row(pa + kb * d.lda, la);
+            dma_row(pa + (kb + 1) * d.lda, la + LDP);
+            dma_row(pb + kb * d.ldb, lb);
+            dma_row(pb + (kb + 1) * d.ldb, lb + LDP);
+        };
+        // Waits are explicit: vmcnt(n) = at most n of this wave's vector memory
+        // operations outstanding (they complete in order), with lgkmcnt(0) so
+        // that this wave's LDS reads are done before the barrier frees their
+        // buffer.  s_waitcnt immediates on this target: vmcnt in bits 3:0,
+        // expcnt 6:4 (7 = no wait), lgkmcnt 11:8.
+        __builtin_amdgcn_s_waitcnt(0x0070);             // stores of the previous tile, if any
+        __builtin_amdgcn_s_barrier();                   // every wave is done with the ring
+        asm volatile("" ::: "memory");
+        issue(q0, 0);
+        if (q0 + 1 < q1) issue(q0 + 1, 1);
+        if (q0 + 2 < q1) issue(q0 + 2, 2);
+        const int m = lane % MF::LPK;
+        for (int64_t q = q0; q < q1; ++q) {
+            const int slot = (int)((q - q0) & (RING - 1));
+            const int64_t later = (q1 - 1 - q) < 2 ? (q1 - 1 - q) : 2;   // sub-stages issued after q
+            if (later == 2) __builtin_amdgcn_s_waitcnt(0x0078);
+            else if (later == 1) __builtin_amdgcn_s_waitcnt(0x0074);
+            else __builtin_amdgcn_s_waitcnt(0x0070);
+            __builtin_amdgcn_s_barrier();                // sub-stage q is in LDS for every wave,
+            asm volatile("" ::: "memory");               // and slot q - 1 is free
+            if (q + 3 < q1) issue(q + 3, (slot + 3) & (RING - 1));
+            const T(*Aq)[LDP] = As + slot * SUB;
+            const T(*Bq)[LDP] = Bs + slot * SUB;
+#pragma unroll
+            for (int kk = 0; kk < SUB; kk += MF::KSTEP) {
+                const int kr = kk + lane / MF::LPK;
+                T a[MF::NB], b[MF::NB];
+#pragma unroll
+                for (int bi = 0; bi < MF::NB; ++bi) a[bi] = Aq[kr][wr * 64 + bi * MF::BLK + m];
+#pragma unroll
+                for (int bj = 0; bj < MF::NB; ++bj) b[bj] = Bq[kr][wc * 64 + bj * MF::BLK + m];
+#pragma unroll
+                for (int bi = 0; bi < MF::NB; ++bi)
+#pragma unroll
+                    for (int bj = 0; bj < MF::NB; ++bj) acc[bi][bj] = MF::mma(a[bi], b[bj], acc[bi][bj]);
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(0x0070);
+        __builtin_amdgcn_s_barrier();                   // the ring may be refilled by the next tile
+        asm volatile("" ::: "memory");
+    }
+
     template <typename OutT>
     __device__ static void epilogue(const GemmDesc &d, int64_t i0, int64_t j0, const acc_t (&acc)[MF::NB][MF::NB])
     {
@@ -331,7 +428,7 @@ struct StreamK {
     }
 };
 
-template <typename T, typename OutT>
+template <typename T, typename OutT, bool DMA>
 __global__ __launch_bounds__(NT, 2) void gemm_tn_streamk_kernel(GemmDesc d, StreamK k, int vecA, int vecB,
                                                                T *partials, unsigned *flags)
 {
@@ -360,7 +457,10 @@ __global__ __launch_bounds__(NT, 2) void gemm_tn_streamk_kernel(GemmDesc d, Stre
         }
         int64_t i0, j0;
         tile_coords(d, tile, k.tiles_m, k.tiles_n, i0, j0);
-        TL::mainloop(d, i0, j0, s0, s1, vecA, vecB, sm, acc);
+        if constexpr (DMA)
+            TL::mainloop_dma(d, i0, j0, s0, s1, sm, acc);
+        else
+            TL::mainloop(d, i0, j0, s0, s1, vecA, vecB, sm, acc);
         bool epi = (s0 == 0 && s1 == k.nstage);
         unsigned *flag = nullptr;
         if (!epi) {
@@ -464,8 +564,14 @@ hipError_t launch_streamk(const GemmDesc &d, void *partials, unsigned *flags, hi
     k.dp_tiles = (k.ntiles / k.workers - 1) * k.workers;
     const int vecA = (d.lda % V == 0) && (((uintptr_t)d.A & 15) == 0);
     const int vecB = (d.ldb % V == 0) && (((uintptr_t)d.B & 15) == 0);
-    hipLaunchKernelGGL((gemm_tn_streamk_kernel<T, OutT>), dim3((unsigned)k.workers), dim3(NT), 0, s, d, k, vecA,
-                       vecB, (T *)partials, flags);
+    const bool dma = (d.Kd % BK == 0) && (d.M % 2 == 0) && (d.N % 2 == 0) && (d.lda % 2 == 0) &&
+                     (d.ldb % 2 == 0) && (((uintptr_t)d.A & 15) == 0) && (((uintptr_t)d.B & 15) == 0);
+    if (dma)
+        hipLaunchKernelGGL((gemm_tn_streamk_kernel<T, OutT, true>), dim3((unsigned)k.workers), dim3(NT), 0, s, d, k,
+                           vecA, vecB, (T *)partials, flags);
+    else
+        hipLaunchKernelGGL((gemm_tn_streamk_kernel<T, OutT, false>), dim3((unsigned)k.workers), dim3(NT), 0, s, d,
+                           k, vecA, vecB, (T *)partials, flags);
     return hipGetLastError();
 }
 

@@ -142,10 +142,12 @@ def test_psd_random_indefinite(gq, orc, K):
     assert _relF(P, P64) < 1e-5
 
 
-def test_psd_stream_k_path_ragged(gq):
-    """K=4100: 33 tile rows (the last one 4 wide), 561 lower tiles, more than
-    the resident workgroups, so the products run the stream-K kernel with split
-    tiles.  The oracle's eigendecomposition takes minutes at this size, so the
+@pytest.mark.parametrize("K", [4100, 4112])
+def test_psd_stream_k_path_ragged(gq, K):
+    """K=4100 and 4112: 33 tile rows (the last one 4 or 16 wide), 561 lower
+    tiles, more than the resident workgroups, so the products run the stream-K
+    kernel with split tiles; 4112 (a multiple of 16) takes the DMA main loop,
+    4100 the register-staged one.  The oracle's eigendecomposition takes minutes at this size, so the
     input has a known spectrum instead: H = Q diag(lam) Q^T with Q orthogonal
     (Householder QR of a Gaussian matrix, LAPACK through numpy) and lam spread
     over [-1, 1], whose projection is Q diag(max(lam, 0)) Q^T exactly.
@@ -153,8 +155,7 @@ def test_psd_stream_k_path_ragged(gq):
     onto a convex set is non-expansive), about 6e-8 of ||P||_F here.  A second
     call on the same input must give the same bits (split tiles are summed in a
     fixed order whichever side finishes last)."""
-    K = 4100
-    rng = np.random.default_rng(4100)
+    rng = np.random.default_rng(K)
     Q, _ = np.linalg.qr(rng.standard_normal((K, K)))
     lam = np.linspace(-1.0, 1.0, K)
     rng.shuffle(lam)
