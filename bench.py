@@ -28,8 +28,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "GPTQ int4 weights quantized/sec at K=5120/17408; Hessian TFLOP/s vs MFMA peak"
-# MI355X published peaks (dense): HBM 8 TB/s; bf16 2.5 PFLOP/s; fp32 157.3; fp64 78.6 TFLOP/s
-PEAK_TFLOPS = {"bf16": 2516.6, "f32": 157.3, "f64": 78.6}
+# MI355X published peaks (dense): HBM 8 TB/s; bf16 2.5 PFLOP/s; int8 5.0 POP/s; fp32 157.3;
+# fp64 78.6 TFLOP/s
+PEAK_TFLOPS = {"bf16": 2516.6, "i8": 5000.0, "f32": 157.3, "f64": 78.6}
+OZ_MODULI = 14             # residue products per emulated fp64 product (psd_project, K < 65536)
 PEAK_HBM_GBS = 8000.0
 SWEEP_BLOCK = 128          # lazy-batch width of gptq_sweep (include/gq.h)
 
@@ -38,11 +40,8 @@ SWEEP_BLOCK = 128          # lazy-batch width of gptq_sweep (include/gq.h)
 # kernel of known size in the same run (profiles/gemm_tn_streamk_attn5120_traffic.md).
 # Valid only for the kernel sources they were taken on: any change to those
 # files makes the figure stale and it is reported as null.
-TRAFFIC = {
-    "attn5120": {"fetch_bytes": 3231715.5390625 * 1.99958 * 1024, "write_bytes": 270044.0828125 * 1.00000 * 1024,
-                 "sources_sha256_16": "9b34bcfcb06de956"},
-}
-TRAFFIC_SOURCES = ("post_weight_quantization_accumulate_amd/csrc/gemm_tn.hip",
+TRAFFIC = {}
+TRAFFIC_SOURCES = ("post_weight_quantization_accumulate_amd/csrc/ozaki.hip",
                    "post_weight_quantization_accumulate_amd/csrc/gq_internal.h")
 
 
@@ -164,20 +163,32 @@ def main():
     for _ in range(args.warmup):
         step(False)
     torch.cuda.synchronize()
+    # psd_project brackets each launch of its product kernel with HIP events on
+    # this stream (two event records per launch)
+    gq.gq_set_timing(True)
+    prod = {"launches": 0, "ms": 0.0, "kernel": ""}
     t0 = time.perf_counter()
     for _ in range(args.steps):
         step(True)
+        n_l, ms_l, name = gq.psd_project_last_timing()
+        prod["launches"] += n_l
+        prod["ms"] += ms_l
+        prod["kernel"] = name
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    gq.gq_set_timing(False)
     ms_step = wall * 1e3 / args.steps
     stage_ms = {s: acc[s] / args.steps for s in stages}
 
     gram_flops = T * K * (K + 1)
     gram_tflops = gram_flops / (stage_ms["accumulate"] * 1e-3) / 1e12
     n_prod = gq.psd_project_products()
-    prod_flops = K * K * (K + 1)
-    prod_ms = stage_ms["psd"] / n_prod
-    prod_tflops = prod_flops / (prod_ms * 1e-3) / 1e12
+    prod_flops = K * K * (K + 1)                     # one symmetric product, lower triangle
+    emulated = prod["kernel"].startswith("oz_gemm")
+    per_launch = prod_flops * (OZ_MODULI if emulated else 1)
+    prod_ms = prod["ms"] / prod["launches"]          # the product kernel alone, live HIP events
+    prod_tops = per_launch / (prod_ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS["i8" if emulated else "f64"]
     upd_flops = sum(2 * N * min(SWEEP_BLOCK, K - b0) * (K - b0 - min(SWEEP_BLOCK, K - b0))
                     for b0 in range(0, K, SWEEP_BLOCK))
     gptq_ms = stage_ms["factor"] + stage_ms["sweep"]
@@ -195,7 +206,9 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f64",
-        "dtype_by_stage": {"accumulate": "bf16 products, f32 accumulate", "psd": "f64",
+        "dtype_by_stage": {"accumulate": "bf16 products, f32 accumulate",
+                           "psd": ("f64 products emulated exactly: int8 residues mod 14 moduli, int32 sums, "
+                                   "128-bit CRT, f64 epilogue" if emulated else "f64"),
                            "factor": "f64", "sweep": "f32", "storage": "u16/u32 bits"},
         "data": "synthetic",
         "config": {"workload": wl.name, "T": T, "K": K, "N": N, "group": G, "damp": damp,
@@ -207,22 +220,23 @@ def main():
         "gptq_weights_per_s": N * K / (gptq_ms * 1e-3),
         "sweep_update_tflops": upd_flops / (stage_ms["sweep"] * 1e-3) / 1e12,
         "qerr": qerr[0],
+        "psd_f64_equivalent_tflops": n_prod * prod_flops / (stage_ms["psd"] * 1e-3) / 1e12,
         "roofline": {
             "bound": "mfma",
-            "kernel": ("gemm_tn_streamk_kernel<double,double> (sign-iteration symmetric product); "
-                       "launch time = psd_project time / products, so it also carries the norm and "
-                       "symmetrisation kernels"),
-            "achieved": prod_tflops,
-            "peak": PEAK_TFLOPS["f64"],
-            "unit": "TFLOP/s",
-            "frac": prod_tflops / PEAK_TFLOPS["f64"],
+            "kernel": prod["kernel"] + ", sign-iteration symmetric product; timed alone with HIP events",
+            "achieved": prod_tops,
+            "peak": peak,
+            "unit": "TOP/s" if emulated else "TFLOP/s",
+            "frac": prod_tops / peak,
             "traffic": traffic,
             "traffic_detail": traffic_detail,
-            "algorithmic_bytes_per_launch": {"read_AB": 2 * K * K * 8, "read_cin_step_products": K * K * 8,
-                                             "write_lower_and_mirror": K * K * 8},
-            "per_launch_flops": prod_flops,
+            "algorithmic_bytes_per_launch": (
+                {"read_residue_planes_A_B": 2 * OZ_MODULI * K * K, "write_residues_lower": OZ_MODULI * K * (K + 1) // 2}
+                if emulated else
+                {"read_AB": 2 * K * K * 8, "read_cin_step_products": K * K * 8, "write_lower_and_mirror": K * K * 8}),
+            "per_launch_ops": per_launch,
             "avg_launch_ms": prod_ms,
-            "launches_per_step": n_prod,
+            "launches_per_step": prod["launches"] / args.steps,
         },
     }
     if not args.no_cpu_baseline:

@@ -41,7 +41,8 @@ typedef enum gq_status {
     GQ_ERR_NOT_PD = 2,         /* a Cholesky pivot of the damped Hessian was <= 0     */
     GQ_ERR_NONFINITE = 3,      /* NaN or Inf in W, in the lower triangle of H, or imp */
     GQ_ERR_NO_CALIBRATION = 4, /* mean(diag H) <= 0: refuse rather than guess         */
-    GQ_ERR_HIP = 5             /* a HIP runtime call failed                           */
+    GQ_ERR_HIP = 5,            /* a HIP runtime call failed                           */
+    GQ_ERR_INTERNAL = 6        /* an internal numerical invariant failed (a bug)      */
 } gq_status;
 
 typedef enum gq_dtype { GQ_F32 = 0, GQ_BF16 = 1 } gq_dtype;
@@ -109,19 +110,34 @@ double psd_project_flops(int64_t K);
 /* Number of symmetric products psd_project launches for any K. Host-only query. */
 int psd_project_products(void);
 
+/* Per-kernel timing of psd_project, for profiling.  gq_set_timing(1) makes
+ * later psd_project calls on this host thread bracket each launch of their
+ * product kernel with HIP events on the caller's stream; psd_project_last_timing
+ * then reports, for the last such call on this thread, the number of product
+ * launches, their summed duration in ms (*product_ms), and the name of that
+ * kernel (static string).  Returns GQ_ERR_INVALID_ARG if no timed call was
+ * made.  Timing is off by default and costs two event records per launch. */
+void gq_set_timing(int on);
+int psd_project_last_timing(int *launches, double *product_ms, const char **kernel);
+
 /*
  * psd_project -- H <- nearest positive-semidefinite matrix in Frobenius norm:
  * eigenvalues clipped at zero, rebuilt, symmetrised (hipfire-calib-data, "The
  * fix"; required before Cholesky on stored Hessians).  Computed on the device
  * without an eigendecomposition, as P = (H + sign(H) H) / 2 with sign(H) from a
- * scaled Newton-Schulz iteration run in fp64 on the matrix cores.
+ * scaled Newton-Schulz iteration.  For K < 65536 its symmetric products are
+ * fp64 products emulated exactly in integers on the int8 matrix cores (row
+ * scaling to 47-48-bit integers, residues modulo 14 moduli, Chinese remainder
+ * reconstruction: relative rounding 2^-47 per entry); above that, fp64 matrix
+ * core products.
  *   H   K x K fp32; the lower triangle is read, the full symmetric result is
  *       written in place.
  *   ws  device workspace of at least psd_project_workspace_size(K) bytes.
  * Synchronises `stream`.
  * Errors: GQ_ERR_INVALID_ARG (null pointer, K < 1, short workspace),
- *         GQ_ERR_NONFINITE (NaN/Inf in the lower triangle of H).  An all-zero H
- *         returns all zeros.
+ *         GQ_ERR_NONFINITE (NaN/Inf in the lower triangle of H),
+ *         GQ_ERR_INTERNAL (an iterate left the range the emulation needs; not
+ *         expected for any input).  An all-zero H returns all zeros.
  */
 int psd_project(float *H, int64_t K, void *ws, size_t ws_bytes, hipStream_t stream);
 

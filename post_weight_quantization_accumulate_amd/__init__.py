@@ -18,13 +18,13 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libgq.so")
 
-GQ_OK, GQ_ERR_INVALID_ARG, GQ_ERR_NOT_PD, GQ_ERR_NONFINITE, GQ_ERR_NO_CALIBRATION, GQ_ERR_HIP = range(6)
+GQ_OK, GQ_ERR_INVALID_ARG, GQ_ERR_NOT_PD, GQ_ERR_NONFINITE, GQ_ERR_NO_CALIBRATION, GQ_ERR_HIP, GQ_ERR_INTERNAL = range(7)
 GQ_F32, GQ_BF16 = 0, 1
 
 EXPORTS = (
     "gq_abi_version", "gq_last_error", "hessian_accumulate", "hessian_tril_bytes",
     "hessian_pack_tril", "hessian_unpack_tril", "psd_project_workspace_size", "psd_project",
-    "psd_project_flops", "psd_project_products",
+    "psd_project_flops", "psd_project_products", "gq_set_timing", "psd_project_last_timing",
     "gptq_factor_workspace_size", "gptq_factor", "gptq_sweep_workspace_size", "gptq_sweep",
     "gptq_quantize_workspace_size", "gptq_quantize",
 )
@@ -60,6 +60,8 @@ def lib() -> ctypes.CDLL:
             "psd_project": (I, [P, I64, P, SZ, P]),
             "psd_project_flops": (D, [I64]),
             "psd_project_products": (I, []),
+            "gq_set_timing": (None, [I]),
+            "psd_project_last_timing": (I, [ctypes.POINTER(I), ctypes.POINTER(D), ctypes.POINTER(ctypes.c_char_p)]),
             "gptq_factor_workspace_size": (SZ, [I64]),
             "gptq_factor": (I, [P, P, I64, F, P, SZ, P]),
             "gptq_sweep_workspace_size": (SZ, [I64, I64, I64]),
@@ -150,6 +152,22 @@ def psd_project_flops(K: int) -> float:
 
 def psd_project_products() -> int:
     return int(lib().psd_project_products())
+
+
+def gq_set_timing(on: bool) -> None:
+    """Per-kernel event timing of later psd_project calls on this thread."""
+    lib().gq_set_timing(1 if on else 0)
+
+
+def psd_project_last_timing():
+    """(launches, summed ms, kernel name) of the product kernel in the last timed
+    psd_project call on this thread."""
+    n = ctypes.c_int(0)
+    ms = ctypes.c_double(0.0)
+    name = ctypes.c_char_p()
+    _check(lib().psd_project_last_timing(ctypes.byref(n), ctypes.byref(ms), ctypes.byref(name)),
+           "psd_project_last_timing")
+    return n.value, ms.value, name.value.decode()
 
 
 def psd_project(H: torch.Tensor, ws: torch.Tensor) -> None:

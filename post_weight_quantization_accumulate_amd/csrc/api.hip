@@ -146,27 +146,55 @@ std::vector<double> sign_schedule()
     return alphas;
 }
 
+// Products of psd_project: emulated in integers on the int8 matrix cores below
+// this order (exact int32 sums need K 128^2 < 2^31; beta stays >= 46), fp64
+// matrix-core products at and above it.
+constexpr int64_t kOzMaxK = 65536;
+bool psd_emulated(int64_t K) { return K < kOzMaxK; }
+
 struct PsdWs {
     Scalars sc;
     double *H64, *X, *Y, *Xn;
-    double *partials;          // stream-K split-tile accumulators (large K only)
+    double *partials;          // stream-K split-tile accumulators (fp64 path, large K)
     unsigned *flags;           // stream-K boundary counters
+    int8_t *RH, *RX, *RY;      // split forms of H, the iterate X and Y = X^2 (emulated path)
+    uint8_t *Cres;             // residues of one product
+    int *eH;                   // row exponents of H's split form
 };
 
 PsdWs carve_psd(Carver &c, int64_t K)
 {
-    PsdWs w;
+    PsdWs w{};
     w.sc = carve_scalars(c);
     const size_t n = (size_t)K * (size_t)K;
     w.H64 = c.take<double>(n);
     w.X = c.take<double>(n);
-    w.Y = c.take<double>(n);
     w.Xn = c.take<double>(n);
-    const bool sk = streamk_lower_worthwhile(K);
-    w.partials = sk ? c.take<double>(streamk_partials_bytes(sizeof(double)) / sizeof(double)) : nullptr;
-    w.flags = sk ? c.take<unsigned>(kStreamKMaxWorkers) : nullptr;
+    if (psd_emulated(K)) {
+        const size_t pb = oz_planes_bytes(K);
+        w.RH = c.take<int8_t>(pb);
+        w.RX = c.take<int8_t>(pb);
+        w.RY = c.take<int8_t>(pb);
+        w.Cres = c.take<uint8_t>(pb);
+        w.eH = c.take<int>((size_t)oz_padded(K));
+    } else {
+        w.Y = c.take<double>(n);
+        const bool sk = streamk_lower_worthwhile(K);
+        w.partials = sk ? c.take<double>(streamk_partials_bytes(sizeof(double)) / sizeof(double)) : nullptr;
+        w.flags = sk ? c.take<unsigned>(kStreamKMaxWorkers) : nullptr;
+    }
     return w;
 }
+
+// Optional per-kernel timing of psd_project (gq_set_timing).
+struct PsdTiming {
+    bool on = false, valid = false;
+    std::vector<hipEvent_t> ev;
+    int launches = 0;
+    double ms = 0.0;
+    const char *kernel = "";
+};
+thread_local PsdTiming g_timing;
 
 struct FactorWs {
     Scalars sc;
@@ -372,6 +400,18 @@ extern "C" {
 
 int gq_abi_version(void) { return GQ_ABI_VERSION; }
 
+void gq_set_timing(int on) { g_timing.on = on != 0; }
+
+int psd_project_last_timing(int *launches, double *product_ms, const char **kernel)
+{
+    g_last_error.clear();
+    if (!g_timing.valid) return fail(GQ_ERR_INVALID_ARG, "no timed psd_project call on this thread");
+    if (launches) *launches = g_timing.launches;
+    if (product_ms) *product_ms = g_timing.ms;
+    if (kernel) *kernel = g_timing.kernel;
+    return GQ_OK;
+}
+
 const char *gq_last_error(void) { return g_last_error.c_str(); }
 
 int hessian_accumulate(float *H, const void *X, int x_dtype, int64_t T, int64_t K, hipStream_t stream)
@@ -448,69 +488,178 @@ int psd_project(float *H, int64_t K, void *ws, size_t ws_bytes, hipStream_t stre
     GQ_HIP(launch_sym_lower_to_f64(w.H64, H, K, status, stream), "symmetrise");
     GQ_HIP(launch_frobenius(fro, w.H64, n, w.sc.partials, stream), "norm");
     GQ_HIP(launch_scalar_combine(inv, fro, -1.0, nullptr, 0.0, stream), "inverse norm");
-
-    // X0 = H / ||H||_F;  Y0 = X0^2;  c = ||Y0||_F^(-1/2) tightens the bound
-    // (||H||_2 <= ||H^2||_F^(1/2)), so the spectrum of c X0 lies in [-1, 1].
-    GemmDesc sq = gemm(w.H64, K, w.H64, K, K, K, K, w.Y, K);
-    sq.alpha_dev = inv;
-    sq.alpha_pow = 2;
-    sq.mode = TILE_LOWER;
-    sq.tri = 1;
-    sq.out_t = w.Y;
-    GQ_HIP(gemm_tn_f64_streamk(sq, w.partials, w.flags, stream), "sign square");
-    GQ_HIP(launch_frobenius(yfro, w.Y, n, w.sc.partials, stream), "norm");
-    GQ_HIP(launch_scalar_combine(c, yfro, -0.5, nullptr, 0.0, stream), "bound");
-    GQ_HIP(launch_scalar_combine(c1inv, c, 1.0, inv, 1.0, stream), "scalars");
-    GQ_HIP(launch_scalar_combine(c3inv, c, 3.0, inv, 1.0, stream), "scalars");
     const std::vector<double> al = sign_schedule();
-    double *X = w.X, *Xn = w.Xn;
-    for (size_t k = 0; k < al.size(); ++k) {
-        const double a = 1.5 * al[k], b = -0.5 * al[k] * al[k] * al[k];
-        if (k == 0) {
-            // X0 = inv H, so X1 = a (c inv) H + b (c^3 inv) H Y0
-            GemmDesc st = gemm(w.H64, K, w.Y, K, K, K, K, X, K);
-            st.cin = w.H64;
+
+    PsdTiming &tm = g_timing;
+    const bool timing = tm.on;
+    if (timing) {
+        const size_t need = 2 * (size_t)psd_project_products();
+        while (tm.ev.size() < need) {
+            hipEvent_t e;
+            GQ_HIP(hipEventCreate(&e), "timing event");
+            tm.ev.push_back(e);
+        }
+        tm.valid = false;
+    }
+    int launched = 0;
+    auto mark = [&](bool before) -> hipError_t {
+        if (!timing) return hipSuccess;
+        return hipEventRecord(tm.ev[2 * launched + (before ? 0 : 1)], stream);
+    };
+
+    if (psd_emulated(K)) {
+        // Products emulated exactly in integers (ozaki.hip).  H enters in its
+        // row-scaled split form; every iterate (spectrum in [-1, 1], so entries
+        // below 2 in magnitude) is split at exponent 1 by the product that makes
+        // it.  The CRT writes only the K x K corner of a split form, so the
+        // padding of the iterates' planes is cleared here once.
+        const int beta = oz_beta(K);
+        const size_t pb = oz_planes_bytes(K);
+        GQ_HIP(launch_zero_bytes(w.RX, pb, stream), "clear");
+        GQ_HIP(launch_zero_bytes(w.RY, pb, stream), "clear");
+        GQ_HIP(oz_split(w.H64, K, beta, w.RH, w.eH, stream), "split H");
+        auto product = [&](const GemmDesc &d, const int8_t *RA, const int *ea, const int8_t *RB, const int *eb,
+                           bool out_f32, int8_t *planes_out) -> hipError_t {
+            hipError_t e = mark(true);
+            if (e == hipSuccess) e = oz_product(d, RA, ea, RB, eb, beta, w.Cres, out_f32, planes_out, status, stream,
+                                                timing ? tm.ev[2 * launched + 1] : nullptr);
+            ++launched;
+            return e;
+        };
+        // Y0 = (H / ||H||_F)^2 (fp64 into Xn for its norm, split form into RY)
+        GemmDesc y0 = gemm(nullptr, K, nullptr, K, K, K, K, w.Xn, K);
+        y0.out_t = w.Xn;
+        y0.alpha_dev = inv;
+        y0.alpha_pow = 2;
+        GQ_HIP(product(y0, w.RH, w.eH, w.RH, w.eH, false, w.RY), "sign square");
+        GQ_HIP(launch_frobenius(yfro, w.Xn, n, w.sc.partials, stream), "norm");
+        GQ_HIP(launch_scalar_combine(c, yfro, -0.5, nullptr, 0.0, stream), "bound");
+        GQ_HIP(launch_scalar_combine(c1inv, c, 1.0, inv, 1.0, stream), "scalars");
+        GQ_HIP(launch_scalar_combine(c3inv, c, 3.0, inv, 1.0, stream), "scalars");
+        double *X = w.X, *Xn = w.Xn;
+        for (size_t k = 0; k < al.size(); ++k) {
+            const double a = 1.5 * al[k], b = -0.5 * al[k] * al[k] * al[k];
+            if (k == 0) {
+                // X1 = a (c inv) H + b (c^3 inv) H Y0
+                GemmDesc st = gemm(nullptr, K, nullptr, K, K, K, K, X, K);
+                st.out_t = X;
+                st.cin = w.H64;
+                st.alpha = b;
+                st.alpha_dev = c3inv;
+                st.alpha_pow = 1;
+                st.beta = a;
+                st.beta_dev = c1inv;
+                st.beta_pow = 1;
+                GQ_HIP(product(st, w.RH, w.eH, w.RY, nullptr, false, w.RX), "sign step");
+                continue;
+            }
+            // Y = X^2, needed only in split form
+            GemmDesc y = gemm(nullptr, K, nullptr, K, K, K, K, nullptr, K);
+            GQ_HIP(product(y, w.RX, nullptr, w.RX, nullptr, false, w.RY), "sign square");
+            // X' = a X + b X Y (fp64 for the next step's a X, split form into RX)
+            GemmDesc st = gemm(nullptr, K, nullptr, K, K, K, K, Xn, K);
+            st.out_t = Xn;
+            st.cin = X;
             st.alpha = b;
-            st.alpha_dev = c3inv;
-            st.alpha_pow = 1;
             st.beta = a;
-            st.beta_dev = c1inv;
-            st.beta_pow = 1;
+            GQ_HIP(product(st, w.RX, nullptr, w.RY, nullptr, false, w.RX), "sign step");
+            double *t = X;
+            X = Xn;
+            Xn = t;
+        }
+        // P = (H + sign(H) H) / 2, written to H as fp32 (both triangles)
+        GemmDesc fin = gemm(nullptr, K, nullptr, K, K, K, K, H, K);
+        fin.out_t = H;
+        fin.cin = w.H64;
+        fin.alpha = 0.5;
+        fin.beta = 0.5;
+        GQ_HIP(product(fin, w.RX, nullptr, w.RH, w.eH, true, nullptr), "projection");
+    } else {
+        auto product = [&](const GemmDesc &d, bool out_f32) -> hipError_t {
+            hipError_t e = mark(true);
+            if (e == hipSuccess)
+                e = out_f32 ? gemm_tn_f64_out_f32_streamk(d, w.partials, w.flags, stream)
+                            : gemm_tn_f64_streamk(d, w.partials, w.flags, stream);
+            if (e == hipSuccess) e = mark(false);
+            ++launched;
+            return e;
+        };
+        // X0 = H / ||H||_F;  Y0 = X0^2;  c = ||Y0||_F^(-1/2) tightens the bound
+        // (||H||_2 <= ||H^2||_F^(1/2)), so the spectrum of c X0 lies in [-1, 1].
+        GemmDesc sq = gemm(w.H64, K, w.H64, K, K, K, K, w.Y, K);
+        sq.alpha_dev = inv;
+        sq.alpha_pow = 2;
+        sq.mode = TILE_LOWER;
+        sq.tri = 1;
+        sq.out_t = w.Y;
+        GQ_HIP(product(sq, false), "sign square");
+        GQ_HIP(launch_frobenius(yfro, w.Y, n, w.sc.partials, stream), "norm");
+        GQ_HIP(launch_scalar_combine(c, yfro, -0.5, nullptr, 0.0, stream), "bound");
+        GQ_HIP(launch_scalar_combine(c1inv, c, 1.0, inv, 1.0, stream), "scalars");
+        GQ_HIP(launch_scalar_combine(c3inv, c, 3.0, inv, 1.0, stream), "scalars");
+        double *X = w.X, *Xn = w.Xn;
+        for (size_t k = 0; k < al.size(); ++k) {
+            const double a = 1.5 * al[k], b = -0.5 * al[k] * al[k] * al[k];
+            if (k == 0) {
+                // X0 = inv H, so X1 = a (c inv) H + b (c^3 inv) H Y0
+                GemmDesc st = gemm(w.H64, K, w.Y, K, K, K, K, X, K);
+                st.cin = w.H64;
+                st.alpha = b;
+                st.alpha_dev = c3inv;
+                st.alpha_pow = 1;
+                st.beta = a;
+                st.beta_dev = c1inv;
+                st.beta_pow = 1;
+                st.mode = TILE_LOWER;
+                st.tri = 1;
+                st.out_t = X;
+                GQ_HIP(product(st, false), "sign step");
+                continue;
+            }
+            GemmDesc y = gemm(X, K, X, K, K, K, K, w.Y, K);
+            y.mode = TILE_LOWER;
+            y.tri = 1;
+            y.out_t = w.Y;
+            GQ_HIP(product(y, false), "sign square");
+            GemmDesc st = gemm(X, K, w.Y, K, K, K, K, Xn, K);
+            st.cin = X;
+            st.alpha = b;
+            st.beta = a;
             st.mode = TILE_LOWER;
             st.tri = 1;
-            st.out_t = X;
-            GQ_HIP(gemm_tn_f64_streamk(st, w.partials, w.flags, stream), "sign step");
-            continue;
+            st.out_t = Xn;
+            GQ_HIP(product(st, false), "sign step");
+            double *t = X;
+            X = Xn;
+            Xn = t;
         }
-        GemmDesc y = gemm(X, K, X, K, K, K, K, w.Y, K);
-        y.mode = TILE_LOWER;
-        y.tri = 1;
-        y.out_t = w.Y;
-        GQ_HIP(gemm_tn_f64_streamk(y, w.partials, w.flags, stream), "sign square");
-        GemmDesc st = gemm(X, K, w.Y, K, K, K, K, Xn, K);
-        st.cin = X;
-        st.alpha = b;
-        st.beta = a;
-        st.mode = TILE_LOWER;
-        st.tri = 1;
-        st.out_t = Xn;
-        GQ_HIP(gemm_tn_f64_streamk(st, w.partials, w.flags, stream), "sign step");
-        double *t = X;
-        X = Xn;
-        Xn = t;
+        // P = (H + sign(H) H) / 2, written to H as fp32 (both triangles)
+        GemmDesc fin = gemm(X, K, w.H64, K, K, K, K, H, K);
+        fin.cin = w.H64;
+        fin.alpha = 0.5;
+        fin.beta = 0.5;
+        fin.mode = TILE_LOWER;
+        fin.tri = 1;
+        fin.out_t = H;
+        GQ_HIP(product(fin, true), "projection");
     }
-    // P = (H + sign(H) H) / 2, written to H as fp32 (both triangles)
-    GemmDesc fin = gemm(X, K, w.H64, K, K, K, K, H, K);
-    fin.cin = w.H64;
-    fin.alpha = 0.5;
-    fin.beta = 0.5;
-    fin.mode = TILE_LOWER;
-    fin.tri = 1;
-    fin.out_t = H;
-    GQ_HIP(gemm_tn_f64_out_f32_streamk(fin, w.partials, w.flags, stream), "projection");
     unsigned st = 0;
     int rc = read_status(status, stream, &st);
     if (rc) return rc;
+    if (timing) {
+        double total = 0.0;
+        for (int i = 0; i < launched; ++i) {
+            float ms = 0.0f;
+            GQ_HIP(hipEventElapsedTime(&ms, tm.ev[2 * i], tm.ev[2 * i + 1]), "timing");
+            total += ms;
+        }
+        tm.launches = launched;
+        tm.ms = total;
+        tm.kernel = psd_emulated(K) ? "oz_gemm_kernel (int8 residue products, 14 moduli)"
+                                    : "gemm_tn_streamk_kernel<double,double> (fp64 products)";
+        tm.valid = true;
+    }
+    if (st & ST_RANGE) return fail(GQ_ERR_INTERNAL, "an iterate of the sign iteration left the range [-2, 2]");
     return status_to_code(st);
 }
 

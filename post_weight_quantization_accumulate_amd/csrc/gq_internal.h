@@ -29,6 +29,7 @@ enum : unsigned {
     ST_NOT_PD = 1u,      // a Cholesky pivot was not > 0
     ST_NONFINITE = 2u,   // NaN / Inf in an input
     ST_NO_CALIB = 4u,    // mean(diag H) <= 0 (or not finite)
+    ST_RANGE = 8u,       // an emulated product's output left the range its split form needs
 };
 
 // Which output tiles a GEMM launch computes.
@@ -75,6 +76,42 @@ constexpr bool streamk_lower_worthwhile(int64_t K)
 }
 hipError_t gemm_tn_f64_streamk(const GemmDesc &d, void *partials, unsigned *flags, hipStream_t s);
 hipError_t gemm_tn_f64_out_f32_streamk(const GemmDesc &d, void *partials, unsigned *flags, hipStream_t s);
+
+// Products of symmetric fp64 matrices by modular integer emulation on the int8
+// matrix cores (ozaki.hip).  oz_split writes, for a K x K symmetric Z (ld K),
+// the residues of its row-scaled integer form modulo each of kOzMods moduli
+// (oz_planes_bytes(K) bytes, planes of Kp x Kp, zero padded) and the row
+// exponents (Kp ints).  oz_product computes out = alpha * A B + beta * cin over
+// the lower triangle (and the mirror, when out_t is set) from the split forms
+// of A and B: d describes the epilogue (out, out_t, ldo, cin, ldc, alpha, beta
+// and their device factors) with M = N = Kd = K; out may be null when only the
+// split form is wanted.  A null exponent array means exponent 1 on every row
+// (entries below 2 in magnitude).  Cres holds oz_planes_bytes(K) bytes of
+// scratch.  beta is oz_beta(K), the same for both operands.  With planes_out
+// set, the split form of the (symmetric) output at exponent 1 is written there
+// too (its padding must already be zero), and ST_RANGE is OR-ed into *status
+// if an output entry is 2 or more in magnitude.
+constexpr int kOzMods = 14;
+struct OzConst {
+    int m[kOzMods];
+    double inv_m[kOzMods];
+    unsigned long long w_lo[kOzMods], w_hi[kOzMods];   // CRT weights W_r = (M/m_r) ((M/m_r)^-1 mod m_r)
+    unsigned long long M_lo, M_hi;                     // M = prod m_r
+    double invMd;
+};
+const OzConst &oz_const();
+int oz_beta(int64_t K);
+int64_t oz_padded(int64_t K);
+size_t oz_planes_bytes(int64_t K);
+hipError_t oz_split(const double *Z, int64_t K, int beta, int8_t *planes, int *rowexp, hipStream_t s);
+// after_gemm, if set, is recorded on s right after the int8 product kernel
+// (for per-kernel timing).
+hipError_t oz_product(const GemmDesc &d, const int8_t *RA, const int *ea, const int8_t *RB, const int *eb, int beta,
+                      uint8_t *Cres, bool out_f32, int8_t *planes_out, unsigned *status, hipStream_t s,
+                      hipEvent_t after_gemm = nullptr);
+// Zeroes n bytes at p (n a multiple of 16, p 16-byte aligned) with a kernel,
+// so that it can sit inside captured graphs.
+hipError_t launch_zero_bytes(void *p, size_t n, hipStream_t s);
 
 // bf16 Gram: H_lower += X^T X, X T x K bf16 row-major.
 hipError_t launch_gram_bf16(float *H, const uint16_t *X, int64_t T, int64_t K, hipStream_t s);

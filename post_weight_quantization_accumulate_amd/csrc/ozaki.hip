@@ -1,0 +1,532 @@
+// ozaki.hip -- products of symmetric fp64 matrices on the int8 matrix cores, in
+// exact integer arithmetic (the modular "Ozaki scheme II": Ozaki, Uchino and
+// Imamura, emulation of floating-point matrix products with integer matrix
+// units and the Chinese remainder theorem).
+//
+// The sign iteration of psd_project multiplies symmetric matrices whose entries
+// are bounded by their spectral norm (<= 1 after scaling).  For such a product
+// C = A B:
+//   1. split: every row i of A is scaled by a power of two 2^(beta - e_i) (e_i
+//      the binary exponent of the row's largest magnitude) and rounded to an
+//      integer, |a_ik| <= 2^beta; likewise B by rows j.  Because both matrices
+//      are symmetric, C_ij = 2^(e_i + e_j - 2 beta) sum_k a_ik b_jk: the integer
+//      operands are read row by row, k contiguous, which is the layout the int8
+//      matrix instruction wants for both of its operands.
+//   2. each integer matrix is stored as its residues modulo kOzMods pairwise
+//      coprime moduli m_r <= 256, each residue centred to fit int8;
+//   3. per modulus, one int8 GEMM with exact int32 accumulation gives
+//      sum_k a_ik b_jk mod m_r (|sum| < K 128^2 < 2^31 for K < 2^17);
+//   4. the Chinese remainder theorem recovers the integer sum exactly from its
+//      residues, since |sum| <= K 2^(2 beta) < M / 2, M = prod m_r; it is then
+//      scaled back and rounded to fp64 once.
+// The only rounding is the truncation of step 1 (relative 2^-beta per entry of
+// the row's scale) and the final conversion, beta = 47..48 at the sizes of the
+// path.  The 14 int8 products run at the int8 matrix rate, 64 times the fp64 one.
+#include "gq_internal.h"
+
+namespace gq {
+
+namespace {
+
+constexpr int kMods[kOzMods] = {256, 255, 253, 251, 247, 241, 239, 233, 229, 227, 223, 217, 211, 199};
+
+typedef unsigned __int128 u128;
+typedef __int128 i128;
+
+// ---------------------------------------------------------------- split
+constexpr int SPL_NT = 256;
+
+__device__ inline int centred_residue(double z, double m, double inv_m, double hi, double lo);
+
+__global__ __launch_bounds__(SPL_NT) void oz_split_kernel(const double *__restrict__ Z, int64_t K, int64_t Kp,
+                                                          int beta, int8_t *__restrict__ planes,
+                                                          int *__restrict__ rowexp, OzConst c)
+{
+    __shared__ double red[SPL_NT / 64];
+    __shared__ int e_sh;
+    const int64_t i = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int64_t plane = Kp * Kp;
+    int8_t *row = planes + i * Kp;
+    if (i >= K) {                       // padding rows: zero in every plane
+        for (int64_t k = 8 * tid; k < Kp; k += 8 * SPL_NT)
+#pragma unroll
+            for (int r = 0; r < kOzMods; ++r) *(uint2 *)(row + r * plane + k) = make_uint2(0u, 0u);
+        if (tid == 0) rowexp[i] = 0;
+        return;
+    }
+    const double *zr = Z + i * K;
+    double mx = 0.0;
+    for (int64_t k = tid; k < K; k += SPL_NT) mx = fmax(mx, fabs(zr[k]));
+    for (int o = 32; o > 0; o >>= 1) mx = fmax(mx, __shfl_xor(mx, o, 64));
+    if ((tid & 63) == 0) red[tid >> 6] = mx;
+    __syncthreads();
+    if (tid == 0) {
+        double m = red[0];
+        for (int w = 1; w < SPL_NT / 64; ++w) m = fmax(m, red[w]);
+        int e = 0;
+        if (m > 0.0) frexp(m, &e);      // m = f 2^e, f in [1/2, 1): |z| <= 2^e
+        e_sh = e;
+        rowexp[i] = e;
+    }
+    __syncthreads();
+    const double sc = ldexp(1.0, beta - e_sh);
+    for (int64_t k0 = 8 * tid; k0 < Kp; k0 += 8 * SPL_NT) {
+        double z[8];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) z[t] = (k0 + t < K) ? rint(zr[k0 + t] * sc) : 0.0;   // exact integers
+#pragma unroll
+        for (int r = 0; r < kOzMods; ++r) {
+            const double m = (double)c.m[r];
+            const double hi = (double)((c.m[r] - 1) / 2), lo = -(double)(c.m[r] / 2);
+            unsigned w0 = 0, w1 = 0;
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                const unsigned b = (unsigned)centred_residue(z[t], m, c.inv_m[r], hi, lo) & 0xFFu;
+                if (t < 4) w0 |= b << (8 * t); else w1 |= b << (8 * (t - 4));
+            }
+            *(uint2 *)(row + r * plane + k0) = make_uint2(w0, w1);
+        }
+    }
+}
+
+// ---------------------------------------------------------------- int8 GEMM
+// P_r = RA_r RB_r^T mod m_r over the lower 256 x 256 tiles, all moduli in one
+// launch (blockIdx.y = modulus).  8 waves of 64 x 128 (4 x 2), each 2 x 4 blocks
+// of v_mfma_i32_32x32x32_i8: lane l feeds 16 consecutive k of row l % 32 of each
+// operand (k = 16 (l / 32) + 0..15) and holds results C[8 (e/4) + 4 (l/32) + e%4][l % 32].
+// The large tile halves the operand bytes per operation against 128 x 128
+// (the product is bound by how fast operands reach the CUs, not by the matrix
+// cores), and the 64 x 128 wave tile needs 6 LDS reads per 8 instructions.
+//
+// Operands reach LDS by DMA (global_load_lds_dwordx4: a wave instruction lands
+// 64 x 16 bytes contiguously, here 16 rows of a 64-byte k-slice) through a ring
+// of ORING slots, three stages in flight, so no registers hold them and the
+// global latency is covered three stages deep.  Rows are unpadded; the 16-byte
+// chunk c of row r sits at position c ^ swz(r), which lets any 16 consecutive
+// rows read one chunk without bank conflicts (each lane fetches the chunk that
+// belongs at its position).
+constexpr int OBM = 256, OBK = 64, ONT = 512, ORING = 4;
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+
+__device__ inline int swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+
+constexpr int kXcd = 8;
+constexpr int64_t kGroup = 4;
+
+__device__ inline int64_t xcd_logical(int64_t w, int64_t n)
+{
+    const int64_t x = w % kXcd, j = w / kXcd;
+    int64_t base = 0;
+    for (int64_t y = 0; y < x; ++y) base += (n - y + kXcd - 1) / kXcd;
+    return base + j;
+}
+
+// Lower triangle (ti >= tj) of an nt x nt grid, grouped by kGroup tile rows.
+__device__ inline void lower_tile(int64_t l, int64_t nt, int64_t &ti, int64_t &tj)
+{
+    int64_t g = 0, start = 0;
+    for (;;) {
+        const int64_t r0 = g * kGroup;
+        const int64_t r1 = (r0 + kGroup < nt) ? r0 + kGroup : nt;
+        const int64_t cnt = (r1 * (r1 + 1) - r0 * (r0 + 1)) / 2;
+        if (l < start + cnt) {
+            int64_t off = l - start;
+            const int64_t full = r0 * (r1 - r0);
+            if (off < full) {
+                tj = off / (r1 - r0);
+                ti = r0 + off % (r1 - r0);
+            } else {
+                off -= full;
+                int64_t cc = r0;
+                while (off >= r1 - cc) { off -= r1 - cc; ++cc; }
+                tj = cc;
+                ti = cc + off;
+            }
+            return;
+        }
+        start += cnt;
+        ++g;
+    }
+}
+
+// One DMA instruction: each lane's 16 bytes at gptr land at LDS byte address
+// lds + 16 * lane.  Issued from asm so that the compiler adds no waits of its
+// own (it cannot tell the ring's slots apart); the waits below are explicit.
+// The instruction writes no register.
+__device__ inline void dma16(const int8_t *gptr, const int8_t *lds)
+{
+    typedef __attribute__((address_space(3))) const void lds_cvoid;
+    const unsigned addr = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)(lds_cvoid *)lds);
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(gptr), "s"(addr)
+                 : "memory", "m0");
+}
+
+__global__ __launch_bounds__(ONT, 1) void oz_gemm_kernel(const int8_t *__restrict__ RA,
+                                                        const int8_t *__restrict__ RB, int64_t Kp,
+                                                        uint8_t *__restrict__ Cres, OzConst c)
+{
+    extern __shared__ __attribute__((aligned(1024))) int8_t oz_lds[];
+    int8_t *As = oz_lds;                               // [ORING][OBM * OBK]
+    int8_t *Bs = oz_lds + ORING * OBM * OBK;
+    const int r = blockIdx.y;
+    const int64_t nt = Kp / OBM;
+    int64_t ti, tj;
+    lower_tile(xcd_logical(blockIdx.x, gridDim.x), nt, ti, tj);
+    const int64_t i0 = ti * OBM, j0 = tj * OBM;
+    const int64_t plane = Kp * Kp;
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wr = wave >> 1, wc = wave & 1;          // 4 x 2 waves of 64 x 128
+    // DMA roles: wave w copies rows 32 w .. 32 w + 31 of both operands (two
+    // instructions each); lane l of an instruction covering rows 16 h' .. 16 h' + 15
+    // lands at row 16 h' + l / 4, position l % 4, and fetches chunk (l % 4) ^ swz(row)
+    const int8_t *ga[2], *gb[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int row = 32 * wave + 16 * h + (lane >> 2);
+        const int chunk = (lane & 3) ^ swz(row);
+        ga[h] = RA + r * plane + (i0 + row) * Kp + 16 * chunk;
+        gb[h] = RB + r * plane + (j0 + row) * Kp + 16 * chunk;
+    }
+    auto issue = [&](int64_t kt, int slot) {
+        const int64_t kb = kt * OBK;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            dma16(ga[h] + kb, As + slot * OBM * OBK + (32 * wave + 16 * h) * OBK);
+            dma16(gb[h] + kb, Bs + slot * OBM * OBK + (32 * wave + 16 * h) * OBK);
+        }
+    };
+
+    v16i acc[2][4];
+#pragma unroll
+    for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+        for (int bj = 0; bj < 4; ++bj)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[bi][bj][e] = 0;
+
+    // MFMA read offsets (bytes within a slot) for the two k32 halves of a stage
+    const int m = lane & 31;
+    int offa[2][2], offb[2][4];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int ch = 2 * h + (lane >> 5);
+#pragma unroll
+        for (int bb = 0; bb < 2; ++bb) {
+            const int ra = wr * 64 + bb * 32 + m;
+            offa[h][bb] = ra * OBK + 16 * (ch ^ swz(ra));
+        }
+#pragma unroll
+        for (int bb = 0; bb < 4; ++bb) {
+            const int rb = wc * 128 + bb * 32 + m;
+            offb[h][bb] = rb * OBK + 16 * (ch ^ swz(rb));
+        }
+    }
+
+    const int64_t nk = Kp / OBK;
+    // waits: vmcnt(n) = at most n of this wave's vector memory operations
+    // outstanding (in-order completion), with lgkmcnt(0) so that this wave's LDS
+    // reads are done before the barrier frees their slot.  Immediate layout:
+    // vmcnt 3:0, expcnt 6:4 (7 = no wait), lgkmcnt 11:8.
+    issue(0, 0);
+    if (nk > 1) issue(1, 1);
+    if (nk > 2) issue(2, 2);
+    for (int64_t kt = 0; kt < nk; ++kt) {
+        const int slot = (int)(kt & (ORING - 1));
+        const int64_t later = (nk - 1 - kt) < 2 ? (nk - 1 - kt) : 2;      // stages issued after kt
+        if (later == 2) __builtin_amdgcn_s_waitcnt(0x0078);
+        else if (later == 1) __builtin_amdgcn_s_waitcnt(0x0074);
+        else __builtin_amdgcn_s_waitcnt(0x0070);
+        __builtin_amdgcn_s_barrier();                 // stage kt is in LDS, slot kt-1 is free
+        asm volatile("" ::: "memory");
+        if (kt + 3 < nk) issue(kt + 3, (slot + 3) & (ORING - 1));
+        const int8_t *Aq = As + slot * OBM * OBK, *Bq = Bs + slot * OBM * OBK;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            v4i a[2], b[4];
+#pragma unroll
+            for (int bb = 0; bb < 2; ++bb) a[bb] = *(const v4i *)(Aq + offa[h][bb]);
+#pragma unroll
+            for (int bb = 0; bb < 4; ++bb) b[bb] = *(const v4i *)(Bq + offb[h][bb]);
+#pragma unroll
+            for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+                for (int bj = 0; bj < 4; ++bj)
+                    acc[bi][bj] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[bi], b[bj], acc[bi][bj], 0, 0, 0);
+        }
+    }
+
+    // residue mod m in [0, m): the fp64 quotient of |P| < 2^31 by m < 2^9 is
+    // nowhere near an integer boundary it could round across, so floor is exact
+    const double md = (double)c.m[r], im = c.inv_m[r];
+    uint8_t *out = Cres + r * plane;
+#pragma unroll
+    for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+        for (int bj = 0; bj < 4; ++bj)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int64_t gi = i0 + wr * 64 + bi * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+                const int64_t gj = j0 + wc * 128 + bj * 32 + m;
+                const double p = (double)acc[bi][bj][e];
+                const double q = floor(p * im);
+                const int res = (int)fma(-md, q, p);
+                if (gi >= gj) out[gi * Kp + gj] = (uint8_t)res;
+            }
+}
+
+constexpr size_t kOzGemmLds = (size_t)2 * ORING * OBM * OBK;      // 128 KiB
+
+// ---------------------------------------------------------------- CRT
+// One 64 x 64 lower tile per workgroup: reconstruct sum_k a_ik b_jk from its
+// residues (128-bit integers), scale to fp64, apply alpha / beta / cin, and
+// write the tile and, through LDS, its mirror.  A null exponent array stands
+// for the exponent 1 on every row (operands whose entries are below 2 in
+// magnitude, as every iterate of the sign iteration is).  With `planes` set the
+// kernel also writes the split form of its own (symmetric) output for the next
+// product, at the exponent 1: entries of 2 or more in magnitude would break the
+// bound the reconstruction relies on and set ST_RANGE instead.
+constexpr int CT = 64, CNT = 256;
+
+// Residue of the integer z (|z| <= 2^53) modulo m, centred into int8 range.
+__device__ inline int centred_residue(double z, double m, double inv_m, double hi, double lo)
+{
+    // z - m rint(z / m) is exact (|q m| < 2^53) and within one m of the centred
+    // residue; one correction each way centres it
+    const double q = rint(z * inv_m);
+    double rr = fma(-m, q, z);
+    rr = rr > hi ? rr - m : rr;
+    rr = rr < lo ? rr + m : rr;
+    return (int)rr;
+}
+
+template <typename OutT>
+__global__ __launch_bounds__(CNT) void oz_crt_kernel(GemmDesc d, const uint8_t *__restrict__ Cres, int64_t Kp,
+                                                    const int *__restrict__ ea, const int *__restrict__ eb,
+                                                    int twobeta, OzConst c, int8_t *__restrict__ planes, int beta,
+                                                    unsigned *status)
+{
+    __shared__ double tile[CT][CT + 1];
+    const int64_t K = d.M;
+    int64_t ti = 0, tj = 0;
+    {
+        // tile index -> (ti >= tj) in row order
+        const int64_t id = blockIdx.x;
+        int64_t t = (int64_t)((sqrt(8.0 * (double)id + 1.0) - 1.0) * 0.5);
+        while (t * (t + 1) / 2 > id) --t;
+        while ((t + 1) * (t + 2) / 2 <= id) ++t;
+        ti = t;
+        tj = id - t * (t + 1) / 2;
+    }
+    const int64_t i0 = ti * CT, j0 = tj * CT;
+    double alpha = d.alpha, beta_c = d.beta;
+    if (d.alpha_dev) { for (int p = 0; p < d.alpha_pow; ++p) alpha *= *d.alpha_dev; }
+    if (d.beta_dev) { for (int p = 0; p < d.beta_pow; ++p) beta_c *= *d.beta_dev; }
+    const double *cin = (const double *)d.cin;
+    const u128 Mq = ((u128)c.M_hi << 64) | c.M_lo;
+    const int64_t plane = Kp * Kp;
+    const int tid = threadIdx.x;
+    const int cj = tid & (CT - 1), rg = tid >> 6;       // column, row group (4 x 16 rows)
+    const int64_t gj = j0 + cj;
+    bool range_bad = false;
+    for (int rr = 0; rr < CT / 4; ++rr) {
+        const int li = rg * (CT / 4) + rr;
+        const int64_t gi = i0 + li;
+        double v = 0.0;
+        if (gi < K && gj < K && gi >= gj) {
+            u128 S = 0;
+            const uint8_t *p = Cres + gi * Kp + gj;
+#pragma unroll
+            for (int r = 0; r < kOzMods; ++r) {
+                const u128 w = ((u128)c.w_hi[r] << 64) | c.w_lo[r];
+                S += (u128)p[r * plane] * w;
+            }
+            // S < 14 * 255 * M: q = floor(S / M) from a double estimate, then
+            // an exact correction of at most one step each way
+            const double Sd = ldexp((double)(unsigned long long)(S >> 64), 64) + (double)(unsigned long long)S;
+            const unsigned long long q = (unsigned long long)floor(Sd * c.invMd);
+            i128 x = (i128)S - (i128)((u128)q * Mq);
+            if (x < 0) x += (i128)Mq;
+            if (x >= (i128)Mq) x -= (i128)Mq;
+            if (x > (i128)(Mq >> 1)) x -= (i128)Mq;          // centred: the signed integer sum
+            const double xd = ldexp((double)(long long)(x >> 64), 64) + (double)(unsigned long long)x;
+            const int e = (ea ? ea[gi] : 1) + (eb ? eb[gj] : 1);
+            v = alpha * ldexp(xd, e - twobeta);
+            if (beta_c != 0.0) v += beta_c * cin[gi * d.ldc + gj];
+            range_bad = range_bad || !(fabs(v) < 2.0);
+        }
+        tile[li][cj] = v;
+    }
+    __syncthreads();
+    OutT *out = (OutT *)d.out;
+    OutT *out_t = (OutT *)d.out_t;
+    if (out) {
+        for (int rr = 0; rr < CT / 4; ++rr) {
+            const int li = rg * (CT / 4) + rr;
+            const int64_t gi = i0 + li;
+            if (gi < K && gj < K && gi >= gj) out[gi * d.ldo + gj] = (OutT)tile[li][cj];
+            // mirror: element (j0 + li, i0 + cj) of the transposed block
+            const int64_t mi = i0 + cj, mj = j0 + li;        // source (mi, mj) with mi >= mj
+            if (out_t && mi < K && mj < K && mi >= mj) out_t[mj * d.ldo + mi] = (OutT)tile[cj][li];
+        }
+    }
+    if (!planes) return;
+    if (range_bad) atomicOr(status, ST_RANGE);
+    // split form of the symmetric output at exponent 1: rows i0.. (this block)
+    // and, for an off-diagonal tile, rows j0.. (the mirror block).  Entries of
+    // the diagonal tile above its diagonal come from its mirror; entries past K
+    // are 0 and keep the padding zero.
+    const double sc = ldexp(1.0, beta - 1);
+    const int lr = tid >> 4, c4 = 4 * (tid & 15);
+    for (int pass = 0; pass < (ti == tj ? 1 : 2); ++pass) {
+        const int64_t rbase = pass ? j0 : i0, cbase = pass ? i0 : j0;
+        for (int rr = 0; rr < CT / 16; ++rr) {
+            const int li = rr * 16 + lr;
+            if (rbase + li >= K) continue;
+            double z[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const int cc = c4 + t;
+                // value at (rbase + li, cbase + cc) of the symmetric output
+                const double v = pass ? tile[cc][li] : (ti == tj && cc > li ? tile[cc][li] : tile[li][cc]);
+                z[t] = rint(v * sc);
+            }
+#pragma unroll
+            for (int r = 0; r < kOzMods; ++r) {
+                const double m = (double)c.m[r];
+                const double hi = (double)((c.m[r] - 1) / 2), lo = -(double)(c.m[r] / 2);
+                unsigned w = 0;
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+                    w |= ((unsigned)centred_residue(z[t], m, c.inv_m[r], hi, lo) & 0xFFu) << (8 * t);
+                *(unsigned *)(planes + r * plane + (rbase + li) * Kp + cbase + c4) = w;
+            }
+        }
+    }
+}
+
+__global__ void zero16_kernel(uint4 *p, int64_t n16)
+{
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride) p[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+
+u128 mulmod(u128 a, u128 b, u128 m)
+{
+    // a, b < m < 2^112: double-and-add (host only, once)
+    u128 r = 0;
+    a %= m;
+    while (b) {
+        if (b & 1) r = (r + a) % m;
+        a = (a << 1) % m;
+        b >>= 1;
+    }
+    return r;
+}
+
+int inv_mod_small(int64_t a, int64_t m)
+{
+    int64_t t = 0, nt = 1, r = m, nr = ((a % m) + m) % m;
+    while (nr) {
+        const int64_t q = r / nr;
+        int64_t x = t - q * nt; t = nt; nt = x;
+        x = r - q * nr; r = nr; nr = x;
+    }
+    return (int)((t % m + m) % m);
+}
+
+}  // namespace
+
+const OzConst &oz_const()
+{
+    static OzConst c = [] {
+        OzConst k{};
+        u128 M = 1;
+        for (int r = 0; r < kOzMods; ++r) M *= (u128)kMods[r];
+        for (int r = 0; r < kOzMods; ++r) {
+            k.m[r] = kMods[r];
+            k.inv_m[r] = 1.0 / (double)kMods[r];
+            const u128 Mr = M / (u128)kMods[r];
+            const int inv = inv_mod_small((int64_t)(Mr % (u128)kMods[r]), kMods[r]);
+            const u128 w = mulmod(Mr, (u128)inv, M);
+            k.w_lo[r] = (unsigned long long)w;
+            k.w_hi[r] = (unsigned long long)(w >> 64);
+        }
+        k.M_lo = (unsigned long long)M;
+        k.M_hi = (unsigned long long)(M >> 64);
+        const double Md = ldexp((double)k.M_hi, 64) + (double)k.M_lo;
+        k.invMd = 1.0 / Md;
+        return k;
+    }();
+    return c;
+}
+
+int oz_beta(int64_t K)
+{
+    // largest beta with K 2^(2 beta) < M / 2, i.e. 2 beta < log2 M - 1 - log2 K
+    const OzConst &c = oz_const();
+    const double log2M = std::log2(ldexp((double)c.M_hi, 64) + (double)c.M_lo);
+    const double room = log2M - 1.0 - std::log2((double)(K > 1 ? K : 1)) - 1e-9;
+    return (int)std::floor(room / 2.0);
+}
+
+int64_t oz_padded(int64_t K) { return (K + OBM - 1) / OBM * OBM; }
+
+size_t oz_planes_bytes(int64_t K)
+{
+    const int64_t Kp = oz_padded(K);
+    return (size_t)kOzMods * (size_t)Kp * (size_t)Kp;
+}
+
+hipError_t oz_split(const double *Z, int64_t K, int beta, int8_t *planes, int *rowexp, hipStream_t s)
+{
+    const int64_t Kp = oz_padded(K);
+    hipLaunchKernelGGL(oz_split_kernel, dim3((unsigned)Kp), dim3(SPL_NT), 0, s, Z, K, Kp, beta, planes, rowexp,
+                       oz_const());
+    return hipGetLastError();
+}
+
+hipError_t oz_product(const GemmDesc &d, const int8_t *RA, const int *ea, const int8_t *RB, const int *eb, int beta,
+                      uint8_t *Cres, bool out_f32, int8_t *planes_out, unsigned *status, hipStream_t s,
+                      hipEvent_t after_gemm)
+{
+    const int64_t K = d.M;
+    if (K <= 0) return hipSuccess;
+    if (d.N != K || d.Kd != K) return hipErrorInvalidValue;
+    const int64_t Kp = oz_padded(K);
+    const int64_t nt = Kp / OBM;
+    static bool lds_ok = hipFuncSetAttribute((const void *)oz_gemm_kernel,
+                                             hipFuncAttributeMaxDynamicSharedMemorySize,
+                                             (int)kOzGemmLds) == hipSuccess;
+    if (!lds_ok) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(oz_gemm_kernel, dim3((unsigned)(nt * (nt + 1) / 2), kOzMods), dim3(ONT), kOzGemmLds, s, RA,
+                       RB, Kp, Cres, oz_const());
+    if (after_gemm) {
+        const hipError_t e = hipEventRecord(after_gemm, s);
+        if (e != hipSuccess) return e;
+    }
+    const int64_t ct = (K + CT - 1) / CT;
+    if (out_f32)
+        hipLaunchKernelGGL(oz_crt_kernel<float>, dim3((unsigned)(ct * (ct + 1) / 2)), dim3(CNT), 0, s, d, Cres, Kp,
+                           ea, eb, 2 * beta, oz_const(), planes_out, beta, status);
+    else
+        hipLaunchKernelGGL(oz_crt_kernel<double>, dim3((unsigned)(ct * (ct + 1) / 2)), dim3(CNT), 0, s, d, Cres, Kp,
+                           ea, eb, 2 * beta, oz_const(), planes_out, beta, status);
+    return hipGetLastError();
+}
+
+hipError_t launch_zero_bytes(void *p, size_t n, hipStream_t s)
+{
+    if (n == 0) return hipSuccess;
+    if ((n & 15) || ((uintptr_t)p & 15)) return hipErrorInvalidValue;
+    const int64_t n16 = (int64_t)(n / 16);
+    const int64_t blocks = (n16 + 255) / 256 < 4096 ? (n16 + 255) / 256 : 4096;
+    hipLaunchKernelGGL(zero16_kernel, dim3((unsigned)blocks), dim3(256), 0, s, (uint4 *)p, n16);
+    return hipGetLastError();
+}
+
+}  // namespace gq
