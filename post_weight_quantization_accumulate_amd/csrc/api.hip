@@ -157,7 +157,7 @@ struct PsdWs {
     double *H64, *X, *Y, *Xn;
     double *partials;          // stream-K split-tile accumulators (fp64 path, large K)
     unsigned *flags;           // stream-K boundary counters
-    int8_t *RH, *RX, *RY;      // split forms of H, the iterate X and Y = X^2 (emulated path)
+    int8_t *RH, *RX, *RY;      // split forms of H, the iterate X and Y0 / Z (emulated path)
     uint8_t *Cres;             // residues of one product
     int *eH;                   // row exponents of H's split form
 };
@@ -168,7 +168,6 @@ PsdWs carve_psd(Carver &c, int64_t K)
     w.sc = carve_scalars(c);
     const size_t n = (size_t)K * (size_t)K;
     w.H64 = c.take<double>(n);
-    w.X = c.take<double>(n);
     w.Xn = c.take<double>(n);
     if (psd_emulated(K)) {
         const size_t pb = oz_planes_bytes(K);
@@ -178,6 +177,7 @@ PsdWs carve_psd(Carver &c, int64_t K)
         w.Cres = c.take<uint8_t>(pb);
         w.eH = c.take<int>((size_t)oz_padded(K));
     } else {
+        w.X = c.take<double>(n);
         w.Y = c.take<double>(n);
         const bool sk = streamk_lower_worthwhile(K);
         w.partials = sk ? c.take<double>(streamk_partials_bytes(sizeof(double)) / sizeof(double)) : nullptr;
@@ -509,40 +509,43 @@ int psd_project(float *H, int64_t K, void *ws, size_t ws_bytes, hipStream_t stre
 
     if (psd_emulated(K)) {
         // Products emulated exactly in integers (ozaki.hip).  H enters in its
-        // row-scaled split form; every iterate (spectrum in [-1, 1], so entries
-        // below 2 in magnitude) is split at exponent 1 by the product that makes
-        // it.  The CRT writes only the K x K corner of a split form, so the
-        // padding of the iterates' planes is cleared here once.
+        // row-scaled split form.  Every later operand is made, in split form
+        // only, by the product before it:
+        //   Y0 = (H / ||H||_F)^2                      (spectrum in [0, 1], exponent 1)
+        //   X1 = a (c inv) H + b (c^3 inv) H Y0        (spectrum in [-1, 1], exponent 1)
+        //   Z  = a I + b X^2                          (spectrum in [a + b, a], |a| < 2.6: exponent 2)
+        //   X' = X Z                                  (= a X + b X^3)
+        // so no fp64 iterate is stored.  The CRT writes only the K x K corner
+        // of a split form, so the padding of those planes is cleared here once.
         const int beta = oz_beta(K);
         const size_t pb = oz_planes_bytes(K);
         GQ_HIP(launch_zero_bytes(w.RX, pb, stream), "clear");
         GQ_HIP(launch_zero_bytes(w.RY, pb, stream), "clear");
         GQ_HIP(oz_split(w.H64, K, beta, w.RH, w.eH, stream), "split H");
-        auto product = [&](const GemmDesc &d, const int8_t *RA, const int *ea, const int8_t *RB, const int *eb,
-                           bool out_f32, int8_t *planes_out) -> hipError_t {
+        const OzOperand opH{w.RH, w.eH, 0}, opX{w.RX, nullptr, 1}, opY0{w.RY, nullptr, 1}, opZ{w.RY, nullptr, 2};
+        auto product = [&](const GemmDesc &d, const OzOperand &A, const OzOperand &B, bool out_f32,
+                           const OzOut &o) -> hipError_t {
             hipError_t e = mark(true);
-            if (e == hipSuccess) e = oz_product(d, RA, ea, RB, eb, beta, w.Cres, out_f32, planes_out, status, stream,
-                                                timing ? tm.ev[2 * launched + 1] : nullptr);
+            if (e == hipSuccess)
+                e = oz_product(d, A, B, beta, w.Cres, out_f32, o, status, stream,
+                               timing ? tm.ev[2 * launched + 1] : nullptr);
             ++launched;
             return e;
         };
-        // Y0 = (H / ||H||_F)^2 (fp64 into Xn for its norm, split form into RY)
+        // Y0 (fp64 into Xn for its norm, split form into RY)
         GemmDesc y0 = gemm(nullptr, K, nullptr, K, K, K, K, w.Xn, K);
         y0.out_t = w.Xn;
         y0.alpha_dev = inv;
         y0.alpha_pow = 2;
-        GQ_HIP(product(y0, w.RH, w.eH, w.RH, w.eH, false, w.RY), "sign square");
+        GQ_HIP(product(y0, opH, opH, false, OzOut{w.RY, 1, 0.0}), "sign square");
         GQ_HIP(launch_frobenius(yfro, w.Xn, n, w.sc.partials, stream), "norm");
         GQ_HIP(launch_scalar_combine(c, yfro, -0.5, nullptr, 0.0, stream), "bound");
         GQ_HIP(launch_scalar_combine(c1inv, c, 1.0, inv, 1.0, stream), "scalars");
         GQ_HIP(launch_scalar_combine(c3inv, c, 3.0, inv, 1.0, stream), "scalars");
-        double *X = w.X, *Xn = w.Xn;
         for (size_t k = 0; k < al.size(); ++k) {
             const double a = 1.5 * al[k], b = -0.5 * al[k] * al[k] * al[k];
             if (k == 0) {
-                // X1 = a (c inv) H + b (c^3 inv) H Y0
-                GemmDesc st = gemm(nullptr, K, nullptr, K, K, K, K, X, K);
-                st.out_t = X;
+                GemmDesc st = gemm(nullptr, K, nullptr, K, K, K, K, nullptr, K);
                 st.cin = w.H64;
                 st.alpha = b;
                 st.alpha_dev = c3inv;
@@ -550,22 +553,14 @@ int psd_project(float *H, int64_t K, void *ws, size_t ws_bytes, hipStream_t stre
                 st.beta = a;
                 st.beta_dev = c1inv;
                 st.beta_pow = 1;
-                GQ_HIP(product(st, w.RH, w.eH, w.RY, nullptr, false, w.RX), "sign step");
+                GQ_HIP(product(st, opH, opY0, false, OzOut{w.RX, 1, 0.0}), "sign step");
                 continue;
             }
-            // Y = X^2, needed only in split form
             GemmDesc y = gemm(nullptr, K, nullptr, K, K, K, K, nullptr, K);
-            GQ_HIP(product(y, w.RX, nullptr, w.RX, nullptr, false, w.RY), "sign square");
-            // X' = a X + b X Y (fp64 for the next step's a X, split form into RX)
-            GemmDesc st = gemm(nullptr, K, nullptr, K, K, K, K, Xn, K);
-            st.out_t = Xn;
-            st.cin = X;
-            st.alpha = b;
-            st.beta = a;
-            GQ_HIP(product(st, w.RX, nullptr, w.RY, nullptr, false, w.RX), "sign step");
-            double *t = X;
-            X = Xn;
-            Xn = t;
+            y.alpha = b;
+            GQ_HIP(product(y, opX, opX, false, OzOut{w.RY, 2, a}), "sign square");
+            GemmDesc st = gemm(nullptr, K, nullptr, K, K, K, K, nullptr, K);
+            GQ_HIP(product(st, opX, opZ, false, OzOut{w.RX, 1, 0.0}), "sign step");
         }
         // P = (H + sign(H) H) / 2, written to H as fp32 (both triangles)
         GemmDesc fin = gemm(nullptr, K, nullptr, K, K, K, K, H, K);
@@ -573,7 +568,7 @@ int psd_project(float *H, int64_t K, void *ws, size_t ws_bytes, hipStream_t stre
         fin.cin = w.H64;
         fin.alpha = 0.5;
         fin.beta = 0.5;
-        GQ_HIP(product(fin, w.RX, nullptr, w.RH, w.eH, true, nullptr), "projection");
+        GQ_HIP(product(fin, opX, opH, true, OzOut{nullptr, 1, 0.0}), "projection");
     } else {
         auto product = [&](const GemmDesc &d, bool out_f32) -> hipError_t {
             hipError_t e = mark(true);

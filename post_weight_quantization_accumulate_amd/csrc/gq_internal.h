@@ -78,19 +78,20 @@ hipError_t gemm_tn_f64_streamk(const GemmDesc &d, void *partials, unsigned *flag
 hipError_t gemm_tn_f64_out_f32_streamk(const GemmDesc &d, void *partials, unsigned *flags, hipStream_t s);
 
 // Products of symmetric fp64 matrices by modular integer emulation on the int8
-// matrix cores (ozaki.hip).  oz_split writes, for a K x K symmetric Z (ld K),
-// the residues of its row-scaled integer form modulo each of kOzMods moduli
-// (oz_planes_bytes(K) bytes, planes of Kp x Kp, zero padded) and the row
-// exponents (Kp ints).  oz_product computes out = alpha * A B + beta * cin over
-// the lower triangle (and the mirror, when out_t is set) from the split forms
-// of A and B: d describes the epilogue (out, out_t, ldo, cin, ldc, alpha, beta
-// and their device factors) with M = N = Kd = K; out may be null when only the
-// split form is wanted.  A null exponent array means exponent 1 on every row
-// (entries below 2 in magnitude).  Cres holds oz_planes_bytes(K) bytes of
-// scratch.  beta is oz_beta(K), the same for both operands.  With planes_out
-// set, the split form of the (symmetric) output at exponent 1 is written there
-// too (its padding must already be zero), and ST_RANGE is OR-ed into *status
-// if an output entry is 2 or more in magnitude.
+// matrix cores (ozaki.hip).  The split form of a K x K symmetric matrix Z holds
+// the residues, modulo each of kOzMods moduli, of its row-scaled integer form
+// rint(Z_ik 2^(beta - e_i)) (oz_planes_bytes(K) bytes: kOzMods planes of
+// Kp x Kp int8, zero padded), with e_i either per row (rowexp) or one exponent
+// for every row (entries below 2^exp in magnitude).  oz_split writes it with
+// per-row exponents.  oz_product computes
+//     out = alpha * A B + beta * cin   over the lower triangle (+ mirror)
+// from the split forms of A and B: d carries out, out_t, ldo, cin, ldc, alpha,
+// beta and their device factors, with M = N = Kd = K; out may be null.  With
+// o.planes set it also writes the split form of (that value + o.diag_shift on
+// the diagonal) at the single exponent o.exp (its padding must already be
+// zero), and ORs ST_RANGE into *status if an entry reaches 2^o.exp.  Cres is
+// oz_planes_bytes(K) bytes of scratch; beta is oz_beta(K) for every operand.
+// after_gemm, if set, is recorded on s right after the int8 product kernel.
 constexpr int kOzMods = 14;
 struct OzConst {
     int m[kOzMods];
@@ -99,16 +100,23 @@ struct OzConst {
     unsigned long long M_lo, M_hi;                     // M = prod m_r
     double invMd;
 };
+struct OzOperand {
+    const int8_t *planes;
+    const int *rowexp;          // per-row exponents, or null for `exp` on every row
+    int exp;
+};
+struct OzOut {
+    int8_t *planes;             // null: no split form written
+    int exp;
+    double diag_shift;
+};
 const OzConst &oz_const();
 int oz_beta(int64_t K);
 int64_t oz_padded(int64_t K);
 size_t oz_planes_bytes(int64_t K);
 hipError_t oz_split(const double *Z, int64_t K, int beta, int8_t *planes, int *rowexp, hipStream_t s);
-// after_gemm, if set, is recorded on s right after the int8 product kernel
-// (for per-kernel timing).
-hipError_t oz_product(const GemmDesc &d, const int8_t *RA, const int *ea, const int8_t *RB, const int *eb, int beta,
-                      uint8_t *Cres, bool out_f32, int8_t *planes_out, unsigned *status, hipStream_t s,
-                      hipEvent_t after_gemm = nullptr);
+hipError_t oz_product(const GemmDesc &d, const OzOperand &A, const OzOperand &B, int beta, uint8_t *Cres,
+                      bool out_f32, const OzOut &o, unsigned *status, hipStream_t s, hipEvent_t after_gemm = nullptr);
 // Zeroes n bytes at p (n a multiple of 16, p 16-byte aligned) with a kernel,
 // so that it can sit inside captured graphs.
 hipError_t launch_zero_bytes(void *p, size_t n, hipStream_t s);

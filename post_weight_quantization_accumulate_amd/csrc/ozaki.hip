@@ -110,7 +110,7 @@ constexpr int OBM = 256, OBK = 64, ONT = 512, ORING = 4;
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 
-__device__ inline int swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+__device__ inline int swz(int r) { return (r >> 2) & 3; }
 
 constexpr int kXcd = 8;
 constexpr int64_t kGroup = 4;
@@ -245,19 +245,24 @@ __global__ __launch_bounds__(ONT, 1) void oz_gemm_kernel(const int8_t *__restric
         asm volatile("" ::: "memory");
         if (kt + 3 < nk) issue(kt + 3, (slot + 3) & (ORING - 1));
         const int8_t *Aq = As + slot * OBM * OBK, *Bq = Bs + slot * OBM * OBK;
+        // both k32 halves' operands are read at once, so the second half's LDS
+        // latency hides behind the first half's matrix instructions
+        v4i a[2][2], b[2][4];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-            v4i a[2], b[4];
 #pragma unroll
-            for (int bb = 0; bb < 2; ++bb) a[bb] = *(const v4i *)(Aq + offa[h][bb]);
+            for (int bb = 0; bb < 2; ++bb) a[h][bb] = *(const v4i *)(Aq + offa[h][bb]);
 #pragma unroll
-            for (int bb = 0; bb < 4; ++bb) b[bb] = *(const v4i *)(Bq + offb[h][bb]);
+            for (int bb = 0; bb < 4; ++bb) b[h][bb] = *(const v4i *)(Bq + offb[h][bb]);
+        }
+        __builtin_amdgcn_sched_barrier(0);              // keep all twelve reads ahead of the MFMAs
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
 #pragma unroll
             for (int bi = 0; bi < 2; ++bi)
 #pragma unroll
                 for (int bj = 0; bj < 4; ++bj)
-                    acc[bi][bj] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[bi], b[bj], acc[bi][bj], 0, 0, 0);
-        }
+                    acc[bi][bj] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[h][bi], b[h][bj], acc[bi][bj], 0, 0, 0);
     }
 
     // residue mod m in [0, m): the fp64 quotient of |P| < 2^31 by m < 2^9 is
@@ -284,12 +289,12 @@ constexpr size_t kOzGemmLds = (size_t)2 * ORING * OBM * OBK;      // 128 KiB
 // ---------------------------------------------------------------- CRT
 // One 64 x 64 lower tile per workgroup: reconstruct sum_k a_ik b_jk from its
 // residues (128-bit integers), scale to fp64, apply alpha / beta / cin, and
-// write the tile and, through LDS, its mirror.  A null exponent array stands
-// for the exponent 1 on every row (operands whose entries are below 2 in
-// magnitude, as every iterate of the sign iteration is).  With `planes` set the
-// kernel also writes the split form of its own (symmetric) output for the next
-// product, at the exponent 1: entries of 2 or more in magnitude would break the
-// bound the reconstruction relies on and set ST_RANGE instead.
+// write the tile and, through LDS, its mirror.  An operand without a row
+// exponent array has the same exponent on every row (entries below 2^exp in
+// magnitude).  With o.planes set the kernel also writes the split form of its
+// own (symmetric) output, plus o.diag_shift on the diagonal, for the next
+// product at the exponent o.exp: an entry of 2^o.exp or more in magnitude
+// would break the bound the reconstruction relies on and sets ST_RANGE.
 constexpr int CT = 64, CNT = 256;
 
 // Residue of the integer z (|z| <= 2^53) modulo m, centred into int8 range.
@@ -306,11 +311,15 @@ __device__ inline int centred_residue(double z, double m, double inv_m, double h
 
 template <typename OutT>
 __global__ __launch_bounds__(CNT) void oz_crt_kernel(GemmDesc d, const uint8_t *__restrict__ Cres, int64_t Kp,
-                                                    const int *__restrict__ ea, const int *__restrict__ eb,
-                                                    int twobeta, OzConst c, int8_t *__restrict__ planes, int beta,
-                                                    unsigned *status)
+                                                    OzOperand A, OzOperand B, int twobeta, OzConst c, OzOut o,
+                                                    int beta, unsigned *status)
 {
+    const int *__restrict__ ea = A.rowexp;
+    const int *__restrict__ eb = B.rowexp;
+    int8_t *__restrict__ planes = o.planes;
+    const double bound = ldexp(1.0, o.exp);
     __shared__ double tile[CT][CT + 1];
+    __shared__ unsigned rt[CT][CT / 4 + 1];            // one modulus' residue bytes of the tile
     const int64_t K = d.M;
     int64_t ti = 0, tj = 0;
     {
@@ -322,6 +331,7 @@ __global__ __launch_bounds__(CNT) void oz_crt_kernel(GemmDesc d, const uint8_t *
         ti = t;
         tj = id - t * (t + 1) / 2;
     }
+    const bool diag = (ti == tj);
     const int64_t i0 = ti * CT, j0 = tj * CT;
     double alpha = d.alpha, beta_c = d.beta;
     if (d.alpha_dev) { for (int p = 0; p < d.alpha_pow; ++p) alpha *= *d.alpha_dev; }
@@ -330,41 +340,61 @@ __global__ __launch_bounds__(CNT) void oz_crt_kernel(GemmDesc d, const uint8_t *
     const u128 Mq = ((u128)c.M_hi << 64) | c.M_lo;
     const int64_t plane = Kp * Kp;
     const int tid = threadIdx.x;
-    const int cj = tid & (CT - 1), rg = tid >> 6;       // column, row group (4 x 16 rows)
-    const int64_t gj = j0 + cj;
+    // thread -> 4 consecutive columns c4 .. c4+3 of rows lr, lr+16, lr+32, lr+48
+    const int lr = tid >> 4, c4 = 4 * (tid & 15);
     bool range_bad = false;
-    for (int rr = 0; rr < CT / 4; ++rr) {
-        const int li = rg * (CT / 4) + rr;
+#pragma unroll 1
+    for (int rr = 0; rr < CT / 16; ++rr) {
+        const int li = rr * 16 + lr;
         const int64_t gi = i0 + li;
-        double v = 0.0;
-        if (gi < K && gj < K && gi >= gj) {
-            u128 S = 0;
-            const uint8_t *p = Cres + gi * Kp + gj;
+        // residues of 4 consecutive outputs: one dword per plane (Kp is a multiple
+        // of 256, j0 + c4 of 4: aligned)
+        unsigned rs[kOzMods];
+        const bool row_in = gi < K;
+        const uint8_t *p = Cres + (row_in ? gi : 0) * Kp + j0 + c4;
 #pragma unroll
-            for (int r = 0; r < kOzMods; ++r) {
-                const u128 w = ((u128)c.w_hi[r] << 64) | c.w_lo[r];
-                S += (u128)p[r * plane] * w;
+        for (int r = 0; r < kOzMods; ++r) rs[r] = *(const unsigned *)(p + r * plane);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const int64_t gj = j0 + c4 + t;
+            double v = 0.0;
+            if (row_in && gj < K && gi >= gj) {
+                // S = sum_r c_r W_r by 32-bit limbs of W_r: each limb sum is below
+                // 14 * 255 * 2^32 < 2^44, one carry pass assembles the 128 bits
+                unsigned long long L0 = 0, L1 = 0, L2 = 0, L3 = 0;
+#pragma unroll
+                for (int r = 0; r < kOzMods; ++r) {
+                    const unsigned long long cr = (rs[r] >> (8 * t)) & 0xFFu;
+                    L0 += cr * (unsigned)c.w_lo[r];
+                    L1 += cr * (unsigned)(c.w_lo[r] >> 32);
+                    L2 += cr * (unsigned)c.w_hi[r];
+                    L3 += cr * (unsigned)(c.w_hi[r] >> 32);
+                }
+                const u128 S = (u128)L0 + ((u128)L1 << 32) + ((u128)L2 << 64) + ((u128)L3 << 96);
+                // S < 14 * 255 * M: q = floor(S / M) from a double estimate, then
+                // an exact correction of at most one step each way
+                const double Sd = ldexp((double)(unsigned long long)(S >> 64), 64) + (double)(unsigned long long)S;
+                const unsigned long long q = (unsigned long long)floor(Sd * c.invMd);
+                i128 x = (i128)S - (i128)((u128)q * Mq);
+                if (x < 0) x += (i128)Mq;
+                if (x >= (i128)Mq) x -= (i128)Mq;
+                if (x > (i128)(Mq >> 1)) x -= (i128)Mq;      // centred: the signed integer sum
+                const double xd = ldexp((double)(long long)(x >> 64), 64) + (double)(unsigned long long)x;
+                const int e = (ea ? ea[gi] : A.exp) + (eb ? eb[gj] : B.exp);
+                v = alpha * ldexp(xd, e - twobeta);
+                if (beta_c != 0.0) v += beta_c * cin[gi * d.ldc + gj];
+                if (gi == gj) v += o.diag_shift;
+                range_bad = range_bad || !(fabs(v) < bound);
             }
-            // S < 14 * 255 * M: q = floor(S / M) from a double estimate, then
-            // an exact correction of at most one step each way
-            const double Sd = ldexp((double)(unsigned long long)(S >> 64), 64) + (double)(unsigned long long)S;
-            const unsigned long long q = (unsigned long long)floor(Sd * c.invMd);
-            i128 x = (i128)S - (i128)((u128)q * Mq);
-            if (x < 0) x += (i128)Mq;
-            if (x >= (i128)Mq) x -= (i128)Mq;
-            if (x > (i128)(Mq >> 1)) x -= (i128)Mq;          // centred: the signed integer sum
-            const double xd = ldexp((double)(long long)(x >> 64), 64) + (double)(unsigned long long)x;
-            const int e = (ea ? ea[gi] : 1) + (eb ? eb[gj] : 1);
-            v = alpha * ldexp(xd, e - twobeta);
-            if (beta_c != 0.0) v += beta_c * cin[gi * d.ldc + gj];
-            range_bad = range_bad || !(fabs(v) < 2.0);
+            tile[li][c4 + t] = v;
         }
-        tile[li][cj] = v;
     }
     __syncthreads();
     OutT *out = (OutT *)d.out;
     OutT *out_t = (OutT *)d.out_t;
     if (out) {
+        const int cj = tid & (CT - 1), rg = tid >> 6;
+        const int64_t gj = j0 + cj;
         for (int rr = 0; rr < CT / 4; ++rr) {
             const int li = rg * (CT / 4) + rr;
             const int64_t gi = i0 + li;
@@ -376,35 +406,48 @@ __global__ __launch_bounds__(CNT) void oz_crt_kernel(GemmDesc d, const uint8_t *
     }
     if (!planes) return;
     if (range_bad) atomicOr(status, ST_RANGE);
-    // split form of the symmetric output at exponent 1: rows i0.. (this block)
-    // and, for an off-diagonal tile, rows j0.. (the mirror block).  Entries of
-    // the diagonal tile above its diagonal come from its mirror; entries past K
-    // are 0 and keep the padding zero.
-    const double sc = ldexp(1.0, beta - 1);
-    const int lr = tid >> 4, c4 = 4 * (tid & 15);
-    for (int pass = 0; pass < (ti == tj ? 1 : 2); ++pass) {
-        const int64_t rbase = pass ? j0 : i0, cbase = pass ? i0 : j0;
-        for (int rr = 0; rr < CT / 16; ++rr) {
+    // Split form of the symmetric output at exponent 1, one modulus at a time:
+    // each element's residue is computed once into rt, then written to rows
+    // i0.. (this block) and, off the diagonal, transposed to rows j0.. (the
+    // mirror).  On the diagonal tile, entries above its diagonal come from
+    // their mirror.  Entries past K are 0 and keep the padding zero.
+    const double sc = ldexp(1.0, beta - o.exp);
+    double z[4][4];
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const int li = rr * 16 + lr, cc = c4 + t;
+            const double v = (diag && cc > li) ? tile[cc][li] : tile[li][cc];
+            z[rr][t] = rint(v * sc);
+        }
+#pragma unroll 1
+    for (int r = 0; r < kOzMods; ++r) {
+        const double m = (double)c.m[r];
+        const double hi = (double)((c.m[r] - 1) / 2), lo = -(double)(c.m[r] / 2);
+        int8_t *pl = planes + r * plane;
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+            unsigned w = 0;
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+                w |= ((unsigned)centred_residue(z[rr][t], m, c.inv_m[r], hi, lo) & 0xFFu) << (8 * t);
             const int li = rr * 16 + lr;
-            if (rbase + li >= K) continue;
-            double z[4];
+            rt[li][c4 >> 2] = w;
+            if (i0 + li < K) *(unsigned *)(pl + (i0 + li) * Kp + j0 + c4) = w;
+        }
+        if (!diag) {
+            __syncthreads();
+            // mirror rows j0 + li: bytes (i0 + c4 + t) come from rt[c4 + t][li]
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const int cc = c4 + t;
-                // value at (rbase + li, cbase + cc) of the symmetric output
-                const double v = pass ? tile[cc][li] : (ti == tj && cc > li ? tile[cc][li] : tile[li][cc]);
-                z[t] = rint(v * sc);
-            }
-#pragma unroll
-            for (int r = 0; r < kOzMods; ++r) {
-                const double m = (double)c.m[r];
-                const double hi = (double)((c.m[r] - 1) / 2), lo = -(double)(c.m[r] / 2);
+            for (int rr = 0; rr < 4; ++rr) {
+                const int li = rr * 16 + lr;
                 unsigned w = 0;
 #pragma unroll
-                for (int t = 0; t < 4; ++t)
-                    w |= ((unsigned)centred_residue(z[t], m, c.inv_m[r], hi, lo) & 0xFFu) << (8 * t);
-                *(unsigned *)(planes + r * plane + (rbase + li) * Kp + cbase + c4) = w;
+                for (int t = 0; t < 4; ++t) w |= ((rt[c4 + t][li >> 2] >> (8 * (li & 3))) & 0xFFu) << (8 * t);
+                if (j0 + li < K) *(unsigned *)(pl + (j0 + li) * Kp + i0 + c4) = w;
             }
+            __syncthreads();
         }
     }
 }
@@ -490,9 +533,8 @@ hipError_t oz_split(const double *Z, int64_t K, int beta, int8_t *planes, int *r
     return hipGetLastError();
 }
 
-hipError_t oz_product(const GemmDesc &d, const int8_t *RA, const int *ea, const int8_t *RB, const int *eb, int beta,
-                      uint8_t *Cres, bool out_f32, int8_t *planes_out, unsigned *status, hipStream_t s,
-                      hipEvent_t after_gemm)
+hipError_t oz_product(const GemmDesc &d, const OzOperand &A, const OzOperand &B, int beta, uint8_t *Cres,
+                      bool out_f32, const OzOut &o, unsigned *status, hipStream_t s, hipEvent_t after_gemm)
 {
     const int64_t K = d.M;
     if (K <= 0) return hipSuccess;
@@ -503,8 +545,8 @@ hipError_t oz_product(const GemmDesc &d, const int8_t *RA, const int *ea, const 
                                              hipFuncAttributeMaxDynamicSharedMemorySize,
                                              (int)kOzGemmLds) == hipSuccess;
     if (!lds_ok) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(oz_gemm_kernel, dim3((unsigned)(nt * (nt + 1) / 2), kOzMods), dim3(ONT), kOzGemmLds, s, RA,
-                       RB, Kp, Cres, oz_const());
+    hipLaunchKernelGGL(oz_gemm_kernel, dim3((unsigned)(nt * (nt + 1) / 2), kOzMods), dim3(ONT), kOzGemmLds, s,
+                       A.planes, B.planes, Kp, Cres, oz_const());
     if (after_gemm) {
         const hipError_t e = hipEventRecord(after_gemm, s);
         if (e != hipSuccess) return e;
@@ -512,10 +554,10 @@ hipError_t oz_product(const GemmDesc &d, const int8_t *RA, const int *ea, const 
     const int64_t ct = (K + CT - 1) / CT;
     if (out_f32)
         hipLaunchKernelGGL(oz_crt_kernel<float>, dim3((unsigned)(ct * (ct + 1) / 2)), dim3(CNT), 0, s, d, Cres, Kp,
-                           ea, eb, 2 * beta, oz_const(), planes_out, beta, status);
+                           A, B, 2 * beta, oz_const(), o, beta, status);
     else
         hipLaunchKernelGGL(oz_crt_kernel<double>, dim3((unsigned)(ct * (ct + 1) / 2)), dim3(CNT), 0, s, d, Cres, Kp,
-                           ea, eb, 2 * beta, oz_const(), planes_out, beta, status);
+                           A, B, 2 * beta, oz_const(), o, beta, status);
     return hipGetLastError();
 }
 
