@@ -37,10 +37,13 @@ SWEEP_BLOCK = 128          # lazy-batch width of gptq_sweep (include/gq.h)
 
 # HBM bytes per launch of the dominant kernel, from two rocprofv3 --pmc passes
 # (FETCH_SIZE, WRITE_SIZE) scaled by what the same counters read for the copy
-# kernel of known size in the same run (profiles/gemm_tn_streamk_attn5120_traffic.md).
+# kernel of known size in the same run (profiles/oz_gemm_attn5120_traffic.md).
 # Valid only for the kernel sources they were taken on: any change to those
 # files makes the figure stale and it is reported as null.
-TRAFFIC = {}
+TRAFFIC = {
+    "attn5120": {"fetch_bytes": 1198615.2530487804 * 1.99958 * 1024, "write_bytes": 184582.82317073172 * 1.00000 * 1024,
+                 "sources_sha256_16": "2999067a68ec517c"},
+}
 TRAFFIC_SOURCES = ("post_weight_quantization_accumulate_amd/csrc/ozaki.hip",
                    "post_weight_quantization_accumulate_amd/csrc/gq_internal.h")
 

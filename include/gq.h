@@ -120,6 +120,15 @@ int psd_project_products(void);
 void gq_set_timing(int on);
 int psd_project_last_timing(int *launches, double *product_ms, const char **kernel);
 
+/* Kind of the symmetric products inside psd_project, for tests and comparisons.
+ * GQ_PSD_AUTO (default): emulated in integers on the int8 matrix cores for
+ * K < 65536, fp64 matrix-core products above.  GQ_PSD_F64: fp64 matrix-core
+ * products at every K.  Applies to later psd_project calls on this host thread;
+ * psd_project_workspace_size covers both kinds.  Returns GQ_ERR_INVALID_ARG for
+ * any other value (the setting is then unchanged). */
+enum { GQ_PSD_AUTO = 0, GQ_PSD_F64 = 1 };
+int gq_set_psd_products(int kind);
+
 /*
  * psd_project -- H <- nearest positive-semidefinite matrix in Frobenius norm:
  * eigenvalues clipped at zero, rebuilt, symmetrised (hipfire-calib-data, "The

@@ -20,11 +20,12 @@ LIB_PATH = os.path.join(_HERE, "libgq.so")
 
 GQ_OK, GQ_ERR_INVALID_ARG, GQ_ERR_NOT_PD, GQ_ERR_NONFINITE, GQ_ERR_NO_CALIBRATION, GQ_ERR_HIP, GQ_ERR_INTERNAL = range(7)
 GQ_F32, GQ_BF16 = 0, 1
+GQ_PSD_AUTO, GQ_PSD_F64 = 0, 1
 
 EXPORTS = (
     "gq_abi_version", "gq_last_error", "hessian_accumulate", "hessian_tril_bytes",
     "hessian_pack_tril", "hessian_unpack_tril", "psd_project_workspace_size", "psd_project",
-    "psd_project_flops", "psd_project_products", "gq_set_timing", "psd_project_last_timing",
+    "psd_project_flops", "psd_project_products", "gq_set_timing", "psd_project_last_timing", "gq_set_psd_products",
     "gptq_factor_workspace_size", "gptq_factor", "gptq_sweep_workspace_size", "gptq_sweep",
     "gptq_quantize_workspace_size", "gptq_quantize",
 )
@@ -61,6 +62,7 @@ def lib() -> ctypes.CDLL:
             "psd_project_flops": (D, [I64]),
             "psd_project_products": (I, []),
             "gq_set_timing": (None, [I]),
+            "gq_set_psd_products": (I, [I]),
             "psd_project_last_timing": (I, [ctypes.POINTER(I), ctypes.POINTER(D), ctypes.POINTER(ctypes.c_char_p)]),
             "gptq_factor_workspace_size": (SZ, [I64]),
             "gptq_factor": (I, [P, P, I64, F, P, SZ, P]),
@@ -157,6 +159,12 @@ def psd_project_products() -> int:
 def gq_set_timing(on: bool) -> None:
     """Per-kernel event timing of later psd_project calls on this thread."""
     lib().gq_set_timing(1 if on else 0)
+
+
+def gq_set_psd_products(kind: int) -> None:
+    """GQ_PSD_AUTO or GQ_PSD_F64: kind of the products of later psd_project calls
+    on this thread."""
+    _check(lib().gq_set_psd_products(int(kind)), "gq_set_psd_products")
 
 
 def psd_project_last_timing():

@@ -4,6 +4,7 @@
 #include <string>
 #include <cmath>
 #include <vector>
+#include <algorithm>
 
 #include "gq.h"
 #include "gq_internal.h"
@@ -150,7 +151,9 @@ std::vector<double> sign_schedule()
 // this order (exact int32 sums need K 128^2 < 2^31; beta stays >= 46), fp64
 // matrix-core products at and above it.
 constexpr int64_t kOzMaxK = 65536;
-bool psd_emulated(int64_t K) { return K < kOzMaxK; }
+// Product kind chosen by gq_set_psd_products on this thread (GQ_PSD_*).
+thread_local int g_psd_kind = GQ_PSD_AUTO;
+bool psd_emulated(int64_t K) { return K < kOzMaxK && g_psd_kind != GQ_PSD_F64; }
 
 struct PsdWs {
     Scalars sc;
@@ -162,14 +165,14 @@ struct PsdWs {
     int *eH;                   // row exponents of H's split form
 };
 
-PsdWs carve_psd(Carver &c, int64_t K)
+PsdWs carve_psd(Carver &c, int64_t K, bool emulated)
 {
     PsdWs w{};
     w.sc = carve_scalars(c);
     const size_t n = (size_t)K * (size_t)K;
     w.H64 = c.take<double>(n);
     w.Xn = c.take<double>(n);
-    if (psd_emulated(K)) {
+    if (emulated) {
         const size_t pb = oz_planes_bytes(K);
         w.RH = c.take<int8_t>(pb);
         w.RX = c.take<int8_t>(pb);
@@ -228,11 +231,16 @@ SweepWs carve_sweep(Carver &c, int64_t N, int64_t K)
     return w;
 }
 
+// Enough for either kind of product when both are possible, so that the size
+// does not depend on gq_set_psd_products.
 size_t psd_bytes(int64_t K)
 {
     Carver c(nullptr);
-    carve_psd(c, K);
-    return c.off;
+    carve_psd(c, K, false);
+    if (K >= kOzMaxK) return c.off;
+    Carver e(nullptr);
+    carve_psd(e, K, true);
+    return std::max(c.off, e.off);
 }
 
 size_t factor_bytes(int64_t K)
@@ -402,6 +410,14 @@ int gq_abi_version(void) { return GQ_ABI_VERSION; }
 
 void gq_set_timing(int on) { g_timing.on = on != 0; }
 
+int gq_set_psd_products(int kind)
+{
+    g_last_error.clear();
+    if (kind != GQ_PSD_AUTO && kind != GQ_PSD_F64) return fail(GQ_ERR_INVALID_ARG, "unknown product kind");
+    g_psd_kind = kind;
+    return GQ_OK;
+}
+
 int psd_project_last_timing(int *launches, double *product_ms, const char **kernel)
 {
     g_last_error.clear();
@@ -478,7 +494,7 @@ int psd_project(float *H, int64_t K, void *ws, size_t ws_bytes, hipStream_t stre
     if (K < 1) return fail(GQ_ERR_INVALID_ARG, "K must be >= 1");
     if (ws_bytes < psd_bytes(K)) return fail(GQ_ERR_INVALID_ARG, "workspace too small");
     Carver cv(ws);
-    PsdWs w = carve_psd(cv, K);
+    PsdWs w = carve_psd(cv, K, psd_emulated(K));
     const int64_t n = K * K;
     unsigned *status = w.sc.status;
     double *fro = w.sc.d + 0, *inv = w.sc.d + 1, *yfro = w.sc.d + 2, *c = w.sc.d + 3;

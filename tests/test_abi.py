@@ -39,6 +39,17 @@ def test_size_queries_are_host_only():
     assert gq.gptq_quantize_workspace_size(64, 128, 32) > gq.gptq_sweep_workspace_size(64, 128, 32)
 
 
+@pytest.mark.skipif(not os.path.exists(gq.LIB_PATH), reason="libgq.so not built")
+def test_product_kind_switch_is_host_only():
+    # The workspace covers both kinds of product, so its size does not move.
+    n = gq.psd_project_workspace_size(5120)
+    gq.gq_set_psd_products(gq.GQ_PSD_F64)
+    assert gq.psd_project_workspace_size(5120) == n
+    gq.gq_set_psd_products(gq.GQ_PSD_AUTO)
+    with pytest.raises(gq.GQError):
+        gq.gq_set_psd_products(7)
+
+
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(gq, "LIB_PATH", str(tmp_path / "missing.so"))
     monkeypatch.setattr(gq, "_lib", None)

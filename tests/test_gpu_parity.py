@@ -142,19 +142,22 @@ def test_psd_random_indefinite(gq, orc, K):
     assert _relF(P, P64) < 1e-5
 
 
+@pytest.mark.parametrize("kind", ["emulated", "f64"])
 @pytest.mark.parametrize("K", [4100, 4112])
-def test_psd_stream_k_path_ragged(gq, K):
-    """K=4100 and 4112: 33 tile rows (the last one 4 or 16 wide), 561 lower
-    tiles, more than the resident workgroups, so the products run the stream-K
-    kernel with split tiles; 4112 (a multiple of 16) takes the DMA main loop,
-    4100 the register-staged one.  The oracle's eigendecomposition takes minutes at this size, so the
+def test_psd_known_spectrum_ragged(gq, K, kind):
+    """K=4100 and 4112: 33 tile rows of 128 (the last one 4 or 16 wide).
+    Emulated products: the split forms are padded to 4352 = 17 tiles of 256,
+    the last one mostly zero padding.  fp64 products: 561 lower tiles, more than
+    the resident workgroups, so they run the stream-K kernel with split tiles;
+    4112 (a multiple of 16) takes the DMA main loop, 4100 the register-staged
+    one.  The oracle's eigendecomposition takes minutes at this size, so the
     input has a known spectrum instead: H = Q diag(lam) Q^T with Q orthogonal
     (Householder QR of a Gaussian matrix, LAPACK through numpy) and lam spread
     over [-1, 1], whose projection is Q diag(max(lam, 0)) Q^T exactly.
     Rounding H to fp32 moves the projection by at most ||H32 - H||_F (projection
     onto a convex set is non-expansive), about 6e-8 of ||P||_F here.  A second
-    call on the same input must give the same bits (split tiles are summed in a
-    fixed order whichever side finishes last)."""
+    call on the same input must give the same bits (integer sums are exact;
+    split fp64 tiles are summed in a fixed order whichever side finishes last)."""
     rng = np.random.default_rng(K)
     Q, _ = np.linalg.qr(rng.standard_normal((K, K)))
     lam = np.linspace(-1.0, 1.0, K)
@@ -164,10 +167,15 @@ def test_psd_stream_k_path_ragged(gq, K):
     P_exact = (Q * np.maximum(lam, 0.0)) @ Q.T
     H = H64.astype(np.float32)
     assert np.linalg.norm(H - H64) / np.linalg.norm(P_exact) < 1e-7
-    P = _gpu_psd(gq, H)
+    gq.gq_set_psd_products(gq.GQ_PSD_F64 if kind == "f64" else gq.GQ_PSD_AUTO)
+    try:
+        P = _gpu_psd(gq, H)
+        P2 = _gpu_psd(gq, H)
+    finally:
+        gq.gq_set_psd_products(gq.GQ_PSD_AUTO)
     assert np.array_equal(P, P.T)
     assert _relF(P, P_exact) < 1e-5
-    assert np.array_equal(_gpu_psd(gq, H).view(np.uint32), P.view(np.uint32))
+    assert np.array_equal(P2.view(np.uint32), P.view(np.uint32))
 
 
 def test_psd_stored_hessian_full_size(gq, orc):
