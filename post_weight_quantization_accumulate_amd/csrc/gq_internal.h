@@ -81,7 +81,8 @@ hipError_t gemm_tn_f64_out_f32_streamk(const GemmDesc &d, void *partials, unsign
 // matrix cores (ozaki.hip).  The split form of a K x K symmetric matrix Z holds
 // the residues, modulo each of kOzMods moduli, of its row-scaled integer form
 // rint(Z_ik 2^(beta - e_i)) (oz_planes_bytes(K) bytes: kOzMods planes of
-// Kp x Kp int8, zero padded), with e_i either per row (rowexp) or one exponent
+// Kp x Kp int8 in blocks of 256 rows x 64 k, zero padded), with e_i either per
+// row (rowexp) or one exponent
 // for every row (entries below 2^exp in magnitude).  oz_split writes it with
 // per-row exponents.  oz_product computes
 //     out = alpha * A B + beta * cin   over the lower triangle (+ mirror)

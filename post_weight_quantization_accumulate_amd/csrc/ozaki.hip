@@ -37,6 +37,7 @@ typedef __int128 i128;
 constexpr int SPL_NT = 256;
 
 __device__ inline int centred_residue(double z, double m, double inv_m, double hi, double lo);
+__device__ inline int64_t poff(int64_t row, int64_t k, int64_t Kp);
 
 __global__ __launch_bounds__(SPL_NT) void oz_split_kernel(const double *__restrict__ Z, int64_t K, int64_t Kp,
                                                           int beta, int8_t *__restrict__ planes,
@@ -47,11 +48,10 @@ __global__ __launch_bounds__(SPL_NT) void oz_split_kernel(const double *__restri
     const int64_t i = blockIdx.x;
     const int tid = threadIdx.x;
     const int64_t plane = Kp * Kp;
-    int8_t *row = planes + i * Kp;
     if (i >= K) {                       // padding rows: zero in every plane
         for (int64_t k = 8 * tid; k < Kp; k += 8 * SPL_NT)
 #pragma unroll
-            for (int r = 0; r < kOzMods; ++r) *(uint2 *)(row + r * plane + k) = make_uint2(0u, 0u);
+            for (int r = 0; r < kOzMods; ++r) *(uint2 *)(planes + r * plane + poff(i, k, Kp)) = make_uint2(0u, 0u);
         if (tid == 0) rowexp[i] = 0;
         return;
     }
@@ -85,7 +85,7 @@ __global__ __launch_bounds__(SPL_NT) void oz_split_kernel(const double *__restri
                 const unsigned b = (unsigned)centred_residue(z[t], m, c.inv_m[r], hi, lo) & 0xFFu;
                 if (t < 4) w0 |= b << (8 * t); else w1 |= b << (8 * (t - 4));
             }
-            *(uint2 *)(row + r * plane + k0) = make_uint2(w0, w1);
+            *(uint2 *)(planes + r * plane + poff(i, k0, Kp)) = make_uint2(w0, w1);
         }
     }
 }
@@ -93,24 +93,35 @@ __global__ __launch_bounds__(SPL_NT) void oz_split_kernel(const double *__restri
 // ---------------------------------------------------------------- int8 GEMM
 // P_r = RA_r RB_r^T mod m_r over the lower 256 x 256 tiles, all moduli in one
 // launch (blockIdx.y = modulus).  8 waves of 64 x 128 (4 x 2), each 2 x 4 blocks
-// of v_mfma_i32_32x32x32_i8: lane l feeds 16 consecutive k of row l % 32 of each
-// operand (k = 16 (l / 32) + 0..15) and holds results C[8 (e/4) + 4 (l/32) + e%4][l % 32].
-// The large tile halves the operand bytes per operation against 128 x 128
-// (the product is bound by how fast operands reach the CUs, not by the matrix
-// cores), and the 64 x 128 wave tile needs 6 LDS reads per 8 instructions.
+// of v_mfma_i32_32x32x32_i8.  The instruction computes X Y^T for 32-row panels X
+// and Y of 32 k: lane l feeds k = 16 (l / 32) + 0..15 of row l % 32 of each, and
+// result e of lane l is (X Y^T)[8 (e / 4) + 4 (l / 32) + e % 4][l % 32].  The B
+// panel goes first, so that e % 4 runs along a row of the output tile and each
+// lane holds 4 consecutive residues of a row, one dword.
 //
-// Operands reach LDS by DMA (global_load_lds_dwordx4: a wave instruction lands
-// 64 x 16 bytes contiguously, here 16 rows of a 64-byte k-slice) through a ring
-// of ORING slots, three stages in flight, so no registers hold them and the
-// global latency is covered three stages deep.  Rows are unpadded; the 16-byte
-// chunk c of row r sits at position c ^ swz(r), which lets any 16 consecutive
-// rows read one chunk without bank conflicts (each lane fetches the chunk that
-// belongs at its position).
-constexpr int OBM = 256, OBK = 64, ONT = 512, ORING = 4;
+// Each stage (64 k) of an operand is one contiguous 16 KiB block of the tiled
+// plane layout, already in the order LDS wants: each wave copies 4 KiB of it
+// with 16-byte loads into registers two stages ahead, and stores them to a
+// double-buffered LDS slot one stage ahead.  The 64 x 128 wave tile needs 6
+// 16-byte LDS reads per 8 matrix instructions; the 16-byte chunk c of block row
+// rho sits at position c ^ swz(rho), so 16 consecutive rows read one chunk
+// without bank conflicts.
+constexpr int OBM = 256, OBK = 64, ONT = 512;
+constexpr int kOzBlock = OBM * OBK;             // bytes of one stage of one operand
+constexpr int kOzEpiRow = 272;                  // LDS row stride of the output tile
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 
 __device__ inline int swz(int r) { return (r >> 2) & 3; }
+
+// Byte offset of element (row, k) in a plane of the tiled layout: blocks of
+// 256 rows x 64 bytes, block (row / 256, k / 64) at index (row / 256) (Kp / 64)
+// + k / 64, rows of 64 bytes inside, chunk c of row rho at position c ^ swz(rho).
+__device__ inline int64_t poff(int64_t row, int64_t k, int64_t Kp)
+{
+    return ((((row >> 8) * (Kp >> 6)) + (k >> 6)) << 14) + ((row & 255) << 6) +
+           ((((k >> 4) & 3) ^ ((row >> 2) & 3)) << 4) + (k & 15);
+}
 
 constexpr int kXcd = 8;
 constexpr int64_t kGroup = 4;
@@ -151,54 +162,47 @@ __device__ inline void lower_tile(int64_t l, int64_t nt, int64_t &ti, int64_t &t
     }
 }
 
-// One DMA instruction: each lane's 16 bytes at gptr land at LDS byte address
-// lds + 16 * lane.  Issued from asm so that the compiler adds no waits of its
-// own (it cannot tell the ring's slots apart); the waits below are explicit.
-// The instruction writes no register.
-__device__ inline void dma16(const int8_t *gptr, const int8_t *lds)
-{
-    typedef __attribute__((address_space(3))) const void lds_cvoid;
-    const unsigned addr = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)(lds_cvoid *)lds);
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-                 :
-                 : "v"(gptr), "s"(addr)
-                 : "memory", "m0");
-}
+// Waits with an immediate: lgkmcnt(0) only (vmcnt and expcnt left at their
+// maxima), so that loads in flight to registers are not waited for.
+constexpr int kWaitLgkm0 = 0xC07F;
 
 __global__ __launch_bounds__(ONT, 1) void oz_gemm_kernel(const int8_t *__restrict__ RA,
                                                         const int8_t *__restrict__ RB, int64_t Kp,
                                                         uint8_t *__restrict__ Cres, OzConst c)
 {
     extern __shared__ __attribute__((aligned(1024))) int8_t oz_lds[];
-    int8_t *As = oz_lds;                               // [ORING][OBM * OBK]
-    int8_t *Bs = oz_lds + ORING * OBM * OBK;
+    int8_t *As = oz_lds;                               // [2][kOzBlock]
+    int8_t *Bs = oz_lds + 2 * kOzBlock;                // [2][kOzBlock]
     const int r = blockIdx.y;
     const int64_t nt = Kp / OBM;
     int64_t ti, tj;
     lower_tile(xcd_logical(blockIdx.x, gridDim.x), nt, ti, tj);
     const int64_t i0 = ti * OBM, j0 = tj * OBM;
     const int64_t plane = Kp * Kp;
+    const int64_t nk = Kp / OBK;                      // a multiple of 4
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wr = wave >> 1, wc = wave & 1;          // 4 x 2 waves of 64 x 128
-    // DMA roles: wave w copies rows 32 w .. 32 w + 31 of both operands (two
-    // instructions each); lane l of an instruction covering rows 16 h' .. 16 h' + 15
-    // lands at row 16 h' + l / 4, position l % 4, and fetches chunk (l % 4) ^ swz(row)
-    const int8_t *ga[2], *gb[2];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        const int row = 32 * wave + 16 * h + (lane >> 2);
-        const int chunk = (lane & 3) ^ swz(row);
-        ga[h] = RA + r * plane + (i0 + row) * Kp + 16 * chunk;
-        gb[h] = RB + r * plane + (j0 + row) * Kp + 16 * chunk;
-    }
-    auto issue = [&](int64_t kt, int slot) {
-        const int64_t kb = kt * OBK;
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            dma16(ga[h] + kb, As + slot * OBM * OBK + (32 * wave + 16 * h) * OBK);
-            dma16(gb[h] + kb, Bs + slot * OBM * OBK + (32 * wave + 16 * h) * OBK);
-        }
+    const int woff = 2048 * wave + 16 * lane;         // this lane's bytes of a block: woff, woff + 1024
+    const int8_t *ga = RA + r * plane + ((ti * (Kp / OBK)) << 14) + woff;
+    const int8_t *gb = RB + r * plane + ((tj * (Kp / OBK)) << 14) + woff;
+
+    v4i g[2][4];
+    auto gload = [&](auto P, int64_t kt) {
+        constexpr int p = decltype(P)::value;
+        const int64_t kb = kt * kOzBlock;
+        g[p][0] = *(const v4i *)(ga + kb);
+        g[p][1] = *(const v4i *)(gb + kb);
+        g[p][2] = *(const v4i *)(ga + kb + 1024);
+        g[p][3] = *(const v4i *)(gb + kb + 1024);
+    };
+    auto lstore = [&](auto P, int slot) {
+        constexpr int p = decltype(P)::value;
+        int8_t *a0 = As + slot * kOzBlock + woff, *b0 = Bs + slot * kOzBlock + woff;
+        *(v4i *)a0 = g[p][0];
+        *(v4i *)b0 = g[p][1];
+        *(v4i *)(a0 + 1024) = g[p][2];
+        *(v4i *)(b0 + 1024) = g[p][3];
     };
 
     v16i acc[2][4];
@@ -209,7 +213,7 @@ __global__ __launch_bounds__(ONT, 1) void oz_gemm_kernel(const int8_t *__restric
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[bi][bj][e] = 0;
 
-    // MFMA read offsets (bytes within a slot) for the two k32 halves of a stage
+    // LDS read offsets (bytes within a slot) for the two k32 halves of a stage
     const int m = lane & 31;
     int offa[2][2], offb[2][4];
 #pragma unroll
@@ -227,26 +231,17 @@ __global__ __launch_bounds__(ONT, 1) void oz_gemm_kernel(const int8_t *__restric
         }
     }
 
-    const int64_t nk = Kp / OBK;
-    // waits: vmcnt(n) = at most n of this wave's vector memory operations
-    // outstanding (in-order completion), with lgkmcnt(0) so that this wave's LDS
-    // reads are done before the barrier frees their slot.  Immediate layout:
-    // vmcnt 3:0, expcnt 6:4 (7 = no wait), lgkmcnt 11:8.
-    issue(0, 0);
-    if (nk > 1) issue(1, 1);
-    if (nk > 2) issue(2, 2);
-    for (int64_t kt = 0; kt < nk; ++kt) {
-        const int slot = (int)(kt & (ORING - 1));
-        const int64_t later = (nk - 1 - kt) < 2 ? (nk - 1 - kt) : 2;      // stages issued after kt
-        if (later == 2) __builtin_amdgcn_s_waitcnt(0x0078);
-        else if (later == 1) __builtin_amdgcn_s_waitcnt(0x0074);
-        else __builtin_amdgcn_s_waitcnt(0x0070);
-        __builtin_amdgcn_s_barrier();                 // stage kt is in LDS, slot kt-1 is free
+    // Stage kt: the barrier publishes stage kt (stored in LDS during stage kt - 1)
+    // and frees the other slot (read during stage kt - 1).  The registers of
+    // parity 1 - p hold stage kt + 1 (loaded during stage kt - 2): they go to
+    // LDS, then receive stage kt + 3.  The flags are compile-time so that the
+    // loop body has no branches and the compiler's wait counts stay exact.
+    auto step = [&](auto P, auto STORE, auto LOAD, int64_t kt) {
+        constexpr int p = decltype(P)::value;
+        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+        __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
-        if (kt + 3 < nk) issue(kt + 3, (slot + 3) & (ORING - 1));
-        const int8_t *Aq = As + slot * OBM * OBK, *Bq = Bs + slot * OBM * OBK;
-        // both k32 halves' operands are read at once, so the second half's LDS
-        // latency hides behind the first half's matrix instructions
+        const int8_t *Aq = As + p * kOzBlock, *Bq = Bs + p * kOzBlock;
         v4i a[2][2], b[2][4];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
@@ -255,36 +250,81 @@ __global__ __launch_bounds__(ONT, 1) void oz_gemm_kernel(const int8_t *__restric
 #pragma unroll
             for (int bb = 0; bb < 4; ++bb) b[h][bb] = *(const v4i *)(Bq + offb[h][bb]);
         }
-        __builtin_amdgcn_sched_barrier(0);              // keep all twelve reads ahead of the MFMAs
+        if constexpr (decltype(STORE)::value) lstore(std::integral_constant<int, 1 - p>{}, 1 - p);
+        if constexpr (decltype(LOAD)::value) gload(std::integral_constant<int, 1 - p>{}, kt + 3);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int h = 0; h < 2; ++h)
 #pragma unroll
             for (int bi = 0; bi < 2; ++bi)
 #pragma unroll
                 for (int bj = 0; bj < 4; ++bj)
-                    acc[bi][bj] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[h][bi], b[h][bj], acc[bi][bj], 0, 0, 0);
+                    acc[bi][bj] = __builtin_amdgcn_mfma_i32_32x32x32_i8(b[h][bj], a[h][bi], acc[bi][bj], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using Y = std::true_type;
+    using N = std::false_type;
+    gload(I0{}, 0);
+    lstore(I0{}, 0);
+    gload(I1{}, 1);
+    gload(I0{}, 2);
+    for (int64_t kt = 0; kt < nk - 4; kt += 2) {
+        step(I0{}, Y{}, Y{}, kt);
+        step(I1{}, Y{}, Y{}, kt + 1);
     }
+    step(I0{}, Y{}, Y{}, nk - 4);
+    step(I1{}, Y{}, N{}, nk - 3);
+    step(I0{}, Y{}, N{}, nk - 2);
+    step(I1{}, N{}, N{}, nk - 1);
 
-    // residue mod m in [0, m): the fp64 quotient of |P| < 2^31 by m < 2^9 is
-    // nowhere near an integer boundary it could round across, so floor is exact
-    const double md = (double)c.m[r], im = c.inv_m[r];
-    uint8_t *out = Cres + r * plane;
+    // Residues mod m in [0, m), 4 columns to a dword, through LDS to 16-byte
+    // row stores.  |P| <= K 2^14 < 2^30: the fp32 quotient is within 1 of
+    // P / m, so q is floor(P / m) or one off, |q| < 2^23 (an exact 24-bit
+    // product), and one correction each way lands in [0, m).  Diagonal tiles
+    // are written whole: entries above the diagonal are residues of the
+    // symmetric product too.
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    const int mi = c.m[r];
+    const float invm = 1.0f / (float)mi;
 #pragma unroll
     for (int bi = 0; bi < 2; ++bi)
 #pragma unroll
         for (int bj = 0; bj < 4; ++bj)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int64_t gi = i0 + wr * 64 + bi * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-                const int64_t gj = j0 + wc * 128 + bj * 32 + m;
-                const double p = (double)acc[bi][bj][e];
-                const double q = floor(p * im);
-                const int res = (int)fma(-md, q, p);
-                if (gi >= gj) out[gi * Kp + gj] = (uint8_t)res;
+            for (int q = 0; q < 4; ++q) {
+                unsigned w = 0;
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    const int pv = acc[bi][bj][4 * q + t];
+                    const int qq = (int)floorf((float)pv * invm);
+                    int res = pv - __mul24(qq, mi);
+                    res += res < 0 ? mi : 0;
+                    res -= res >= mi ? mi : 0;
+                    w |= (unsigned)res << (8 * t);
+                }
+                const int li = wr * 64 + bi * 32 + m;
+                const int lj = wc * 128 + bj * 32 + 8 * q + 4 * (lane >> 5);
+                *(unsigned *)(oz_lds + li * kOzEpiRow + lj) = w;
             }
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    uint8_t *out = Cres + r * plane + i0 * Kp + j0;
+#pragma unroll
+    for (int u = 0; u < OBM * OBM / 16 / ONT; ++u) {
+        const int cidx = tid + ONT * u;
+        const int row = cidx >> 4, col = 16 * (cidx & 15);
+        *(v4i *)(out + row * Kp + col) = *(const v4i *)(oz_lds + row * kOzEpiRow + col);
+    }
 }
 
-constexpr size_t kOzGemmLds = (size_t)2 * ORING * OBM * OBK;      // 128 KiB
+// dynamic LDS: the output tile (68 KiB) outlasts the two-slot ring (64 KiB)
+constexpr size_t kOzGemmLds = (size_t)OBM * kOzEpiRow;
+static_assert(kOzGemmLds >= (size_t)4 * kOzBlock, "LDS ring");
 
 // ---------------------------------------------------------------- CRT
 // One 64 x 64 lower tile per workgroup: reconstruct sum_k a_ik b_jk from its
@@ -434,7 +474,7 @@ __global__ __launch_bounds__(CNT) void oz_crt_kernel(GemmDesc d, const uint8_t *
                 w |= ((unsigned)centred_residue(z[rr][t], m, c.inv_m[r], hi, lo) & 0xFFu) << (8 * t);
             const int li = rr * 16 + lr;
             rt[li][c4 >> 2] = w;
-            if (i0 + li < K) *(unsigned *)(pl + (i0 + li) * Kp + j0 + c4) = w;
+            if (i0 + li < K) *(unsigned *)(pl + poff(i0 + li, j0 + c4, Kp)) = w;
         }
         if (!diag) {
             __syncthreads();
@@ -445,7 +485,7 @@ __global__ __launch_bounds__(CNT) void oz_crt_kernel(GemmDesc d, const uint8_t *
                 unsigned w = 0;
 #pragma unroll
                 for (int t = 0; t < 4; ++t) w |= ((rt[c4 + t][li >> 2] >> (8 * (li & 3))) & 0xFFu) << (8 * t);
-                if (j0 + li < K) *(unsigned *)(pl + (j0 + li) * Kp + i0 + c4) = w;
+                if (j0 + li < K) *(unsigned *)(pl + poff(j0 + li, i0 + c4, Kp)) = w;
             }
             __syncthreads();
         }
