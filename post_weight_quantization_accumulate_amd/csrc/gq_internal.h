@@ -97,9 +97,7 @@ constexpr int kOzMods = 14;
 struct OzConst {
     int m[kOzMods];
     double inv_m[kOzMods];
-    unsigned long long w_lo[kOzMods], w_hi[kOzMods];   // CRT weights W_r = (M/m_r) ((M/m_r)^-1 mod m_r)
     unsigned long long M_lo, M_hi;                     // M = prod m_r
-    double invMd;
 };
 struct OzOperand {
     const int8_t *planes;

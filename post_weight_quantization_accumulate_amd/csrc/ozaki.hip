@@ -33,15 +33,84 @@ constexpr int kMods[kOzMods] = {256, 255, 253, 251, 247, 241, 239, 233, 229, 227
 typedef unsigned __int128 u128;
 typedef __int128 i128;
 
+// The reconstruction's constants, at compile time: M = prod m_r and the weights
+// W_r = (M / m_r) ((M / m_r)^-1 mod m_r) (so that sum_r c_r W_r = x mod M for
+// the residues c_r of x), each as 7 limbs of 16 bits (M < 2^111), which keeps
+// every limb product c_r w below 2^24 (a full-rate 24-bit multiply).
+constexpr int kLimbs = 7;
+struct OzLimbs {
+    unsigned short w[kOzMods][kLimbs];
+    unsigned short M[kLimbs];
+    double invM;
+};
+constexpr u128 oz_modulus()
+{
+    u128 M = 1;
+    for (int r = 0; r < kOzMods; ++r) M *= (u128)kMods[r];
+    return M;
+}
+constexpr OzLimbs oz_limbs()
+{
+    OzLimbs L{};
+    const u128 M = oz_modulus();
+    for (int r = 0; r < kOzMods; ++r) {
+        const u128 Mr = M / (u128)kMods[r];
+        const int t = (int)(Mr % (u128)kMods[r]);
+        int y = 1;
+        while ((t * y) % kMods[r] != 1) ++y;
+        const u128 W = Mr * (u128)y;                    // y < m_r, so W < M
+        for (int k = 0; k < kLimbs; ++k) L.w[r][k] = (unsigned short)(W >> (16 * k));
+    }
+    for (int k = 0; k < kLimbs; ++k) L.M[k] = (unsigned short)(M >> (16 * k));
+    L.invM = 1.0 / ((double)(unsigned long long)(M >> 64) * 18446744073709551616.0 +
+                    (double)(unsigned long long)M);
+    return L;
+}
+constexpr u128 kOzM = oz_modulus();
+struct OzInv { double v[kOzMods]; };
+constexpr OzInv oz_inverses()
+{
+    OzInv t{};
+    for (int r = 0; r < kOzMods; ++r) t.v[r] = 1.0 / (double)kMods[r];
+    return t;
+}
+constexpr OzInv kOzInv = oz_inverses();
+constexpr OzLimbs kOzLimbs = oz_limbs();
+static_assert((kOzM >> (16 * kLimbs - 1)) == 0, "M fits the limbs");
+
+// sum_k D[k] 2^(16 k) for signed limbs |D[k]| < 2^31
+__device__ inline i128 from_signed_limbs(const int (&D)[kLimbs])
+{
+    // two's complement sums in unsigned arithmetic (wrapping, shifts defined)
+    const unsigned long long p0 = (unsigned long long)(long long)D[0] + ((unsigned long long)(long long)D[1] << 16);
+    const unsigned long long p1 = (unsigned long long)(long long)D[2] + ((unsigned long long)(long long)D[3] << 16);
+    const unsigned long long p2 = (unsigned long long)(long long)D[4] + ((unsigned long long)(long long)D[5] << 16);
+    const u128 x = (u128)(i128)(long long)p0 + ((u128)(i128)(long long)p1 << 32) + ((u128)(i128)(long long)p2 << 64) +
+                   ((u128)(i128)D[6] << 96);
+    return (i128)x;
+}
+
+// Residue of the integer z (|z| <= 2^48) modulo kMods[r], as the int8 byte the
+// products use.  Odd m: the fp64 quotient z (1/m) is within 2^-11.6 of z / m,
+// which lies at least 1/(2m) > 2^-9 from a half-integer, so rint gives the
+// nearest integer and z - m rint(z / m) is the centred residue, exactly (fma).
+// m = 256: z - 256 floor(z / 256) in [0, 256), whose low byte is the two's
+// complement residue.
+__device__ inline unsigned residue_byte(double z, int r)
+{
+    if (r == 0) return (unsigned)(int)fma(-256.0, floor(z * (1.0 / 256.0)), z) & 0xFFu;
+    const double m = (double)kMods[r];
+    return (unsigned)(int)fma(-m, rint(z * kOzInv.v[r]), z) & 0xFFu;
+}
+
 // ---------------------------------------------------------------- split
 constexpr int SPL_NT = 256;
 
-__device__ inline int centred_residue(double z, double m, double inv_m, double hi, double lo);
 __device__ inline int64_t poff(int64_t row, int64_t k, int64_t Kp);
 
 __global__ __launch_bounds__(SPL_NT) void oz_split_kernel(const double *__restrict__ Z, int64_t K, int64_t Kp,
                                                           int beta, int8_t *__restrict__ planes,
-                                                          int *__restrict__ rowexp, OzConst c)
+                                                          int *__restrict__ rowexp)
 {
     __shared__ double red[SPL_NT / 64];
     __shared__ int e_sh;
@@ -77,12 +146,10 @@ __global__ __launch_bounds__(SPL_NT) void oz_split_kernel(const double *__restri
         for (int t = 0; t < 8; ++t) z[t] = (k0 + t < K) ? rint(zr[k0 + t] * sc) : 0.0;   // exact integers
 #pragma unroll
         for (int r = 0; r < kOzMods; ++r) {
-            const double m = (double)c.m[r];
-            const double hi = (double)((c.m[r] - 1) / 2), lo = -(double)(c.m[r] / 2);
             unsigned w0 = 0, w1 = 0;
 #pragma unroll
             for (int t = 0; t < 8; ++t) {
-                const unsigned b = (unsigned)centred_residue(z[t], m, c.inv_m[r], hi, lo) & 0xFFu;
+                const unsigned b = residue_byte(z[t], r);
                 if (t < 4) w0 |= b << (8 * t); else w1 |= b << (8 * (t - 4));
             }
             *(uint2 *)(planes + r * plane + poff(i, k0, Kp)) = make_uint2(w0, w1);
@@ -337,21 +404,10 @@ static_assert(kOzGemmLds >= (size_t)4 * kOzBlock, "LDS ring");
 // would break the bound the reconstruction relies on and sets ST_RANGE.
 constexpr int CT = 64, CNT = 256;
 
-// Residue of the integer z (|z| <= 2^53) modulo m, centred into int8 range.
-__device__ inline int centred_residue(double z, double m, double inv_m, double hi, double lo)
-{
-    // z - m rint(z / m) is exact (|q m| < 2^53) and within one m of the centred
-    // residue; one correction each way centres it
-    const double q = rint(z * inv_m);
-    double rr = fma(-m, q, z);
-    rr = rr > hi ? rr - m : rr;
-    rr = rr < lo ? rr + m : rr;
-    return (int)rr;
-}
 
 template <typename OutT>
 __global__ __launch_bounds__(CNT) void oz_crt_kernel(GemmDesc d, const uint8_t *__restrict__ Cres, int64_t Kp,
-                                                    OzOperand A, OzOperand B, int twobeta, OzConst c, OzOut o,
+                                                    OzOperand A, OzOperand B, int twobeta, OzOut o,
                                                     int beta, unsigned *status)
 {
     const int *__restrict__ ea = A.rowexp;
@@ -359,7 +415,6 @@ __global__ __launch_bounds__(CNT) void oz_crt_kernel(GemmDesc d, const uint8_t *
     int8_t *__restrict__ planes = o.planes;
     const double bound = ldexp(1.0, o.exp);
     __shared__ double tile[CT][CT + 1];
-    __shared__ unsigned rt[CT][CT / 4 + 1];            // one modulus' residue bytes of the tile
     const int64_t K = d.M;
     int64_t ti = 0, tj = 0;
     {
@@ -377,48 +432,49 @@ __global__ __launch_bounds__(CNT) void oz_crt_kernel(GemmDesc d, const uint8_t *
     if (d.alpha_dev) { for (int p = 0; p < d.alpha_pow; ++p) alpha *= *d.alpha_dev; }
     if (d.beta_dev) { for (int p = 0; p < d.beta_pow; ++p) beta_c *= *d.beta_dev; }
     const double *cin = (const double *)d.cin;
-    const u128 Mq = ((u128)c.M_hi << 64) | c.M_lo;
     const int64_t plane = Kp * Kp;
     const int tid = threadIdx.x;
     // thread -> 4 consecutive columns c4 .. c4+3 of rows lr, lr+16, lr+32, lr+48
     const int lr = tid >> 4, c4 = 4 * (tid & 15);
     bool range_bad = false;
-#pragma unroll 1
-    for (int rr = 0; rr < CT / 16; ++rr) {
-        const int li = rr * 16 + lr;
-        const int64_t gi = i0 + li;
-        // residues of 4 consecutive outputs: one dword per plane (Kp is a multiple
-        // of 256, j0 + c4 of 4: aligned)
-        unsigned rs[kOzMods];
-        const bool row_in = gi < K;
-        const uint8_t *p = Cres + (row_in ? gi : 0) * Kp + j0 + c4;
+    // residues of 4 consecutive outputs of row li = 16 rr + lr: one dword per
+    // plane (Kp is a multiple of 256, j0 + c4 of 4: aligned)
+    auto load_row = [&](unsigned (&rs)[kOzMods], int rr) {
+        const int64_t gi = i0 + rr * 16 + lr;
+        const uint8_t *p = Cres + (gi < K ? gi : 0) * Kp + j0 + c4;
 #pragma unroll
         for (int r = 0; r < kOzMods; ++r) rs[r] = *(const unsigned *)(p + r * plane);
+    };
+    auto do_row = [&](const unsigned (&rs)[kOzMods], int rr) {
+        const int li = rr * 16 + lr;
+        const int64_t gi = i0 + li;
+        const bool row_in = gi < K;
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             const int64_t gj = j0 + c4 + t;
             double v = 0.0;
             if (row_in && gj < K && gi >= gj) {
-                // S = sum_r c_r W_r by 32-bit limbs of W_r: each limb sum is below
-                // 14 * 255 * 2^32 < 2^44, one carry pass assembles the 128 bits
-                unsigned long long L0 = 0, L1 = 0, L2 = 0, L3 = 0;
+                // S = sum_r c_r W_r by 16-bit limbs of W_r: each limb sum is below
+                // 14 * 255 * 2^16 < 2^28
+                unsigned L[kLimbs] = {0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
                 for (int r = 0; r < kOzMods; ++r) {
-                    const unsigned long long cr = (rs[r] >> (8 * t)) & 0xFFu;
-                    L0 += cr * (unsigned)c.w_lo[r];
-                    L1 += cr * (unsigned)(c.w_lo[r] >> 32);
-                    L2 += cr * (unsigned)c.w_hi[r];
-                    L3 += cr * (unsigned)(c.w_hi[r] >> 32);
+                    const unsigned cr = (rs[r] >> (8 * t)) & 0xFFu;
+#pragma unroll
+                    for (int k = 0; k < kLimbs; ++k) L[k] = __umul24(cr, kOzLimbs.w[r][k]) + L[k];
                 }
-                const u128 S = (u128)L0 + ((u128)L1 << 32) + ((u128)L2 << 64) + ((u128)L3 << 96);
-                // S < 14 * 255 * M: q = floor(S / M) from a double estimate, then
-                // an exact correction of at most one step each way
-                const double Sd = ldexp((double)(unsigned long long)(S >> 64), 64) + (double)(unsigned long long)S;
-                const unsigned long long q = (unsigned long long)floor(Sd * c.invMd);
-                i128 x = (i128)S - (i128)((u128)q * Mq);
-                if (x < 0) x += (i128)Mq;
-                if (x >= (i128)Mq) x -= (i128)Mq;
-                if (x > (i128)(Mq >> 1)) x -= (i128)Mq;      // centred: the signed integer sum
+                // The centred value is x = S - q M with q the integer nearest S / M:
+                // |x| <= K 2^(2 beta) < 0.497 M (the choice of beta), and the fp64
+                // estimate of S / M < 2^12 is within 2^-38 of it.  x by signed limbs
+                // L[k] - q M[k] (q M[k] < 2^28), one carry pass in 128 bits.
+                double Sd = (double)L[kLimbs - 1];
+#pragma unroll
+                for (int k = kLimbs - 2; k >= 0; --k) Sd = fma(Sd, 65536.0, (double)L[k]);
+                const int nq = -(int)rint(Sd * kOzLimbs.invM);
+                int D[kLimbs];
+#pragma unroll
+                for (int k = 0; k < kLimbs; ++k) D[k] = __mul24(nq, (int)kOzLimbs.M[k]) + (int)L[k];
+                const i128 x = from_signed_limbs(D);
                 const double xd = ldexp((double)(long long)(x >> 64), 64) + (double)(unsigned long long)x;
                 const int e = (ea ? ea[gi] : A.exp) + (eb ? eb[gj] : B.exp);
                 v = alpha * ldexp(xd, e - twobeta);
@@ -428,6 +484,12 @@ __global__ __launch_bounds__(CNT) void oz_crt_kernel(GemmDesc d, const uint8_t *
             }
             tile[li][c4 + t] = v;
         }
+    };
+#pragma unroll 1
+    for (int rr = 0; rr < CT / 16; ++rr) {
+        unsigned rs[kOzMods];
+        load_row(rs, rr);
+        do_row(rs, rr);
     }
     __syncthreads();
     OutT *out = (OutT *)d.out;
@@ -446,11 +508,12 @@ __global__ __launch_bounds__(CNT) void oz_crt_kernel(GemmDesc d, const uint8_t *
     }
     if (!planes) return;
     if (range_bad) atomicOr(status, ST_RANGE);
-    // Split form of the symmetric output at exponent 1, one modulus at a time:
-    // each element's residue is computed once into rt, then written to rows
-    // i0.. (this block) and, off the diagonal, transposed to rows j0.. (the
-    // mirror).  On the diagonal tile, entries above its diagonal come from
-    // their mirror.  Entries past K are 0 and keep the padding zero.
+    // Split form of the symmetric output at exponent o.exp: each element's
+    // residues are computed once, written to rows i0.. (this block) and, off the
+    // diagonal, staged in LDS (7 moduli at a time, in the space of the fp64
+    // tile) and written transposed to rows j0.. (the mirror).  On the diagonal
+    // tile, entries above its diagonal come from their mirror.  Entries past K
+    // are 0 and keep the padding zero.
     const double sc = ldexp(1.0, beta - o.exp);
     double z[4][4];
 #pragma unroll
@@ -461,34 +524,42 @@ __global__ __launch_bounds__(CNT) void oz_crt_kernel(GemmDesc d, const uint8_t *
             const double v = (diag && cc > li) ? tile[cc][li] : tile[li][cc];
             z[rr][t] = rint(v * sc);
         }
+    constexpr int kHalf = kOzMods / 2;
+    static_assert(sizeof(unsigned) * kHalf * CT * (CT / 4 + 1) <= sizeof(double) * CT * (CT + 1), "LDS reuse");
+    unsigned (*rt)[CT][CT / 4 + 1] = reinterpret_cast<unsigned (*)[CT][CT / 4 + 1]>(&tile[0][0]);
+    __syncthreads();                    // the fp64 tile is no longer read
 #pragma unroll 1
-    for (int r = 0; r < kOzMods; ++r) {
-        const double m = (double)c.m[r];
-        const double hi = (double)((c.m[r] - 1) / 2), lo = -(double)(c.m[r] / 2);
-        int8_t *pl = planes + r * plane;
+    for (int half = 0; half < 2; ++half) {
+#pragma unroll 1
+        for (int q = 0; q < kHalf; ++q) {
+            const int r = kHalf * half + q;
+            int8_t *pl = planes + r * plane;
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-            unsigned w = 0;
+            for (int rr = 0; rr < 4; ++rr) {
+                unsigned w = 0;
 #pragma unroll
-            for (int t = 0; t < 4; ++t)
-                w |= ((unsigned)centred_residue(z[rr][t], m, c.inv_m[r], hi, lo) & 0xFFu) << (8 * t);
-            const int li = rr * 16 + lr;
-            rt[li][c4 >> 2] = w;
-            if (i0 + li < K) *(unsigned *)(pl + poff(i0 + li, j0 + c4, Kp)) = w;
+                for (int t = 0; t < 4; ++t) w |= residue_byte(z[rr][t], r) << (8 * t);
+                const int li = rr * 16 + lr;
+                rt[q][li][c4 >> 2] = w;
+                if (i0 + li < K) *(unsigned *)(pl + poff(i0 + li, j0 + c4, Kp)) = w;
+            }
         }
-        if (!diag) {
-            __syncthreads();
-            // mirror rows j0 + li: bytes (i0 + c4 + t) come from rt[c4 + t][li]
+        if (diag) continue;
+        __syncthreads();
+        // mirror rows j0 + li: bytes (i0 + c4 + t) come from rt[q][c4 + t][li]
+#pragma unroll 1
+        for (int q = 0; q < kHalf; ++q) {
+            int8_t *pl = planes + (kHalf * half + q) * plane;
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) {
                 const int li = rr * 16 + lr;
                 unsigned w = 0;
 #pragma unroll
-                for (int t = 0; t < 4; ++t) w |= ((rt[c4 + t][li >> 2] >> (8 * (li & 3))) & 0xFFu) << (8 * t);
+                for (int t = 0; t < 4; ++t) w |= ((rt[q][c4 + t][li >> 2] >> (8 * (li & 3))) & 0xFFu) << (8 * t);
                 if (j0 + li < K) *(unsigned *)(pl + poff(j0 + li, i0 + c4, Kp)) = w;
             }
-            __syncthreads();
         }
+        __syncthreads();
     }
 }
 
@@ -498,51 +569,18 @@ __global__ void zero16_kernel(uint4 *p, int64_t n16)
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride) p[i] = make_uint4(0u, 0u, 0u, 0u);
 }
 
-u128 mulmod(u128 a, u128 b, u128 m)
-{
-    // a, b < m < 2^112: double-and-add (host only, once)
-    u128 r = 0;
-    a %= m;
-    while (b) {
-        if (b & 1) r = (r + a) % m;
-        a = (a << 1) % m;
-        b >>= 1;
-    }
-    return r;
-}
-
-int inv_mod_small(int64_t a, int64_t m)
-{
-    int64_t t = 0, nt = 1, r = m, nr = ((a % m) + m) % m;
-    while (nr) {
-        const int64_t q = r / nr;
-        int64_t x = t - q * nt; t = nt; nt = x;
-        x = r - q * nr; r = nr; nr = x;
-    }
-    return (int)((t % m + m) % m);
-}
-
 }  // namespace
 
 const OzConst &oz_const()
 {
     static OzConst c = [] {
         OzConst k{};
-        u128 M = 1;
-        for (int r = 0; r < kOzMods; ++r) M *= (u128)kMods[r];
         for (int r = 0; r < kOzMods; ++r) {
             k.m[r] = kMods[r];
             k.inv_m[r] = 1.0 / (double)kMods[r];
-            const u128 Mr = M / (u128)kMods[r];
-            const int inv = inv_mod_small((int64_t)(Mr % (u128)kMods[r]), kMods[r]);
-            const u128 w = mulmod(Mr, (u128)inv, M);
-            k.w_lo[r] = (unsigned long long)w;
-            k.w_hi[r] = (unsigned long long)(w >> 64);
         }
-        k.M_lo = (unsigned long long)M;
-        k.M_hi = (unsigned long long)(M >> 64);
-        const double Md = ldexp((double)k.M_hi, 64) + (double)k.M_lo;
-        k.invMd = 1.0 / Md;
+        k.M_lo = (unsigned long long)kOzM;
+        k.M_hi = (unsigned long long)(kOzM >> 64);
         return k;
     }();
     return c;
@@ -550,10 +588,12 @@ const OzConst &oz_const()
 
 int oz_beta(int64_t K)
 {
-    // largest beta with K 2^(2 beta) < M / 2, i.e. 2 beta < log2 M - 1 - log2 K
+    // largest beta with K 2^(2 beta) <= 0.497 M, i.e. 2 beta <= log2 M - 1.01 - log2 K:
+    // the reconstruction rounds S / M to the nearest integer and needs the
+    // centred sum to stay clear of M / 2
     const OzConst &c = oz_const();
     const double log2M = std::log2(ldexp((double)c.M_hi, 64) + (double)c.M_lo);
-    const double room = log2M - 1.0 - std::log2((double)(K > 1 ? K : 1)) - 1e-9;
+    const double room = log2M - 1.01 - std::log2((double)(K > 1 ? K : 1));
     return (int)std::floor(room / 2.0);
 }
 
@@ -568,8 +608,7 @@ size_t oz_planes_bytes(int64_t K)
 hipError_t oz_split(const double *Z, int64_t K, int beta, int8_t *planes, int *rowexp, hipStream_t s)
 {
     const int64_t Kp = oz_padded(K);
-    hipLaunchKernelGGL(oz_split_kernel, dim3((unsigned)Kp), dim3(SPL_NT), 0, s, Z, K, Kp, beta, planes, rowexp,
-                       oz_const());
+    hipLaunchKernelGGL(oz_split_kernel, dim3((unsigned)Kp), dim3(SPL_NT), 0, s, Z, K, Kp, beta, planes, rowexp);
     return hipGetLastError();
 }
 
@@ -594,10 +633,10 @@ hipError_t oz_product(const GemmDesc &d, const OzOperand &A, const OzOperand &B,
     const int64_t ct = (K + CT - 1) / CT;
     if (out_f32)
         hipLaunchKernelGGL(oz_crt_kernel<float>, dim3((unsigned)(ct * (ct + 1) / 2)), dim3(CNT), 0, s, d, Cres, Kp,
-                           A, B, 2 * beta, oz_const(), o, beta, status);
+                           A, B, 2 * beta, o, beta, status);
     else
         hipLaunchKernelGGL(oz_crt_kernel<double>, dim3((unsigned)(ct * (ct + 1) / 2)), dim3(CNT), 0, s, d, Cres, Kp,
-                           A, B, 2 * beta, oz_const(), o, beta, status);
+                           A, B, 2 * beta, o, beta, status);
     return hipGetLastError();
 }
 
