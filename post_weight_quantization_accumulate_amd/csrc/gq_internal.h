@@ -32,6 +32,50 @@ enum : unsigned {
     ST_RANGE = 8u,       // an emulated product's output left the range its split form needs
 };
 
+// Tile order of the large-tile kernels.  Workgroups are dispatched round-robin
+// over the chip's 8 XCDs (workgroup w runs on XCD w % 8, each with its own L2):
+// xcd_order gives each XCD a contiguous range of logical tile indices, and
+// lower_tile_grouped walks the lower triangle (ti >= tj) of an nt x nt grid in
+// groups of kTileGroup tile rows, so tiles that run together on one XCD share
+// their row and column panels in its L2.
+constexpr int kXcds = 8;
+constexpr int64_t kTileGroup = 4;
+
+__device__ inline int64_t xcd_order(int64_t w, int64_t n)
+{
+    const int64_t x = w % kXcds, j = w / kXcds;
+    int64_t base = 0;
+    for (int64_t y = 0; y < x; ++y) base += (n - y + kXcds - 1) / kXcds;
+    return base + j;
+}
+
+__device__ inline void lower_tile_grouped(int64_t l, int64_t nt, int64_t &ti, int64_t &tj)
+{
+    int64_t g = 0, start = 0;
+    for (;;) {
+        const int64_t r0 = g * kTileGroup;
+        const int64_t r1 = (r0 + kTileGroup < nt) ? r0 + kTileGroup : nt;
+        const int64_t cnt = (r1 * (r1 + 1) - r0 * (r0 + 1)) / 2;
+        if (l < start + cnt) {
+            int64_t off = l - start;
+            const int64_t full = r0 * (r1 - r0);
+            if (off < full) {
+                tj = off / (r1 - r0);
+                ti = r0 + off % (r1 - r0);
+            } else {
+                off -= full;
+                int64_t cc = r0;
+                while (off >= r1 - cc) { off -= r1 - cc; ++cc; }
+                tj = cc;
+                ti = cc + off;
+            }
+            return;
+        }
+        start += cnt;
+        ++g;
+    }
+}
+
 // Which output tiles a GEMM launch computes.
 enum TileMode : int { TILE_RECT = 0, TILE_LOWER = 1, TILE_UPPER = 2 };
 

@@ -4,19 +4,26 @@
 // tokens, and chunk sums add (hipfire-calib-data, "Hessian storage"; AtomicChat
 // GGUF page, "The importance matrix").  Products of two bf16 values are exact
 // in fp32; each launch accumulates its chunk in fp32 registers from zero and adds
-// the result to H once, so streaming many chunks rounds once per chunk.
+// the result to H once, so streaming many chunks rounds once per chunk and the
+// result does not depend on scheduling.
 //
-// Layout problem: v_mfma_f32_32x32x16_bf16 wants, per lane, 8 consecutive k
-// values (tokens) of one output row (channel), but X is token-major.  Each
-// thread therefore loads a 4-token x 8-channel patch with four 16-byte row
-// loads, regroups it in registers into eight 4-token words and stores those to
-// an LDS panel laid out [channel][token]; the MFMA operands are then single
-// 16-byte LDS reads.  The token order inside a lane is irrelevant to the sum
-// as long as A and B use the same one, which they do (same panel layout).
+// One workgroup per lower 256 x 256 tile (tile order as in the int8 product:
+// XCD-contiguous, grouped by tile rows), 8 waves of 64 x 128 (4 x 2), each 2 x 4
+// blocks of v_mfma_f32_32x32x16_bf16.  The instruction computes X Y^T for
+// 32-row panels X and Y of 16 k: lane l feeds k = 8 (l / 32) + 0..7 of row
+// l % 32 of each, and result e of lane l is (X Y^T)[8 (e/4) + 4 (l/32) + e%4][l % 32].
 //
-// Only lower tiles (ti >= tj) are launched; a diagonal tile reads one panel for
-// both operands.  128 x 128 tiles, 256 threads (2 x 2 waves of 64 x 64), 32
-// tokens per LDS stage, double-buffered.
+// X is token-major, the instruction wants 8 consecutive tokens of one channel
+// per lane: the transpose happens on the way into LDS.  A stage is 32 tokens;
+// each of the 256 loader threads of a panel loads a 4-token x 8-channel patch
+// (four 16-byte loads, two stages ahead into registers) and stores 8 words of
+// 4 tokens, one per channel.  A panel in LDS is 256 rows of 64 bytes (32
+// tokens); channel rho lives in physical row 32 (rho % 8) + rho / 8 and its
+// 16-byte token chunk c at position c ^ (rho % 4) ^ (rho / 64 % 4).  A wave
+// loads 2 token rows x 512 bytes per instruction (X rows are far apart, so
+// wide contiguous segments keep many L2 channels busy); with that placement its
+// 8-byte stores of one channel index spread over all banks, and so do the
+// 16-byte matrix-operand reads of 32 consecutive channels.
 #include "gq_internal.h"
 
 namespace gq {
@@ -26,54 +33,65 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int BM = 128, BKT = 32, NT = 256;
-constexpr int PITCH = BKT + 8;      // bf16 elements per LDS row (80 bytes)
+constexpr int GBM = 256;                    // tile edge (channels)
+constexpr int GBT = 32;                     // tokens per stage
+constexpr int GNT = 512;                    // threads
+constexpr int kPanelBytes = GBM * GBT * 2;  // 16 KiB
+// dynamic LDS: two slots of the A and B panels
+constexpr size_t kGramLds = (size_t)4 * kPanelBytes;
+// lgkmcnt(0) only: loads in flight to registers are not waited for
+constexpr int kWaitLgkm0 = 0xC07F;
 
-__device__ inline void tri_index(int64_t id, int64_t &ti, int64_t &tj)
+// VEC: K % 8 == 0 and X 16-byte aligned, so that every 8-channel octet is
+// wholly inside or wholly outside [0, K) and loads as one 16-byte word.
+template <bool VEC>
+__global__ __launch_bounds__(GNT, 1) void gram_bf16_kernel(float *__restrict__ H,
+                                                           const uint16_t *__restrict__ X,
+                                                           int64_t T, int64_t K)
 {
-    int64_t t = (int64_t)((sqrt(8.0 * (double)id + 1.0) - 1.0) * 0.5);
-    while (t * (t + 1) / 2 > id) --t;
-    while ((t + 1) * (t + 2) / 2 <= id) ++t;
-    ti = t;
-    tj = id - t * (t + 1) / 2;
-}
-
-__global__ __launch_bounds__(NT) void gram_bf16_kernel(float *__restrict__ H,
-                                                       const uint16_t *__restrict__ X,
-                                                       int64_t T, int64_t K, int vec)
-{
-    __shared__ __attribute__((aligned(16))) uint16_t Ps[2][2][BM][PITCH];  // [buf][panel][ch][tok]
-
+    extern __shared__ __attribute__((aligned(1024))) int8_t g_lds[];
+    const int64_t nt = (K + GBM - 1) / GBM;
     int64_t ti, tj;
-    tri_index(blockIdx.x, ti, tj);
-    const bool diag = (ti == tj);
-    const int64_t i0 = ti * BM, j0 = tj * BM;
+    lower_tile_grouped(xcd_order(blockIdx.x, gridDim.x), nt, ti, tj);
+    const int64_t i0 = ti * GBM, j0 = tj * GBM;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wr = wave >> 1, wc = wave & 1;
 
-    // loader role: threads 0..127 -> panel A (channels i0..), 128..255 -> panel B
-    const int panel = tid >> 7;
-    const int u = tid & 127;
-    const int q = u >> 4;          // token quad 0..7
-    const int o = u & 15;          // channel octet 0..15
+    // loader role: threads 0..255 -> panel A (channels i0..), 256..511 -> panel B
+    // (channels j0.., which on a diagonal tile are A's again); channels
+    // 8 o .. 8 o + 7, tokens 4 q .. 4 q + 3 of each stage
+    const int panel = tid >> 8, u = tid & 255;
+    const int o = u & 31, q = u >> 5;        // a wave instruction: 2 token rows x 512 bytes
     const int64_t cbase = (panel ? j0 : i0) + 8 * o;
-    const bool loader = !(diag && panel == 1);
+    // byte offset of this thread's patch from the start of its stage's first
+    // token row (below 2^32 for K < 2^24), and whether its octet is in range
+    const unsigned voff = (unsigned)((4 * q * K + cbase) * 2);
+    const bool c_in = cbase < K;
+    // Stages past T load zeros: the stage count is rounded up to an even
+    // number, at least 4, so that the pipeline below needs no run-time cases.
+    int64_t nk = (T + GBT - 1) / GBT;
+    nk += nk & 1;
+    if (nk < 4) nk = 4;
 
-    // Interior tiles and full token stages take unconditional 16-byte loads; the
-    // ragged edges load 16-bit elements from clamped addresses and zero the
-    // out-of-range ones with a select (no divergent branches around loads).
-    const bool full_c = vec && (i0 + BM <= K) && (j0 + BM <= K);
-    u32x4 v[4];
-    auto gload = [&](int64_t t0) {
-        if (!loader) return;
-        if (full_c && t0 + BKT <= T) {
+    u32x4 g[2][4];
+    auto gload = [&](auto P, int64_t kt) {
+        constexpr int p = decltype(P)::value;
+        const int64_t t0 = kt * GBT + 4 * q;
+        if constexpr (VEC) {
+            // out-of-range rows read X[0..7] and are replaced by zeros
+            const char *sb = (const char *)X + kt * GBT * K * 2;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) v[r] = *(const u32x4 *)(X + (t0 + 4 * q + r) * K + cbase);
+            for (int r = 0; r < 4; ++r) {
+                const bool ok = c_in && t0 + r < T;
+                const char *src = ok ? sb + (int64_t)r * K * 2 + voff : (const char *)X;
+                const u32x4 v = *(const u32x4 *)src;
+                g[p][r] = ok ? v : u32x4{0u, 0u, 0u, 0u};
+            }
         } else {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int64_t t = t0 + 4 * q + r;
+                const int64_t t = t0 + r;
                 unsigned w[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
@@ -83,75 +101,116 @@ __global__ __launch_bounds__(NT) void gram_bf16_kernel(float *__restrict__ H,
                     const unsigned hi = X[ok1 ? t * K + c0 + 1 : 0];
                     w[e] = (ok0 ? lo : 0u) | ((ok1 ? hi : 0u) << 16);
                 }
-                v[r] = u32x4{w[0], w[1], w[2], w[3]};
+                g[p][r] = u32x4{w[0], w[1], w[2], w[3]};
             }
         }
     };
-    auto sstore = [&](int buf) {
-        if (!loader) return;
-        // channel 8o + c gets tokens 4q..4q+3 as one 8-byte word
+    // channel rho = 8 o + c gets tokens 4 q .. 4 q + 3 as one 8-byte word, at
+    // byte 8 (q % 2) of chunk q / 2 of its row: physical row 32 c + o, chunk
+    // position (q / 2) ^ (c % 4) ^ (o / 8 % 4), i.e. byte 2048 c + sbase[c % 4]
+    int sbase[4];
+#pragma unroll
+    for (int x = 0; x < 4; ++x)
+        sbase[x] = panel * kPanelBytes + 64 * o + 16 * ((q >> 1) ^ x ^ ((o >> 3) & 3)) + 8 * (q & 1);
+    auto lstore = [&](auto P, auto SLOT) {
+        constexpr int p = decltype(P)::value;
+        int8_t *base = g_lds + 2 * decltype(SLOT)::value * kPanelBytes;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             // dword e of each token row holds channels 2e (low half) and 2e+1 (high half)
-            const unsigned a0 = v[0][e], a1 = v[1][e], a2 = v[2][e], a3 = v[3][e];
-            const unsigned lo_c0 = (a0 & 0xFFFFu) | (a1 << 16);
-            const unsigned hi_c0 = (a2 & 0xFFFFu) | (a3 << 16);
-            const unsigned lo_c1 = (a0 >> 16) | (a1 & 0xFFFF0000u);
-            const unsigned hi_c1 = (a2 >> 16) | (a3 & 0xFFFF0000u);
-            uint2 *p0 = (uint2 *)&Ps[buf][panel][8 * o + 2 * e][4 * q];
-            uint2 *p1 = (uint2 *)&Ps[buf][panel][8 * o + 2 * e + 1][4 * q];
-            *p0 = make_uint2(lo_c0, hi_c0);
-            *p1 = make_uint2(lo_c1, hi_c1);
+            const unsigned a0 = g[p][0][e], a1 = g[p][1][e], a2 = g[p][2][e], a3 = g[p][3][e];
+            const uint2 w0 = make_uint2((a0 & 0xFFFFu) | (a1 << 16), (a2 & 0xFFFFu) | (a3 << 16));
+            const uint2 w1 = make_uint2((a0 >> 16) | (a1 & 0xFFFF0000u), (a2 >> 16) | (a3 & 0xFFFF0000u));
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int c = 2 * e + h;
+                *(uint2 *)(base + 2048 * c + sbase[c & 3]) = h ? w1 : w0;
+            }
         }
     };
 
-    f32x16 acc[2][2];
-#pragma unroll
-    for (int a = 0; a < 2; ++a)
-#pragma unroll
-        for (int b = 0; b < 2; ++b)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.0f;
-
-    const int pb = diag ? 0 : 1;
-    const int64_t nk = (T + BKT - 1) / BKT;
-    if (nk > 0) {
-        gload(0);
-        sstore(0);
-        __syncthreads();
-        for (int64_t kt = 0; kt < nk; ++kt) {
-            const int buf = (int)(kt & 1);
-            if (kt + 1 < nk) gload((kt + 1) * BKT);
-#pragma unroll
-            for (int kh = 0; kh < 2; ++kh) {
-                const int tok = 16 * kh + 8 * (lane >> 5);
-                bf16x8 a[2], b[2];
-#pragma unroll
-                for (int bi = 0; bi < 2; ++bi)
-                    a[bi] = *(const bf16x8 *)&Ps[buf][0][wr * 64 + bi * 32 + (lane & 31)][tok];
-#pragma unroll
-                for (int bj = 0; bj < 2; ++bj)
-                    b[bj] = *(const bf16x8 *)&Ps[buf][pb][wc * 64 + bj * 32 + (lane & 31)][tok];
-#pragma unroll
-                for (int bi = 0; bi < 2; ++bi)
-#pragma unroll
-                    for (int bj = 0; bj < 2; ++bj)
-                        acc[bi][bj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[bi], b[bj], acc[bi][bj], 0, 0, 0);
-            }
-            if (kt + 1 < nk) sstore(buf ^ 1);
-            __syncthreads();
-        }
-    }
-
+    f32x16 acc[2][4];
 #pragma unroll
     for (int bi = 0; bi < 2; ++bi)
 #pragma unroll
-        for (int bj = 0; bj < 2; ++bj)
+        for (int bj = 0; bj < 4; ++bj)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int64_t gi = i0 + wr * 64 + bi * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-                const int64_t gj = j0 + wc * 64 + bj * 32 + (lane & 31);
-                if (gi < K && gj < K && gi >= gj) H[gi * K + gj] += acc[bi][bj][r];
+            for (int e = 0; e < 16; ++e) acc[bi][bj][e] = 0.0f;
+
+    // operand read offsets (bytes within a panel) for the two k16 halves of a
+    // stage: channel rho = r0 + 32 bb + m (r0 a multiple of 32) sits in physical
+    // row 32 (m % 8) + r0 / 8 + 4 bb + m / 8, chunk ch at position
+    // ch ^ (m % 4) ^ (rho / 64 % 4).  A wave's A rows share rho / 64 = wr; its B
+    // rows have rho / 64 = 2 wc + bb / 2.
+    const int m = lane & 31;
+    int offa[2], offb[2][2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int ch = 2 * h + (lane >> 5);
+        const int row = 64 * (32 * (m & 7) + (m >> 3));
+        offa[h] = row + 16 * (ch ^ (m & 3) ^ wr) + 512 * wr;
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb)
+            offb[h][hb] = row + 16 * (ch ^ (m & 3) ^ ((2 * wc + hb) & 3)) + 1024 * wc + 512 * hb;
+    }
+
+    // Stage kt: the barrier publishes stage kt (stored during stage kt - 1) and
+    // frees the other slot (read during stage kt - 1).  Registers of parity
+    // 1 - p hold stage kt + 1 (loaded during stage kt - 2): they go to LDS, then
+    // receive stage kt + 3.
+    auto step = [&](auto P, auto STORE, auto LOAD, int64_t kt) {
+        constexpr int p = decltype(P)::value;
+        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        const int8_t *Aq = g_lds + (2 * p) * kPanelBytes, *Bq = g_lds + (2 * p + 1) * kPanelBytes;
+        bf16x8 a[2][2], b[2][4];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+#pragma unroll
+            for (int bb = 0; bb < 2; ++bb) a[h][bb] = *(const bf16x8 *)(Aq + offa[h] + 256 * bb);
+#pragma unroll
+            for (int bb = 0; bb < 4; ++bb) b[h][bb] = *(const bf16x8 *)(Bq + offb[h][bb >> 1] + 256 * (bb & 1));
+        }
+        if constexpr (decltype(STORE)::value) lstore(std::integral_constant<int, 1 - p>{}, std::integral_constant<int, 1 - p>{});
+        if constexpr (decltype(LOAD)::value) gload(std::integral_constant<int, 1 - p>{}, kt + 3);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+                for (int bj = 0; bj < 4; ++bj)
+                    acc[bi][bj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[h][bi], b[h][bj], acc[bi][bj], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using Y = std::true_type;
+    using N = std::false_type;
+    gload(I0{}, 0);
+    lstore(I0{}, I0{});
+    gload(I1{}, 1);
+    gload(I0{}, 2);
+    for (int64_t kt = 0; kt < nk - 4; kt += 2) {
+        step(I0{}, Y{}, Y{}, kt);
+        step(I1{}, Y{}, Y{}, kt + 1);
+    }
+    step(I0{}, Y{}, Y{}, nk - 4);
+    step(I1{}, Y{}, N{}, nk - 3);
+    step(I0{}, Y{}, N{}, nk - 2);
+    step(I1{}, N{}, N{}, nk - 1);
+
+    // H += acc on the lower triangle
+#pragma unroll
+    for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+        for (int bj = 0; bj < 4; ++bj)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int64_t gi = i0 + wr * 64 + bi * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+                const int64_t gj = j0 + wc * 128 + bj * 32 + m;
+                if (gi < K && gj < K && gi >= gj) H[gi * K + gj] += acc[bi][bj][e];
             }
 }
 
@@ -160,10 +219,18 @@ __global__ __launch_bounds__(NT) void gram_bf16_kernel(float *__restrict__ H,
 hipError_t launch_gram_bf16(float *H, const uint16_t *X, int64_t T, int64_t K, hipStream_t s)
 {
     if (T <= 0 || K <= 0) return hipSuccess;
-    const int64_t nt = (K + BM - 1) / BM;
-    const int vec = (K % 8 == 0) && (((uintptr_t)X & 15) == 0);
-    hipLaunchKernelGGL(gram_bf16_kernel, dim3((unsigned)(nt * (nt + 1) / 2)), dim3(NT), 0, s, H, X,
-                       T, K, vec);
+    static const bool lds_ok =
+        hipFuncSetAttribute((const void *)gram_bf16_kernel<true>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)kGramLds) == hipSuccess &&
+        hipFuncSetAttribute((const void *)gram_bf16_kernel<false>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)kGramLds) == hipSuccess;
+    if (!lds_ok) return hipErrorInvalidConfiguration;
+    const int64_t nt = (K + GBM - 1) / GBM;
+    const dim3 grid((unsigned)(nt * (nt + 1) / 2));
+    if ((K % 8 == 0) && (((uintptr_t)X & 15) == 0))
+        hipLaunchKernelGGL(gram_bf16_kernel<true>, grid, dim3(GNT), kGramLds, s, H, X, T, K);
+    else
+        hipLaunchKernelGGL(gram_bf16_kernel<false>, grid, dim3(GNT), kGramLds, s, H, X, T, K);
     return hipGetLastError();
 }
 

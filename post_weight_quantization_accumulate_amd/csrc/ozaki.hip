@@ -190,45 +190,6 @@ __device__ inline int64_t poff(int64_t row, int64_t k, int64_t Kp)
            ((((k >> 4) & 3) ^ ((row >> 2) & 3)) << 4) + (k & 15);
 }
 
-constexpr int kXcd = 8;
-constexpr int64_t kGroup = 4;
-
-__device__ inline int64_t xcd_logical(int64_t w, int64_t n)
-{
-    const int64_t x = w % kXcd, j = w / kXcd;
-    int64_t base = 0;
-    for (int64_t y = 0; y < x; ++y) base += (n - y + kXcd - 1) / kXcd;
-    return base + j;
-}
-
-// Lower triangle (ti >= tj) of an nt x nt grid, grouped by kGroup tile rows.
-__device__ inline void lower_tile(int64_t l, int64_t nt, int64_t &ti, int64_t &tj)
-{
-    int64_t g = 0, start = 0;
-    for (;;) {
-        const int64_t r0 = g * kGroup;
-        const int64_t r1 = (r0 + kGroup < nt) ? r0 + kGroup : nt;
-        const int64_t cnt = (r1 * (r1 + 1) - r0 * (r0 + 1)) / 2;
-        if (l < start + cnt) {
-            int64_t off = l - start;
-            const int64_t full = r0 * (r1 - r0);
-            if (off < full) {
-                tj = off / (r1 - r0);
-                ti = r0 + off % (r1 - r0);
-            } else {
-                off -= full;
-                int64_t cc = r0;
-                while (off >= r1 - cc) { off -= r1 - cc; ++cc; }
-                tj = cc;
-                ti = cc + off;
-            }
-            return;
-        }
-        start += cnt;
-        ++g;
-    }
-}
-
 // Waits with an immediate: lgkmcnt(0) only (vmcnt and expcnt left at their
 // maxima), so that loads in flight to registers are not waited for.
 constexpr int kWaitLgkm0 = 0xC07F;
@@ -243,7 +204,7 @@ __global__ __launch_bounds__(ONT, 1) void oz_gemm_kernel(const int8_t *__restric
     const int r = blockIdx.y;
     const int64_t nt = Kp / OBM;
     int64_t ti, tj;
-    lower_tile(xcd_logical(blockIdx.x, gridDim.x), nt, ti, tj);
+    lower_tile_grouped(xcd_order(blockIdx.x, gridDim.x), nt, ti, tj);
     const int64_t i0 = ti * OBM, j0 = tj * OBM;
     const int64_t plane = Kp * Kp;
     const int64_t nk = Kp / OBK;                      // a multiple of 4
