@@ -16,7 +16,7 @@
 // X is token-major, the instruction wants 8 consecutive tokens of one channel
 // per lane: the transpose happens on the way into LDS.  A stage is 32 tokens;
 // each of the 256 loader threads of a panel loads a 4-token x 8-channel patch
-// (four 16-byte loads, two stages ahead into registers) and stores 8 words of
+// (four 16-byte loads, three stages ahead into registers) and stores 8 words of
 // 4 tokens, one per channel.  A panel in LDS is 256 rows of 64 bytes (32
 // tokens); channel rho lives in physical row 32 (rho % 8) + rho / 8 and its
 // 16-byte token chunk c at position c ^ (rho % 4) ^ (rho / 64 % 4).  A wave
@@ -68,25 +68,25 @@ __global__ __launch_bounds__(GNT, 1) void gram_bf16_kernel(float *__restrict__ H
     // token row (below 2^32 for K < 2^24), and whether its octet is in range
     const unsigned voff = (unsigned)((4 * q * K + cbase) * 2);
     const bool c_in = cbase < K;
-    // Stages past T load zeros: the stage count is rounded up to an even
-    // number, at least 4, so that the pipeline below needs no run-time cases.
-    int64_t nk = (T + GBT - 1) / GBT;
-    nk += nk & 1;
-    if (nk < 4) nk = 4;
+    // Stages past T load zeros: the stage count is rounded up to a multiple of
+    // 6 (the pipeline's period), so that the pipeline below needs no run-time cases.
+    const int64_t nk = ((T + GBT - 1) / GBT + 5) / 6 * 6 > 0 ? ((T + GBT - 1) / GBT + 5) / 6 * 6 : 6;
 
-    u32x4 g[2][4];
+    u32x4 g[3][4];
     auto gload = [&](auto P, int64_t kt) {
         constexpr int p = decltype(P)::value;
         const int64_t t0 = kt * GBT + 4 * q;
         if constexpr (VEC) {
-            // out-of-range rows read X[0..7] and are replaced by zeros
-            const char *sb = (const char *)X + kt * GBT * K * 2;
+            // Address = uniform row base (clamped into X) + per-thread byte
+            // offset; out-of-range rows read the first 8 channels of a valid row
+            // and lstore replaces them by zeros (a select here would wait for
+            // the load at once).
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const bool ok = c_in && t0 + r < T;
-                const char *src = ok ? sb + (int64_t)r * K * 2 + voff : (const char *)X;
-                const u32x4 v = *(const u32x4 *)src;
-                g[p][r] = ok ? v : u32x4{0u, 0u, 0u, 0u};
+                const int64_t row = kt * GBT + r < T ? kt * GBT + r : T - 1;
+                const char *sb = (const char *)X + row * K * 2;
+                const unsigned off = (c_in && t0 + r < T) ? voff : 0u;
+                g[p][r] = *(const u32x4 *)(sb + off);
             }
         } else {
 #pragma unroll
@@ -112,9 +112,14 @@ __global__ __launch_bounds__(GNT, 1) void gram_bf16_kernel(float *__restrict__ H
 #pragma unroll
     for (int x = 0; x < 4; ++x)
         sbase[x] = panel * kPanelBytes + 64 * o + 16 * ((q >> 1) ^ x ^ ((o >> 3) & 3)) + 8 * (q & 1);
-    auto lstore = [&](auto P, auto SLOT) {
+    auto lstore = [&](auto P, auto SLOT, int64_t kt) {
         constexpr int p = decltype(P)::value;
         int8_t *base = g_lds + 2 * decltype(SLOT)::value * kPanelBytes;
+        if constexpr (VEC) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                if (!(c_in && kt * GBT + 4 * q + r < T)) g[p][r] = u32x4{0u, 0u, 0u, 0u};
+        }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             // dword e of each token row holds channels 2e (low half) and 2e+1 (high half)
@@ -155,51 +160,70 @@ __global__ __launch_bounds__(GNT, 1) void gram_bf16_kernel(float *__restrict__ H
     }
 
     // Stage kt: the barrier publishes stage kt (stored during stage kt - 1) and
-    // frees the other slot (read during stage kt - 1).  Registers of parity
-    // 1 - p hold stage kt + 1 (loaded during stage kt - 2): they go to LDS, then
-    // receive stage kt + 3.
-    auto step = [&](auto P, auto STORE, auto LOAD, int64_t kt) {
-        constexpr int p = decltype(P)::value;
+    // frees the other LDS slot (read during stage kt - 1).  Register set
+    // (kt + 1) % 3 holds stage kt + 1 (loaded during stage kt - 3): it goes to
+    // LDS, then receives stage kt + 4, so global loads have three stages to
+    // land.  The operands of the two k16 halves are read one half at a time
+    // (the second while the first half's matrix instructions run).  P (LDS
+    // parity), S (register set) and the flags are compile-time, so that the
+    // loop body has no branches and the compiler's wait counts stay exact.
+    auto step = [&](auto P, auto S, auto STORE, auto LOAD, int64_t kt) {
+        constexpr int p = decltype(P)::value, sset = decltype(S)::value;
         __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
         const int8_t *Aq = g_lds + (2 * p) * kPanelBytes, *Bq = g_lds + (2 * p + 1) * kPanelBytes;
-        bf16x8 a[2][2], b[2][4];
+        bf16x8 a[2], b[4];
+        auto rd = [&](int h) {
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
+            for (int bb = 0; bb < 2; ++bb) a[bb] = *(const bf16x8 *)(Aq + offa[h] + 256 * bb);
 #pragma unroll
-            for (int bb = 0; bb < 2; ++bb) a[h][bb] = *(const bf16x8 *)(Aq + offa[h] + 256 * bb);
-#pragma unroll
-            for (int bb = 0; bb < 4; ++bb) b[h][bb] = *(const bf16x8 *)(Bq + offb[h][bb >> 1] + 256 * (bb & 1));
-        }
-        if constexpr (decltype(STORE)::value) lstore(std::integral_constant<int, 1 - p>{}, std::integral_constant<int, 1 - p>{});
-        if constexpr (decltype(LOAD)::value) gload(std::integral_constant<int, 1 - p>{}, kt + 3);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
+            for (int bb = 0; bb < 4; ++bb) b[bb] = *(const bf16x8 *)(Bq + offb[h][bb >> 1] + 256 * (bb & 1));
+        };
+        auto mm = [&]() {
 #pragma unroll
             for (int bi = 0; bi < 2; ++bi)
 #pragma unroll
                 for (int bj = 0; bj < 4; ++bj)
-                    acc[bi][bj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[h][bi], b[h][bj], acc[bi][bj], 0, 0, 0);
+                    acc[bi][bj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[bi], b[bj], acc[bi][bj], 0, 0, 0);
+        };
+        rd(0);
+        if constexpr (decltype(STORE)::value)
+            lstore(std::integral_constant<int, sset>{}, std::integral_constant<int, 1 - p>{}, kt + 1);
+        if constexpr (decltype(LOAD)::value) gload(std::integral_constant<int, sset>{}, kt + 4);
+        __builtin_amdgcn_sched_barrier(0);
+        mm();
+        __builtin_amdgcn_sched_barrier(0);
+        rd(1);
+        __builtin_amdgcn_sched_barrier(0);
+        mm();
         __builtin_amdgcn_sched_barrier(0);
     };
-    using I0 = std::integral_constant<int, 0>;
-    using I1 = std::integral_constant<int, 1>;
     using Y = std::true_type;
     using N = std::false_type;
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
     gload(I0{}, 0);
-    lstore(I0{}, I0{});
     gload(I1{}, 1);
-    gload(I0{}, 2);
-    for (int64_t kt = 0; kt < nk - 4; kt += 2) {
-        step(I0{}, Y{}, Y{}, kt);
-        step(I1{}, Y{}, Y{}, kt + 1);
+    gload(I2{}, 2);
+    lstore(I0{}, I0{}, 0);
+    gload(I0{}, 3);
+    // stage kt uses LDS parity kt % 2 and register set (kt + 1) % 3: a period of 6
+    for (int64_t kt = 0; kt < nk - 6; kt += 6) {
+        step(I0{}, I1{}, Y{}, Y{}, kt);
+        step(I1{}, I2{}, Y{}, Y{}, kt + 1);
+        step(I0{}, I0{}, Y{}, Y{}, kt + 2);
+        step(I1{}, I1{}, Y{}, Y{}, kt + 3);
+        step(I0{}, I2{}, Y{}, Y{}, kt + 4);
+        step(I1{}, I0{}, Y{}, Y{}, kt + 5);
     }
-    step(I0{}, Y{}, Y{}, nk - 4);
-    step(I1{}, Y{}, N{}, nk - 3);
-    step(I0{}, Y{}, N{}, nk - 2);
-    step(I1{}, N{}, N{}, nk - 1);
+    step(I0{}, I1{}, Y{}, Y{}, nk - 6);
+    step(I1{}, I2{}, Y{}, Y{}, nk - 5);
+    step(I0{}, I0{}, Y{}, N{}, nk - 4);
+    step(I1{}, I1{}, Y{}, N{}, nk - 3);
+    step(I0{}, I2{}, Y{}, N{}, nk - 2);
+    step(I1{}, I0{}, N{}, N{}, nk - 1);
 
     // H += acc on the lower triangle
 #pragma unroll
