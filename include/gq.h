@@ -135,10 +135,10 @@ int gq_set_psd_products(int kind);
  * fix"; required before Cholesky on stored Hessians).  Computed on the device
  * without an eigendecomposition, as P = (H + sign(H) H) / 2 with sign(H) from a
  * scaled Newton-Schulz iteration.  For K < 65536 its symmetric products are
- * fp64 products emulated exactly in integers on the int8 matrix cores (row
- * scaling to 47-48-bit integers, residues modulo 14 moduli, Chinese remainder
- * reconstruction: relative rounding 2^-47 per entry); above that, fp64 matrix
- * core products.
+ * computed exactly in integers on the int8 matrix cores from operands rounded
+ * to 51-52-bit integers (one power-of-two scale per row; residues modulo 15
+ * moduli, Chinese remainder reconstruction, one rounding to fp64); above that,
+ * fp64 matrix core products.
  *   H   K x K fp32; the lower triangle is read, the full symmetric result is
  *       written in place.
  *   ws  device workspace of at least psd_project_workspace_size(K) bytes.

@@ -20,24 +20,25 @@
 //      residues, since |sum| <= K 2^(2 beta) < M / 2, M = prod m_r; it is then
 //      scaled back and rounded to fp64 once.
 // The only rounding is the truncation of step 1 (relative 2^-beta per entry of
-// the row's scale) and the final conversion, beta = 47..48 at the sizes of the
-// path.  The 14 int8 products run at the int8 matrix rate, 64 times the fp64 one.
+// the row's scale) and the final conversion; with 15 moduli (M ~ 2^117.8) beta
+// is 52 at K = 5120 and 51 at K = 17408.  The 15 int8 products run at the int8
+// matrix rate, 64 times the fp64 one.
 #include "gq_internal.h"
 
 namespace gq {
 
 namespace {
 
-constexpr int kMods[kOzMods] = {256, 255, 253, 251, 247, 241, 239, 233, 229, 227, 223, 217, 211, 199};
+constexpr int kMods[kOzMods] = {256, 255, 253, 251, 247, 241, 239, 233, 229, 227, 223, 217, 211, 199, 197};
 
 typedef unsigned __int128 u128;
 typedef __int128 i128;
 
 // The reconstruction's constants, at compile time: M = prod m_r and the weights
 // W_r = (M / m_r) ((M / m_r)^-1 mod m_r) (so that sum_r c_r W_r = x mod M for
-// the residues c_r of x), each as 7 limbs of 16 bits (M < 2^111), which keeps
+// the residues c_r of x), each as 8 limbs of 16 bits (M < 2^118), which keeps
 // every limb product c_r w below 2^24 (a full-rate 24-bit multiply).
-constexpr int kLimbs = 7;
+constexpr int kLimbs = 8;
 struct OzLimbs {
     unsigned short w[kOzMods][kLimbs];
     unsigned short M[kLimbs];
@@ -85,22 +86,26 @@ __device__ inline i128 from_signed_limbs(const int (&D)[kLimbs])
     const unsigned long long p0 = (unsigned long long)(long long)D[0] + ((unsigned long long)(long long)D[1] << 16);
     const unsigned long long p1 = (unsigned long long)(long long)D[2] + ((unsigned long long)(long long)D[3] << 16);
     const unsigned long long p2 = (unsigned long long)(long long)D[4] + ((unsigned long long)(long long)D[5] << 16);
+    const unsigned long long p3 = (unsigned long long)(long long)D[6] + ((unsigned long long)(long long)D[7] << 16);
     const u128 x = (u128)(i128)(long long)p0 + ((u128)(i128)(long long)p1 << 32) + ((u128)(i128)(long long)p2 << 64) +
-                   ((u128)(i128)D[6] << 96);
+                   ((u128)(i128)(long long)p3 << 96);
     return (i128)x;
 }
 
-// Residue of the integer z (|z| <= 2^48) modulo kMods[r], as the int8 byte the
-// products use.  Odd m: the fp64 quotient z (1/m) is within 2^-11.6 of z / m,
-// which lies at least 1/(2m) > 2^-9 from a half-integer, so rint gives the
-// nearest integer and z - m rint(z / m) is the centred residue, exactly (fma).
-// m = 256: z - 256 floor(z / 256) in [0, 256), whose low byte is the two's
-// complement residue.
+// Residue of the integer z (|z| <= 2^52) modulo kMods[r], as the int8 byte the
+// products use.  Odd m: the fp64 quotient z (1/m) is within 2^-7 of z / m, so
+// its rint is within one of the integer nearest z / m; z - m rint(z (1/m)) is
+// exact (fma) and one correction each way centres it in [-(m-1)/2, (m-1)/2].
+// m = 256: z - 256 floor(z / 256) in [0, 256) (exact), whose low byte is the
+// two's complement residue.
 __device__ inline unsigned residue_byte(double z, int r)
 {
     if (r == 0) return (unsigned)(int)fma(-256.0, floor(z * (1.0 / 256.0)), z) & 0xFFu;
-    const double m = (double)kMods[r];
-    return (unsigned)(int)fma(-m, rint(z * kOzInv.v[r]), z) & 0xFFu;
+    const int m = kMods[r], h = (kMods[r] - 1) / 2;
+    int v = (int)fma(-(double)m, rint(z * kOzInv.v[r]), z);
+    v -= v > h ? m : 0;
+    v += v < -h ? m : 0;
+    return (unsigned)v & 0xFFu;
 }
 
 // ---------------------------------------------------------------- split
@@ -416,8 +421,8 @@ __global__ __launch_bounds__(CNT) void oz_crt_kernel(GemmDesc d, const uint8_t *
             double v = 0.0;
             if (row_in && gj < K && gi >= gj) {
                 // S = sum_r c_r W_r by 16-bit limbs of W_r: each limb sum is below
-                // 14 * 255 * 2^16 < 2^28
-                unsigned L[kLimbs] = {0, 0, 0, 0, 0, 0, 0};
+                // 15 * 255 * 2^16 < 2^28
+                unsigned L[kLimbs] = {};
 #pragma unroll
                 for (int r = 0; r < kOzMods; ++r) {
                     const unsigned cr = (rs[r] >> (8 * t)) & 0xFFu;
@@ -471,7 +476,7 @@ __global__ __launch_bounds__(CNT) void oz_crt_kernel(GemmDesc d, const uint8_t *
     if (range_bad) atomicOr(status, ST_RANGE);
     // Split form of the symmetric output at exponent o.exp: each element's
     // residues are computed once, written to rows i0.. (this block) and, off the
-    // diagonal, staged in LDS (7 moduli at a time, in the space of the fp64
+    // diagonal, staged in LDS (5 moduli at a time, in the space of the fp64
     // tile) and written transposed to rows j0.. (the mirror).  On the diagonal
     // tile, entries above its diagonal come from their mirror.  Entries past K
     // are 0 and keep the padding zero.
@@ -485,15 +490,16 @@ __global__ __launch_bounds__(CNT) void oz_crt_kernel(GemmDesc d, const uint8_t *
             const double v = (diag && cc > li) ? tile[cc][li] : tile[li][cc];
             z[rr][t] = rint(v * sc);
         }
-    constexpr int kHalf = kOzMods / 2;
-    static_assert(sizeof(unsigned) * kHalf * CT * (CT / 4 + 1) <= sizeof(double) * CT * (CT + 1), "LDS reuse");
+    constexpr int kBatch = 5;
+    static_assert(kOzMods % kBatch == 0, "whole batches");
+    static_assert(sizeof(unsigned) * kBatch * CT * (CT / 4 + 1) <= sizeof(double) * CT * (CT + 1), "LDS reuse");
     unsigned (*rt)[CT][CT / 4 + 1] = reinterpret_cast<unsigned (*)[CT][CT / 4 + 1]>(&tile[0][0]);
     __syncthreads();                    // the fp64 tile is no longer read
 #pragma unroll 1
-    for (int half = 0; half < 2; ++half) {
+    for (int batch = 0; batch < kOzMods / kBatch; ++batch) {
 #pragma unroll 1
-        for (int q = 0; q < kHalf; ++q) {
-            const int r = kHalf * half + q;
+        for (int q = 0; q < kBatch; ++q) {
+            const int r = kBatch * batch + q;
             int8_t *pl = planes + r * plane;
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) {
@@ -509,8 +515,8 @@ __global__ __launch_bounds__(CNT) void oz_crt_kernel(GemmDesc d, const uint8_t *
         __syncthreads();
         // mirror rows j0 + li: bytes (i0 + c4 + t) come from rt[q][c4 + t][li]
 #pragma unroll 1
-        for (int q = 0; q < kHalf; ++q) {
-            int8_t *pl = planes + (kHalf * half + q) * plane;
+        for (int q = 0; q < kBatch; ++q) {
+            int8_t *pl = planes + (kBatch * batch + q) * plane;
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) {
                 const int li = rr * 16 + lr;
@@ -549,13 +555,15 @@ const OzConst &oz_const()
 
 int oz_beta(int64_t K)
 {
-    // largest beta with K 2^(2 beta) <= 0.497 M, i.e. 2 beta <= log2 M - 1.01 - log2 K:
-    // the reconstruction rounds S / M to the nearest integer and needs the
-    // centred sum to stay clear of M / 2
+    // largest beta with K 2^(2 beta) <= 0.497 M, i.e. 2 beta <= log2 M - 1.01 - log2 K
+    // (the reconstruction rounds S / M to the nearest integer and needs the
+    // centred sum to stay clear of M / 2), and at most 52, so that the split
+    // integers are exact in fp64 and residue_byte's quotient stays within one
     const OzConst &c = oz_const();
     const double log2M = std::log2(ldexp((double)c.M_hi, 64) + (double)c.M_lo);
     const double room = log2M - 1.01 - std::log2((double)(K > 1 ? K : 1));
-    return (int)std::floor(room / 2.0);
+    const int b = (int)std::floor(room / 2.0);
+    return b < 52 ? b : 52;
 }
 
 int64_t oz_padded(int64_t K) { return (K + OBM - 1) / OBM * OBM; }
