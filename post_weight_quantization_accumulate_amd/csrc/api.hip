@@ -21,8 +21,9 @@ thread_local std::string g_last_error;
 // the default priority and kept until the process ends.
 struct Lookahead {
     int dev = -1;
-    hipStream_t side = nullptr;
-    hipEvent_t to_side = nullptr, to_main = nullptr;
+    hipStream_t side = nullptr;                        // diagonal blocks of the Cholesky
+    hipStream_t inv = nullptr;                         // the triangular inverse, alongside
+    hipEvent_t to_side = nullptr, to_main = nullptr, to_inv = nullptr, inv_done = nullptr;
 };
 thread_local std::vector<Lookahead> g_lookahead;
 
@@ -36,8 +37,11 @@ hipError_t lookahead_for_current_device(Lookahead **out)
     Lookahead l;
     l.dev = dev;
     if ((e = hipStreamCreateWithFlags(&l.side, hipStreamNonBlocking)) != hipSuccess) return e;
+    if ((e = hipStreamCreateWithFlags(&l.inv, hipStreamNonBlocking)) != hipSuccess) return e;
     if ((e = hipEventCreateWithFlags(&l.to_side, hipEventDisableTiming)) != hipSuccess) return e;
     if ((e = hipEventCreateWithFlags(&l.to_main, hipEventDisableTiming)) != hipSuccess) return e;
+    if ((e = hipEventCreateWithFlags(&l.to_inv, hipEventDisableTiming)) != hipSuccess) return e;
+    if ((e = hipEventCreateWithFlags(&l.inv_done, hipEventDisableTiming)) != hipSuccess) return e;
     g_lookahead.push_back(l);
     *out = &g_lookahead.back();
     return hipSuccess;
@@ -290,6 +294,34 @@ int run_factor(float *U, const float *H, int64_t K, float damp, FactorWs &w, hip
     const int64_t nblk = (K + kPanel - 1) / kPanel;
     Lookahead *la = nullptr;
     GQ_HIP(lookahead_for_current_device(&la), "lookahead stream");
+    // The triangular inverse X = L^-1 (L = R^T, stored below M's diagonal) is
+    // built on a third stream while the factorisation proceeds, block row by
+    // block row from the top (right-looking forward substitution of L X = I,
+    // X starting as I): once panel p is solved, its column block of L is final,
+    // so X_p = L_pp^-1 X_p and then X_k -= L_kp X_p for the rows k below,
+    // restricted to the columns left of the next panel (X_p is zero beyond).
+    GQ_HIP(hipEventRecord(la->to_inv, s), "record");
+    GQ_HIP(hipStreamWaitEvent(la->inv, la->to_inv, 0), "wait");
+    GQ_HIP(launch_set_identity_f64(w.X, K, la->inv), "identity");
+    auto inverse_rows = [&](int64_t p) -> hipError_t {
+        const int64_t q0 = p * kPanel;
+        const int nbq = (int)((K - q0) < kPanel ? (K - q0) : kPanel);
+        const int64_t q1 = q0 + nbq;
+        hipError_t e = hipEventRecord(la->to_inv, s);
+        if (e == hipSuccess) e = hipStreamWaitEvent(la->inv, la->to_inv, 0);
+        if (e != hipSuccess) return e;
+        // X_p[a][c] = sum_b (L_pp^-1)[a][b] X_p[b][c], L_pp^-1 = Dinv_p^T; in place
+        // (each output tile reads its whole column range before writing it)
+        GemmDesc r = gemm(w.Dinv + p * kPanel * kPanel, nbq, w.X + q0 * K, K, nbq, q1, nbq, w.X + q0 * K, K);
+        e = gemm_tn_f64(r, la->inv);
+        if (e != hipSuccess || q1 >= K) return e;
+        // X_k -= L_kp X_p for rows k >= q1, columns < q1; L_kp[k][b] = R[q0 + b][k]
+        GemmDesc u = gemm(w.M + q0 * K + q1, K, w.X + q0 * K, K, K - q1, q1, nbq, w.X + q1 * K, K);
+        u.cin = w.X + q1 * K;
+        u.alpha = -1.0;
+        u.beta = 1.0;
+        return gemm_tn_f64(u, la->inv);
+    };
     // Right-looking blocked Cholesky with a look-ahead of one panel: once the
     // block row of panel p+1 has its update from panel p, the diagonal block
     // p+1 is factored on the side stream while the rest of the trailing update
@@ -302,11 +334,15 @@ int run_factor(float *U, const float *H, int64_t K, float damp, FactorWs &w, hip
         const int64_t p1 = p0 + nbp;
         const double *Dinv = w.Dinv + p * kPanel * kPanel;
         if (p > 0) GQ_HIP(hipStreamWaitEvent(s, la->to_main, 0), "wait diagonal block");
-        if (p1 >= K) break;
+        if (p1 >= K) {
+            GQ_HIP(inverse_rows(p), "inverse rows");
+            break;
+        }
         // panel rows: R_{p,rest} = R_pp^{-T} A_{p,rest}, mirrored below the diagonal
         GemmDesc t = gemm(Dinv, nbp, w.M + p0 * K + p1, K, nbp, K - p1, nbp, w.M + p0 * K + p1, K);
         t.out_t = w.M + p1 * K + p0;
         GQ_HIP(gemm_tn_f64(t, s), "trsm");
+        GQ_HIP(inverse_rows(p), "inverse rows");
         // trailing update of the upper triangle, A_rest -= R_{p,rest}^T R_{p,rest}:
         // first the block row of panel p+1 ...
         const int nbn = (int)((K - p1) < kPanel ? (K - p1) : kPanel);
@@ -336,23 +372,10 @@ int run_factor(float *U, const float *H, int64_t K, float damp, FactorWs &w, hip
             GQ_HIP(gemm_tn_f64(u, s), "syrk");
         }
     }
-    // X = R^{-1}, block rows from the bottom up
-    GQ_HIP(launch_set_identity_f64(w.X, K, s), "identity");
-    for (int64_t p = nblk - 1; p >= 0; --p) {
-        const int64_t q0 = p * kPanel;
-        const int nbq = (int)((K - q0) < kPanel ? (K - q0) : kPanel);
-        const double *DinvT = w.DinvT + p * kPanel * kPanel;
-        GemmDesc a = gemm(DinvT, nbq, w.X + q0 * K + q0, K, nbq, K - q0, nbq, w.X + q0 * K + q0, K);
-        GQ_HIP(gemm_tn_f64(a, s), "trtri row");
-        if (q0 > 0) {
-            GemmDesc b = gemm(w.M + q0 * K, K, w.X + q0 * K + q0, K, q0, K - q0, nbq, w.X + q0, K);
-            b.cin = w.X + q0;
-            b.alpha = -1.0;
-            b.beta = 1.0;
-            GQ_HIP(gemm_tn_f64(b, s), "trtri update");
-        }
-    }
-    GQ_HIP(launch_flip_transpose(U, w.X, K, s), "flip transpose");
+    GQ_HIP(hipEventRecord(la->inv_done, la->inv), "record");
+    GQ_HIP(hipStreamWaitEvent(s, la->inv_done, 0), "wait inverse");
+    // U = J R^-T J = J L^-1 J: U[i][j] = X[K-1-i][K-1-j]
+    GQ_HIP(launch_flip(U, w.X, K, s), "flip");
     return GQ_OK;
 }
 

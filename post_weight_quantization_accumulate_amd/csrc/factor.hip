@@ -431,25 +431,14 @@ __global__ __launch_bounds__(PNT) void potrf_diag_kernel(double *__restrict__ M,
     if (t == 0 && bad) atomicOr(status, ST_NOT_PD);
 }
 
-// U[i][j] = X[K-1-j][K-1-i] for i <= j, 0 below; transposed through LDS tiles.
-constexpr int TF = 32;
-__global__ __launch_bounds__(NT) void flip_transpose_kernel(float *__restrict__ U, const double *__restrict__ X,
-                                                           int64_t K)
+// U[i][j] = X[K-1-i][K-1-j] (as fp32) for i <= j, 0 below: the lower triangular
+// X turned by 180 degrees.
+__global__ __launch_bounds__(NT) void flip_kernel(float *__restrict__ U, const double *__restrict__ X, int64_t K)
 {
-    __shared__ double tile[TF][TF + 1];
-    const int64_t bi = blockIdx.y, bj = blockIdx.x;   // output tile (rows bi, cols bj)
-    const int c = threadIdx.x & 31, r0 = threadIdx.x >> 5;
-    // source rows a = K-1-j for j in the output column tile, cols b = K-1-i
-    for (int r = r0; r < TF; r += NT / TF) {
-        const int64_t j = bj * TF + r, i = bi * TF + c;
-        double v = 0.0;
-        if (i < K && j < K && i <= j) v = X[(K - 1 - j) * K + (K - 1 - i)];
-        tile[r][c] = v;          // tile[j - j0][i - i0]
-    }
-    __syncthreads();
-    for (int r = r0; r < TF; r += NT / TF) {
-        const int64_t i = bi * TF + r, j = bj * TF + c;
-        if (i < K && j < K) U[i * K + j] = (float)tile[c][r];
+    const int64_t n = K * K;
+    for (int64_t e = (int64_t)blockIdx.x * NT + threadIdx.x; e < n; e += (int64_t)gridDim.x * NT) {
+        const int64_t i = e / K, j = e - i * K;
+        U[e] = (i <= j) ? (float)X[(K - 1 - i) * K + (K - 1 - j)] : 0.0f;
     }
 }
 
@@ -529,10 +518,9 @@ hipError_t launch_potrf_diag(double *M, int64_t K, int64_t p0, int nb, double *D
     return hipGetLastError();
 }
 
-hipError_t launch_flip_transpose(float *U, const double *X, int64_t K, hipStream_t s)
+hipError_t launch_flip(float *U, const double *X, int64_t K, hipStream_t s)
 {
-    const unsigned nt = (unsigned)((K + TF - 1) / TF);
-    hipLaunchKernelGGL(flip_transpose_kernel, dim3(nt, nt), dim3(NT), 0, s, U, X, K);
+    hipLaunchKernelGGL(flip_kernel, dim3(grid_for(K * K)), dim3(NT), 0, s, U, X, K);
     return hipGetLastError();
 }
 

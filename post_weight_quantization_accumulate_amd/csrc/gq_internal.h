@@ -199,8 +199,8 @@ constexpr int kPanel = 128;
 // mirrored below), write its inverse to Dinv and the transpose to DinvT.
 hipError_t launch_potrf_diag(double *M, int64_t K, int64_t p0, int nb, double *Dinv,
                              double *DinvT, unsigned *status, hipStream_t s);
-// U[i][j] = X[K-1-j][K-1-i] for i <= j (as fp32), 0 below the diagonal.
-hipError_t launch_flip_transpose(float *U, const double *X, int64_t K, hipStream_t s);
+// U[i][j] = X[K-1-i][K-1-j] for i <= j (as fp32), 0 below the diagonal.
+hipError_t launch_flip(float *U, const double *X, int64_t K, hipStream_t s);
 
 // GPTQ (gptq.hip).
 constexpr int kSweepBlock = 128;      // lazy-batch block width (columns)
