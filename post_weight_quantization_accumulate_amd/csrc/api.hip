@@ -208,9 +208,13 @@ struct PsdTiming {
 };
 thread_local PsdTiming g_timing;
 
+// Per panel: the inverses of its four 32 x 32 diagonal sub-blocks.
+constexpr int64_t kXdPerPanel = 4 * 32 * 32;
+static_assert(kPanel == 128, "four 32-row sub-blocks per panel");
+
 struct FactorWs {
     Scalars sc;
-    double *M, *X, *Dinv, *DinvT;
+    double *M, *X, *XD;
 };
 
 FactorWs carve_factor(Carver &c, int64_t K)
@@ -221,8 +225,7 @@ FactorWs carve_factor(Carver &c, int64_t K)
     const size_t nblk = (size_t)((K + kPanel - 1) / kPanel);
     w.M = c.take<double>(n);
     w.X = c.take<double>(n);
-    w.Dinv = c.take<double>(nblk * kPanel * kPanel);
-    w.DinvT = c.take<double>(nblk * kPanel * kPanel);
+    w.XD = c.take<double>(nblk * kXdPerPanel);
     return w;
 }
 
@@ -310,10 +313,9 @@ int run_factor(float *U, const float *H, int64_t K, float damp, FactorWs &w, hip
         hipError_t e = hipEventRecord(la->to_inv, s);
         if (e == hipSuccess) e = hipStreamWaitEvent(la->inv, la->to_inv, 0);
         if (e != hipSuccess) return e;
-        // X_p[a][c] = sum_b (L_pp^-1)[a][b] X_p[b][c], L_pp^-1 = Dinv_p^T; in place
-        // (each output tile reads its whole column range before writing it)
-        GemmDesc r = gemm(w.Dinv + p * kPanel * kPanel, nbq, w.X + q0 * K, K, nbq, q1, nbq, w.X + q0 * K, K);
-        e = gemm_tn_f64(r, la->inv);
+        // X_p = L_pp^-1 X_p = R_pp^-T X_p, in place, over the columns < q1
+        e = launch_trsm_rt(w.M, K, q0, nbq, w.XD + p * kXdPerPanel, w.X + q0 * K, K, w.X + q0 * K, K, nullptr, 0, q1,
+                           la->inv);
         if (e != hipSuccess || q1 >= K) return e;
         // X_k -= L_kp X_p for rows k >= q1, columns < q1; L_kp[k][b] = R[q0 + b][k]
         GemmDesc u = gemm(w.M + q0 * K + q1, K, w.X + q0 * K, K, K - q1, q1, nbq, w.X + q1 * K, K);
@@ -326,22 +328,20 @@ int run_factor(float *U, const float *H, int64_t K, float damp, FactorWs &w, hip
     // block row of panel p+1 has its update from panel p, the diagonal block
     // p+1 is factored on the side stream while the rest of the trailing update
     // of panel p runs on the caller's stream.
-    GQ_HIP(launch_potrf_diag(w.M, K, 0, (int)(K < kPanel ? K : kPanel), w.Dinv, w.DinvT, w.sc.status, s),
-           "potrf diag");
+    GQ_HIP(launch_potrf_diag(w.M, K, 0, (int)(K < kPanel ? K : kPanel), w.XD, w.sc.status, s), "potrf diag");
     for (int64_t p = 0; p < nblk; ++p) {
         const int64_t p0 = p * kPanel;
         const int nbp = (int)((K - p0) < kPanel ? (K - p0) : kPanel);
         const int64_t p1 = p0 + nbp;
-        const double *Dinv = w.Dinv + p * kPanel * kPanel;
         if (p > 0) GQ_HIP(hipStreamWaitEvent(s, la->to_main, 0), "wait diagonal block");
         if (p1 >= K) {
             GQ_HIP(inverse_rows(p), "inverse rows");
             break;
         }
         // panel rows: R_{p,rest} = R_pp^{-T} A_{p,rest}, mirrored below the diagonal
-        GemmDesc t = gemm(Dinv, nbp, w.M + p0 * K + p1, K, nbp, K - p1, nbp, w.M + p0 * K + p1, K);
-        t.out_t = w.M + p1 * K + p0;
-        GQ_HIP(gemm_tn_f64(t, s), "trsm");
+        GQ_HIP(launch_trsm_rt(w.M, K, p0, nbp, w.XD + p * kXdPerPanel, w.M + p0 * K + p1, K, w.M + p0 * K + p1, K,
+                              w.M + p1 * K + p0, K, K - p1, s),
+               "trsm");
         GQ_HIP(inverse_rows(p), "inverse rows");
         // trailing update of the upper triangle, A_rest -= R_{p,rest}^T R_{p,rest}:
         // first the block row of panel p+1 ...
@@ -356,8 +356,7 @@ int run_factor(float *U, const float *H, int64_t K, float damp, FactorWs &w, hip
         // ... then its diagonal block on the side stream ...
         GQ_HIP(hipEventRecord(la->to_side, s), "record");
         GQ_HIP(hipStreamWaitEvent(la->side, la->to_side, 0), "wait trailing row");
-        GQ_HIP(launch_potrf_diag(w.M, K, p1, nbn, w.Dinv + (p + 1) * kPanel * kPanel,
-                                 w.DinvT + (p + 1) * kPanel * kPanel, w.sc.status, la->side),
+        GQ_HIP(launch_potrf_diag(w.M, K, p1, nbn, w.XD + (p + 1) * kXdPerPanel, w.sc.status, la->side),
                "potrf diag");
         GQ_HIP(hipEventRecord(la->to_main, la->side), "record");
         // ... while the rest of the trailing update runs here

@@ -136,20 +136,18 @@ __global__ __launch_bounds__(NT) void damp_reverse_kernel(double *__restrict__ M
     }
 }
 
-// Upper Cholesky (A = R^T R) of one nb x nb diagonal block (nb <= 128) and its
-// triangular inverse, blocked by 32 so that the sequential part runs in one wave
-// without workgroup barriers:
+// Upper Cholesky (A = R^T R) of one nb x nb diagonal block (nb <= 128), blocked
+// by 32 so that the sequential part runs in one wave without workgroup barriers:
 //   - one wave factors and inverts each 32 x 32 diagonal sub-block D in its
 //     registers (each lane a 4 x 4 tile), publishing the pivot row (column) of
 //     each step through LDS;
 //   - all 8 waves then apply it: the strip solve R[D, rest] = R_DD^-T A[D, rest]
-//     and the trailing update A[rest, rest] -= R[D, rest]^T R[D, rest];
-//   - the inverse of the whole block is built by block back substitution,
-//     X[i, rest] = -X_ii R[i, rest] X[rest, rest].
-// The block lives in LDS: R in the upper triangle, the inverse transposed in the
-// lower triangle (its diagonal apart).  Writes R (upper) and R^T (lower) back
-// into M, and the inverse and its transpose to Dinv / DinvT (nb x nb, ld = nb).
-// Rows and columns beyond nb are padded with the identity, which decouples them.
+//     and the trailing update A[rest, rest] -= R[D, rest]^T R[D, rest].
+// The block lives in LDS (R in the upper triangle).  Writes R (upper) and R^T
+// (lower) back into M, and the four sub-block inverses R_DD^-1 (dense 32 x 32,
+// zero below the diagonal) to XD, for the block substitutions that use the
+// panel.  Rows and columns beyond nb are padded with the identity, which
+// decouples them.
 constexpr int NBMAX = kPanel;
 constexpr int SB = 32;
 constexpr int PNT = 512;
@@ -158,10 +156,9 @@ constexpr int PNT = 512;
 // owns rows 4 (l / 8) + i and columns 4 (l % 8) + k.  A wave's LDS operations
 // complete in issue order, so a value published to LDS is visible to the reads
 // that follow it; the wave barriers only stop the compiler from reordering them.
-// Writes R (upper) into A, the inverse dense into XD and transposed into the
-// sub-block's strict lower triangle (diagonal into xdiag).  Returns true if a
+// Writes R (upper) into A and the inverse dense into XD.  Returns true if a
 // pivot of a real (not padded) row was not positive.
-__device__ __attribute__((noinline)) bool wave_factor32(double (*A)[NBMAX + 1], double *xdiag, double (*XD)[SB + 1],
+__device__ __attribute__((noinline)) bool wave_factor32(double (*A)[NBMAX + 1], double (*XD)[SB + 1],
                               double *rowj, double *colj, double *invd, int o, int nb, int lane)
 {
     const int br = lane >> 3, bc = lane & 7;
@@ -252,28 +249,15 @@ __device__ __attribute__((noinline)) bool wave_factor32(double (*A)[NBMAX + 1], 
             const int r = 4 * br + i, c = 4 * bc + k;
             if (c >= r) A[o + r][o + c] = a[i][k];
             XD[r][c] = x[i][k];
-            if (r < c) A[o + c][o + r] = x[i][k];
-            if (r == c) xdiag[o + r] = x[i][k];
         }
     return badp;
 }
 
-// X[k][c] of the inverse for k, c in the finished lower-right part: stored
-// transposed below the diagonal, diagonal apart, zero for k > c.
-__device__ inline double xval(double (*A)[NBMAX + 1], const double *xdiag, int k, int c)
-{
-    const double lo = A[c][k];
-    const double dg = xdiag[c];
-    return (k < c) ? lo : ((k == c) ? dg : 0.0);
-}
-
 __global__ __launch_bounds__(PNT) void potrf_diag_kernel(double *__restrict__ M, int64_t K, int64_t p0,
-                                                        int nb, double *__restrict__ Dinv,
-                                                        double *__restrict__ DinvT, unsigned *status)
+                                                        int nb, double *__restrict__ XDout, unsigned *status)
 {
     __shared__ double A[NBMAX][NBMAX + 1];
     __shared__ double XD[SB][SB + 1];
-    __shared__ double xdiag[NBMAX];
     __shared__ double rowj[SB], colj[SB], invd[SB];
     __shared__ int bad;
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
@@ -305,10 +289,12 @@ __global__ __launch_bounds__(PNT) void potrf_diag_kernel(double *__restrict__ M,
     for (int s = 0; s < NBMAX / SB; ++s) {
         const int o = s * SB;
         if (wave == 0) {
-            const bool b = wave_factor32(A, xdiag, XD, rowj, colj, invd, o, nb, lane);
+            const bool b = wave_factor32(A, XD, rowj, colj, invd, o, nb, lane);
             if (b && lane == 0) bad = 1;
         }
         __syncthreads();
+        // the sub-block's inverse, for the block substitutions that use this panel
+        for (int e = t; e < SB * SB; e += PNT) XDout[s * SB * SB + e] = XD[e / SB][e % SB];
         if (o + SB >= NBMAX) break;
         // strip: R[o+rr][c] = sum_k XD[k][rr] A[o+k][c]  (XD is zero below its diagonal)
         const int c = o + SB + cc;
@@ -364,71 +350,88 @@ __global__ __launch_bounds__(PNT) void potrf_diag_kernel(double *__restrict__ M,
         __syncthreads();
     }
 
-    // R is final: write it (upper) and R^T (lower) back, before the upper
-    // triangle is reused as scratch by the inverse
+    // R is final: write it (upper) and R^T (lower) back
     for (int e = t; e < NBMAX * NBMAX; e += PNT) {
         const int r = e >> 7, c = e & 127;
         if (r < nb && c < nb) M[(p0 + r) * K + p0 + c] = (c >= r) ? A[r][c] : A[c][r];
     }
-    __syncthreads();
-
-    // ---- inverse, block rows from the bottom: X[i, rest] = -X_ii (R[i, rest] X[rest, rest])
-#pragma unroll 1
-    for (int i = NBMAX / SB - 2; i >= 0; --i) {
-        const int o = i * SB;
-        const int c = o + SB + cc;
-        double tv[8];
-#pragma unroll
-        for (int q = 0; q < 8; ++q) tv[q] = 0.0;
-        {
-            // the same trip count on every lane (xval is 0 for k > c), so the
-            // loop unrolls and its LDS reads overlap
-            const int cs = c < NBMAX ? c : NBMAX - 1;
-#pragma unroll 4
-            for (int k = o + SB; k < NBMAX; ++k) {
-                const double xk = xval(A, xdiag, k, cs);
-#pragma unroll
-                for (int q = 0; q < 8; ++q) tv[q] = fma(A[o + rg * 8 + q][k], xk, tv[q]);
-            }
-        }
-        __syncthreads();
-        if (c < NBMAX) {                      // T replaces R[i, rest] (already written out)
-#pragma unroll
-            for (int q = 0; q < 8; ++q) A[o + rg * 8 + q][c] = tv[q];
-        }
-        __syncthreads();
-        // X_ii dense in XD (zero below its diagonal) for the product below
-        for (int e = t; e < SB * SB; e += PNT) {
-            const int rr = e / SB, m = e % SB;
-            XD[rr][m] = xval(A, xdiag, o + rr, o + m);
-        }
-        __syncthreads();
-        if (c < NBMAX) {
-            double xo[8];
-#pragma unroll
-            for (int q = 0; q < 8; ++q) xo[q] = 0.0;
-#pragma unroll 4
-            for (int m = 0; m < SB; ++m) {
-                const double tm = A[o + m][c];
-#pragma unroll
-                for (int q = 0; q < 8; ++q) xo[q] = fma(-XD[rg * 8 + q][m], tm, xo[q]);
-            }
-#pragma unroll
-            for (int q = 0; q < 8; ++q) A[c][o + rg * 8 + q] = xo[q];     // X[o+rr][c], transposed
-        }
-        __syncthreads();
-    }
-
-    // X[r][c] (upper) is kept transposed below A's diagonal, its diagonal in xdiag
-    for (int e = t; e < NBMAX * NBMAX; e += PNT) {
-        const int r = e >> 7, c = e & 127;
-        if (r < nb && c < nb) Dinv[r * nb + c] = (c > r) ? A[c][r] : ((c == r) ? xdiag[r] : 0.0);
-    }
-    for (int e = t; e < NBMAX * NBMAX; e += PNT) {
-        const int c = e >> 7, r = e & 127;        // DinvT[c][r] = X[r][c], written row by row
-        if (r < nb && c < nb) DinvT[c * nb + r] = (c > r) ? A[c][r] : ((c == r) ? xdiag[r] : 0.0);
-    }
     if (t == 0 && bad) atomicOr(status, ST_NOT_PD);
+}
+
+// Y = R^-T B for the nb x nb upper block R at (p0, p0) of M (nb <= 128), by block
+// forward substitution over its 32 x 32 diagonal sub-blocks, whose inverses XD
+// (dense 32 x 32, zero below the diagonal) the diagonal kernel wrote:
+//     Y_s = XD_s^T (B_s - sum_{t < s} R_ts^T Y_t).
+// One workgroup per 64 columns of B (nb x ncols, ld ldb), held in LDS; thread
+// (a, g) owns row a of the current 32-row block in columns 8 g .. 8 g + 7.  Y
+// goes to out (ld ldo; out may be B: each workgroup reads its columns before it
+// writes them) and, with out_t set, transposed to out_t (out_t[c ldt + a] = Y[a][c]).
+constexpr int TSC = 64;
+constexpr int TST = 256;
+__global__ __launch_bounds__(TST) void trsm_rt_kernel(const double *__restrict__ M, int64_t K, int64_t p0, int nb,
+                                                      const double *__restrict__ XD, const double *B, int64_t ldb,
+                                                      double *out, int64_t ldo, double *out_t, int64_t ldt,
+                                                      int64_t ncols)
+{
+    __shared__ double Ys[NBMAX][TSC + 1];
+    __shared__ double Rs[SB][SB + 1];
+    const int t = threadIdx.x, a = t & 31, cg = t >> 5;
+    const int64_t c0 = (int64_t)blockIdx.x * TSC;
+    const int nsb = (nb + SB - 1) / SB;
+    for (int e = t; e < NBMAX * TSC; e += TST) {
+        const int r = e / TSC, c = e % TSC;
+        Ys[r][c] = (r < nb && c0 + c < ncols) ? B[r * ldb + c0 + c] : 0.0;
+    }
+    __syncthreads();
+#pragma unroll 1
+    for (int s = 0; s < nsb; ++s) {
+        double acc[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[j] = Ys[SB * s + a][8 * cg + j];
+#pragma unroll 1
+        for (int tb = 0; tb < s; ++tb) {
+            // R_ts (rows 32 tb.., columns 32 s..); past nb it is zero
+            for (int e = t; e < SB * SB; e += TST) {
+                const int k = e / SB, aa = e % SB, rr = SB * tb + k, cc = SB * s + aa;
+                Rs[k][aa] = (rr < nb && cc < nb) ? M[(p0 + rr) * K + p0 + cc] : 0.0;
+            }
+            __syncthreads();
+#pragma unroll 4
+            for (int k = 0; k < SB; ++k) {
+                const double r = Rs[k][a];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) acc[j] = fma(-r, Ys[SB * tb + k][8 * cg + j], acc[j]);
+            }
+            __syncthreads();
+        }
+        for (int e = t; e < SB * SB; e += TST) Rs[e / SB][e % SB] = XD[s * SB * SB + e];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) Ys[SB * s + a][8 * cg + j] = acc[j];
+        __syncthreads();
+        double y[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) y[j] = 0.0;
+#pragma unroll 4
+        for (int b = 0; b < SB; ++b) {
+            const double xv = Rs[b][a];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) y[j] = fma(xv, Ys[SB * s + b][8 * cg + j], y[j]);
+        }
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < 8; ++j) Ys[SB * s + a][8 * cg + j] = y[j];
+        __syncthreads();
+    }
+    for (int e = t; e < NBMAX * TSC; e += TST) {
+        const int r = e / TSC, c = e % TSC;
+        if (r < nb && c0 + c < ncols) out[r * ldo + c0 + c] = Ys[r][c];
+    }
+    if (out_t) {
+        for (int e = t; e < NBMAX * TSC; e += TST) {
+            const int c = e / NBMAX, r = e % NBMAX;
+            if (r < nb && c0 + c < ncols) out_t[(c0 + c) * ldt + r] = Ys[r][c];
+        }
+    }
 }
 
 // U[i][j] = X[K-1-i][K-1-j] (as fp32) for i <= j, 0 below: the lower triangular
@@ -510,11 +513,22 @@ hipError_t launch_damp_reverse(double *M, const float *H, int64_t K, double damp
     return hipGetLastError();
 }
 
-hipError_t launch_potrf_diag(double *M, int64_t K, int64_t p0, int nb, double *Dinv, double *DinvT,
-                             unsigned *status, hipStream_t s)
+hipError_t launch_potrf_diag(double *M, int64_t K, int64_t p0, int nb, double *XD, unsigned *status,
+                             hipStream_t s)
 {
     if (nb < 1 || nb > NBMAX) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(potrf_diag_kernel, dim3(1), dim3(PNT), 0, s, M, K, p0, nb, Dinv, DinvT, status);
+    hipLaunchKernelGGL(potrf_diag_kernel, dim3(1), dim3(PNT), 0, s, M, K, p0, nb, XD, status);
+    return hipGetLastError();
+}
+
+hipError_t launch_trsm_rt(const double *M, int64_t K, int64_t p0, int nb, const double *XD, const double *B,
+                          int64_t ldb, double *out, int64_t ldo, double *out_t, int64_t ldt, int64_t ncols,
+                          hipStream_t s)
+{
+    if (nb < 1 || nb > NBMAX) return hipErrorInvalidValue;
+    if (ncols < 1) return hipSuccess;
+    hipLaunchKernelGGL(trsm_rt_kernel, dim3((unsigned)((ncols + TSC - 1) / TSC)), dim3(TST), 0, s, M, K, p0, nb, XD,
+                       B, ldb, out, ldo, out_t, ldt, ncols);
     return hipGetLastError();
 }
 
