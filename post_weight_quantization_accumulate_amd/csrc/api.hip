@@ -208,13 +208,12 @@ struct PsdTiming {
 };
 thread_local PsdTiming g_timing;
 
-// Per panel: the inverses of its four 32 x 32 diagonal sub-blocks.
-constexpr int64_t kXdPerPanel = 4 * 32 * 32;
-static_assert(kPanel == 128, "four 32-row sub-blocks per panel");
+// Per panel: 1 / R_kk of its diagonal block.
+constexpr int64_t kRinvPerPanel = kPanel;
 
 struct FactorWs {
     Scalars sc;
-    double *M, *X, *XD;
+    double *M, *X, *rinv;
 };
 
 FactorWs carve_factor(Carver &c, int64_t K)
@@ -225,7 +224,7 @@ FactorWs carve_factor(Carver &c, int64_t K)
     const size_t nblk = (size_t)((K + kPanel - 1) / kPanel);
     w.M = c.take<double>(n);
     w.X = c.take<double>(n);
-    w.XD = c.take<double>(nblk * kXdPerPanel);
+    w.rinv = c.take<double>(nblk * kRinvPerPanel);
     return w;
 }
 
@@ -314,7 +313,7 @@ int run_factor(float *U, const float *H, int64_t K, float damp, FactorWs &w, hip
         if (e == hipSuccess) e = hipStreamWaitEvent(la->inv, la->to_inv, 0);
         if (e != hipSuccess) return e;
         // X_p = L_pp^-1 X_p = R_pp^-T X_p, in place, over the columns < q1
-        e = launch_trsm_rt(w.M, K, q0, nbq, w.XD + p * kXdPerPanel, w.X + q0 * K, K, w.X + q0 * K, K, nullptr, 0, q1,
+        e = launch_trsm_rt(w.M, K, q0, nbq, w.rinv + p * kRinvPerPanel, w.X + q0 * K, K, w.X + q0 * K, K, nullptr, 0, q1,
                            la->inv);
         if (e != hipSuccess || q1 >= K) return e;
         // X_k -= L_kp X_p for rows k >= q1, columns < q1; L_kp[k][b] = R[q0 + b][k]
@@ -328,7 +327,7 @@ int run_factor(float *U, const float *H, int64_t K, float damp, FactorWs &w, hip
     // block row of panel p+1 has its update from panel p, the diagonal block
     // p+1 is factored on the side stream while the rest of the trailing update
     // of panel p runs on the caller's stream.
-    GQ_HIP(launch_potrf_diag(w.M, K, 0, (int)(K < kPanel ? K : kPanel), w.XD, w.sc.status, s), "potrf diag");
+    GQ_HIP(launch_potrf_diag(w.M, K, 0, (int)(K < kPanel ? K : kPanel), w.rinv, w.sc.status, s), "potrf diag");
     for (int64_t p = 0; p < nblk; ++p) {
         const int64_t p0 = p * kPanel;
         const int nbp = (int)((K - p0) < kPanel ? (K - p0) : kPanel);
@@ -339,7 +338,7 @@ int run_factor(float *U, const float *H, int64_t K, float damp, FactorWs &w, hip
             break;
         }
         // panel rows: R_{p,rest} = R_pp^{-T} A_{p,rest}, mirrored below the diagonal
-        GQ_HIP(launch_trsm_rt(w.M, K, p0, nbp, w.XD + p * kXdPerPanel, w.M + p0 * K + p1, K, w.M + p0 * K + p1, K,
+        GQ_HIP(launch_trsm_rt(w.M, K, p0, nbp, w.rinv + p * kRinvPerPanel, w.M + p0 * K + p1, K, w.M + p0 * K + p1, K,
                               w.M + p1 * K + p0, K, K - p1, s),
                "trsm");
         GQ_HIP(inverse_rows(p), "inverse rows");
@@ -356,7 +355,7 @@ int run_factor(float *U, const float *H, int64_t K, float damp, FactorWs &w, hip
         // ... then its diagonal block on the side stream ...
         GQ_HIP(hipEventRecord(la->to_side, s), "record");
         GQ_HIP(hipStreamWaitEvent(la->side, la->to_side, 0), "wait trailing row");
-        GQ_HIP(launch_potrf_diag(w.M, K, p1, nbn, w.XD + (p + 1) * kXdPerPanel, w.sc.status, la->side),
+        GQ_HIP(launch_potrf_diag(w.M, K, p1, nbn, w.rinv + (p + 1) * kRinvPerPanel, w.sc.status, la->side),
                "potrf diag");
         GQ_HIP(hipEventRecord(la->to_main, la->side), "record");
         // ... while the rest of the trailing update runs here

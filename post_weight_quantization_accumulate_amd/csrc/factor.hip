@@ -138,38 +138,37 @@ __global__ __launch_bounds__(NT) void damp_reverse_kernel(double *__restrict__ M
 
 // Upper Cholesky (A = R^T R) of one nb x nb diagonal block (nb <= 128), blocked
 // by 32 so that the sequential part runs in one wave without workgroup barriers:
-//   - one wave factors and inverts each 32 x 32 diagonal sub-block D in its
+//   - one wave factors each 32 x 32 diagonal sub-block D in its
 //     registers (each lane a 4 x 4 tile), publishing the pivot row (column) of
 //     each step through LDS;
-//   - all 8 waves then apply it: the strip solve R[D, rest] = R_DD^-T A[D, rest]
-//     and the trailing update A[rest, rest] -= R[D, rest]^T R[D, rest].
+//   - then the strip solve R[D, rest] = R_DD^-T A[D, rest] by substitution, one
+//     column per thread, and the trailing update A[rest, rest] -= R[D, rest]^T
+//     R[D, rest] by all 8 waves.
 // The block lives in LDS (R in the upper triangle).  Writes R (upper) and R^T
-// (lower) back into M, and the four sub-block inverses R_DD^-1 (dense 32 x 32,
-// zero below the diagonal) to XD, for the block substitutions that use the
-// panel.  Rows and columns beyond nb are padded with the identity, which
-// decouples them.
+// (lower) back into M, and 1 / R_kk for k < 128 to rinv (1 on padded rows), for
+// the block substitutions that use the panel.  Rows and columns beyond nb are
+// padded with the identity, which decouples them.
 constexpr int NBMAX = kPanel;
 constexpr int SB = 32;
 constexpr int PNT = 512;
 
-// One wave: Cholesky and inverse of the 32 x 32 block at (o, o) of A.  Lane l
-// owns rows 4 (l / 8) + i and columns 4 (l % 8) + k.  A wave's LDS operations
-// complete in issue order, so a value published to LDS is visible to the reads
-// that follow it; the wave barriers only stop the compiler from reordering them.
-// Writes R (upper) into A and the inverse dense into XD.  Returns true if a
-// pivot of a real (not padded) row was not positive.
-__device__ __attribute__((noinline)) bool wave_factor32(double (*A)[NBMAX + 1], double (*XD)[SB + 1],
-                              double *rowj, double *colj, double *invd, int o, int nb, int lane)
+// One wave: Cholesky of the 32 x 32 block at (o, o) of A.  Lane l owns rows
+// 4 (l / 8) + i and columns 4 (l % 8) + k.  A wave's LDS operations complete in
+// issue order, so a value published to LDS is visible to the reads that follow
+// it; the wave barriers only stop the compiler from reordering them.  Writes R
+// (upper) into A and 1 / R_jj into rinv[o + j].  Returns true if a pivot of a
+// real (not padded) row was not positive.
+__device__ __attribute__((noinline)) bool wave_factor32(double (*A)[NBMAX + 1], double *rowj, double *rinv, int o,
+                                                        int nb, int lane)
 {
     const int br = lane >> 3, bc = lane & 7;
-    double a[4][4], x[4][4];
+    double a[4][4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
             const int r = 4 * br + i, c = 4 * bc + k;
             a[i][k] = (c >= r) ? A[o + r][o + c] : 0.0;
-            x[i][k] = (r == c) ? 1.0 : 0.0;
         }
     bool badp = false;
     // Step j with j a compile-time constant: row and column tests against j fold
@@ -193,7 +192,7 @@ __device__ __attribute__((noinline)) bool wave_factor32(double (*A)[NBMAX + 1], 
         inv = fma(inv, fma(-hp * inv, inv, 0.5), inv);
         inv = fma(inv, fma(-hp * inv, inv, 0.5), inv);
         const double rjj = piv * inv;
-        if (lane == 0) invd[j] = inv;
+        if (lane == 0) rinv[o + j] = inv;
         double vr[4], vc[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) vr[i] = rowj[4 * br + i] * inv;
@@ -211,54 +210,50 @@ __device__ __attribute__((noinline)) bool wave_factor32(double (*A)[NBMAX + 1], 
             }
         __builtin_amdgcn_wave_barrier();
     });
-    // X = R^{-1}: for j = 31 .. 0: X[j][:] /= R[j][j]; X[r][:] -= R[r][j] X[j][:] (r < j)
-    static_for<SB>([&](auto JJ) {
-        constexpr int j = SB - 1 - decltype(JJ)::value;
-        if (bc == (j >> 2)) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) colj[4 * br + i] = a[i][j & 3];
-        }
-        __builtin_amdgcn_wave_barrier();
-        const double inv = invd[j];                   // 1 / R_jj from the factor steps
-        if (br == (j >> 2)) {
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                x[j & 3][k] *= inv;
-                rowj[4 * bc + k] = x[j & 3][k];
-            }
-        }
-        __builtin_amdgcn_wave_barrier();
-        double vr[4], vc[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) vr[i] = colj[4 * br + i];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) vc[k] = rowj[4 * bc + k];
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const double v = x[i][k];
-                x[i][k] = (4 * br + i < j) ? fma(-vr[i], vc[k], v) : v;
-            }
-        __builtin_amdgcn_wave_barrier();
-    });
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
             const int r = 4 * br + i, c = 4 * bc + k;
             if (c >= r) A[o + r][o + c] = a[i][k];
-            XD[r][c] = x[i][k];
         }
     return badp;
 }
 
+// As solve32 for a 32 x 32 block stored at rows 0..31, columns o.. of R.
+__device__ inline void solve32_rows(const double (*R)[NBMAX + 1], const double *rinv, int o, double (&b)[SB])
+{
+    static_for<SB>([&](auto KK) {
+        constexpr int k = decltype(KK)::value;
+        b[k] *= rinv[o + k];
+        static_for<SB - 1 - k>([&](auto JJ) {
+            constexpr int j = k + 1 + decltype(JJ)::value;
+            b[j] = fma(-R[k][o + j], b[k], b[j]);
+        });
+    });
+}
+
+// In one thread: b <- R^-T b for the 32 x 32 upper block R at (o, o) of A (its
+// 1 / R_kk in rinv[o + k]), b in registers; forward substitution, R read by
+// broadcast.
+__device__ inline void solve32(const double (*R)[NBMAX + 1], const double *rinv, int o, double (&b)[SB])
+{
+    static_for<SB>([&](auto KK) {
+        constexpr int k = decltype(KK)::value;
+        b[k] *= rinv[o + k];
+        static_for<SB - 1 - k>([&](auto JJ) {
+            constexpr int j = k + 1 + decltype(JJ)::value;
+            b[j] = fma(-R[o + k][o + j], b[k], b[j]);
+        });
+    });
+}
+
 __global__ __launch_bounds__(PNT) void potrf_diag_kernel(double *__restrict__ M, int64_t K, int64_t p0,
-                                                        int nb, double *__restrict__ XDout, unsigned *status)
+                                                        int nb, double *__restrict__ rinv_out, unsigned *status)
 {
     __shared__ double A[NBMAX][NBMAX + 1];
-    __shared__ double XD[SB][SB + 1];
-    __shared__ double rowj[SB], colj[SB], invd[SB];
+    __shared__ double rinv[NBMAX];
+    __shared__ double rowj[SB];
     __shared__ int bad;
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
 
@@ -283,36 +278,25 @@ __global__ __launch_bounds__(PNT) void potrf_diag_kernel(double *__restrict__ M,
     if (t == 0) bad = 0;
     __syncthreads();
 
-    const int cc = t & 127, rg = t >> 7;             // strip mapping: one column, 8 rows
     const int ty = t >> 5, tx = t & 31;              // trailing mapping: 16 x 32 grid
 #pragma unroll 1
     for (int s = 0; s < NBMAX / SB; ++s) {
         const int o = s * SB;
         if (wave == 0) {
-            const bool b = wave_factor32(A, XD, rowj, colj, invd, o, nb, lane);
+            const bool b = wave_factor32(A, rowj, rinv, o, nb, lane);
             if (b && lane == 0) bad = 1;
         }
         __syncthreads();
-        // the sub-block's inverse, for the block substitutions that use this panel
-        for (int e = t; e < SB * SB; e += PNT) XDout[s * SB * SB + e] = XD[e / SB][e % SB];
         if (o + SB >= NBMAX) break;
-        // strip: R[o+rr][c] = sum_k XD[k][rr] A[o+k][c]  (XD is zero below its diagonal)
-        const int c = o + SB + cc;
-        double out[8];
+        // strip: R[o.., c] = R_DD^-T A[o.., c], one column per thread
+        if (t < NBMAX - o - SB) {
+            const int c = o + SB + t;
+            double b[SB];
 #pragma unroll
-        for (int q = 0; q < 8; ++q) out[q] = 0.0;
-        if (c < NBMAX) {
-#pragma unroll 4
-            for (int k = 0; k < SB; ++k) {
-                const double ak = A[o + k][c];
+            for (int k = 0; k < SB; ++k) b[k] = A[o + k][c];
+            solve32(A, rinv, o, b);
 #pragma unroll
-                for (int q = 0; q < 8; ++q) out[q] += XD[k][rg * 8 + q] * ak;
-            }
-        }
-        __syncthreads();
-        if (c < NBMAX) {
-#pragma unroll
-            for (int q = 0; q < 8; ++q) A[o + rg * 8 + q][c] = out[q];
+            for (int k = 0; k < SB; ++k) A[o + k][c] = b[k];
         }
         __syncthreads();
         // trailing: A[r][c] -= sum_k R[o+k][r] R[o+k][c], r <= c in [o+32, 128)
@@ -350,7 +334,8 @@ __global__ __launch_bounds__(PNT) void potrf_diag_kernel(double *__restrict__ M,
         __syncthreads();
     }
 
-    // R is final: write it (upper) and R^T (lower) back
+    // R is final: write it (upper) and R^T (lower) back, and 1 / R_kk
+    if (t < NBMAX) rinv_out[t] = rinv[t];
     for (int e = t; e < NBMAX * NBMAX; e += PNT) {
         const int r = e >> 7, c = e & 127;
         if (r < nb && c < nb) M[(p0 + r) * K + p0 + c] = (c >= r) ? A[r][c] : A[c][r];
@@ -359,22 +344,25 @@ __global__ __launch_bounds__(PNT) void potrf_diag_kernel(double *__restrict__ M,
 }
 
 // Y = R^-T B for the nb x nb upper block R at (p0, p0) of M (nb <= 128), by block
-// forward substitution over its 32 x 32 diagonal sub-blocks, whose inverses XD
-// (dense 32 x 32, zero below the diagonal) the diagonal kernel wrote:
-//     Y_s = XD_s^T (B_s - sum_{t < s} R_ts^T Y_t).
-// One workgroup per 64 columns of B (nb x ncols, ld ldb), held in LDS; thread
-// (a, g) owns row a of the current 32-row block in columns 8 g .. 8 g + 7.  Y
-// goes to out (ld ldo; out may be B: each workgroup reads its columns before it
-// writes them) and, with out_t set, transposed to out_t (out_t[c ldt + a] = Y[a][c]).
+// forward substitution over its 32 x 32 diagonal sub-blocks:
+//     Y_s = R_ss^-T (B_s - sum_{t < s} R_ts^T Y_t),
+// the update as small products (thread (a, g): row a of the block, columns
+// 8 g .. 8 g + 7), the diagonal solve by substitution in one thread per
+// column with 1 / R_kk from rinv (which the diagonal kernel wrote).  One
+// workgroup per 64 columns of B (nb x ncols, ld ldb), held in LDS.  Y goes to
+// out (ld ldo; out may be B: each workgroup reads its columns before it writes
+// them) and, with out_t set, transposed to out_t (out_t[c ldt + a] = Y[a][c]).
 constexpr int TSC = 64;
 constexpr int TST = 256;
 __global__ __launch_bounds__(TST) void trsm_rt_kernel(const double *__restrict__ M, int64_t K, int64_t p0, int nb,
-                                                      const double *__restrict__ XD, const double *B, int64_t ldb,
+                                                      const double *__restrict__ rinv_in, const double *B,
+                                                      int64_t ldb,
                                                       double *out, int64_t ldo, double *out_t, int64_t ldt,
                                                       int64_t ncols)
 {
     __shared__ double Ys[NBMAX][TSC + 1];
-    __shared__ double Rs[SB][SB + 1];
+    __shared__ double Rs[SB][NBMAX + 1];          // R_ts rows of the current block (solve32 layout)
+    __shared__ double rinv[NBMAX];
     const int t = threadIdx.x, a = t & 31, cg = t >> 5;
     const int64_t c0 = (int64_t)blockIdx.x * TSC;
     const int nsb = (nb + SB - 1) / SB;
@@ -382,6 +370,7 @@ __global__ __launch_bounds__(TST) void trsm_rt_kernel(const double *__restrict__
         const int r = e / TSC, c = e % TSC;
         Ys[r][c] = (r < nb && c0 + c < ncols) ? B[r * ldb + c0 + c] : 0.0;
     }
+    if (t < NBMAX) rinv[t] = rinv_in[t];
     __syncthreads();
 #pragma unroll 1
     for (int s = 0; s < nsb; ++s) {
@@ -404,22 +393,23 @@ __global__ __launch_bounds__(TST) void trsm_rt_kernel(const double *__restrict__
             }
             __syncthreads();
         }
-        for (int e = t; e < SB * SB; e += TST) Rs[e / SB][e % SB] = XD[s * SB * SB + e];
+        // R_ss (identity past nb) into Rs columns 32 s.., as rows 0..31 of a
+        // block at offset (0, 32 s) of the solve32 layout
+        for (int e = t; e < SB * SB; e += TST) {
+            const int k = e / SB, aa = e % SB, rr = SB * s + k, cc = SB * s + aa;
+            Rs[k][SB * s + aa] = (rr < nb && cc < nb) ? M[(p0 + rr) * K + p0 + cc] : (rr == cc ? 1.0 : 0.0);
+        }
 #pragma unroll
         for (int j = 0; j < 8; ++j) Ys[SB * s + a][8 * cg + j] = acc[j];
         __syncthreads();
-        double y[8];
+        if (t < TSC) {
+            double b[SB];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) y[j] = 0.0;
-#pragma unroll 4
-        for (int b = 0; b < SB; ++b) {
-            const double xv = Rs[b][a];
+            for (int k = 0; k < SB; ++k) b[k] = Ys[SB * s + k][t];
+            solve32_rows(Rs, rinv, SB * s, b);
 #pragma unroll
-            for (int j = 0; j < 8; ++j) y[j] = fma(xv, Ys[SB * s + b][8 * cg + j], y[j]);
+            for (int k = 0; k < SB; ++k) Ys[SB * s + k][t] = b[k];
         }
-        __syncthreads();
-#pragma unroll
-        for (int j = 0; j < 8; ++j) Ys[SB * s + a][8 * cg + j] = y[j];
         __syncthreads();
     }
     for (int e = t; e < NBMAX * TSC; e += TST) {
@@ -513,21 +503,21 @@ hipError_t launch_damp_reverse(double *M, const float *H, int64_t K, double damp
     return hipGetLastError();
 }
 
-hipError_t launch_potrf_diag(double *M, int64_t K, int64_t p0, int nb, double *XD, unsigned *status,
+hipError_t launch_potrf_diag(double *M, int64_t K, int64_t p0, int nb, double *rinv, unsigned *status,
                              hipStream_t s)
 {
     if (nb < 1 || nb > NBMAX) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(potrf_diag_kernel, dim3(1), dim3(PNT), 0, s, M, K, p0, nb, XD, status);
+    hipLaunchKernelGGL(potrf_diag_kernel, dim3(1), dim3(PNT), 0, s, M, K, p0, nb, rinv, status);
     return hipGetLastError();
 }
 
-hipError_t launch_trsm_rt(const double *M, int64_t K, int64_t p0, int nb, const double *XD, const double *B,
+hipError_t launch_trsm_rt(const double *M, int64_t K, int64_t p0, int nb, const double *rinv, const double *B,
                           int64_t ldb, double *out, int64_t ldo, double *out_t, int64_t ldt, int64_t ncols,
                           hipStream_t s)
 {
     if (nb < 1 || nb > NBMAX) return hipErrorInvalidValue;
     if (ncols < 1) return hipSuccess;
-    hipLaunchKernelGGL(trsm_rt_kernel, dim3((unsigned)((ncols + TSC - 1) / TSC)), dim3(TST), 0, s, M, K, p0, nb, XD,
+    hipLaunchKernelGGL(trsm_rt_kernel, dim3((unsigned)((ncols + TSC - 1) / TSC)), dim3(TST), 0, s, M, K, p0, nb, rinv,
                        B, ldb, out, ldo, out_t, ldt, ncols);
     return hipGetLastError();
 }

@@ -196,14 +196,13 @@ hipError_t launch_damp_reverse(double *M, const float *H, int64_t K, double damp
 // workgroup, and every trailing and inverse update is a GEMM of depth kPanel.
 constexpr int kPanel = 128;
 // Factor the nb x nb diagonal block at (p0, p0) of M (upper Cholesky, in place,
-// mirrored below) and write the inverses of its four 32 x 32 diagonal
-// sub-blocks to XD (4 x 32 x 32 doubles, dense, zero below the diagonal).
-hipError_t launch_potrf_diag(double *M, int64_t K, int64_t p0, int nb, double *XD, unsigned *status,
+// mirrored below) and write 1 / R_kk to rinv (kPanel doubles, 1 past nb).
+hipError_t launch_potrf_diag(double *M, int64_t K, int64_t p0, int nb, double *rinv, unsigned *status,
                              hipStream_t s);
-// out = R^-T B for the factored nb x nb block R at (p0, p0) of M and its XD:
+// out = R^-T B for the factored nb x nb block R at (p0, p0) of M and its rinv:
 // B is nb x ncols (ld ldb), out may equal B; with out_t set, the result is
 // also written transposed (out_t[c * ldt + a]).
-hipError_t launch_trsm_rt(const double *M, int64_t K, int64_t p0, int nb, const double *XD, const double *B,
+hipError_t launch_trsm_rt(const double *M, int64_t K, int64_t p0, int nb, const double *rinv, const double *B,
                           int64_t ldb, double *out, int64_t ldo, double *out_t, int64_t ldt, int64_t ncols,
                           hipStream_t s);
 // U[i][j] = X[K-1-i][K-1-j] for i <= j (as fp32), 0 below the diagonal.
