@@ -136,7 +136,7 @@ int gq_set_psd_products(int kind);
  * without an eigendecomposition, as P = (H + sign(H) H) / 2 with sign(H) from a
  * scaled Newton-Schulz iteration.  For K < 65536 its symmetric products are
  * computed exactly in integers on the int8 matrix cores from operands rounded
- * to 51-52-bit integers (one power-of-two scale per row; residues modulo 15
+ * to 47-48-bit integers (one power-of-two scale per row; residues modulo 14
  * moduli, Chinese remainder reconstruction, one rounding to fp64); above that,
  * fp64 matrix core products.
  *   H   K x K fp32; the lower triangle is read, the full symmetric result is

@@ -20,8 +20,8 @@
 //      residues, since |sum| <= K 2^(2 beta) < M / 2, M = prod m_r; it is then
 //      scaled back and rounded to fp64 once.
 // The only rounding is the truncation of step 1 (relative 2^-beta per entry of
-// the row's scale) and the final conversion; with 15 moduli (M ~ 2^117.8) beta
-// is 52 at K = 5120 and 51 at K = 17408.  The 15 int8 products run at the int8
+// the row's scale) and the final conversion; with 14 moduli (M ~ 2^110.2) beta
+// is 48 at K = 5120 and 47 at K = 17408.  The 14 int8 products run at the int8
 // matrix rate, 64 times the fp64 one.
 #include "gq_internal.h"
 
@@ -29,27 +29,33 @@ namespace gq {
 
 namespace {
 
-constexpr int kMods[kOzMods] = {256, 255, 253, 251, 247, 241, 239, 233, 229, 227, 223, 217, 211, 199, 197};
+constexpr int kMods[kOzMods] = {256, 255, 253, 251, 247, 241, 239, 233, 229, 227, 223, 217, 211, 199};
 
 typedef unsigned __int128 u128;
 typedef __int128 i128;
 
 // The reconstruction's constants, at compile time: M = prod m_r and the weights
 // W_r = (M / m_r) ((M / m_r)^-1 mod m_r) (so that sum_r c_r W_r = x mod M for
-// the residues c_r of x), each as 8 limbs of 16 bits (M < 2^118), which keeps
-// every limb product c_r w below 2^24 (a full-rate 24-bit multiply).
-constexpr int kLimbs = 8;
-struct OzLimbs {
-    unsigned short w[kOzMods][kLimbs];
-    unsigned short M[kLimbs];
-    double invM;
-};
+// the residues c_r of x), each as limbs of 16 bits (7 for M ~ 2^110.2), which
+// keeps every limb product c_r w below 2^24 (a full-rate 24-bit multiply).
 constexpr u128 oz_modulus()
 {
     u128 M = 1;
     for (int r = 0; r < kOzMods; ++r) M *= (u128)kMods[r];
     return M;
 }
+constexpr int oz_limb_count()
+{
+    int bits = 0;
+    for (u128 m = oz_modulus(); m; m >>= 1) ++bits;
+    return (bits + 15) / 16;
+}
+constexpr int kLimbs = oz_limb_count();
+struct OzLimbs {
+    unsigned short w[kOzMods][kLimbs];
+    unsigned short M[kLimbs];
+    double invM;
+};
 constexpr OzLimbs oz_limbs()
 {
     OzLimbs L{};
@@ -82,13 +88,15 @@ static_assert((kOzM >> (16 * kLimbs - 1)) == 0, "M fits the limbs");
 // sum_k D[k] 2^(16 k) for signed limbs |D[k]| < 2^31
 __device__ inline i128 from_signed_limbs(const int (&D)[kLimbs])
 {
-    // two's complement sums in unsigned arithmetic (wrapping, shifts defined)
-    const unsigned long long p0 = (unsigned long long)(long long)D[0] + ((unsigned long long)(long long)D[1] << 16);
-    const unsigned long long p1 = (unsigned long long)(long long)D[2] + ((unsigned long long)(long long)D[3] << 16);
-    const unsigned long long p2 = (unsigned long long)(long long)D[4] + ((unsigned long long)(long long)D[5] << 16);
-    const unsigned long long p3 = (unsigned long long)(long long)D[6] + ((unsigned long long)(long long)D[7] << 16);
-    const u128 x = (u128)(i128)(long long)p0 + ((u128)(i128)(long long)p1 << 32) + ((u128)(i128)(long long)p2 << 64) +
-                   ((u128)(i128)(long long)p3 << 96);
+    // two's complement sums in unsigned arithmetic (wrapping, shifts defined),
+    // limbs paired into 64-bit words first
+    u128 x = 0;
+    static_for<(kLimbs + 1) / 2>([&](auto P) {
+        constexpr int k = 2 * decltype(P)::value;
+        unsigned long long pk = (unsigned long long)(long long)D[k];
+        if constexpr (k + 1 < kLimbs) pk += (unsigned long long)(long long)D[k + 1] << 16;
+        x += (u128)(i128)(long long)pk << (16 * k);
+    });
     return (i128)x;
 }
 
@@ -421,7 +429,7 @@ __global__ __launch_bounds__(CNT) void oz_crt_kernel(GemmDesc d, const uint8_t *
             double v = 0.0;
             if (row_in && gj < K && gi >= gj) {
                 // S = sum_r c_r W_r by 16-bit limbs of W_r: each limb sum is below
-                // 15 * 255 * 2^16 < 2^28
+                // 14 * 255 * 2^16 < 2^28
                 unsigned L[kLimbs] = {};
 #pragma unroll
                 for (int r = 0; r < kOzMods; ++r) {
@@ -476,7 +484,7 @@ __global__ __launch_bounds__(CNT) void oz_crt_kernel(GemmDesc d, const uint8_t *
     if (range_bad) atomicOr(status, ST_RANGE);
     // Split form of the symmetric output at exponent o.exp: each element's
     // residues are computed once, written to rows i0.. (this block) and, off the
-    // diagonal, staged in LDS (5 moduli at a time, in the space of the fp64
+    // diagonal, staged in LDS (7 moduli at a time, in the space of the fp64
     // tile) and written transposed to rows j0.. (the mirror).  On the diagonal
     // tile, entries above its diagonal come from their mirror.  Entries past K
     // are 0 and keep the padding zero.
@@ -490,7 +498,7 @@ __global__ __launch_bounds__(CNT) void oz_crt_kernel(GemmDesc d, const uint8_t *
             const double v = (diag && cc > li) ? tile[cc][li] : tile[li][cc];
             z[rr][t] = rint(v * sc);
         }
-    constexpr int kBatch = 5;
+    constexpr int kBatch = 7;
     static_assert(kOzMods % kBatch == 0, "whole batches");
     static_assert(sizeof(unsigned) * kBatch * CT * (CT / 4 + 1) <= sizeof(double) * CT * (CT + 1), "LDS reuse");
     unsigned (*rt)[CT][CT / 4 + 1] = reinterpret_cast<unsigned (*)[CT][CT / 4 + 1]>(&tile[0][0]);

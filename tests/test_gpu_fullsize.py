@@ -116,17 +116,17 @@ def test_attn_projection_matches_eigendecomposition(gq, attn):
     by LAPACK's symmetric eigensolver through numpy in fp64 (a library check,
     independent of the device path): eigenvalues of the stored Hessian clipped
     at zero and the matrix rebuilt.  The device result carries the rounding of
-    its products (operands rounded to 52-bit integers per row) through the
-    sign iteration plus the fp32 output; an fp64 model of that arithmetic
-    lands 5e-7 from the exact projection on this input, so 2e-6 is the
-    regression bound here (the acceptance bar is 1e-5)."""
+    its products (operands rounded to 48-bit integers per row) through the
+    sign iteration, the unconverged eigenvalues below l_0 and the fp32 output:
+    measured 2.6e-8 here, so 2e-7 is the regression bound (the acceptance bar
+    is 1e-5)."""
     wl, X, W, H, blob, Hs, P = attn
     Hs64 = _sym64(Hs.cpu().numpy())
     w, V = np.linalg.eigh(Hs64)
     Pex = (V * np.maximum(w, 0.0)) @ V.T
     rel = np.linalg.norm(P.cpu().numpy().astype(np.float64) - Pex) / np.linalg.norm(Pex)
     print(f"attn5120 projection: relative Frobenius distance to the eigendecomposition {rel:.3e}")
-    assert rel < 2e-6
+    assert rel < 2e-7
 
 
 def test_attn_gptq_full(gq, orc, attn):
