@@ -83,6 +83,20 @@ constexpr OzInv oz_inverses()
 }
 constexpr OzInv kOzInv = oz_inverses();
 constexpr OzLimbs kOzLimbs = oz_limbs();
+// The weight limbs of moduli 2j and 2j+1 side by side (u16 pairs), for
+// v_dot2_u32_u16: one instruction adds both moduli's products into a limb sum.
+static_assert(kOzMods % 2 == 0, "moduli in pairs");
+struct OzPairs { unsigned w[kOzMods / 2][kLimbs]; };
+constexpr OzPairs oz_pairs()
+{
+    OzPairs P{};
+    for (int j = 0; j < kOzMods / 2; ++j)
+        for (int k = 0; k < kLimbs; ++k)
+            P.w[j][k] = (unsigned)kOzLimbs.w[2 * j][k] | ((unsigned)kOzLimbs.w[2 * j + 1][k] << 16);
+    return P;
+}
+constexpr OzPairs kOzPairs = oz_pairs();
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 static_assert((kOzM >> (16 * kLimbs - 1)) == 0, "M fits the limbs");
 
 // sum_k D[k] 2^(16 k) for signed limbs |D[k]| < 2^31
@@ -100,20 +114,17 @@ __device__ inline i128 from_signed_limbs(const int (&D)[kLimbs])
     return (i128)x;
 }
 
-// Residue of the integer z (|z| <= 2^52) modulo kMods[r], as the int8 byte the
-// products use.  Odd m: the fp64 quotient z (1/m) is within 2^-7 of z / m, so
-// its rint is within one of the integer nearest z / m; z - m rint(z (1/m)) is
-// exact (fma) and one correction each way centres it in [-(m-1)/2, (m-1)/2].
-// m = 256: z - 256 floor(z / 256) in [0, 256) (exact), whose low byte is the
-// two's complement residue.
+// Residue of the integer z (|z| <= 2^48) modulo kMods[r], as the int8 byte the
+// products use.  Odd m: the fp64 quotient z (1/m) is within 2^-11.6 of z / m,
+// which lies at least 1/(2m) > 2^-9 from a half-integer, so rint gives the
+// nearest integer and z - m rint(z (1/m)) is the centred residue, exactly (fma).
+// m = 256: z - 256 floor(z / 256) in [0, 256), whose low byte is the two's
+// complement residue.
 __device__ inline unsigned residue_byte(double z, int r)
 {
     if (r == 0) return (unsigned)(int)fma(-256.0, floor(z * (1.0 / 256.0)), z) & 0xFFu;
-    const int m = kMods[r], h = (kMods[r] - 1) / 2;
-    int v = (int)fma(-(double)m, rint(z * kOzInv.v[r]), z);
-    v -= v > h ? m : 0;
-    v += v < -h ? m : 0;
-    return (unsigned)v & 0xFFu;
+    const double m = (double)kMods[r];
+    return (unsigned)(int)fma(-m, rint(z * kOzInv.v[r]), z) & 0xFFu;
 }
 
 // ---------------------------------------------------------------- split
@@ -429,14 +440,20 @@ __global__ __launch_bounds__(CNT) void oz_crt_kernel(GemmDesc d, const uint8_t *
             double v = 0.0;
             if (row_in && gj < K && gi >= gj) {
                 // S = sum_r c_r W_r by 16-bit limbs of W_r: each limb sum is below
-                // 14 * 255 * 2^16 < 2^28
+                // 14 * 255 * 2^16 < 2^28.  The residues of moduli 2j, 2j+1 (byte t
+                // of rs[2j], rs[2j+1]) are put side by side as u16s by one byte
+                // permute, and each limb takes one dot2 per pair.
+                u16x2 cp[kOzMods / 2];
+#pragma unroll
+                for (int j = 0; j < kOzMods / 2; ++j)
+                    cp[j] = __builtin_bit_cast(u16x2, __builtin_amdgcn_perm(rs[2 * j + 1], rs[2 * j],
+                                                                            0x0C000C00u | ((4u + t) << 16) | (unsigned)t));
                 unsigned L[kLimbs] = {};
 #pragma unroll
-                for (int r = 0; r < kOzMods; ++r) {
-                    const unsigned cr = (rs[r] >> (8 * t)) & 0xFFu;
+                for (int k = 0; k < kLimbs; ++k)
 #pragma unroll
-                    for (int k = 0; k < kLimbs; ++k) L[k] = __umul24(cr, kOzLimbs.w[r][k]) + L[k];
-                }
+                    for (int j = 0; j < kOzMods / 2; ++j)
+                        L[k] = __builtin_amdgcn_udot2(cp[j], __builtin_bit_cast(u16x2, kOzPairs.w[j][k]), L[k], false);
                 // The centred value is x = S - q M with q the integer nearest S / M:
                 // |x| <= K 2^(2 beta) < 0.497 M (the choice of beta), and the fp64
                 // estimate of S / M < 2^12 is within 2^-38 of it.  x by signed limbs
@@ -565,13 +582,13 @@ int oz_beta(int64_t K)
 {
     // largest beta with K 2^(2 beta) <= 0.497 M, i.e. 2 beta <= log2 M - 1.01 - log2 K
     // (the reconstruction rounds S / M to the nearest integer and needs the
-    // centred sum to stay clear of M / 2), and at most 52, so that the split
-    // integers are exact in fp64 and residue_byte's quotient stays within one
+    // centred sum to stay clear of M / 2), and at most 48, where residue_byte's
+    // quotient is exact (48 from K = 4100 up to 8192, 47 to 17408)
     const OzConst &c = oz_const();
     const double log2M = std::log2(ldexp((double)c.M_hi, 64) + (double)c.M_lo);
     const double room = log2M - 1.01 - std::log2((double)(K > 1 ? K : 1));
     const int b = (int)std::floor(room / 2.0);
-    return b < 52 ? b : 52;
+    return b < 48 ? b : 48;
 }
 
 int64_t oz_padded(int64_t K) { return (K + OBM - 1) / OBM * OBM; }
