@@ -183,22 +183,27 @@ __global__ __launch_bounds__(SPL_NT) void oz_split_kernel(const double *__restri
 
 // ---------------------------------------------------------------- int8 GEMM
 // P_r = RA_r RB_r^T mod m_r over the lower 256 x 256 tiles, all moduli in one
-// launch (blockIdx.y = modulus).  8 waves of 64 x 128 (4 x 2), each 2 x 4 blocks
-// of v_mfma_i32_32x32x32_i8.  The instruction computes X Y^T for 32-row panels X
-// and Y of 32 k: lane l feeds k = 16 (l / 32) + 0..15 of row l % 32 of each, and
-// result e of lane l is (X Y^T)[8 (e / 4) + 4 (l / 32) + e % 4][l % 32].  The B
-// panel goes first, so that e % 4 runs along a row of the output tile and each
-// lane holds 4 consecutive residues of a row, one dword.
+// launch (blockIdx.y = modulus).  4 waves of 128 x 128 (2 x 2), one per SIMD,
+// each 4 x 4 blocks of v_mfma_i32_32x32x32_i8 per k32 half, the sums in AGPRs.
+// The instruction computes X Y^T for 32-row panels X and Y of 32 k: lane l
+// feeds k = 16 (l / 32) + 0..15 of row l % 32 of each, and result e of lane l
+// is (X Y^T)[8 (e / 4) + 4 (l / 32) + e % 4][l % 32].  The B panel goes first,
+// so that e % 4 runs along a row of the output tile and each lane holds 4
+// consecutive residues of a row, one dword.
 //
 // Each stage (64 k) of an operand is one contiguous 16 KiB block of the tiled
-// plane layout, already in the order LDS wants: each wave copies 4 KiB of it
-// with 16-byte loads into registers two stages ahead, and stores them to a
-// double-buffered LDS slot one stage ahead.  The 64 x 128 wave tile needs 6
-// 16-byte LDS reads per 8 matrix instructions; the 16-byte chunk c of block row
-// rho sits at position c ^ swz(rho), so 16 consecutive rows read one chunk
-// without bank conflicts.
-constexpr int OBM = 256, OBK = 64, ONT = 512;
+// plane layout, already in the order LDS wants.  It goes straight from memory
+// to one of 4 LDS slots with 16-byte global_load_lds (no registers), three
+// stages ahead; the 16-byte chunk c of block row rho sits at position
+// c ^ swz(rho), so 16 consecutive rows read one chunk without bank conflicts.
+// One barrier per stage, between its two k32 halves: the second half's
+// instructions run while the next stage's first-half operands are read.  Every
+// LDS read and every copy is issued right after one matrix instruction, so the
+// wave never stalls on a full LDS or memory queue while its SIMD's matrix pipe
+// runs dry (the compiler's order is pinned by scheduling barriers).
+constexpr int OBM = 256, OBK = 64, ONT = 256, OSLOTS = 4;
 constexpr int kOzBlock = OBM * OBK;             // bytes of one stage of one operand
+constexpr int kOzSlot = 2 * kOzBlock;           // one stage of both operands
 constexpr int kOzEpiRow = 272;                  // LDS row stride of the output tile
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
@@ -215,135 +220,164 @@ __device__ inline int64_t poff(int64_t row, int64_t k, int64_t Kp)
 }
 
 // Waits with an immediate: lgkmcnt(0) only (vmcnt and expcnt left at their
-// maxima), so that loads in flight to registers are not waited for.
+// maxima), so that copies in flight are not waited for.
 constexpr int kWaitLgkm0 = 0xC07F;
 
+// 64 lanes x 16 bytes from g (per lane) to LDS at l + 16 lane.  Written as
+// inline asm so that the compiler, which would otherwise wait for every such
+// copy before any LDS read, leaves the waits to wait_vm; the kernel issues no
+// other vector-memory loads while copies are in flight.  M0 is set right
+// before each copy and used by nothing else in the kernel.
+__device__ inline void copy16_lds(const int8_t *g, unsigned l)
+{
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(l) : "memory");
+}
+template <int N> __device__ inline void wait_vm()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// SPLIT: the epilogue's quotient with 1/m in two fp32 parts (|P| up to 2^30,
+// Kp > 32768); one part suffices for |P| <= 2^29.
+template <bool SPLIT>
 __global__ __launch_bounds__(ONT, 1) void oz_gemm_kernel(const int8_t *__restrict__ RA,
                                                         const int8_t *__restrict__ RB, int64_t Kp,
                                                         uint8_t *__restrict__ Cres, OzConst c)
 {
     extern __shared__ __attribute__((aligned(1024))) int8_t oz_lds[];
-    int8_t *As = oz_lds;                               // [2][kOzBlock]
-    int8_t *Bs = oz_lds + 2 * kOzBlock;                // [2][kOzBlock]
+    constexpr int S = OSLOTS;
     const int r = blockIdx.y;
     const int64_t nt = Kp / OBM;
     int64_t ti, tj;
     lower_tile_grouped(xcd_order(blockIdx.x, gridDim.x), nt, ti, tj);
     const int64_t i0 = ti * OBM, j0 = tj * OBM;
     const int64_t plane = Kp * Kp;
-    const int64_t nk = Kp / OBK;                      // a multiple of 4
-
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wr = wave >> 1, wc = wave & 1;          // 4 x 2 waves of 64 x 128
-    const int woff = 2048 * wave + 16 * lane;         // this lane's bytes of a block: woff, woff + 1024
-    const int8_t *ga = RA + r * plane + ((ti * (Kp / OBK)) << 14) + woff;
-    const int8_t *gb = RB + r * plane + ((tj * (Kp / OBK)) << 14) + woff;
-
-    v4i g[2][4];
-    auto gload = [&](auto P, int64_t kt) {
-        constexpr int p = decltype(P)::value;
-        const int64_t kb = kt * kOzBlock;
-        g[p][0] = *(const v4i *)(ga + kb);
-        g[p][1] = *(const v4i *)(gb + kb);
-        g[p][2] = *(const v4i *)(ga + kb + 1024);
-        g[p][3] = *(const v4i *)(gb + kb + 1024);
-    };
-    auto lstore = [&](auto P, int slot) {
-        constexpr int p = decltype(P)::value;
-        int8_t *a0 = As + slot * kOzBlock + woff, *b0 = Bs + slot * kOzBlock + woff;
-        *(v4i *)a0 = g[p][0];
-        *(v4i *)b0 = g[p][1];
-        *(v4i *)(a0 + 1024) = g[p][2];
-        *(v4i *)(b0 + 1024) = g[p][3];
+    const int nk = (int)(Kp / OBK);                  // >= 4 = S
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wr = wave >> 1, wc = wave & 1;
+    // this wave copies chunks 4 wave + u / 2 (1 KiB each) of both operands' blocks
+    const int8_t *ga = RA + r * plane + ((ti * (Kp / OBK)) << 14) + 4096 * wave + 16 * lane;
+    const int8_t *gb = RB + r * plane + ((tj * (Kp / OBK)) << 14) + 4096 * wave + 16 * lane;
+    const unsigned lbase = (unsigned)(uintptr_t)(const __attribute__((address_space(3))) void *)oz_lds + 4096u * wave;
+    // copy u of stage kt (u even: A chunk u / 2, odd: B chunk u / 2) into a slot
+    auto copy = [&](int kt, int slot, int u) {
+        const int64_t kb = (int64_t)kt * kOzBlock + 1024 * (u >> 1);
+        copy16_lds(((u & 1) ? gb : ga) + kb, lbase + slot * kOzSlot + 1024 * (u >> 1) + (u & 1) * kOzBlock);
     };
 
-    v16i acc[2][4];
+    v16i acc[4][4];
 #pragma unroll
-    for (int bi = 0; bi < 2; ++bi)
+    for (int bi = 0; bi < 4; ++bi)
 #pragma unroll
         for (int bj = 0; bj < 4; ++bj)
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[bi][bj][e] = 0;
-
-    // LDS read offsets (bytes within a slot) for the two k32 halves of a stage
+    // LDS read offsets within a slot: row wr 128 + 32 bb + m of A (wc 128 + ... of
+    // B), chunk 2h + lane / 32 at position chunk ^ swz(row) = chunk ^ swz(m).
     const int m = lane & 31;
-    int offa[2][2], offb[2][4];
+    int oa[2], ob[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-        const int ch = 2 * h + (lane >> 5);
-#pragma unroll
-        for (int bb = 0; bb < 2; ++bb) {
-            const int ra = wr * 64 + bb * 32 + m;
-            offa[h][bb] = ra * OBK + 16 * (ch ^ swz(ra));
-        }
-#pragma unroll
-        for (int bb = 0; bb < 4; ++bb) {
-            const int rb = wc * 128 + bb * 32 + m;
-            offb[h][bb] = rb * OBK + 16 * (ch ^ swz(rb));
-        }
+        const int ch = (2 * h + (lane >> 5)) ^ swz(m);
+        oa[h] = (wr * 128 + m) * OBK + 16 * ch;
+        ob[h] = kOzBlock + (wc * 128 + m) * OBK + 16 * ch;
     }
-
-    // Stage kt: the barrier publishes stage kt (stored in LDS during stage kt - 1)
-    // and frees the other slot (read during stage kt - 1).  The registers of
-    // parity 1 - p hold stage kt + 1 (loaded during stage kt - 2): they go to
-    // LDS, then receive stage kt + 3.  The flags are compile-time so that the
-    // loop body has no branches and the compiler's wait counts stay exact.
-    auto step = [&](auto P, auto STORE, auto LOAD, int64_t kt) {
-        constexpr int p = decltype(P)::value;
-        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-        __builtin_amdgcn_s_barrier();
-        asm volatile("" ::: "memory");
-        const int8_t *Aq = As + p * kOzBlock, *Bq = Bs + p * kOzBlock;
-        v4i a[2][2], b[2][4];
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-#pragma unroll
-            for (int bb = 0; bb < 2; ++bb) a[h][bb] = *(const v4i *)(Aq + offa[h][bb]);
-#pragma unroll
-            for (int bb = 0; bb < 4; ++bb) b[h][bb] = *(const v4i *)(Bq + offb[h][bb]);
-        }
-        if constexpr (decltype(STORE)::value) lstore(std::integral_constant<int, 1 - p>{}, 1 - p);
-        if constexpr (decltype(LOAD)::value) gload(std::integral_constant<int, 1 - p>{}, kt + 3);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-            for (int bi = 0; bi < 2; ++bi)
-#pragma unroll
-                for (int bj = 0; bj < 4; ++bj)
-                    acc[bi][bj] = __builtin_amdgcn_mfma_i32_32x32x32_i8(b[h][bj], a[h][bi], acc[bi][bj], 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
+    // operand read u of half h, in the order the instructions first use them:
+    // a0, b0 .. b3, a1 .. a3
+    auto read = [&](v4i (&a)[4], v4i (&b)[4], int slot, int h, int u) {
+        const int8_t *q = oz_lds + slot * kOzSlot;
+        if (u == 0) a[0] = *(const v4i *)(q + oa[h]);
+        else if (u <= 4) b[u - 1] = *(const v4i *)(q + ob[h] + 2048 * (u - 1));
+        else a[u - 4] = *(const v4i *)(q + oa[h] + 2048 * (u - 4));
     };
-    using I0 = std::integral_constant<int, 0>;
-    using I1 = std::integral_constant<int, 1>;
-    using Y = std::true_type;
-    using N = std::false_type;
-    gload(I0{}, 0);
-    lstore(I0{}, 0);
-    gload(I1{}, 1);
-    gload(I0{}, 2);
-    for (int64_t kt = 0; kt < nk - 4; kt += 2) {
-        step(I0{}, Y{}, Y{}, kt);
-        step(I1{}, Y{}, Y{}, kt + 1);
+    // the 16 instructions of one k32 half, side(i) issued after instruction i
+    auto mma = [&](const v4i (&a)[4], const v4i (&b)[4], auto &&side) {
+        static_for<16>([&](auto I) {
+            constexpr int i = decltype(I)::value;
+            acc[i / 4][i % 4] = __builtin_amdgcn_mfma_i32_32x32x32_i8(b[i % 4], a[i / 4], acc[i / 4][i % 4], 0, 0, 0);
+            side(I);
+            __builtin_amdgcn_sched_barrier(0);
+        });
+    };
+
+    v4i a0[4], b0[4], a1[4], b1[4];
+    // Stage kt, entered with stage kt published and its first-half operands in
+    // a0/b0 (or on their way): first half, reading the second half's operands;
+    // wait for this wave's copies of stage kt + 1 and barrier (stage kt + 1
+    // published, every wave past its reads of stage kt - 1); second half,
+    // reading stage kt + 1's first-half operands.  Stage j's A chunks are copied
+    // in the second half of stage j - S + 1 (after the barrier that frees slot
+    // j % S), its B chunks in the first half of stage j - S + 2 (nothing reads
+    // the slot before stage j - 1's barrier).  WN: copies that may stay in
+    // flight at the barrier; CA / CB: copy A / B chunks; NEXT: not the last stage.
+    auto step = [&](auto WN, auto CA, auto CB, auto NEXT, int kt, int slot) {
+        const int nslot = slot == S - 1 ? 0 : slot + 1;
+        const int fslot = slot == 0 ? S - 1 : slot - 1;    // slot of stages kt - 1 and kt + S - 1
+        const int bslot = fslot == 0 ? S - 1 : fslot - 1;  // slot of stage kt + S - 2
+        mma(a0, b0, [&](auto I) {
+            constexpr int i = decltype(I)::value;
+            if constexpr (i % 2 == 0) read(a1, b1, slot, 1, i / 2);
+            else if constexpr (decltype(CB)::value && i % 4 == 1) copy(kt + S - 2, bslot, 2 * (i / 4) + 1);
+        });
+        if constexpr (decltype(NEXT)::value) {
+            wait_vm<decltype(WN)::value>();
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        mma(a1, b1, [&](auto I) {
+            constexpr int i = decltype(I)::value;
+            if constexpr (decltype(NEXT)::value) {
+                if constexpr (i % 2 == 0) read(a0, b0, nslot, 0, i / 2);
+                else if constexpr (decltype(CA)::value && i % 4 == 1) copy(kt + S - 1, fslot, 2 * (i / 4));
+            }
+        });
+    };
+    using T = std::true_type;
+    using F = std::false_type;
+    // prologue: stages 0 .. S - 3 whole, stage S - 2's A chunks
+#pragma unroll
+    for (int st = 0; st < S - 2; ++st)
+#pragma unroll
+        for (int u = 0; u < 8; ++u) copy(st, st, u);
+#pragma unroll
+    for (int u = 0; u < 8; u += 2) copy(S - 2, S - 2, u);
+    wait_vm<8 * (S - 3) + 4>();
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int u = 0; u < 8; ++u) read(a0, b0, 0, 0, u);
+    int slot = 0, kt = 0;
+    for (; kt <= nk - S; ++kt) {
+        step(std::integral_constant<int, 8 * (S - 3)>{}, T{}, T{}, T{}, kt, slot);
+        slot = slot == S - 1 ? 0 : slot + 1;
     }
-    step(I0{}, Y{}, Y{}, nk - 4);
-    step(I1{}, Y{}, N{}, nk - 3);
-    step(I0{}, Y{}, N{}, nk - 2);
-    step(I1{}, N{}, N{}, nk - 1);
+    static_for<S - 2>([&](auto J) {
+        constexpr int j = decltype(J)::value;
+        step(std::integral_constant<int, 8 * (S - 3 - j)>{}, F{}, std::integral_constant<bool, j == 0>{}, T{}, kt,
+             slot);
+        ++kt;
+        slot = slot == S - 1 ? 0 : slot + 1;
+    });
+    step(std::integral_constant<int, 0>{}, F{}, F{}, F{}, kt, slot);
 
     // Residues mod m in [0, m), 4 columns to a dword, through LDS to 16-byte
-    // row stores.  |P| <= K 2^14 < 2^30: the fp32 quotient is within 1 of
-    // P / m, so q is floor(P / m) or one off, |q| < 2^23 (an exact 24-bit
-    // product), and one correction each way lands in [0, m).  Diagonal tiles
-    // are written whole: entries above the diagonal are residues of the
-    // symmetric product too.
+    // row stores.  With |P| <= Kp 2^14, the fp32 value P / m - 1/2 (one fma) is
+    // within 1/2 of the exact one (checked on the CPU at and near the bounds),
+    // so q = floor of it is floor(P / m) or one below, P - q m lies in [0, 2m),
+    // and min(r, r - m) over unsigned ints lands in [0, m).  Diagonal tiles are
+    // written whole: entries above the diagonal are residues of the symmetric
+    // product too.
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     const int mi = c.m[r];
-    const float invm = 1.0f / (float)mi;
+    const float inv_hi = (float)c.inv_m[r];
+    const float inv_lo = (float)(c.inv_m[r] - (double)inv_hi);
 #pragma unroll
-    for (int bi = 0; bi < 2; ++bi)
+    for (int bi = 0; bi < 4; ++bi)
 #pragma unroll
         for (int bj = 0; bj < 4; ++bj)
 #pragma unroll
@@ -352,13 +386,14 @@ __global__ __launch_bounds__(ONT, 1) void oz_gemm_kernel(const int8_t *__restric
 #pragma unroll
                 for (int t = 0; t < 4; ++t) {
                     const int pv = acc[bi][bj][4 * q + t];
-                    const int qq = (int)floorf((float)pv * invm);
-                    int res = pv - __mul24(qq, mi);
-                    res += res < 0 ? mi : 0;
-                    res -= res >= mi ? mi : 0;
-                    w |= (unsigned)res << (8 * t);
+                    const float pf = (float)pv;
+                    const float y = SPLIT ? fmaf(pf, inv_hi, fmaf(pf, inv_lo, -0.5f)) : fmaf(pf, inv_hi, -0.5f);
+                    int qq;
+                    asm("v_cvt_flr_i32_f32 %0, %1" : "=v"(qq) : "v"(y));
+                    const unsigned rr = (unsigned)(__mul24(qq, -mi) + pv);
+                    w |= min(rr, rr - (unsigned)mi) << (8 * t);
                 }
-                const int li = wr * 64 + bi * 32 + m;
+                const int li = wr * 128 + bi * 32 + m;
                 const int lj = wc * 128 + bj * 32 + 8 * q + 4 * (lane >> 5);
                 *(unsigned *)(oz_lds + li * kOzEpiRow + lj) = w;
             }
@@ -374,9 +409,9 @@ __global__ __launch_bounds__(ONT, 1) void oz_gemm_kernel(const int8_t *__restric
     }
 }
 
-// dynamic LDS: the output tile (68 KiB) outlasts the two-slot ring (64 KiB)
-constexpr size_t kOzGemmLds = (size_t)OBM * kOzEpiRow;
-static_assert(kOzGemmLds >= (size_t)4 * kOzBlock, "LDS ring");
+// dynamic LDS: the 4-slot ring (128 KiB); the output tile (68 KiB) reuses it
+constexpr size_t kOzGemmLds = (size_t)OSLOTS * kOzSlot;
+static_assert(kOzGemmLds >= (size_t)OBM * kOzEpiRow, "output tile");
 
 // ---------------------------------------------------------------- CRT
 // One 64 x 64 lower tile per workgroup: reconstruct sum_k a_ik b_jk from its
@@ -614,12 +649,18 @@ hipError_t oz_product(const GemmDesc &d, const OzOperand &A, const OzOperand &B,
     if (d.N != K || d.Kd != K) return hipErrorInvalidValue;
     const int64_t Kp = oz_padded(K);
     const int64_t nt = Kp / OBM;
-    static bool lds_ok = hipFuncSetAttribute((const void *)oz_gemm_kernel,
-                                             hipFuncAttributeMaxDynamicSharedMemorySize,
-                                             (int)kOzGemmLds) == hipSuccess;
+    static bool lds_ok = hipFuncSetAttribute((const void *)oz_gemm_kernel<false>,
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)kOzGemmLds) == hipSuccess &&
+                         hipFuncSetAttribute((const void *)oz_gemm_kernel<true>,
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)kOzGemmLds) == hipSuccess;
     if (!lds_ok) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(oz_gemm_kernel, dim3((unsigned)(nt * (nt + 1) / 2), kOzMods), dim3(ONT), kOzGemmLds, s,
-                       A.planes, B.planes, Kp, Cres, oz_const());
+    // residues centred in [-128, 128): |P| <= Kp 2^14, within 2^29 up to Kp = 32768
+    if (Kp <= 32768)
+        hipLaunchKernelGGL(oz_gemm_kernel<false>, dim3((unsigned)(nt * (nt + 1) / 2), kOzMods), dim3(ONT), kOzGemmLds,
+                           s, A.planes, B.planes, Kp, Cres, oz_const());
+    else
+        hipLaunchKernelGGL(oz_gemm_kernel<true>, dim3((unsigned)(nt * (nt + 1) / 2), kOzMods), dim3(ONT), kOzGemmLds,
+                           s, A.planes, B.planes, Kp, Cres, oz_const());
     if (after_gemm) {
         const hipError_t e = hipEventRecord(after_gemm, s);
         if (e != hipSuccess) return e;
