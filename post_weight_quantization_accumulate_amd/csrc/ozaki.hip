@@ -48,7 +48,7 @@ constexpr int oz_limb_count()
 {
     int bits = 0;
     for (u128 m = oz_modulus(); m; m >>= 1) ++bits;
-    return (bits + 15) / 16;
+    return (bits + 16) / 16;                  // one spare bit: signed limbs of values up to M
 }
 constexpr int kLimbs = oz_limb_count();
 struct OzLimbs {
