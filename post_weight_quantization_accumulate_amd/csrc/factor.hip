@@ -152,14 +152,27 @@ constexpr int NBMAX = kPanel;
 constexpr int SB = 32;
 constexpr int PNT = 512;
 
+// fp64 lane exchanges: the value of lane `lane` (compile-time), and of lane
+// addr / 4 for each lane (ds_bpermute)
+__device__ inline double readlane_f64(double v, int lane)
+{
+    const int2 w = __builtin_bit_cast(int2, v);
+    return __builtin_bit_cast(double, make_int2(__builtin_amdgcn_readlane(w.x, lane), __builtin_amdgcn_readlane(w.y, lane)));
+}
+__device__ inline double bpermute_f64(int addr, double v)
+{
+    const int2 w = __builtin_bit_cast(int2, v);
+    return __builtin_bit_cast(double, make_int2(__builtin_amdgcn_ds_bpermute(addr, w.x), __builtin_amdgcn_ds_bpermute(addr, w.y)));
+}
+
 // One wave: Cholesky of the 32 x 32 block at (o, o) of A.  Lane l owns rows
-// 4 (l / 8) + i and columns 4 (l % 8) + k.  A wave's LDS operations complete in
-// issue order, so a value published to LDS is visible to the reads that follow
-// it; the wave barriers only stop the compiler from reordering them.  Writes R
-// (upper) into A and 1 / R_jj into rinv[o + j].  Returns true if a pivot of a
-// real (not padded) row was not positive.
-__device__ __attribute__((noinline)) bool wave_factor32(double (*A)[NBMAX + 1], double *rowj, double *rinv, int o,
-                                                        int nb, int lane)
+// 4 (l / 8) + i and columns 4 (l % 8) + k in registers.  Step j takes the pivot
+// from the lane holding (j, j) (readlane) and the pivot row from the 8 lanes
+// holding row j (one permute per value, issued while the pivot's inverse square
+// root is computed).  Writes R (upper) into A and 1 / R_jj into rinv[o + j].
+// Returns true if a pivot of a real (not padded) row was not positive.
+__device__ __attribute__((noinline)) bool wave_factor32(double (*A)[NBMAX + 1], double *rinv, int o, int nb,
+                                                        int lane)
 {
     const int br = lane >> 3, bc = lane & 7;
     double a[4][4];
@@ -171,17 +184,18 @@ __device__ __attribute__((noinline)) bool wave_factor32(double (*A)[NBMAX + 1], 
             a[i][k] = (c >= r) ? A[o + r][o + c] : 0.0;
         }
     bool badp = false;
-    // Step j with j a compile-time constant: row and column tests against j fold
-    // wherever the lane's static tile index decides them.
     static_for<SB>([&](auto J) {
         constexpr int j = decltype(J)::value;
-        if (br == (j >> 2)) {
+        constexpr int g = j >> 2, e = j & 3;             // row j: lanes 8 g + bc, register row e
+        const double piv0 = readlane_f64(a[e][e], 9 * g);   // (j, j): lane 8 g + g
+        // row j of the current matrix: columns 4 br + i (for the row factors) and
+        // 4 bc + k (for the column factors)
+        double vr[4], vc[4];
 #pragma unroll
-            for (int k = 0; k < 4; ++k) rowj[4 * bc + k] = a[j & 3][k];
-        }
-        __builtin_amdgcn_wave_barrier();
-        const double piv0 = rowj[j];
-        badp = badp || (!(piv0 > 0.0) && o + j < nb);
+        for (int i = 0; i < 4; ++i) vr[i] = bpermute_f64(4 * (8 * g + br), a[e][i]);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) vc[k] = bpermute_f64(4 * (8 * g + bc), a[e][k]);
+        badp |= !(piv0 > 0.0) & (o + j < nb);
         const double piv = piv0 > 0.0 ? piv0 : 1.0;
         // 1/sqrt(piv) from the hardware estimate and two Newton steps
         // y <- y + y (1/2 - (piv/2) y^2) (quadratic convergence to full double
@@ -193,22 +207,25 @@ __device__ __attribute__((noinline)) bool wave_factor32(double (*A)[NBMAX + 1], 
         inv = fma(inv, fma(-hp * inv, inv, 0.5), inv);
         const double rjj = piv * inv;
         if (lane == 0) rinv[o + j] = inv;
-        double vr[4], vc[4];
+        // A[r][c] -= R_jr R_jc = (A_jr / piv) A_jc for r > j, c >= r: the row
+        // factor is 0 for r <= j, so every lane updates its whole tile with plain
+        // fmas (entries below the diagonal are never read back)
+        const double inv2 = inv * inv;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) vr[i] = rowj[4 * br + i] * inv;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) vc[k] = rowj[4 * bc + k] * inv;
+        for (int i = 0; i < 4; ++i) vr[i] = (4 * br + i > j) ? vr[i] * inv2 : 0.0;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {          // branch-free: every lane computes both
-                const int r = 4 * br + i, c = 4 * bc + k;
-                const double v = a[i][k];
-                const double scl = (c == j) ? rjj : ((c > j) ? v * inv : v);
-                const double upd = fma(-vr[i], vc[k], v);
-                a[i][k] = (r == j) ? scl : ((r > j && c >= r) ? upd : v);
+            for (int k = 0; k < 4; ++k) a[i][k] = fma(-vr[i], vc[k], a[i][k]);
+        // row j of R: R_jj = sqrt(piv), R_jc = A_jc / sqrt(piv) for c > j
+        if (br == g) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int c = 4 * bc + k;
+                const double v = a[e][k];
+                a[e][k] = (c == j) ? rjj : ((c > j) ? v * inv : v);
             }
-        __builtin_amdgcn_wave_barrier();
+        }
     });
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -253,7 +270,6 @@ __global__ __launch_bounds__(PNT) void potrf_diag_kernel(double *__restrict__ M,
 {
     __shared__ double A[NBMAX][NBMAX + 1];
     __shared__ double rinv[NBMAX];
-    __shared__ double rowj[SB];
     __shared__ int bad;
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
 
@@ -283,7 +299,7 @@ __global__ __launch_bounds__(PNT) void potrf_diag_kernel(double *__restrict__ M,
     for (int s = 0; s < NBMAX / SB; ++s) {
         const int o = s * SB;
         if (wave == 0) {
-            const bool b = wave_factor32(A, rowj, rinv, o, nb, lane);
+            const bool b = wave_factor32(A, rinv, o, nb, lane);
             if (b && lane == 0) bad = 1;
         }
         __syncthreads();
