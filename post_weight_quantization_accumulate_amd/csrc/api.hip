@@ -21,7 +21,7 @@ thread_local std::string g_last_error;
 // the default priority and kept until the process ends.
 struct Lookahead {
     int dev = -1;
-    hipStream_t side = nullptr;                        // diagonal blocks of the Cholesky
+    hipStream_t side = nullptr;                        // trailing updates of the Cholesky
     hipStream_t inv = nullptr;                         // the triangular inverse, alongside
     hipEvent_t to_side = nullptr, to_main = nullptr, to_inv = nullptr, inv_done = nullptr;
 };
@@ -323,16 +323,20 @@ int run_factor(float *U, const float *H, int64_t K, float damp, FactorWs &w, hip
         u.beta = 1.0;
         return gemm_tn_f64(u, la->inv);
     };
-    // Right-looking blocked Cholesky with a look-ahead of one panel: once the
-    // block row of panel p+1 has its update from panel p, the diagonal block
-    // p+1 is factored on the side stream while the rest of the trailing update
-    // of panel p runs on the caller's stream.
+    // Right-looking blocked Cholesky with a look-ahead of one panel.  Once the
+    // block row of panel p+1 has its update from panel p, the diagonal block p+1
+    // is factored right behind it on the caller's stream, while the rest of the
+    // trailing update of panel p runs on the side stream.  The diagonal kernel
+    // (one workgroup holding its block in LDS) thus reaches the hardware before
+    // the large update's workgroups fill every CU, instead of waiting for one to
+    // drain.  The block row of panel p+2 needs that update before its own, so
+    // the next block-row update waits for the side stream.
     GQ_HIP(launch_potrf_diag(w.M, K, 0, (int)(K < kPanel ? K : kPanel), w.rinv, w.sc.status, s), "potrf diag");
+    bool side_pending = false;
     for (int64_t p = 0; p < nblk; ++p) {
         const int64_t p0 = p * kPanel;
         const int nbp = (int)((K - p0) < kPanel ? (K - p0) : kPanel);
         const int64_t p1 = p0 + nbp;
-        if (p > 0) GQ_HIP(hipStreamWaitEvent(s, la->to_main, 0), "wait diagonal block");
         if (p1 >= K) {
             GQ_HIP(inverse_rows(p), "inverse rows");
             break;
@@ -343,23 +347,22 @@ int run_factor(float *U, const float *H, int64_t K, float damp, FactorWs &w, hip
                "trsm");
         GQ_HIP(inverse_rows(p), "inverse rows");
         // trailing update of the upper triangle, A_rest -= R_{p,rest}^T R_{p,rest}:
-        // first the block row of panel p+1 ...
+        // first the block row of panel p+1 (which has panel p-1's update once the
+        // side stream's last product is done) ...
         const int nbn = (int)((K - p1) < kPanel ? (K - p1) : kPanel);
         const int64_t p2 = p1 + nbn;
+        if (side_pending) GQ_HIP(hipStreamWaitEvent(s, la->to_main, 0), "wait trailing update");
         GemmDesc un = gemm(w.M + p0 * K + p1, K, w.M + p0 * K + p1, K, nbn, K - p1, nbp, w.M + p1 * K + p1, K);
         un.cin = w.M + p1 * K + p1;
         un.alpha = -1.0;
         un.beta = 1.0;
         un.tri = 2;
         GQ_HIP(gemm_tn_f64(un, s), "syrk next row");
-        // ... then its diagonal block on the side stream ...
-        GQ_HIP(hipEventRecord(la->to_side, s), "record");
-        GQ_HIP(hipStreamWaitEvent(la->side, la->to_side, 0), "wait trailing row");
-        GQ_HIP(launch_potrf_diag(w.M, K, p1, nbn, w.rinv + (p + 1) * kRinvPerPanel, w.sc.status, la->side),
-               "potrf diag");
-        GQ_HIP(hipEventRecord(la->to_main, la->side), "record");
-        // ... while the rest of the trailing update runs here
-        if (p2 < K) {
+        // ... then the rest on the side stream ...
+        side_pending = p2 < K;
+        if (side_pending) {
+            GQ_HIP(hipEventRecord(la->to_side, s), "record");
+            GQ_HIP(hipStreamWaitEvent(la->side, la->to_side, 0), "wait block row");
             GemmDesc u = gemm(w.M + p0 * K + p2, K, w.M + p0 * K + p2, K, K - p2, K - p2, nbp,
                               w.M + p2 * K + p2, K);
             u.cin = w.M + p2 * K + p2;
@@ -367,9 +370,13 @@ int run_factor(float *U, const float *H, int64_t K, float damp, FactorWs &w, hip
             u.beta = 1.0;
             u.mode = TILE_UPPER;
             u.tri = 2;
-            GQ_HIP(gemm_tn_f64(u, s), "syrk");
+            GQ_HIP(gemm_tn_f64(u, la->side), "syrk");
+            GQ_HIP(hipEventRecord(la->to_main, la->side), "record");
         }
+        // ... while the diagonal block of panel p+1 is factored here
+        GQ_HIP(launch_potrf_diag(w.M, K, p1, nbn, w.rinv + (p + 1) * kRinvPerPanel, w.sc.status, s), "potrf diag");
     }
+    if (side_pending) GQ_HIP(hipStreamWaitEvent(s, la->to_main, 0), "wait trailing update");
     GQ_HIP(hipEventRecord(la->inv_done, la->inv), "record");
     GQ_HIP(hipStreamWaitEvent(s, la->inv_done, 0), "wait inverse");
     // U = J R^-T J = J L^-1 J: U[i][j] = X[K-1-i][K-1-j]
