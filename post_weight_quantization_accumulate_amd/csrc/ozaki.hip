@@ -83,6 +83,9 @@ constexpr OzInv oz_inverses()
 }
 constexpr OzInv kOzInv = oz_inverses();
 constexpr OzLimbs kOzLimbs = oz_limbs();
+static_assert(kLimbs >= 3, "quotient estimate from the top three limbs");
+// 1/M scaled by the weight of limb kLimbs - 3 (a power of two: exact)
+constexpr double kOzInvMTop = kOzLimbs.invM * (double)((u128)1 << (16 * (kLimbs - 3)));
 // The weight limbs of moduli 2j and 2j+1 side by side (u16 pairs), for
 // v_dot2_u32_u16: one instruction adds both moduli's products into a limb sum.
 static_assert(kOzMods % 2 == 0, "moduli in pairs");
@@ -114,17 +117,31 @@ __device__ inline i128 from_signed_limbs(const int (&D)[kLimbs])
     return (i128)x;
 }
 
-// Residue of the integer z (|z| <= 2^48) modulo kMods[r], as the int8 byte the
-// products use.  Odd m: the fp64 quotient z (1/m) is within 2^-11.6 of z / m,
-// which lies at least 1/(2m) > 2^-9 from a half-integer, so rint gives the
-// nearest integer and z - m rint(z (1/m)) is the centred residue, exactly (fma).
-// m = 256: z - 256 floor(z / 256) in [0, 256), whose low byte is the two's
-// complement residue.
-__device__ inline unsigned residue_byte(double z, int r)
+// Residues of the integers z[0..3] (|z| <= 2^48) modulo kMods[r], packed as the
+// int8 bytes the products use (byte t from z[t]).  Odd m: z (1/m) + 1.5 2^52,
+// rounded once by the fma, is 1.5 2^52 plus the integer q nearest z / m (z / m
+// lies at least 1/(2m) > 2^-9 from a half-integer, and the fp64 1/m moves it by
+// under 2^-12), so z - m q is the centred residue, exactly; plus 1.5 2^52 it
+// sits, in two's complement, in the low 32 bits.  m = 256: the low byte of
+// z + 1.5 2^52 is z mod 256.
+constexpr double kOzMagic = 6755399441055744.0;   // 1.5 2^52
+__device__ inline unsigned residue_word(const double (&z)[4], int r)
 {
-    if (r == 0) return (unsigned)(int)fma(-256.0, floor(z * (1.0 / 256.0)), z) & 0xFFu;
-    const double m = (double)kMods[r];
-    return (unsigned)(int)fma(-m, rint(z * kOzInv.v[r]), z) & 0xFFu;
+    unsigned b[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        double v;
+        if (r == 0) {
+            v = z[t] + kOzMagic;
+        } else {
+            const double q = fma(z[t], kOzInv.v[r], kOzMagic) - kOzMagic;
+            v = fma(-(double)kMods[r], q, z[t]) + kOzMagic;
+        }
+        b[t] = (unsigned)__builtin_bit_cast(unsigned long long, v);
+    }
+    const unsigned x01 = __builtin_amdgcn_perm(b[1], b[0], 0x0C0C0400u);
+    const unsigned x23 = __builtin_amdgcn_perm(b[3], b[2], 0x0C0C0400u);
+    return __builtin_amdgcn_perm(x23, x01, 0x05040100u);
 }
 
 // ---------------------------------------------------------------- split
@@ -168,16 +185,10 @@ __global__ __launch_bounds__(SPL_NT) void oz_split_kernel(const double *__restri
         double z[8];
 #pragma unroll
         for (int t = 0; t < 8; ++t) z[t] = (k0 + t < K) ? rint(zr[k0 + t] * sc) : 0.0;   // exact integers
+        const double z0[4] = {z[0], z[1], z[2], z[3]}, z1[4] = {z[4], z[5], z[6], z[7]};
 #pragma unroll
-        for (int r = 0; r < kOzMods; ++r) {
-            unsigned w0 = 0, w1 = 0;
-#pragma unroll
-            for (int t = 0; t < 8; ++t) {
-                const unsigned b = residue_byte(z[t], r);
-                if (t < 4) w0 |= b << (8 * t); else w1 |= b << (8 * (t - 4));
-            }
-            *(uint2 *)(planes + r * plane + poff(i, k0, Kp)) = make_uint2(w0, w1);
-        }
+        for (int r = 0; r < kOzMods; ++r)
+            *(uint2 *)(planes + r * plane + poff(i, k0, Kp)) = make_uint2(residue_word(z0, r), residue_word(z1, r));
     }
 }
 
@@ -490,13 +501,13 @@ __global__ __launch_bounds__(CNT) void oz_crt_kernel(GemmDesc d, const uint8_t *
                     for (int j = 0; j < kOzMods / 2; ++j)
                         L[k] = __builtin_amdgcn_udot2(cp[j], __builtin_bit_cast(u16x2, kOzPairs.w[j][k]), L[k], false);
                 // The centred value is x = S - q M with q the integer nearest S / M:
-                // |x| <= K 2^(2 beta) < 0.497 M (the choice of beta), and the fp64
-                // estimate of S / M < 2^12 is within 2^-38 of it.  x by signed limbs
-                // L[k] - q M[k] (q M[k] < 2^28), one carry pass in 128 bits.
-                double Sd = (double)L[kLimbs - 1];
-#pragma unroll
-                for (int k = kLimbs - 2; k >= 0; --k) Sd = fma(Sd, 65536.0, (double)L[k]);
-                const int nq = -(int)rint(Sd * kOzLimbs.invM);
+                // |x| <= K 2^(2 beta) < 0.497 M (the choice of beta).  S / M < 2^12 is
+                // estimated from the top three limbs (the rest adds below 2^-19 to
+                // it) within 2^-19 + 2^-38, far inside the 0.003 margin.  x by signed
+                // limbs L[k] - q M[k] (q M[k] < 2^28), one carry pass in 128 bits.
+                const double St = fma(fma((double)L[kLimbs - 1], 65536.0, (double)L[kLimbs - 2]), 65536.0,
+                                      (double)L[kLimbs - 3]);
+                const int nq = -(int)rint(St * kOzInvMTop);
                 int D[kLimbs];
 #pragma unroll
                 for (int k = 0; k < kLimbs; ++k) D[k] = __mul24(nq, (int)kOzLimbs.M[k]) + (int)L[k];
@@ -511,11 +522,16 @@ __global__ __launch_bounds__(CNT) void oz_crt_kernel(GemmDesc d, const uint8_t *
             tile[li][c4 + t] = v;
         }
     };
+    // two rows in flight: each row's residues are loaded while the one before is
+    // reconstructed (the last load repeats row 3, in bounds and unused)
+    unsigned ra[kOzMods], rb[kOzMods];
+    load_row(ra, 0);
 #pragma unroll 1
-    for (int rr = 0; rr < CT / 16; ++rr) {
-        unsigned rs[kOzMods];
-        load_row(rs, rr);
-        do_row(rs, rr);
+    for (int rr = 0; rr < CT / 16; rr += 2) {
+        load_row(rb, rr + 1);
+        do_row(ra, rr);
+        load_row(ra, rr + 2 < CT / 16 ? rr + 2 : rr + 1);
+        do_row(rb, rr + 1);
     }
     __syncthreads();
     OutT *out = (OutT *)d.out;
@@ -563,9 +579,7 @@ __global__ __launch_bounds__(CNT) void oz_crt_kernel(GemmDesc d, const uint8_t *
             int8_t *pl = planes + r * plane;
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) {
-                unsigned w = 0;
-#pragma unroll
-                for (int t = 0; t < 4; ++t) w |= residue_byte(z[rr][t], r) << (8 * t);
+                const unsigned w = residue_word(z[rr], r);
                 const int li = rr * 16 + lr;
                 rt[q][li][c4 >> 2] = w;
                 if (i0 + li < K) *(unsigned *)(pl + poff(i0 + li, j0 + c4, Kp)) = w;
@@ -617,7 +631,7 @@ int oz_beta(int64_t K)
 {
     // largest beta with K 2^(2 beta) <= 0.497 M, i.e. 2 beta <= log2 M - 1.01 - log2 K
     // (the reconstruction rounds S / M to the nearest integer and needs the
-    // centred sum to stay clear of M / 2), and at most 48, where residue_byte's
+    // centred sum to stay clear of M / 2), and at most 48, where residue_word's
     // quotient is exact (48 from K = 4100 up to 8192, 47 to 17408)
     const OzConst &c = oz_const();
     const double log2M = std::log2(ldexp((double)c.M_hi, 64) + (double)c.M_lo);
