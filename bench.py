@@ -243,9 +243,35 @@ def main():
             "launches_per_step": prod["launches"] / args.steps,
         },
     }
+    out["rtn"] = rtn_measure(gq, torch, W, imp, G, dev)
+    out["rtn"]["qerr_gptq_over_rtn"] = qerr[0] / out["rtn"]["qerr"] if out["rtn"]["qerr"] else None
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, X, W)
     print(json.dumps(out))
+
+
+def rtn_measure(gq, torch, W, imp, G, dev, reps=10):
+    """The round-to-nearest pack of the same weights on the same grid (with qerr,
+    the same importance), timed after the GPTQ steps.  One kernel reads W and imp
+    once and writes codes, scales and qerr's partial sums; ms_per_call is the
+    whole API call (launches, status and qerr readback, host synchronisation)."""
+    N, K = W.shape
+    codes = torch.empty(N * (K // 2), dtype=torch.uint8, device=dev)
+    scales = torch.empty(N * (K // G), dtype=torch.float32, device=dev)
+    ws = gq.workspace(gq.rtn_quantize_workspace_size(N, K, G), dev)
+    q = gq.rtn_quantize(codes, scales, W, imp, G, ws)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(reps):
+        gq.rtn_quantize(codes, scales, W, imp, G, ws)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    nbytes = 4 * N * K + N * K // 2 + 4 * N * K // G + 4 * K
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"ms_per_call": ms, "algorithmic_bytes": nbytes, "achieved_gb_per_s": gbs,
+            "frac_of_hbm_peak": gbs / 8000.0, "weights_per_s": N * K / (ms * 1e-3), "qerr": q}
 
 
 if __name__ == "__main__":

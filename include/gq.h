@@ -213,6 +213,27 @@ int gptq_quantize(uint8_t *codes, float *scales, double *qerr_out, const float *
                   const float *H, const float *imp, int64_t N, int64_t K, int64_t group,
                   float damp, void *ws, size_t ws_bytes, hipStream_t stream);
 
+/* Workspace bytes rtn_quantize needs (a few KB, independent of the sizes). */
+size_t rtn_quantize_workspace_size(int64_t N, int64_t K, int64_t group);
+
+/*
+ * rtn_quantize -- round-to-nearest pack of W on the same int4 grid as
+ * gptq_sweep, with no error feedback: per (row, group) scale absmax/7 of the
+ * original weights, code = clamp(rint(w / scale), -8, 7) with an IEEE fp32
+ * division and ties to even (0 for an all-zero group), and optionally the same
+ * qerr.  It is the uniform pack whose qerr a re-tiering pass ranks by, and the
+ * comparator GPTQ's codes are judged against (ork-driver wiki, "Exp 2026-08-18
+ * GPTQ Int4": the producer of a pack's qerr field and its uniform-weight check).
+ * Codes and scales are identical whether or not qerr_out is given.
+ *   codes, scales, qerr_out, W, imp, N, K, group: as for gptq_sweep (device
+ *             pointers except qerr_out; codes and scales written, W and imp read).
+ *   ws        at least rtn_quantize_workspace_size(N, K, group) bytes.
+ * Synchronises `stream`.
+ * Errors: GQ_ERR_INVALID_ARG, GQ_ERR_NONFINITE (W or imp).
+ */
+int rtn_quantize(uint8_t *codes, float *scales, double *qerr_out, const float *W, const float *imp,
+                 int64_t N, int64_t K, int64_t group, void *ws, size_t ws_bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

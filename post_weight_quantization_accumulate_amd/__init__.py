@@ -27,7 +27,7 @@ EXPORTS = (
     "hessian_pack_tril", "hessian_unpack_tril", "psd_project_workspace_size", "psd_project",
     "psd_project_flops", "psd_project_products", "gq_set_timing", "psd_project_last_timing", "gq_set_psd_products",
     "gptq_factor_workspace_size", "gptq_factor", "gptq_sweep_workspace_size", "gptq_sweep",
-    "gptq_quantize_workspace_size", "gptq_quantize",
+    "gptq_quantize_workspace_size", "gptq_quantize", "rtn_quantize_workspace_size", "rtn_quantize",
 )
 
 
@@ -70,6 +70,8 @@ def lib() -> ctypes.CDLL:
             "gptq_sweep": (I, [P, P, P, P, P, P, I64, I64, I64, P, SZ, P]),
             "gptq_quantize_workspace_size": (SZ, [I64, I64, I64]),
             "gptq_quantize": (I, [P, P, P, P, P, P, I64, I64, I64, F, P, SZ, P]),
+            "rtn_quantize_workspace_size": (SZ, [I64, I64, I64]),
+            "rtn_quantize": (I, [P, P, P, P, P, I64, I64, I64, P, SZ, P]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -216,6 +218,25 @@ def gptq_sweep(codes, scales, W, U, imp, group: int, ws, want_qerr: bool = True)
     _check(lib().gptq_sweep(_ptr(codes), _ptr(scales), ctypes.byref(q) if want_qerr else None,
                             _ptr(W), _ptr(U), _ptr(imp), N, K, group, _ptr(ws), ws.numel(),
                             _stream(W)), "gptq_sweep")
+    return q.value if want_qerr else None
+
+
+def rtn_quantize_workspace_size(N: int, K: int, group: int) -> int:
+    return int(lib().rtn_quantize_workspace_size(N, K, group))
+
+
+def rtn_quantize(codes, scales, W, imp, group: int, ws, want_qerr: bool = True):
+    """Round-to-nearest codes/scales of W on the sweep's grid; returns qerr (or None)."""
+    N, K = W.shape
+    _need(W, "W", torch.float32)
+    _need(codes, "codes", torch.uint8, N * (K // 2))
+    _need(scales, "scales", torch.float32, N * (K // max(group, 1)))
+    if imp is not None:
+        _need(imp, "imp", torch.float32, K)
+    _need(ws, "ws", torch.uint8)
+    q = ctypes.c_double(0.0)
+    _check(lib().rtn_quantize(_ptr(codes), _ptr(scales), ctypes.byref(q) if want_qerr else None,
+                              _ptr(W), _ptr(imp), N, K, group, _ptr(ws), ws.numel(), _stream(W)), "rtn_quantize")
     return q.value if want_qerr else None
 
 

@@ -748,6 +748,60 @@ int gptq_sweep(uint8_t *codes, float *scales, double *qerr_out, const float *W, 
     return run_sweep(codes, scales, qerr_out, W, U, imp, N, K, group, w, stream);
 }
 
+struct RtnWs {
+    Scalars sc;
+    double *partials;                                  // rtn_partials(N, K) pairs
+};
+
+RtnWs carve_rtn(Carver &c, int64_t N, int64_t K)
+{
+    RtnWs w;
+    w.sc = carve_scalars(c);
+    w.partials = c.take<double>((size_t)2 * (size_t)rtn_partials(N, K));
+    return w;
+}
+
+size_t rtn_quantize_workspace_size(int64_t N, int64_t K, int64_t group)
+{
+    (void)group;
+    if (N < 1 || K < 1) return 0;
+    Carver c(nullptr);
+    carve_rtn(c, N, K);
+    return c.off;
+}
+
+int rtn_quantize(uint8_t *codes, float *scales, double *qerr_out, const float *W, const float *imp, int64_t N,
+                 int64_t K, int64_t group, void *ws, size_t ws_bytes, hipStream_t stream)
+{
+    g_last_error.clear();
+    if (!codes || !scales || !W) return fail(GQ_ERR_INVALID_ARG, "null required pointer");
+    if (N < 1) return fail(GQ_ERR_INVALID_ARG, "N must be >= 1");
+    if (K < 2 || (K & 1)) return fail(GQ_ERR_INVALID_ARG, "K must be even and >= 2 (two codes per byte)");
+    if (!valid_group(group, K))
+        return fail(GQ_ERR_INVALID_ARG, "group must be a power of two <= 128 that divides K");
+    if (!ws) return fail(GQ_ERR_INVALID_ARG, "null workspace");
+    if (ws_bytes < rtn_quantize_workspace_size(N, K, group)) return fail(GQ_ERR_INVALID_ARG, "workspace too small");
+    Carver cv(ws);
+    const RtnWs w = carve_rtn(cv, N, K);
+    GQ_HIP(launch_fill_u32(w.sc.status, 4, 0u, stream), "fill");
+    if (imp) GQ_HIP(launch_check_finite(imp, K, w.sc.status, stream), "check imp");
+    int64_t nparts = 0;
+    GQ_HIP(launch_rtn(W, codes, scales, imp, qerr_out ? w.partials : nullptr, N, K, group, w.sc.status, stream,
+                      &nparts),
+           "rtn");
+    if (qerr_out) GQ_HIP(launch_qerr_reduce(w.sc.d, w.partials, nparts, stream), "qerr reduce");
+    // status and the two sums come back with one synchronisation
+    unsigned st = 0;
+    double nd[2] = {0.0, 0.0};
+    GQ_HIP(hipMemcpyAsync(&st, w.sc.status, sizeof(st), hipMemcpyDeviceToHost, stream), "status readback");
+    if (qerr_out) GQ_HIP(hipMemcpyAsync(nd, w.sc.d, sizeof(nd), hipMemcpyDeviceToHost, stream), "qerr readback");
+    GQ_HIP(hipStreamSynchronize(stream), "stream synchronize");
+    const int rc = status_to_code(st);
+    if (rc) return rc;
+    if (qerr_out) *qerr_out = nd[1] > 0.0 ? std::sqrt(nd[0] / nd[1]) : 0.0;
+    return GQ_OK;
+}
+
 size_t gptq_quantize_workspace_size(int64_t N, int64_t K, int64_t group)
 {
     (void)group;

@@ -267,6 +267,153 @@ unsigned grid_for(int64_t n)
     return (unsigned)g;
 }
 
+// ---------------------------------------------------------------- round to nearest
+// The same int4 grid without error feedback: per (row, group) scale s = absmax/7
+// from the weights themselves, code = clamp(rint(w / s), -8, 7) (IEEE fp32
+// division, ties to even; 0 for an all-zero group), packed as the sweep packs
+// them.  The comparator the GPTQ codes are judged against, and a uniform pack
+// that still records qerr (ork-driver wiki, "Exp 2026-08-18 GPTQ Int4", the
+// producer for a pack's qerr field).
+__device__ inline float rtn_code(float w, float s)
+{
+    return s == 0.0f ? 0.0f : fminf(fmaxf(rintf(w / s), -8.0f), 7.0f);
+}
+__device__ inline unsigned rtn_nibble(float w, float s) { return (unsigned)(int)rtn_code(w, s) & 0xFu; }
+
+// One thread per 8 consecutive columns of a row at a time (K % 8 == 0, 16-byte
+// aligned W, 4-byte aligned codes): two 16-byte loads, one 4-byte store of 8
+// codes; the grid strides over the rows' 8-column chunks with the same trip
+// count in every thread of a workgroup.  A group of G >= 8 spans G/8
+// consecutive threads, aligned within the wave (the row length K/8 in threads
+// is a multiple of G/8 <= 16), and takes its maximum by lane exchanges; for
+// G < 8 a thread holds whole groups.  The code is rint of the correctly rounded
+// fp32 quotient w / s, formed from y = RN(1/s) by one Markstein correction
+// (Markstein 1990; Muller et al., Handbook of Floating-Point Arithmetic,
+// division via FMA): q0 = RN(w y), r = w - s q0 exactly, RN(q0 + r y) = RN(w / s)
+// while the quotient and 1/s stay normal, so a group with s below 2^-60 (whose
+// weights are all below 2^-57) is first scaled by 2^64, exactly.  Non-finite
+// weights set ST_NONFINITE.  With partials set, the workgroup also writes its
+// pair (sum imp (w - c s)^2, sum imp w^2) in fp64, as qerr_kernel defines them,
+// to partials[2 blockIdx.x ..] (a fixed-order tree, so the sums are
+// deterministic): no second pass over W.
+constexpr int RTN_NT = QNT;
+constexpr int RTN_MAX_WG = 2048;
+__device__ inline float rtn_code_y(float w, float s, float y)
+{
+    const float q0 = w * y;
+    const float r = fmaf(-s, q0, w);
+    return fminf(fmaxf(rintf(fmaf(r, y, q0)), -8.0f), 7.0f);
+}
+__global__ __launch_bounds__(RTN_NT) void rtn8_kernel(const float *__restrict__ W, uint8_t *__restrict__ codes,
+                                                      float *__restrict__ scales, int64_t N, int64_t K, int G,
+                                                      unsigned *status, const float *__restrict__ imp,
+                                                      double *__restrict__ partials)
+{
+    const int64_t chunks = K / 8, total = N * chunks;
+    const int64_t ngroups = K / G;
+    double num = 0.0, den = 0.0;
+    bool bad = false;
+    for (int64_t base = (int64_t)blockIdx.x * RTN_NT; base < total; base += (int64_t)gridDim.x * RTN_NT) {
+        const int64_t idx = base + threadIdx.x;
+        const bool valid = idx < total;
+        const int64_t id = valid ? idx : 0;          // every lane takes part in the exchanges
+        const int64_t row = id / chunks, c = id - row * chunks;
+        const float4 a = *(const float4 *)(W + row * K + 8 * c);
+        const float4 b = *(const float4 *)(W + row * K + 8 * c + 4);
+        const float w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+        for (int t = 0; t < 8; ++t) bad = bad || (valid && !isfinite(w[t]));
+        float sc[8], cv[8];                          // each column's scale and code
+        // the codes of columns t0 .. t1-1 under the group scale sg
+        auto codes_of = [&](float sg, int t0, int t1) {
+            const bool tiny = sg < 0x1p-60f;
+            const float f = tiny ? 0x1p64f : 1.0f;
+            const float ss = sg == 0.0f ? 1.0f : sg * f;
+            const float y = 1.0f / ss;
+            for (int t = t0; t < t1; ++t) {
+                sc[t] = sg;
+                cv[t] = sg == 0.0f ? 0.0f : rtn_code_y(w[t] * f, ss, y);
+            }
+        };
+        if (G >= 8) {
+            float m = 0.0f;
+#pragma unroll
+            for (int t = 0; t < 8; ++t) m = fmaxf(m, fabsf(w[t]));
+            for (int o = 1; o < G / 8; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
+            const float sg = m / 7.0f;
+            if (valid && c % (G / 8) == 0) scales[row * ngroups + 8 * c / G] = sg;
+            codes_of(sg, 0, 8);
+        } else {
+            for (int g0 = 0; g0 < 8; g0 += G) {
+                float m = 0.0f;
+                for (int t = g0; t < g0 + G; ++t) m = fmaxf(m, fabsf(w[t]));
+                const float sg = m / 7.0f;
+                if (valid) scales[row * ngroups + (8 * c + g0) / G] = sg;
+                codes_of(sg, g0, g0 + G);
+            }
+        }
+        unsigned dw = 0;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) dw |= ((unsigned)(int)cv[t] & 0xFu) << (4 * t);
+        if (valid) *(unsigned *)(codes + row * (K / 2) + 4 * c) = dw;
+        if (partials && valid) {
+            float iw[8] = {1.0f, 1.0f, 1.0f, 1.0f, 1.0f, 1.0f, 1.0f, 1.0f};
+            if (imp) {                               // 16-byte aligned (checked at launch)
+                const float4 i0 = *(const float4 *)(imp + 8 * c), i1 = *(const float4 *)(imp + 8 * c + 4);
+                iw[0] = i0.x; iw[1] = i0.y; iw[2] = i0.z; iw[3] = i0.w;
+                iw[4] = i1.x; iw[5] = i1.y; iw[6] = i1.z; iw[7] = i1.w;
+            }
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                const double wi = (double)iw[t];
+                const double d = (double)w[t] - (double)cv[t] * (double)sc[t];
+                num += wi * d * d;
+                den += wi * (double)w[t] * (double)w[t];
+            }
+        }
+    }
+    if (__any(bad) && (threadIdx.x & 63) == 0) atomicOr(status, ST_NONFINITE);
+    if (partials) {                                  // uniform: every thread reaches the tree
+        __shared__ double sh[2 * QNT];
+        block_sum2(num, den, sh);
+        if (threadIdx.x == 0) {
+            partials[2 * blockIdx.x] = num;
+            partials[2 * blockIdx.x + 1] = den;
+        }
+    }
+}
+
+// Any other shape: one thread per unit of P = max(2, G) columns (whole groups,
+// whole code bytes), scalar loads and byte stores.
+__global__ __launch_bounds__(RTN_NT) void rtn_any_kernel(const float *__restrict__ W, uint8_t *__restrict__ codes,
+                                                         float *__restrict__ scales, int64_t N, int64_t K, int G,
+                                                         unsigned *status)
+{
+    const int P = G > 2 ? G : 2;
+    const int64_t units = K / P, idx = (int64_t)blockIdx.x * RTN_NT + threadIdx.x;
+    if (idx >= N * units) return;
+    const int64_t row = idx / units, k0 = (idx - row * units) * P;
+    const float *w = W + row * K + k0;
+    bool bad = false;
+    float sc = 0.0f;
+    unsigned lo = 0;
+    for (int t = 0; t < P; ++t) {
+        if (t % G == 0) {                           // a group starts: its scale
+            float m = 0.0f;
+            for (int u = t; u < t + G; ++u) {
+                bad = bad || !isfinite(w[u]);
+                m = fmaxf(m, fabsf(w[u]));
+            }
+            sc = m / 7.0f;
+            scales[row * (K / G) + (k0 + t) / G] = sc;
+        }
+        const unsigned nib = rtn_nibble(w[t], sc);
+        if (t & 1) codes[row * (K / 2) + (k0 + t) / 2] = (uint8_t)(lo | nib << 4);
+        else lo = nib;
+    }
+    if (bad) atomicOr(status, ST_NONFINITE);
+}
+
 }  // namespace
 
 int64_t qerr_partials(int64_t N)
@@ -324,6 +471,40 @@ hipError_t launch_qerr_reduce(double *out2, const double *partials, int64_t npar
 {
     hipLaunchKernelGGL(qerr_reduce_kernel, dim3(1), dim3(QNT), 0, s, out2, partials, nparts);
     return hipGetLastError();
+}
+
+int64_t rtn_workgroups(int64_t N, int64_t K)
+{
+    const int64_t need = (N * (K / 8) + RTN_NT - 1) / RTN_NT;
+    return need < RTN_MAX_WG ? need : RTN_MAX_WG;
+}
+
+int64_t rtn_partials(int64_t N, int64_t K)
+{
+    const int64_t fused = rtn_workgroups(N, K), sep = qerr_partials(N);
+    return fused > sep ? fused : sep;
+}
+
+hipError_t launch_rtn(const float *W, uint8_t *codes, float *scales, const float *imp, double *partials, int64_t N,
+                      int64_t K, int64_t G, unsigned *status, hipStream_t s, int64_t *nparts)
+{
+    if (G < 1 || G > 128 || (G & (G - 1)) || K % G || K % 2) return hipErrorInvalidValue;
+    const bool wide = K % 8 == 0 && ((uintptr_t)W & 15) == 0 && ((uintptr_t)codes & 3) == 0 &&
+                      ((uintptr_t)imp & 15) == 0;
+    if (wide) {
+        const int64_t nwg = rtn_workgroups(N, K);
+        hipLaunchKernelGGL(rtn8_kernel, dim3((unsigned)nwg), dim3(RTN_NT), 0, s, W, codes, scales, N, K, (int)G,
+                           status, imp, partials);
+        if (nparts) *nparts = nwg;
+        return hipGetLastError();
+    }
+    const int64_t threads = N * (K / (G > 2 ? G : 2));
+    hipLaunchKernelGGL(rtn_any_kernel, dim3((unsigned)((threads + RTN_NT - 1) / RTN_NT)), dim3(RTN_NT), 0, s, W,
+                       codes, scales, N, K, (int)G, status);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || !partials) return e;
+    if (nparts) *nparts = qerr_partials(N);
+    return launch_qerr(partials, W, codes, scales, imp, N, K, G, s);
 }
 
 }  // namespace gq

@@ -220,6 +220,12 @@ hipError_t launch_check_finite(const float *x, int64_t n, unsigned *status, hipS
 hipError_t launch_sweep_block(float *Wk, float *ET, uint8_t *codes, float *scales,
                               const float *U, int64_t N, int64_t K, int64_t G, int64_t b0,
                               hipStream_t s);
+// Round-to-nearest codes and scales of W on the sweep's int4 grid (gptq.hip).
+// With partials set, also qerr's partial sums (as launch_qerr's, *nparts pairs,
+// at most rtn_partials(N, K)), ready for launch_qerr_reduce.
+int64_t rtn_partials(int64_t N, int64_t K);
+hipError_t launch_rtn(const float *W, uint8_t *codes, float *scales, const float *imp, double *partials, int64_t N,
+                      int64_t K, int64_t G, unsigned *status, hipStream_t s, int64_t *nparts);
 hipError_t launch_qerr(double *partials, const float *W, const uint8_t *codes,
                        const float *scales, const float *imp, int64_t N, int64_t K, int64_t G,
                        hipStream_t s);
