@@ -244,10 +244,37 @@ def main():
         },
     }
     out["rtn"] = rtn_measure(gq, torch, W, imp, G, dev)
+    out["hfqm"] = hfqm_measure(gq, blob, imp, K)
     out["rtn"]["qerr_gptq_over_rtn"] = qerr[0] / out["rtn"]["qerr"] if out["rtn"]["qerr"] else None
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, X, W)
     print(json.dumps(out))
+
+
+def hfqm_measure(gq, blob, imp, K, reps=3):
+    """The stored Hessian and its imatrix as a two-entry HFQM package: write to a
+    temporary file and read back (index and both payloads), host to disk and back,
+    after the timed steps; the device blob is copied to the host first (not timed)."""
+    import tempfile
+    ents = [("blk.0.hessian", gq.GQ_HFQM_HESSIAN, (K, K), 0, blob.cpu().numpy()),
+            ("blk.0.imatrix", gq.GQ_HFQM_F32, (K,), 0, imp.cpu().numpy())]
+    nbytes = sum(e[4].nbytes for e in ents)
+    with tempfile.TemporaryDirectory() as d:
+        p = os.path.join(d, "bench.calib.hfq")
+        tw = tr = 0.0
+        for _ in range(reps):
+            t0 = time.perf_counter()
+            gq.hfqm_write(p, 0, '{"producer":"bench"}', ents)
+            t1 = time.perf_counter()
+            _, _, idx = gq.hfqm_read(p)
+            for i, e in enumerate(idx):
+                gq.hfqm_read_payload(p, i, e[4])
+            t2 = time.perf_counter()
+            tw += t1 - t0
+            tr += t2 - t1
+        size = os.path.getsize(p)
+    return {"payload_bytes": nbytes, "file_bytes": size, "write_mb_per_s": nbytes * reps / tw / 1e6,
+            "read_mb_per_s": nbytes * reps / tr / 1e6, "where": "tempfile directory of the host"}
 
 
 def rtn_measure(gq, torch, W, imp, G, dev, reps=10):

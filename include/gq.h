@@ -42,7 +42,9 @@ typedef enum gq_status {
     GQ_ERR_NONFINITE = 3,      /* NaN or Inf in W, in the lower triangle of H, or imp */
     GQ_ERR_NO_CALIBRATION = 4, /* mean(diag H) <= 0: refuse rather than guess         */
     GQ_ERR_HIP = 5,            /* a HIP runtime call failed                           */
-    GQ_ERR_INTERNAL = 6        /* an internal numerical invariant failed (a bug)      */
+    GQ_ERR_INTERNAL = 6,       /* an internal numerical invariant failed (a bug)      */
+    GQ_ERR_IO = 7              /* a file could not be read or written, or is not a
+                                  well-formed HFQM package                            */
 } gq_status;
 
 typedef enum gq_dtype { GQ_F32 = 0, GQ_BF16 = 1 } gq_dtype;
@@ -233,6 +235,57 @@ size_t rtn_quantize_workspace_size(int64_t N, int64_t K, int64_t group);
  */
 int rtn_quantize(uint8_t *codes, float *scales, double *qerr_out, const float *W, const float *imp,
                  int64_t N, int64_t K, int64_t group, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * HFQM calibration package (.calib.hfq), the container that carries stored
+ * Hessians and importance vectors (hipfire-calib-data dataset card, ".calib.hfq —
+ * HFQM calibration package").  Little-endian: a 32-byte header ("HFQM", version
+ * u32 = 1, arch_id u32, n_entries u32, metadata_offset u64, data_offset u64), one
+ * self-delimited JSON value at metadata_offset, the index right after it
+ * (n_entries u32, then per entry name_len u16, name, quant_type u8, n_dims u8,
+ * shape[n_dims] u32, group_size u32, data_size u64), and the payloads
+ * concatenated in index order from data_offset.  A tensor contributes
+ * "<name>.hessian" (quant_type GQ_HFQM_HESSIAN: the hessian_pack_tril blob, shape
+ * K x K) and "<name>.imatrix" (GQ_HFQM_F32 values, shape K).  Host code and host
+ * buffers only; each call opens, reads or writes and closes the file.
+ * Errors: GQ_ERR_INVALID_ARG, GQ_ERR_IO (open/read/write failure, or not a
+ * well-formed package: bad magic or version, offsets, index or sizes).
+ */
+enum { GQ_HFQM_F32 = 0, GQ_HFQM_HESSIAN = 130 };
+
+/*
+ * hfqm_write -- write a package of n_entries entries to path (replaced if it
+ * exists).  metadata_json: exactly one JSON object or array, no surrounding
+ * whitespace.  Entry i: names[i] (NUL-terminated, < 65536 bytes),
+ * quant_types[i], n_dims[i] <= 4, shapes[4 i .. 4 i + n_dims[i] - 1],
+ * group_sizes[i], and data_sizes[i] bytes at host pointer data[i].
+ */
+int hfqm_write(const char *path, uint32_t arch_id, const char *metadata_json, int64_t n_entries,
+               const char *const *names, const uint8_t *quant_types, const uint8_t *n_dims,
+               const uint32_t *shapes, const uint32_t *group_sizes, const uint64_t *data_sizes,
+               const void *const *data);
+
+/*
+ * hfqm_read_header -- arch_id, entry count, data_offset and the metadata JSON of
+ * the package at path.  Any output pointer may be NULL; metadata (if not NULL)
+ * receives the JSON text and a NUL in metadata_cap bytes, *metadata_len its
+ * length.
+ */
+int hfqm_read_header(const char *path, uint32_t *arch_id, int64_t *n_entries, uint64_t *data_offset,
+                     char *metadata, size_t metadata_cap, size_t *metadata_len);
+
+/*
+ * hfqm_read_entry -- index entry i (0-based): name (NUL-terminated, in name_cap
+ * bytes), quant_type, n_dims, shape[4] (unused dimensions 0), group_size,
+ * data_size, and the byte offset of its payload in the file.  Any output pointer
+ * may be NULL.
+ */
+int hfqm_read_entry(const char *path, int64_t i, char *name, size_t name_cap, uint8_t *quant_type,
+                    uint8_t *n_dims, uint32_t *shape, uint32_t *group_size, uint64_t *data_size,
+                    uint64_t *offset);
+
+/* hfqm_read_payload -- entry i's payload into dst (a host buffer of dst_bytes >= its data_size). */
+int hfqm_read_payload(const char *path, int64_t i, void *dst, size_t dst_bytes);
 
 #ifdef __cplusplus
 }

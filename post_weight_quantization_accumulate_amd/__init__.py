@@ -18,7 +18,9 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libgq.so")
 
-GQ_OK, GQ_ERR_INVALID_ARG, GQ_ERR_NOT_PD, GQ_ERR_NONFINITE, GQ_ERR_NO_CALIBRATION, GQ_ERR_HIP, GQ_ERR_INTERNAL = range(7)
+(GQ_OK, GQ_ERR_INVALID_ARG, GQ_ERR_NOT_PD, GQ_ERR_NONFINITE, GQ_ERR_NO_CALIBRATION, GQ_ERR_HIP, GQ_ERR_INTERNAL,
+ GQ_ERR_IO) = range(8)
+GQ_HFQM_F32, GQ_HFQM_HESSIAN = 0, 130
 GQ_F32, GQ_BF16 = 0, 1
 GQ_PSD_AUTO, GQ_PSD_F64 = 0, 1
 
@@ -28,6 +30,7 @@ EXPORTS = (
     "psd_project_flops", "psd_project_products", "gq_set_timing", "psd_project_last_timing", "gq_set_psd_products",
     "gptq_factor_workspace_size", "gptq_factor", "gptq_sweep_workspace_size", "gptq_sweep",
     "gptq_quantize_workspace_size", "gptq_quantize", "rtn_quantize_workspace_size", "rtn_quantize",
+    "hfqm_write", "hfqm_read_header", "hfqm_read_entry", "hfqm_read_payload",
 )
 
 
@@ -72,6 +75,10 @@ def lib() -> ctypes.CDLL:
             "gptq_quantize": (I, [P, P, P, P, P, P, I64, I64, I64, F, P, SZ, P]),
             "rtn_quantize_workspace_size": (SZ, [I64, I64, I64]),
             "rtn_quantize": (I, [P, P, P, P, P, I64, I64, I64, P, SZ, P]),
+            "hfqm_write": (I, [ctypes.c_char_p, ctypes.c_uint32, ctypes.c_char_p, I64, P, P, P, P, P, P, P]),
+            "hfqm_read_header": (I, [ctypes.c_char_p, P, P, P, P, SZ, P]),
+            "hfqm_read_entry": (I, [ctypes.c_char_p, I64, P, SZ, P, P, P, P, P, P]),
+            "hfqm_read_payload": (I, [ctypes.c_char_p, I64, P, SZ]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -259,3 +266,60 @@ def gptq_quantize(codes, scales, W, H, imp, group: int, damp: float, ws, want_qe
                                _ptr(W), _ptr(H), _ptr(imp), N, K, group, float(damp), _ptr(ws),
                                ws.numel(), _stream(W)), "gptq_quantize")
     return q.value if want_qerr else None
+
+
+# ------------------------------------------------------------------ HFQM package
+def _host_bytes(x) -> "np.ndarray":
+    import numpy as np
+    if isinstance(x, torch.Tensor):
+        x = x.detach().contiguous().view(torch.uint8).cpu().numpy()
+    return np.ascontiguousarray(np.frombuffer(memoryview(x).cast("B"), dtype=np.uint8))
+
+
+def hfqm_write(path: str, arch_id: int, metadata: str, entries):
+    """Write an HFQM package.  entries: (name, quant_type, shape, group_size, payload)
+    in index order; payload is bytes, a numpy array or a tensor (host or device)."""
+    n = len(entries)
+    names = (ctypes.c_char_p * max(n, 1))(*[e[0].encode() for e in entries])
+    qts = (ctypes.c_uint8 * max(n, 1))(*[e[1] for e in entries])
+    nds = (ctypes.c_uint8 * max(n, 1))(*[len(e[2]) for e in entries])
+    shp = (ctypes.c_uint32 * max(4 * n, 1))()
+    for i, e in enumerate(entries):
+        if len(e[2]) > 4:
+            raise ValueError("at most 4 dimensions per entry")
+        for d, v in enumerate(e[2]):
+            shp[4 * i + d] = v
+    grp = (ctypes.c_uint32 * max(n, 1))(*[e[3] for e in entries])
+    bufs = [_host_bytes(e[4]) for e in entries]
+    sizes = (ctypes.c_uint64 * max(n, 1))(*[b.size for b in bufs])
+    data = (ctypes.c_void_p * max(n, 1))(*[b.ctypes.data for b in bufs])
+    _check(lib().hfqm_write(path.encode(), arch_id, metadata.encode(), n, names, qts, nds, shp, grp, sizes, data),
+           "hfqm_write")
+
+
+def hfqm_read(path: str):
+    """(arch_id, metadata JSON text, [(name, quant_type, shape, group_size, data_size, offset)])."""
+    arch, n, doff, mlen = ctypes.c_uint32(), ctypes.c_int64(), ctypes.c_uint64(), ctypes.c_size_t()
+    _check(lib().hfqm_read_header(path.encode(), ctypes.byref(arch), ctypes.byref(n), ctypes.byref(doff), None, 0,
+                                  ctypes.byref(mlen)), "hfqm_read_header")
+    meta = ctypes.create_string_buffer(mlen.value + 1)
+    _check(lib().hfqm_read_header(path.encode(), None, None, None, meta, mlen.value + 1, None), "hfqm_read_header")
+    out = []
+    for i in range(n.value):
+        name = ctypes.create_string_buffer(65536)
+        qt, nd = ctypes.c_uint8(), ctypes.c_uint8()
+        shape = (ctypes.c_uint32 * 4)()
+        grp, size, off = ctypes.c_uint32(), ctypes.c_uint64(), ctypes.c_uint64()
+        _check(lib().hfqm_read_entry(path.encode(), i, name, 65536, ctypes.byref(qt), ctypes.byref(nd), shape,
+                                     ctypes.byref(grp), ctypes.byref(size), ctypes.byref(off)), "hfqm_read_entry")
+        out.append((name.value.decode(), qt.value, tuple(shape[:nd.value]), grp.value, size.value, off.value))
+    return arch.value, meta.value.decode(), out
+
+
+def hfqm_read_payload(path: str, i: int, size: int):
+    """Entry i's payload (size bytes, from hfqm_read) as a numpy uint8 array."""
+    import numpy as np
+    dst = np.empty(size, np.uint8)
+    _check(lib().hfqm_read_payload(path.encode(), i, dst.ctypes.data if size else None, size), "hfqm_read_payload")
+    return dst
+

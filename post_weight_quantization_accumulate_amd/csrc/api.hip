@@ -437,6 +437,13 @@ int run_sweep(uint8_t *codes, float *scales, double *qerr_out, const float *W, c
 
 }  // namespace
 
+// The message gq_last_error returns, set by the other translation units (hfqm.hip).
+int gq::set_error(int status, const char *msg)
+{
+    g_last_error = msg ? msg : "";
+    return status;
+}
+
 extern "C" {
 
 int gq_abi_version(void) { return GQ_ABI_VERSION; }

@@ -233,4 +233,7 @@ hipError_t launch_qerr_reduce(double *out2, const double *partials, int64_t npar
                               hipStream_t s);
 int64_t qerr_partials(int64_t N);
 
+// Sets the message gq_last_error returns (defined in api.hip); returns status.
+int set_error(int status, const char *msg);
+
 }  // namespace gq
