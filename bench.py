@@ -245,10 +245,39 @@ def main():
     }
     out["rtn"] = rtn_measure(gq, torch, W, imp, G, dev)
     out["hfqm"] = hfqm_measure(gq, blob, imp, K)
+    out["hadamard"] = hadamard_measure(gq, torch, W, Hs, dev)
     out["rtn"]["qerr_gptq_over_rtn"] = qerr[0] / out["rtn"]["qerr"] if out["rtn"]["qerr"] else None
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, X, W)
     print(json.dumps(out))
+
+
+def hadamard_measure(gq, torch, W, H, dev, block=1024, reps=10):
+    """The block Walsh-Hadamard rotation (blocks of 1024, random signs) of a copy of
+    W (W R^T) and of the step's Hessian (R H R^T), timed after the steps with HIP
+    events.  Algorithmic bytes: one read and one write of each matrix; the
+    Hessian's two-sided rotation runs as rows, transpose, rows, copy (4x that)."""
+    N, K = W.shape
+    g = torch.Generator(device="cpu").manual_seed(1)
+    signs = (torch.randint(0, 2, (K,), generator=g) * 2 - 1).float().to(dev)
+    Wc, Hc = W.clone(), H.clone()
+    ws = gq.workspace(gq.hadamard_rotate_hessian_workspace_size(K), dev)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    res = {"block": block}
+    for name, fn, nbytes in (("rows", lambda: gq.hadamard_rotate_rows(Wc, block, signs), 8 * N * K),
+                             ("hessian", lambda: gq.hadamard_rotate_hessian(Hc, block, ws, signs), 8 * K * K)):
+        fn()
+        torch.cuda.synchronize()
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / reps
+        res[name + "_ms"] = ms
+        res[name + "_gb_per_s"] = nbytes / (ms * 1e-3) / 1e9
+        res[name + "_frac_of_hbm_peak"] = nbytes / (ms * 1e-3) / 1e9 / 8000.0
+    return res
 
 
 def hfqm_measure(gq, blob, imp, K, reps=3):

@@ -215,6 +215,29 @@ int gptq_quantize(uint8_t *codes, float *scales, double *qerr_out, const float *
                   const float *H, const float *imp, int64_t N, int64_t K, int64_t group,
                   float damp, void *ws, size_t ws_bytes, hipStream_t stream);
 
+/*
+ * Block Walsh-Hadamard rotation, the rotation GPTQ composes with (ork-driver wiki,
+ * "Exp 2026-08-18 GPTQ Int4": rotate, then quantise, as in QuaRot).
+ * R = blockdiag(H_b, ..., H_b) diag(signs) / sqrt(b) over the K input channels,
+ * H_b the Sylvester Hadamard matrix of order b (H_1 = [1],
+ * H_2m = [[H_m, H_m], [H_m, -H_m]]), b = block a power of two <= 4096 that
+ * divides K, signs a K-vector of +1/-1 (fp32, device) or NULL for all +1.  R is
+ * orthogonal: W' = W R^T and X' = X R^T leave W X^T unchanged, and the Hessian of
+ * X' is R H R^T.  Both calls are asynchronous (argument and launch errors only).
+ */
+/* hadamard_rotate_rows -- A[r, :] <- A[r, :] R^T for each of `rows` rows of the
+ * fp32 matrix A (row r at A + r*ld, ld >= K), in place: W or X. */
+int hadamard_rotate_rows(float *A, int64_t rows, int64_t K, int64_t ld, int64_t block, const float *signs,
+                         hipStream_t stream);
+
+/* Workspace bytes hadamard_rotate_hessian needs (one K x K fp32 matrix). */
+size_t hadamard_rotate_hessian_workspace_size(int64_t K);
+
+/* hadamard_rotate_hessian -- H <- R H R^T for a full symmetric K x K fp32 H (both
+ * triangles read and written), in place through the workspace. */
+int hadamard_rotate_hessian(float *H, int64_t K, int64_t block, const float *signs, void *ws,
+                            size_t ws_bytes, hipStream_t stream);
+
 /* Workspace bytes rtn_quantize needs (a few KB, independent of the sizes). */
 size_t rtn_quantize_workspace_size(int64_t N, int64_t K, int64_t group);
 

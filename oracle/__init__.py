@@ -320,3 +320,41 @@ def gptq_replay(cand_codes, cand_scales, W, U, G: int, rows=None, delta: float =
                           _p(rows), len(rows), delta, scale_tol)
     return {"exact": int(stats[0]), "tie_flips": int(stats[1]), "inadmissible": int(stats[2]),
             "scale_mismatch": int(stats[3]), "max_scale_rel": mrel.value}
+
+
+# ------------------------------------------------------------------ Hadamard rotation
+def sylvester_hadamard(b: int):
+    """H_b by Sylvester's doubling: H_1 = [1], H_2m = [[H_m, H_m], [H_m, -H_m]]
+    (the rotation GPTQ composes with, ork-driver wiki "Exp 2026-08-18 GPTQ Int4")."""
+    if b < 1 or b & (b - 1):
+        raise ValueError("b must be a power of two")
+    Hm = np.ones((1, 1))
+    while Hm.shape[0] < b:
+        Hm = np.block([[Hm, Hm], [Hm, -Hm]])
+    return Hm
+
+
+def hadamard_rotation(K: int, b: int, signs=None):
+    """R = blockdiag(H_b, ..., H_b) diag(signs) / sqrt(b), K x K, fp64."""
+    if K % b:
+        raise ValueError("b must divide K")
+    Hb = sylvester_hadamard(b) / np.sqrt(b)
+    R = np.kron(np.eye(K // b), Hb)
+    if signs is not None:
+        R = R * np.asarray(signs, np.float64)[None, :]
+    return R
+
+
+def hadamard_rotate_rows(A, b: int, signs=None):
+    """A R^T in fp64 (each row rotated), returned as fp32."""
+    A = np.asarray(A, np.float64)
+    R = hadamard_rotation(A.shape[1], b, signs)
+    return (A @ R.T).astype(np.float32)
+
+
+def hadamard_rotate_hessian(H, b: int, signs=None):
+    """R H R^T in fp64, returned as fp32."""
+    H = np.asarray(H, np.float64)
+    R = hadamard_rotation(H.shape[0], b, signs)
+    return (R @ H @ R.T).astype(np.float32)
+

@@ -31,6 +31,7 @@ EXPORTS = (
     "gptq_factor_workspace_size", "gptq_factor", "gptq_sweep_workspace_size", "gptq_sweep",
     "gptq_quantize_workspace_size", "gptq_quantize", "rtn_quantize_workspace_size", "rtn_quantize",
     "hfqm_write", "hfqm_read_header", "hfqm_read_entry", "hfqm_read_payload",
+    "hadamard_rotate_rows", "hadamard_rotate_hessian_workspace_size", "hadamard_rotate_hessian",
 )
 
 
@@ -79,6 +80,9 @@ def lib() -> ctypes.CDLL:
             "hfqm_read_header": (I, [ctypes.c_char_p, P, P, P, P, SZ, P]),
             "hfqm_read_entry": (I, [ctypes.c_char_p, I64, P, SZ, P, P, P, P, P, P]),
             "hfqm_read_payload": (I, [ctypes.c_char_p, I64, P, SZ]),
+            "hadamard_rotate_rows": (I, [P, I64, I64, I64, I64, P, P]),
+            "hadamard_rotate_hessian_workspace_size": (SZ, [I64]),
+            "hadamard_rotate_hessian": (I, [P, I64, I64, P, P, SZ, P]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -266,6 +270,35 @@ def gptq_quantize(codes, scales, W, H, imp, group: int, damp: float, ws, want_qe
                                _ptr(W), _ptr(H), _ptr(imp), N, K, group, float(damp), _ptr(ws),
                                ws.numel(), _stream(W)), "gptq_quantize")
     return q.value if want_qerr else None
+
+
+# ------------------------------------------------------------------ Hadamard rotation
+def hadamard_rotate_rows(A, block: int, signs=None):
+    """A[r, :] <- A[r, :] R^T in place for an fp32 (rows x K) tensor (row stride may exceed K)."""
+    if not isinstance(A, torch.Tensor) or not A.is_cuda or A.dtype != torch.float32:
+        raise ValueError("A must be a CUDA (HIP) float32 tensor")
+    if A.dim() != 2 or A.stride(1) != 1:
+        raise ValueError("A must be 2-D with unit column stride")
+    rows, K = A.shape
+    if signs is not None:
+        _need(signs, "signs", torch.float32, K)
+    _check(lib().hadamard_rotate_rows(_ptr(A), rows, K, A.stride(0), block, _ptr(signs), _stream(A)),
+           "hadamard_rotate_rows")
+
+
+def hadamard_rotate_hessian_workspace_size(K: int) -> int:
+    return int(lib().hadamard_rotate_hessian_workspace_size(K))
+
+
+def hadamard_rotate_hessian(H, block: int, ws, signs=None):
+    """H <- R H R^T in place for a full symmetric fp32 K x K tensor."""
+    K = H.shape[0]
+    _need(H, "H", torch.float32, K * K)
+    _need(ws, "ws", torch.uint8)
+    if signs is not None:
+        _need(signs, "signs", torch.float32, K)
+    _check(lib().hadamard_rotate_hessian(_ptr(H), K, block, _ptr(signs), _ptr(ws), ws.numel(), _stream(H)),
+           "hadamard_rotate_hessian")
 
 
 # ------------------------------------------------------------------ HFQM package

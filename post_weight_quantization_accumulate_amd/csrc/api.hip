@@ -768,6 +768,43 @@ RtnWs carve_rtn(Carver &c, int64_t N, int64_t K)
     return w;
 }
 
+int hadamard_rotate_rows(float *A, int64_t rows, int64_t K, int64_t ld, int64_t block, const float *signs,
+                         hipStream_t stream)
+{
+    g_last_error.clear();
+    if (!A) return fail(GQ_ERR_INVALID_ARG, "null matrix");
+    if (rows < 0 || K < 1 || ld < K) return fail(GQ_ERR_INVALID_ARG, "bad sizes");
+    if (!hadamard_block_ok(K, block))
+        return fail(GQ_ERR_INVALID_ARG, "block must be a power of two <= 4096 that divides K");
+    GQ_HIP(launch_fwht_rows(A, rows, K, ld, block, signs, stream), "fwht rows");
+    return GQ_OK;
+}
+
+size_t hadamard_rotate_hessian_workspace_size(int64_t K)
+{
+    if (K < 1) return 0;
+    return align_up((size_t)K * (size_t)K * sizeof(float));
+}
+
+int hadamard_rotate_hessian(float *H, int64_t K, int64_t block, const float *signs, void *ws, size_t ws_bytes,
+                            hipStream_t stream)
+{
+    g_last_error.clear();
+    if (!H || !ws) return fail(GQ_ERR_INVALID_ARG, "null matrix or workspace");
+    if (K < 1) return fail(GQ_ERR_INVALID_ARG, "K must be >= 1");
+    if (!hadamard_block_ok(K, block))
+        return fail(GQ_ERR_INVALID_ARG, "block must be a power of two <= 4096 that divides K");
+    if (ws_bytes < hadamard_rotate_hessian_workspace_size(K)) return fail(GQ_ERR_INVALID_ARG, "workspace too small");
+    // H' = R H R^T: T = H R^T (each row of H rotated), and H' = R T = (T^T R^T)^T;
+    // H' is symmetric, so it is T^T R^T itself: the rows of T^T rotated
+    float *T = (float *)ws;
+    GQ_HIP(launch_fwht_rows(H, K, K, K, block, signs, stream), "fwht rows");
+    GQ_HIP(launch_transpose(T, H, K, stream), "transpose");
+    GQ_HIP(launch_fwht_rows(T, K, K, K, block, signs, stream), "fwht rows");
+    GQ_HIP(hipMemcpyAsync(H, T, (size_t)K * (size_t)K * sizeof(float), hipMemcpyDeviceToDevice, stream), "copy");
+    return GQ_OK;
+}
+
 size_t rtn_quantize_workspace_size(int64_t N, int64_t K, int64_t group)
 {
     (void)group;

@@ -233,6 +233,15 @@ hipError_t launch_qerr_reduce(double *out2, const double *partials, int64_t npar
                               hipStream_t s);
 int64_t qerr_partials(int64_t N);
 
+// Block Walsh-Hadamard rotation (hadamard.hip): A[r, :] <- A[r, :] R^T for rows
+// r < rows (ld apart), R = blockdiag(H_b) diag(signs) / sqrt(b); signs may be
+// null (all +1).  hadamard_block_ok: b a power of two <= 4096 dividing K.
+bool hadamard_block_ok(int64_t K, int64_t b);
+hipError_t launch_fwht_rows(float *A, int64_t rows, int64_t K, int64_t ld, int64_t b, const float *signs,
+                            hipStream_t s);
+// out = in^T for K x K row-major fp32 matrices (out and in distinct).
+hipError_t launch_transpose(float *out, const float *in, int64_t K, hipStream_t s);
+
 // Sets the message gq_last_error returns (defined in api.hip); returns status.
 int set_error(int status, const char *msg);
 
