@@ -93,6 +93,11 @@ def _load(path):
         "orc_unpack_codes": (None, [P, P, I64, I64]),
         "orc_gptq": (I, [P, P, P, P, P, P, I64, I64, I64, D]),
         "orc_gptq_replay": (None, [P, P, P, P, P, P, I64, I64, P, I64, D, D]),
+        "orc_gptq_sweep_ex": (None, [P, P, P, P, I64, I64, P, I64, I, P]),
+        "orc_rtn_ex": (None, [P, P, P, I64, I64, I64, I, P]),
+        "orc_qerr_ex": (D, [P, P, P, P, I64, I64, I64, P, P]),
+        "orc_gptq_ex": (I, [P, P, P, P, P, P, I64, I64, I64, D, I, P]),
+        "orc_gptq_replay_ex": (None, [P, P, P, P, P, P, I64, I64, P, I64, D, D, I, P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -241,28 +246,60 @@ def gptq_U(H, damp: float = 0.01):
     return st, U, mu.value
 
 
-def gptq_sweep(W, U, G: int, rows=None):
-    """Codes (len(rows) x K int8) and scales of the GPTQ sweep of W's rows under U."""
+# Sweep and pack switches (gq_oracle.c): scales fixed from the original weights
+# before the sweep; the NF4 codebook instead of the uniform int4 grid.
+STATIC_GROUPS = 1
+NF4 = 2
+
+_NF4 = None
+
+
+def nf4_levels():
+    """The 16 NF4 levels as fp32, ascending (QLoRA, Dettmers et al. 2023, the
+    4-bit NormalFloat data type): quantiles of the standard normal at evenly
+    spaced probabilities, 8 on the positive side and 7 on the negative side so
+    that 0 is a level, the outermost probability 1 - d with d = (1/32 + 1/30)/2
+    (the mean of the half-bin widths of 16 and 15 bins) so that it stays finite,
+    then scaled to [-1, 1] by the largest.  The quantile function is scipy's."""
+    global _NF4
+    if _NF4 is None:
+        from scipy.stats import norm
+        d = 0.5 * (1.0 / 32 + 1.0 / 30)
+        pos = norm.ppf(np.linspace(1.0 - d, 0.5, 9)[:-1])
+        neg = -norm.ppf(np.linspace(1.0 - d, 0.5, 8)[:-1])
+        L = np.sort(np.concatenate([neg, [0.0], pos]))
+        _NF4 = (L / pos.max()).astype(np.float32)
+    return _NF4.copy()
+
+
+def _book(flags):
+    return nf4_levels() if flags & NF4 else None
+
+
+def gptq_sweep(W, U, G: int, rows=None, flags: int = 0):
+    """Codes (len(rows) x K int8: signed int4, or NF4 level indices) and scales of
+    the GPTQ sweep of W's rows under U."""
     W = _np(W, np.float32)
     U = _c(U, np.float64)
     N, K = W.shape
     rows = np.arange(N, dtype=np.int64) if rows is None else _c(rows, np.int64)
     codes = np.zeros((len(rows), K), np.int8)
     scales = np.zeros((len(rows), K // G), np.float32)
-    lib().orc_gptq_sweep(_p(codes), _p(scales), _p(W), _p(U), K, G, _p(rows), len(rows))
+    lib().orc_gptq_sweep_ex(_p(codes), _p(scales), _p(W), _p(U), K, G, _p(rows), len(rows), flags,
+                            _p(_book(flags)))
     return codes, scales
 
 
-def rtn(W, G: int):
+def rtn(W, G: int, flags: int = 0):
     W = _np(W, np.float32)
     N, K = W.shape
     codes = np.zeros((N, K), np.int8)
     scales = np.zeros((N, K // G), np.float32)
-    lib().orc_rtn(_p(codes), _p(scales), _p(W), N, K, G)
+    lib().orc_rtn_ex(_p(codes), _p(scales), _p(W), N, K, G, flags, _p(_book(flags)))
     return codes, scales
 
 
-def qerr(codes, scales, W, imp=None, return_sums: bool = False):
+def qerr(codes, scales, W, imp=None, return_sums: bool = False, flags: int = 0):
     W = _np(W, np.float32)
     N, K = W.shape
     codes = _c(codes, np.int8)
@@ -270,7 +307,7 @@ def qerr(codes, scales, W, imp=None, return_sums: bool = False):
     G = K // scales.shape[1]
     imp = None if imp is None else _np(imp, np.float32)
     nd = np.zeros(2, np.float64)
-    q = float(lib().orc_qerr(_p(codes), _p(scales), _p(W), _p(imp), N, K, G, _p(nd)))
+    q = float(lib().orc_qerr_ex(_p(codes), _p(scales), _p(W), _p(imp), N, K, G, _p(_book(flags)), _p(nd)))
     return (q, nd) if return_sums else q
 
 
@@ -282,15 +319,19 @@ def pack_codes(codes):
     return out
 
 
-def unpack_codes(packed, K: int):
+def unpack_codes(packed, K: int, flags: int = 0):
+    """Codes from two nibbles per byte (column 2m low): signed int4, or with NF4
+    the unsigned level indices 0..15."""
     packed = _c(packed, np.uint8)
     N = packed.shape[0]
     codes = np.zeros((N, K), np.int8)
     lib().orc_unpack_codes(_p(codes), _p(packed), N, K)
+    if flags & NF4:
+        codes = (codes & 0xF).astype(np.int8)
     return codes
 
 
-def gptq(W, H, G: int, damp: float = 0.01, imp=None, want_qerr: bool = True):
+def gptq(W, H, G: int, damp: float = 0.01, imp=None, want_qerr: bool = True, flags: int = 0):
     """(status, codes int8 N x K, scales N x K/G, qerr or None)."""
     W = _np(W, np.float32)
     H = _np(H, np.float32)
@@ -299,13 +340,13 @@ def gptq(W, H, G: int, damp: float = 0.01, imp=None, want_qerr: bool = True):
     codes = np.zeros((N, K), np.int8)
     scales = np.zeros((N, max(1, K // max(G, 1))), np.float32)
     q = ctypes.c_double(0.0)
-    st = lib().orc_gptq(_p(codes), _p(scales), ctypes.byref(q) if want_qerr else None,
-                        _p(W), _p(H), _p(imp), N, K, G, damp)
+    st = lib().orc_gptq_ex(_p(codes), _p(scales), ctypes.byref(q) if want_qerr else None,
+                           _p(W), _p(H), _p(imp), N, K, G, damp, flags, _p(_book(flags)))
     return st, codes, scales, (q.value if want_qerr else None)
 
 
 def gptq_replay(cand_codes, cand_scales, W, U, G: int, rows=None, delta: float = 1e-3,
-                scale_tol: float = 1e-5):
+                scale_tol: float = 1e-5, flags: int = 0):
     """Admissibility of candidate codes/scales for W's listed rows (see gq_oracle.c)."""
     W = _np(W, np.float32)
     U = _c(U, np.float64)
@@ -316,8 +357,8 @@ def gptq_replay(cand_codes, cand_scales, W, U, G: int, rows=None, delta: float =
     assert cc.shape == (len(rows), K) and cs.shape == (len(rows), K // G)
     stats = np.zeros(4, np.int64)
     mrel = ctypes.c_double(0.0)
-    lib().orc_gptq_replay(_p(stats), ctypes.byref(mrel), _p(cc), _p(cs), _p(W), _p(U), K, G,
-                          _p(rows), len(rows), delta, scale_tol)
+    lib().orc_gptq_replay_ex(_p(stats), ctypes.byref(mrel), _p(cc), _p(cs), _p(W), _p(U), K, G,
+                             _p(rows), len(rows), delta, scale_tol, flags, _p(_book(flags)))
     return {"exact": int(stats[0]), "tie_flips": int(stats[1]), "inadmissible": int(stats[2]),
             "scale_mismatch": int(stats[3]), "max_scale_rel": mrel.value}
 

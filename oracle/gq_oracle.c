@@ -29,6 +29,11 @@
  *                  opening description; GPTQ is Frantar et al. 2022).
  *   qerr           sqrt(sum imp[k] (w - q)^2 / sum imp[k] w^2), imp = 1 when
  *                  absent (same wiki page, qerr definition).
+ *   variants       static groups (every scale from the original weights, fixed
+ *                  before the sweep) and the NF4 codebook (the wiki's qerr
+ *                  section scores an NF4 pack beside the uniform one): scale
+ *                  absmax, code = the nearest of 16 levels in [-1, 1], passed
+ *                  in by the caller.
  *
  * Readings where the pages are silent are stated at each function.  Decisions
  * that turn floating point into an integer (the scale and the rounded code) are
@@ -565,6 +570,37 @@ int orc_gptq_U(double *U, const float *H, int64_t K, double damp, double *mu_out
 /* fp32 scale of a group from its absolute maximum: fl32(amax) / 7 in fp32. */
 static float group_scale(double amax) { return (float)amax / 7.0f; }
 
+/* Sweep and pack switches.  ORC_STATIC_GROUPS: every group's scale is fixed
+ * before the sweep from the original weights (AutoGPTQ's static_groups), instead
+ * of at the group's first column from its error-updated values.  ORC_NF4: the
+ * codes index a 16-level codebook (NF4, the comparison pack of the ork-driver
+ * wiki's qerr section) instead of the uniform int4 grid. */
+#define ORC_STATIC_GROUPS 1
+#define ORC_NF4 2
+
+/* Scale on the chosen grid: absmax/7 for the uniform grid; absmax itself for a
+ * codebook, whose levels span [-1, 1]. */
+static float grid_scale(double amax, const float *book)
+{
+    return book ? (float)amax : group_scale(amax);
+}
+
+/* Index of the codebook level nearest to x = fl32(w) / s, decided in fp32: the
+ * number of midpoints fl32(L[j] + L[j+1]) / 2 that x exceeds, so a value exactly
+ * on a midpoint takes the lower level.  s == 0 gives the level 0.0 (an all-zero
+ * group reconstructs exactly). */
+static int book_code(double w, float s, const float *L)
+{
+    float x = 0.0f;
+    if (s != 0.0f) x = (float)w / s;
+    int c = 0;
+    for (int j = 0; j < 15; j++) {
+        float mid = (L[j] + L[j + 1]) * 0.5f;
+        if (x > mid) c++;
+    }
+    return c;
+}
+
 /* Code of value w under scale s, decided in fp32: clamp(rint(fl32(w) / s), -8, 7),
  * ties to even; an all-zero group (s == 0) gives code 0. */
 static int quant_code(double w, float s)
@@ -577,17 +613,40 @@ static int quant_code(double w, float s)
     return (int)r;
 }
 
+/* Code of w under scale s on the chosen grid, and the value it stands for. */
+static int grid_code(double w, float s, const float *book)
+{
+    return book ? book_code(w, s, book) : quant_code(w, s);
+}
+static double grid_value(int c, float s, const float *book)
+{
+    return (book ? (double)book[c] : (double)c) * (double)s;
+}
+
+/* absmax of w[i .. i+G-1] in fp64. */
+static double group_amax_f32(const float *w, int64_t i, int64_t G)
+{
+    double amax = 0.0;
+    for (int64_t k = i; k < i + G; k++) amax = fmax(amax, fabs((double)w[k]));
+    return amax;
+}
+
 /* GPTQ error-feedback sweep of the listed rows, natural column order, fp64
  * working copy (ork-driver wiki, GPTQ Int4: error-compensated
  * column-sequential rounding).  For column i of row n:
  *   at a group start (i % G == 0) the scale is absmax/7 of the group's current,
- *   error-updated values;
- *   c = clamp(rint(w_i / s), -8, 7);  e = (w_i - c s) / U[i][i];
+ *   error-updated values (with ORC_STATIC_GROUPS: of the original weights);
+ *   c = clamp(rint(w_i / s), -8, 7)  (ORC_NF4: the nearest level of `book`,
+ *   scale absmax);  e = (w_i - value(c)) / U[i][i];
  *   w_j -= e * U[i][j] for every later column j.
- * codes: nrows x K (one signed code per byte), scales: nrows x K/G. */
-void orc_gptq_sweep(int8_t *codes, float *scales, const float *W, const double *U,
-                    int64_t K, int64_t G, const int64_t *rows, int64_t nrows)
+ * codes: nrows x K (one code per byte: signed int4, or the NF4 level index),
+ * scales: nrows x K/G. */
+void orc_gptq_sweep_ex(int8_t *codes, float *scales, const float *W, const double *U,
+                       int64_t K, int64_t G, const int64_t *rows, int64_t nrows, int flags,
+                       const float *book)
 {
+    const int stat = (flags & ORC_STATIC_GROUPS) != 0;
+    if (!(flags & ORC_NF4)) book = NULL;
 #pragma omp parallel for schedule(dynamic, 1)
     for (int64_t r = 0; r < nrows; r++) {
         const float *w0 = W + rows[r] * K;
@@ -598,16 +657,16 @@ void orc_gptq_sweep(int8_t *codes, float *scales, const float *W, const double *
             if (i % G == 0) {
                 double amax = 0.0;
                 for (int64_t k = i; k < i + G; k++) amax = fmax(amax, fabs(wk[k]));
+                if (stat) amax = group_amax_f32(w0, i, G);
 #if ORC_MUTANT == 3
-                amax = 0.0;   /* mutant: static group scale from the original weights */
-                for (int64_t k = i; k < i + G; k++) amax = fmax(amax, fabs((double)w0[k]));
+                amax = group_amax_f32(w0, i, G);   /* mutant: static scales in the default sweep */
 #endif
-                s = group_scale(amax);
+                s = grid_scale(amax, book);
                 scales[r * (K / G) + i / G] = s;
             }
-            int c = quant_code(wk[i], s);
+            int c = grid_code(wk[i], s, book);
             codes[r * K + i] = (int8_t)c;
-            double e = (wk[i] - (double)c * (double)s) / U[i * K + i];
+            double e = (wk[i] - grid_value(c, s, book)) / U[i * K + i];
 #if ORC_MUTANT == 2
             e = -e;   /* mutant: wrong sign of the error feedback */
 #endif
@@ -618,34 +677,46 @@ void orc_gptq_sweep(int8_t *codes, float *scales, const float *W, const double *
     }
 }
 
-/* Round-to-nearest with the same grid: scales from the original weights. */
-void orc_rtn(int8_t *codes, float *scales, const float *W, int64_t N, int64_t K, int64_t G)
+void orc_gptq_sweep(int8_t *codes, float *scales, const float *W, const double *U,
+                    int64_t K, int64_t G, const int64_t *rows, int64_t nrows)
 {
+    orc_gptq_sweep_ex(codes, scales, W, U, K, G, rows, nrows, 0, NULL);
+}
+
+/* Round-to-nearest on the same grid (flags: ORC_NF4 with `book`): scales from
+ * the original weights. */
+void orc_rtn_ex(int8_t *codes, float *scales, const float *W, int64_t N, int64_t K, int64_t G, int flags,
+                const float *book)
+{
+    if (!(flags & ORC_NF4)) book = NULL;
 #pragma omp parallel for schedule(static)
     for (int64_t n = 0; n < N; n++) {
         const float *w = W + n * K;
         for (int64_t g = 0; g < K / G; g++) {
-            double amax = 0.0;
-            for (int64_t k = g * G; k < (g + 1) * G; k++) amax = fmax(amax, fabs((double)w[k]));
-            float s = group_scale(amax);
+            float s = grid_scale(group_amax_f32(w, g * G, G), book);
             scales[n * (K / G) + g] = s;
-            for (int64_t k = g * G; k < (g + 1) * G; k++) codes[n * K + k] = (int8_t)quant_code(w[k], s);
+            for (int64_t k = g * G; k < (g + 1) * G; k++) codes[n * K + k] = (int8_t)grid_code(w[k], s, book);
         }
     }
+}
+
+void orc_rtn(int8_t *codes, float *scales, const float *W, int64_t N, int64_t K, int64_t G)
+{
+    orc_rtn_ex(codes, scales, W, N, K, G, 0, NULL);
 }
 
 /* qerr = sqrt(sum_n sum_k imp[k] (w - c s)^2 / sum_n sum_k imp[k] w^2), w the
  * original weights, imp = 1 when NULL; 0 when the denominator is 0.  Also
  * returns the two sums (num_den[0], num_den[1]) when num_den is non-NULL. */
-double orc_qerr(const int8_t *codes, const float *scales, const float *W, const float *imp,
-                int64_t N, int64_t K, int64_t G, double *num_den)
+double orc_qerr_ex(const int8_t *codes, const float *scales, const float *W, const float *imp,
+                   int64_t N, int64_t K, int64_t G, const float *book, double *num_den)
 {
     double num = 0.0, den = 0.0;
     for (int64_t n = 0; n < N; n++)
         for (int64_t k = 0; k < K; k++) {
             double wi = imp ? (double)imp[k] : 1.0;
             double w = (double)W[n * K + k];
-            double q = (double)codes[n * K + k] * (double)scales[n * (K / G) + k / G];
+            double q = grid_value(codes[n * K + k], scales[n * (K / G) + k / G], book);
 #if ORC_MUTANT == 6
             num += (w - q) * (w - q);   /* mutant: numerator ignores the importance */
 #else
@@ -655,6 +726,12 @@ double orc_qerr(const int8_t *codes, const float *scales, const float *W, const 
         }
     if (num_den) { num_den[0] = num; num_den[1] = den; }
     return den > 0.0 ? sqrt(num / den) : 0.0;
+}
+
+double orc_qerr(const int8_t *codes, const float *scales, const float *W, const float *imp,
+                int64_t N, int64_t K, int64_t G, double *num_den)
+{
+    return orc_qerr_ex(codes, scales, W, imp, N, K, G, NULL, num_den);
 }
 
 /* Two signed codes per byte: column 2m in the low nibble of byte m, column
@@ -681,10 +758,14 @@ void orc_unpack_codes(int8_t *codes, const uint8_t *packed, int64_t N, int64_t K
 }
 
 /* Full GPTQ of W (N x K) under H: codes (N x K, one per byte), scales, qerr.
- * imp NULL => 1, qerr_out NULL => not computed. */
-int orc_gptq(int8_t *codes, float *scales, double *qerr_out, const float *W, const float *H,
-             const float *imp, int64_t N, int64_t K, int64_t G, double damp)
+ * imp NULL => 1, qerr_out NULL => not computed; flags and book as for
+ * orc_gptq_sweep_ex. */
+int orc_gptq_ex(int8_t *codes, float *scales, double *qerr_out, const float *W, const float *H,
+                const float *imp, int64_t N, int64_t K, int64_t G, double damp, int flags,
+                const float *book)
 {
+    if (!(flags & ORC_NF4)) book = NULL;
+    if ((flags & ORC_NF4) && !book) return ORC_ERR_INVALID_ARG;
     if (N < 1 || K < 2 || (K & 1) || G < 1 || K % G != 0) return ORC_ERR_INVALID_ARG;
     if (!all_finite_f32(W, N * K)) return ORC_ERR_NONFINITE;
     if (imp && !all_finite_f32(imp, K)) return ORC_ERR_NONFINITE;
@@ -693,11 +774,17 @@ int orc_gptq(int8_t *codes, float *scales, double *qerr_out, const float *W, con
     if (st != ORC_OK) { free(U); return st; }
     int64_t *rows = (int64_t *)malloc((size_t)N * sizeof(int64_t));
     for (int64_t n = 0; n < N; n++) rows[n] = n;
-    orc_gptq_sweep(codes, scales, W, U, K, G, rows, N);
+    orc_gptq_sweep_ex(codes, scales, W, U, K, G, rows, N, flags, book);
     free(rows);
     free(U);
-    if (qerr_out) *qerr_out = orc_qerr(codes, scales, W, imp, N, K, G, NULL);
+    if (qerr_out) *qerr_out = orc_qerr_ex(codes, scales, W, imp, N, K, G, book, NULL);
     return ORC_OK;
+}
+
+int orc_gptq(int8_t *codes, float *scales, double *qerr_out, const float *W, const float *H,
+             const float *imp, int64_t N, int64_t K, int64_t G, double damp)
+{
+    return orc_gptq_ex(codes, scales, qerr_out, W, H, imp, N, K, G, damp, 0, NULL);
 }
 
 /* ------------------------------------------------------------ replay checker */
@@ -705,19 +792,24 @@ int orc_gptq(int8_t *codes, float *scales, double *qerr_out, const float *W, con
 /* Replays the sweep on the listed rows, feeding it the candidate codes and
  * scales, and classifies each candidate code against the decision the
  * reference arithmetic takes at the same point:
- *   stats[0] codes equal to clamp(rint(v))                      (exact)
+ *   stats[0] codes equal to the reference's                      (exact)
  *   stats[1] the other neighbour, with v within delta of a tie   (tie flips)
  *   stats[2] anything else                                       (inadmissible)
  *   stats[3] groups whose scale differs by more than scale_tol (relative)
- * v = fl32(w)/s with the reference's own scale; the trajectory follows the
- * candidate (w_j -= e U[i][j] with e from the candidate's c and s), so a
- * tie flip's downstream effect is not counted again.  max_rel[0] gets the
- * largest relative scale difference. */
-void orc_gptq_replay(int64_t *stats, double *max_rel, const int8_t *cand_codes,
-                     const float *cand_scales, const float *W, const double *U,
-                     int64_t K, int64_t G, const int64_t *rows, int64_t nrows,
-                     double delta, double scale_tol)
+ * v = fl32(w)/s with the reference's own scale (on the uniform grid v is in
+ * steps and a tie is a half-integer; on a codebook a tie is the midpoint of two
+ * neighbouring levels and delta is a fraction of their spacing); the trajectory
+ * follows the candidate (w_j -= e U[i][j] with e from the candidate's code and
+ * scale), so a tie flip's downstream effect is not counted again.  max_rel[0]
+ * gets the largest relative scale difference.  flags and book as for
+ * orc_gptq_sweep_ex. */
+void orc_gptq_replay_ex(int64_t *stats, double *max_rel, const int8_t *cand_codes,
+                        const float *cand_scales, const float *W, const double *U,
+                        int64_t K, int64_t G, const int64_t *rows, int64_t nrows,
+                        double delta, double scale_tol, int flags, const float *book)
 {
+    const int stat = (flags & ORC_STATIC_GROUPS) != 0;
+    if (!(flags & ORC_NF4)) book = NULL;
     int64_t exact = 0, flips = 0, bad = 0, smis = 0;
     double mrel = 0.0;
 #pragma omp parallel for schedule(dynamic, 1) reduction(+ : exact, flips, bad, smis) reduction(max : mrel)
@@ -730,7 +822,8 @@ void orc_gptq_replay(int64_t *stats, double *max_rel, const int8_t *cand_codes,
             if (i % G == 0) {
                 double amax = 0.0;
                 for (int64_t k = i; k < i + G; k++) amax = fmax(amax, fabs(wk[k]));
-                s_ref = group_scale(amax);
+                if (stat) amax = group_amax_f32(w0, i, G);
+                s_ref = grid_scale(amax, book);
                 s_c = cand_scales[r * (K / G) + i / G];
                 double den = fabs((double)s_ref) > 0.0 ? fabs((double)s_ref) : 1e-30;
                 double rel = fabs((double)s_c - (double)s_ref) / den;
@@ -739,10 +832,10 @@ void orc_gptq_replay(int64_t *stats, double *max_rel, const int8_t *cand_codes,
                 if (rel > scale_tol) smis++;
             }
             int cg = cand_codes[r * K + i];
-            int cr = quant_code(wk[i], s_ref);
+            int cr = grid_code(wk[i], s_ref, book);
             if (cg == cr) {
                 exact++;
-            } else if (s_ref != 0.0f) {
+            } else if (s_ref != 0.0f && !book) {
                 double v = (double)((float)wk[i] / s_ref);
                 double rv = nearbyint(v);
                 double dist = fabs(v - rv);
@@ -751,10 +844,17 @@ void orc_gptq_replay(int64_t *stats, double *max_rel, const int8_t *cand_codes,
                 if (other < -8.0) other = -8.0;
                 if (dist >= 0.5 - delta && (double)cg == other) flips++;
                 else bad++;
+            } else if (s_ref != 0.0f && (cg == cr + 1 || cg == cr - 1) && cg >= 0 && cg < 16) {
+                int lo = cg < cr ? cg : cr;
+                double v = (double)((float)wk[i] / s_ref);
+                double mid = 0.5 * ((double)book[lo] + (double)book[lo + 1]);
+                if (fabs(v - mid) <= delta * ((double)book[lo + 1] - (double)book[lo])) flips++;
+                else bad++;
             } else {
                 bad++;
             }
-            double e = (wk[i] - (double)cg * (double)s_c) / U[i * K + i];
+            double cv = (cg >= -8 && cg < 16 && (book ? cg >= 0 : cg < 8)) ? grid_value(cg, s_c, book) : 0.0;
+            double e = (wk[i] - cv) / U[i * K + i];
             const double *ui = U + i * K;
             for (int64_t j = i + 1; j < K; j++) wk[j] -= e * ui[j];
         }
@@ -765,4 +865,13 @@ void orc_gptq_replay(int64_t *stats, double *max_rel, const int8_t *cand_codes,
     stats[2] = bad;
     stats[3] = smis;
     *max_rel = mrel;
+}
+
+void orc_gptq_replay(int64_t *stats, double *max_rel, const int8_t *cand_codes,
+                     const float *cand_scales, const float *W, const double *U,
+                     int64_t K, int64_t G, const int64_t *rows, int64_t nrows,
+                     double delta, double scale_tol)
+{
+    orc_gptq_replay_ex(stats, max_rel, cand_codes, cand_scales, W, U, K, G, rows, nrows, delta, scale_tol, 0,
+                       NULL);
 }
