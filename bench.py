@@ -41,8 +41,8 @@ SWEEP_BLOCK = 128          # lazy-batch width of gptq_sweep (include/gq.h)
 # Valid only for the kernel sources they were taken on: any change to those
 # files makes the figure stale and it is reported as null.
 TRAFFIC = {
-    "attn5120": {"fetch_bytes": 1072593.536585366 * 1.99957 * 1024, "write_bytes": 188160.0 * 1.00000 * 1024,
-                 "sources_sha256_16": "f82695a20032dd0b"},
+    "attn5120": {"fetch_bytes": 1077887.3658536586 * 1.99975 * 1024, "write_bytes": 188160.0 * 1.00000 * 1024,
+                 "sources_sha256_16": "b4ffe360e44d515c"},
 }
 TRAFFIC_SOURCES = ("post_weight_quantization_accumulate_amd/csrc/ozaki.hip",
                    "post_weight_quantization_accumulate_amd/csrc/gq_internal.h")
@@ -246,6 +246,7 @@ def main():
     out["rtn"] = rtn_measure(gq, torch, W, imp, G, dev)
     out["hfqm"] = hfqm_measure(gq, blob, imp, K)
     out["hadamard"] = hadamard_measure(gq, torch, W, Hs, dev)
+    out["variants"] = variants_measure(gq, torch, W, U, imp, G, dev)
     out["rtn"]["qerr_gptq_over_rtn"] = qerr[0] / out["rtn"]["qerr"] if out["rtn"]["qerr"] else None
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, X, W)
@@ -277,6 +278,38 @@ def hadamard_measure(gq, torch, W, H, dev, block=1024, reps=10):
         res[name + "_ms"] = ms
         res[name + "_gb_per_s"] = nbytes / (ms * 1e-3) / 1e9
         res[name + "_frac_of_hbm_peak"] = nbytes / (ms * 1e-3) / 1e9 / 8000.0
+    return res
+
+
+def variants_measure(gq, torch, W, U, imp, G, dev, reps=3):
+    """The sweep's variants under the step's U (static groups, the NF4 codebook,
+    both; "plain" is gptq_sweep_ex with no flag, the step's own sweep) and NF4
+    round to nearest, each timed per API call with HIP events after the steps,
+    with its qerr (same importance)."""
+    N, K = W.shape
+    codes = torch.empty(N * (K // 2), dtype=torch.uint8, device=dev)
+    scales = torch.empty(N * (K // G), dtype=torch.float32, device=dev)
+    ws = gq.workspace(gq.gptq_sweep_workspace_size(N, K, G), dev)
+    ws_r = gq.workspace(gq.rtn_quantize_workspace_size(N, K, G), dev)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    res = {"sweep_ms": {}, "qerr": {}}
+    calls = [(name, lambda f=f: gq.gptq_sweep_ex(codes, scales, W, U, imp, G, f, ws))
+             for name, f in (("plain", 0), ("static", gq.GQ_STATIC_GROUPS), ("nf4", gq.GQ_NF4),
+                             ("static_nf4", gq.GQ_STATIC_GROUPS | gq.GQ_NF4))]
+    calls.append(("rtn_nf4", lambda: gq.rtn_quantize_ex(codes, scales, W, imp, G, gq.GQ_NF4, ws_r)))
+    for name, fn in calls:
+        q = fn()
+        torch.cuda.synchronize()
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        if name == "rtn_nf4":
+            res["rtn_nf4_ms"] = a.elapsed_time(b) / reps
+        else:
+            res["sweep_ms"][name] = a.elapsed_time(b) / reps
+        res["qerr"][name] = q
     return res
 
 

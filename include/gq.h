@@ -216,6 +216,44 @@ int gptq_quantize(uint8_t *codes, float *scales, double *qerr_out, const float *
                   float damp, void *ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * Variants of the sweep and of the round-to-nearest pack, added as new symbols
+ * that the originals forward to with flags = 0 (ork-driver wiki, "Exp 2026-08-18
+ * GPTQ Int4": extend by a variant, never by changing a signature).  Flag bits:
+ *   GQ_STATIC_GROUPS  every (row, group) scale is fixed before the sweep from the
+ *                     original weights (as AutoGPTQ's static_groups), instead of
+ *                     at the group's first column from its error-updated values.
+ *                     Error feedback may then carry a value past the grid's
+ *                     ends, where the code clamps.  No effect on rtn_quantize_ex,
+ *                     whose scales are always the original weights'.
+ *   GQ_NF4            the 16-level NF4 codebook (the 4-bit pack the same wiki's
+ *                     qerr section scores beside the uniform grid) instead of the
+ *                     uniform int4 grid: scale = absmax of the group, code = the
+ *                     unsigned index 0..15 of the level nearest to w / scale
+ *                     (a value on the midpoint of two levels takes the lower),
+ *                     w ~ level[code] * scale; an all-zero group takes code 7
+ *                     (level 0.0).  gq_nf4_levels gives the table.
+ * Other bits are GQ_ERR_INVALID_ARG.  Codes are packed two per byte as for
+ * gptq_sweep (unsigned nibbles under GQ_NF4); qerr uses the dequantised value of
+ * the chosen grid.
+ */
+enum { GQ_STATIC_GROUPS = 1u, GQ_NF4 = 2u };
+
+/* The 16 NF4 levels, ascending, fp32 (QLoRA's 4-bit NormalFloat: standard normal
+ * quantiles at evenly spaced probabilities, 7 below zero and 8 above, the
+ * outermost at 1 - (1/32 + 1/30)/2, scaled to [-1, 1]).  levels: host, 16 floats. */
+void gq_nf4_levels(float *levels);
+
+/* gptq_sweep with flags (above); everything else as gptq_sweep, same workspace. */
+int gptq_sweep_ex(uint8_t *codes, float *scales, double *qerr_out, const float *W, const float *U,
+                  const float *imp, int64_t N, int64_t K, int64_t group, uint32_t flags, void *ws,
+                  size_t ws_bytes, hipStream_t stream);
+
+/* gptq_quantize with flags (above); same workspace as gptq_quantize. */
+int gptq_quantize_ex(uint8_t *codes, float *scales, double *qerr_out, const float *W, const float *H,
+                     const float *imp, int64_t N, int64_t K, int64_t group, float damp, uint32_t flags, void *ws,
+                     size_t ws_bytes, hipStream_t stream);
+
+/*
  * Block Walsh-Hadamard rotation, the rotation GPTQ composes with (ork-driver wiki,
  * "Exp 2026-08-18 GPTQ Int4": rotate, then quantise, as in QuaRot).
  * R = blockdiag(H_b, ..., H_b) diag(signs) / sqrt(b) over the K input channels,
@@ -258,6 +296,12 @@ size_t rtn_quantize_workspace_size(int64_t N, int64_t K, int64_t group);
  */
 int rtn_quantize(uint8_t *codes, float *scales, double *qerr_out, const float *W, const float *imp,
                  int64_t N, int64_t K, int64_t group, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* rtn_quantize with flags (GQ_NF4: the NF4 codebook; GQ_STATIC_GROUPS changes
+ * nothing); same workspace as rtn_quantize. */
+int rtn_quantize_ex(uint8_t *codes, float *scales, double *qerr_out, const float *W, const float *imp,
+                    int64_t N, int64_t K, int64_t group, uint32_t flags, void *ws, size_t ws_bytes,
+                    hipStream_t stream);
 
 /*
  * HFQM calibration package (.calib.hfq), the container that carries stored

@@ -21,6 +21,7 @@ LIB_PATH = os.path.join(_HERE, "libgq.so")
 (GQ_OK, GQ_ERR_INVALID_ARG, GQ_ERR_NOT_PD, GQ_ERR_NONFINITE, GQ_ERR_NO_CALIBRATION, GQ_ERR_HIP, GQ_ERR_INTERNAL,
  GQ_ERR_IO) = range(8)
 GQ_HFQM_F32, GQ_HFQM_HESSIAN = 0, 130
+GQ_STATIC_GROUPS, GQ_NF4 = 1, 2
 GQ_F32, GQ_BF16 = 0, 1
 GQ_PSD_AUTO, GQ_PSD_F64 = 0, 1
 
@@ -30,6 +31,7 @@ EXPORTS = (
     "psd_project_flops", "psd_project_products", "gq_set_timing", "psd_project_last_timing", "gq_set_psd_products",
     "gptq_factor_workspace_size", "gptq_factor", "gptq_sweep_workspace_size", "gptq_sweep",
     "gptq_quantize_workspace_size", "gptq_quantize", "rtn_quantize_workspace_size", "rtn_quantize",
+    "gptq_sweep_ex", "gptq_quantize_ex", "rtn_quantize_ex", "gq_nf4_levels",
     "hfqm_write", "hfqm_read_header", "hfqm_read_entry", "hfqm_read_payload",
     "hadamard_rotate_rows", "hadamard_rotate_hessian_workspace_size", "hadamard_rotate_hessian",
 )
@@ -54,6 +56,7 @@ def lib() -> ctypes.CDLL:
         L = ctypes.CDLL(LIB_PATH)
         P, I64, I, SZ, F, D = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t,
                                ctypes.c_float, ctypes.c_double)
+        U32 = ctypes.c_uint32
         sig = {
             "gq_abi_version": (I, []),
             "gq_last_error": (ctypes.c_char_p, []),
@@ -76,6 +79,10 @@ def lib() -> ctypes.CDLL:
             "gptq_quantize": (I, [P, P, P, P, P, P, I64, I64, I64, F, P, SZ, P]),
             "rtn_quantize_workspace_size": (SZ, [I64, I64, I64]),
             "rtn_quantize": (I, [P, P, P, P, P, I64, I64, I64, P, SZ, P]),
+            "rtn_quantize_ex": (I, [P, P, P, P, P, I64, I64, I64, U32, P, SZ, P]),
+            "gptq_sweep_ex": (I, [P, P, P, P, P, P, I64, I64, I64, U32, P, SZ, P]),
+            "gptq_quantize_ex": (I, [P, P, P, P, P, P, I64, I64, I64, F, U32, P, SZ, P]),
+            "gq_nf4_levels": (None, [P]),
             "hfqm_write": (I, [ctypes.c_char_p, ctypes.c_uint32, ctypes.c_char_p, I64, P, P, P, P, P, P, P]),
             "hfqm_read_header": (I, [ctypes.c_char_p, P, P, P, P, SZ, P]),
             "hfqm_read_entry": (I, [ctypes.c_char_p, I64, P, SZ, P, P, P, P, P, P]),
@@ -215,21 +222,44 @@ def gptq_sweep_workspace_size(N: int, K: int, group: int) -> int:
     return int(lib().gptq_sweep_workspace_size(N, K, group))
 
 
-def gptq_sweep(codes, scales, W, U, imp, group: int, ws, want_qerr: bool = True):
-    """Codes/scales of the GPTQ sweep of W under U; returns qerr (or None)."""
+def _quant_args(codes, scales, W, M, imp, group, ws, mname):
     N, K = W.shape
     _need(W, "W", torch.float32)
-    _need(U, "U", torch.float32, K * K)
+    if M is not None:
+        _need(M, mname, torch.float32, K * K)
     _need(codes, "codes", torch.uint8, N * (K // 2))
     _need(scales, "scales", torch.float32, N * (K // max(group, 1)))
     if imp is not None:
         _need(imp, "imp", torch.float32, K)
     _need(ws, "ws", torch.uint8)
+    return N, K
+
+
+def gptq_sweep(codes, scales, W, U, imp, group: int, ws, want_qerr: bool = True):
+    """Codes/scales of the GPTQ sweep of W under U; returns qerr (or None)."""
+    N, K = _quant_args(codes, scales, W, U, imp, group, ws, "U")
     q = ctypes.c_double(0.0)
     _check(lib().gptq_sweep(_ptr(codes), _ptr(scales), ctypes.byref(q) if want_qerr else None,
                             _ptr(W), _ptr(U), _ptr(imp), N, K, group, _ptr(ws), ws.numel(),
                             _stream(W)), "gptq_sweep")
     return q.value if want_qerr else None
+
+
+def gptq_sweep_ex(codes, scales, W, U, imp, group: int, flags: int, ws, want_qerr: bool = True):
+    """gptq_sweep with flags (GQ_STATIC_GROUPS, GQ_NF4); returns qerr (or None)."""
+    N, K = _quant_args(codes, scales, W, U, imp, group, ws, "U")
+    q = ctypes.c_double(0.0)
+    _check(lib().gptq_sweep_ex(_ptr(codes), _ptr(scales), ctypes.byref(q) if want_qerr else None,
+                               _ptr(W), _ptr(U), _ptr(imp), N, K, group, flags, _ptr(ws), ws.numel(),
+                               _stream(W)), "gptq_sweep_ex")
+    return q.value if want_qerr else None
+
+
+def nf4_levels():
+    """The library's 16 NF4 levels (fp32, ascending) as a host tensor."""
+    out = (ctypes.c_float * 16)()
+    lib().gq_nf4_levels(out)
+    return torch.tensor(list(out), dtype=torch.float32)
 
 
 def rtn_quantize_workspace_size(N: int, K: int, group: int) -> int:
@@ -238,16 +268,20 @@ def rtn_quantize_workspace_size(N: int, K: int, group: int) -> int:
 
 def rtn_quantize(codes, scales, W, imp, group: int, ws, want_qerr: bool = True):
     """Round-to-nearest codes/scales of W on the sweep's grid; returns qerr (or None)."""
-    N, K = W.shape
-    _need(W, "W", torch.float32)
-    _need(codes, "codes", torch.uint8, N * (K // 2))
-    _need(scales, "scales", torch.float32, N * (K // max(group, 1)))
-    if imp is not None:
-        _need(imp, "imp", torch.float32, K)
-    _need(ws, "ws", torch.uint8)
+    N, K = _quant_args(codes, scales, W, None, imp, group, ws, "")
     q = ctypes.c_double(0.0)
     _check(lib().rtn_quantize(_ptr(codes), _ptr(scales), ctypes.byref(q) if want_qerr else None,
                               _ptr(W), _ptr(imp), N, K, group, _ptr(ws), ws.numel(), _stream(W)), "rtn_quantize")
+    return q.value if want_qerr else None
+
+
+def rtn_quantize_ex(codes, scales, W, imp, group: int, flags: int, ws, want_qerr: bool = True):
+    """rtn_quantize with flags (GQ_NF4); returns qerr (or None)."""
+    N, K = _quant_args(codes, scales, W, None, imp, group, ws, "")
+    q = ctypes.c_double(0.0)
+    _check(lib().rtn_quantize_ex(_ptr(codes), _ptr(scales), ctypes.byref(q) if want_qerr else None,
+                                 _ptr(W), _ptr(imp), N, K, group, flags, _ptr(ws), ws.numel(), _stream(W)),
+           "rtn_quantize_ex")
     return q.value if want_qerr else None
 
 
@@ -255,16 +289,19 @@ def gptq_quantize_workspace_size(N: int, K: int, group: int) -> int:
     return int(lib().gptq_quantize_workspace_size(N, K, group))
 
 
+def gptq_quantize_ex(codes, scales, W, H, imp, group: int, damp: float, flags: int, ws, want_qerr: bool = True):
+    """gptq_quantize with flags (GQ_STATIC_GROUPS, GQ_NF4); returns qerr (or None)."""
+    N, K = _quant_args(codes, scales, W, H, imp, group, ws, "H")
+    q = ctypes.c_double(0.0)
+    _check(lib().gptq_quantize_ex(_ptr(codes), _ptr(scales), ctypes.byref(q) if want_qerr else None,
+                                  _ptr(W), _ptr(H), _ptr(imp), N, K, group, float(damp), flags, _ptr(ws),
+                                  ws.numel(), _stream(W)), "gptq_quantize_ex")
+    return q.value if want_qerr else None
+
+
 def gptq_quantize(codes, scales, W, H, imp, group: int, damp: float, ws, want_qerr: bool = True):
     """Damping, Cholesky, U and the sweep in one call; returns qerr (or None)."""
-    N, K = W.shape
-    _need(W, "W", torch.float32)
-    _need(H, "H", torch.float32, K * K)
-    _need(codes, "codes", torch.uint8, N * (K // 2))
-    _need(scales, "scales", torch.float32, N * (K // max(group, 1)))
-    if imp is not None:
-        _need(imp, "imp", torch.float32, K)
-    _need(ws, "ws", torch.uint8)
+    N, K = _quant_args(codes, scales, W, H, imp, group, ws, "H")
     q = ctypes.c_double(0.0)
     _check(lib().gptq_quantize(_ptr(codes), _ptr(scales), ctypes.byref(q) if want_qerr else None,
                                _ptr(W), _ptr(H), _ptr(imp), N, K, group, float(damp), _ptr(ws),

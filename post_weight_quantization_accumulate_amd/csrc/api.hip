@@ -268,6 +268,12 @@ size_t sweep_bytes(int64_t N, int64_t K)
     return c.off;
 }
 
+// The public flags map onto the kernels' mode bits.
+int mode_of(uint32_t flags)
+{
+    return ((flags & GQ_STATIC_GROUPS) ? MODE_STATIC : 0) | ((flags & GQ_NF4) ? MODE_NF4 : 0);
+}
+
 bool valid_group(int64_t G, int64_t K)
 {
     if (G < 1 || G > 128) return false;
@@ -385,11 +391,15 @@ int run_factor(float *U, const float *H, int64_t K, float damp, FactorWs &w, hip
 }
 
 int run_sweep(uint8_t *codes, float *scales, double *qerr_out, const float *W, const float *U,
-              const float *imp, int64_t N, int64_t K, int64_t G, SweepWs &w, hipStream_t s)
+              const float *imp, int64_t N, int64_t K, int64_t G, int mode, SweepWs &w, hipStream_t s)
 {
     GQ_HIP(launch_fill_u32(w.sc.status, 4, 0u, s), "fill");
     GQ_HIP(launch_copy_check(w.Wk, W, N * K, w.sc.status, s), "copy W");
     if (imp) GQ_HIP(launch_check_finite(imp, K, w.sc.status, s), "check imp");
+    // static groups: every scale from the original weights, before the sweep
+    // (the round-to-nearest pass writes them; its codes are overwritten below)
+    if (mode & MODE_STATIC)
+        GQ_HIP(launch_rtn(W, codes, scales, nullptr, nullptr, N, K, G, mode, w.sc.status, s, nullptr), "scales");
     // Column order as in the unblocked sweep; every column receives the
     // feedback of all earlier columns before it is quantised: from its own
     // block inside the sweep kernel, from earlier blocks of its group through
@@ -399,7 +409,7 @@ int run_sweep(uint8_t *codes, float *scales, double *qerr_out, const float *W, c
         for (int64_t b0 = g0; b0 < g1; b0 += kSweepBlock) {
             const int64_t bw = (g1 - b0) < kSweepBlock ? (g1 - b0) : kSweepBlock;
             float *ETb = w.ET + (b0 - g0) * N;          // this block's rows of the group's E^T
-            GQ_HIP(launch_sweep_block(w.Wk, ETb, codes, scales, U, N, K, G, b0, s), "sweep block");
+            GQ_HIP(launch_sweep_block(w.Wk, ETb, codes, scales, U, N, K, G, b0, mode, s), "sweep block");
             const int64_t e = b0 + bw;
             if (e < g1) {
                 GemmDesc d = gemm(ETb, N, U + b0 * K + e, K, N, g1 - e, bw, w.Wk + e, K);
@@ -418,7 +428,7 @@ int run_sweep(uint8_t *codes, float *scales, double *qerr_out, const float *W, c
         }
     }
     if (qerr_out) {
-        GQ_HIP(launch_qerr(w.sc.partials, W, codes, scales, imp, N, K, G, s), "qerr");
+        GQ_HIP(launch_qerr(w.sc.partials, W, codes, scales, imp, N, K, G, mode, s), "qerr");
         GQ_HIP(launch_qerr_reduce(w.sc.d, w.sc.partials, qerr_partials(N), s), "qerr reduce");
     }
     unsigned st = 0;
@@ -741,18 +751,32 @@ size_t gptq_sweep_workspace_size(int64_t N, int64_t K, int64_t group)
     return sweep_bytes(N, K);
 }
 
-int gptq_sweep(uint8_t *codes, float *scales, double *qerr_out, const float *W, const float *U,
-               const float *imp, int64_t N, int64_t K, int64_t group, void *ws, size_t ws_bytes,
-               hipStream_t stream)
+int gptq_sweep_ex(uint8_t *codes, float *scales, double *qerr_out, const float *W, const float *U,
+                  const float *imp, int64_t N, int64_t K, int64_t group, uint32_t flags, void *ws,
+                  size_t ws_bytes, hipStream_t stream)
 {
     g_last_error.clear();
     int rc = check_sweep_args(codes, scales, W, U, N, K, group);
     if (rc) return rc;
+    if (flags & ~(uint32_t)(GQ_STATIC_GROUPS | GQ_NF4)) return fail(GQ_ERR_INVALID_ARG, "unknown flag bits");
     if (!ws) return fail(GQ_ERR_INVALID_ARG, "null workspace");
     if (ws_bytes < sweep_bytes(N, K)) return fail(GQ_ERR_INVALID_ARG, "workspace too small");
     Carver cv(ws);
     SweepWs w = carve_sweep(cv, N, K);
-    return run_sweep(codes, scales, qerr_out, W, U, imp, N, K, group, w, stream);
+    return run_sweep(codes, scales, qerr_out, W, U, imp, N, K, group, mode_of(flags), w, stream);
+}
+
+int gptq_sweep(uint8_t *codes, float *scales, double *qerr_out, const float *W, const float *U,
+               const float *imp, int64_t N, int64_t K, int64_t group, void *ws, size_t ws_bytes,
+               hipStream_t stream)
+{
+    return gptq_sweep_ex(codes, scales, qerr_out, W, U, imp, N, K, group, 0u, ws, ws_bytes, stream);
+}
+
+void gq_nf4_levels(float *levels)
+{
+    if (levels)
+        for (int i = 0; i < 16; ++i) levels[i] = kNF4[i];
 }
 
 struct RtnWs {
@@ -814,10 +838,12 @@ size_t rtn_quantize_workspace_size(int64_t N, int64_t K, int64_t group)
     return c.off;
 }
 
-int rtn_quantize(uint8_t *codes, float *scales, double *qerr_out, const float *W, const float *imp, int64_t N,
-                 int64_t K, int64_t group, void *ws, size_t ws_bytes, hipStream_t stream)
+int rtn_quantize_ex(uint8_t *codes, float *scales, double *qerr_out, const float *W, const float *imp, int64_t N,
+                    int64_t K, int64_t group, uint32_t flags, void *ws, size_t ws_bytes, hipStream_t stream)
 {
     g_last_error.clear();
+    if (flags & ~(uint32_t)(GQ_STATIC_GROUPS | GQ_NF4)) return fail(GQ_ERR_INVALID_ARG, "unknown flag bits");
+    const int mode = mode_of(flags);
     if (!codes || !scales || !W) return fail(GQ_ERR_INVALID_ARG, "null required pointer");
     if (N < 1) return fail(GQ_ERR_INVALID_ARG, "N must be >= 1");
     if (K < 2 || (K & 1)) return fail(GQ_ERR_INVALID_ARG, "K must be even and >= 2 (two codes per byte)");
@@ -830,8 +856,8 @@ int rtn_quantize(uint8_t *codes, float *scales, double *qerr_out, const float *W
     GQ_HIP(launch_fill_u32(w.sc.status, 4, 0u, stream), "fill");
     if (imp) GQ_HIP(launch_check_finite(imp, K, w.sc.status, stream), "check imp");
     int64_t nparts = 0;
-    GQ_HIP(launch_rtn(W, codes, scales, imp, qerr_out ? w.partials : nullptr, N, K, group, w.sc.status, stream,
-                      &nparts),
+    GQ_HIP(launch_rtn(W, codes, scales, imp, qerr_out ? w.partials : nullptr, N, K, group, mode, w.sc.status,
+                      stream, &nparts),
            "rtn");
     if (qerr_out) GQ_HIP(launch_qerr_reduce(w.sc.d, w.partials, nparts, stream), "qerr reduce");
     // status and the two sums come back with one synchronisation
@@ -846,6 +872,12 @@ int rtn_quantize(uint8_t *codes, float *scales, double *qerr_out, const float *W
     return GQ_OK;
 }
 
+int rtn_quantize(uint8_t *codes, float *scales, double *qerr_out, const float *W, const float *imp, int64_t N,
+                 int64_t K, int64_t group, void *ws, size_t ws_bytes, hipStream_t stream)
+{
+    return rtn_quantize_ex(codes, scales, qerr_out, W, imp, N, K, group, 0u, ws, ws_bytes, stream);
+}
+
 size_t gptq_quantize_workspace_size(int64_t N, int64_t K, int64_t group)
 {
     (void)group;
@@ -853,13 +885,14 @@ size_t gptq_quantize_workspace_size(int64_t N, int64_t K, int64_t group)
     return factor_bytes(K) + align_up((size_t)K * (size_t)K * sizeof(float)) + sweep_bytes(N, K);
 }
 
-int gptq_quantize(uint8_t *codes, float *scales, double *qerr_out, const float *W, const float *H,
-                  const float *imp, int64_t N, int64_t K, int64_t group, float damp, void *ws,
-                  size_t ws_bytes, hipStream_t stream)
+int gptq_quantize_ex(uint8_t *codes, float *scales, double *qerr_out, const float *W, const float *H,
+                     const float *imp, int64_t N, int64_t K, int64_t group, float damp, uint32_t flags, void *ws,
+                     size_t ws_bytes, hipStream_t stream)
 {
     g_last_error.clear();
     int rc = check_sweep_args(codes, scales, W, H, N, K, group);
     if (rc) return rc;
+    if (flags & ~(uint32_t)(GQ_STATIC_GROUPS | GQ_NF4)) return fail(GQ_ERR_INVALID_ARG, "unknown flag bits");
     if (!ws) return fail(GQ_ERR_INVALID_ARG, "null workspace");
     if (ws_bytes < gptq_quantize_workspace_size(N, K, group)) return fail(GQ_ERR_INVALID_ARG, "workspace too small");
     char *base = (char *)ws;
@@ -868,7 +901,15 @@ int gptq_quantize(uint8_t *codes, float *scales, double *qerr_out, const float *
     void *sweep_ws = base + fb + align_up((size_t)K * (size_t)K * sizeof(float));
     rc = gptq_factor(U, H, K, damp, base, fb, stream);
     if (rc) return rc;
-    return gptq_sweep(codes, scales, qerr_out, W, U, imp, N, K, group, sweep_ws, sweep_bytes(N, K), stream);
+    return gptq_sweep_ex(codes, scales, qerr_out, W, U, imp, N, K, group, flags, sweep_ws, sweep_bytes(N, K),
+                         stream);
+}
+
+int gptq_quantize(uint8_t *codes, float *scales, double *qerr_out, const float *W, const float *H,
+                  const float *imp, int64_t N, int64_t K, int64_t group, float damp, void *ws,
+                  size_t ws_bytes, hipStream_t stream)
+{
+    return gptq_quantize_ex(codes, scales, qerr_out, W, H, imp, N, K, group, damp, 0u, ws, ws_bytes, stream);
 }
 
 }  // extern "C"

@@ -15,6 +15,13 @@
 // the scheduler can overlap.  Group maxima are a 16-lane xor-shuffle reduction.
 // The per-column errors leave the kernel transposed (k-major) through LDS, as
 // the A operand of the matrix-core block update that follows.
+//
+// Variants (the MODE template bits): static groups read every scale from
+// `scales`, written before the sweep from the original weights; NF4 takes scale
+// absmax and the nearest of the 16 codebook levels.  For NF4, lane j < 15 of a
+// row group compares the broadcast quotient with midpoint j, and the count of
+// true lanes in the row group (a ballot and a popcount) is the level index; the
+// level's value comes from a 16-entry LDS table.
 #include "gq_internal.h"
 
 namespace gq {
@@ -31,19 +38,25 @@ template <int src> __device__ inline float row_bcast(float x)
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x150 + src, 0xF, 0xF, false));
 }
 
+// Midpoint j of the NF4 levels in fp32 (j = 15: above every value).
+__device__ inline float nf4_mid(int j) { return j < 15 ? (kNF4[j] + kNF4[j + 1]) * 0.5f : INFINITY; }
+
 // Four waves per SIMD (two workgroups per CU): the grid has one workgroup per
 // 32 rows, which for ten thousand rows is just over one per CU.
-template <int G>
+template <int G, int MODE>
 __global__ __launch_bounds__(SW_NT, 4) void sweep_block_kernel(float *__restrict__ Wk, float *__restrict__ ET,
                                                            uint8_t *__restrict__ codes,
                                                            float *__restrict__ scales,
                                                            const float *__restrict__ U, int64_t N,
                                                            int64_t K, int64_t b0)
 {
+    constexpr bool STATIC = (MODE & MODE_STATIC) != 0, NF4 = (MODE & MODE_NF4) != 0;
     __shared__ __attribute__((aligned(16))) float Us[BW * UPITCH];
     __shared__ float rdiag[BW];
+    __shared__ float lev[16];
     const int tid = threadIdx.x;
     const int bw = (int)((K - b0) < BW ? (K - b0) : BW);
+    if (NF4 && tid < 16) lev[tid] = kNF4[tid];
 
     // U's block, zero outside the bw x bw corner; past bw the reciprocal
     // diagonal is 0, so padded columns carry zero error and change nothing.
@@ -70,7 +83,24 @@ __global__ __launch_bounds__(SW_NT, 4) void sweep_block_kernel(float *__restrict
         w[t] = (rv && col < bw) ? Wk[row * K + b0 + col] : 0.0f;
     }
 
-    float s = 1.0f, y = 1.0f;  // the group's scale (1 for an all-zero group) and RN(1/s)
+    // static groups: the scale of column cb + t's group (one group per lane when
+    // G >= 8); columns past bw have none
+    float sl[8];
+    if constexpr (STATIC) {
+        if constexpr (G >= 8) {
+            const float v = (rv && cb < bw) ? scales[row * ngroups + (b0 + cb) / G] : 0.0f;
+#pragma unroll
+            for (int t = 0; t < 8; ++t) sl[t] = v;
+        } else {
+#pragma unroll
+            for (int t = 0; t < 8; ++t) sl[t] = (rv && cb + t < bw) ? scales[row * ngroups + (b0 + cb + t) / G] : 0.0f;
+        }
+    }
+    // NF4: this lane's midpoint and the lanes 0..14 of its row group
+    const float mymid = nf4_mid(g16);
+    const unsigned long long rowmask = 0x7FFFull << (lane & 48);
+
+    float s = 1.0f, y = 0.0f;  // the group's scale (1 for an all-zero group) and RN(1/s) (0 there)
     float4 nu0 = *(const float4 *)&Us[cb], nu1 = *(const float4 *)&Us[cb + 4];
     // one column: the static index lets the broadcast source and the group test
     // be immediates
@@ -79,25 +109,31 @@ __global__ __launch_bounds__(SW_NT, 4) void sweep_block_kernel(float *__restrict
         constexpr int q = i / 8, t = i % 8;
         const float wi = row_bcast<q>(w[t]);
         if constexpr (i % G == 0) {
-            float m = 0.0f;
+            float sc;
+            if constexpr (STATIC) {
+                sc = row_bcast<q>(sl[t]);
+            } else {
+                float m = 0.0f;
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const int col = cb + u;
-                m = (col >= i && col < i + G) ? fmaxf(m, fabsf(w[u])) : m;
+                for (int u = 0; u < 8; ++u) {
+                    const int col = cb + u;
+                    m = (col >= i && col < i + G) ? fmaxf(m, fabsf(w[u])) : m;
+                }
+                m = fmaxf(m, __shfl_xor(m, 1, 16));
+                m = fmaxf(m, __shfl_xor(m, 2, 16));
+                m = fmaxf(m, __shfl_xor(m, 4, 16));
+                m = fmaxf(m, __shfl_xor(m, 8, 16));
+                sc = NF4 ? m : m / 7.0f;
+                if (g16 == 0 && rv && i < bw) scales[row * ngroups + (b0 + i) / G] = sc;
             }
-            m = fmaxf(m, __shfl_xor(m, 1, 16));
-            m = fmaxf(m, __shfl_xor(m, 2, 16));
-            m = fmaxf(m, __shfl_xor(m, 4, 16));
-            m = fmaxf(m, __shfl_xor(m, 8, 16));
-            const float sc = m / 7.0f;
-            if (g16 == 0 && rv && i < bw) scales[row * ngroups + (b0 + i) / G] = sc;
-            // A group whose scale is 0 is all zeros at its start, and its
-            // columns feed back nothing to each other, so every value met in it
-            // is 0; dividing by 1 there gives code 0 without a branch.
+            // A group whose scale is 0 takes the zero code: y = 0 makes the
+            // quotient 0 for any value, and with s = 1 the error is the value
+            // itself (with dynamic scales every value met there is 0; with
+            // static ones feedback may have moved it, and it passes on whole).
             s = sc != 0.0f ? sc : 1.0f;
-            y = 1.0f / s;
+            y = sc != 0.0f ? 1.0f / s : 0.0f;
         }
-        // q = RN(wi / s) by Markstein's correction step (Markstein 1990; Muller
+        // x = RN(wi / s) by Markstein's correction step (Markstein 1990; Muller
         // et al., Handbook of Floating-Point Arithmetic, division via FMA): with
         // y = RN(1/s) and q0 = RN(wi y), r = wi - s q0 is exact and RN(q0 + r y)
         // is the correctly rounded quotient (normal range), so the code is the
@@ -105,8 +141,19 @@ __global__ __launch_bounds__(SW_NT, 4) void sweep_block_kernel(float *__restrict
         // of the division's dozen.
         const float q0 = wi * y;
         const float rr = fmaf(-s, q0, wi);
-        const float c = fminf(fmaxf(rintf(fmaf(rr, y, q0)), -8.0f), 7.0f);
-        const float e = fmaf(-c, s, wi) * rdiag[i];       // s = 1 only where c = wi = 0
+        const float x = fmaf(rr, y, q0);
+        float c;                   // the value's multiple of s: the code, or its level
+        unsigned nib;
+        if constexpr (NF4) {
+            const unsigned long long gt = __ballot(x > mymid);
+            const int ci = __popcll(gt & rowmask);
+            c = lev[ci];
+            nib = (unsigned)ci;
+        } else {
+            c = fminf(fmaxf(rintf(x), -8.0f), 7.0f);
+            nib = (unsigned)(int)c & 0xFu;
+        }
+        const float e = fmaf(-c, s, wi) * rdiag[i];
         // U's row i was read one column ahead; read row i + 1 now
         const float4 u0 = nu0, u1 = nu1;
         if constexpr (i + 1 < BW) {
@@ -123,7 +170,7 @@ __global__ __launch_bounds__(SW_NT, 4) void sweep_block_kernel(float *__restrict
         w[7] = fmaf(-e, u1.w, w[7]);
         const bool own = (g16 == q);
         w[t] = own ? e : w[t];
-        cdw |= own ? ((unsigned)(int)c & 0xFu) << (4 * t) : 0u;
+        cdw |= own ? nib << (4 * t) : 0u;
         asm("" : "+v"(cdw));       // pack now: sunk to the end, the 128 codes would all stay live
     };
     static_for<BW>(column);
@@ -211,7 +258,9 @@ __device__ void block_sum2(double &a, double &b, double *sh)
     b = sh[QNT];
 }
 
-// Partial sums over a fixed row range per workgroup: sum imp (w - c s)^2, sum imp w^2.
+// Partial sums over a fixed row range per workgroup: sum imp (w - c s)^2, sum imp w^2,
+// with c the signed code, or with NF4 the level its unsigned index names.
+template <bool NF4>
 __global__ __launch_bounds__(QNT) void qerr_kernel(double *__restrict__ partials, const float *__restrict__ W,
                                                   const uint8_t *__restrict__ codes,
                                                   const float *__restrict__ scales,
@@ -219,6 +268,9 @@ __global__ __launch_bounds__(QNT) void qerr_kernel(double *__restrict__ partials
                                                   int64_t G, int64_t rows_per)
 {
     __shared__ double sh[2 * QNT];
+    __shared__ float lev[16];
+    if (NF4 && threadIdx.x < 16) lev[threadIdx.x] = kNF4[threadIdx.x];
+    __syncthreads();
     const int64_t r0 = blockIdx.x * rows_per;
     const int64_t r1 = (r0 + rows_per < N) ? r0 + rows_per : N;
     const int64_t half = K / 2, ng = K / G;
@@ -226,13 +278,20 @@ __global__ __launch_bounds__(QNT) void qerr_kernel(double *__restrict__ partials
     for (int64_t n = r0; n < r1; ++n) {
         for (int64_t m = threadIdx.x; m < half; m += QNT) {
             const unsigned b = codes[n * half + m];
-            const int c0 = (int)(b & 0xFu) - ((b & 0x8u) ? 16 : 0);
-            const int c1 = (int)(b >> 4) - ((b & 0x80u) ? 16 : 0);
+            float c0, c1;
+            if constexpr (NF4) {
+                c0 = lev[b & 0xFu];
+                c1 = lev[b >> 4];
+            } else {
+                c0 = (float)((int)(b & 0xFu) - ((b & 0x8u) ? 16 : 0));
+                c1 = (float)((int)(b >> 4) - ((b & 0x80u) ? 16 : 0));
+            }
             const int64_t k0 = 2 * m, k1 = 2 * m + 1;
             const float w0 = W[n * K + k0], w1 = W[n * K + k1];
             const float s0 = scales[n * ng + k0 / G], s1 = scales[n * ng + k1 / G];
             const double i0 = imp ? (double)imp[k0] : 1.0, i1 = imp ? (double)imp[k1] : 1.0;
-            const double d0 = (double)fmaf(-(float)c0, s0, w0), d1 = (double)fmaf(-(float)c1, s1, w1);
+            // exact products in fp64, one rounding in the difference
+            const double d0 = (double)w0 - (double)c0 * (double)s0, d1 = (double)w1 - (double)c1 * (double)s1;
             num += i0 * d0 * d0 + i1 * d1 * d1;
             den += i0 * (double)w0 * (double)w0 + i1 * (double)w1 * (double)w1;
         }
@@ -278,7 +337,17 @@ __device__ inline float rtn_code(float w, float s)
 {
     return s == 0.0f ? 0.0f : fminf(fmaxf(rintf(w / s), -8.0f), 7.0f);
 }
-__device__ inline unsigned rtn_nibble(float w, float s) { return (unsigned)(int)rtn_code(w, s) & 0xFu; }
+
+// NF4: the index of the level nearest to x (x in units of the scale), by a
+// four-step binary search over the 15 midpoints (mid[15] = +inf) held in LDS.
+__device__ inline int nf4_index(float x, const float *mid)
+{
+    int c = x > mid[7] ? 8 : 0;
+    c += x > mid[c + 3] ? 4 : 0;
+    c += x > mid[c + 1] ? 2 : 0;
+    c += x > mid[c] ? 1 : 0;
+    return c;
+}
 
 // One thread per 8 consecutive columns of a row at a time (K % 8 == 0, 16-byte
 // aligned W, 4-byte aligned codes): two 16-byte loads, one 4-byte store of 8
@@ -298,17 +367,26 @@ __device__ inline unsigned rtn_nibble(float w, float s) { return (unsigned)(int)
 // deterministic): no second pass over W.
 constexpr int RTN_NT = QNT;
 constexpr int RTN_MAX_WG = 2048;
-__device__ inline float rtn_code_y(float w, float s, float y)
+__device__ inline float rtn_quot_y(float w, float s, float y)
 {
     const float q0 = w * y;
     const float r = fmaf(-s, q0, w);
-    return fminf(fmaxf(rintf(fmaf(r, y, q0)), -8.0f), 7.0f);
+    return fmaf(r, y, q0);
 }
+// NF4 (template flag): scale absmax, code the nearest level's index (nf4_index of
+// the same correctly rounded quotient), and qerr from the level's value.
+template <bool NF4>
 __global__ __launch_bounds__(RTN_NT) void rtn8_kernel(const float *__restrict__ W, uint8_t *__restrict__ codes,
                                                       float *__restrict__ scales, int64_t N, int64_t K, int G,
                                                       unsigned *status, const float *__restrict__ imp,
                                                       double *__restrict__ partials)
 {
+    __shared__ float mid[16], lev[16];
+    if (NF4 && threadIdx.x < 16) {
+        mid[threadIdx.x] = nf4_mid(threadIdx.x);
+        lev[threadIdx.x] = kNF4[threadIdx.x];
+    }
+    if (NF4) __syncthreads();
     const int64_t chunks = K / 8, total = N * chunks;
     const int64_t ngroups = K / G;
     double num = 0.0, den = 0.0;
@@ -323,16 +401,25 @@ __global__ __launch_bounds__(RTN_NT) void rtn8_kernel(const float *__restrict__ 
         const float w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
 #pragma unroll
         for (int t = 0; t < 8; ++t) bad = bad || (valid && !isfinite(w[t]));
-        float sc[8], cv[8];                          // each column's scale and code
+        float sc[8], cv[8];                          // each column's scale and multiple of it
+        unsigned nb[8];                              // each column's nibble
         // the codes of columns t0 .. t1-1 under the group scale sg
         auto codes_of = [&](float sg, int t0, int t1) {
             const bool tiny = sg < 0x1p-60f;
             const float f = tiny ? 0x1p64f : 1.0f;
             const float ss = sg == 0.0f ? 1.0f : sg * f;
-            const float y = 1.0f / ss;
+            const float y = sg == 0.0f ? 0.0f : 1.0f / ss;    // quotient 0 in an all-zero group
             for (int t = t0; t < t1; ++t) {
                 sc[t] = sg;
-                cv[t] = sg == 0.0f ? 0.0f : rtn_code_y(w[t] * f, ss, y);
+                const float x = rtn_quot_y(w[t] * f, ss, y);
+                if constexpr (NF4) {
+                    const int ci = nf4_index(x, mid);
+                    cv[t] = lev[ci];
+                    nb[t] = (unsigned)ci;
+                } else {
+                    cv[t] = fminf(fmaxf(rintf(x), -8.0f), 7.0f);
+                    nb[t] = (unsigned)(int)cv[t] & 0xFu;
+                }
             }
         };
         if (G >= 8) {
@@ -340,21 +427,21 @@ __global__ __launch_bounds__(RTN_NT) void rtn8_kernel(const float *__restrict__ 
 #pragma unroll
             for (int t = 0; t < 8; ++t) m = fmaxf(m, fabsf(w[t]));
             for (int o = 1; o < G / 8; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
-            const float sg = m / 7.0f;
+            const float sg = NF4 ? m : m / 7.0f;
             if (valid && c % (G / 8) == 0) scales[row * ngroups + 8 * c / G] = sg;
             codes_of(sg, 0, 8);
         } else {
             for (int g0 = 0; g0 < 8; g0 += G) {
                 float m = 0.0f;
                 for (int t = g0; t < g0 + G; ++t) m = fmaxf(m, fabsf(w[t]));
-                const float sg = m / 7.0f;
+                const float sg = NF4 ? m : m / 7.0f;
                 if (valid) scales[row * ngroups + (8 * c + g0) / G] = sg;
                 codes_of(sg, g0, g0 + G);
             }
         }
         unsigned dw = 0;
 #pragma unroll
-        for (int t = 0; t < 8; ++t) dw |= ((unsigned)(int)cv[t] & 0xFu) << (4 * t);
+        for (int t = 0; t < 8; ++t) dw |= nb[t] << (4 * t);
         if (valid) *(unsigned *)(codes + row * (K / 2) + 4 * c) = dw;
         if (partials && valid) {
             float iw[8] = {1.0f, 1.0f, 1.0f, 1.0f, 1.0f, 1.0f, 1.0f, 1.0f};
@@ -384,11 +471,15 @@ __global__ __launch_bounds__(RTN_NT) void rtn8_kernel(const float *__restrict__ 
 }
 
 // Any other shape: one thread per unit of P = max(2, G) columns (whole groups,
-// whole code bytes), scalar loads and byte stores.
+// whole code bytes), scalar loads and byte stores; NF4 as in rtn8_kernel.
+template <bool NF4>
 __global__ __launch_bounds__(RTN_NT) void rtn_any_kernel(const float *__restrict__ W, uint8_t *__restrict__ codes,
                                                          float *__restrict__ scales, int64_t N, int64_t K, int G,
                                                          unsigned *status)
 {
+    __shared__ float mid[16];
+    if (NF4 && threadIdx.x < 16) mid[threadIdx.x] = nf4_mid(threadIdx.x);
+    if (NF4) __syncthreads();
     const int P = G > 2 ? G : 2;
     const int64_t units = K / P, idx = (int64_t)blockIdx.x * RTN_NT + threadIdx.x;
     if (idx >= N * units) return;
@@ -404,10 +495,11 @@ __global__ __launch_bounds__(RTN_NT) void rtn_any_kernel(const float *__restrict
                 bad = bad || !isfinite(w[u]);
                 m = fmaxf(m, fabsf(w[u]));
             }
-            sc = m / 7.0f;
+            sc = NF4 ? m : m / 7.0f;
             scales[row * (K / G) + (k0 + t) / G] = sc;
         }
-        const unsigned nib = rtn_nibble(w[t], sc);
+        const unsigned nib = NF4 ? (unsigned)nf4_index(sc == 0.0f ? 0.0f : w[t] / sc, mid)
+                                 : (unsigned)(int)rtn_code(w[t], sc) & 0xFu;
         if (t & 1) codes[row * (K / 2) + (k0 + t) / 2] = (uint8_t)(lo | nib << 4);
         else lo = nib;
     }
@@ -437,33 +529,55 @@ hipError_t launch_check_finite(const float *x, int64_t n, unsigned *status, hipS
     return hipGetLastError();
 }
 
-hipError_t launch_sweep_block(float *Wk, float *ET, uint8_t *codes, float *scales, const float *U,
-                              int64_t N, int64_t K, int64_t G, int64_t b0, hipStream_t s)
+template <int MODE>
+hipError_t launch_sweep_mode(float *Wk, float *ET, uint8_t *codes, float *scales, const float *U, int64_t N,
+                             int64_t K, int64_t G, int64_t b0, hipStream_t s)
 {
     const int64_t nwg = (N + ROWS_WG - 1) / ROWS_WG;
     const dim3 grid((unsigned)nwg), block(SW_NT);
+#define GQ_SWEEP_CASE(g)                                                                                          \
+    case g:                                                                                                       \
+        hipLaunchKernelGGL((sweep_block_kernel<g, MODE>), grid, block, 0, s, Wk, ET, codes, scales, U, N, K, b0); \
+        break;
     switch (G) {
-    case 1: hipLaunchKernelGGL(sweep_block_kernel<1>, grid, block, 0, s, Wk, ET, codes, scales, U, N, K, b0); break;
-    case 2: hipLaunchKernelGGL(sweep_block_kernel<2>, grid, block, 0, s, Wk, ET, codes, scales, U, N, K, b0); break;
-    case 4: hipLaunchKernelGGL(sweep_block_kernel<4>, grid, block, 0, s, Wk, ET, codes, scales, U, N, K, b0); break;
-    case 8: hipLaunchKernelGGL(sweep_block_kernel<8>, grid, block, 0, s, Wk, ET, codes, scales, U, N, K, b0); break;
-    case 16: hipLaunchKernelGGL(sweep_block_kernel<16>, grid, block, 0, s, Wk, ET, codes, scales, U, N, K, b0); break;
-    case 32: hipLaunchKernelGGL(sweep_block_kernel<32>, grid, block, 0, s, Wk, ET, codes, scales, U, N, K, b0); break;
-    case 64: hipLaunchKernelGGL(sweep_block_kernel<64>, grid, block, 0, s, Wk, ET, codes, scales, U, N, K, b0); break;
-    case 128: hipLaunchKernelGGL(sweep_block_kernel<128>, grid, block, 0, s, Wk, ET, codes, scales, U, N, K, b0); break;
+        GQ_SWEEP_CASE(1)
+        GQ_SWEEP_CASE(2)
+        GQ_SWEEP_CASE(4)
+        GQ_SWEEP_CASE(8)
+        GQ_SWEEP_CASE(16)
+        GQ_SWEEP_CASE(32)
+        GQ_SWEEP_CASE(64)
+        GQ_SWEEP_CASE(128)
     default: return hipErrorInvalidValue;      // the API admits powers of two up to 128 only
     }
+#undef GQ_SWEEP_CASE
     return hipGetLastError();
 }
 
+hipError_t launch_sweep_block(float *Wk, float *ET, uint8_t *codes, float *scales, const float *U,
+                              int64_t N, int64_t K, int64_t G, int64_t b0, int mode, hipStream_t s)
+{
+    switch (mode) {
+    case 0: return launch_sweep_mode<0>(Wk, ET, codes, scales, U, N, K, G, b0, s);
+    case MODE_STATIC: return launch_sweep_mode<MODE_STATIC>(Wk, ET, codes, scales, U, N, K, G, b0, s);
+    case MODE_NF4: return launch_sweep_mode<MODE_NF4>(Wk, ET, codes, scales, U, N, K, G, b0, s);
+    case MODE_STATIC | MODE_NF4:
+        return launch_sweep_mode<MODE_STATIC | MODE_NF4>(Wk, ET, codes, scales, U, N, K, G, b0, s);
+    default: return hipErrorInvalidValue;
+    }
+}
 hipError_t launch_qerr(double *partials, const float *W, const uint8_t *codes, const float *scales,
-                       const float *imp, int64_t N, int64_t K, int64_t G, hipStream_t s)
+                       const float *imp, int64_t N, int64_t K, int64_t G, int mode, hipStream_t s)
 {
     const int64_t np = N < QPARTS ? N : QPARTS;
     const int64_t rows_per = (N + np - 1) / np;
     const int64_t nwg = qerr_partials(N);
-    hipLaunchKernelGGL(qerr_kernel, dim3((unsigned)nwg), dim3(QNT), 0, s, partials, W, codes, scales, imp,
-                       N, K, G, rows_per);
+    if (mode & MODE_NF4)
+        hipLaunchKernelGGL(qerr_kernel<true>, dim3((unsigned)nwg), dim3(QNT), 0, s, partials, W, codes, scales, imp,
+                           N, K, G, rows_per);
+    else
+        hipLaunchKernelGGL(qerr_kernel<false>, dim3((unsigned)nwg), dim3(QNT), 0, s, partials, W, codes, scales, imp,
+                           N, K, G, rows_per);
     return hipGetLastError();
 }
 
@@ -486,25 +600,33 @@ int64_t rtn_partials(int64_t N, int64_t K)
 }
 
 hipError_t launch_rtn(const float *W, uint8_t *codes, float *scales, const float *imp, double *partials, int64_t N,
-                      int64_t K, int64_t G, unsigned *status, hipStream_t s, int64_t *nparts)
+                      int64_t K, int64_t G, int mode, unsigned *status, hipStream_t s, int64_t *nparts)
 {
     if (G < 1 || G > 128 || (G & (G - 1)) || K % G || K % 2) return hipErrorInvalidValue;
+    const bool nf4 = (mode & MODE_NF4) != 0;
     const bool wide = K % 8 == 0 && ((uintptr_t)W & 15) == 0 && ((uintptr_t)codes & 3) == 0 &&
                       ((uintptr_t)imp & 15) == 0;
     if (wide) {
         const int64_t nwg = rtn_workgroups(N, K);
-        hipLaunchKernelGGL(rtn8_kernel, dim3((unsigned)nwg), dim3(RTN_NT), 0, s, W, codes, scales, N, K, (int)G,
-                           status, imp, partials);
+        if (nf4)
+            hipLaunchKernelGGL(rtn8_kernel<true>, dim3((unsigned)nwg), dim3(RTN_NT), 0, s, W, codes, scales, N, K,
+                               (int)G, status, imp, partials);
+        else
+            hipLaunchKernelGGL(rtn8_kernel<false>, dim3((unsigned)nwg), dim3(RTN_NT), 0, s, W, codes, scales, N, K,
+                               (int)G, status, imp, partials);
         if (nparts) *nparts = nwg;
         return hipGetLastError();
     }
     const int64_t threads = N * (K / (G > 2 ? G : 2));
-    hipLaunchKernelGGL(rtn_any_kernel, dim3((unsigned)((threads + RTN_NT - 1) / RTN_NT)), dim3(RTN_NT), 0, s, W,
-                       codes, scales, N, K, (int)G, status);
+    const dim3 grid((unsigned)((threads + RTN_NT - 1) / RTN_NT));
+    if (nf4)
+        hipLaunchKernelGGL(rtn_any_kernel<true>, grid, dim3(RTN_NT), 0, s, W, codes, scales, N, K, (int)G, status);
+    else
+        hipLaunchKernelGGL(rtn_any_kernel<false>, grid, dim3(RTN_NT), 0, s, W, codes, scales, N, K, (int)G, status);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || !partials) return e;
     if (nparts) *nparts = qerr_partials(N);
-    return launch_qerr(partials, W, codes, scales, imp, N, K, G, s);
+    return launch_qerr(partials, W, codes, scales, imp, N, K, G, mode, s);
 }
 
 }  // namespace gq

@@ -217,17 +217,34 @@ constexpr int kSweepSuper = 512;
 hipError_t launch_copy_check(float *dst, const float *src, int64_t n, unsigned *status,
                              hipStream_t s);
 hipError_t launch_check_finite(const float *x, int64_t n, unsigned *status, hipStream_t s);
+// The NF4 codebook (QLoRA's 4-bit NormalFloat): 16 levels in [-1, 1], ascending,
+// 0 at index 7; normal quantiles at evenly spaced probabilities, 7 below zero and
+// 8 above, the outermost at 1 - (1/32 + 1/30)/2, scaled by the largest.  A value
+// x = w / absmax takes the nearest level: the count of midpoints
+// fl32(L[j] + L[j+1]) / 2 below x (a value on a midpoint takes the lower level).
+constexpr float kNF4[16] = {
+    -0x1p+0f,          -0x1.647362p-1f, -0x1.0cd65cp-1f, -0x1.94653cp-2f,
+    -0x1.234496p-2f,   -0x1.7a6a7ap-3f, -0x1.74f0d2p-4f, 0.0f,
+    0x1.45f602p-4f,    0x1.4995bep-3f,  0x1.f809b4p-3f,  0x1.5a066cp-2f,
+    0x1.c3496ap-2f,    0x1.200f52p-1f,  0x1.722760p-1f,  0x1p+0f};
+// Quantiser modes (bit set): scales fixed before the sweep from the original
+// weights; the NF4 codebook (scale absmax, unsigned level index per nibble).
+enum : int { MODE_STATIC = 1, MODE_NF4 = 2 };
+
+// Sweep of one lazy block.  With MODE_STATIC the scales are read from `scales`
+// (written beforehand for every row and group), not computed and stored.
 hipError_t launch_sweep_block(float *Wk, float *ET, uint8_t *codes, float *scales,
-                              const float *U, int64_t N, int64_t K, int64_t G, int64_t b0,
+                              const float *U, int64_t N, int64_t K, int64_t G, int64_t b0, int mode,
                               hipStream_t s);
-// Round-to-nearest codes and scales of W on the sweep's int4 grid (gptq.hip).
-// With partials set, also qerr's partial sums (as launch_qerr's, *nparts pairs,
-// at most rtn_partials(N, K)), ready for launch_qerr_reduce.
+// Round-to-nearest codes and scales of W on the sweep's grid (gptq.hip): the
+// uniform int4 grid, or NF4 with MODE_NF4 in mode.  With partials set, also
+// qerr's partial sums (as launch_qerr's, *nparts pairs, at most
+// rtn_partials(N, K)), ready for launch_qerr_reduce.
 int64_t rtn_partials(int64_t N, int64_t K);
 hipError_t launch_rtn(const float *W, uint8_t *codes, float *scales, const float *imp, double *partials, int64_t N,
-                      int64_t K, int64_t G, unsigned *status, hipStream_t s, int64_t *nparts);
+                      int64_t K, int64_t G, int mode, unsigned *status, hipStream_t s, int64_t *nparts);
 hipError_t launch_qerr(double *partials, const float *W, const uint8_t *codes,
-                       const float *scales, const float *imp, int64_t N, int64_t K, int64_t G,
+                       const float *scales, const float *imp, int64_t N, int64_t K, int64_t G, int mode,
                        hipStream_t s);
 hipError_t launch_qerr_reduce(double *out2, const double *partials, int64_t nparts,
                               hipStream_t s);

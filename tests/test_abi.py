@@ -55,3 +55,12 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(gq, "_lib", None)
     with pytest.raises(RuntimeError, match="missing"):
         gq.lib()
+
+
+@pytest.mark.skipif(not os.path.exists(gq.LIB_PATH), reason="libgq.so not built")
+def test_nf4_table_is_the_oracles(orc):
+    """The library's NF4 levels (literals in its source) are the oracle's (built
+    from scipy's normal quantile function), bit for bit; host-only call."""
+    import numpy as np
+    lib_levels = gq.nf4_levels().numpy()
+    assert np.array_equal(lib_levels.view(np.uint32), orc.nf4_levels().view(np.uint32))

@@ -129,7 +129,16 @@ def test_attn_projection_matches_eigendecomposition(gq, attn):
     assert rel < 2e-7
 
 
-def test_attn_gptq_full(gq, orc, attn):
+@pytest.fixture(scope="module")
+def attn_U(orc, attn):
+    """The oracle's U of the projected K=5120 Hessian (computed once)."""
+    wl, X, W, H, blob, Hs, P = attn
+    st, U, mu = orc.gptq_U(P.cpu().numpy(), wl.damp)
+    assert st == orc.OK
+    return U
+
+
+def test_attn_gptq_full(gq, orc, attn, attn_U):
     """All 10240 rows: codes, scales and qerr against the oracle run on the same
     projected Hessian, with the stored diagonal as importance."""
     wl, X, W, H, blob, Hs, P = attn
@@ -139,9 +148,8 @@ def test_attn_gptq_full(gq, orc, attn):
     scales = torch.empty(N, K // G, dtype=torch.float32, device=DEV)
     q = gq.gptq_quantize(codes, scales, W.to(DEV), P, imp, G, wl.damp,
                          gq.workspace(gq.gptq_quantize_workspace_size(N, K, G), DEV))
-    Pn, Wn, impn = P.cpu().numpy(), W.numpy(), imp.cpu().numpy().copy()
-    st, U, mu = orc.gptq_U(Pn, wl.damp)
-    assert st == orc.OK
+    Wn, impn = W.numpy(), imp.cpu().numpy().copy()
+    U = attn_U
     cg = orc.unpack_codes(codes.cpu().numpy(), K)
     sg = scales.cpu().numpy()
     oc, os_ = orc.gptq_sweep(Wn, U, G)
@@ -152,6 +160,41 @@ def test_attn_gptq_full(gq, orc, attn):
     assert ident >= 0.999
     qo = orc.qerr(oc, os_, Wn, impn)
     assert abs(q - qo) / qo < 1e-4
+
+
+@pytest.mark.parametrize("flags", [1, 2, 3])
+def test_attn_gptq_variants(gq, orc, attn, attn_U, flags):
+    """The variants (static groups, NF4, both) at full size: 96 sampled rows
+    against the oracle's sweep and replay under the same U, static scales against
+    round to nearest bit for bit, and the device's qerr against the oracle's qerr
+    of the device's own codes over all 10240 rows.  Every decision must be
+    admissible and at least 99.9% of them identical given the same history (the
+    replay); the raw identity against the oracle's own trajectory is held to 99%
+    under NF4 with dynamic scales, where each tie flip (about one per 160000
+    decisions) is followed by a few hundred differing codes further along its row
+    (the plain grid: under two hundred)."""
+    wl, X, W, H, blob, Hs, P = attn
+    N, K, G = wl.N[0], wl.K, wl.group
+    imp = blob[: 4 * K].view(torch.float32)
+    codes = torch.empty(N, K // 2, dtype=torch.uint8, device=DEV)
+    scales = torch.empty(N, K // G, dtype=torch.float32, device=DEV)
+    q = gq.gptq_quantize_ex(codes, scales, W.to(DEV), P, imp, G, wl.damp, flags,
+                            gq.workspace(gq.gptq_quantize_workspace_size(N, K, G), DEV))
+    Wn, impn = W.numpy(), imp.cpu().numpy().copy()
+    call = orc.unpack_codes(codes.cpu().numpy(), K, flags=flags)
+    sall = scales.cpu().numpy()
+    rows = np.sort(np.random.default_rng(flags).choice(N, 96, replace=False))
+    rep = orc.gptq_replay(call[rows], sall[rows], Wn, attn_U, G, rows=rows, flags=flags)
+    oc, os_ = orc.gptq_sweep(Wn, attn_U, G, rows=rows, flags=flags)
+    ident = float((call[rows] == oc).mean())
+    print(f"K=5120 flags {flags}: code identity {ident:.6f} on 96 rows, replay {rep}, qerr {q:.5f}")
+    assert rep["inadmissible"] == 0 and rep["scale_mismatch"] == 0
+    assert rep["exact"] >= 0.999 * call[rows].size
+    assert ident >= (0.999 if flags == orc.STATIC_GROUPS else 0.99)
+    if flags & orc.STATIC_GROUPS:
+        _, rs = orc.rtn(Wn, G, flags=flags & orc.NF4)
+        assert np.array_equal(sall, rs)
+    assert q == pytest.approx(orc.qerr(call, sall, Wn, impn, flags=flags), rel=1e-6)
 
 
 def test_attn_raw_stored_hessian_needs_projection(gq, orc, attn):
