@@ -98,6 +98,9 @@ def _load(path):
         "orc_qerr_ex": (D, [P, P, P, P, I64, I64, I64, P, P]),
         "orc_gptq_ex": (I, [P, P, P, P, P, P, I64, I64, I64, D, I, P]),
         "orc_gptq_replay_ex": (None, [P, P, P, P, P, P, I64, I64, P, I64, D, D, I, P]),
+        "orc_gptq_sweep_gx": (None, [P, P, P, P, I64, I64, P, I64, I, P, P]),
+        "orc_gptq_replay_gx": (None, [P, P, P, P, P, P, I64, I64, P, I64, D, D, I, P, P]),
+        "orc_act_order_perm": (None, [P, P, I64]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -250,6 +253,7 @@ def gptq_U(H, damp: float = 0.01):
 # before the sweep; the NF4 codebook instead of the uniform int4 grid.
 STATIC_GROUPS = 1
 NF4 = 2
+ACT_ORDER = 4          # with STATIC_GROUPS: columns by decreasing diag(H) (gq_oracle.c)
 
 _NF4 = None
 
@@ -276,17 +280,29 @@ def _book(flags):
     return nf4_levels() if flags & NF4 else None
 
 
-def gptq_sweep(W, U, G: int, rows=None, flags: int = 0):
+def act_order_perm(H):
+    """perm[a] = the column with the a-th largest diagonal entry of H (fp32),
+    equal entries in increasing column order."""
+    H = _np(H, np.float32)
+    K = H.shape[0]
+    perm = np.zeros(K, np.int64)
+    lib().orc_act_order_perm(_p(perm), _p(H), K)
+    return perm
+
+
+def gptq_sweep(W, U, G: int, rows=None, flags: int = 0, gidx=None):
     """Codes (len(rows) x K int8: signed int4, or NF4 level indices) and scales of
-    the GPTQ sweep of W's rows under U."""
+    the GPTQ sweep of W's rows under U.  gidx (static groups only): the group of
+    each column in this order, when not contiguous (act order)."""
     W = _np(W, np.float32)
     U = _c(U, np.float64)
     N, K = W.shape
     rows = np.arange(N, dtype=np.int64) if rows is None else _c(rows, np.int64)
     codes = np.zeros((len(rows), K), np.int8)
     scales = np.zeros((len(rows), K // G), np.float32)
-    lib().orc_gptq_sweep_ex(_p(codes), _p(scales), _p(W), _p(U), K, G, _p(rows), len(rows), flags,
-                            _p(_book(flags)))
+    gidx = None if gidx is None else _c(gidx, np.int64)
+    lib().orc_gptq_sweep_gx(_p(codes), _p(scales), _p(W), _p(U), K, G, _p(rows), len(rows), flags,
+                            _p(_book(flags)), _p(gidx))
     return codes, scales
 
 
@@ -346,7 +362,7 @@ def gptq(W, H, G: int, damp: float = 0.01, imp=None, want_qerr: bool = True, fla
 
 
 def gptq_replay(cand_codes, cand_scales, W, U, G: int, rows=None, delta: float = 1e-3,
-                scale_tol: float = 1e-5, flags: int = 0):
+                scale_tol: float = 1e-5, flags: int = 0, gidx=None):
     """Admissibility of candidate codes/scales for W's listed rows (see gq_oracle.c)."""
     W = _np(W, np.float32)
     U = _c(U, np.float64)
@@ -357,8 +373,9 @@ def gptq_replay(cand_codes, cand_scales, W, U, G: int, rows=None, delta: float =
     assert cc.shape == (len(rows), K) and cs.shape == (len(rows), K // G)
     stats = np.zeros(4, np.int64)
     mrel = ctypes.c_double(0.0)
-    lib().orc_gptq_replay_ex(_p(stats), ctypes.byref(mrel), _p(cc), _p(cs), _p(W), _p(U), K, G,
-                             _p(rows), len(rows), delta, scale_tol, flags, _p(_book(flags)))
+    gidx = None if gidx is None else _c(gidx, np.int64)
+    lib().orc_gptq_replay_gx(_p(stats), ctypes.byref(mrel), _p(cc), _p(cs), _p(W), _p(U), K, G,
+                             _p(rows), len(rows), delta, scale_tol, flags, _p(_book(flags)), _p(gidx))
     return {"exact": int(stats[0]), "tie_flips": int(stats[1]), "inadmissible": int(stats[2]),
             "scale_mismatch": int(stats[3]), "max_scale_rel": mrel.value}
 

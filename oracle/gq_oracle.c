@@ -577,6 +577,10 @@ static float group_scale(double amax) { return (float)amax / 7.0f; }
  * wiki's qerr section) instead of the uniform int4 grid. */
 #define ORC_STATIC_GROUPS 1
 #define ORC_NF4 2
+/* ORC_ACT_ORDER (with ORC_STATIC_GROUPS only): columns are quantised in order of
+ * decreasing diag(H) (AutoGPTQ's desc_act), each with its original group's
+ * static scale; codes come back in the original column order. */
+#define ORC_ACT_ORDER 4
 
 /* Scale on the chosen grid: absmax/7 for the uniform grid; absmax itself for a
  * codebook, whose levels span [-1, 1]. */
@@ -641,28 +645,50 @@ static double group_amax_f32(const float *w, int64_t i, int64_t G)
  *   w_j -= e * U[i][j] for every later column j.
  * codes: nrows x K (one code per byte: signed int4, or the NF4 level index),
  * scales: nrows x K/G. */
-void orc_gptq_sweep_ex(int8_t *codes, float *scales, const float *W, const double *U,
+/* Static scales of one row: stab[g] = the grid's scale of the absolute maximum
+ * of the original values w0[k] over the columns k of group g (gidx[k] == g, or
+ * k / G when gidx is NULL). */
+static void static_scales(float *stab, const float *w0, int64_t K, int64_t G, const int64_t *gidx,
+                          const float *book)
+{
+    double *amax = (double *)calloc((size_t)(K / G), sizeof(double));
+    for (int64_t k = 0; k < K; k++) {
+        int64_t g = gidx ? gidx[k] : k / G;
+        amax[g] = fmax(amax[g], fabs((double)w0[k]));
+    }
+    for (int64_t g = 0; g < K / G; g++) stab[g] = grid_scale(amax[g], book);
+    free(amax);
+}
+
+/* The sweep, with an optional group map for static groups: column i takes the
+ * static scale of group gidx[i] (the act-order permutation's original groups);
+ * gidx NULL means contiguous groups, i / G. */
+void orc_gptq_sweep_gx(int8_t *codes, float *scales, const float *W, const double *U,
                        int64_t K, int64_t G, const int64_t *rows, int64_t nrows, int flags,
-                       const float *book)
+                       const float *book, const int64_t *gidx)
 {
     const int stat = (flags & ORC_STATIC_GROUPS) != 0;
     if (!(flags & ORC_NF4)) book = NULL;
+    if (!stat) gidx = NULL;
 #pragma omp parallel for schedule(dynamic, 1)
     for (int64_t r = 0; r < nrows; r++) {
         const float *w0 = W + rows[r] * K;
         double *wk = (double *)malloc((size_t)K * sizeof(double));
         for (int64_t k = 0; k < K; k++) wk[k] = (double)w0[k];
+        float *srow = scales + r * (K / G);
+        if (stat) static_scales(srow, w0, K, G, gidx, book);
         float s = 0.0f;
         for (int64_t i = 0; i < K; i++) {
-            if (i % G == 0) {
+            if (stat) {
+                s = srow[gidx ? gidx[i] : i / G];
+            } else if (i % G == 0) {
                 double amax = 0.0;
                 for (int64_t k = i; k < i + G; k++) amax = fmax(amax, fabs(wk[k]));
-                if (stat) amax = group_amax_f32(w0, i, G);
 #if ORC_MUTANT == 3
                 amax = group_amax_f32(w0, i, G);   /* mutant: static scales in the default sweep */
 #endif
                 s = grid_scale(amax, book);
-                scales[r * (K / G) + i / G] = s;
+                srow[i / G] = s;
             }
             int c = grid_code(wk[i], s, book);
             codes[r * K + i] = (int8_t)c;
@@ -675,6 +701,13 @@ void orc_gptq_sweep_ex(int8_t *codes, float *scales, const float *W, const doubl
         }
         free(wk);
     }
+}
+
+void orc_gptq_sweep_ex(int8_t *codes, float *scales, const float *W, const double *U,
+                       int64_t K, int64_t G, const int64_t *rows, int64_t nrows, int flags,
+                       const float *book)
+{
+    orc_gptq_sweep_gx(codes, scales, W, U, K, G, rows, nrows, flags, book, NULL);
 }
 
 void orc_gptq_sweep(int8_t *codes, float *scales, const float *W, const double *U,
@@ -757,26 +790,81 @@ void orc_unpack_codes(int8_t *codes, const uint8_t *packed, int64_t N, int64_t K
         }
 }
 
+/* Act-order permutation: perm[a] = the column with the a-th largest diagonal
+ * entry of H (fp32 values of the stored diagonal), equal entries in increasing
+ * column order (a stable sort), so the result is unique. */
+static const float *g_perm_diag;
+static int cmp_desc_diag(const void *pa, const void *pb)
+{
+    int64_t a = *(const int64_t *)pa, b = *(const int64_t *)pb;
+    float da = g_perm_diag[a], db = g_perm_diag[b];
+    if (da > db) return -1;
+    if (da < db) return 1;
+    return (a > b) - (a < b);
+}
+
+void orc_act_order_perm(int64_t *perm, const float *H, int64_t K)
+{
+    float *d = (float *)malloc((size_t)K * sizeof(float));
+    for (int64_t i = 0; i < K; i++) { d[i] = H[i * K + i]; perm[i] = i; }
+    g_perm_diag = d;
+    qsort(perm, (size_t)K, sizeof(int64_t), cmp_desc_diag);
+    free(d);
+}
+
 /* Full GPTQ of W (N x K) under H: codes (N x K, one per byte), scales, qerr.
  * imp NULL => 1, qerr_out NULL => not computed; flags and book as for
- * orc_gptq_sweep_ex. */
+ * orc_gptq_sweep_ex.  With ORC_ACT_ORDER (and ORC_STATIC_GROUPS) the columns of W
+ * and the rows and columns of H are permuted by orc_act_order_perm, U is formed
+ * from the permuted H, the sweep runs in that order with each column's original
+ * group's static scale, and the codes are put back in the original order. */
 int orc_gptq_ex(int8_t *codes, float *scales, double *qerr_out, const float *W, const float *H,
                 const float *imp, int64_t N, int64_t K, int64_t G, double damp, int flags,
                 const float *book)
 {
     if (!(flags & ORC_NF4)) book = NULL;
     if ((flags & ORC_NF4) && !book) return ORC_ERR_INVALID_ARG;
+    if ((flags & ORC_ACT_ORDER) && !(flags & ORC_STATIC_GROUPS)) return ORC_ERR_INVALID_ARG;
+    for (int64_t i = 0; i < K; i++)
+        for (int64_t j = 0; j <= i; j++)
+            if (!isfinite(H[i * K + j])) return ORC_ERR_NONFINITE;
     if (N < 1 || K < 2 || (K & 1) || G < 1 || K % G != 0) return ORC_ERR_INVALID_ARG;
     if (!all_finite_f32(W, N * K)) return ORC_ERR_NONFINITE;
     if (imp && !all_finite_f32(imp, K)) return ORC_ERR_NONFINITE;
     double *U = (double *)malloc((size_t)(K * K) * sizeof(double));
-    int st = orc_gptq_U(U, H, K, damp, NULL);
-    if (st != ORC_OK) { free(U); return st; }
     int64_t *rows = (int64_t *)malloc((size_t)N * sizeof(int64_t));
     for (int64_t n = 0; n < N; n++) rows[n] = n;
-    orc_gptq_sweep_ex(codes, scales, W, U, K, G, rows, N, flags, book);
+    int st;
+    if (flags & ORC_ACT_ORDER) {
+        int64_t *perm = (int64_t *)malloc((size_t)K * sizeof(int64_t));
+        int64_t *gidx = (int64_t *)malloc((size_t)K * sizeof(int64_t));
+        float *Hp = (float *)malloc((size_t)(K * K) * sizeof(float));
+        float *Wp = (float *)malloc((size_t)(N * K) * sizeof(float));
+        int8_t *cp = (int8_t *)malloc((size_t)(N * K));
+        orc_act_order_perm(perm, H, K);     /* H is finite here (checked above) */
+        /* Hp[a][b] = H[perm[a]][perm[b]], read from H's lower triangle */
+        for (int64_t a = 0; a < K; a++)
+            for (int64_t b = 0; b < K; b++) {
+                int64_t i = perm[a], j = perm[b];
+                Hp[a * K + b] = i >= j ? H[i * K + j] : H[j * K + i];
+            }
+        for (int64_t n = 0; n < N; n++)
+            for (int64_t a = 0; a < K; a++) Wp[n * K + a] = W[n * K + perm[a]];
+        for (int64_t a = 0; a < K; a++) gidx[a] = perm[a] / G;
+        st = orc_gptq_U(U, Hp, K, damp, NULL);
+        if (st == ORC_OK) {
+            orc_gptq_sweep_gx(cp, scales, Wp, U, K, G, rows, N, flags, book, gidx);
+            for (int64_t n = 0; n < N; n++)
+                for (int64_t a = 0; a < K; a++) codes[n * K + perm[a]] = cp[n * K + a];
+        }
+        free(perm); free(gidx); free(Hp); free(Wp); free(cp);
+    } else {
+        st = orc_gptq_U(U, H, K, damp, NULL);
+        if (st == ORC_OK) orc_gptq_sweep_ex(codes, scales, W, U, K, G, rows, N, flags, book);
+    }
     free(rows);
     free(U);
+    if (st != ORC_OK) return st;
     if (qerr_out) *qerr_out = orc_qerr_ex(codes, scales, W, imp, N, K, G, book, NULL);
     return ORC_OK;
 }
@@ -803,26 +891,48 @@ int orc_gptq(int8_t *codes, float *scales, double *qerr_out, const float *W, con
  * scale), so a tie flip's downstream effect is not counted again.  max_rel[0]
  * gets the largest relative scale difference.  flags and book as for
  * orc_gptq_sweep_ex. */
-void orc_gptq_replay_ex(int64_t *stats, double *max_rel, const int8_t *cand_codes,
+void orc_gptq_replay_gx(int64_t *stats, double *max_rel, const int8_t *cand_codes,
                         const float *cand_scales, const float *W, const double *U,
                         int64_t K, int64_t G, const int64_t *rows, int64_t nrows,
-                        double delta, double scale_tol, int flags, const float *book)
+                        double delta, double scale_tol, int flags, const float *book,
+                        const int64_t *gidx)
 {
     const int stat = (flags & ORC_STATIC_GROUPS) != 0;
     if (!(flags & ORC_NF4)) book = NULL;
+    if (!stat) gidx = NULL;
     int64_t exact = 0, flips = 0, bad = 0, smis = 0;
     double mrel = 0.0;
+    /* first[i]: column i is the first of its group in this order */
+    char *first = (char *)calloc((size_t)K, 1);
+    char *seen = (char *)calloc((size_t)(K / G), 1);
+    for (int64_t i = 0; i < K; i++) {
+        const int64_t gi = gidx ? gidx[i] : i / G;
+        if (!seen[gi]) { seen[gi] = 1; first[i] = 1; }
+    }
+    free(seen);
 #pragma omp parallel for schedule(dynamic, 1) reduction(+ : exact, flips, bad, smis) reduction(max : mrel)
     for (int64_t r = 0; r < nrows; r++) {
         const float *w0 = W + rows[r] * K;
         double *wk = (double *)malloc((size_t)K * sizeof(double));
         for (int64_t k = 0; k < K; k++) wk[k] = (double)w0[k];
         float s_ref = 0.0f, s_c = 0.0f;
+        float *stab = (float *)malloc((size_t)(K / G) * sizeof(float));
+        if (stat) static_scales(stab, w0, K, G, gidx, book);
         for (int64_t i = 0; i < K; i++) {
-            if (i % G == 0) {
+            const int64_t gi = gidx ? gidx[i] : i / G;
+            if (stat) {
+                s_ref = stab[gi];
+                s_c = cand_scales[r * (K / G) + gi];
+                if (first[i]) {         /* each group's scale is compared once */
+                    double den = fabs((double)s_ref) > 0.0 ? fabs((double)s_ref) : 1e-30;
+                    double rel = fabs((double)s_c - (double)s_ref) / den;
+                    if (s_ref == 0.0f && s_c == 0.0f) rel = 0.0;
+                    if (rel > mrel) mrel = rel;
+                    if (rel > scale_tol) smis++;
+                }
+            } else if (i % G == 0) {
                 double amax = 0.0;
                 for (int64_t k = i; k < i + G; k++) amax = fmax(amax, fabs(wk[k]));
-                if (stat) amax = group_amax_f32(w0, i, G);
                 s_ref = grid_scale(amax, book);
                 s_c = cand_scales[r * (K / G) + i / G];
                 double den = fabs((double)s_ref) > 0.0 ? fabs((double)s_ref) : 1e-30;
@@ -858,13 +968,24 @@ void orc_gptq_replay_ex(int64_t *stats, double *max_rel, const int8_t *cand_code
             const double *ui = U + i * K;
             for (int64_t j = i + 1; j < K; j++) wk[j] -= e * ui[j];
         }
+        free(stab);
         free(wk);
     }
+    free(first);
     stats[0] = exact;
     stats[1] = flips;
     stats[2] = bad;
     stats[3] = smis;
     *max_rel = mrel;
+}
+
+void orc_gptq_replay_ex(int64_t *stats, double *max_rel, const int8_t *cand_codes,
+                        const float *cand_scales, const float *W, const double *U,
+                        int64_t K, int64_t G, const int64_t *rows, int64_t nrows,
+                        double delta, double scale_tol, int flags, const float *book)
+{
+    orc_gptq_replay_gx(stats, max_rel, cand_codes, cand_scales, W, U, K, G, rows, nrows, delta, scale_tol,
+                       flags, book, NULL);
 }
 
 void orc_gptq_replay(int64_t *stats, double *max_rel, const int8_t *cand_codes,

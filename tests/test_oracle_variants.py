@@ -11,7 +11,11 @@ What fixes them from outside the oracle:
   - static groups: scales equal to the round-to-nearest scales bit for bit, and
     a diagonal Hessian reducing every variant to round-to-nearest;
   - an independent OBQ recursion (freshly inverted Hessians of the columns not yet
-    quantised) carrying each variant's scale rule and grid.
+    quantised) carrying each variant's scale rule and grid;
+  - act order (AutoGPTQ's desc_act, with static groups): the permutation against
+    numpy's stable argsort, the OBQ recursion run in that column order with each
+    column's original group's scale, and the identity permutation when the
+    diagonal already decreases.
 """
 import json
 import math
@@ -217,3 +221,112 @@ def test_nf4_pack_roundtrip(orc):
     packed = orc.pack_codes(codes)
     assert np.array_equal(orc.unpack_codes(packed, 64, flags=orc.NF4), codes)
     assert np.array_equal(packed[:, 0] & 0xF, codes[:, 0].astype(np.uint8))
+
+
+# ------------------------------------------------------------------ act order
+def _obq_order(W, H, G, damp, perm, book=None):
+    """OBQ (freshly inverted Hessians of the remaining columns) taking the columns
+    in the order perm, each with the static scale of its original contiguous group
+    (absmax of the original weights; /7 on the uniform grid); codes returned in
+    the original column order."""
+    W0 = W.astype(np.float64)
+    N, K = W.shape
+    Hs = H.astype(np.float64)
+    Hd = Hs + damp * np.trace(Hs) / K * np.eye(K)
+    Hp = Hd[np.ix_(perm, perm)]
+    Wp = W0[:, perm].copy()
+    Lb = None if book is None else np.asarray(book, np.float64)
+    amax = np.abs(W0).reshape(N, -1, G).max(-1).astype(np.float32)
+    stab = amax if Lb is not None else (amax / np.float32(7)).astype(np.float32)
+    cp = np.zeros((N, K), np.int8)
+    for a in range(K):
+        Finv = np.linalg.inv(Hp[a:, a:])
+        s = stab[:, perm[a] // G]
+        v = np.where(s > 0, Wp[:, a].astype(np.float32) / np.where(s > 0, s, 1), 0).astype(np.float32)
+        if Lb is None:
+            c = np.clip(np.rint(v), -8, 7)
+            q = c * s.astype(np.float64)
+        else:
+            c = np.abs(v.astype(np.float64)[:, None] - Lb).argmin(1)
+            q = Lb[c] * s.astype(np.float64)
+        cp[:, a] = c
+        err = (Wp[:, a] - q) / Finv[0, 0]
+        Wp[:, a:] -= np.outer(err, Finv[0, :])
+    codes = np.zeros_like(cp)
+    codes[:, perm] = cp
+    return codes, stab
+
+
+def test_act_order_permutation(orc):
+    rng = np.random.default_rng(21)
+    K = 40
+    X = (rng.standard_normal((100, K)) * rng.uniform(0.2, 3.0, K)).astype(np.float32)
+    H = _gram32(orc, X)
+    H[5, 5] = H[9, 9] = H[30, 30] = H[2, 2]                   # ties, kept in column order
+    perm = orc.act_order_perm(H)
+    assert np.array_equal(perm, np.argsort(-np.diag(H), kind="stable"))
+    d = np.diag(H)[perm]
+    assert np.all(d[:-1] >= d[1:])
+
+
+@pytest.mark.parametrize("book_flag", [0, 2])
+def test_act_order_equals_obq_in_that_order(orc, book_flag):
+    rng = np.random.default_rng(13)
+    N, K, G = 20, 48, 16
+    X = (rng.standard_normal((160, 12)) @ rng.standard_normal((12, K)) +
+         0.3 * rng.standard_normal((160, K))).astype(np.float32)
+    X *= rng.uniform(0.3, 3.0, K).astype(np.float32)            # a spread of channel energies
+    H = _gram32(orc, X)
+    W = rng.uniform(-1, 1, (N, K)).astype(np.float32)
+    flags = orc.STATIC_GROUPS | orc.ACT_ORDER | book_flag
+    st, codes, scales, _ = orc.gptq(W, H, G, 0.01, want_qerr=False, flags=flags)
+    assert st == orc.OK
+    perm = np.argsort(-np.diag(H), kind="stable")
+    assert not np.array_equal(perm, np.arange(K))
+    rc, rs = _obq_order(W, H, G, 0.01, perm, orc.nf4_levels() if book_flag else None)
+    assert np.array_equal(codes, rc)
+    assert np.array_equal(scales, rs)
+    # and it differs from the natural order
+    _, c0, _, _ = orc.gptq(W, H, G, 0.01, want_qerr=False, flags=orc.STATIC_GROUPS | book_flag)
+    assert not np.array_equal(codes, c0)
+
+
+def test_act_order_with_sorted_diagonal_is_static(orc):
+    """A Hessian whose diagonal already decreases gives the identity permutation,
+    so act order changes nothing."""
+    rng = np.random.default_rng(14)
+    K, G = 64, 16
+    C = orc.gram(rng.standard_normal((200, K)).astype(np.float32))
+    C = C / np.sqrt(np.outer(np.diag(C), np.diag(C)))          # unit diagonal
+    D = np.linspace(3.0, 0.5, K)
+    H = (D[:, None] * C * D[None, :]).astype(np.float32)       # diagonal D^2, decreasing
+    assert np.all(np.diff(np.diag(H)) < 0)
+    W = rng.uniform(-1, 1, (12, K)).astype(np.float32)
+    for book_flag in (0, orc.NF4):
+        a = orc.gptq(W, H, G, 0.01, flags=orc.STATIC_GROUPS | orc.ACT_ORDER | book_flag)
+        b = orc.gptq(W, H, G, 0.01, flags=orc.STATIC_GROUPS | book_flag)
+        assert a[0] == b[0] == orc.OK
+        assert np.array_equal(a[1], b[1]) and np.array_equal(a[2], b[2]) and a[3] == b[3]
+
+
+def test_act_order_needs_static_groups(orc):
+    W = np.ones((2, 8), np.float32)
+    H = np.eye(8, dtype=np.float32)
+    st, *_ = orc.gptq(W, H, 4, 0.01, flags=orc.ACT_ORDER)
+    assert st == orc.ERR_INVALID_ARG
+
+
+def test_replay_with_group_map(orc):
+    """The replay on the permuted problem (W and H permuted, each column's original
+    group as its group) accepts act order's codes put in that order."""
+    wl = g.WORKLOADS["tiny"]
+    W = g.weights(wl).numpy()[:24]
+    H = _gram32(orc, g.x_chunk(wl))
+    G = wl.group
+    flags = orc.STATIC_GROUPS | orc.ACT_ORDER
+    st, codes, scales, _ = orc.gptq(W, H, G, 0.01, want_qerr=False, flags=flags)
+    perm = orc.act_order_perm(H)
+    Hp = H[np.ix_(perm, perm)]
+    st, Up, _ = orc.gptq_U(Hp, 0.01)
+    rep = orc.gptq_replay(codes[:, perm], scales, W[:, perm], Up, G, flags=orc.STATIC_GROUPS, gidx=perm // G)
+    assert rep["exact"] == codes.size and rep["scale_mismatch"] == 0
