@@ -41,8 +41,8 @@ SWEEP_BLOCK = 128          # lazy-batch width of gptq_sweep (include/gq.h)
 # Valid only for the kernel sources they were taken on: any change to those
 # files makes the figure stale and it is reported as null.
 TRAFFIC = {
-    "attn5120": {"fetch_bytes": 1077887.3658536586 * 1.99975 * 1024, "write_bytes": 188160.0 * 1.00000 * 1024,
-                 "sources_sha256_16": "b4ffe360e44d515c"},
+    "attn5120": {"fetch_bytes": 1070706.655487805 * 1.99970 * 1024, "write_bytes": 188160.0 * 1.00000 * 1024,
+                 "sources_sha256_16": "b513380d64ea1a4d"},
 }
 TRAFFIC_SOURCES = ("post_weight_quantization_accumulate_amd/csrc/ozaki.hip",
                    "post_weight_quantization_accumulate_amd/csrc/gq_internal.h")
@@ -246,7 +246,7 @@ def main():
     out["rtn"] = rtn_measure(gq, torch, W, imp, G, dev)
     out["hfqm"] = hfqm_measure(gq, blob, imp, K)
     out["hadamard"] = hadamard_measure(gq, torch, W, Hs, dev)
-    out["variants"] = variants_measure(gq, torch, W, U, imp, G, dev)
+    out["variants"] = variants_measure(gq, torch, W, U, Hs, imp, G, damp, dev)
     out["rtn"]["qerr_gptq_over_rtn"] = qerr[0] / out["rtn"]["qerr"] if out["rtn"]["qerr"] else None
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, X, W)
@@ -281,11 +281,14 @@ def hadamard_measure(gq, torch, W, H, dev, block=1024, reps=10):
     return res
 
 
-def variants_measure(gq, torch, W, U, imp, G, dev, reps=3):
+def variants_measure(gq, torch, W, U, H, imp, G, damp, dev, reps=3):
     """The sweep's variants under the step's U (static groups, the NF4 codebook,
     both; "plain" is gptq_sweep_ex with no flag, the step's own sweep) and NF4
     round to nearest, each timed per API call with HIP events after the steps,
-    with its qerr (same importance)."""
+    with its qerr (same importance).  Act order needs the factor of the permuted
+    Hessian, so it is timed as a whole gptq_quantize_ex call (permutation, permuted
+    H, factor, permuted sweep, codes put back) beside the same call with static
+    groups alone."""
     N, K = W.shape
     codes = torch.empty(N * (K // 2), dtype=torch.uint8, device=dev)
     scales = torch.empty(N * (K // G), dtype=torch.float32, device=dev)
@@ -297,6 +300,11 @@ def variants_measure(gq, torch, W, U, imp, G, dev, reps=3):
              for name, f in (("plain", 0), ("static", gq.GQ_STATIC_GROUPS), ("nf4", gq.GQ_NF4),
                              ("static_nf4", gq.GQ_STATIC_GROUPS | gq.GQ_NF4))]
     calls.append(("rtn_nf4", lambda: gq.rtn_quantize_ex(codes, scales, W, imp, G, gq.GQ_NF4, ws_r)))
+    act = gq.GQ_STATIC_GROUPS | gq.GQ_ACT_ORDER
+    ws_q = gq.workspace(gq.gptq_quantize_ex_workspace_size(N, K, G, act), dev)
+    for name, f in (("quantize_static", gq.GQ_STATIC_GROUPS), ("quantize_static_act", act)):
+        calls.append((name, lambda f=f: gq.gptq_quantize_ex(codes, scales, W, H, imp, G, damp, f, ws_q)))
+    res["quantize_ms"] = {}
     for name, fn in calls:
         q = fn()
         torch.cuda.synchronize()
@@ -307,6 +315,8 @@ def variants_measure(gq, torch, W, U, imp, G, dev, reps=3):
         torch.cuda.synchronize()
         if name == "rtn_nf4":
             res["rtn_nf4_ms"] = a.elapsed_time(b) / reps
+        elif name.startswith("quantize_"):
+            res["quantize_ms"][name[len("quantize_"):]] = a.elapsed_time(b) / reps
         else:
             res["sweep_ms"][name] = a.elapsed_time(b) / reps
         res["qerr"][name] = q

@@ -232,11 +232,17 @@ int gptq_quantize(uint8_t *codes, float *scales, double *qerr_out, const float *
  *                     (a value on the midpoint of two levels takes the lower),
  *                     w ~ level[code] * scale; an all-zero group takes code 7
  *                     (level 0.0).  gq_nf4_levels gives the table.
+ *   GQ_ACT_ORDER      (gptq_quantize_ex only, with GQ_STATIC_GROUPS) columns are
+ *                     quantised in order of decreasing diag(H) (AutoGPTQ's
+ *                     desc_act; equal entries in column order): H is permuted on
+ *                     both sides and factored, and each column keeps its original
+ *                     contiguous group's static scale, so codes and scales come
+ *                     back in the ordinary layout (original column order).
  * Other bits are GQ_ERR_INVALID_ARG.  Codes are packed two per byte as for
  * gptq_sweep (unsigned nibbles under GQ_NF4); qerr uses the dequantised value of
  * the chosen grid.
  */
-enum { GQ_STATIC_GROUPS = 1u, GQ_NF4 = 2u };
+enum { GQ_STATIC_GROUPS = 1u, GQ_NF4 = 2u, GQ_ACT_ORDER = 4u };
 
 /* The 16 NF4 levels, ascending, fp32 (QLoRA's 4-bit NormalFloat: standard normal
  * quantiles at evenly spaced probabilities, 7 below zero and 8 above, the
@@ -248,7 +254,12 @@ int gptq_sweep_ex(uint8_t *codes, float *scales, double *qerr_out, const float *
                   const float *imp, int64_t N, int64_t K, int64_t group, uint32_t flags, void *ws,
                   size_t ws_bytes, hipStream_t stream);
 
-/* gptq_quantize with flags (above); same workspace as gptq_quantize. */
+/* Workspace bytes gptq_quantize_ex needs: gptq_quantize's, plus with
+ * GQ_ACT_ORDER a permuted K x K Hessian, the permutation and permuted codes. */
+size_t gptq_quantize_ex_workspace_size(int64_t N, int64_t K, int64_t group, uint32_t flags);
+
+/* gptq_quantize with flags (above); ws at least
+ * gptq_quantize_ex_workspace_size(N, K, group, flags) bytes. */
 int gptq_quantize_ex(uint8_t *codes, float *scales, double *qerr_out, const float *W, const float *H,
                      const float *imp, int64_t N, int64_t K, int64_t group, float damp, uint32_t flags, void *ws,
                      size_t ws_bytes, hipStream_t stream);

@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(_HERE, "libgq.so")
 (GQ_OK, GQ_ERR_INVALID_ARG, GQ_ERR_NOT_PD, GQ_ERR_NONFINITE, GQ_ERR_NO_CALIBRATION, GQ_ERR_HIP, GQ_ERR_INTERNAL,
  GQ_ERR_IO) = range(8)
 GQ_HFQM_F32, GQ_HFQM_HESSIAN = 0, 130
-GQ_STATIC_GROUPS, GQ_NF4 = 1, 2
+GQ_STATIC_GROUPS, GQ_NF4, GQ_ACT_ORDER = 1, 2, 4
 GQ_F32, GQ_BF16 = 0, 1
 GQ_PSD_AUTO, GQ_PSD_F64 = 0, 1
 
@@ -31,7 +31,7 @@ EXPORTS = (
     "psd_project_flops", "psd_project_products", "gq_set_timing", "psd_project_last_timing", "gq_set_psd_products",
     "gptq_factor_workspace_size", "gptq_factor", "gptq_sweep_workspace_size", "gptq_sweep",
     "gptq_quantize_workspace_size", "gptq_quantize", "rtn_quantize_workspace_size", "rtn_quantize",
-    "gptq_sweep_ex", "gptq_quantize_ex", "rtn_quantize_ex", "gq_nf4_levels",
+    "gptq_sweep_ex", "gptq_quantize_ex", "rtn_quantize_ex", "gq_nf4_levels", "gptq_quantize_ex_workspace_size",
     "hfqm_write", "hfqm_read_header", "hfqm_read_entry", "hfqm_read_payload",
     "hadamard_rotate_rows", "hadamard_rotate_hessian_workspace_size", "hadamard_rotate_hessian",
 )
@@ -83,6 +83,7 @@ def lib() -> ctypes.CDLL:
             "gptq_sweep_ex": (I, [P, P, P, P, P, P, I64, I64, I64, U32, P, SZ, P]),
             "gptq_quantize_ex": (I, [P, P, P, P, P, P, I64, I64, I64, F, U32, P, SZ, P]),
             "gq_nf4_levels": (None, [P]),
+            "gptq_quantize_ex_workspace_size": (SZ, [I64, I64, I64, U32]),
             "hfqm_write": (I, [ctypes.c_char_p, ctypes.c_uint32, ctypes.c_char_p, I64, P, P, P, P, P, P, P]),
             "hfqm_read_header": (I, [ctypes.c_char_p, P, P, P, P, SZ, P]),
             "hfqm_read_entry": (I, [ctypes.c_char_p, I64, P, SZ, P, P, P, P, P, P]),
@@ -289,8 +290,12 @@ def gptq_quantize_workspace_size(N: int, K: int, group: int) -> int:
     return int(lib().gptq_quantize_workspace_size(N, K, group))
 
 
+def gptq_quantize_ex_workspace_size(N: int, K: int, group: int, flags: int) -> int:
+    return int(lib().gptq_quantize_ex_workspace_size(N, K, group, flags))
+
+
 def gptq_quantize_ex(codes, scales, W, H, imp, group: int, damp: float, flags: int, ws, want_qerr: bool = True):
-    """gptq_quantize with flags (GQ_STATIC_GROUPS, GQ_NF4); returns qerr (or None)."""
+    """gptq_quantize with flags (GQ_STATIC_GROUPS, GQ_NF4, GQ_ACT_ORDER); returns qerr (or None)."""
     N, K = _quant_args(codes, scales, W, H, imp, group, ws, "H")
     q = ctypes.c_double(0.0)
     _check(lib().gptq_quantize_ex(_ptr(codes), _ptr(scales), ctypes.byref(q) if want_qerr else None,

@@ -390,11 +390,23 @@ int run_factor(float *U, const float *H, int64_t K, float damp, FactorWs &w, hip
     return GQ_OK;
 }
 
+// Act order's buffers: the permutation, its inverse, each permuted column's
+// original group, and the codes in permuted column order.
+struct ActOrder {
+    int *perm, *inv, *gidx;
+    uint8_t *cperm;
+};
+
 int run_sweep(uint8_t *codes, float *scales, double *qerr_out, const float *W, const float *U,
-              const float *imp, int64_t N, int64_t K, int64_t G, int mode, SweepWs &w, hipStream_t s)
+              const float *imp, int64_t N, int64_t K, int64_t G, int mode, SweepWs &w, hipStream_t s,
+              const ActOrder *act = nullptr)
 {
     GQ_HIP(launch_fill_u32(w.sc.status, 4, 0u, s), "fill");
-    GQ_HIP(launch_copy_check(w.Wk, W, N * K, w.sc.status, s), "copy W");
+    if (act)
+        GQ_HIP(launch_gather_cols(w.Wk, W, act->perm, N, K, w.sc.status, s), "permute W");
+    else
+        GQ_HIP(launch_copy_check(w.Wk, W, N * K, w.sc.status, s), "copy W");
+    uint8_t *const sweep_codes = act ? act->cperm : codes;
     if (imp) GQ_HIP(launch_check_finite(imp, K, w.sc.status, s), "check imp");
     // static groups: every scale from the original weights, before the sweep
     // (the round-to-nearest pass writes them; its codes are overwritten below)
@@ -409,7 +421,9 @@ int run_sweep(uint8_t *codes, float *scales, double *qerr_out, const float *W, c
         for (int64_t b0 = g0; b0 < g1; b0 += kSweepBlock) {
             const int64_t bw = (g1 - b0) < kSweepBlock ? (g1 - b0) : kSweepBlock;
             float *ETb = w.ET + (b0 - g0) * N;          // this block's rows of the group's E^T
-            GQ_HIP(launch_sweep_block(w.Wk, ETb, codes, scales, U, N, K, G, b0, mode, s), "sweep block");
+            GQ_HIP(launch_sweep_block(w.Wk, ETb, sweep_codes, scales, U, N, K, G, b0, mode,
+                                      act ? act->gidx : nullptr, s),
+                   "sweep block");
             const int64_t e = b0 + bw;
             if (e < g1) {
                 GemmDesc d = gemm(ETb, N, U + b0 * K + e, K, N, g1 - e, bw, w.Wk + e, K);
@@ -427,6 +441,7 @@ int run_sweep(uint8_t *codes, float *scales, double *qerr_out, const float *W, c
             GQ_HIP(gemm_tn_f32(d, s), "group update");
         }
     }
+    if (act) GQ_HIP(launch_unpermute_codes(codes, act->cperm, act->inv, N, K, s), "unpermute codes");
     if (qerr_out) {
         GQ_HIP(launch_qerr(w.sc.partials, W, codes, scales, imp, N, K, G, mode, s), "qerr");
         GQ_HIP(launch_qerr_reduce(w.sc.d, w.sc.partials, qerr_partials(N), s), "qerr reduce");
@@ -758,6 +773,8 @@ int gptq_sweep_ex(uint8_t *codes, float *scales, double *qerr_out, const float *
     g_last_error.clear();
     int rc = check_sweep_args(codes, scales, W, U, N, K, group);
     if (rc) return rc;
+    if (flags & GQ_ACT_ORDER)
+        return fail(GQ_ERR_INVALID_ARG, "act order needs the factor of the permuted Hessian: use gptq_quantize_ex");
     if (flags & ~(uint32_t)(GQ_STATIC_GROUPS | GQ_NF4)) return fail(GQ_ERR_INVALID_ARG, "unknown flag bits");
     if (!ws) return fail(GQ_ERR_INVALID_ARG, "null workspace");
     if (ws_bytes < sweep_bytes(N, K)) return fail(GQ_ERR_INVALID_ARG, "workspace too small");
@@ -885,6 +902,21 @@ size_t gptq_quantize_workspace_size(int64_t N, int64_t K, int64_t group)
     return factor_bytes(K) + align_up((size_t)K * (size_t)K * sizeof(float)) + sweep_bytes(N, K);
 }
 
+// Workspace of gptq_quantize_ex: gptq_quantize's, plus for act order the
+// permuted H, the permutation's three int arrays and the permuted codes.
+size_t act_bytes(int64_t N, int64_t K)
+{
+    return align_up((size_t)K * (size_t)K * sizeof(float)) + 3 * align_up((size_t)K * sizeof(int)) +
+           align_up((size_t)N * (size_t)(K / 2));
+}
+
+size_t gptq_quantize_ex_workspace_size(int64_t N, int64_t K, int64_t group, uint32_t flags)
+{
+    if (N < 1 || K < 1) return 0;
+    const size_t base = gptq_quantize_workspace_size(N, K, group);
+    return (flags & GQ_ACT_ORDER) ? base + act_bytes(N, K) : base;
+}
+
 int gptq_quantize_ex(uint8_t *codes, float *scales, double *qerr_out, const float *W, const float *H,
                      const float *imp, int64_t N, int64_t K, int64_t group, float damp, uint32_t flags, void *ws,
                      size_t ws_bytes, hipStream_t stream)
@@ -892,7 +924,36 @@ int gptq_quantize_ex(uint8_t *codes, float *scales, double *qerr_out, const floa
     g_last_error.clear();
     int rc = check_sweep_args(codes, scales, W, H, N, K, group);
     if (rc) return rc;
-    if (flags & ~(uint32_t)(GQ_STATIC_GROUPS | GQ_NF4)) return fail(GQ_ERR_INVALID_ARG, "unknown flag bits");
+    if (flags & ~(uint32_t)(GQ_STATIC_GROUPS | GQ_NF4 | GQ_ACT_ORDER))
+        return fail(GQ_ERR_INVALID_ARG, "unknown flag bits");
+    if ((flags & GQ_ACT_ORDER) && !(flags & GQ_STATIC_GROUPS))
+        return fail(GQ_ERR_INVALID_ARG, "act order needs static groups (the packed layout keeps contiguous groups)");
+    if ((flags & GQ_ACT_ORDER) && K > INT32_MAX / 2) return fail(GQ_ERR_INVALID_ARG, "K too large for act order");
+    if (flags & GQ_ACT_ORDER) {
+        if (!ws) return fail(GQ_ERR_INVALID_ARG, "null workspace");
+        if (ws_bytes < gptq_quantize_ex_workspace_size(N, K, group, flags))
+            return fail(GQ_ERR_INVALID_ARG, "workspace too small");
+        // columns by decreasing diag(H): permute H on both sides, factor it, and
+        // sweep W's permuted columns with their original groups' static scales
+        char *base = (char *)ws;
+        const size_t fb = factor_bytes(K), ub = align_up((size_t)K * (size_t)K * sizeof(float));
+        float *U = (float *)(base + fb);
+        char *sweep_ws = base + fb + ub;
+        Carver cv(sweep_ws + sweep_bytes(N, K));
+        float *Hp = cv.take<float>((size_t)K * (size_t)K);
+        ActOrder act;
+        act.perm = cv.take<int>((size_t)K);
+        act.inv = cv.take<int>((size_t)K);
+        act.gidx = cv.take<int>((size_t)K);
+        act.cperm = cv.take<uint8_t>((size_t)N * (size_t)(K / 2));
+        GQ_HIP(launch_act_perm(act.perm, act.inv, act.gidx, H, K, group, stream), "act order");
+        GQ_HIP(launch_perm_sym(Hp, H, act.perm, K, stream), "permute H");
+        rc = gptq_factor(U, Hp, K, damp, base, fb, stream);
+        if (rc) return rc;
+        Carver sc(sweep_ws);
+        SweepWs w = carve_sweep(sc, N, K);
+        return run_sweep(codes, scales, qerr_out, W, U, imp, N, K, group, mode_of(flags), w, stream, &act);
+    }
     if (!ws) return fail(GQ_ERR_INVALID_ARG, "null workspace");
     if (ws_bytes < gptq_quantize_workspace_size(N, K, group)) return fail(GQ_ERR_INVALID_ARG, "workspace too small");
     char *base = (char *)ws;

@@ -48,7 +48,7 @@ __global__ __launch_bounds__(SW_NT, 4) void sweep_block_kernel(float *__restrict
                                                            uint8_t *__restrict__ codes,
                                                            float *__restrict__ scales,
                                                            const float *__restrict__ U, int64_t N,
-                                                           int64_t K, int64_t b0)
+                                                           int64_t K, int64_t b0, const int *__restrict__ gidx)
 {
     constexpr bool STATIC = (MODE & MODE_STATIC) != 0, NF4 = (MODE & MODE_NF4) != 0;
     __shared__ __attribute__((aligned(16))) float Us[BW * UPITCH];
@@ -83,17 +83,18 @@ __global__ __launch_bounds__(SW_NT, 4) void sweep_block_kernel(float *__restrict
         w[t] = (rv && col < bw) ? Wk[row * K + b0 + col] : 0.0f;
     }
 
-    // static groups: the scale of column cb + t's group (one group per lane when
-    // G >= 8); columns past bw have none
-    float sl[8];
+    // static groups: the scale of column cb + t's group -- group gidx[column]
+    // when a group map is given (act order), else column / G -- and RN(1/scale)
+    // (0 for a zero scale); columns past bw have none
+    float sl[8], yl[8];
     if constexpr (STATIC) {
-        if constexpr (G >= 8) {
-            const float v = (rv && cb < bw) ? scales[row * ngroups + (b0 + cb) / G] : 0.0f;
 #pragma unroll
-            for (int t = 0; t < 8; ++t) sl[t] = v;
-        } else {
-#pragma unroll
-            for (int t = 0; t < 8; ++t) sl[t] = (rv && cb + t < bw) ? scales[row * ngroups + (b0 + cb + t) / G] : 0.0f;
+        for (int t = 0; t < 8; ++t) {
+            const int64_t col = b0 + cb + t;
+            const bool ok = rv && cb + t < bw;
+            const int64_t gi = ok ? (gidx ? (int64_t)gidx[col] : col / G) : 0;
+            sl[t] = ok ? scales[row * ngroups + gi] : 0.0f;
+            yl[t] = sl[t] != 0.0f ? 1.0f / sl[t] : 0.0f;
         }
     }
     // NF4: this lane's midpoint and the lanes 0..14 of its row group
@@ -108,11 +109,14 @@ __global__ __launch_bounds__(SW_NT, 4) void sweep_block_kernel(float *__restrict
         constexpr int i = decltype(I)::value;
         constexpr int q = i / 8, t = i % 8;
         const float wi = row_bcast<q>(w[t]);
-        if constexpr (i % G == 0) {
+        if constexpr (STATIC) {
+            // every column takes its own group's scale from the lane holding it
+            const float sc = row_bcast<q>(sl[t]);
+            s = sc != 0.0f ? sc : 1.0f;
+            y = row_bcast<q>(yl[t]);
+        } else if constexpr (i % G == 0) {
             float sc;
-            if constexpr (STATIC) {
-                sc = row_bcast<q>(sl[t]);
-            } else {
+            {
                 float m = 0.0f;
 #pragma unroll
                 for (int u = 0; u < 8; ++u) {
@@ -531,13 +535,14 @@ hipError_t launch_check_finite(const float *x, int64_t n, unsigned *status, hipS
 
 template <int MODE>
 hipError_t launch_sweep_mode(float *Wk, float *ET, uint8_t *codes, float *scales, const float *U, int64_t N,
-                             int64_t K, int64_t G, int64_t b0, hipStream_t s)
+                             int64_t K, int64_t G, int64_t b0, const int *gidx, hipStream_t s)
 {
     const int64_t nwg = (N + ROWS_WG - 1) / ROWS_WG;
     const dim3 grid((unsigned)nwg), block(SW_NT);
-#define GQ_SWEEP_CASE(g)                                                                                          \
-    case g:                                                                                                       \
-        hipLaunchKernelGGL((sweep_block_kernel<g, MODE>), grid, block, 0, s, Wk, ET, codes, scales, U, N, K, b0); \
+#define GQ_SWEEP_CASE(g)                                                                                      \
+    case g:                                                                                                   \
+        hipLaunchKernelGGL((sweep_block_kernel<g, MODE>), grid, block, 0, s, Wk, ET, codes, scales, U, N, K, b0, \
+                           gidx);                                                                             \
         break;
     switch (G) {
         GQ_SWEEP_CASE(1)
@@ -555,17 +560,111 @@ hipError_t launch_sweep_mode(float *Wk, float *ET, uint8_t *codes, float *scales
 }
 
 hipError_t launch_sweep_block(float *Wk, float *ET, uint8_t *codes, float *scales, const float *U,
-                              int64_t N, int64_t K, int64_t G, int64_t b0, int mode, hipStream_t s)
+                              int64_t N, int64_t K, int64_t G, int64_t b0, int mode, const int *gidx,
+                              hipStream_t s)
 {
+    if (gidx && !(mode & MODE_STATIC)) return hipErrorInvalidValue;
     switch (mode) {
-    case 0: return launch_sweep_mode<0>(Wk, ET, codes, scales, U, N, K, G, b0, s);
-    case MODE_STATIC: return launch_sweep_mode<MODE_STATIC>(Wk, ET, codes, scales, U, N, K, G, b0, s);
-    case MODE_NF4: return launch_sweep_mode<MODE_NF4>(Wk, ET, codes, scales, U, N, K, G, b0, s);
+    case 0: return launch_sweep_mode<0>(Wk, ET, codes, scales, U, N, K, G, b0, nullptr, s);
+    case MODE_STATIC: return launch_sweep_mode<MODE_STATIC>(Wk, ET, codes, scales, U, N, K, G, b0, gidx, s);
+    case MODE_NF4: return launch_sweep_mode<MODE_NF4>(Wk, ET, codes, scales, U, N, K, G, b0, nullptr, s);
     case MODE_STATIC | MODE_NF4:
-        return launch_sweep_mode<MODE_STATIC | MODE_NF4>(Wk, ET, codes, scales, U, N, K, G, b0, s);
+        return launch_sweep_mode<MODE_STATIC | MODE_NF4>(Wk, ET, codes, scales, U, N, K, G, b0, gidx, s);
     default: return hipErrorInvalidValue;
     }
 }
+
+// ---------------------------------------------------------------- act order
+// Column a of the act order is the column with the a-th largest diagonal entry
+// of H, equal entries in increasing column order.  Column i's rank counts the
+// columns that come before it in that strict total order (NaN entries after all
+// others, so the ranks stay a permutation whatever H holds; the factor refuses
+// such an H anyway).  perm[rank] = i, inv[i] = rank, gidx[rank] = i / G.
+__device__ inline bool act_before(float dj, int j, float di, int i)
+{
+    const bool nj = dj != dj, ni = di != di;
+    if (nj != ni) return ni;
+    if (nj) return j < i;
+    return dj > di || (dj == di && j < i);
+}
+
+constexpr int AP_NT = 256;
+__global__ __launch_bounds__(AP_NT) void act_perm_kernel(int *__restrict__ perm, int *__restrict__ inv,
+                                                         int *__restrict__ gidx, const float *__restrict__ H,
+                                                         int64_t K, int64_t G)
+{
+    __shared__ float dt[AP_NT];
+    const int64_t i = (int64_t)blockIdx.x * AP_NT + threadIdx.x;
+    const float di = i < K ? H[i * K + i] : 0.0f;
+    int rank = 0;
+    for (int64_t j0 = 0; j0 < K; j0 += AP_NT) {
+        const int64_t j = j0 + threadIdx.x;
+        dt[threadIdx.x] = j < K ? H[j * K + j] : 0.0f;
+        __syncthreads();
+        const int n = (int)((K - j0) < AP_NT ? (K - j0) : AP_NT);
+        for (int u = 0; u < n; ++u) rank += act_before(dt[u], (int)(j0 + u), di, (int)i) ? 1 : 0;
+        __syncthreads();
+    }
+    if (i < K) {
+        perm[rank] = (int)i;
+        inv[i] = rank;
+        gidx[rank] = (int)(i / G);
+    }
+}
+
+// Hp[a][b] = H[perm[a]][perm[b]] from H's lower triangle (both triangles of Hp).
+__global__ __launch_bounds__(256) void perm_sym_kernel(float *__restrict__ Hp, const float *__restrict__ H,
+                                                       const int *__restrict__ perm, int64_t K)
+{
+    for (int64_t a = blockIdx.y; a < K; a += gridDim.y) {
+        const int64_t i = perm[a];
+        for (int64_t b = (int64_t)blockIdx.x * 256 + threadIdx.x; b < K; b += (int64_t)gridDim.x * 256) {
+            const int64_t j = perm[b];
+            Hp[a * K + b] = i >= j ? H[i * K + j] : H[j * K + i];
+        }
+    }
+}
+
+// Wk[n][a] = W[n][perm[a]], with the finite check of the plain copy.
+__global__ __launch_bounds__(256) void gather_cols_kernel(float *__restrict__ Wk, const float *__restrict__ W,
+                                                          const int *__restrict__ perm, int64_t N, int64_t K,
+                                                          unsigned *status)
+{
+    bool bad = false;
+    for (int64_t n = blockIdx.y; n < N; n += gridDim.y)
+        for (int64_t a = (int64_t)blockIdx.x * 256 + threadIdx.x; a < K; a += (int64_t)gridDim.x * 256) {
+            const float v = W[n * K + perm[a]];
+            bad = bad || !isfinite(v);
+            Wk[n * K + a] = v;
+        }
+    if (bad) atomicOr(status, ST_NONFINITE);
+}
+
+// codes[n][k] = cperm[n][inv[k]] for packed nibbles (two columns per byte).
+__global__ __launch_bounds__(256) void unpermute_codes_kernel(uint8_t *__restrict__ codes,
+                                                              const uint8_t *__restrict__ cperm,
+                                                              const int *__restrict__ inv, int64_t N, int64_t K)
+{
+    const int64_t half = K / 2;
+    for (int64_t n = blockIdx.y; n < N; n += gridDim.y) {
+        const uint8_t *src = cperm + n * half;
+        for (int64_t m = (int64_t)blockIdx.x * 256 + threadIdx.x; m < half; m += (int64_t)gridDim.x * 256) {
+            const int a0 = inv[2 * m], a1 = inv[2 * m + 1];
+            const unsigned lo = (src[a0 >> 1] >> (4 * (a0 & 1))) & 0xFu;
+            const unsigned hi = (src[a1 >> 1] >> (4 * (a1 & 1))) & 0xFu;
+            codes[n * half + m] = (uint8_t)(lo | (hi << 4));
+        }
+    }
+}
+
+unsigned cols_grid(int64_t cols)
+{
+    int64_t g = (cols + 255) / 256;
+    return (unsigned)(g < 1 ? 1 : (g > 64 ? 64 : g));
+}
+
+// rows of a row-strided launch: at most 65535 (the y limit), the kernels stride
+unsigned rows_grid(int64_t rows) { return (unsigned)(rows < 1 ? 1 : (rows > 65535 ? 65535 : rows)); }
 hipError_t launch_qerr(double *partials, const float *W, const uint8_t *codes, const float *scales,
                        const float *imp, int64_t N, int64_t K, int64_t G, int mode, hipStream_t s)
 {
@@ -627,6 +726,39 @@ hipError_t launch_rtn(const float *W, uint8_t *codes, float *scales, const float
     if (e != hipSuccess || !partials) return e;
     if (nparts) *nparts = qerr_partials(N);
     return launch_qerr(partials, W, codes, scales, imp, N, K, G, mode, s);
+}
+
+hipError_t launch_act_perm(int *perm, int *inv, int *gidx, const float *H, int64_t K, int64_t G, hipStream_t s)
+{
+    if (K <= 0) return hipSuccess;
+    hipLaunchKernelGGL(act_perm_kernel, dim3((unsigned)((K + AP_NT - 1) / AP_NT)), dim3(AP_NT), 0, s, perm, inv, gidx,
+                       H, K, G);
+    return hipGetLastError();
+}
+
+hipError_t launch_perm_sym(float *Hp, const float *H, const int *perm, int64_t K, hipStream_t s)
+{
+    if (K <= 0) return hipSuccess;
+    hipLaunchKernelGGL(perm_sym_kernel, dim3(cols_grid(K), rows_grid(K)), dim3(256), 0, s, Hp, H, perm, K);
+    return hipGetLastError();
+}
+
+hipError_t launch_gather_cols(float *Wk, const float *W, const int *perm, int64_t N, int64_t K, unsigned *status,
+                              hipStream_t s)
+{
+    if (N <= 0 || K <= 0) return hipSuccess;
+    hipLaunchKernelGGL(gather_cols_kernel, dim3(cols_grid(K), rows_grid(N)), dim3(256), 0, s, Wk, W, perm, N, K,
+                       status);
+    return hipGetLastError();
+}
+
+hipError_t launch_unpermute_codes(uint8_t *codes, const uint8_t *cperm, const int *inv, int64_t N, int64_t K,
+                                  hipStream_t s)
+{
+    if (N <= 0 || K <= 0) return hipSuccess;
+    hipLaunchKernelGGL(unpermute_codes_kernel, dim3(cols_grid(K / 2), rows_grid(N)), dim3(256), 0, s, codes, cperm,
+                       inv, N, K);
+    return hipGetLastError();
 }
 
 }  // namespace gq

@@ -233,9 +233,21 @@ enum : int { MODE_STATIC = 1, MODE_NF4 = 2 };
 
 // Sweep of one lazy block.  With MODE_STATIC the scales are read from `scales`
 // (written beforehand for every row and group), not computed and stored.
+// gidx (static groups only, else null): the group of each column of W's order,
+// when the columns are not in their natural order (act order).
 hipError_t launch_sweep_block(float *Wk, float *ET, uint8_t *codes, float *scales,
                               const float *U, int64_t N, int64_t K, int64_t G, int64_t b0, int mode,
+                              const int *gidx, hipStream_t s);
+// Act order: perm[a] = the column with the a-th largest diagonal entry of H (ties
+// in column order), inv its inverse, gidx[a] = perm[a] / G; Hp = H permuted on
+// both sides (from H's lower triangle); Wk = W's columns permuted (with the finite
+// check); codes put back in the original column order (packed nibbles).
+hipError_t launch_act_perm(int *perm, int *inv, int *gidx, const float *H, int64_t K, int64_t G, hipStream_t s);
+hipError_t launch_perm_sym(float *Hp, const float *H, const int *perm, int64_t K, hipStream_t s);
+hipError_t launch_gather_cols(float *Wk, const float *W, const int *perm, int64_t N, int64_t K, unsigned *status,
                               hipStream_t s);
+hipError_t launch_unpermute_codes(uint8_t *codes, const uint8_t *cperm, const int *inv, int64_t N, int64_t K,
+                                  hipStream_t s);
 // Round-to-nearest codes and scales of W on the sweep's grid (gptq.hip): the
 // uniform int4 grid, or NF4 with MODE_NF4 in mode.  With partials set, also
 // qerr's partial sums (as launch_qerr's, *nparts pairs, at most

@@ -197,6 +197,41 @@ def test_attn_gptq_variants(gq, orc, attn, attn_U, flags):
     assert q == pytest.approx(orc.qerr(call, sall, Wn, impn, flags=flags), rel=1e-6)
 
 
+def test_attn_gptq_act_order(gq, orc, attn):
+    """Act order with static groups at full size: the device's codes, put in the
+    order of decreasing diag(P), against the oracle's sweep and replay of 96
+    sampled rows of the permuted problem (U of the permuted P, each column with
+    its original group); scales are round to nearest's bit for bit."""
+    wl, X, W, H, blob, Hs, P = attn
+    N, K, G = wl.N[0], wl.K, wl.group
+    flags = gq.GQ_STATIC_GROUPS | gq.GQ_ACT_ORDER
+    imp = blob[: 4 * K].view(torch.float32)
+    codes = torch.empty(N, K // 2, dtype=torch.uint8, device=DEV)
+    scales = torch.empty(N, K // G, dtype=torch.float32, device=DEV)
+    q = gq.gptq_quantize_ex(codes, scales, W.to(DEV), P, imp, G, wl.damp, flags,
+                            gq.workspace(gq.gptq_quantize_ex_workspace_size(N, K, G, flags), DEV))
+    Pn, Wn, impn = P.cpu().numpy(), W.numpy(), imp.cpu().numpy().copy()
+    perm = orc.act_order_perm(Pn)
+    assert not np.array_equal(perm, np.arange(K))
+    st, Up, _ = orc.gptq_U(_sym64(Pn)[np.ix_(perm, perm)].astype(np.float32), wl.damp)
+    assert st == orc.OK
+    call = orc.unpack_codes(codes.cpu().numpy(), K)
+    sall = scales.cpu().numpy()
+    rows = np.sort(np.random.default_rng(5).choice(N, 96, replace=False))
+    Wp = np.ascontiguousarray(Wn[:, perm])
+    rep = orc.gptq_replay(call[rows][:, perm], sall[rows], Wp, Up, G, rows=rows, flags=orc.STATIC_GROUPS,
+                          gidx=perm // G)
+    oc, _ = orc.gptq_sweep(Wp, Up, G, rows=rows, flags=orc.STATIC_GROUPS, gidx=perm // G)
+    ident = float((call[rows][:, perm] == oc).mean())
+    print(f"K=5120 act order: code identity {ident:.6f} on 96 rows, replay {rep}, qerr {q:.5f}")
+    assert rep["inadmissible"] == 0 and rep["scale_mismatch"] == 0
+    assert rep["exact"] >= 0.999 * oc.size
+    assert ident >= 0.99
+    _, rs = orc.rtn(Wn, G)
+    assert np.array_equal(sall, rs)
+    assert q == pytest.approx(orc.qerr(call, sall, Wn, impn), rel=1e-6)
+
+
 def test_attn_raw_stored_hessian_needs_projection(gq, orc, attn):
     """The dataset card: a stored Hessian fails Cholesky at small damping on about
     half the K=5120 tensors, and succeeds at damp 0.01 once projected.  On this

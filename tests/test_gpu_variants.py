@@ -12,7 +12,13 @@ inadmissible code (a code differs only where the oracle's value lies within
 off by more than 1e-5 relative, at least 99.9% identical codes, and qerr within
 1e-4 of the oracle's.  Static scales equal the oracle's round-to-nearest scales
 bit for bit.  Shapes: several tiles, ragged row counts and widths, groups of 2
-to 128, an all-zero group under static groups.
+to 128, an all-zero group under static groups.  Act order (columns by
+decreasing diag(H), static groups) is checked on the permuted problem: the
+replay runs on W and H permuted by the oracle's permutation, each column with
+its original group, over the device's codes put in that order; every decision
+must be admissible and 99.9% of them identical given the same history, while
+raw identity with the oracle's own run is held to 99% (one legitimate tie flip
+on a long row of an ill-conditioned problem moves a few hundred later codes).
 """
 import numpy as np
 import pytest
@@ -87,7 +93,7 @@ def _gpu_gptq(gq, W, H, G, flags, damp=0.01, imp=None, want_qerr=True):
     it = None if imp is None else torch.from_numpy(np.ascontiguousarray(imp, np.float32)).to(DEV)
     codes = torch.zeros(N, K // 2, dtype=torch.uint8, device=DEV)
     scales = torch.zeros(N, K // G, dtype=torch.float32, device=DEV)
-    ws = gq.workspace(gq.gptq_quantize_workspace_size(N, K, G), DEV)
+    ws = gq.workspace(gq.gptq_quantize_ex_workspace_size(N, K, G, flags), DEV)
     q = gq.gptq_quantize_ex(codes, scales, Wt, Ht, it, G, damp, flags, ws, want_qerr)
     return codes.cpu().numpy(), scales.cpu().numpy(), q
 
@@ -189,3 +195,75 @@ def test_nf4_gptq_beats_nf4_rtn_on_output(gq, orc):
     H64 = H.astype(np.float64)
     out = lambda Q: float(np.einsum("nk,kl,nl->", W - Q, H64, W - Q))
     assert out(deq(cg, sg)) < 0.9 * out(deq(cr, sr))
+
+
+def _check_act(orc, W, H, G, flags, codes_packed, scales, q, imp=None, damp=0.01):
+    N, K = W.shape
+    perm = orc.act_order_perm(H)
+    Hs = np.tril(H) + np.tril(H, -1).T
+    st, Up, _ = orc.gptq_U(Hs[np.ix_(perm, perm)], damp)
+    assert st == orc.OK
+    codes = orc.unpack_codes(codes_packed, K, flags=flags)
+    st, oc, os_, qo = orc.gptq(W, H, G, damp, imp, want_qerr=q is not None, flags=flags)
+    assert st == orc.OK
+    ident = float((codes == oc).mean())
+    rep = orc.gptq_replay(codes[:, perm], scales, W[:, perm], Up, G, flags=flags & ~orc.ACT_ORDER,
+                          gidx=perm // G)
+    # every decision admissible, 99.9% identical given the same history; the raw
+    # identity with the oracle's own trajectory can lose a few hundred codes to a
+    # single legitimate tie flip on a long row (ill-conditioned H, few rows)
+    assert rep["inadmissible"] == 0, rep
+    assert rep["scale_mismatch"] == 0, rep
+    assert rep["exact"] >= 0.999 * codes.size, rep
+    assert ident >= 0.99, (ident, rep)
+    _, rs = orc.rtn(W, G, flags=flags & orc.NF4)
+    assert np.array_equal(scales, rs)                         # static scales, original groups
+    if q is not None:
+        assert abs(q - qo) / qo < 1e-4
+        assert abs(q - orc.qerr(codes, scales, W, imp, flags=flags)) / q < 1e-6
+    return ident, rep
+
+
+def _spread_channels(N, K, seed):
+    """Correlated activations with a spread of channel energies (so the
+    permutation is far from the identity)."""
+    X = g.normal_matrix(seed, g.S_X, 2 * K, K).numpy()
+    mix = g.normal_matrix(seed, g.S_A, K, K, 1.0 / np.sqrt(K)).numpy()
+    scale = np.exp(g.normal_matrix(seed, g.S_S, 1, K).numpy()[0])
+    return ((X @ (np.eye(K) + mix)) * scale).astype(np.float32)
+
+
+@pytest.mark.parametrize("flags", [5, 7])
+@pytest.mark.parametrize("N,K,G", [(200, 256, 32), (33, 384, 128), (130, 200, 8), (64, 130, 2), (40, 1024, 64)])
+def test_act_order(gq, orc, flags, N, K, G):
+    X = _spread_channels(N, K, N + K)
+    H = orc.gram(X).astype(np.float32)
+    H = np.tril(H)                                            # the lower triangle is all that is read
+    W = g.uniform_weights(N + K, N, K).numpy()
+    imp = np.diag(H).copy()
+    codes, scales, q = _gpu_gptq(gq, W, H, G, flags, imp=imp)
+    _check_act(orc, W, H, G, flags, codes, scales, q, imp)
+
+
+def test_act_order_argument_errors(gq, orc):
+    wl = g.WORKLOADS["tiny"]
+    W = torch.from_numpy(g.weights(wl).numpy()).to(DEV)
+    H = torch.from_numpy(orc.gram(g.x_chunk(wl)).astype(np.float32)).to(DEV)
+    N, K = W.shape
+    G = wl.group
+    c = torch.zeros(N, K // 2, dtype=torch.uint8, device=DEV)
+    s = torch.zeros(N, K // G, dtype=torch.float32, device=DEV)
+    big = gq.workspace(gq.gptq_quantize_ex_workspace_size(N, K, G, 5), DEV)
+    assert gq.gptq_quantize_ex_workspace_size(N, K, G, 5) > gq.gptq_quantize_workspace_size(N, K, G)
+    for flags in (gq.GQ_ACT_ORDER, gq.GQ_ACT_ORDER | gq.GQ_NF4):       # needs static groups
+        with pytest.raises(gq.GQError) as e:
+            gq.gptq_quantize_ex(c, s, W, H, None, G, wl.damp, flags, big)
+        assert e.value.status == gq.GQ_ERR_INVALID_ARG
+    small = gq.workspace(gq.gptq_quantize_workspace_size(N, K, G), DEV)
+    with pytest.raises(gq.GQError) as e:                                  # act order's workspace is larger
+        gq.gptq_quantize_ex(c, s, W, H, None, G, wl.damp, 5, small)
+    assert e.value.status == gq.GQ_ERR_INVALID_ARG
+    U = torch.empty(K, K, dtype=torch.float32, device=DEV)
+    with pytest.raises(gq.GQError) as e:                                  # not through the split sweep
+        gq.gptq_sweep_ex(c, s, W, U, None, G, 5, gq.workspace(gq.gptq_sweep_workspace_size(N, K, G), DEV))
+    assert e.value.status == gq.GQ_ERR_INVALID_ARG
