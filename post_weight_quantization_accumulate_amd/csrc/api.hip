@@ -947,7 +947,8 @@ int gptq_quantize_ex(uint8_t *codes, float *scales, double *qerr_out, const floa
         act.gidx = cv.take<int>((size_t)K);
         act.cperm = cv.take<uint8_t>((size_t)N * (size_t)(K / 2));
         GQ_HIP(launch_act_perm(act.perm, act.inv, act.gidx, H, K, group, stream), "act order");
-        GQ_HIP(launch_perm_sym(Hp, H, act.perm, K, stream), "permute H");
+        // U's buffer is free until the factor: it holds H's full symmetric copy
+        GQ_HIP(launch_perm_sym(Hp, H, act.perm, U, K, stream), "permute H");
         rc = gptq_factor(U, Hp, K, damp, base, fb, stream);
         if (rc) return rc;
         Carver sc(sweep_ws);

@@ -588,27 +588,32 @@ __device__ inline bool act_before(float dj, int j, float di, int i)
     return dj > di || (dj == di && j < i);
 }
 
+// rank[i] += the number of columns j in chunk blockIdx.y (AP_NT columns) that
+// come before i; rank starts at zero, and integer sums do not depend on order.
 constexpr int AP_NT = 256;
-__global__ __launch_bounds__(AP_NT) void act_perm_kernel(int *__restrict__ perm, int *__restrict__ inv,
-                                                         int *__restrict__ gidx, const float *__restrict__ H,
-                                                         int64_t K, int64_t G)
+__global__ __launch_bounds__(AP_NT) void act_rank_kernel(int *__restrict__ rank, const float *__restrict__ H,
+                                                         int64_t K)
 {
     __shared__ float dt[AP_NT];
     const int64_t i = (int64_t)blockIdx.x * AP_NT + threadIdx.x;
+    const int64_t j0 = (int64_t)blockIdx.y * AP_NT;
     const float di = i < K ? H[i * K + i] : 0.0f;
-    int rank = 0;
-    for (int64_t j0 = 0; j0 < K; j0 += AP_NT) {
-        const int64_t j = j0 + threadIdx.x;
-        dt[threadIdx.x] = j < K ? H[j * K + j] : 0.0f;
-        __syncthreads();
-        const int n = (int)((K - j0) < AP_NT ? (K - j0) : AP_NT);
-        for (int u = 0; u < n; ++u) rank += act_before(dt[u], (int)(j0 + u), di, (int)i) ? 1 : 0;
-        __syncthreads();
-    }
+    dt[threadIdx.x] = j0 + threadIdx.x < K ? H[(j0 + threadIdx.x) * K + j0 + threadIdx.x] : 0.0f;
+    __syncthreads();
+    const int n = (int)((K - j0) < AP_NT ? (K - j0) : AP_NT);
+    int c = 0;
+    for (int u = 0; u < n; ++u) c += act_before(dt[u], (int)(j0 + u), di, (int)i) ? 1 : 0;
+    if (i < K && c) atomicAdd(&rank[i], c);
+}
+
+// perm[rank[i]] = i, gidx[rank[i]] = i / G (rank is the inverse permutation).
+__global__ __launch_bounds__(AP_NT) void act_scatter_kernel(int *__restrict__ perm, int *__restrict__ gidx,
+                                                            const int *__restrict__ rank, int64_t K, int64_t G)
+{
+    const int64_t i = (int64_t)blockIdx.x * AP_NT + threadIdx.x;
     if (i < K) {
-        perm[rank] = (int)i;
-        inv[i] = rank;
-        gidx[rank] = (int)(i / G);
+        perm[rank[i]] = (int)i;
+        gidx[rank[i]] = (int)(i / G);
     }
 }
 
@@ -638,6 +643,55 @@ __global__ __launch_bounds__(256) void gather_cols_kernel(float *__restrict__ Wk
             Wk[n * K + a] = v;
         }
     if (bad) atomicOr(status, ST_NONFINITE);
+}
+
+// out[a][b] = in[rowperm[a]][perm[b]] (rowperm null: row a itself) for K-wide
+// rows: each workgroup holds one source row in LDS (read once, coalesced) and
+// writes the output row in order, so neither side is a scattered access.  With
+// status set, non-finite values set ST_NONFINITE.  K <= kRowGatherMaxK.
+constexpr int64_t kRowGatherMaxK = 32768;          // 128 KB of LDS
+constexpr int RG_NT = 512;
+__global__ __launch_bounds__(RG_NT) void row_gather_kernel(float *__restrict__ out, const float *__restrict__ in,
+                                                           const int *__restrict__ rowperm,
+                                                           const int *__restrict__ perm, int64_t rows, int64_t K,
+                                                           unsigned *status)
+{
+    extern __shared__ float rowbuf[];
+    bool bad = false;
+    for (int64_t a = blockIdx.x; a < rows; a += gridDim.x) {
+        const float *src = in + (rowperm ? (int64_t)rowperm[a] : a) * K;
+        for (int64_t k = threadIdx.x; k < K; k += RG_NT) rowbuf[k] = src[k];
+        __syncthreads();
+        for (int64_t b = threadIdx.x; b < K; b += RG_NT) {
+            const float v = rowbuf[perm[b]];
+            bad = bad || !isfinite(v);
+            out[a * K + b] = v;
+        }
+        __syncthreads();
+    }
+    if (status && bad) atomicOr(status, ST_NONFINITE);
+}
+
+// S = the full symmetric matrix whose lower triangle is H's (K x K, row stride
+// K): each 64 x 64 tile on or below the diagonal is read once and written to
+// its place and, transposed through LDS, to the mirrored place.
+__global__ __launch_bounds__(256) void sym_full_kernel(float *__restrict__ S, const float *__restrict__ H, int64_t K)
+{
+    const int64_t bi = blockIdx.y, bj = blockIdx.x;
+    if (bj > bi) return;
+    __shared__ float t[64][65];
+    const int64_t r0 = bi * 64, c0 = bj * 64;
+    const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+    for (int r = ty; r < 64; r += 4)
+        if (r0 + r < K && c0 + tx < K) t[r][tx] = H[(r0 + r) * K + c0 + tx];
+    __syncthreads();
+    for (int r = ty; r < 64; r += 4) {
+        const int64_t gr = r0 + r, gc = c0 + tx;
+        if (gr < K && gc < K) S[gr * K + gc] = (bi != bj || r >= tx) ? t[r][tx] : t[tx][r];
+    }
+    if (bi != bj)
+        for (int c = ty; c < 64; c += 4)
+            if (c0 + c < K && r0 + tx < K) S[(c0 + c) * K + r0 + tx] = t[tx][c];
 }
 
 // codes[n][k] = cperm[n][inv[k]] for packed nibbles (two columns per byte).
@@ -731,14 +785,45 @@ hipError_t launch_rtn(const float *W, uint8_t *codes, float *scales, const float
 hipError_t launch_act_perm(int *perm, int *inv, int *gidx, const float *H, int64_t K, int64_t G, hipStream_t s)
 {
     if (K <= 0) return hipSuccess;
-    hipLaunchKernelGGL(act_perm_kernel, dim3((unsigned)((K + AP_NT - 1) / AP_NT)), dim3(AP_NT), 0, s, perm, inv, gidx,
-                       H, K, G);
+    const unsigned nb = (unsigned)((K + AP_NT - 1) / AP_NT);
+    hipError_t e = launch_fill_u32((unsigned *)inv, K, 0u, s);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(act_rank_kernel, dim3(nb, nb), dim3(AP_NT), 0, s, inv, H, K);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(act_scatter_kernel, dim3(nb), dim3(AP_NT), 0, s, perm, gidx, inv, K, G);
     return hipGetLastError();
 }
 
-hipError_t launch_perm_sym(float *Hp, const float *H, const int *perm, int64_t K, hipStream_t s)
+namespace {
+bool row_gather_ready()
+{
+    static const bool ok = hipFuncSetAttribute((const void *)row_gather_kernel,
+                                               hipFuncAttributeMaxDynamicSharedMemorySize,
+                                               (int)(kRowGatherMaxK * sizeof(float))) == hipSuccess;
+    return ok;
+}
+
+hipError_t launch_row_gather(float *out, const float *in, const int *rowperm, const int *perm, int64_t rows,
+                             int64_t K, unsigned *status, hipStream_t s)
+{
+    const int64_t g = rows < 4096 ? rows : 4096;
+    hipLaunchKernelGGL(row_gather_kernel, dim3((unsigned)g), dim3(RG_NT), (size_t)K * sizeof(float), s, out, in,
+                       rowperm, perm, rows, K, status);
+    return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_perm_sym(float *Hp, const float *H, const int *perm, float *tmp, int64_t K, hipStream_t s)
 {
     if (K <= 0) return hipSuccess;
+    if (tmp && K <= kRowGatherMaxK && row_gather_ready()) {
+        const unsigned nt = (unsigned)((K + 63) / 64);
+        hipLaunchKernelGGL(sym_full_kernel, dim3(nt, nt), dim3(256), 0, s, tmp, H, K);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        return launch_row_gather(Hp, tmp, perm, perm, K, K, nullptr, s);
+    }
     hipLaunchKernelGGL(perm_sym_kernel, dim3(cols_grid(K), rows_grid(K)), dim3(256), 0, s, Hp, H, perm, K);
     return hipGetLastError();
 }
@@ -747,6 +832,7 @@ hipError_t launch_gather_cols(float *Wk, const float *W, const int *perm, int64_
                               hipStream_t s)
 {
     if (N <= 0 || K <= 0) return hipSuccess;
+    if (K <= kRowGatherMaxK && row_gather_ready()) return launch_row_gather(Wk, W, nullptr, perm, N, K, status, s);
     hipLaunchKernelGGL(gather_cols_kernel, dim3(cols_grid(K), rows_grid(N)), dim3(256), 0, s, Wk, W, perm, N, K,
                        status);
     return hipGetLastError();

@@ -243,7 +243,8 @@ hipError_t launch_sweep_block(float *Wk, float *ET, uint8_t *codes, float *scale
 // both sides (from H's lower triangle); Wk = W's columns permuted (with the finite
 // check); codes put back in the original column order (packed nibbles).
 hipError_t launch_act_perm(int *perm, int *inv, int *gidx, const float *H, int64_t K, int64_t G, hipStream_t s);
-hipError_t launch_perm_sym(float *Hp, const float *H, const int *perm, int64_t K, hipStream_t s);
+// tmp: K x K scratch for a full symmetric copy (or null: a direct gather).
+hipError_t launch_perm_sym(float *Hp, const float *H, const int *perm, float *tmp, int64_t K, hipStream_t s);
 hipError_t launch_gather_cols(float *Wk, const float *W, const int *perm, int64_t N, int64_t K, unsigned *status,
                               hipStream_t s);
 hipError_t launch_unpermute_codes(uint8_t *codes, const uint8_t *cperm, const int *inv, int64_t N, int64_t K,
