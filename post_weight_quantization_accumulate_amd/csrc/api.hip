@@ -841,6 +841,9 @@ int hadamard_rotate_hessian(float *H, int64_t K, int64_t block, const float *sig
     float *T = (float *)ws;
     GQ_HIP(launch_fwht_rows(H, K, K, K, block, signs, stream), "fwht rows");
     GQ_HIP(launch_transpose(T, H, K, stream), "transpose");
+    if (launch_fwht_rows(H, K, K, K, block, signs, stream, T) == hipSuccess) return GQ_OK;   // T's rows into H
+    (void)hipGetLastError();
+    // small blocks or unaligned buffers: rotate in place, then copy back
     GQ_HIP(launch_fwht_rows(T, K, K, K, block, signs, stream), "fwht rows");
     GQ_HIP(hipMemcpyAsync(H, T, (size_t)K * (size_t)K * sizeof(float), hipMemcpyDeviceToDevice, stream), "copy");
     return GQ_OK;

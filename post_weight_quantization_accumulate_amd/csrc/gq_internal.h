@@ -267,8 +267,11 @@ int64_t qerr_partials(int64_t N);
 // r < rows (ld apart), R = blockdiag(H_b) diag(signs) / sqrt(b); signs may be
 // null (all +1).  hadamard_block_ok: b a power of two <= 4096 dividing K.
 bool hadamard_block_ok(int64_t K, int64_t b);
+// With src set, the rows are read from src (same shape and stride) and the
+// rotated rows written to A, for the vector kernel's cases only (b >= 16, K and
+// ld multiples of 4, 16-byte aligned pointers; else hipErrorInvalidValue).
 hipError_t launch_fwht_rows(float *A, int64_t rows, int64_t K, int64_t ld, int64_t b, const float *signs,
-                            hipStream_t s);
+                            hipStream_t s, const float *src = nullptr);
 // out = in^T for K x K row-major fp32 matrices (out and in distinct).
 hipError_t launch_transpose(float *out, const float *in, int64_t K, hipStream_t s);
 

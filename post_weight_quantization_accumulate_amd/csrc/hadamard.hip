@@ -69,14 +69,16 @@ __global__ __launch_bounds__(HT) void fwht_rows_kernel(float *__restrict__ A, in
     }
 }
 
-// The same transform for b >= 16 with K, ld and A 16-byte aligned: thread t owns
-// the P = E / 256 consecutive elements t P .. t P + P - 1 of the workgroup's E,
-// all in one segment, loaded and stored as 16-byte vectors with one address
-// computation per thread; the stages h < P (pairs inside a thread) run in
-// registers, the rest through LDS.
+// The same transform for b >= 16 with K, ld and both matrices 16-byte aligned:
+// thread t owns the P = E / 256 consecutive elements t P .. t P + P - 1 of the
+// workgroup's E, all in one segment, loaded and stored as 16-byte vectors with
+// one address computation per thread; the stages h < P (pairs inside a thread)
+// run in registers, the rest through LDS.  It reads src and writes A (the same
+// matrix for the in-place rotation; a thread stores only what it loaded).
 template <int P>
-__global__ __launch_bounds__(HT) void fwht_rows_vec_kernel(float *__restrict__ A, int64_t rows, int64_t K, int64_t ld,
-                                                           int b, const float *__restrict__ signs, float scale)
+__global__ __launch_bounds__(HT) void fwht_rows_vec_kernel(float *A, const float *src, int64_t rows, int64_t K,
+                                                           int64_t ld, int b, const float *__restrict__ signs,
+                                                           float scale)
 {
     __shared__ float x[HT * P];
     constexpr int E = HT * P;
@@ -91,7 +93,7 @@ __global__ __launch_bounds__(HT) void fwht_rows_vec_kernel(float *__restrict__ A
     if (valid) {
 #pragma unroll
         for (int u = 0; u < P; u += 4) {
-            const float4 q = *(const float4 *)(A + r * ld + col + u);
+            const float4 q = *(const float4 *)(src + r * ld + col + u);
             v[u] = q.x; v[u + 1] = q.y; v[u + 2] = q.z; v[u + 3] = q.w;
         }
         if (signs) {
@@ -163,7 +165,7 @@ bool hadamard_block_ok(int64_t K, int64_t b)
 }
 
 hipError_t launch_fwht_rows(float *A, int64_t rows, int64_t K, int64_t ld, int64_t b, const float *signs,
-                            hipStream_t s)
+                            hipStream_t s, const float *src)
 {
     if (rows <= 0 || K <= 0) return hipSuccess;
     if (!hadamard_block_ok(K, b) || ld < K) return hipErrorInvalidValue;
@@ -171,16 +173,19 @@ hipError_t launch_fwht_rows(float *A, int64_t rows, int64_t K, int64_t ld, int64
     const int64_t nseg = rows * (K / b), per = E / b;
     const int64_t nwg = (nseg + per - 1) / per;
     const float scale = (float)(1.0 / std::sqrt((double)b));
-    const bool vec = b >= 16 && K % 4 == 0 && ld % 4 == 0 && ((uintptr_t)A & 15) == 0 && ((uintptr_t)signs & 15) == 0;
+    const bool vec = b >= 16 && K % 4 == 0 && ld % 4 == 0 && ((uintptr_t)A & 15) == 0 &&
+                     ((uintptr_t)signs & 15) == 0 && ((uintptr_t)src & 15) == 0;
+    if (src && !vec) return hipErrorInvalidValue;     // out of place: the vector kernel only
+    if (!src) src = A;
     if (vec && E == 1024)
-        hipLaunchKernelGGL(fwht_rows_vec_kernel<4>, dim3((unsigned)nwg), dim3(HT), 0, s, A, rows, K, ld, (int)b, signs,
-                           scale);
+        hipLaunchKernelGGL(fwht_rows_vec_kernel<4>, dim3((unsigned)nwg), dim3(HT), 0, s, A, src, rows, K, ld, (int)b,
+                           signs, scale);
     else if (vec && E == 2048)
-        hipLaunchKernelGGL(fwht_rows_vec_kernel<8>, dim3((unsigned)nwg), dim3(HT), 0, s, A, rows, K, ld, (int)b, signs,
-                           scale);
+        hipLaunchKernelGGL(fwht_rows_vec_kernel<8>, dim3((unsigned)nwg), dim3(HT), 0, s, A, src, rows, K, ld, (int)b,
+                           signs, scale);
     else if (vec && E == 4096)
-        hipLaunchKernelGGL(fwht_rows_vec_kernel<16>, dim3((unsigned)nwg), dim3(HT), 0, s, A, rows, K, ld, (int)b, signs,
-                           scale);
+        hipLaunchKernelGGL(fwht_rows_vec_kernel<16>, dim3((unsigned)nwg), dim3(HT), 0, s, A, src, rows, K, ld, (int)b,
+                           signs, scale);
     else
         hipLaunchKernelGGL(fwht_rows_kernel, dim3((unsigned)nwg), dim3(HT), 0, s, A, rows, K, ld, (int)b, E, signs,
                            scale);
