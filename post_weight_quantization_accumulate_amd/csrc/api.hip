@@ -238,7 +238,9 @@ SweepWs carve_sweep(Carver &c, int64_t N, int64_t K)
     SweepWs w;
     w.sc = carve_scalars(c);
     w.Wk = c.take<float>((size_t)N * (size_t)K);
-    w.ET = c.take<float>((size_t)kSweepSuper * (size_t)N);
+    // errors of two groups, k-major: a group's rows stay until the side stream's
+    // update has read them, which ends before the group after next is swept
+    w.ET = c.take<float>((size_t)2 * kSweepSuper * (size_t)N);
     return w;
 }
 
@@ -415,12 +417,30 @@ int run_sweep(uint8_t *codes, float *scales, double *qerr_out, const float *W, c
     // Column order as in the unblocked sweep; every column receives the
     // feedback of all earlier columns before it is quantised: from its own
     // block inside the sweep kernel, from earlier blocks of its group through
-    // the per-block products, and from earlier groups through the group products.
+    // the per-block products, and from earlier groups through the group
+    // products.  Once group j is swept, its errors go into the next group on
+    // this stream and into every later column on the side stream, one large
+    // product that overlaps the next group's sweep (disjoint columns, finished
+    // error rows); this stream waits for it only before it updates those
+    // columns itself.
+    Lookahead *la = nullptr;
+    GQ_HIP(lookahead_for_current_device(&la), "lookahead stream");
+    bool side_pending = false;
+    auto update = [&](const float *Eg, int64_t k0, int64_t k1, int64_t c0, int64_t c1,
+                      hipStream_t st) -> hipError_t {
+        // Wk[:, c0:c1] -= E[k0:k1]^T U[k0:k1, c0:c1], E's rows k0.. at Eg
+        GemmDesc d = gemm(Eg, N, U + k0 * K + c0, K, N, c1 - c0, k1 - k0, w.Wk + c0, K);
+        d.cin = w.Wk + c0;
+        d.alpha = -1.0;
+        d.beta = 1.0;
+        return gemm_tn_f32(d, st);
+    };
     for (int64_t g0 = 0; g0 < K; g0 += kSweepSuper) {
         const int64_t g1 = (K - g0) < kSweepSuper ? K : g0 + kSweepSuper;
+        float *const ETg = w.ET + ((g0 / kSweepSuper) & 1) * (int64_t)kSweepSuper * N;   // this group's E^T
         for (int64_t b0 = g0; b0 < g1; b0 += kSweepBlock) {
             const int64_t bw = (g1 - b0) < kSweepBlock ? (g1 - b0) : kSweepBlock;
-            float *ETb = w.ET + (b0 - g0) * N;          // this block's rows of the group's E^T
+            float *ETb = ETg + (b0 - g0) * N;          // this block's rows of E^T
             GQ_HIP(launch_sweep_block(w.Wk, ETb, sweep_codes, scales, U, N, K, G, b0, mode,
                                       act ? act->gidx : nullptr, s),
                    "sweep block");
@@ -434,13 +454,22 @@ int run_sweep(uint8_t *codes, float *scales, double *qerr_out, const float *W, c
             }
         }
         if (g1 < K) {
-            GemmDesc d = gemm(w.ET, N, U + g0 * K + g1, K, N, K - g1, g1 - g0, w.Wk + g1, K);
-            d.cin = w.Wk + g1;
-            d.alpha = -1.0;
-            d.beta = 1.0;
-            GQ_HIP(gemm_tn_f32(d, s), "group update");
+            const int64_t n1 = (K - g1) < kSweepSuper ? K : g1 + kSweepSuper;   // the next group's end
+            if (side_pending) {
+                GQ_HIP(hipStreamWaitEvent(s, la->to_main, 0), "wait side update");
+                side_pending = false;
+            }
+            if (n1 < K) {
+                GQ_HIP(hipEventRecord(la->to_side, s), "record");
+                GQ_HIP(hipStreamWaitEvent(la->side, la->to_side, 0), "wait group swept");
+                GQ_HIP(update(ETg, g0, g1, n1, K, la->side), "group update (later groups)");
+                GQ_HIP(hipEventRecord(la->to_main, la->side), "record");
+                side_pending = true;
+            }
+            GQ_HIP(update(ETg, g0, g1, g1, n1, s), "group update (next group)");
         }
     }
+    if (side_pending) GQ_HIP(hipStreamWaitEvent(s, la->to_main, 0), "wait side update");
     if (act) GQ_HIP(launch_unpermute_codes(codes, act->cperm, act->inv, N, K, s), "unpermute codes");
     if (qerr_out) {
         GQ_HIP(launch_qerr(w.sc.partials, W, codes, scales, imp, N, K, G, mode, s), "qerr");
