@@ -2,7 +2,8 @@
 hadamard_rotate_hessian) against the oracle's dense fp64 rotation, through the C
 ABI.  The device runs log2(b) fp32 butterfly stages, so the bar is 1e-5 relative
 Frobenius (the Hessian bar), with every entry checked.  Shapes: blocks of 1 to
-4096, a row stride above K, signs or none, the bench workload's W (10240 x 5120,
+4096 (the Hessian's below 16 take the in-place kernel and a copy back), a row
+stride above K, signs or none, the bench workload's W (10240 x 5120,
 b = 1024) on sampled rows and its K = 5120 Hessian; plus the output invariance
 and the rotated path through GPTQ."""
 import numpy as np
@@ -50,7 +51,7 @@ def test_rotate_rows(gq, orc, rows, K, b, extra, signed):
     assert np.array_equal(out[:, K:], A[:, K:])             # the columns past K are not touched
 
 
-@pytest.mark.parametrize("K,b", [(256, 128), (1024, 1024), (96, 32)])
+@pytest.mark.parametrize("K,b", [(256, 128), (1024, 1024), (96, 32), (48, 8), (20, 4), (10, 1)])
 def test_rotate_hessian(gq, orc, K, b):
     rng = np.random.default_rng(K)
     X = rng.standard_normal((3 * K, K)).astype(np.float32)
