@@ -28,8 +28,8 @@ namespace gq {
 namespace {
 
 constexpr int BW = kSweepBlock;        // 128
-constexpr int SW_NT = 512;             // 8 waves
-constexpr int ROWS_WG = 32;            // 4 rows per wave
+constexpr int SW_NT = 1024;            // 16 waves
+constexpr int ROWS_WG = 64;            // 4 rows per wave
 constexpr int UPITCH = BW + 4;
 
 // Value of register x in lane `src` of each 16-lane row, to every lane of it.
@@ -41,8 +41,10 @@ template <int src> __device__ inline float row_bcast(float x)
 // Midpoint j of the NF4 levels in fp32 (j = 15: above every value).
 __device__ inline float nf4_mid(int j) { return j < 15 ? (kNF4[j] + kNF4[j + 1]) * 0.5f : INFINITY; }
 
-// Four waves per SIMD (two workgroups per CU): the grid has one workgroup per
-// 32 rows, which for ten thousand rows is just over one per CU.
+// Four waves per SIMD (one workgroup of 16 waves per CU): the grid has one
+// workgroup per 64 rows, 160 for ten thousand rows, so each block of U is read
+// from memory half as often as with 32 rows, and CUs stay free for the update
+// products that run beside the sweep on a second stream.
 template <int G, int MODE>
 __global__ __launch_bounds__(SW_NT, 4) void sweep_block_kernel(float *__restrict__ Wk, float *__restrict__ ET,
                                                            uint8_t *__restrict__ codes,
