@@ -472,8 +472,9 @@ int run_sweep(uint8_t *codes, float *scales, double *qerr_out, const float *W, c
     if (side_pending) GQ_HIP(hipStreamWaitEvent(s, la->to_main, 0), "wait side update");
     if (act) GQ_HIP(launch_unpermute_codes(codes, act->cperm, act->inv, N, K, s), "unpermute codes");
     if (qerr_out) {
-        GQ_HIP(launch_qerr(w.sc.partials, W, codes, scales, imp, N, K, G, mode, s), "qerr");
-        GQ_HIP(launch_qerr_reduce(w.sc.d, w.sc.partials, qerr_partials(N), s), "qerr reduce");
+        int64_t nparts = 0;
+        GQ_HIP(launch_qerr(w.sc.partials, W, codes, scales, imp, N, K, G, mode, s, &nparts), "qerr");
+        GQ_HIP(launch_qerr_reduce(w.sc.d, w.sc.partials, nparts, s), "qerr reduce");
     }
     unsigned st = 0;
     int rc = read_status(w.sc.status, s, &st);

@@ -309,6 +309,52 @@ __global__ __launch_bounds__(QNT) void qerr_kernel(double *__restrict__ partials
     }
 }
 
+// The same sums for K a multiple of 8 with W (and imp) 16-byte and the codes
+// 4-byte aligned: a thread takes 8 consecutive columns of a row at a time (two
+// 16-byte loads of W, one 4-byte word of codes), the grid strides over the rows'
+// 8-column chunks, and each workgroup folds its sums in the fixed-order tree.
+template <bool NF4>
+__global__ __launch_bounds__(QNT) void qerr8_kernel(double *__restrict__ partials, const float *__restrict__ W,
+                                                   const uint8_t *__restrict__ codes,
+                                                   const float *__restrict__ scales,
+                                                   const float *__restrict__ imp, int64_t N, int64_t K, int64_t G)
+{
+    __shared__ double sh[2 * QNT];
+    __shared__ float lev[16];
+    if (NF4 && threadIdx.x < 16) lev[threadIdx.x] = kNF4[threadIdx.x];
+    __syncthreads();
+    const int64_t chunks = K / 8, total = N * chunks, ng = K / G;
+    double num = 0.0, den = 0.0;
+    for (int64_t idx = (int64_t)blockIdx.x * QNT + threadIdx.x; idx < total; idx += (int64_t)gridDim.x * QNT) {
+        const int64_t row = idx / chunks, c = idx - row * chunks;
+        const float4 a = *(const float4 *)(W + row * K + 8 * c);
+        const float4 b = *(const float4 *)(W + row * K + 8 * c + 4);
+        const float w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+        const unsigned cw = *(const unsigned *)(codes + row * (K / 2) + 4 * c);
+        float iw[8] = {1.0f, 1.0f, 1.0f, 1.0f, 1.0f, 1.0f, 1.0f, 1.0f};
+        if (imp) {
+            const float4 i0 = *(const float4 *)(imp + 8 * c), i1 = *(const float4 *)(imp + 8 * c + 4);
+            iw[0] = i0.x; iw[1] = i0.y; iw[2] = i0.z; iw[3] = i0.w;
+            iw[4] = i1.x; iw[5] = i1.y; iw[6] = i1.z; iw[7] = i1.w;
+        }
+        const float *srow = scales + row * ng;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            const unsigned nib = (cw >> (4 * t)) & 0xFu;
+            const float cv = NF4 ? lev[nib] : (float)((int)nib - ((nib & 8u) ? 16 : 0));
+            const float sc = srow[(8 * c + t) / G];
+            const double d = (double)w[t] - (double)cv * (double)sc;
+            num += (double)iw[t] * d * d;
+            den += (double)iw[t] * (double)w[t] * (double)w[t];
+        }
+    }
+    block_sum2(num, den, sh);
+    if (threadIdx.x == 0) {
+        partials[2 * blockIdx.x] = num;
+        partials[2 * blockIdx.x + 1] = den;
+    }
+}
+
 __global__ __launch_bounds__(QNT) void qerr_reduce_kernel(double *out2, const double *partials, int64_t nparts)
 {
     __shared__ double sh[2 * QNT];
@@ -722,8 +768,23 @@ unsigned cols_grid(int64_t cols)
 // rows of a row-strided launch: at most 65535 (the y limit), the kernels stride
 unsigned rows_grid(int64_t rows) { return (unsigned)(rows < 1 ? 1 : (rows > 65535 ? 65535 : rows)); }
 hipError_t launch_qerr(double *partials, const float *W, const uint8_t *codes, const float *scales,
-                       const float *imp, int64_t N, int64_t K, int64_t G, int mode, hipStream_t s)
+                       const float *imp, int64_t N, int64_t K, int64_t G, int mode, hipStream_t s, int64_t *nparts)
 {
+    const bool wide = K % 8 == 0 && ((uintptr_t)W & 15) == 0 && ((uintptr_t)codes & 3) == 0 &&
+                      ((uintptr_t)imp & 15) == 0;
+    if (wide) {
+        const int64_t need = (N * (K / 8) + QNT - 1) / QNT;
+        const int64_t nwg = need < QPARTS ? (need < 1 ? 1 : need) : QPARTS;
+        if (mode & MODE_NF4)
+            hipLaunchKernelGGL(qerr8_kernel<true>, dim3((unsigned)nwg), dim3(QNT), 0, s, partials, W, codes, scales,
+                               imp, N, K, G);
+        else
+            hipLaunchKernelGGL(qerr8_kernel<false>, dim3((unsigned)nwg), dim3(QNT), 0, s, partials, W, codes, scales,
+                               imp, N, K, G);
+        if (nparts) *nparts = nwg;
+        return hipGetLastError();
+    }
+    if (nparts) *nparts = qerr_partials(N);
     const int64_t np = N < QPARTS ? N : QPARTS;
     const int64_t rows_per = (N + np - 1) / np;
     const int64_t nwg = qerr_partials(N);
@@ -780,8 +841,7 @@ hipError_t launch_rtn(const float *W, uint8_t *codes, float *scales, const float
         hipLaunchKernelGGL(rtn_any_kernel<false>, grid, dim3(RTN_NT), 0, s, W, codes, scales, N, K, (int)G, status);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || !partials) return e;
-    if (nparts) *nparts = qerr_partials(N);
-    return launch_qerr(partials, W, codes, scales, imp, N, K, G, mode, s);
+    return launch_qerr(partials, W, codes, scales, imp, N, K, G, mode, s, nparts);
 }
 
 hipError_t launch_act_perm(int *perm, int *inv, int *gidx, const float *H, int64_t K, int64_t G, hipStream_t s)

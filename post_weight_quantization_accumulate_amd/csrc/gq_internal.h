@@ -256,9 +256,11 @@ hipError_t launch_unpermute_codes(uint8_t *codes, const uint8_t *cperm, const in
 int64_t rtn_partials(int64_t N, int64_t K);
 hipError_t launch_rtn(const float *W, uint8_t *codes, float *scales, const float *imp, double *partials, int64_t N,
                       int64_t K, int64_t G, int mode, unsigned *status, hipStream_t s, int64_t *nparts);
+// qerr's partial sums: *nparts pairs (at most 1024 and at most rtn_partials(N, K))
+// for launch_qerr_reduce.
 hipError_t launch_qerr(double *partials, const float *W, const uint8_t *codes,
                        const float *scales, const float *imp, int64_t N, int64_t K, int64_t G, int mode,
-                       hipStream_t s);
+                       hipStream_t s, int64_t *nparts);
 hipError_t launch_qerr_reduce(double *out2, const double *partials, int64_t nparts,
                               hipStream_t s);
 int64_t qerr_partials(int64_t N);
