@@ -338,11 +338,12 @@ __global__ __launch_bounds__(QNT) void qerr8_kernel(double *__restrict__ partial
             iw[4] = i1.x; iw[5] = i1.y; iw[6] = i1.z; iw[7] = i1.w;
         }
         const float *srow = scales + row * ng;
+        const float s8 = G >= 8 ? srow[8 * c / G] : 0.0f;     // one group holds all 8 columns
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
             const unsigned nib = (cw >> (4 * t)) & 0xFu;
             const float cv = NF4 ? lev[nib] : (float)((int)nib - ((nib & 8u) ? 16 : 0));
-            const float sc = srow[(8 * c + t) / G];
+            const float sc = G >= 8 ? s8 : srow[(8 * c + t) / G];
             const double d = (double)w[t] - (double)cv * (double)sc;
             num += (double)iw[t] * d * d;
             den += (double)iw[t] * (double)w[t] * (double)w[t];
