@@ -169,12 +169,14 @@ hipError_t launch_fwht_rows(float *A, int64_t rows, int64_t K, int64_t ld, int64
 {
     if (rows <= 0 || K <= 0) return hipSuccess;
     if (!hadamard_block_ok(K, b) || ld < K) return hipErrorInvalidValue;
-    const int E = b > 1024 ? (int)b : 1024;
-    const int64_t nseg = rows * (K / b), per = E / b;
-    const int64_t nwg = (nseg + per - 1) / per;
     const float scale = (float)(1.0 / std::sqrt((double)b));
     const bool vec = b >= 16 && K % 4 == 0 && ld % 4 == 0 && ((uintptr_t)A & 15) == 0 &&
                      ((uintptr_t)signs & 15) == 0 && ((uintptr_t)src & 15) == 0;
+    // the vector kernel takes 16 elements per thread (4096 per workgroup): the
+    // first four butterfly stages stay in registers; the generic one 1024
+    const int E = vec ? 4096 : (b > 1024 ? (int)b : 1024);
+    const int64_t nseg = rows * (K / b), per = E / b;
+    const int64_t nwg = (nseg + per - 1) / per;
     if (src && !vec) return hipErrorInvalidValue;     // out of place: the vector kernel only
     if (!src) src = A;
     if (vec && E == 1024)
