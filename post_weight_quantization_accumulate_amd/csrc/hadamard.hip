@@ -179,13 +179,7 @@ hipError_t launch_fwht_rows(float *A, int64_t rows, int64_t K, int64_t ld, int64
     const int64_t nwg = (nseg + per - 1) / per;
     if (src && !vec) return hipErrorInvalidValue;     // out of place: the vector kernel only
     if (!src) src = A;
-    if (vec && E == 1024)
-        hipLaunchKernelGGL(fwht_rows_vec_kernel<4>, dim3((unsigned)nwg), dim3(HT), 0, s, A, src, rows, K, ld, (int)b,
-                           signs, scale);
-    else if (vec && E == 2048)
-        hipLaunchKernelGGL(fwht_rows_vec_kernel<8>, dim3((unsigned)nwg), dim3(HT), 0, s, A, src, rows, K, ld, (int)b,
-                           signs, scale);
-    else if (vec && E == 4096)
+    if (vec)
         hipLaunchKernelGGL(fwht_rows_vec_kernel<16>, dim3((unsigned)nwg), dim3(HT), 0, s, A, src, rows, K, ld, (int)b,
                            signs, scale);
     else
