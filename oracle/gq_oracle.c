@@ -586,6 +586,9 @@ static float group_scale(double amax) { return (float)amax / 7.0f; }
  * codebook, whose levels span [-1, 1]. */
 static float grid_scale(double amax, const float *book)
 {
+#if ORC_MUTANT == 9
+    if (book) return (float)amax / 7.0f;   /* mutant: the uniform grid's step as the codebook scale */
+#endif
     return book ? (float)amax : group_scale(amax);
 }
 
@@ -600,6 +603,9 @@ static int book_code(double w, float s, const float *L)
     int c = 0;
     for (int j = 0; j < 15; j++) {
         float mid = (L[j] + L[j + 1]) * 0.5f;
+#if ORC_MUTANT == 10
+        mid = L[j + 1];                     /* mutant: the level below instead of the nearest */
+#endif
         if (x > mid) c++;
     }
     return c;
@@ -667,7 +673,10 @@ void orc_gptq_sweep_gx(int8_t *codes, float *scales, const float *W, const doubl
                        int64_t K, int64_t G, const int64_t *rows, int64_t nrows, int flags,
                        const float *book, const int64_t *gidx)
 {
-    const int stat = (flags & ORC_STATIC_GROUPS) != 0;
+    int stat = (flags & ORC_STATIC_GROUPS) != 0;
+#if ORC_MUTANT == 13
+    stat = 0;                               /* mutant: the static switch ignored */
+#endif
     if (!(flags & ORC_NF4)) book = NULL;
     if (!stat) gidx = NULL;
 #pragma omp parallel for schedule(dynamic, 1)
@@ -798,6 +807,9 @@ static int cmp_desc_diag(const void *pa, const void *pb)
 {
     int64_t a = *(const int64_t *)pa, b = *(const int64_t *)pb;
     float da = g_perm_diag[a], db = g_perm_diag[b];
+#if ORC_MUTANT == 11
+    { float t = da; da = db; db = t; }     /* mutant: increasing diagonal */
+#endif
     if (da > db) return -1;
     if (da < db) return 1;
     return (a > b) - (a < b);
@@ -851,6 +863,9 @@ int orc_gptq_ex(int8_t *codes, float *scales, double *qerr_out, const float *W, 
         for (int64_t n = 0; n < N; n++)
             for (int64_t a = 0; a < K; a++) Wp[n * K + a] = W[n * K + perm[a]];
         for (int64_t a = 0; a < K; a++) gidx[a] = perm[a] / G;
+#if ORC_MUTANT == 12
+        for (int64_t a = 0; a < K; a++) gidx[a] = a / G;   /* mutant: groups of the permuted order */
+#endif
         st = orc_gptq_U(U, Hp, K, damp, NULL);
         if (st == ORC_OK) {
             orc_gptq_sweep_gx(cp, scales, Wp, U, K, G, rows, N, flags, book, gidx);

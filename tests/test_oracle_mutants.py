@@ -78,6 +78,60 @@ def _qerr_pin_holds(orc):
     return np.isclose(nd[0], (imp * (W - D) ** 2).sum(), rtol=1e-12)
 
 
+def _nf4_qerr_pin_holds(orc):
+    """The wiki's NF4 qerr on uniform weights (qerr section, 0.09358)."""
+    gold = json.load(open(os.path.join(GOLD, "pages_values.json")))["qerr_nf4"]
+    W = g.uniform_weights(8, 256, 1024).numpy()
+    codes, scales = orc.rtn(W, 1024, flags=orc.NF4)
+    return abs(orc.qerr(codes, scales, W, flags=orc.NF4) - gold["measured"]) / gold["measured"] < 0.01
+
+
+def _nf4_nearest_pin_holds(orc):
+    """NF4 codes are the nearest levels (brute-force argmin), away from midpoints."""
+    rng = np.random.default_rng(4)
+    W = rng.standard_normal((16, 128)).astype(np.float32)
+    codes, scales = orc.rtn(W, 32, flags=orc.NF4)
+    L = orc.nf4_levels().astype(np.float64)
+    x = (W / np.repeat(scales, 32, axis=1)).astype(np.float32).astype(np.float64)
+    d = np.abs(x[..., None] - L)
+    srt = np.sort(d, -1)
+    clear = srt[..., 1] - srt[..., 0] > 1e-6
+    return np.array_equal(codes[clear], d.argmin(-1)[clear])
+
+
+def _act_perm_pin_holds(orc):
+    """Act order's permutation is numpy's stable argsort of the negated diagonal."""
+    rng = np.random.default_rng(21)
+    X = (rng.standard_normal((100, 40)) * rng.uniform(0.2, 3.0, 40)).astype(np.float32)
+    H = orc.gram(X).astype(np.float32)
+    return np.array_equal(orc.act_order_perm(H), np.argsort(-np.diag(H), kind="stable"))
+
+
+def _act_obq_pin_holds(orc):
+    """Act order equals OBQ taken in that column order with each column's own group."""
+    from test_oracle_variants import _obq_order
+    rng = np.random.default_rng(13)
+    N, K, G = 20, 48, 16
+    X = (rng.standard_normal((160, 12)) @ rng.standard_normal((12, K)) +
+         0.3 * rng.standard_normal((160, K))).astype(np.float32)
+    X *= rng.uniform(0.3, 3.0, K).astype(np.float32)
+    H = orc.gram(X).astype(np.float32)
+    H = (np.tril(H) + np.tril(H, -1).T).astype(np.float32)
+    W = rng.uniform(-1, 1, (N, K)).astype(np.float32)
+    st, codes, scales, _ = orc.gptq(W, H, G, 0.01, want_qerr=False, flags=orc.STATIC_GROUPS | orc.ACT_ORDER)
+    rc, rs = _obq_order(W, H, G, 0.01, np.argsort(-np.diag(H), kind="stable"))
+    return st == 0 and np.array_equal(codes, rc) and np.array_equal(scales, rs)
+
+
+def _static_pin_holds(orc):
+    """Static scales are the round-to-nearest scales of the original weights."""
+    wl = g.WORKLOADS["tiny"]
+    W = g.weights(wl).numpy()
+    H = orc.gram(g.x_chunk(wl)).astype(np.float32)
+    st, codes, scales, _ = orc.gptq(W, H, wl.group, 0.01, flags=orc.STATIC_GROUPS)
+    return st == 0 and np.array_equal(scales, orc.rtn(W, wl.group)[1])
+
+
 PINS = {
     1: _truncation_pin_holds,      # RNE instead of truncation
     2: _sweep_pin_holds,           # error feedback with the wrong sign
@@ -87,6 +141,11 @@ PINS = {
     6: _qerr_pin_holds,            # importance dropped from the numerator
     7: _gram_pin_holds,            # last token dropped
     8: _index_pin_holds,           # tril row stored reversed
+    9: _nf4_qerr_pin_holds,        # NF4 scale absmax/7
+    10: _nf4_nearest_pin_holds,    # NF4 rounds down to a level
+    11: _act_perm_pin_holds,       # act order ascending
+    12: _act_obq_pin_holds,        # act order's groups taken in the permuted order
+    13: _static_pin_holds,         # the static switch ignored
 }
 
 
