@@ -1,8 +1,21 @@
 /*
  * gq.h -- C ABI of the calibration-Hessian GPTQ int4 library for AMD MI355X
- * (gfx950).  Everything runs in hand-written HIP kernels on the stream the
- * caller passes; the library never allocates or frees device memory: the
- * caller owns every buffer and workspace.
+ * (gfx950).  Everything runs in hand-written HIP kernels; the library never
+ * allocates or frees device memory: the caller owns every buffer and workspace.
+ *
+ * State the library keeps across calls
+ *   - a thread-local error string (gq_last_error);
+ *   - per host thread and device, two HIP streams (default priority,
+ *     non-blocking) and four events, created on the first gptq_factor or
+ *     gptq_sweep on that device and kept until the process ends.  Those calls
+ *     fork part of their work onto the two streams (the Cholesky's trailing
+ *     updates and the triangular inverse beside the panel chain; each sweep
+ *     group's update of the later columns beside the next group's sweep), and
+ *     join it back into the caller's stream with events before they
+ *     synchronise it, so no work of a call is pending when it returns;
+ *   - the testing and profiling settings at the end of this header
+ *     (thread-local).
+ *   Nothing else: no device memory, no cache of inputs or results.
  *
  * Conventions shared by every call
  *   - Pointers are DEVICE pointers unless marked "host".  Device buffers must be
@@ -103,40 +116,29 @@ int hessian_unpack_tril(float *H, const void *blob, int64_t K, hipStream_t strea
 /* Workspace bytes psd_project needs for size K. */
 size_t psd_project_workspace_size(int64_t K);
 
-/* Floating-point operations psd_project executes for size K (the method's cost;
- * the dataset card's "The fix" prices the eigendecomposition at O(K^3)): each
- * symmetric K x K product of the sign iteration counts K*K*(K+1) (the lower
- * triangle it computes), plus the final rebuild.  Host-only query. */
+/* Floating-point operations psd_project executes for size K under its shortest
+ * schedule (the method's cost; the dataset card's "The fix" prices the
+ * eigendecomposition at O(K^3)): each symmetric K x K product of the sign
+ * iteration counts K*K*(K+1) (the lower triangle it computes), plus the final
+ * rebuild.  Host-only query. */
 double psd_project_flops(int64_t K);
 
-/* Number of symmetric products psd_project launches for any K. Host-only query. */
+/* Number of symmetric products psd_project launches under its shortest
+ * schedule, for any K (41).  A Hessian whose spectral bound is large against its
+ * mean diagonal gets a few more (see psd_project); the testing section's
+ * psd_project_last_timing reports the count of a given call.  Host-only query. */
 int psd_project_products(void);
-
-/* Per-kernel timing of psd_project, for profiling.  gq_set_timing(1) makes
- * later psd_project calls on this host thread bracket each launch of their
- * product kernel with HIP events on the caller's stream; psd_project_last_timing
- * then reports, for the last such call on this thread, the number of product
- * launches, their summed duration in ms (*product_ms), and the name of that
- * kernel (static string).  Returns GQ_ERR_INVALID_ARG if no timed call was
- * made.  Timing is off by default and costs two event records per launch. */
-void gq_set_timing(int on);
-int psd_project_last_timing(int *launches, double *product_ms, const char **kernel);
-
-/* Kind of the symmetric products inside psd_project, for tests and comparisons.
- * GQ_PSD_AUTO (default): emulated in integers on the int8 matrix cores for
- * K < 65536, fp64 matrix-core products above.  GQ_PSD_F64: fp64 matrix-core
- * products at every K.  Applies to later psd_project calls on this host thread;
- * psd_project_workspace_size covers both kinds.  Returns GQ_ERR_INVALID_ARG for
- * any other value (the setting is then unchanged). */
-enum { GQ_PSD_AUTO = 0, GQ_PSD_F64 = 1 };
-int gq_set_psd_products(int kind);
 
 /*
  * psd_project -- H <- nearest positive-semidefinite matrix in Frobenius norm:
  * eigenvalues clipped at zero, rebuilt, symmetrised (hipfire-calib-data, "The
  * fix"; required before Cholesky on stored Hessians).  Computed on the device
  * without an eigendecomposition, as P = (H + sign(H) H) / 2 with sign(H) from a
- * scaled Newton-Schulz iteration.  For K < 65536 its symmetric products are
+ * scaled Newton-Schulz iteration.  Its schedule starts from the spectral bound
+ * and mean(diag H), read back once, so that every eigenvalue of the result stays
+ * above -1e-6 mean(diag H): 20 iterations (41 products) when the bound is
+ * within about 67 times the mean diagonal, a few more when it is larger (three
+ * at a thousand times).  For K < 65536 its symmetric products are
  * computed exactly in integers on the int8 matrix cores from operands rounded
  * to 47-48-bit integers (one power-of-two scale per row; residues modulo 14
  * moduli, Chinese remainder reconstruction, one rounding to fp64); above that,
@@ -364,6 +366,35 @@ int hfqm_read_entry(const char *path, int64_t i, char *name, size_t name_cap, ui
 
 /* hfqm_read_payload -- entry i's payload into dst (a host buffer of dst_bytes >= its data_size). */
 int hfqm_read_payload(const char *path, int64_t i, void *dst, size_t dst_bytes);
+
+/*
+ * ---------------------------------------------------------------------------
+ * Testing and profiling controls.  Not part of the computation's contract:
+ * they change how later calls on the same host thread run (which product kind
+ * psd_project uses, whether it times its launches), never what a correct
+ * result is.  Each setting is thread-local, starts at its default on every
+ * thread, and stays until changed.
+ * ---------------------------------------------------------------------------
+ */
+
+/* Per-kernel timing of psd_project, for profiling.  gq_set_timing(1) makes
+ * later psd_project calls on this host thread bracket each launch of their
+ * product kernel with HIP events on the caller's stream; psd_project_last_timing
+ * then reports, for the last such call on this thread, the number of product
+ * launches, their summed duration in ms (*product_ms), and the name of that
+ * kernel (static string).  Returns GQ_ERR_INVALID_ARG if no timed call was
+ * made.  Timing is off by default and costs two event records per launch. */
+void gq_set_timing(int on);
+int psd_project_last_timing(int *launches, double *product_ms, const char **kernel);
+
+/* Kind of the symmetric products inside psd_project, for tests and comparisons.
+ * GQ_PSD_AUTO (default): emulated in integers on the int8 matrix cores for
+ * K < 65536, fp64 matrix-core products above.  GQ_PSD_F64: fp64 matrix-core
+ * products at every K.  Applies to later psd_project calls on this host thread;
+ * psd_project_workspace_size covers both kinds.  Returns GQ_ERR_INVALID_ARG for
+ * any other value (the setting is then unchanged). */
+enum { GQ_PSD_AUTO = 0, GQ_PSD_F64 = 1 };
+int gq_set_psd_products(int kind);
 
 #ifdef __cplusplus
 }

@@ -100,6 +100,7 @@ def _load(path):
         "orc_gptq_replay_ex": (None, [P, P, P, P, P, P, I64, I64, P, I64, D, D, I, P]),
         "orc_gptq_sweep_gx": (None, [P, P, P, P, I64, I64, P, I64, I, P, P]),
         "orc_gptq_replay_gx": (None, [P, P, P, P, P, P, I64, I64, P, I64, D, D, I, P, P]),
+        "orc_gptq_replay_hx": (None, [P, P, P, P, P, P, I64, I64, P, I64, D, D, I, P, P, P]),
         "orc_act_order_perm": (None, [P, P, I64]),
     }
     for name, (res, args) in sig.items():
@@ -249,6 +250,40 @@ def gptq_U(H, damp: float = 0.01):
     return st, U, mu.value
 
 
+def gptq_U_lapack(H, damp: float = 0.01):
+    """The same U as gptq_U, by the same literal route, for sizes where the plain
+    C loops take minutes (K = 17408): L = chol(H_d), H_d^-1 = L^-T L^-1, U = the
+    upper Cholesky factor of H_d^-1, with H_d = H + damp * mean(diag H) * I read
+    from H's lower triangle (ork-driver wiki "Exp 2026-08-18 GPTQ Int4":
+    Cholesky-based Hessian inverse; hipfire-calib-data "The fix": damping in units
+    of mean(diag H)).  Each step is one LAPACK primitive through torch's CPU
+    backend in fp64 (potrf, potri, potrf); statuses as gptq_U.  Pinned to gptq_U
+    in tests/test_oracle_gptq.py.  Returns (status, U fp64 upper, mu)."""
+    import torch
+    H = _np(H, np.float32)
+    K = H.shape[0]
+    low = np.tril(H)
+    if not np.isfinite(low).all():
+        return ERR_NONFINITE, None, float("nan")
+    mu = float(np.diag(H).astype(np.float64).sum() / K)
+    if not mu > 0.0:
+        return ERR_NO_CALIBRATION, None, mu
+    A = torch.from_numpy(low.astype(np.float64))
+    A = A + torch.tril(A, -1).T
+    A.diagonal().add_(damp * mu)
+    L, info = torch.linalg.cholesky_ex(A)
+    del A
+    if int(info) != 0:
+        return ERR_NOT_PD, None, mu
+    Hinv = torch.cholesky_inverse(L)          # (L L^T)^-1 = L^-T L^-1
+    del L
+    Lh, info = torch.linalg.cholesky_ex(Hinv)
+    del Hinv
+    if int(info) != 0:
+        return ERR_NOT_PD, None, mu
+    return OK, Lh.T.contiguous().numpy(), mu
+
+
 # Sweep and pack switches (gq_oracle.c): scales fixed from the original weights
 # before the sweep; the NF4 codebook instead of the uniform int4 grid.
 STATIC_GROUPS = 1
@@ -363,7 +398,10 @@ def gptq(W, H, G: int, damp: float = 0.01, imp=None, want_qerr: bool = True, fla
 
 def gptq_replay(cand_codes, cand_scales, W, U, G: int, rows=None, delta: float = 1e-3,
                 scale_tol: float = 1e-5, flags: int = 0, gidx=None):
-    """Admissibility of candidate codes/scales for W's listed rows (see gq_oracle.c)."""
+    """Admissibility of candidate codes/scales for W's listed rows (see gq_oracle.c).
+    flip_gap_hist counts the accepted tie flips by their distance from the exact
+    tie, in steps: [0, 1e-7), [1e-7, 1e-6), [1e-6, 1e-5), [1e-5, 1e-4),
+    [1e-4, 1e-3), [1e-3, delta]."""
     W = _np(W, np.float32)
     U = _c(U, np.float64)
     N, K = W.shape
@@ -372,12 +410,15 @@ def gptq_replay(cand_codes, cand_scales, W, U, G: int, rows=None, delta: float =
     cs = _c(cand_scales, np.float32)
     assert cc.shape == (len(rows), K) and cs.shape == (len(rows), K // G)
     stats = np.zeros(4, np.int64)
+    hist = np.zeros(6, np.int64)
     mrel = ctypes.c_double(0.0)
     gidx = None if gidx is None else _c(gidx, np.int64)
-    lib().orc_gptq_replay_gx(_p(stats), ctypes.byref(mrel), _p(cc), _p(cs), _p(W), _p(U), K, G,
-                             _p(rows), len(rows), delta, scale_tol, flags, _p(_book(flags)), _p(gidx))
+    lib().orc_gptq_replay_hx(_p(stats), ctypes.byref(mrel), _p(cc), _p(cs), _p(W), _p(U), K, G,
+                             _p(rows), len(rows), delta, scale_tol, flags, _p(_book(flags)), _p(gidx),
+                             _p(hist))
     return {"exact": int(stats[0]), "tie_flips": int(stats[1]), "inadmissible": int(stats[2]),
-            "scale_mismatch": int(stats[3]), "max_scale_rel": mrel.value}
+            "scale_mismatch": int(stats[3]), "max_scale_rel": mrel.value,
+            "flip_gap_hist": [int(x) for x in hist]}
 
 
 # ------------------------------------------------------------------ Hadamard rotation

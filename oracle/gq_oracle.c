@@ -905,12 +905,15 @@ int orc_gptq(int8_t *codes, float *scales, double *qerr_out, const float *W, con
  * follows the candidate (w_j -= e U[i][j] with e from the candidate's code and
  * scale), so a tie flip's downstream effect is not counted again.  max_rel[0]
  * gets the largest relative scale difference.  flags and book as for
- * orc_gptq_sweep_ex. */
-void orc_gptq_replay_gx(int64_t *stats, double *max_rel, const int8_t *cand_codes,
+ * orc_gptq_sweep_ex.  flip_hist (nullable, 6 counters) sorts the accepted tie
+ * flips by how far v was from the exact tie, in units of one step (of the
+ * level spacing on a codebook): [0, 1e-7), [1e-7, 1e-6), [1e-6, 1e-5),
+ * [1e-5, 1e-4), [1e-4, 1e-3), [1e-3, delta]. */
+void orc_gptq_replay_hx(int64_t *stats, double *max_rel, const int8_t *cand_codes,
                         const float *cand_scales, const float *W, const double *U,
                         int64_t K, int64_t G, const int64_t *rows, int64_t nrows,
                         double delta, double scale_tol, int flags, const float *book,
-                        const int64_t *gidx)
+                        const int64_t *gidx, int64_t *flip_hist)
 {
     const int stat = (flags & ORC_STATIC_GROUPS) != 0;
     if (!(flags & ORC_NF4)) book = NULL;
@@ -925,7 +928,8 @@ void orc_gptq_replay_gx(int64_t *stats, double *max_rel, const int8_t *cand_code
         if (!seen[gi]) { seen[gi] = 1; first[i] = 1; }
     }
     free(seen);
-#pragma omp parallel for schedule(dynamic, 1) reduction(+ : exact, flips, bad, smis) reduction(max : mrel)
+    int64_t h0 = 0, h1 = 0, h2 = 0, h3 = 0, h4 = 0, h5 = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(+ : exact, flips, bad, smis, h0, h1, h2, h3, h4, h5) reduction(max : mrel)
     for (int64_t r = 0; r < nrows; r++) {
         const float *w0 = W + rows[r] * K;
         double *wk = (double *)malloc((size_t)K * sizeof(double));
@@ -967,14 +971,26 @@ void orc_gptq_replay_gx(int64_t *stats, double *max_rel, const int8_t *cand_code
                 double other = rv + (v > rv ? 1.0 : -1.0);
                 if (other > 7.0) other = 7.0;
                 if (other < -8.0) other = -8.0;
-                if (dist >= 0.5 - delta && (double)cg == other) flips++;
-                else bad++;
+                if (dist >= 0.5 - delta && (double)cg == other) {
+                    flips++;
+                    const double gap = 0.5 - dist;
+                    if (gap < 1e-7) h0++; else if (gap < 1e-6) h1++; else if (gap < 1e-5) h2++;
+                    else if (gap < 1e-4) h3++; else if (gap < 1e-3) h4++; else h5++;
+                } else {
+                    bad++;
+                }
             } else if (s_ref != 0.0f && (cg == cr + 1 || cg == cr - 1) && cg >= 0 && cg < 16) {
                 int lo = cg < cr ? cg : cr;
                 double v = (double)((float)wk[i] / s_ref);
                 double mid = 0.5 * ((double)book[lo] + (double)book[lo + 1]);
-                if (fabs(v - mid) <= delta * ((double)book[lo + 1] - (double)book[lo])) flips++;
-                else bad++;
+                const double gap = fabs(v - mid) / ((double)book[lo + 1] - (double)book[lo]);
+                if (gap <= delta) {
+                    flips++;
+                    if (gap < 1e-7) h0++; else if (gap < 1e-6) h1++; else if (gap < 1e-5) h2++;
+                    else if (gap < 1e-4) h3++; else if (gap < 1e-3) h4++; else h5++;
+                } else {
+                    bad++;
+                }
             } else {
                 bad++;
             }
@@ -992,6 +1008,20 @@ void orc_gptq_replay_gx(int64_t *stats, double *max_rel, const int8_t *cand_code
     stats[2] = bad;
     stats[3] = smis;
     *max_rel = mrel;
+    if (flip_hist) {
+        flip_hist[0] = h0; flip_hist[1] = h1; flip_hist[2] = h2;
+        flip_hist[3] = h3; flip_hist[4] = h4; flip_hist[5] = h5;
+    }
+}
+
+void orc_gptq_replay_gx(int64_t *stats, double *max_rel, const int8_t *cand_codes,
+                        const float *cand_scales, const float *W, const double *U,
+                        int64_t K, int64_t G, const int64_t *rows, int64_t nrows,
+                        double delta, double scale_tol, int flags, const float *book,
+                        const int64_t *gidx)
+{
+    orc_gptq_replay_hx(stats, max_rel, cand_codes, cand_scales, W, U, K, G, rows, nrows, delta, scale_tol,
+                       flags, book, gidx, NULL);
 }
 
 void orc_gptq_replay_ex(int64_t *stats, double *max_rel, const int8_t *cand_codes,

@@ -139,15 +139,33 @@ GemmDesc gemm(const void *A, int64_t lda, const void *B, int64_t ldb, int64_t M,
 // The schedule stops once l > 1 - 1e-9: 20 iterations from 3e-7.  The last
 // one matters less for the eigenvalues above l_0 (already within 3.3e-8 of
 // +-1) than for those just below it, which it multiplies by 1.5 on their way
-// to +-1: at K = 17408 the stored Hessian's small negative eigenvalues need it
-// to keep the projection positive semidefinite to 1e-5 mean(diag).
+// to +-1.
+//
+// An eigenvalue lambda < 0 below the converged band leaves P with the
+// eigenvalue lambda (1 + s) / 2, s = the iteration's value there, not 0.  Over
+// the whole band the most negative such value is at most 0.036 l_0 b (b = the
+// spectral bound the iteration is scaled by; 7.95e-9 b from l_0 = 3e-7,
+// 3.3e-10 b from 1e-8: the schedule's polynomial evaluated on the real line).
+// The projection must keep every eigenvalue above -1e-6 mean(diag H)
+// (hipfire-calib-data, "The fix": the PSD bar), so the schedule starts at
+// l_0 = min(3e-7, 2e-5 mean(diag H) / b), a floor of at most -7.2e-7
+// mean(diag H): heavy-tailed Hessians, whose bound is a thousand times their
+// mean diagonal, get three more iterations; a bound below 67 times it, none.
 constexpr double kSignL0 = 3e-7;
+constexpr double kSignL0Min = 1e-12;
+constexpr double kSignFloor = 2e-5;
 constexpr double kSignTol = 1e-9;
 
-std::vector<double> sign_schedule()
+double sign_start(double mu, double bound)
+{
+    if (!(mu > 0.0) || !(bound > 0.0) || !std::isfinite(mu) || !std::isfinite(bound)) return kSignL0;
+    return std::max(kSignL0Min, std::min(kSignL0, kSignFloor * mu / bound));
+}
+
+std::vector<double> sign_schedule(double l0 = kSignL0)
 {
     std::vector<double> alphas;
-    double l = kSignL0;
+    double l = l0;
     while (l < 1.0 - kSignTol && alphas.size() < 64) {
         const double a = std::sqrt(3.0 / (1.0 + l + l * l));
         alphas.push_back(a);
@@ -599,12 +617,26 @@ int psd_project(float *H, int64_t K, void *ws, size_t ws_bytes, hipStream_t stre
     GQ_HIP(launch_sym_lower_to_f64(w.H64, H, K, status, stream), "symmetrise");
     GQ_HIP(launch_frobenius(fro, w.H64, n, w.sc.partials, stream), "norm");
     GQ_HIP(launch_scalar_combine(inv, fro, -1.0, nullptr, 0.0, stream), "inverse norm");
-    const std::vector<double> al = sign_schedule();
+    // mean(diag H) for the schedule's start (its status word is a scratch word
+    // that nobody reads: an all-zero H is projected, not refused)
+    double *mu = w.sc.d + 6;
+    GQ_HIP(launch_diag_mean_check(mu, H, K, status + 3, stream), "diag mean");
+    std::vector<double> al;
+    // once the bound is on the device: read it and mean(diag H) back and fix the
+    // schedule (one small copy and a synchronisation, before the iterations)
+    auto schedule = [&]() -> int {
+        double hs[8];
+        GQ_HIP(hipMemcpyAsync(hs, w.sc.d, sizeof(hs), hipMemcpyDeviceToHost, stream), "bound readback");
+        GQ_HIP(hipStreamSynchronize(stream), "stream synchronize");
+        // the spectrum of c * inv * H lies in [-1, 1]: the bound is 1 / (c * inv)
+        al = sign_schedule(sign_start(hs[6], 1.0 / (hs[3] * hs[1])));
+        return GQ_OK;
+    };
 
     PsdTiming &tm = g_timing;
     const bool timing = tm.on;
     if (timing) {
-        const size_t need = 2 * (size_t)psd_project_products();
+        const size_t need = 2 * (2 * sign_schedule(kSignL0Min).size() + 1);   // the longest schedule
         while (tm.ev.size() < need) {
             hipEvent_t e;
             GQ_HIP(hipEventCreate(&e), "timing event");
@@ -653,6 +685,7 @@ int psd_project(float *H, int64_t K, void *ws, size_t ws_bytes, hipStream_t stre
         GQ_HIP(launch_scalar_combine(c, yfro, -0.5, nullptr, 0.0, stream), "bound");
         GQ_HIP(launch_scalar_combine(c1inv, c, 1.0, inv, 1.0, stream), "scalars");
         GQ_HIP(launch_scalar_combine(c3inv, c, 3.0, inv, 1.0, stream), "scalars");
+        if (int rc = schedule()) return rc;
         for (size_t k = 0; k < al.size(); ++k) {
             const double a = 1.5 * al[k], b = -0.5 * al[k] * al[k] * al[k];
             if (k == 0) {
@@ -703,6 +736,7 @@ int psd_project(float *H, int64_t K, void *ws, size_t ws_bytes, hipStream_t stre
         GQ_HIP(launch_scalar_combine(c, yfro, -0.5, nullptr, 0.0, stream), "bound");
         GQ_HIP(launch_scalar_combine(c1inv, c, 1.0, inv, 1.0, stream), "scalars");
         GQ_HIP(launch_scalar_combine(c3inv, c, 3.0, inv, 1.0, stream), "scalars");
+        if (int rc = schedule()) return rc;
         double *X = w.X, *Xn = w.Xn;
         for (size_t k = 0; k < al.size(); ++k) {
             const double a = 1.5 * al[k], b = -0.5 * al[k] * al[k] * al[k];

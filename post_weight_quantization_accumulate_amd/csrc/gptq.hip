@@ -86,9 +86,10 @@ __global__ __launch_bounds__(SW_NT, 4) void sweep_block_kernel(float *__restrict
     }
 
     // static groups: the scale of column cb + t's group -- group gidx[column]
-    // when a group map is given (act order), else column / G -- and RN(1/scale)
-    // (0 for a zero scale); columns past bw have none
-    float sl[8], yl[8];
+    // when a group map is given (act order), else column / G -- its power-of-two
+    // guard factor (below) and RN(1 / (scale * factor)) (0 for a zero scale);
+    // columns past bw have none
+    float sl[8], yl[8], fl[8];
     if constexpr (STATIC) {
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
@@ -96,14 +97,20 @@ __global__ __launch_bounds__(SW_NT, 4) void sweep_block_kernel(float *__restrict
             const bool ok = rv && cb + t < bw;
             const int64_t gi = ok ? (gidx ? (int64_t)gidx[col] : col / G) : 0;
             sl[t] = ok ? scales[row * ngroups + gi] : 0.0f;
-            yl[t] = sl[t] != 0.0f ? 1.0f / sl[t] : 0.0f;
+            fl[t] = sl[t] < 0x1p-60f ? 0x1p64f : 1.0f;
+            yl[t] = sl[t] != 0.0f ? 1.0f / (sl[t] * fl[t]) : 0.0f;
         }
     }
     // NF4: this lane's midpoint and the lanes 0..14 of its row group
     const float mymid = nf4_mid(g16);
     const unsigned long long rowmask = 0x7FFFull << (lane & 48);
 
-    float s = 1.0f, y = 0.0f;  // the group's scale (1 for an all-zero group) and RN(1/s) (0 there)
+    // the group's scale s (1 for an all-zero group), its guard factor f, and
+    // y = RN(1 / (s f)) (0 there).  A scale below 2^-60 (weights all below about
+    // 2^-57) is scaled by f = 2^64 for the quotient, exactly, with the value
+    // scaled alike, so the correction step's remainder cannot underflow and
+    // 1/s cannot overflow: the quotient stays the IEEE one.
+    float s = 1.0f, y = 0.0f, f = 1.0f;
     float4 nu0 = *(const float4 *)&Us[cb], nu1 = *(const float4 *)&Us[cb + 4];
     // one column: the static index lets the broadcast source and the group test
     // be immediates
@@ -116,6 +123,7 @@ __global__ __launch_bounds__(SW_NT, 4) void sweep_block_kernel(float *__restrict
             const float sc = row_bcast<q>(sl[t]);
             s = sc != 0.0f ? sc : 1.0f;
             y = row_bcast<q>(yl[t]);
+            f = row_bcast<q>(fl[t]);
         } else if constexpr (i % G == 0) {
             float sc;
             {
@@ -137,16 +145,18 @@ __global__ __launch_bounds__(SW_NT, 4) void sweep_block_kernel(float *__restrict
             // itself (with dynamic scales every value met there is 0; with
             // static ones feedback may have moved it, and it passes on whole).
             s = sc != 0.0f ? sc : 1.0f;
-            y = sc != 0.0f ? 1.0f / s : 0.0f;
+            f = sc < 0x1p-60f ? 0x1p64f : 1.0f;
+            y = sc != 0.0f ? 1.0f / (s * f) : 0.0f;
         }
         // x = RN(wi / s) by Markstein's correction step (Markstein 1990; Muller
         // et al., Handbook of Floating-Point Arithmetic, division via FMA): with
         // y = RN(1/s) and q0 = RN(wi y), r = wi - s q0 is exact and RN(q0 + r y)
         // is the correctly rounded quotient (normal range), so the code is the
         // same as from an IEEE division, in three dependent operations instead
-        // of the division's dozen.
-        const float q0 = wi * y;
-        const float rr = fmaf(-s, q0, wi);
+        // of the division's dozen.  Value and scale enter scaled by f.
+        const float wq = wi * f;
+        const float q0 = wq * y;
+        const float rr = fmaf(-(s * f), q0, wq);
         const float x = fmaf(rr, y, q0);
         float c;                   // the value's multiple of s: the code, or its level
         unsigned nib;

@@ -166,17 +166,40 @@ def x_chunk(wl: Workload, chunk: int = 0, device="cpu", tokens=None) -> torch.Te
         X = c * (F @ A + 0.1 * E)
         return to_bf16_rne(X.to(torch.float32))
     if wl.name == "mlpdown17408":
-        # Student-t (nu = 3) activations with log-normal (sigma = 1) per-channel scales
-        z = normal_tensor(seed, S_X, (T, K), device=device)
-        chi2 = (normal_tensor(seed, S_T1, (T, K), device=device) ** 2
-                + normal_tensor(seed, S_T2, (T, K), device=device) ** 2
-                + normal_tensor(seed, S_T3, (T, K), device=device) ** 2)
-        t = z / torch.sqrt(chi2 / 3.0)
-        del z, chi2
-        s = torch.exp(normal_tensor(seed, S_S, (K,), device=device))
-        c = 1.0 / math.sqrt(wl.T * 3.0 * float((s * s).mean()))
-        return to_bf16_rne((c * s[None, :] * t).to(torch.float32))
+        return heavy_tailed_x(seed, T, K, wl.T, device=device)
     raise KeyError(wl.name)
+
+
+def heavy_tailed_x(seed: int, T: int, K: int, T_norm: int, device="cpu") -> torch.Tensor:
+    """Student-t (nu = 3) activations with log-normal (sigma = 1) per-channel
+    scales, as bf16: t = z / sqrt(chi2_3 / 3), x = c s_k t with s_k = exp(N(0,1))
+    and c = 1 / sqrt(T_norm * 3 * mean(s^2)), so that mean(diag X^T X) is about 1
+    over T_norm tokens.  The MLP down-projection recipe (K = 17408) and its
+    smaller blocks."""
+    z = normal_tensor(seed, S_X, (T, K), device=device)
+    chi2 = (normal_tensor(seed, S_T1, (T, K), device=device) ** 2
+            + normal_tensor(seed, S_T2, (T, K), device=device) ** 2
+            + normal_tensor(seed, S_T3, (T, K), device=device) ** 2)
+    t = z / torch.sqrt(chi2 / 3.0)
+    del z, chi2
+    s = torch.exp(normal_tensor(seed, S_S, (K,), device=device))
+    c = 1.0 / math.sqrt(T_norm * 3.0 * float((s * s).mean()))
+    return to_bf16_rne((c * s[None, :] * t).to(torch.float32))
+
+
+def common_mode_x(seed: int, T: int, K: int, device="cpu") -> torch.Tensor:
+    """Strongly correlated activations, as bf16: one factor shared by every
+    channel, x_tk = c (0.88 u_t m_k + 0.45 z_tk) with u, z ~ N(0, 1) and loadings
+    m_k = 1 + 0.05 N(0, 1), c = 1 / sqrt(T (0.88^2 + 0.45^2)).  Their Gram matrix
+    has a mean diagonal near 1 and off-diagonal entries near 0.77, like the
+    dataset card's K=5120 tensor (mean diag 0.995, off-diagonal RMS 0.789), so
+    the truncated storage of it leaves sizeable negative eigenvalues when
+    T < K."""
+    u = normal_tensor(seed, S_F, (T, 1), device=device)
+    m = 1.0 + 0.05 * normal_tensor(seed, S_A, (1, K), device=device)
+    z = normal_tensor(seed, S_E, (T, K), device=device)
+    c = 1.0 / math.sqrt(T * (0.88 ** 2 + 0.45 ** 2))
+    return to_bf16_rne((c * (0.88 * u * m + 0.45 * z)).to(torch.float32))
 
 
 def weights(wl: Workload, t: int = 0, device="cpu", rows=None) -> torch.Tensor:

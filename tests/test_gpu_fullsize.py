@@ -1,15 +1,18 @@
 """GPU parity at the workloads' full sizes, in the launch configuration the
 benchmark times: the attention-projection shape (T=8192, K=5120, N=10240,
 bf16 X), the MLP down-projection shape (T=8192, K=17408, N=5120, heavy-tailed
-bf16 X) and the streamed accumulation (8192-token chunks at K=5120).
+bf16 X) and the streamed accumulation (128 chunks of 8192 tokens at K=5120,
+then four weight tensors that share the Hessian).
 
 Where the oracle finishes in seconds it checks every output (Gram, storage,
-GPTQ codes/scales/qerr at K=5120).  Where it cannot, it checks outputs it can
-compute one by one (sampled Gram entries at K=17408; a block-diagonal Hessian of
-the full size whose U the oracle builds block by block) or properties that hold
-at any size: the projection onto the PSD cone is characterised by P >= 0,
-P - H >= 0 and <P, P - H> = 0, and is at least as close to H as the PSD Gram
-matrix it was stored from.
+projection and GPTQ codes/scales/qerr at K=5120).  At K=17408 it checks
+outputs it can compute one by one or in blocks: sampled Gram entries; GPTQ rows
+replayed under the oracle's U of the device's projected Hessian (the same
+stage input on both sides); the projection of a full-size block-diagonal
+stored Hessian whose blocks the oracle projects one by one; and properties
+that hold at any size: the projection onto the PSD cone is characterised by
+P >= 0, P - H >= 0 and <P, P - H> = 0, and is at least as close to H as the
+PSD Gram matrix it was stored from.
 """
 import numpy as np
 import pytest
@@ -104,6 +107,8 @@ def test_attn_projection_certificates(gq, orc, attn):
     assert np.array_equal(Pn, Pn.T)
     ok1, ok2, comp, change = _kkt_certificates(P, Hs, 1e-5)
     assert ok1 and ok2 and abs(comp) < 1e-3, (ok1, ok2, comp)
+    # no eigenvalue below -1e-6 mean(diag) (dataset card, "The fix": the PSD bar)
+    assert _eigen_floor(P, Hs, 1e-6)
     # no farther from the stored matrix than the pre-storage PSD Gram (a feasible point)
     Hs64 = _sym64(Hs.cpu().numpy())
     H32 = _sym64(H.cpu().numpy())
@@ -127,6 +132,27 @@ def test_attn_projection_matches_eigendecomposition(gq, attn):
     rel = np.linalg.norm(P.cpu().numpy().astype(np.float64) - Pex) / np.linalg.norm(Pex)
     print(f"attn5120 projection: relative Frobenius distance to the eigendecomposition {rel:.3e}")
     assert rel < 2e-7
+
+
+def test_attn_projection_matches_oracle(gq, orc, attn):
+    """The K=5120 projection against the oracle's own (dataset card, "The fix":
+    eigendecomposition, negative eigenvalues clipped to zero, rebuilt and
+    symmetrised; the oracle's Householder tridiagonalisation and implicit QR in
+    fp64), entry by entry, at the Hessian bar of 1e-5 relative Frobenius."""
+    wl, X, W, H, blob, Hs, P = attn
+    Po = orc.psd_project(Hs.cpu().numpy())
+    rel = _relF(P.cpu().numpy(), Po)
+    print(f"attn5120 projection: relative Frobenius distance to the oracle {rel:.3e}")
+    assert rel < 1e-5
+
+
+def _eigen_floor(P, Hs, eps):
+    """Cholesky certificate (LAPACK through torch, fp64) that every eigenvalue of
+    P is at least -eps * mean(diag Hs)."""
+    P64 = P.to(torch.float64)
+    mu = float(torch.diagonal(Hs).to(torch.float64).mean())
+    P64.diagonal().add_(eps * mu)
+    return int(torch.linalg.cholesky_ex(P64).info) == 0
 
 
 @pytest.fixture(scope="module")
@@ -157,6 +183,7 @@ def test_attn_gptq_full(gq, orc, attn, attn_U):
     rep = orc.gptq_replay(cg, sg, Wn, U, G)
     print(f"K=5120 code identity {ident:.6f}, replay {rep}")
     assert rep["inadmissible"] == 0 and rep["scale_mismatch"] == 0
+    assert sum(rep["flip_gap_hist"][4:]) == 0          # every accepted flip within 1e-4 of the tie
     assert ident >= 0.999
     qo = orc.qerr(oc, os_, Wn, impn)
     assert abs(q - qo) / qo < 1e-4
@@ -290,6 +317,9 @@ def test_mlp_projection_certificates(gq, mlp):
     assert torch.equal(Pc, Pc.T)
     ok1, ok2, comp, change = _kkt_certificates(P, Hs, 1e-5)
     assert ok1 and ok2 and abs(comp) < 1e-3, (ok1, ok2, comp)
+    # no eigenvalue below -1e-6 mean(diag) (dataset card, "The fix": the PSD bar);
+    # the bound of this heavy-tailed Hessian is about 1200 times its mean diagonal
+    assert _eigen_floor(P, Hs, 1e-6)
     Hs64 = Hs.to(torch.float64)
     H64 = H.to(torch.float64)
     Hsym = torch.tril(H64) + torch.tril(H64, -1).T          # the GPU Gram fills the lower triangle
@@ -325,10 +355,12 @@ def mlp_blockdiag(orc):
 def test_mlp_gptq_blockdiag_hessian(gq, orc, mlp_w, mlp_blockdiag, flags):
     """Full K=17408 launch configuration (N=5120, G=128) on the block-diagonal
     Hessian, plain and with static groups, NF4 or both; the oracle sweeps sampled
-    rows under its own U.  The plain sweep keeps 99.9% raw identity; the variants
-    must have every decision admissible and 99.9% of them identical given the
-    same history, and 99% raw identity (a tie flip on one of five 17408-wide rows
-    can move a few hundred later codes)."""
+    rows under its own U (64 rows: 1.1 M decisions).  Every decision must be
+    admissible and 99.9% of them identical given the same history.  The uniform
+    grid, with dynamic or static scales, keeps 99.9% raw identity; the NF4
+    variants are held to 99% (NF4's midpoints near zero are closer than the
+    uniform steps, so ties come more often, and each moves a few hundred later
+    codes of its 17408-wide row)."""
     wl = g.WORKLOADS["mlpdown17408"]
     K, N, G = wl.K, wl.N[0], wl.group
     W = mlp_w
@@ -337,7 +369,8 @@ def test_mlp_gptq_blockdiag_hessian(gq, orc, mlp_w, mlp_blockdiag, flags):
     scales = torch.empty(N, K // G, dtype=torch.float32, device=DEV)
     q = gq.gptq_quantize_ex(codes, scales, W.to(DEV), torch.from_numpy(Hd).to(DEV), None, G, 0.01, flags,
                             gq.workspace(gq.gptq_quantize_ex_workspace_size(N, K, G, flags), DEV))
-    rows = np.array([0, 1, 777, 2500, N - 1])
+    rows = np.unique(np.concatenate([[0, 1, 777, 2500, N - 1],
+                                     np.random.default_rng(flags).choice(N, 59, replace=False)]))
     cg = orc.unpack_codes(codes.cpu().numpy()[rows], K, flags=flags)
     sg = scales.cpu().numpy()[rows]
     Wn = W.numpy()
@@ -347,7 +380,7 @@ def test_mlp_gptq_blockdiag_hessian(gq, orc, mlp_w, mlp_blockdiag, flags):
     print(f"K=17408 block-diagonal, flags {flags}: identity {ident:.6f}, replay {rep}")
     assert rep["inadmissible"] == 0 and rep["scale_mismatch"] == 0
     assert rep["exact"] >= 0.999 * cg.size
-    assert ident >= (0.999 if flags == 0 else 0.99)
+    assert ident >= (0.99 if flags & orc.NF4 else 0.999)
     if flags & orc.STATIC_GROUPS:
         _, rs = orc.rtn(Wn[rows], G, flags=flags & orc.NF4)
         assert np.array_equal(sg, rs)
@@ -368,21 +401,136 @@ def test_mlp_gptq_diagonal_is_rtn(gq, orc, mlp_w):
     assert np.array_equal(scales.cpu().numpy(), rs)
 
 
-def test_mlp_gptq_projected_beats_rtn_on_output(gq, orc, mlp, mlp_w):
+@pytest.fixture(scope="module")
+def mlp_gptq(gq, mlp, mlp_w):
+    """The device's GPTQ of the K=17408 weights with its projected Hessian and
+    the stored diagonal as importance (computed once)."""
+    wl, X, H, blob, Hs, P = mlp
+    K, N, G = wl.K, wl.N[0], wl.group
+    imp = blob[: 4 * K].view(torch.float32)
+    codes = torch.empty(N, K // 2, dtype=torch.uint8, device=DEV)
+    scales = torch.empty(N, K // G, dtype=torch.float32, device=DEV)
+    q = gq.gptq_quantize(codes, scales, mlp_w.to(DEV), P, imp, G, wl.damp,
+                         gq.workspace(gq.gptq_quantize_workspace_size(N, K, G), DEV))
+    return codes.cpu().numpy(), scales.cpu().numpy(), q, imp.cpu().numpy().copy()
+
+
+def test_mlp_gptq_projected_matches_oracle(gq, orc, mlp, mlp_w, mlp_gptq):
+    """GPTQ on the projected K=17408 Hessian at damp 0.01 against the oracle:
+    its U of the same projected matrix (the literal route, one LAPACK primitive
+    per step, fp64), its sweep and replay of 64 sampled rows (1.1 M decisions).
+    No decision may be inadmissible, scales agree to 1e-5, raw code identity is at
+    least 99.9%, and the sampled rows' qerr of the device's codes is within 1e-4
+    of the oracle's own; the device's qerr over all rows equals the oracle's qerr
+    of the device's codes."""
+    wl, X, H, blob, Hs, P = mlp
+    K, N, G = wl.K, wl.N[0], wl.group
+    codes, scales, q, impn = mlp_gptq
+    st, U, mu = orc.gptq_U_lapack(P.cpu().numpy(), wl.damp)
+    assert st == orc.OK
+    Wn = mlp_w.numpy()
+    rows = np.sort(np.random.default_rng(17408).choice(N, 64, replace=False))
+    cg = orc.unpack_codes(codes[rows], K)
+    sg = scales[rows]
+    rep = orc.gptq_replay(cg, sg, Wn, U, G, rows=rows)
+    oc, os_ = orc.gptq_sweep(Wn, U, G, rows=rows)
+    ident = float((cg == oc).mean())
+    qg = orc.qerr(cg, sg, Wn[rows], impn)
+    qo = orc.qerr(oc, os_, Wn[rows], impn)
+    print(f"K=17408 projected: identity {ident:.6f} on 64 rows, replay {rep}, "
+          f"qerr rows device {qg:.6f} oracle {qo:.6f}")
+    assert rep["inadmissible"] == 0 and rep["scale_mismatch"] == 0
+    assert sum(rep["flip_gap_hist"][4:]) == 0
+    assert ident >= 0.999
+    assert abs(qg - qo) / qo < 1e-4
+    assert q == pytest.approx(orc.qerr(orc.unpack_codes(codes, K), scales, Wn, impn), rel=1e-6)
+
+
+def test_mlp_raw_stored_hessian_outcome(gq, mlp):
+    """The dataset card: at K=17408 the stored Hessian fails Cholesky at any
+    damping up to its cap, and projection is required.  The raw stored matrix's
+    outcome at damp 0.01 is reported, and the device's factor must agree with a
+    library Cholesky (LAPACK through torch, fp64) of the same damped matrix; the
+    projected one factors."""
+    wl, X, H, blob, Hs, P = mlp
+    K = wl.K
+    U = torch.empty(K, K, dtype=torch.float32, device=DEV)
+    ws = gq.workspace(gq.gptq_factor_workspace_size(K), DEV)
+    try:
+        gq.gptq_factor(U, Hs, 0.01, ws)
+        raw = "factors"
+    except gq.GQError as e:
+        assert e.status == gq.GQ_ERR_NOT_PD
+        raw = "NOT_PD"
+    A = Hs.to(torch.float64)
+    mu = float(torch.diagonal(A).mean())
+    A.diagonal().add_(0.01 * mu)
+    lib_ok = int(torch.linalg.cholesky_ex(A).info) == 0
+    del A
+    print(f"raw stored K=17408 Hessian at damp 0.01: {raw} (library Cholesky: "
+          f"{'factors' if lib_ok else 'not positive definite'})")
+    assert (raw == "factors") == lib_ok
+    gq.gptq_factor(U, P, 0.01, ws)
+
+
+@pytest.fixture(scope="module")
+def blockdiag_stored(orc):
+    """A full-size K=17408 stored Hessian that is block-diagonal: 17 blocks of
+    1024 channels, each the bf16-tril storage of the Gram of 512 tokens, so
+    rank-deficient and left with negative eigenvalues by the storage.  Even
+    blocks are strongly correlated (one factor shared by every channel, as on
+    the dataset card's tensor: off-diagonal entries near 0.8 of the diagonal,
+    hundreds of negative eigenvalues down to about -0.06 mean(diag)); odd
+    blocks are heavy-tailed (the MLP recipe, its own channel scales).  Its
+    projection is the block-wise projection, which the oracle computes block by
+    block."""
+    K, B = 17408, 1024
+    Hs = np.zeros((K, K), np.float32)
+    Po = np.zeros((K, K), np.float32)
+    for b in range(K // B):
+        Xb = g.common_mode_x(200 + b, 512, B) if b % 2 == 0 else g.heavy_tailed_x(100 + b, 512, B, 512)
+        Hb = orc.gram(Xb).astype(np.float32)
+        Hsb = orc.unpack_tril(orc.pack_tril(Hb), B)
+        Hs[b * B:(b + 1) * B, b * B:(b + 1) * B] = Hsb
+        Po[b * B:(b + 1) * B, b * B:(b + 1) * B] = orc.psd_project(Hsb)
+    return Hs, Po
+
+
+def test_blockdiag17408_projection_matches_oracle(gq, orc, blockdiag_stored):
+    """psd_project at K=17408 on the block-diagonal stored Hessian, every entry
+    against the oracle's block-wise projection at 1e-5 relative Frobenius (and
+    per block); entries off the blocks stay exactly zero."""
+    Hs, Po = blockdiag_stored
+    K, B = Hs.shape[0], 1024
+    Hd = torch.from_numpy(Hs).to(DEV)
+    P = Hd.clone()
+    gq.psd_project(P, gq.workspace(gq.psd_project_workspace_size(K), DEV))
+    Pn = P.cpu().numpy()
+    rel = _relF(Pn, Po)
+    per = [_relF(Pn[b * B:(b + 1) * B, b * B:(b + 1) * B], Po[b * B:(b + 1) * B, b * B:(b + 1) * B])
+           for b in range(K // B)]
+    off = Pn.copy()
+    for b in range(K // B):
+        off[b * B:(b + 1) * B, b * B:(b + 1) * B] = 0.0
+    neg = int((orc.eigvalsh(Hs[:B, :B]) < 0).sum())
+    print(f"block-diagonal K=17408 projection: relative Frobenius {rel:.3e} to the oracle, worst block "
+          f"{max(per):.3e}; {neg} negative eigenvalues in the first stored block")
+    assert rel < 1e-5 and max(per) < 1e-5
+    assert not off.any()
+    assert neg > 0
+
+
+def test_mlp_gptq_projected_beats_rtn_on_output(gq, orc, mlp, mlp_w, mlp_gptq):
     """GPTQ with the projected K=17408 Hessian at damp 0.01 (which the dataset
     card says needs the projection) factors, and its output error ||(W - Q) X||
     on a row sample is below round-to-nearest's."""
     wl, X, H, blob, Hs, P = mlp
     K, N, G = wl.K, wl.N[0], wl.group
     W = mlp_w
-    imp = blob[: 4 * K].view(torch.float32)
-    codes = torch.empty(N, K // 2, dtype=torch.uint8, device=DEV)
-    scales = torch.empty(N, K // G, dtype=torch.float32, device=DEV)
-    q = gq.gptq_quantize(codes, scales, W.to(DEV), P, imp, G, wl.damp,
-                         gq.workspace(gq.gptq_quantize_workspace_size(N, K, G), DEV))
+    codes, scales, q, _ = mlp_gptq
     rows = np.arange(0, N, 40)
-    cg = orc.unpack_codes(codes.cpu().numpy()[rows], K).astype(np.float64)
-    sg = scales.cpu().numpy()[rows].astype(np.float64)
+    cg = orc.unpack_codes(codes[rows], K).astype(np.float64)
+    sg = scales[rows].astype(np.float64)
     Wr = W.numpy()[rows].astype(np.float64)
     Qg = (cg.reshape(len(rows), -1, G) * sg[:, :, None]).reshape(len(rows), K)
     rc, rs = orc.rtn(W.numpy()[rows], G)
@@ -400,65 +548,136 @@ def test_stream_chunks_full_width(gq, orc):
     two halves with a host round trip of H in between: bitwise equal to the
     uninterrupted run, and equal to the oracle's sum on sampled entries."""
     wl = g.WORKLOADS["stream5120"]
-    small = g.Workload("stream5120", wl.T, wl.K, wl.N, wl.group, wl.damp, "bf16", True, 8, wl.seed)
     K = wl.K
-    chunks = [g.x_chunk(small, c) for c in range(small.chunks)]
+    chunks = [g.x_chunk(wl, c, device=DEV) for c in range(8)]
     H = torch.zeros(K, K, dtype=torch.float32, device=DEV)
     for X in chunks:
-        gq.hessian_accumulate(H, X.to(DEV))
+        gq.hessian_accumulate(H, X)
     H2 = torch.zeros(K, K, dtype=torch.float32, device=DEV)
     for X in chunks[:4]:
-        gq.hessian_accumulate(H2, X.to(DEV))
+        gq.hessian_accumulate(H2, X)
     H3 = H2.cpu().to(DEV)
     for X in chunks[4:]:
-        gq.hessian_accumulate(H3, X.to(DEV))
+        gq.hessian_accumulate(H3, X)
     torch.cuda.synchronize()
     assert torch.equal(H.cpu(), H3.cpu())
     rng = np.random.default_rng(1)
     I = rng.integers(0, K, 64)
     J = rng.integers(0, K, 64)
     I, J = np.maximum(I, J), np.minimum(I, J)
-    ref = sum(orc.gram_entries(X, I, J) for X in chunks)
+    ref = sum(orc.gram_entries(X.cpu(), I, J) for X in chunks)
     assert _relF(H.cpu().numpy()[I, J], ref) < 1e-5
 
 
-def test_stream_tensors_share_one_factor(gq, orc, attn, attn_U):
+@pytest.fixture(scope="module")
+def stream(gq, orc):
+    """The streamed recipe as specified: all 128 chunks of 8192 tokens (1,048,576
+    tokens at K=5120) accumulated on the device into one H, then stored, unpacked
+    and projected.  The chunks are generated on the device one at a time; the
+    columns the sampled Gram entries need are kept on the host for the oracle."""
+    wl = g.WORKLOADS["stream5120"]
+    K = wl.K
+    rng = np.random.default_rng(4)
+    I = np.concatenate([rng.integers(0, K, 60), [0, K - 1, K - 1, 2048]])
+    J = np.concatenate([rng.integers(0, K, 60), [0, 0, K - 1, 2047]])
+    I, J = np.maximum(I, J), np.minimum(I, J)
+    cols = np.unique(np.concatenate([I, J]))
+    pos = {c: k for k, c in enumerate(cols)}
+    Ic = np.array([pos[c] for c in I])
+    Jc = np.array([pos[c] for c in J])
+    colsd = torch.from_numpy(cols).to(DEV)
+    H = torch.zeros(K, K, dtype=torch.float32, device=DEV)
+    kept = []
+    for c in range(wl.chunks):
+        X = g.x_chunk(wl, c, device=DEV)
+        gq.hessian_accumulate(H, X)
+        kept.append(X.index_select(1, colsd).float().cpu())
+    torch.cuda.synchronize()
+    Xcols = torch.cat(kept).numpy()
+    del kept
+    blob = torch.empty(gq.hessian_tril_bytes(K), dtype=torch.uint8, device=DEV)
+    gq.hessian_pack_tril(blob, H)
+    Hs = torch.empty(K, K, dtype=torch.float32, device=DEV)
+    gq.hessian_unpack_tril(Hs, blob)
+    P = Hs.clone()
+    gq.psd_project(P, gq.workspace(gq.psd_project_workspace_size(K), DEV))
+    torch.cuda.synchronize()
+    return wl, H, blob, Hs, P, (I, J, Ic, Jc, Xcols)
+
+
+def test_stream_gram_all_chunks(gq, orc, stream):
+    """The 128-chunk statistic equals the sum of the chunks' Gram matrices
+    (AtomicChat GGUF page, "The importance matrix": a sum over chunks) on sampled
+    entries, each summed by the oracle over all 1,048,576 tokens; mean(diag H)
+    is about 1 by the recipe's scaling."""
+    wl, H, blob, Hs, P, (I, J, Ic, Jc, Xcols) = stream
+    assert Xcols.shape[0] == wl.T * wl.chunks
+    ref = orc.gram_entries(Xcols, Ic, Jc)
+    got = H.cpu().numpy()[I, J]
+    rel = _relF(got, ref)
+    print(f"stream Gram over 128 chunks: relative Frobenius {rel:.3e} on {len(I)} sampled entries")
+    assert rel < 1e-5
+    d = torch.diagonal(H).to(torch.float64)
+    assert abs(float(d.mean()) - 1.0) < 0.05
+
+
+def test_stream_storage_and_projection(gq, orc, stream):
+    """The 128-chunk Hessian's storage is bit-exact against the oracle's, and its
+    projection passes the projection certificates and the eigenvalue floor."""
+    wl, H, blob, Hs, P, _ = stream
+    ref = orc.pack_tril(H.cpu().numpy())
+    assert np.array_equal(blob.cpu().numpy(), ref)
+    assert np.array_equal(Hs.cpu().numpy().view(np.uint32), orc.unpack_tril(ref, wl.K).view(np.uint32))
+    ok1, ok2, comp, change = _kkt_certificates(P, Hs, 1e-5)
+    assert ok1 and ok2 and abs(comp) < 1e-3, (ok1, ok2, comp)
+    assert change < 0.00391
+    assert _eigen_floor(P, Hs, 1e-6)
+
+
+def test_stream_tensors_share_one_factor(gq, orc, stream):
     """The four weight tensors of the streamed recipe (N = 5120, 10240, 1024 and
-    1024 rows at K=5120) share one Hessian: gptq_factor runs once and gptq_sweep
-    once per tensor under that U.  On 96 sampled rows of each tensor, the
-    oracle's replay under its own U of the same projected Hessian finds every
-    decision admissible and 99.9% of them identical given the same history; raw
-    identity with the oracle's own sweep is held to 99% (a single legitimate tie
-    flip moves a few hundred later codes of its 5120-wide row).  The last
-    tensor's codes, scales and qerr equal gptq_quantize's bytes."""
-    wl, X, W0, H, blob, Hs, P = attn
-    sw = g.WORKLOADS["stream5120"]
-    K, G = sw.K, sw.group
+    1024 rows at K=5120) share the 128-chunk Hessian: gptq_factor runs once on
+    its projection and gptq_sweep once per tensor under that U.  The oracle's U
+    of the same projected Hessian replays every row of the two 1024-row tensors
+    and 1024 sampled rows of the others (4096 rows, 21 M decisions): no decision
+    inadmissible, scales within 1e-5, raw code identity with the oracle's own
+    sweep at least 99.9% per tensor, the rows' qerr within 1e-4 of the oracle's
+    own, and the device's qerr over all rows equal to the oracle's qerr of the
+    device's codes.  The last tensor's codes, scales and qerr equal
+    gptq_quantize's bytes."""
+    wl, H, blob, Hs, P, _ = stream
+    K, G = wl.K, wl.group
+    st, Uo, _ = orc.gptq_U(P.cpu().numpy(), wl.damp)
+    assert st == orc.OK
     U = torch.empty(K, K, dtype=torch.float32, device=DEV)
-    gq.gptq_factor(U, P, sw.damp, gq.workspace(gq.gptq_factor_workspace_size(K), DEV))
+    gq.gptq_factor(U, P, wl.damp, gq.workspace(gq.gptq_factor_workspace_size(K), DEV))
     imp = blob[: 4 * K].view(torch.float32)
     impn = imp.cpu().numpy().copy()
-    for t, N in enumerate(sw.N):
-        W = g.weights(sw, t)
-        Wd = W.to(DEV)
+    for t, N in enumerate(wl.N):
+        W = g.weights(wl, t, device=DEV)
         codes = torch.empty(N, K // 2, dtype=torch.uint8, device=DEV)
         scales = torch.empty(N, K // G, dtype=torch.float32, device=DEV)
         ws = gq.workspace(gq.gptq_sweep_workspace_size(N, K, G), DEV)
-        q = gq.gptq_sweep(codes, scales, Wd, U, imp, G, ws)
-        Wn = W.numpy()
-        rows = np.sort(np.random.default_rng(t).choice(N, 96, replace=False))
-        cg = orc.unpack_codes(codes.cpu().numpy()[rows], K)
-        sg = scales.cpu().numpy()[rows]
-        rep = orc.gptq_replay(cg, sg, Wn, attn_U, G, rows=rows)
-        oc, _ = orc.gptq_sweep(Wn, attn_U, G, rows=rows)
+        q = gq.gptq_sweep(codes, scales, W, U, imp, G, ws)
+        Wn = W.cpu().numpy()
+        rows = np.arange(N) if N <= 1024 else np.sort(np.random.default_rng(t).choice(N, 1024, replace=False))
+        call = orc.unpack_codes(codes.cpu().numpy(), K)
+        sall = scales.cpu().numpy()
+        cg, sg = call[rows], sall[rows]
+        rep = orc.gptq_replay(cg, sg, Wn, Uo, G, rows=rows)
+        oc, os_ = orc.gptq_sweep(Wn, Uo, G, rows=rows)
         ident = float((cg == oc).mean())
-        print(f"stream tensor {t} (N={N}): identity {ident:.6f}, replay {rep}, qerr {q:.5f}")
+        qg = orc.qerr(cg, sg, Wn[rows], impn)
+        qo = orc.qerr(oc, os_, Wn[rows], impn)
+        print(f"stream tensor {t} (N={N}): identity {ident:.6f} on {len(rows)} rows, replay {rep}, "
+              f"qerr {q:.5f}, rows device {qg:.6f} oracle {qo:.6f}")
         assert rep["inadmissible"] == 0 and rep["scale_mismatch"] == 0
-        assert rep["exact"] >= 0.999 * cg.size and ident >= 0.99
-        assert q == pytest.approx(orc.qerr(orc.unpack_codes(codes.cpu().numpy(), K), scales.cpu().numpy(), Wn, impn),
-                                  rel=1e-6)
+        assert sum(rep["flip_gap_hist"][4:]) == 0
+        assert ident >= 0.999
+        assert abs(qg - qo) / qo < 1e-4
+        assert q == pytest.approx(orc.qerr(call, sall, Wn, impn), rel=1e-6)
     c2 = torch.empty_like(codes)
     s2 = torch.empty_like(scales)
-    q2 = gq.gptq_quantize(c2, s2, Wd, P, imp, G, sw.damp,
+    q2 = gq.gptq_quantize(c2, s2, W, P, imp, G, wl.damp,
                           gq.workspace(gq.gptq_quantize_workspace_size(N, K, G), DEV))
     assert torch.equal(c2, codes) and torch.equal(s2, scales) and q2 == q

@@ -308,6 +308,54 @@ def test_gptq_diagonal_hessian_is_rtn_bitwise(gq, orc):
     assert np.array_equal(scales, rs)
 
 
+def _tiny_scale_weights():
+    """Rows whose groups need the exact power-of-two guard of the quotient: a
+    group of weights around 1e-30 (scale near 2^-102, where the correction
+    step's remainder would underflow), a group of zeros and one subnormal value
+    (a subnormal scale, whose reciprocal overflows), an all-subnormal group, and
+    an ordinary group beside them."""
+    rng = np.random.default_rng(7)
+    W = np.zeros((4, 256), np.float32)
+    W[:, 0:64] = (rng.uniform(-1, 1, (4, 64)) * 1e-30).astype(np.float32)
+    W[:, 64:128] = 0.0
+    W[:, 64 + 5] = np.float32(3e-39)                  # subnormal
+    W[1, 64 + 9] = np.float32(-2e-39)
+    W[:, 128:192] = (rng.uniform(-1, 1, (4, 64)) * 1e-39).astype(np.float32)
+    W[:, 192:256] = rng.uniform(-1, 1, (4, 64)).astype(np.float32)
+    return W
+
+
+@pytest.mark.parametrize("flags", [0, 1])
+def test_gptq_tiny_scales_are_rtn_bitwise(gq, orc, flags):
+    """Diagonal H reduces GPTQ to round to nearest bit for bit also where the
+    scale is tiny or subnormal.  The expected codes are checked on the CPU first:
+    the subnormal value is the group's maximum, so it takes code 7 and the zeros
+    beside it take 0; the 1e-30 group spans the whole grid."""
+    W = _tiny_scale_weights()
+    rc, rs = orc.rtn(W, 64)
+    assert (rs[:, 1] > 0).all() and (rs[:, 1] < np.float32(1.2e-38)).all()     # subnormal scales
+    assert (rc[:, 64 + 5] == 7).all() and (rc[0, 64:128][np.arange(64) != 5] == 0).all()
+    assert rc[:, 0:64].min() == -7 and rc[:, 0:64].max() == 7
+    assert (rs[:, 0] < 2.0 ** -60).all()
+    d = np.exp(np.random.default_rng(1).standard_normal(256)).astype(np.float32)
+    if flags:
+        codes, scales, _ = _gpu_gptq_ex(gq, W, np.diag(d), 64, flags)
+    else:
+        codes, scales, _ = _gpu_gptq(gq, W, np.diag(d), 64, 0.01, want_qerr=False)
+    assert np.array_equal(scales, rs)
+    assert np.array_equal(orc.unpack_codes(codes, 256), rc)
+
+
+def _gpu_gptq_ex(gq, W, H, G, flags, damp=0.01):
+    N, K = W.shape
+    c = torch.empty(N, K // 2, dtype=torch.uint8, device=DEV)
+    s = torch.empty(N, K // G, dtype=torch.float32, device=DEV)
+    ws = gq.workspace(gq.gptq_quantize_ex_workspace_size(N, K, G, flags), DEV)
+    q = gq.gptq_quantize_ex(c, s, torch.from_numpy(W).to(DEV), torch.from_numpy(H).to(DEV), None, G, damp,
+                            flags, ws, want_qerr=False)
+    return c.cpu().numpy(), s.cpu().numpy(), q
+
+
 def test_gptq_qerr_request_leaves_codes_identical(gq, orc):
     wl = g.WORKLOADS["tiny"]
     W = g.weights(wl).numpy()

@@ -75,6 +75,28 @@ def test_U_literal_route_equals_reverse_cholesky_inverse(orc):
     np.testing.assert_allclose(U, np.linalg.inv(R), rtol=1e-9, atol=1e-12)
 
 
+def test_U_lapack_route_equals_plain_route(orc):
+    """gptq_U_lapack (the literal route with one LAPACK primitive per step, for
+    the largest sizes) against gptq_U's plain loops on a correlated, ill-
+    conditioned stored-style Hessian, and the same statuses on bad inputs."""
+    wl = g.WORKLOADS["stored1024"]
+    X = g.x_chunk(wl, tokens=700)            # T < K: singular before damping
+    H = _gram32(orc, X)
+    st, U, mu = orc.gptq_U(H, 0.01)
+    st2, U2, mu2 = orc.gptq_U_lapack(H, 0.01)
+    assert st == st2 == orc.OK and mu == pytest.approx(mu2, rel=1e-14)
+    assert np.array_equal(U2, np.triu(U2))
+    rel = np.linalg.norm(U2 - U) / np.linalg.norm(U)
+    assert rel < 1e-9, rel
+    Hn = H.copy(); Hn[5, 3] = np.nan
+    assert orc.gptq_U_lapack(Hn, 0.01)[0] == orc.ERR_NONFINITE
+    Hu = H.copy(); Hu[3, 5] = np.nan           # upper triangle is never read
+    assert orc.gptq_U_lapack(Hu, 0.01)[0] == orc.OK
+    assert orc.gptq_U_lapack(np.zeros((8, 8), np.float32), 0.01)[0] == orc.ERR_NO_CALIBRATION
+    Hi = np.eye(6, dtype=np.float32); Hi[4, 4] = -3.0
+    assert orc.gptq_U_lapack(Hi, 0.01)[0] == orc.ERR_NOT_PD == orc.gptq_U(Hi, 0.01)[0]
+
+
 # ------------------------------------------------------------------ GPTQ sweep
 def _obq_reference(W, H, G, damp):
     """Sequential optimal-brain quantisation with freshly inverted Hessians of the
@@ -261,3 +283,25 @@ def test_replay_accepts_own_codes_and_flags_wrong_ones(orc):
     assert r["inadmissible"] >= 1
     rc, rs = orc.rtn(W, 32)                         # RTN codes are not GPTQ codes
     assert orc.gptq_replay(rc, rs, W, U, 32)["inadmissible"] > 100
+
+
+def test_replay_flip_gap_histogram(orc):
+    """With a diagonal H (no feedback) and group scale 1, candidate codes that take
+    the other neighbour of an exact tie (2.5), of a value 5e-5 of a step from one
+    (3.49995) and of a value 5e-4 from one (1.4995) are counted as tie flips in
+    the bins [0, 1e-7), [1e-5, 1e-4) and [1e-4, 1e-3); with delta = 1e-4 the last
+    one is inadmissible."""
+    K, G = 32, 32
+    W = np.zeros((1, K), np.float32)
+    W[0, 0] = 7.0                                      # scale 7 / 7 = 1
+    W[0, 3], W[0, 9], W[0, 20] = 2.5, 3.49995, 1.4995
+    U = np.eye(K)
+    codes, scales = orc.gptq_sweep(W, U, G)
+    assert scales[0, 0] == 1.0 and codes[0, 3] == 2 and codes[0, 9] == 3 and codes[0, 20] == 1
+    cand = codes.copy()
+    cand[0, 3], cand[0, 9], cand[0, 20] = 3, 4, 2
+    r = orc.gptq_replay(cand, scales, W, U, G)
+    assert r["tie_flips"] == 3 and r["inadmissible"] == 0
+    assert r["flip_gap_hist"] == [1, 0, 0, 1, 1, 0]
+    r = orc.gptq_replay(cand, scales, W, U, G, delta=1e-4)
+    assert r["tie_flips"] == 2 and r["inadmissible"] == 1
