@@ -317,6 +317,24 @@ int rtn_quantize_ex(uint8_t *codes, float *scales, double *qerr_out, const float
                     hipStream_t stream);
 
 /*
+ * rtn_quantize_noalloc -- rtn_quantize_ex with no workspace argument, for
+ * callers that cannot allocate device memory (code that must not call
+ * hipMalloc, such as tight serving loops or harnesses that forbid it).  Its
+ * status word and qerr's partial sums live in a fixed scratch array of
+ * GQ_NOALLOC_SCRATCH_BYTES inside the library, one per device, held from its
+ * first use on that device until the process ends; the call allocates nothing
+ * and otherwise does exactly what rtn_quantize_ex does (same kernels, codes,
+ * scales and qerr).  rtn_quantize_workspace_size is at most 49 KiB for any
+ * N, K and group, so every size rtn_quantize_ex takes fits; a size that would
+ * not is refused with GQ_ERR_INVALID_ARG.  Calls on one device share its
+ * scratch: calls that overlap on the same device (other streams or threads)
+ * race and must be serialised by the caller.  Synchronises `stream`.
+ */
+#define GQ_NOALLOC_SCRATCH_BYTES 65536
+int rtn_quantize_noalloc(uint8_t *codes, float *scales, double *qerr_out, const float *W, const float *imp,
+                         int64_t N, int64_t K, int64_t group, uint32_t flags, hipStream_t stream);
+
+/*
  * HFQM calibration package (.calib.hfq), the container that carries stored
  * Hessians and importance vectors (hipfire-calib-data dataset card, ".calib.hfq —
  * HFQM calibration package").  Little-endian: a 32-byte header ("HFQM", version

@@ -34,6 +34,7 @@ EXPORTS = (
     "gptq_sweep_ex", "gptq_quantize_ex", "rtn_quantize_ex", "gq_nf4_levels", "gptq_quantize_ex_workspace_size",
     "hfqm_write", "hfqm_read_header", "hfqm_read_entry", "hfqm_read_payload",
     "hadamard_rotate_rows", "hadamard_rotate_hessian_workspace_size", "hadamard_rotate_hessian",
+    "rtn_quantize_noalloc",
 )
 
 
@@ -80,6 +81,7 @@ def lib() -> ctypes.CDLL:
             "rtn_quantize_workspace_size": (SZ, [I64, I64, I64]),
             "rtn_quantize": (I, [P, P, P, P, P, I64, I64, I64, P, SZ, P]),
             "rtn_quantize_ex": (I, [P, P, P, P, P, I64, I64, I64, U32, P, SZ, P]),
+            "rtn_quantize_noalloc": (I, [P, P, P, P, P, I64, I64, I64, U32, P]),
             "gptq_sweep_ex": (I, [P, P, P, P, P, P, I64, I64, I64, U32, P, SZ, P]),
             "gptq_quantize_ex": (I, [P, P, P, P, P, P, I64, I64, I64, F, U32, P, SZ, P]),
             "gq_nf4_levels": (None, [P]),
@@ -283,6 +285,25 @@ def rtn_quantize_ex(codes, scales, W, imp, group: int, flags: int, ws, want_qerr
     _check(lib().rtn_quantize_ex(_ptr(codes), _ptr(scales), ctypes.byref(q) if want_qerr else None,
                                  _ptr(W), _ptr(imp), N, K, group, flags, _ptr(ws), ws.numel(), _stream(W)),
            "rtn_quantize_ex")
+    return q.value if want_qerr else None
+
+
+NOALLOC_SCRATCH_BYTES = 65536      # GQ_NOALLOC_SCRATCH_BYTES of include/gq.h
+
+
+def rtn_quantize_noalloc(codes, scales, W, imp, group: int, flags: int = 0, want_qerr: bool = True):
+    """rtn_quantize_ex without a workspace (the library's fixed per-device
+    scratch; calls that overlap on one device race); returns qerr (or None)."""
+    N, K = W.shape
+    _need(W, "W", torch.float32)
+    _need(codes, "codes", torch.uint8, N * (K // 2))
+    _need(scales, "scales", torch.float32, N * (K // max(group, 1)))
+    if imp is not None:
+        _need(imp, "imp", torch.float32, K)
+    q = ctypes.c_double(0.0)
+    _check(lib().rtn_quantize_noalloc(_ptr(codes), _ptr(scales), ctypes.byref(q) if want_qerr else None,
+                                      _ptr(W), _ptr(imp), N, K, group, flags, _stream(W)),
+           "rtn_quantize_noalloc")
     return q.value if want_qerr else None
 
 

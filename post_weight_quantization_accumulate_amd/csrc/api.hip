@@ -5,6 +5,7 @@
 #include <cmath>
 #include <vector>
 #include <algorithm>
+#include <mutex>
 
 #include "gq.h"
 #include "gq_internal.h"
@@ -922,21 +923,24 @@ size_t rtn_quantize_workspace_size(int64_t N, int64_t K, int64_t group)
     return c.off;
 }
 
-int rtn_quantize_ex(uint8_t *codes, float *scales, double *qerr_out, const float *W, const float *imp, int64_t N,
-                    int64_t K, int64_t group, uint32_t flags, void *ws, size_t ws_bytes, hipStream_t stream)
+static int check_rtn_args(const uint8_t *codes, const float *scales, const float *W, int64_t N, int64_t K,
+                          int64_t group, uint32_t flags)
 {
-    g_last_error.clear();
     if (flags & ~(uint32_t)(GQ_STATIC_GROUPS | GQ_NF4)) return fail(GQ_ERR_INVALID_ARG, "unknown flag bits");
-    const int mode = mode_of(flags);
     if (!codes || !scales || !W) return fail(GQ_ERR_INVALID_ARG, "null required pointer");
     if (N < 1) return fail(GQ_ERR_INVALID_ARG, "N must be >= 1");
     if (K < 2 || (K & 1)) return fail(GQ_ERR_INVALID_ARG, "K must be even and >= 2 (two codes per byte)");
     if (!valid_group(group, K))
         return fail(GQ_ERR_INVALID_ARG, "group must be a power of two <= 128 that divides K");
-    if (!ws) return fail(GQ_ERR_INVALID_ARG, "null workspace");
-    if (ws_bytes < rtn_quantize_workspace_size(N, K, group)) return fail(GQ_ERR_INVALID_ARG, "workspace too small");
-    Carver cv(ws);
-    const RtnWs w = carve_rtn(cv, N, K);
+    return GQ_OK;
+}
+
+// The round-to-nearest pack over a workspace already carved (status word,
+// qerr's scalars and partial sums); the status word is cleared first.
+static int run_rtn(uint8_t *codes, float *scales, double *qerr_out, const float *W, const float *imp, int64_t N,
+                   int64_t K, int64_t group, uint32_t flags, const RtnWs &w, hipStream_t stream)
+{
+    const int mode = mode_of(flags);
     GQ_HIP(launch_fill_u32(w.sc.status, 4, 0u, stream), "fill");
     if (imp) GQ_HIP(launch_check_finite(imp, K, w.sc.status, stream), "check imp");
     int64_t nparts = 0;
@@ -956,10 +960,70 @@ int rtn_quantize_ex(uint8_t *codes, float *scales, double *qerr_out, const float
     return GQ_OK;
 }
 
+int rtn_quantize_ex(uint8_t *codes, float *scales, double *qerr_out, const float *W, const float *imp, int64_t N,
+                    int64_t K, int64_t group, uint32_t flags, void *ws, size_t ws_bytes, hipStream_t stream)
+{
+    g_last_error.clear();
+    int rc = check_rtn_args(codes, scales, W, N, K, group, flags);
+    if (rc) return rc;
+    if (!ws) return fail(GQ_ERR_INVALID_ARG, "null workspace");
+    if (ws_bytes < rtn_quantize_workspace_size(N, K, group)) return fail(GQ_ERR_INVALID_ARG, "workspace too small");
+    Carver cv(ws);
+    const RtnWs w = carve_rtn(cv, N, K);
+    return run_rtn(codes, scales, qerr_out, W, imp, N, K, group, flags, w, stream);
+}
+
 int rtn_quantize(uint8_t *codes, float *scales, double *qerr_out, const float *W, const float *imp, int64_t N,
                  int64_t K, int64_t group, void *ws, size_t ws_bytes, hipStream_t stream)
 {
     return rtn_quantize_ex(codes, scales, qerr_out, W, imp, N, K, group, 0u, ws, ws_bytes, stream);
+}
+
+}  // extern "C"
+
+// Scratch of rtn_quantize_noalloc, in place of a caller workspace: one copy per
+// device, held until the process ends.  Its name is a host-side stand-in; the
+// device address comes from hipGetSymbolAddress, looked up once per device
+// with that device current and kept in g_scratch.
+static __device__ __align__(256) unsigned char scratch[GQ_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+std::mutex g_scratch_mu;
+std::vector<void *> g_scratch;          // by device ordinal; nullptr until looked up
+
+int scratch_for_current_device(void **out)
+{
+    int dev = 0;
+    GQ_HIP(hipGetDevice(&dev), "current device");
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if ((size_t)dev >= g_scratch.size()) g_scratch.resize((size_t)dev + 1, nullptr);
+    if (!g_scratch[(size_t)dev]) {
+        void *p = nullptr;
+        GQ_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "scratch address");
+        if (!p) return fail(GQ_ERR_HIP, "scratch address: null");
+        g_scratch[(size_t)dev] = p;
+    }
+    *out = g_scratch[(size_t)dev];
+    return GQ_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int rtn_quantize_noalloc(uint8_t *codes, float *scales, double *qerr_out, const float *W, const float *imp,
+                         int64_t N, int64_t K, int64_t group, uint32_t flags, hipStream_t stream)
+{
+    g_last_error.clear();
+    int rc = check_rtn_args(codes, scales, W, N, K, group, flags);
+    if (rc) return rc;
+    if (rtn_quantize_workspace_size(N, K, group) > (size_t)GQ_NOALLOC_SCRATCH_BYTES)
+        return fail(GQ_ERR_INVALID_ARG, "needs more scratch than the library's fixed scratch holds");
+    void *ws = nullptr;
+    rc = scratch_for_current_device(&ws);
+    if (rc) return rc;
+    Carver cv(ws);
+    const RtnWs w = carve_rtn(cv, N, K);
+    return run_rtn(codes, scales, qerr_out, W, imp, N, K, group, flags, w, stream);
 }
 
 size_t gptq_quantize_workspace_size(int64_t N, int64_t K, int64_t group)

@@ -37,6 +37,9 @@ def test_size_queries_are_host_only():
     assert gq.hessian_tril_bytes(0) == 0
     assert gq.psd_project_workspace_size(1024) >= 4 * 1024 * 1024 * 8
     assert gq.gptq_quantize_workspace_size(64, 128, 32) > gq.gptq_sweep_workspace_size(64, 128, 32)
+    # every round-to-nearest workspace fits the fixed scratch of rtn_quantize_noalloc
+    for N, K, G in [(1, 2, 1), (10240, 5120, 128), (5120, 17408, 128), (1 << 20, 8192, 1), (7, 130, 2)]:
+        assert gq.rtn_quantize_workspace_size(N, K, G) <= gq.NOALLOC_SCRATCH_BYTES
 
 
 @pytest.mark.skipif(not os.path.exists(gq.LIB_PATH), reason="libgq.so not built")
