@@ -9,11 +9,16 @@ resident in HBM:
        importance = the stored exact diagonal).
 gptq_factor + gptq_sweep is exactly gptq_quantize split in two so each half is
 timed on its own.  The headline value is weights quantised per second of whole
-steps, N*K / step time.  Per-stage times, the Hessian TFLOP/s against the bf16
-matrix-core peak, and the dominant kernel's roofline are reported alongside; the
-CPU oracle is timed on a bounded sample of the same workload on the host cores.
+steps, N*K / step time, on the attention shape (T=8192, K=5120, N=10240).
+Per-stage times, the Hessian TFLOP/s against the bf16 matrix-core peak, and the
+dominant kernel's roofline are reported alongside.  Two more blocks of the same
+JSON line time the same path on the MLP down-projection shape (K=17408,
+"k17408") and on the 128-chunk streamed recipe with its four weight tensors
+("stream"); the CPU oracle runs one whole step of the headline workload on the
+host cores.
 
 Usage: python bench.py [--gpus 1] [--steps 5] [--warmup 2] [--workload attn5120]
+                       [--no-k17408] [--no-stream] [--no-cpu-baseline]
 """
 from __future__ import annotations
 
@@ -69,43 +74,169 @@ def parse():
     p.add_argument("--warmup", type=int, default=2)
     p.add_argument("--workload", default="attn5120", choices=["attn5120", "mlpdown17408", "stored1024"])
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-k17408", action="store_true", help="skip the K=17408 block")
+    p.add_argument("--no-stream", action="store_true", help="skip the 128-chunk streamed block")
+    p.add_argument("--extra-steps", type=int, default=2, help="timed steps of the K=17408 and stream blocks")
     return p.parse_args()
 
 
 def cpu_baseline(wl, X, W):
-    """The CPU oracle on a bounded sample: the same recipe restricted to the first
-    Ks channels, Ts tokens and Ns rows, each stage timed and scaled to the full
-    workload by its cost order (Gram T*K^2, storage K^2, PSD and U K^3, sweep
-    N*K^2, qerr N*K)."""
+    """The CPU oracle on the whole workload: every stage of one step (Gram of the
+    T x K chunk, storage, PSD projection, U, the sweep of all N rows, qerr), timed
+    on the host's cores with nothing scaled or extrapolated."""
     import numpy as np
     import oracle
-    Ks = min(wl.K, 3072)
-    Ts = wl.T
-    Ns = min(wl.N[0], 3072)
-    Xs = X[:Ts, :Ks].float().cpu().numpy()
-    Ws = W[:Ns, :Ks].cpu().numpy()
-    G = wl.group
+    Xs = X.float().cpu().numpy()
+    Ws = W.cpu().numpy()
+    K, G = wl.K, wl.group
     t = {}
     t0 = time.perf_counter(); H = oracle.gram(Xs).astype(np.float32); t["gram"] = time.perf_counter() - t0
-    t0 = time.perf_counter(); blob = oracle.pack_tril(H); Hs = oracle.unpack_tril(blob, Ks)
+    del Xs
+    t0 = time.perf_counter(); blob = oracle.pack_tril(H); Hs = oracle.unpack_tril(blob, K)
     t["storage"] = time.perf_counter() - t0
     t0 = time.perf_counter(); P = oracle.psd_project(Hs); t["psd"] = time.perf_counter() - t0
     t0 = time.perf_counter(); st, U, _ = oracle.gptq_U(P, wl.damp); t["factor"] = time.perf_counter() - t0
-    t0 = time.perf_counter(); c, s = oracle.gptq_sweep(Ws, U, G); t["sweep"] = time.perf_counter() - t0
-    t0 = time.perf_counter(); oracle.qerr(c, s, Ws, blob[:4 * Ks].view(np.float32)); t["qerr"] = time.perf_counter() - t0
-    r = wl.K / Ks
-    full = (t["gram"] * (wl.T / Ts) * r * r + t["storage"] * r * r + (t["psd"] + t["factor"]) * r ** 3
-            + t["sweep"] * (wl.N[0] / Ns) * r * r + t["qerr"] * (wl.N[0] / Ns) * r)
+    t0 = time.perf_counter(); c, sc = oracle.gptq_sweep(Ws, U, G); t["sweep"] = time.perf_counter() - t0
+    t0 = time.perf_counter(); oracle.qerr(c, sc, Ws, blob[:4 * K].view(np.float32)); t["qerr"] = time.perf_counter() - t0
+    full = sum(t.values())
     return {
         "value": wl.N[0] * wl.K / full,
         "unit": "weights/s",
         "cores": oracle.num_threads(),
         "kind": "oracle",
-        "sample": (f"oracle pipeline on the first {Ks} channels, {Ts} tokens, {Ns} weight rows of "
-                   f"this workload ({sum(t.values()):.1f} s of CPU work); each stage scaled to "
-                   f"T={wl.T}, K={wl.K}, N={wl.N[0]} by its cost order"),
-        "est_step_s": full,
-        "sample_stage_s": {k: round(v, 4) for k, v in t.items()},
+        "sample": (f"one whole step of this workload (T={wl.T}, K={wl.K}, N={wl.N[0]}), every stage "
+                   f"run by the oracle, nothing scaled"),
+        "step_s": full,
+        "stage_s": {k: round(v, 4) for k, v in t.items()},
+    }
+
+
+STAGES = ["accumulate", "pack", "unpack", "psd", "factor", "sweep"]
+
+
+def progress(msg):
+    print(f"bench: {msg}", file=sys.stderr, flush=True)
+
+
+def run_path(gq, torch, wl, chunks, Ws, dev, steps, warmup):
+    """Time whole steps of the path: zero H, accumulate every chunk (one
+    hessian_accumulate_chunks call when there are several), pack, unpack,
+    project, factor once, sweep every weight tensor under that U (qerr with the
+    stored diagonal as importance).  Stage times come from torch events on the
+    current stream; psd_project's product launches are timed by the library
+    with HIP events on the same stream."""
+    K, G, damp = wl.K, wl.group, wl.damp
+    H = torch.empty(K, K, dtype=torch.float32, device=dev)
+    blob = torch.empty(gq.hessian_tril_bytes(K), dtype=torch.uint8, device=dev)
+    Hs = torch.empty(K, K, dtype=torch.float32, device=dev)
+    U = torch.empty(K, K, dtype=torch.float32, device=dev)
+    outs = [(torch.empty(W.shape[0], K // 2, dtype=torch.uint8, device=dev),
+             torch.empty(W.shape[0], K // G, dtype=torch.float32, device=dev)) for W in Ws]
+    ws_psd = gq.workspace(gq.psd_project_workspace_size(K), dev)
+    ws_fac = gq.workspace(gq.gptq_factor_workspace_size(K), dev)
+    ws_swp = gq.workspace(max(gq.gptq_sweep_workspace_size(W.shape[0], K, G) for W in Ws), dev)
+    imp = blob[: 4 * K].view(torch.float32)          # stored exact diagonal of H
+    ev = {s: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for s in STAGES}
+    acc = {s: 0.0 for s in STAGES}
+    qerr = [None] * len(Ws)
+
+    def sweeps():
+        for t, (W, (c, sc)) in enumerate(zip(Ws, outs)):
+            qerr[t] = gq.gptq_sweep(c, sc, W, U, imp, G, ws_swp)
+
+    ws_acc = (gq.workspace(max(gq.hessian_accumulate_chunks_workspace_size(K, len(chunks)), 1), dev)
+              if len(chunks) > 1 else None)
+
+    def accumulate():
+        if len(chunks) > 1:
+            gq.hessian_accumulate_chunks(H, chunks, ws_acc)
+        else:
+            gq.hessian_accumulate(H, chunks[0])
+
+    def step(record):
+        def run(name, fn):
+            if record:
+                ev[name][0].record()
+            fn()
+            if record:
+                ev[name][1].record()
+        H.zero_()
+        run("accumulate", accumulate)
+        run("pack", lambda: gq.hessian_pack_tril(blob, H))
+        run("unpack", lambda: gq.hessian_unpack_tril(Hs, blob))
+        run("psd", lambda: gq.psd_project(Hs, ws_psd))
+        run("factor", lambda: gq.gptq_factor(U, Hs, damp, ws_fac))
+        run("sweep", sweeps)
+        if record:
+            torch.cuda.synchronize()
+            for s in STAGES:
+                acc[s] += ev[s][0].elapsed_time(ev[s][1])
+
+    for _ in range(warmup):
+        step(False)
+    torch.cuda.synchronize()
+    # psd_project brackets each launch of its product kernel with HIP events on
+    # this stream (two event records per launch)
+    gq.gq_set_timing(True)
+    prod = {"launches": 0, "ms": 0.0, "kernel": ""}
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step(True)
+        n_l, ms_l, name = gq.psd_project_last_timing()
+        prod["launches"] += n_l
+        prod["ms"] += ms_l
+        prod["kernel"] = name
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gq.gq_set_timing(False)
+    return {"ms_step": wall * 1e3 / steps, "stage_ms": {s: acc[s] / steps for s in STAGES}, "prod": prod,
+            "qerr": qerr, "H": H, "Hs": Hs, "U": U, "blob": blob, "imp": imp}
+
+
+def update_flops(N, K):
+    """Algorithmic flops of the sweep's block updates: 2 N per (column, later
+    column) pair outside each 128-wide block."""
+    return sum(2 * N * min(SWEEP_BLOCK, K - b0) * (K - b0 - min(SWEEP_BLOCK, K - b0))
+               for b0 in range(0, K, SWEEP_BLOCK))
+
+
+def product_roofline(K, r, steps):
+    """The sign iteration's product kernel: its ops per launch and live rate."""
+    prod = r["prod"]
+    emulated = prod["kernel"].startswith("oz_gemm")
+    per_launch = K * K * (K + 1) * (OZ_MODULI if emulated else 1)
+    prod_ms = prod["ms"] / prod["launches"]
+    tops = per_launch / (prod_ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS["i8" if emulated else "f64"]
+    return emulated, per_launch, prod_ms, tops, peak
+
+
+def block_summary(wl, r, steps):
+    """Per-workload figures of a run_path result."""
+    K, G = wl.K, wl.group
+    st = r["stage_ms"]
+    Ns = wl.N
+    emulated, per_launch, prod_ms, tops, peak = product_roofline(K, r, steps)
+    gram_flops = wl.T * wl.chunks * K * (K + 1)
+    gram_tflops = gram_flops / (st["accumulate"] * 1e-3) / 1e12
+    weights = sum(Ns) * K
+    return {
+        "config": {"workload": wl.name, "T": wl.T, "chunks": wl.chunks, "K": K, "N": Ns, "group": G,
+                   "damp": wl.damp, "x_dtype": wl.x_dtype, "seed": wl.seed},
+        "steps": steps,
+        "ms_per_step": r["ms_step"],
+        "weights_per_s": weights / (r["ms_step"] * 1e-3),
+        "tensors_per_s": len(Ns) * 1e3 / r["ms_step"],
+        "stages_ms": {k: round(v, 4) for k, v in st.items()},
+        "gptq_weights_per_s": weights / ((st["factor"] + st["sweep"]) * 1e-3),
+        "hessian_tflops": gram_tflops,
+        "hessian_frac_of_bf16_peak": gram_tflops / PEAK_TFLOPS["bf16"],
+        "sweep_update_tflops": sum(update_flops(N, K) for N in Ns) / (st["sweep"] * 1e-3) / 1e12,
+        "psd_products_per_call": r["prod"]["launches"] / steps,
+        "psd_product_kernel": {"kernel": r["prod"]["kernel"], "avg_launch_ms": prod_ms, "per_launch_ops": per_launch,
+                               "achieved": tops, "peak": peak, "unit": "TOP/s" if emulated else "TFLOP/s",
+                               "frac": tops / peak},
+        "qerr": r["qerr"],
     }
 
 
@@ -128,72 +259,18 @@ def main():
     W = g.weights(wl, device=dev)
     torch.cuda.synchronize()
 
-    H = torch.empty(K, K, dtype=torch.float32, device=dev)
-    blob = torch.empty(gq.hessian_tril_bytes(K), dtype=torch.uint8, device=dev)
-    Hs = torch.empty(K, K, dtype=torch.float32, device=dev)
-    U = torch.empty(K, K, dtype=torch.float32, device=dev)
-    codes = torch.empty(N, K // 2, dtype=torch.uint8, device=dev)
-    scales = torch.empty(N, K // G, dtype=torch.float32, device=dev)
-    ws_psd = gq.workspace(gq.psd_project_workspace_size(K), dev)
-    ws_fac = gq.workspace(gq.gptq_factor_workspace_size(K), dev)
-    ws_swp = gq.workspace(gq.gptq_sweep_workspace_size(N, K, G), dev)
-    imp = blob[: 4 * K].view(torch.float32)          # stored exact diagonal of H
-
-    stages = ["accumulate", "pack", "unpack", "psd", "factor", "sweep"]
-    ev = {s: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for s in stages}
-    acc = {s: 0.0 for s in stages}
-    qerr = [None]
-
-    def step(record):
-        def run(name, fn):
-            if record:
-                ev[name][0].record()
-            fn()
-            if record:
-                ev[name][1].record()
-        H.zero_()
-        run("accumulate", lambda: gq.hessian_accumulate(H, X))
-        run("pack", lambda: gq.hessian_pack_tril(blob, H))
-        run("unpack", lambda: gq.hessian_unpack_tril(Hs, blob))
-        run("psd", lambda: gq.psd_project(Hs, ws_psd))
-        run("factor", lambda: gq.gptq_factor(U, Hs, damp, ws_fac))
-        run("sweep", lambda: qerr.__setitem__(0, gq.gptq_sweep(codes, scales, W, U, imp, G, ws_swp)))
-        if record:
-            torch.cuda.synchronize()
-            for s in stages:
-                acc[s] += ev[s][0].elapsed_time(ev[s][1])
-
-    for _ in range(args.warmup):
-        step(False)
-    torch.cuda.synchronize()
-    # psd_project brackets each launch of its product kernel with HIP events on
-    # this stream (two event records per launch)
-    gq.gq_set_timing(True)
-    prod = {"launches": 0, "ms": 0.0, "kernel": ""}
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step(True)
-        n_l, ms_l, name = gq.psd_project_last_timing()
-        prod["launches"] += n_l
-        prod["ms"] += ms_l
-        prod["kernel"] = name
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    gq.gq_set_timing(False)
-    ms_step = wall * 1e3 / args.steps
-    stage_ms = {s: acc[s] / args.steps for s in stages}
+    r = run_path(gq, torch, wl, [X], [W], dev, args.steps, args.warmup)
+    progress(f"{wl.name}: {args.steps} steps, {r['ms_step']:.2f} ms per step")
+    ms_step, stage_ms = r["ms_step"], r["stage_ms"]
+    Hs, U, blob, imp = r["Hs"], r["U"], r["blob"], r["imp"]
+    qerr = r["qerr"]
 
     gram_flops = T * K * (K + 1)
     gram_tflops = gram_flops / (stage_ms["accumulate"] * 1e-3) / 1e12
-    n_prod = gq.psd_project_products()
     prod_flops = K * K * (K + 1)                     # one symmetric product, lower triangle
-    emulated = prod["kernel"].startswith("oz_gemm")
-    per_launch = prod_flops * (OZ_MODULI if emulated else 1)
-    prod_ms = prod["ms"] / prod["launches"]          # the product kernel alone, live HIP events
-    prod_tops = per_launch / (prod_ms * 1e-3) / 1e12
-    peak = PEAK_TFLOPS["i8" if emulated else "f64"]
-    upd_flops = sum(2 * N * min(SWEEP_BLOCK, K - b0) * (K - b0 - min(SWEEP_BLOCK, K - b0))
-                    for b0 in range(0, K, SWEEP_BLOCK))
+    emulated, per_launch, prod_ms, prod_tops, peak = product_roofline(K, r, args.steps)
+    n_prod = r["prod"]["launches"] / args.steps
+    upd_flops = update_flops(N, K)
     gptq_ms = stage_ms["factor"] + stage_ms["sweep"]
     traffic, traffic_detail = traffic_for(wl.name)
 
@@ -227,7 +304,7 @@ def main():
         "psd_f64_equivalent_tflops": n_prod * prod_flops / (stage_ms["psd"] * 1e-3) / 1e12,
         "roofline": {
             "bound": "mfma",
-            "kernel": prod["kernel"] + ", sign-iteration symmetric product; timed alone with HIP events",
+            "kernel": r["prod"]["kernel"] + ", sign-iteration symmetric product; timed alone with HIP events",
             "achieved": prod_tops,
             "peak": peak,
             "unit": "TOP/s" if emulated else "TFLOP/s",
@@ -240,7 +317,7 @@ def main():
                 {"read_AB": 2 * K * K * 8, "read_cin_step_products": K * K * 8, "write_lower_and_mirror": K * K * 8}),
             "per_launch_ops": per_launch,
             "avg_launch_ms": prod_ms,
-            "launches_per_step": prod["launches"] / args.steps,
+            "launches_per_step": n_prod,
         },
     }
     out["rtn"] = rtn_measure(gq, torch, W, imp, G, dev)
@@ -248,9 +325,48 @@ def main():
     out["hadamard"] = hadamard_measure(gq, torch, W, Hs, dev)
     out["variants"] = variants_measure(gq, torch, W, U, Hs, imp, G, damp, dev)
     out["rtn"]["qerr_gptq_over_rtn"] = qerr[0] / out["rtn"]["qerr"] if out["rtn"]["qerr"] else None
+    progress("round to nearest, HFQM, rotation and variants measured")
+    del r, Hs, U
+    torch.cuda.empty_cache()
+    if not args.no_k17408 and wl.name != "mlpdown17408":
+        out["k17408"] = k17408_measure(gq, torch, g, dev, args.extra_steps)
+        torch.cuda.empty_cache()
+        progress(f"mlpdown17408: {out['k17408']['ms_per_step']:.1f} ms per step")
+    if not args.no_stream:
+        out["stream"] = stream_measure(gq, torch, g, dev, args.extra_steps)
+        torch.cuda.empty_cache()
+        progress(f"stream5120: {out['stream']['ms_per_step']:.1f} ms per step")
     if not args.no_cpu_baseline:
+        progress("CPU oracle: one whole step of the headline workload")
         out["cpu_baseline"] = cpu_baseline(wl, X, W)
+        progress(f"CPU oracle: {out['cpu_baseline']['step_s']:.1f} s")
     print(json.dumps(out))
+
+
+def k17408_measure(gq, torch, g, dev, steps):
+    """The MLP down-projection shape (T=8192, K=17408, N=5120, heavy-tailed bf16
+    activations): whole steps of the same path as the headline, one warm-up."""
+    wl = g.WORKLOADS["mlpdown17408"]
+    X = g.x_chunk(wl, device=dev)
+    W = g.weights(wl, device=dev)
+    torch.cuda.synchronize()
+    r = run_path(gq, torch, wl, [X], [W], dev, steps, 1)
+    return block_summary(wl, r, steps)
+
+
+def stream_measure(gq, torch, g, dev, steps):
+    """The streamed recipe: 128 chunks of 8192 bf16 tokens at K=5120, generated
+    and staged in HBM (10.7 GB) before timing, accumulated into one H per step,
+    then storage, projection, one factor and the sweeps of the four weight
+    tensors (N = 5120, 10240, 1024, 1024) that share it; one warm-up."""
+    wl = g.WORKLOADS["stream5120"]
+    chunks = [g.x_chunk(wl, c, device=dev) for c in range(wl.chunks)]
+    Ws = [g.weights(wl, t, device=dev) for t in range(len(wl.N))]
+    torch.cuda.synchronize()
+    r = run_path(gq, torch, wl, chunks, Ws, dev, steps, 1)
+    out = block_summary(wl, r, steps)
+    out["hessian_target_ms_at_60pct"] = wl.T * wl.chunks * wl.K * (wl.K + 1) / (0.6 * PEAK_TFLOPS["bf16"] * 1e12) * 1e3
+    return out
 
 
 def hadamard_measure(gq, torch, W, H, dev, block=1024, reps=10):

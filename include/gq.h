@@ -90,6 +90,31 @@ const char *gq_last_error(void);
 int hessian_accumulate(float *H, const void *X, int x_dtype, int64_t T, int64_t K,
                        hipStream_t stream);
 
+/*
+ * hessian_accumulate_chunks -- H_lower += sum over c of X_c^T X_c for n chunks in
+ * one call: the same statistic as n hessian_accumulate calls, since it is a sum
+ * over chunks (AtomicChat Qwen3.8-27B GGUF page, "The importance matrix").  For
+ * bf16 chunks with K % 8 == 0 and 16-byte aligned pointers, up to 128 chunks go
+ * into one launch whose workgroups each take one tile and a contiguous range of
+ * chunks; with a workspace, several workgroups share a tile so that every
+ * compute unit is busy, and their partial tiles are added to H in a fixed order
+ * (the result does not depend on timing, and it may differ from n separate
+ * calls in the rounding of the fp32 sums).  Other chunks run as n
+ * hessian_accumulate calls.
+ *   H     K x K fp32, lower triangle updated in place (as hessian_accumulate).
+ *   X     host array of n device pointers, chunk c being T[c] x K row-major.
+ *   T     host array of n token counts (>= 0; 0 skips the chunk).
+ *   ws    device workspace of hessian_accumulate_chunks_workspace_size(K, n)
+ *         bytes (a smaller one means fewer workgroups per tile), or NULL (one
+ *         workgroup per tile).  The size query needs the current device.
+ * Asynchronous, like hessian_accumulate.
+ * Errors: GQ_ERR_INVALID_ARG (null pointers, K < 1, n < 0, T[c] < 0, unknown
+ *         dtype), GQ_ERR_HIP.
+ */
+size_t hessian_accumulate_chunks_workspace_size(int64_t K, int64_t n);
+int hessian_accumulate_chunks(float *H, const void *const *X, const int64_t *T, int64_t n, int x_dtype,
+                              int64_t K, void *ws, size_t ws_bytes, hipStream_t stream);
+
 /* Bytes of a Bf16TrilDiagF32 blob: K*4 + K*(K-1)/2*2 (hipfire-calib-data,
  * "Hessian storage: Bf16TrilDiagF32"). 0 for K < 1. */
 size_t hessian_tril_bytes(int64_t K);

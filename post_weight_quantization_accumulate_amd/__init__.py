@@ -34,7 +34,7 @@ EXPORTS = (
     "gptq_sweep_ex", "gptq_quantize_ex", "rtn_quantize_ex", "gq_nf4_levels", "gptq_quantize_ex_workspace_size",
     "hfqm_write", "hfqm_read_header", "hfqm_read_entry", "hfqm_read_payload",
     "hadamard_rotate_rows", "hadamard_rotate_hessian_workspace_size", "hadamard_rotate_hessian",
-    "rtn_quantize_noalloc",
+    "rtn_quantize_noalloc", "hessian_accumulate_chunks_workspace_size", "hessian_accumulate_chunks",
 )
 
 
@@ -63,6 +63,8 @@ def lib() -> ctypes.CDLL:
             "gq_last_error": (ctypes.c_char_p, []),
             "hessian_accumulate": (I, [P, P, I, I64, I64, P]),
             "hessian_tril_bytes": (SZ, [I64]),
+            "hessian_accumulate_chunks_workspace_size": (SZ, [I64, I64]),
+            "hessian_accumulate_chunks": (I, [P, P, P, I64, I, I64, P, SZ, P]),
             "hessian_pack_tril": (I, [P, P, I64, P]),
             "hessian_unpack_tril": (I, [P, P, I64, P]),
             "psd_project_workspace_size": (SZ, [I64]),
@@ -147,6 +149,34 @@ def hessian_accumulate(H: torch.Tensor, X: torch.Tensor) -> None:
     else:
         raise ValueError("X must be fp32 or bf16")
     _check(lib().hessian_accumulate(_ptr(H), _ptr(X), dt, T, K, _stream(H)), "hessian_accumulate")
+
+
+def hessian_accumulate_chunks_workspace_size(K: int, n: int) -> int:
+    return int(lib().hessian_accumulate_chunks_workspace_size(K, n))
+
+
+def hessian_accumulate_chunks(H: torch.Tensor, chunks, ws=None) -> None:
+    """H[i][j] += sum over the chunks of sum_t X[t][i] X[t][j] for i >= j, in as
+    few launches as the library can (all chunks fp32 or all bf16, same K)."""
+    n = len(chunks)
+    if n == 0:
+        return
+    K = chunks[0].shape[1]
+    _need(H, "H", torch.float32, K * K)
+    dtypes = {X.dtype for X in chunks}
+    if len(dtypes) != 1 or next(iter(dtypes)) not in (torch.float32, torch.bfloat16):
+        raise ValueError("chunks must be all fp32 or all bf16")
+    for X in chunks:
+        _need(X, "X", None)
+        if X.shape[1] != K:
+            raise ValueError("every chunk needs K columns")
+    dt = GQ_BF16 if chunks[0].dtype == torch.bfloat16 else GQ_F32
+    ptrs = (ctypes.c_void_p * n)(*[X.data_ptr() for X in chunks])
+    toks = (ctypes.c_int64 * n)(*[X.shape[0] for X in chunks])
+    if ws is not None:
+        _need(ws, "ws", torch.uint8)
+    _check(lib().hessian_accumulate_chunks(_ptr(H), ptrs, toks, n, dt, K, _ptr(ws), 0 if ws is None else ws.numel(),
+                                           _stream(H)), "hessian_accumulate_chunks")
 
 
 def hessian_tril_bytes(K: int) -> int:

@@ -564,6 +564,93 @@ int hessian_accumulate(float *H, const void *X, int x_dtype, int64_t T, int64_t 
     return GQ_OK;
 }
 
+}  // extern "C"
+
+namespace {
+// Splits per tile for a group of n chunks: the split count that best fills the
+// chip's compute units with equal workgroups (tiles x splits against whole
+// rounds of CUs, times the balance of chunks over splits), with a small charge
+// per split for the partial tiles it writes and reads back.
+int gram_splits(int64_t K, int64_t n, int ncu)
+{
+    if (n <= 1 || ncu <= 0) return 1;
+    const int64_t tiles = gram_tiles(K);
+    int best = 1;
+    double best_eff = -1.0;
+    for (int sp = 1; sp <= (int)std::min<int64_t>(n, 64); ++sp) {
+        const int64_t wg = tiles * sp;
+        const double fill = (double)wg / (double)(((wg + ncu - 1) / ncu) * ncu);
+        const double bal = ((double)n / sp) / (double)((n + sp - 1) / sp);
+        const double eff = fill * bal - 0.002 * sp;
+        if (eff > best_eff + 1e-12) { best_eff = eff; best = sp; }
+    }
+    return best;
+}
+
+int device_cus(int *ncu)
+{
+    int dev = 0;
+    GQ_HIP(hipGetDevice(&dev), "current device");
+    GQ_HIP(hipDeviceGetAttribute(ncu, hipDeviceAttributeMultiprocessorCount, dev), "CU count");
+    return GQ_OK;
+}
+}  // namespace
+
+extern "C" {
+
+size_t hessian_accumulate_chunks_workspace_size(int64_t K, int64_t n)
+{
+    if (K < 1 || n < 2) return 0;
+    int ncu = 0;
+    if (device_cus(&ncu) != GQ_OK) return 0;
+    // the largest over the group sizes a call can form (chunks with T = 0 are
+    // left out of a group)
+    size_t need = 0;
+    for (int64_t m = 2; m <= std::min<int64_t>(n, kGramMaxChunks); ++m)
+        need = std::max(need, gram_split_bytes(K, gram_splits(K, m, ncu)));
+    return need;
+}
+
+int hessian_accumulate_chunks(float *H, const void *const *X, const int64_t *T, int64_t n, int x_dtype, int64_t K,
+                              void *ws, size_t ws_bytes, hipStream_t stream)
+{
+    g_last_error.clear();
+    if (!H || (n > 0 && (!X || !T))) return fail(GQ_ERR_INVALID_ARG, "null required pointer");
+    if (K < 1 || n < 0) return fail(GQ_ERR_INVALID_ARG, "need K >= 1 and n >= 0");
+    if (x_dtype != GQ_F32 && x_dtype != GQ_BF16) return fail(GQ_ERR_INVALID_ARG, "unknown x_dtype");
+    bool dma = x_dtype == GQ_BF16 && K % 8 == 0;
+    for (int64_t c = 0; c < n; ++c) {
+        if (T[c] < 0) return fail(GQ_ERR_INVALID_ARG, "a chunk has T < 0");
+        if (T[c] > 0 && !X[c]) return fail(GQ_ERR_INVALID_ARG, "null chunk pointer");
+        if (T[c] > 0 && ((uintptr_t)X[c] & 15)) dma = false;
+    }
+    if (!dma) {
+        // chunk by chunk, each added to H as hessian_accumulate does
+        for (int64_t c = 0; c < n; ++c) {
+            const int rc = hessian_accumulate(H, X[c], x_dtype, T[c], K, stream);
+            if (rc) return rc;
+        }
+        return GQ_OK;
+    }
+    int ncu = 0;
+    if (int rc = device_cus(&ncu)) return rc;
+    for (int64_t c0 = 0; c0 < n; c0 += kGramMaxChunks) {
+        GramChunks ch{};
+        for (int64_t c = c0; c < n && c < c0 + kGramMaxChunks; ++c)
+            if (T[c] > 0) {
+                ch.x[ch.n] = (const uint16_t *)X[c];
+                ch.t[ch.n] = T[c];
+                ++ch.n;
+            }
+        if (ch.n == 0) continue;
+        // the best split count whose partial tiles fit the workspace
+        int splits = ws ? gram_splits(K, ch.n, ncu) : 1;
+        while (splits > 1 && ws_bytes < gram_split_bytes(K, splits)) --splits;
+        GQ_HIP(launch_gram_bf16_chunks(H, ch, K, splits, (float *)ws, stream), "gram bf16 chunks");
+    }
+    return GQ_OK;
+}
+
 size_t hessian_tril_bytes(int64_t K)
 {
     if (K < 1) return 0;

@@ -166,6 +166,20 @@ hipError_t launch_zero_bytes(void *p, size_t n, hipStream_t s);
 
 // bf16 Gram: H_lower += X^T X, X T x K bf16 row-major.
 hipError_t launch_gram_bf16(float *H, const uint16_t *X, int64_t T, int64_t K, hipStream_t s);
+// Up to kGramMaxChunks bf16 chunks (K % 8 == 0, 16-byte aligned) in one launch,
+// passed by value; `splits` workgroups per tile each take a contiguous range of
+// chunks, and with splits > 1 their tiles go through `part`
+// (gram_split_bytes(K, splits) bytes) and are added to H in split order.
+constexpr int kGramMaxChunks = 128;
+struct GramChunks {
+    const uint16_t *x[kGramMaxChunks];
+    int64_t t[kGramMaxChunks];
+    int n;
+};
+int64_t gram_tiles(int64_t K);
+size_t gram_split_bytes(int64_t K, int splits);
+hipError_t launch_gram_bf16_chunks(float *H, const GramChunks &ch, int64_t K, int splits, float *part,
+                                   hipStream_t s);
 
 // Bf16TrilDiagF32 storage.
 hipError_t launch_tril_pack(uint8_t *blob, const float *H, int64_t K, hipStream_t s);

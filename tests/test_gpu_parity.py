@@ -79,7 +79,8 @@ def test_gram_f32_parity(gq, orc, T, K):
     assert np.all(np.triu(H, 1) == 0)          # the strict upper triangle is not touched
 
 
-@pytest.mark.parametrize("T,K", [(1000, 300), (8192, 1024), (37, 136), (4096, 520)])
+@pytest.mark.parametrize("T,K", [(1000, 300), (8192, 1024), (37, 136), (4096, 520), (1, 8), (130, 2056),
+                                 (200, 264)])
 def test_gram_bf16_parity(gq, orc, T, K):
     wl = g.Workload("attn5120", T, K, [8], 128, 0.01, "bf16", True, 1, 2)
     X = g.x_chunk(wl)
@@ -113,6 +114,45 @@ def test_gram_chunks_add_and_resume_bitwise(gq, orc):
         orc.gram(X.cpu(), ref)
     low = np.tril_indices(384)
     assert _relF(H.cpu().numpy()[low], ref[low]) < 1e-5
+
+
+@pytest.mark.parametrize("K", [520, 256, 300])
+def test_gram_chunks_call(gq, orc, K):
+    """hessian_accumulate_chunks: several chunks of ragged token counts (one
+    empty, one of a single token) in one call, with and without a workspace
+    (workgroups sharing tiles, partial tiles added in a fixed order), against
+    the oracle's sum of the chunks' Gram matrices; repeated calls are bitwise
+    equal, and the result matches the chunk-by-chunk calls to fp32 rounding.
+    K = 300 (not a multiple of 8) takes the chunk-by-chunk route inside."""
+    Ts = [100, 37, 0, 512, 1, 64, 300, 33, 250]
+    wl = g.Workload("stream5120", 512, K, [8], 128, 0.01, "bf16", True, len(Ts), 4)
+    chunks = [g.x_chunk(wl, c, device=DEV, tokens=max(T, 1))[:T].contiguous() for c, T in enumerate(Ts)]
+    ref = np.zeros((K, K))
+    for X in chunks:
+        if X.shape[0]:
+            orc.gram(X.cpu(), ref)
+    low = np.tril_indices(K)
+    ws = gq.workspace(max(gq.hessian_accumulate_chunks_workspace_size(K, len(chunks)), 1), DEV)
+    outs = []
+    for w in (ws, None, ws):
+        H = torch.zeros(K, K, dtype=torch.float32, device=DEV)
+        gq.hessian_accumulate_chunks(H, chunks, w)
+        torch.cuda.synchronize()
+        Hn = H.cpu().numpy()
+        assert _relF(Hn[low], ref[low]) < 1e-5
+        assert np.all(np.triu(Hn, 1) == 0)
+        outs.append(Hn)
+    assert np.array_equal(outs[0].view(np.uint32), outs[2].view(np.uint32))
+    H1 = torch.zeros(K, K, dtype=torch.float32, device=DEV)
+    for X in chunks:
+        gq.hessian_accumulate(H1, X)
+    torch.cuda.synchronize()
+    assert _relF(outs[0][low], H1.cpu().numpy()[low]) < 1e-6
+    # into a non-zero H: the chunks' sum is added
+    H = H1.clone()
+    gq.hessian_accumulate_chunks(H, chunks, ws)
+    torch.cuda.synchronize()
+    assert _relF(H.cpu().numpy()[low], 2 * ref[low]) < 1e-5
 
 
 def test_gram_is_deterministic(gq):
