@@ -3,7 +3,11 @@
 // compensated column-sequential int4 rounding emitting symmetric codes in
 // [-8, 7] with a per-(row, group) scale absmax/7; qerr definition).
 //
-// Sweep layout: rows are independent given U, so a wave holds 4 rows, 16 lanes
+// Two sweep kernels share one arithmetic.  sweep4_kernel (4 lanes per row,
+// described at its definition) runs static groups and groups of 32 columns or
+// more, the common case; sweep_block_kernel runs dynamic groups shorter than 32.
+//
+// sweep_block_kernel: rows are independent given U, so a wave holds 4 rows, 16 lanes
 // per row, 8 consecutive columns per lane (the whole 128-column block of a row
 // lives in registers).  Column i of the block is owned by lane i/8 of each
 // 16-lane row group; a DPP row broadcast hands its current value to the row
@@ -41,6 +45,46 @@ template <int src> __device__ inline float row_bcast(float x)
 // Midpoint j of the NF4 levels in fp32 (j = 15: above every value).
 __device__ inline float nf4_mid(int j) { return j < 15 ? (kNF4[j] + kNF4[j + 1]) * 0.5f : INFINITY; }
 
+// U's 128 x 128 diagonal block at (b0, b0) into LDS, element (r, c) at
+// r * UP + (c / 32) * QP + c % 32, zero outside the bw x bw corner (past bw the
+// reciprocal diagonal is 0, so padded columns carry zero error and change
+// nothing).  Each thread takes 16-byte pieces 32 / (NT / 128) apart and issues
+// 8 loads before it stores any, so the block costs a few memory round trips
+// rather than one per element.  Pieces that are not whole inside the corner, or
+// a K or U that does not allow 16-byte loads, go element by element.
+template <int NT, int UP, int QP>
+__device__ __attribute__((always_inline)) inline void load_u_block(float *Us, const float *__restrict__ U, int64_t K, int64_t b0, int bw, int tid)
+{
+    constexpr int PIECES = BW * BW / 4;             // 16-byte pieces in the block
+    constexpr int PER = PIECES / NT;                // per thread
+    constexpr int BATCH = PER < 8 ? PER : 8;
+    const bool vec = (K % 4) == 0 && (((uintptr_t)U) & 15) == 0;
+#pragma unroll
+    for (int b = 0; b < PER; b += BATCH) {
+        float4 v[BATCH];
+#pragma unroll
+        for (int j = 0; j < BATCH; ++j) {
+            const int p = tid + NT * (b + j);
+            const int r = p / (BW / 4), c = 4 * (p % (BW / 4));
+            const float *src = U + (b0 + r) * K + b0 + c;
+            if (vec && r < bw && c + 4 <= bw) {
+                v[j] = *(const float4 *)src;
+            } else {
+                v[j].x = (r < bw && c < bw) ? src[0] : 0.0f;
+                v[j].y = (r < bw && c + 1 < bw) ? src[1] : 0.0f;
+                v[j].z = (r < bw && c + 2 < bw) ? src[2] : 0.0f;
+                v[j].w = (r < bw && c + 3 < bw) ? src[3] : 0.0f;
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < BATCH; ++j) {
+            const int p = tid + NT * (b + j);
+            const int r = p / (BW / 4), c = 4 * (p % (BW / 4));
+            *(float4 *)(Us + r * UP + (c >> 5) * QP + (c & 31)) = v[j];
+        }
+    }
+}
+
 // Four waves per SIMD (one workgroup of 16 waves per CU): the grid has one
 // workgroup per 64 rows, 160 for ten thousand rows, so each block of U is read
 // from memory half as often as with 32 rows, and CUs stay free for the update
@@ -60,12 +104,7 @@ __global__ __launch_bounds__(SW_NT, 4) void sweep_block_kernel(float *__restrict
     const int bw = (int)((K - b0) < BW ? (K - b0) : BW);
     if (NF4 && tid < 16) lev[tid] = kNF4[tid];
 
-    // U's block, zero outside the bw x bw corner; past bw the reciprocal
-    // diagonal is 0, so padded columns carry zero error and change nothing.
-    for (int e = tid; e < BW * BW; e += SW_NT) {
-        const int r = e / BW, c = e % BW;
-        Us[r * UPITCH + c] = (r < bw && c < bw) ? U[(b0 + r) * K + b0 + c] : 0.0f;
-    }
+    load_u_block<SW_NT, UPITCH, 32>(Us, U, K, b0, bw, tid);
     if (tid < BW) rdiag[tid] = tid < bw ? 1.0f / U[(b0 + tid) * K + b0 + tid] : 0.0f;
     __syncthreads();
 
@@ -216,6 +255,257 @@ __global__ __launch_bounds__(SW_NT, 4) void sweep_block_kernel(float *__restrict
     }
 }
 
+// The same sweep with 4 lanes per row, 32 consecutive columns per lane, for
+// static groups and for groups of 32 columns or more.  The block's columns fall
+// in 4 quarters of 32; lane q of a row's 4-lane group starts with quarter q, and
+// after each quarter the 4 lanes pass their state (weights, codes, static
+// scales) one lane down the group, so the quarter being decided always sits in
+// the group's first lane and one body of 32 columns serves all four quarters.
+// Column i's value reaches the group from that lane by one DPP quad broadcast,
+// the 4 lanes take the same rounding decision, and each applies the error to
+// the 32 columns it holds from 8 16-byte LDS reads of U's row i, issued one
+// column ahead.  U's block sits in LDS as 4 quarters of 32 columns per row, 36
+// floats apart, so the 4 quarters a quad reads fall on different banks (the 16
+// rows of a wave read the same addresses).  A dynamic group starts with a
+// quarter; its absmax combines 1, 2 or 4 lanes by quad exchanges before the
+// quarter's columns, which then run without branches.  NF4 takes the level
+// index as the count of midpoints the quotient exceeds, as the ballot form
+// counts.  Decisions and arithmetic are those of sweep_block_kernel, column by
+// column.  Against 16 lanes per row, each decision is taken by 4 lanes instead
+// of 16 and a wave holds 16 rows instead of 4.
+constexpr int S4_NT = 128;              // 2 waves
+constexpr int S4_ROWS = 32;             // 16 rows per wave
+constexpr int S4_QP = 36;               // floats from one quarter of a U row to the next
+constexpr int S4_UP = 4 * S4_QP;        // floats per U row in LDS
+
+template <int src> __device__ inline float quad_bcast(float x)
+{
+    constexpr int ctrl = src | (src << 2) | (src << 4) | (src << 6);   // quad_perm [src, src, src, src]
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), ctrl, 0xF, 0xF, false));
+}
+
+template <int ctrl> __device__ inline float quad_perm_f(float x)
+{
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), ctrl, 0xF, 0xF, false));
+}
+
+// Lane p of each quad takes the value of lane p + 1 (lane 3 that of lane 0).
+__device__ inline unsigned quad_next(unsigned x)
+{
+    return (unsigned)__builtin_amdgcn_mov_dpp((int)x, 1 | (2 << 2) | (3 << 4) | (0 << 6), 0xF, 0xF, false);
+}
+__device__ inline float quad_next(float x) { return __uint_as_float(quad_next(__float_as_uint(x))); }
+
+template <int MODE>
+__global__ __launch_bounds__(S4_NT, 1) void sweep4_kernel(float *__restrict__ Wk, float *__restrict__ ET,
+                                                          uint8_t *__restrict__ codes, float *__restrict__ scales,
+                                                          const float *__restrict__ U, int64_t N, int64_t K,
+                                                          int lg, int64_t b0, const int *__restrict__ gidx)
+{
+    constexpr bool STATIC = (MODE & MODE_STATIC) != 0, NF4 = (MODE & MODE_NF4) != 0;
+    __shared__ __attribute__((aligned(16))) float Us[BW * S4_UP];
+    __shared__ __attribute__((aligned(16))) float rdiag[BW];
+    __shared__ float lev[16];
+    const int tid = threadIdx.x;
+    const int G = 1 << lg;                // 32, 64 or 128
+    const int bw = (int)((K - b0) < BW ? (K - b0) : BW);
+    if (NF4 && tid < 16) lev[tid] = kNF4[tid];
+    load_u_block<S4_NT, S4_UP, S4_QP>(Us, U, K, b0, bw, tid);
+    if (tid < BW) rdiag[tid] = tid < bw ? 1.0f / U[(b0 + tid) * K + b0 + tid] : 0.0f;
+    __syncthreads();
+
+    const int lane = tid & 63, wave = tid >> 6;
+    const int q = lane & 3;
+    const int rloc = wave * 16 + (lane >> 2);
+    const int64_t row = (int64_t)blockIdx.x * S4_ROWS + rloc;
+    const bool rv = row < N;
+    const int cb = 32 * q;
+    const int64_t ngroups = K >> lg;
+
+    float w[32];
+    {
+        const float *wr = Wk + row * K + b0 + cb;
+        if (rv && cb + 32 <= bw && (((uintptr_t)wr) & 15) == 0) {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const float4 v = *(const float4 *)(wr + 4 * k);
+                w[4 * k] = v.x;
+                w[4 * k + 1] = v.y;
+                w[4 * k + 2] = v.z;
+                w[4 * k + 3] = v.w;
+            }
+        } else {
+#pragma unroll
+            for (int t = 0; t < 32; ++t) w[t] = (rv && cb + t < bw) ? wr[t] : 0.0f;
+        }
+    }
+
+    // static groups: each column's scale (group gidx[column] when a group map is
+    // given, else column / G) and RN(1 / (scale * guard factor))
+    float sl[STATIC ? 32 : 1], yl[STATIC ? 32 : 1];
+    if constexpr (STATIC) {
+#pragma unroll
+        for (int t = 0; t < 32; ++t) {
+            const int64_t col = b0 + cb + t;
+            const bool ok = rv && cb + t < bw;
+            const int64_t gi = ok ? (gidx ? (int64_t)gidx[col] : col >> lg) : 0;
+            sl[t] = ok ? scales[row * ngroups + gi] : 0.0f;
+            const float ft = sl[t] < 0x1p-60f ? 0x1p64f : 1.0f;
+            yl[t] = sl[t] != 0.0f ? 1.0f / (sl[t] * ft) : 0.0f;
+        }
+    }
+    // NF4 midpoints, ascending
+    float mids[NF4 ? 15 : 1];
+    if constexpr (NF4) {
+#pragma unroll
+        for (int j = 0; j < 15; ++j) mids[j] = nf4_mid(j);
+    }
+
+    float s = 1.0f, y = 0.0f, f = 1.0f;   // as in sweep_block_kernel
+    unsigned cdw[4] = {0u, 0u, 0u, 0u};   // codes of the lane's quarter, column t in nibble t % 8 of word t / 8
+    const bool own = (q == 0);            // the group's first lane holds the quarter being decided
+#pragma unroll 1
+    for (int qi = 0; qi < 4; ++qi) {
+        // this lane now holds quarter (q + qi) % 4; the group's first lane holds quarter qi
+        const float *uq = Us + 32 * qi * S4_UP + ((q + qi) & 3) * S4_QP;
+        // the quarter's reciprocal diagonal, in registers
+        float rd[32];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const float4 r4 = *(const float4 *)(rdiag + 32 * qi + 4 * k);
+            rd[4 * k] = r4.x;
+            rd[4 * k + 1] = r4.y;
+            rd[4 * k + 2] = r4.z;
+            rd[4 * k + 3] = r4.w;
+        }
+        // a group starts with the quarter: its scale from the absmax of the
+        // group's quarters, which sit in lanes 0 (G = 32), 0-1 (64) or 0-3 (128)
+        // of the quad
+        if (!STATIC && ((32 * qi) & (G - 1)) == 0) {
+            float m = 0.0f;
+#pragma unroll
+            for (int v = 0; v < 32; ++v) m = fmaxf(m, fabsf(w[v]));
+            if (G >= 64) m = fmaxf(m, quad_perm_f<1 | (0 << 2) | (3 << 4) | (2 << 6)>(m));
+            if (G == 128) m = fmaxf(m, quad_perm_f<2 | (3 << 2) | (0 << 4) | (1 << 6)>(m));
+            m = quad_bcast<0>(m);
+            const float sc = NF4 ? m : m / 7.0f;
+            if (q == 0 && rv && 32 * qi < bw) scales[row * ngroups + ((b0 + 32 * qi) >> lg)] = sc;
+            s = sc != 0.0f ? sc : 1.0f;
+            f = sc < 0x1p-60f ? 0x1p64f : 1.0f;
+            y = sc != 0.0f ? 1.0f / (s * f) : 0.0f;
+        }
+
+        // the rounding decision of column ti of the quarter: packs its code and
+        // returns its scaled error
+        auto decide = [&](auto T) -> float {
+            constexpr int ti = decltype(T)::value;
+            const float wi = quad_bcast<0>(w[ti]);
+            if constexpr (STATIC) {
+                const float sc = quad_bcast<0>(sl[ti]);
+                s = sc != 0.0f ? sc : 1.0f;
+                y = quad_bcast<0>(yl[ti]);
+                f = sc < 0x1p-60f ? 0x1p64f : 1.0f;
+            }
+            // x = RN(wi / s) by Markstein's correction step, value and scale scaled by f
+            const float wq = wi * f;
+            const float q0 = wq * y;
+            const float rr = fmaf(-(s * f), q0, wq);
+            const float x = fmaf(rr, y, q0);
+            float c;
+            unsigned nib;
+            if constexpr (NF4) {
+                int ci = 0;
+#pragma unroll
+                for (int j = 0; j < 15; ++j) ci += x > mids[j] ? 1 : 0;
+                c = lev[ci];
+                nib = (unsigned)ci;
+            } else {
+                c = fminf(fmaxf(rintf(x), -8.0f), 7.0f);
+                nib = (unsigned)(int)c & 0xFu;
+            }
+            cdw[ti / 8] |= own ? nib << (4 * (ti % 8)) : 0u;
+            asm("" : "+v"(cdw[ti / 8]));      // pack now, not at the end
+            return fmaf(-c, s, wi) * rd[ti];
+        };
+
+        // U's rows are read one column ahead, so a whole column covers the LDS
+        // latency, and the columns are pipelined: column ti first updates the
+        // value column ti + 1 decides on, takes that decision, and then
+        // finishes its other 31 updates beside it.
+        float nu[32];
+        auto read_row = [&](int r) {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const float4 v = *(const float4 *)(uq + r * S4_UP + 4 * k);
+                nu[4 * k] = v.x;
+                nu[4 * k + 1] = v.y;
+                nu[4 * k + 2] = v.z;
+                nu[4 * k + 3] = v.w;
+            }
+        };
+        read_row(0);
+        float e = decide(std::integral_constant<int, 0>{});
+        auto column = [&](auto T) {
+            constexpr int ti = decltype(T)::value;
+            float u[32];
+#pragma unroll
+            for (int j = 0; j < 32; ++j) u[j] = nu[j];
+            if constexpr (ti + 1 < 32) read_row(ti + 1);
+            constexpr int nx = ti + 1 < 32 ? ti + 1 : -1;   // the value decided next
+            float en = 0.0f;
+            if constexpr (nx >= 0) {
+                w[nx] = fmaf(-e, u[nx], w[nx]);
+                en = decide(std::integral_constant<int, nx>{});
+            }
+#pragma unroll
+            for (int j = 0; j < 32; ++j)
+                if (j != nx) w[j] = fmaf(-e, u[j], w[j]);
+            w[ti] = own ? e : w[ti];
+            e = en;
+            // nothing crosses: the next row's reads stay a column ahead of their use
+            __builtin_amdgcn_sched_barrier(0);
+        };
+        static_for<32>(column);
+        // pass the state one lane down the group: lane p then holds quarter (p + qi + 1) % 4
+#pragma unroll
+        for (int t = 0; t < 32; ++t) w[t] = quad_next(w[t]);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) cdw[k] = quad_next(cdw[k]);
+        if constexpr (STATIC) {
+#pragma unroll
+            for (int t = 0; t < 32; ++t) {
+                sl[t] = quad_next(sl[t]);
+                yl[t] = quad_next(yl[t]);
+            }
+        }
+    }
+    // after four passes lane q holds its own quarter again
+
+    // codes: two per byte, column 2m in the low nibble
+    if (rv) {
+        uint8_t *crow = codes + row * (K / 2) + (b0 + cb) / 2;
+        if (cb + 32 <= bw && (((uintptr_t)crow & 3) == 0)) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) ((unsigned *)crow)[k] = cdw[k];
+        } else {
+            for (int m = 0; m < 16; ++m)
+                if (cb + 2 * m < bw) crow[m] = (uint8_t)(cdw[m / 4] >> (8 * (m % 4)));
+        }
+    }
+
+    // errors, transposed through LDS: ET[k][n] for the block's k = 0..bw-1
+    __syncthreads();
+    float *Es = Us;                        // reuse: [BW][S4_ROWS + 1]
+#pragma unroll
+    for (int t = 0; t < 32; ++t) Es[(cb + t) * (S4_ROWS + 1) + rloc] = w[t];
+    __syncthreads();
+    const int64_t n0 = (int64_t)blockIdx.x * S4_ROWS;
+    for (int e = tid; e < BW * S4_ROWS; e += S4_NT) {
+        const int k = e / S4_ROWS, r = e % S4_ROWS;
+        if (k < bw && n0 + r < N) ET[k * N + n0 + r] = Es[k * (S4_ROWS + 1) + r];
+    }
+}
+
 __global__ __launch_bounds__(256) void copy_check_kernel(float *__restrict__ dst, const float *__restrict__ src,
                                                         int64_t n, unsigned *status)
 {
@@ -333,31 +623,56 @@ __global__ __launch_bounds__(QNT) void qerr8_kernel(double *__restrict__ partial
     __shared__ float lev[16];
     if (NF4 && threadIdx.x < 16) lev[threadIdx.x] = kNF4[threadIdx.x];
     __syncthreads();
-    const int64_t chunks = K / 8, total = N * chunks, ng = K / G;
+    const int64_t chunks = K / 8, ng = K / G;
+    const int lg = __builtin_ctzll((unsigned long long)G);   // G is a power of two
     double num = 0.0, den = 0.0;
-    for (int64_t idx = (int64_t)blockIdx.x * QNT + threadIdx.x; idx < total; idx += (int64_t)gridDim.x * QNT) {
-        const int64_t row = idx / chunks, c = idx - row * chunks;
-        const float4 a = *(const float4 *)(W + row * K + 8 * c);
-        const float4 b = *(const float4 *)(W + row * K + 8 * c + 4);
-        const float w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-        const unsigned cw = *(const unsigned *)(codes + row * (K / 2) + 4 * c);
-        float iw[8] = {1.0f, 1.0f, 1.0f, 1.0f, 1.0f, 1.0f, 1.0f, 1.0f};
-        if (imp) {
-            const float4 i0 = *(const float4 *)(imp + 8 * c), i1 = *(const float4 *)(imp + 8 * c + 4);
-            iw[0] = i0.x; iw[1] = i0.y; iw[2] = i0.z; iw[3] = i0.w;
-            iw[4] = i1.x; iw[5] = i1.y; iw[6] = i1.z; iw[7] = i1.w;
-        }
-        const float *srow = scales + row * ng;
-        const float s8 = G >= 8 ? srow[8 * c / G] : 0.0f;     // one group holds all 8 columns
+    // rows by workgroup, a row's 8-column chunks by thread; QU chunks per pass
+    // with their loads issued together, so that enough bytes are in flight
+    constexpr int QU = 2;
+    for (int64_t row = blockIdx.x; row < N; row += gridDim.x) {
+      const float *wrow = W + row * K;
+      const uint8_t *crow = codes + row * (K / 2);
+      const float *srow = scales + row * ng;
+      for (int64_t cb = threadIdx.x; cb < chunks; cb += QU * QNT) {
+        // every load of the pass (weights, codes, importance, the group's scale)
+        // is issued before any arithmetic, so that one memory round trip covers it
+        float4 av[QU], bv[QU], iav[QU], ibv[QU];
+        unsigned cwv[QU];
+        float s8v[QU];
 #pragma unroll
-        for (int t = 0; t < 8; ++t) {
-            const unsigned nib = (cw >> (4 * t)) & 0xFu;
-            const float cv = NF4 ? lev[nib] : (float)((int)nib - ((nib & 8u) ? 16 : 0));
-            const float sc = G >= 8 ? s8 : srow[(8 * c + t) / G];
-            const double d = (double)w[t] - (double)cv * (double)sc;
-            num += (double)iw[t] * d * d;
-            den += (double)iw[t] * (double)w[t] * (double)w[t];
+        for (int q = 0; q < QU; ++q) {
+          const int64_t c = cb + q * QNT < chunks ? cb + q * QNT : cb;
+          av[q] = *(const float4 *)(wrow + 8 * c);
+          bv[q] = *(const float4 *)(wrow + 8 * c + 4);
+          cwv[q] = *(const unsigned *)(crow + 4 * c);
+          if (imp) {
+            iav[q] = *(const float4 *)(imp + 8 * c);
+            ibv[q] = *(const float4 *)(imp + 8 * c + 4);
+          } else {
+            iav[q] = ibv[q] = make_float4(1.0f, 1.0f, 1.0f, 1.0f);
+          }
+          s8v[q] = G >= 8 ? srow[(8 * c) >> lg] : 0.0f;        // one group holds all 8 columns
         }
+#pragma unroll
+        for (int q = 0; q < QU; ++q) {
+          const int64_t c = cb + q * QNT;
+          if (c >= chunks) break;
+          const float4 a = av[q], b = bv[q];
+          const float w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+          const unsigned cw = cwv[q];
+          const float iw[8] = {iav[q].x, iav[q].y, iav[q].z, iav[q].w, ibv[q].x, ibv[q].y, ibv[q].z, ibv[q].w};
+          const float s8 = s8v[q];
+#pragma unroll
+          for (int t = 0; t < 8; ++t) {
+              const unsigned nib = (cw >> (4 * t)) & 0xFu;
+              const float cv = NF4 ? lev[nib] : (float)((int)nib - ((nib & 8u) ? 16 : 0));
+              const float sc = G >= 8 ? s8 : srow[(8 * c + t) >> lg];
+              const double d = (double)w[t] - (double)cv * (double)sc;
+              num += (double)iw[t] * d * d;
+              den += (double)iw[t] * (double)w[t] * (double)w[t];
+          }
+        }
+      }
     }
     block_sum2(num, den, sh);
     if (threadIdx.x == 0) {
@@ -450,17 +765,42 @@ __global__ __launch_bounds__(RTN_NT) void rtn8_kernel(const float *__restrict__ 
         lev[threadIdx.x] = kNF4[threadIdx.x];
     }
     if (NF4) __syncthreads();
-    const int64_t chunks = K / 8, total = N * chunks;
+    const int64_t chunks = K / 8;
     const int64_t ngroups = K / G;
+    const int lg = __builtin_ctz((unsigned)G);               // G is a power of two
     double num = 0.0, den = 0.0;
     bool bad = false;
-    for (int64_t base = (int64_t)blockIdx.x * RTN_NT; base < total; base += (int64_t)gridDim.x * RTN_NT) {
-        const int64_t idx = base + threadIdx.x;
-        const bool valid = idx < total;
-        const int64_t id = valid ? idx : 0;          // every lane takes part in the exchanges
-        const int64_t row = id / chunks, c = id - row * chunks;
-        const float4 a = *(const float4 *)(W + row * K + 8 * c);
-        const float4 b = *(const float4 *)(W + row * K + 8 * c + 4);
+    // Passes: rows by workgroup, a row's 8-column chunks 256 at a time (every
+    // lane takes part in each pass, those past the row with a dummy chunk; a
+    // group of G/8 lanes is wholly in or out, since 256 and the row's chunk
+    // count are multiples of G/8).  The next pass's weights are loaded before
+    // this pass's arithmetic, so that two passes' loads are in flight.
+    auto wload = [&](int64_t row, int64_t cbase, float4 &a, float4 &b, float4 &ia, float4 &ib) {
+        const int64_t cc = cbase + threadIdx.x < chunks ? cbase + threadIdx.x : 0;
+        a = *(const float4 *)(W + row * K + 8 * cc);
+        b = *(const float4 *)(W + row * K + 8 * cc + 4);
+        if (partials && imp) {                       // 16-byte aligned (checked at launch)
+            ia = *(const float4 *)(imp + 8 * cc);
+            ib = *(const float4 *)(imp + 8 * cc + 4);
+        } else {
+            ia = ib = make_float4(1.0f, 1.0f, 1.0f, 1.0f);
+        }
+    };
+    float4 na, nbv, nia, nib;
+    int64_t row = blockIdx.x, cbase = 0;
+    if (row < N) wload(row, cbase, na, nbv, nia, nib);
+    for (; row < N;) {
+        const int64_t cb = cbase + threadIdx.x;
+        const bool valid = cb < chunks;
+        const int64_t c = valid ? cb : 0;
+        const float4 a = na, b = nbv, i0 = nia, i1 = nib;
+        const int64_t prow = row;
+        cbase += RTN_NT;
+        if (cbase >= chunks) {
+            cbase = 0;
+            row += gridDim.x;
+        }
+        if (row < N) wload(row, cbase, na, nbv, nia, nib);
         const float w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
 #pragma unroll
         for (int t = 0; t < 8; ++t) bad = bad || (valid && !isfinite(w[t]));
@@ -491,28 +831,23 @@ __global__ __launch_bounds__(RTN_NT) void rtn8_kernel(const float *__restrict__ 
             for (int t = 0; t < 8; ++t) m = fmaxf(m, fabsf(w[t]));
             for (int o = 1; o < G / 8; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
             const float sg = NF4 ? m : m / 7.0f;
-            if (valid && c % (G / 8) == 0) scales[row * ngroups + 8 * c / G] = sg;
+            if (valid && (c & ((G >> 3) - 1)) == 0) scales[prow * ngroups + ((8 * c) >> lg)] = sg;
             codes_of(sg, 0, 8);
         } else {
             for (int g0 = 0; g0 < 8; g0 += G) {
                 float m = 0.0f;
                 for (int t = g0; t < g0 + G; ++t) m = fmaxf(m, fabsf(w[t]));
                 const float sg = NF4 ? m : m / 7.0f;
-                if (valid) scales[row * ngroups + (8 * c + g0) / G] = sg;
+                if (valid) scales[prow * ngroups + ((8 * c + g0) >> lg)] = sg;
                 codes_of(sg, g0, g0 + G);
             }
         }
         unsigned dw = 0;
 #pragma unroll
         for (int t = 0; t < 8; ++t) dw |= nb[t] << (4 * t);
-        if (valid) *(unsigned *)(codes + row * (K / 2) + 4 * c) = dw;
+        if (valid) *(unsigned *)(codes + prow * (K / 2) + 4 * c) = dw;
         if (partials && valid) {
-            float iw[8] = {1.0f, 1.0f, 1.0f, 1.0f, 1.0f, 1.0f, 1.0f, 1.0f};
-            if (imp) {                               // 16-byte aligned (checked at launch)
-                const float4 i0 = *(const float4 *)(imp + 8 * c), i1 = *(const float4 *)(imp + 8 * c + 4);
-                iw[0] = i0.x; iw[1] = i0.y; iw[2] = i0.z; iw[3] = i0.w;
-                iw[4] = i1.x; iw[5] = i1.y; iw[6] = i1.z; iw[7] = i1.w;
-            }
+            const float iw[8] = {i0.x, i0.y, i0.z, i0.w, i1.x, i1.y, i1.z, i1.w};
 #pragma unroll
             for (int t = 0; t < 8; ++t) {
                 const double wi = (double)iw[t];
@@ -596,25 +931,33 @@ template <int MODE>
 hipError_t launch_sweep_mode(float *Wk, float *ET, uint8_t *codes, float *scales, const float *U, int64_t N,
                              int64_t K, int64_t G, int64_t b0, const int *gidx, hipStream_t s)
 {
-    const int64_t nwg = (N + ROWS_WG - 1) / ROWS_WG;
-    const dim3 grid((unsigned)nwg), block(SW_NT);
+    // the API admits powers of two up to 128 only
+    if (G < 1 || G > BW || (G & (G - 1))) return hipErrorInvalidValue;
+    const int lg = __builtin_ctzll((unsigned long long)G);
+    const int64_t nwg = (N + S4_ROWS - 1) / S4_ROWS;
+    if constexpr (!(MODE & MODE_STATIC)) {
+        // groups shorter than a quarter start inside it: the 16-lane form, with
+        // the group size fixed at compile time
+        if (G < 32) {
+            const dim3 grid((unsigned)((N + ROWS_WG - 1) / ROWS_WG)), block(SW_NT);
 #define GQ_SWEEP_CASE(g)                                                                                      \
     case g:                                                                                                   \
         hipLaunchKernelGGL((sweep_block_kernel<g, MODE>), grid, block, 0, s, Wk, ET, codes, scales, U, N, K, b0, \
                            gidx);                                                                             \
         break;
-    switch (G) {
-        GQ_SWEEP_CASE(1)
-        GQ_SWEEP_CASE(2)
-        GQ_SWEEP_CASE(4)
-        GQ_SWEEP_CASE(8)
-        GQ_SWEEP_CASE(16)
-        GQ_SWEEP_CASE(32)
-        GQ_SWEEP_CASE(64)
-        GQ_SWEEP_CASE(128)
-    default: return hipErrorInvalidValue;      // the API admits powers of two up to 128 only
-    }
+            switch (G) {
+                GQ_SWEEP_CASE(1)
+                GQ_SWEEP_CASE(2)
+                GQ_SWEEP_CASE(4)
+                GQ_SWEEP_CASE(8)
+                GQ_SWEEP_CASE(16)
+            }
 #undef GQ_SWEEP_CASE
+            return hipGetLastError();
+        }
+    }
+    hipLaunchKernelGGL((sweep4_kernel<MODE>), dim3((unsigned)nwg), dim3(S4_NT), 0, s, Wk, ET, codes, scales, U,
+                       N, K, lg, b0, gidx);
     return hipGetLastError();
 }
 
