@@ -191,15 +191,17 @@ def test_attn_gptq_full(gq, orc, attn, attn_U):
 
 @pytest.mark.parametrize("flags", [1, 2, 3])
 def test_attn_gptq_variants(gq, orc, attn, attn_U, flags):
-    """The variants (static groups, NF4, both) at full size: 96 sampled rows
+    """The variants (static groups, NF4, both) at full size: all 10240 rows
     against the oracle's sweep and replay under the same U, static scales against
     round to nearest bit for bit, and the device's qerr against the oracle's qerr
-    of the device's own codes over all 10240 rows.  Every decision must be
-    admissible and at least 99.9% of them identical given the same history (the
-    replay); the raw identity against the oracle's own trajectory is held to 99%
-    under NF4 with dynamic scales, where each tie flip (about one per 160000
-    decisions) is followed by a few hundred differing codes further along its row
-    (the plain grid: under two hundred)."""
+    of the device's own codes.  Every decision must be admissible and at least
+    99.9% of them identical given the same history (the replay); the raw identity
+    against the oracle's own trajectory is held to 99.9% on the uniform grid and
+    to 99% under NF4, where each tie flip (about one per 1.3 M decisions on the
+    uniform grid) is followed by a few hundred differing codes further along its
+    row.  Raw identity is taken over all rows: a sample of 96 rows holds a few
+    flips at most, and measured on this workload it ranged from 99.85% to 100%
+    around the all-row 99.98% of the static grid."""
     wl, X, W, H, blob, Hs, P = attn
     N, K, G = wl.N[0], wl.K, wl.group
     imp = blob[: 4 * K].view(torch.float32)
@@ -210,13 +212,12 @@ def test_attn_gptq_variants(gq, orc, attn, attn_U, flags):
     Wn, impn = W.numpy(), imp.cpu().numpy().copy()
     call = orc.unpack_codes(codes.cpu().numpy(), K, flags=flags)
     sall = scales.cpu().numpy()
-    rows = np.sort(np.random.default_rng(flags).choice(N, 96, replace=False))
-    rep = orc.gptq_replay(call[rows], sall[rows], Wn, attn_U, G, rows=rows, flags=flags)
-    oc, os_ = orc.gptq_sweep(Wn, attn_U, G, rows=rows, flags=flags)
-    ident = float((call[rows] == oc).mean())
-    print(f"K=5120 flags {flags}: code identity {ident:.6f} on 96 rows, replay {rep}, qerr {q:.5f}")
+    rep = orc.gptq_replay(call, sall, Wn, attn_U, G, flags=flags)
+    oc, os_ = orc.gptq_sweep(Wn, attn_U, G, flags=flags)
+    ident = float((call == oc).mean())
+    print(f"K=5120 flags {flags}: code identity {ident:.6f} on all rows, replay {rep}, qerr {q:.5f}")
     assert rep["inadmissible"] == 0 and rep["scale_mismatch"] == 0
-    assert rep["exact"] >= 0.999 * call[rows].size
+    assert rep["exact"] >= 0.999 * call.size
     assert ident >= (0.999 if flags == orc.STATIC_GROUPS else 0.99)
     if flags & orc.STATIC_GROUPS:
         _, rs = orc.rtn(Wn, G, flags=flags & orc.NF4)
