@@ -237,19 +237,6 @@ __device__ __attribute__((noinline)) bool wave_factor32(double (*A)[NBMAX + 1], 
     return badp;
 }
 
-// As solve32 for a 32 x 32 block stored at rows 0..31, columns o.. of R.
-__device__ inline void solve32_rows(const double (*R)[NBMAX + 1], const double *rinv, int o, double (&b)[SB])
-{
-    static_for<SB>([&](auto KK) {
-        constexpr int k = decltype(KK)::value;
-        b[k] *= rinv[o + k];
-        static_for<SB - 1 - k>([&](auto JJ) {
-            constexpr int j = k + 1 + decltype(JJ)::value;
-            b[j] = fma(-R[k][o + j], b[k], b[j]);
-        });
-    });
-}
-
 // In one thread: b <- R^-T b for the 32 x 32 upper block R at (o, o) of A (its
 // 1 / R_kk in rinv[o + k]), b in registers; forward substitution, R read by
 // broadcast.
@@ -368,6 +355,10 @@ __global__ __launch_bounds__(PNT) void potrf_diag_kernel(double *__restrict__ M,
 // workgroup per 64 columns of B (nb x ncols, ld ldb), held in LDS.  Y goes to
 // out (ld ldo; out may be B: each workgroup reads its columns before it writes
 // them) and, with out_t set, transposed to out_t (out_t[c ldt + a] = Y[a][c]).
+// Memory is read in batches, every load of a batch issued before any of its
+// values is stored (clamped addresses, selects after): B's block once, and for
+// each s the column strip R[0 .. 32 s + 31][32 s .. 32 s + 31] it needs, so a
+// workgroup waits on memory five times rather than once per element it reads.
 constexpr int TSC = 64;
 constexpr int TST = 256;
 __global__ __launch_bounds__(TST) void trsm_rt_kernel(const double *__restrict__ M, int64_t K, int64_t p0, int nb,
@@ -377,52 +368,76 @@ __global__ __launch_bounds__(TST) void trsm_rt_kernel(const double *__restrict__
                                                       int64_t ncols)
 {
     __shared__ double Ys[NBMAX][TSC + 1];
-    __shared__ double Rs[SB][NBMAX + 1];          // R_ts rows of the current block (solve32 layout)
+    __shared__ double Rs[NBMAX][SB + 1];          // R[0 .. 32 s + 31][32 s .. 32 s + 31]
     __shared__ double rinv[NBMAX];
     const int t = threadIdx.x, a = t & 31, cg = t >> 5;
     const int64_t c0 = (int64_t)blockIdx.x * TSC;
     const int nsb = (nb + SB - 1) / SB;
-    for (int e = t; e < NBMAX * TSC; e += TST) {
-        const int r = e / TSC, c = e % TSC;
-        Ys[r][c] = (r < nb && c0 + c < ncols) ? B[r * ldb + c0 + c] : 0.0;
+    {
+        constexpr int PER = NBMAX * TSC / TST;
+        double v[PER];
+#pragma unroll
+        for (int m = 0; m < PER; ++m) {
+            const int e = t + TST * m, r = e / TSC, c = e % TSC;
+            const bool in = r < nb && c0 + c < ncols;
+            v[m] = B[in ? r * ldb + c0 + c : 0];
+        }
+#pragma unroll
+        for (int m = 0; m < PER; ++m) {
+            const int e = t + TST * m, r = e / TSC, c = e % TSC;
+            const bool in = r < nb && c0 + c < ncols;
+            Ys[r][c] = in ? v[m] : 0.0;
+        }
     }
     if (t < NBMAX) rinv[t] = rinv_in[t];
-    __syncthreads();
 #pragma unroll 1
     for (int s = 0; s < nsb; ++s) {
+        // the strip of R this block row needs: rows 0 .. 32 s + 31 of its 32
+        // columns (the identity past nb); element (rr, aa) is m-th of thread t
+        // for rr * SB + aa = t + TST m
+        {
+            constexpr int PER = NBMAX * SB / TST;
+            const int rows = SB * (s + 1);
+            double v[PER];
+#pragma unroll
+            for (int m = 0; m < PER; ++m) {
+                const int e = t + TST * m, rr = e / SB, cc = SB * s + e % SB;
+                const bool in = rr < rows && rr < nb && cc < nb;
+                v[m] = M[in ? (p0 + rr) * K + p0 + cc : p0 * K + p0];
+            }
+#pragma unroll
+            for (int m = 0; m < PER; ++m) {
+                const int e = t + TST * m, rr = e / SB, cc = SB * s + e % SB;
+                if (rr < rows) Rs[rr][e % SB] = (rr < nb && cc < nb) ? v[m] : (rr == cc ? 1.0 : 0.0);
+            }
+        }
+        __syncthreads();
         double acc[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc[j] = Ys[SB * s + a][8 * cg + j];
-#pragma unroll 1
-        for (int tb = 0; tb < s; ++tb) {
-            // R_ts (rows 32 tb.., columns 32 s..); past nb it is zero
-            for (int e = t; e < SB * SB; e += TST) {
-                const int k = e / SB, aa = e % SB, rr = SB * tb + k, cc = SB * s + aa;
-                Rs[k][aa] = (rr < nb && cc < nb) ? M[(p0 + rr) * K + p0 + cc] : 0.0;
-            }
-            __syncthreads();
 #pragma unroll 4
-            for (int k = 0; k < SB; ++k) {
-                const double r = Rs[k][a];
+        for (int k = 0; k < SB * s; ++k) {
+            const double r = Rs[k][a];
 #pragma unroll
-                for (int j = 0; j < 8; ++j) acc[j] = fma(-r, Ys[SB * tb + k][8 * cg + j], acc[j]);
-            }
-            __syncthreads();
+            for (int j = 0; j < 8; ++j) acc[j] = fma(-r, Ys[k][8 * cg + j], acc[j]);
         }
-        // R_ss (identity past nb) into Rs columns 32 s.., as rows 0..31 of a
-        // block at offset (0, 32 s) of the solve32 layout
-        for (int e = t; e < SB * SB; e += TST) {
-            const int k = e / SB, aa = e % SB, rr = SB * s + k, cc = SB * s + aa;
-            Rs[k][SB * s + aa] = (rr < nb && cc < nb) ? M[(p0 + rr) * K + p0 + cc] : (rr == cc ? 1.0 : 0.0);
-        }
+        // (the update reads rows of Ys before block s only)
 #pragma unroll
         for (int j = 0; j < 8; ++j) Ys[SB * s + a][8 * cg + j] = acc[j];
         __syncthreads();
         if (t < TSC) {
+            // b <- R_ss^-T b, R_ss = Rs[32 s + k][j]
             double b[SB];
 #pragma unroll
             for (int k = 0; k < SB; ++k) b[k] = Ys[SB * s + k][t];
-            solve32_rows(Rs, rinv, SB * s, b);
+            static_for<SB>([&](auto KK) {
+                constexpr int k = decltype(KK)::value;
+                b[k] *= rinv[SB * s + k];
+                static_for<SB - 1 - k>([&](auto JJ) {
+                    constexpr int j = k + 1 + decltype(JJ)::value;
+                    b[j] = fma(-Rs[SB * s + k][j], b[k], b[j]);
+                });
+            });
 #pragma unroll
             for (int k = 0; k < SB; ++k) Ys[SB * s + k][t] = b[k];
         }
