@@ -166,15 +166,19 @@ template <typename T> struct Tile {
                 for (int r = 0; r < MF::NACC; ++r) acc[bi][bj][r] = (T)0;
         if (s1 <= s0) return;
 
-        vec_t ra[NV], rb[NV];
-        auto gload = [&](int64_t kb) {
+        // Global loads go through registers: fp32 keeps two stages in flight
+        // (a stage of its 64-cycle instructions is shorter than a load under
+        // load), fp64 one.
+        constexpr int D = sizeof(T) == 4 ? 2 : 1;
+        vec_t ra[D][NV], rb[D][NV];
+        auto gload = [&](int64_t kb, int sl) {
             const bool full_k = kb + BK <= d.Kd;
             if (full_i && full_k) {
 #pragma unroll
                 for (int v = 0; v < NV; ++v) {
                     const int lin = tid + NT * v;
                     const int kr = lin / VPR, cc = (lin % VPR) * V;
-                    ra[v] = *(const vec_t *)(A + (kb + kr) * d.lda + i0 + cc);
+                    ra[sl][v] = *(const vec_t *)(A + (kb + kr) * d.lda + i0 + cc);
                 }
             } else {
 #pragma unroll
@@ -186,7 +190,7 @@ template <typename T> struct Tile {
                     for (int e = 0; e < V; ++e) {
                         const bool ok = k < d.Kd && i0 + cc + e < d.M;
                         const T x = A[ok ? k * d.lda + i0 + cc + e : 0];
-                        ra[v][e] = ok ? x : (T)0;
+                        ra[sl][v][e] = ok ? x : (T)0;
                     }
                 }
             }
@@ -195,7 +199,7 @@ template <typename T> struct Tile {
                 for (int v = 0; v < NV; ++v) {
                     const int lin = tid + NT * v;
                     const int kr = lin / VPR, cc = (lin % VPR) * V;
-                    rb[v] = *(const vec_t *)(B + (kb + kr) * d.ldb + j0 + cc);
+                    rb[sl][v] = *(const vec_t *)(B + (kb + kr) * d.ldb + j0 + cc);
                 }
             } else {
 #pragma unroll
@@ -207,27 +211,21 @@ template <typename T> struct Tile {
                     for (int e = 0; e < V; ++e) {
                         const bool ok = k < d.Kd && j0 + cc + e < d.N;
                         const T x = B[ok ? k * d.ldb + j0 + cc + e : 0];
-                        rb[v][e] = ok ? x : (T)0;
+                        rb[sl][v][e] = ok ? x : (T)0;
                     }
                 }
             }
         };
-        auto sstore = [&](int buf) {
+        auto sstore = [&](int buf, int sl) {
 #pragma unroll
             for (int v = 0; v < NV; ++v) {
                 const int lin = tid + NT * v;
                 const int kr = lin / VPR, cc = (lin % VPR) * V;
-                *(vec_t *)&sm.As[buf][kr][cc] = ra[v];
-                *(vec_t *)&sm.Bs[buf][kr][cc] = rb[v];
+                *(vec_t *)&sm.As[buf][kr][cc] = ra[sl][v];
+                *(vec_t *)&sm.Bs[buf][kr][cc] = rb[sl][v];
             }
         };
-
-        gload(s0 * BK);
-        sstore(0);
-        __syncthreads();
-        for (int64_t kt = s0; kt < s1; ++kt) {
-            const int buf = (int)((kt - s0) & 1);
-            if (kt + 1 < s1) gload((kt + 1) * BK);
+        auto compute = [&](int buf) {
             const int m = lane % MF::LPK;
 #pragma unroll
             for (int kk = 0; kk < BK; kk += MF::KSTEP) {
@@ -242,8 +240,39 @@ template <typename T> struct Tile {
 #pragma unroll
                     for (int bj = 0; bj < MF::NB; ++bj) acc[bi][bj] = MF::mma(a[bi], b[bj], acc[bi][bj]);
             }
-            if (kt + 1 < s1) sstore(buf ^ 1);
-            __syncthreads();
+        };
+
+        gload(s0 * BK, 0);
+        sstore(0, 0);
+        if constexpr (D == 2) {
+            if (s0 + 1 < s1) gload((s0 + 1) * BK, 1);
+        }
+        __syncthreads();
+        if constexpr (D == 2) {
+            // stage kt sits in LDS buffer (kt - s0) & 1; stage kt + 1 in register
+            // slot (kt - s0 + 1) & 1, and stage kt + 2 is loaded into the other
+            int64_t kt = s0;
+            auto iter = [&](auto SL) {
+                constexpr int sl = decltype(SL)::value;        // (kt - s0) & 1
+                if (kt + 2 < s1) gload((kt + 2) * BK, sl);
+                compute(sl);
+                if (kt + 1 < s1) sstore(sl ^ 1, sl ^ 1);
+                __syncthreads();
+                ++kt;
+            };
+            while (kt + 1 < s1) {
+                iter(std::integral_constant<int, 0>{});
+                iter(std::integral_constant<int, 1>{});
+            }
+            if (kt < s1) iter(std::integral_constant<int, 0>{});
+        } else {
+            for (int64_t kt = s0; kt < s1; ++kt) {
+                const int buf = (int)((kt - s0) & 1);
+                if (kt + 1 < s1) gload((kt + 1) * BK, 0);
+                compute(buf);
+                if (kt + 1 < s1) sstore(buf ^ 1, 0);
+                __syncthreads();
+            }
         }
     }
 
@@ -355,8 +384,24 @@ template <typename T> struct Tile {
         OutT *out = (OutT *)d.out;
         OutT *out_t = (OutT *)d.out_t;
         const T *cin = (const T *)d.cin;
+        // One row of blocks at a time (32 fp32 or 16 fp64 values per lane): its
+        // cin values are all loaded, from clamped addresses, before any is used,
+        // so the tile waits on memory once per block row rather than once per
+        // element.
 #pragma unroll
-        for (int bi = 0; bi < MF::NB; ++bi)
+        for (int bi = 0; bi < MF::NB; ++bi) {
+            T c[MF::NB][MF::NACC];
+            if (beta != 0.0) {
+#pragma unroll
+                for (int bj = 0; bj < MF::NB; ++bj)
+#pragma unroll
+                    for (int r = 0; r < MF::NACC; ++r) {
+                        const int64_t gi = i0 + wr * 64 + bi * MF::BLK + MF::row(lane, r);
+                        const int64_t gj = j0 + wc * 64 + bj * MF::BLK + MF::col(lane, r);
+                        const bool in = gi < d.M && gj < d.N;
+                        c[bj][r] = cin[in ? gi * d.ldc + gj : 0];
+                    }
+            }
 #pragma unroll
             for (int bj = 0; bj < MF::NB; ++bj)
 #pragma unroll
@@ -367,10 +412,11 @@ template <typename T> struct Tile {
                     if (d.tri == 1 && gi < gj) continue;
                     if (d.tri == 2 && gi > gj) continue;
                     double v = alpha * (double)acc[bi][bj][r];
-                    if (beta != 0.0) v += beta * (double)cin[gi * d.ldc + gj];
+                    if (beta != 0.0) v += beta * (double)c[bj][r];
                     out[gi * d.ldo + gj] = (OutT)v;
                     if (out_t) out_t[gj * d.ldo + gi] = (OutT)v;
                 }
+        }
     }
 };
 
