@@ -344,12 +344,28 @@ __global__ __launch_bounds__(S4_NT, 1) void sweep4_kernel(float *__restrict__ Wk
     // given, else column / G) and RN(1 / (scale * guard factor))
     float sl[STATIC ? 32 : 1], yl[STATIC ? 32 : 1];
     if constexpr (STATIC) {
+        // every group index, then every scale, loaded from clamped addresses
+        // before any is used: two waits on memory instead of one per column
+        int64_t gi[32];
+        if (gidx) {
+            int gv[32];
+#pragma unroll
+            for (int t = 0; t < 32; ++t) gv[t] = gidx[(rv && cb + t < bw) ? b0 + cb + t : 0];
+#pragma unroll
+            for (int t = 0; t < 32; ++t) gi[t] = gv[t];
+        } else {
+#pragma unroll
+            for (int t = 0; t < 32; ++t) gi[t] = (b0 + cb + t) >> lg;
+        }
 #pragma unroll
         for (int t = 0; t < 32; ++t) {
-            const int64_t col = b0 + cb + t;
             const bool ok = rv && cb + t < bw;
-            const int64_t gi = ok ? (gidx ? (int64_t)gidx[col] : col >> lg) : 0;
-            sl[t] = ok ? scales[row * ngroups + gi] : 0.0f;
+            sl[t] = scales[ok ? row * ngroups + gi[t] : 0];
+        }
+#pragma unroll
+        for (int t = 0; t < 32; ++t) {
+            const bool ok = rv && cb + t < bw;
+            sl[t] = ok ? sl[t] : 0.0f;
             const float ft = sl[t] < 0x1p-60f ? 0x1p64f : 1.0f;
             yl[t] = sl[t] != 0.0f ? 1.0f / (sl[t] * ft) : 0.0f;
         }

@@ -225,17 +225,26 @@ __global__ __launch_bounds__(GNT, 1) void gram_bf16_kernel(float *__restrict__ H
     step(I0{}, I2{}, Y{}, N{}, nk - 2);
     step(I1{}, I0{}, N{}, N{}, nk - 1);
 
-    // H += acc on the lower triangle
+    // H += acc on the lower triangle, one 32 x 32 block at a time (its values
+    // of H loaded before any is updated)
 #pragma unroll
     for (int bi = 0; bi < 2; ++bi)
 #pragma unroll
-        for (int bj = 0; bj < 4; ++bj)
+        for (int bj = 0; bj < 4; ++bj) {
+            float h[16];
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
                 const int64_t gi = i0 + wr * 64 + bi * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
                 const int64_t gj = j0 + wc * 128 + bj * 32 + m;
-                if (gi < K && gj < K && gi >= gj) H[gi * K + gj] += acc[bi][bj][e];
+                h[e] = H[(gi < K && gj < K) ? gi * K + gj : 0];
             }
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int64_t gi = i0 + wr * 64 + bi * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+                const int64_t gj = j0 + wc * 128 + bj * 32 + m;
+                if (gi < K && gj < K && gi >= gj) H[gi * K + gj] = h[e] + acc[bi][bj][e];
+            }
+        }
 }
 
 
@@ -446,17 +455,27 @@ __global__ __launch_bounds__(RNT, 1) void gram_bf16_dma_kernel(float *__restrict
 
     const int m = lane & 31;
     if constexpr (DIRECT) {
-        // H += acc on the lower triangle
+        // H += acc on the lower triangle, one 32 x 32 block at a time: its 16
+        // values of H are loaded (from clamped addresses) before any is
+        // updated, so the tile waits on memory once per block, not per element
 #pragma unroll
         for (int bi = 0; bi < 4; ++bi)
 #pragma unroll
-            for (int bj = 0; bj < 4; ++bj)
+            for (int bj = 0; bj < 4; ++bj) {
+                float h[16];
 #pragma unroll
                 for (int x = 0; x < 16; ++x) {
                     const int64_t gi = i0 + wr * 128 + bi * 32 + 8 * (x >> 2) + 4 * (lane >> 5) + (x & 3);
                     const int64_t gj = j0 + wc * 128 + bj * 32 + m;
-                    if (gi < K && gj < K && gi >= gj) H[gi * K + gj] += acc[bi][bj][x];
+                    h[x] = H[(gi < K && gj < K) ? gi * K + gj : 0];
                 }
+#pragma unroll
+                for (int x = 0; x < 16; ++x) {
+                    const int64_t gi = i0 + wr * 128 + bi * 32 + 8 * (x >> 2) + 4 * (lane >> 5) + (x & 3);
+                    const int64_t gj = j0 + wc * 128 + bj * 32 + m;
+                    if (gi < K && gj < K && gi >= gj) H[gi * K + gj] = h[x] + acc[bi][bj][x];
+                }
+            }
     } else {
         // this split's tile, thread-major: 256 floats per thread
         float4 *dst = (float4 *)(part + ((tile * splits + split) * RNT + tid) * 256);
@@ -499,11 +518,18 @@ __global__ __launch_bounds__(RNT) void gram_split_sum_kernel(float *__restrict__
                 sum[4 * v + 3] += q.w;
             }
         }
+        float h[16];
 #pragma unroll
         for (int x = 0; x < 16; ++x) {
             const int64_t gi = i0 + wr * 128 + bi * 32 + 8 * (x >> 2) + 4 * (lane >> 5) + (x & 3);
             const int64_t gj = j0 + wc * 128 + bj * 32 + m;
-            if (gi < K && gj < K && gi >= gj) H[gi * K + gj] += sum[x];
+            h[x] = H[(gi < K && gj < K) ? gi * K + gj : 0];
+        }
+#pragma unroll
+        for (int x = 0; x < 16; ++x) {
+            const int64_t gi = i0 + wr * 128 + bi * 32 + 8 * (x >> 2) + 4 * (lane >> 5) + (x & 3);
+            const int64_t gj = j0 + wc * 128 + bj * 32 + m;
+            if (gi < K && gj < K && gi >= gj) H[gi * K + gj] = h[x] + sum[x];
         }
     }
 }

@@ -130,7 +130,21 @@ __global__ __launch_bounds__(256) void tril_unpack4_kernel(float *__restrict__ H
     const uint16_t *tril = (const uint16_t *)(blob + 4 * K);
     const int c4 = 4 * (threadIdx.x & 15);
     const int rq = threadIdx.x >> 4;      // 0..15
-    // lower part (and diagonal) of the tile, row by row
+    // lower part (and diagonal) of the tile, row by row.  Every value the
+    // thread needs is loaded first, from clamped addresses, so it waits on
+    // memory once rather than once per element.
+    uint16_t tv[TU / 16][4];
+    uint32_t dv[TU / 16];
+#pragma unroll
+    for (int k = 0; k < TU / 16; ++k) {
+        const int64_t i = i0 + rq + 16 * k;
+        dv[k] = diag[i < K ? i : 0];
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+            const int64_t j = j0 + c4 + x;
+            tv[k][x] = tril[(i < K && j < i) ? i * (i - 1) / 2 + j : 0];
+        }
+    }
 #pragma unroll
     for (int k = 0; k < TU / 16; ++k) {
         const int r = rq + 16 * k;
@@ -140,8 +154,8 @@ __global__ __launch_bounds__(256) void tril_unpack4_kernel(float *__restrict__ H
         for (int x = 0; x < 4; ++x) {
             const int64_t j = j0 + c4 + x;
             float f = 0.0f;
-            if (i < K && j < i) f = __uint_as_float((uint32_t)tril[i * (i - 1) / 2 + j] << 16);
-            else if (i < K && j == i) f = __uint_as_float(diag[i]);
+            if (i < K && j < i) f = __uint_as_float((uint32_t)tv[k][x] << 16);
+            else if (i < K && j == i) f = __uint_as_float(dv[k]);
             v[x] = f;
             tile[r][c4 + x] = f;
         }
