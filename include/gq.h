@@ -14,8 +14,12 @@
  *     join it back into the caller's stream with events before they
  *     synchronise it, so no work of a call is pending when it returns;
  *   - the testing and profiling settings at the end of this header
- *     (thread-local).
- *   Nothing else: no device memory, no cache of inputs or results.
+ *     (thread-local), and the HIP events timed psd_project calls record into
+ *     (created when timing is first used on a thread);
+ *   - one 64 KiB static device array per device (GQ_NOALLOC_SCRATCH_BYTES),
+ *     part of the code object: the scratch of rtn_quantize_noalloc only.
+ *   Nothing else: no device memory allocated at run time, no cache of inputs
+ *   or results.
  *
  * Conventions shared by every call
  *   - Pointers are DEVICE pointers unless marked "host".  Device buffers must be
