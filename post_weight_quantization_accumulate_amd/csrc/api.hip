@@ -191,6 +191,7 @@ struct PsdWs {
     int8_t *RH, *RX, *RY;      // split forms of H, the iterate X and Y0 / Z (emulated path)
     uint8_t *Cres;             // residues of one product
     int *eH;                   // row exponents of H's split form
+    unsigned long long *hmax;  // largest magnitude of each row of H (fp64 bits)
 };
 
 PsdWs carve_psd(Carver &c, int64_t K, bool emulated)
@@ -207,6 +208,7 @@ PsdWs carve_psd(Carver &c, int64_t K, bool emulated)
         w.RY = c.take<int8_t>(pb);
         w.Cres = c.take<uint8_t>(pb);
         w.eH = c.take<int>((size_t)oz_padded(K));
+        w.hmax = c.take<unsigned long long>((size_t)K);
     } else {
         w.X = c.take<double>(n);
         w.Y = c.take<double>(n);
@@ -702,7 +704,8 @@ int psd_project(float *H, int64_t K, void *ws, size_t ws_bytes, hipStream_t stre
     double *c1inv = w.sc.d + 4, *c3inv = w.sc.d + 5;
     GQ_HIP(launch_fill_u32(status, 4, 0u, stream), "fill");
     if (w.flags) GQ_HIP(launch_fill_u32(w.flags, kStreamKMaxWorkers, 0u, stream), "fill");
-    GQ_HIP(launch_sym_lower_to_f64(w.H64, H, K, status, stream), "symmetrise");
+    if (w.hmax) GQ_HIP(launch_fill_u32((unsigned *)w.hmax, 2 * K, 0u, stream), "fill");
+    GQ_HIP(launch_sym_lower_to_f64(w.H64, H, K, status, stream, w.hmax), "symmetrise");
     GQ_HIP(launch_frobenius(fro, w.H64, n, w.sc.partials, stream), "norm");
     GQ_HIP(launch_scalar_combine(inv, fro, -1.0, nullptr, 0.0, stream), "inverse norm");
     // mean(diag H) for the schedule's start (its status word is a scratch word
@@ -747,12 +750,12 @@ int psd_project(float *H, int64_t K, void *ws, size_t ws_bytes, hipStream_t stre
         //   Z  = a I + b X^2                          (spectrum in [a + b, a], |a| < 2.6: exponent 2)
         //   X' = X Z                                  (= a X + b X^3)
         // so no fp64 iterate is stored.  The CRT writes only the K x K corner
-        // of a split form, so the padding of those planes is cleared here once.
+        // of a split form (rounded up to 64 columns), so the rest of those
+        // planes is cleared here once.
         const int beta = oz_beta(K);
-        const size_t pb = oz_planes_bytes(K);
-        GQ_HIP(launch_zero_bytes(w.RX, pb, stream), "clear");
-        GQ_HIP(launch_zero_bytes(w.RY, pb, stream), "clear");
-        GQ_HIP(oz_split(w.H64, K, beta, w.RH, w.eH, stream), "split H");
+        GQ_HIP(oz_clear_padding(w.RX, K, stream), "clear");
+        GQ_HIP(oz_clear_padding(w.RY, K, stream), "clear");
+        GQ_HIP(oz_split(w.H64, K, beta, w.RH, w.eH, stream, w.hmax), "split H");
         const OzOperand opH{w.RH, w.eH, 0}, opX{w.RX, nullptr, 1}, opY0{w.RY, nullptr, 1}, opZ{w.RY, nullptr, 2};
         auto product = [&](const GemmDesc &d, const OzOperand &A, const OzOperand &B, bool out_f32,
                            const OzOut &o) -> hipError_t {

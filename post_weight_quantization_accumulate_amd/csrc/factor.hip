@@ -33,16 +33,55 @@ __global__ void set_identity_f64_kernel(double *X, int64_t K)
         X[e] = (e / K == e % K) ? 1.0 : 0.0;
 }
 
-// D[i][j] = D[j][i] = H[max][min] as fp64, from the lower triangle only.
+// D[i][j] = D[j][i] = H[max][min] as fp64, from the lower triangle only.  One
+// 64 x 64 lower tile of H per workgroup, read by rows into LDS and written to
+// D both as it is and transposed (the mirror), so that every read and write
+// runs along rows.  On a diagonal tile the entries above the diagonal come
+// from their mirror inside the tile.  With rowmax set (zeroed beforehand) it
+// also leaves there the largest magnitude of each row of D, as the bits of a
+// non-negative fp64 (whose order is that of unsigned integers, so the rows'
+// maxima over the tiles are taken with atomicMax, in any order).
+constexpr int SYT = 64;
 __global__ __launch_bounds__(NT) void sym_lower_kernel(double *__restrict__ D, const float *__restrict__ H,
-                                                      int64_t K, unsigned *status)
+                                                      int64_t K, unsigned *status,
+                                                      unsigned long long *__restrict__ rowmax)
 {
-    const int64_t i = blockIdx.x;
+    __shared__ float t[SYT][SYT + 1];
+    const int64_t id = blockIdx.x;
+    int64_t ti = (int64_t)((sqrt(8.0 * (double)id + 1.0) - 1.0) * 0.5);
+    while (ti * (ti + 1) / 2 > id) --ti;
+    while ((ti + 1) * (ti + 2) / 2 <= id) ++ti;
+    const int64_t tj = id - ti * (ti + 1) / 2;
+    const int64_t i0 = ti * SYT, j0 = tj * SYT;
+    const int tx = threadIdx.x & (SYT - 1), ty = threadIdx.x / SYT;
     bool bad = false;
-    for (int64_t j = threadIdx.x; j < K; j += NT) {
-        const float h = (j <= i) ? H[i * K + j] : H[j * K + i];
-        if (j <= i && !isfinite(h)) bad = true;
-        D[i * K + j] = (double)h;
+    for (int r = ty; r < SYT; r += NT / SYT) {
+        const int64_t gi = i0 + r, gj = j0 + tx;
+        float h = 0.0f;
+        if (gi < K && gj <= gi) {
+            h = H[gi * K + gj];
+            if (!isfinite(h)) bad = true;
+        }
+        t[r][tx] = h;
+    }
+    __syncthreads();
+    for (int r = ty; r < SYT; r += NT / SYT) {
+        const int64_t gi = i0 + r, gj = j0 + tx;
+        if (gi < K && gj < K) D[gi * K + gj] = (double)(gj <= gi ? t[r][tx] : t[tx][r]);
+        if (ti != tj) {
+            const int64_t mi = j0 + r, mj = i0 + tx;        // mirror: D[mi][mj] = H[mj][mi]
+            if (mj < K) D[mi * K + mj] = (double)t[tx][r];
+        }
+    }
+    // rows i0 + r (this tile's rows) and j0 + r (its columns, the mirror's rows)
+    if (rowmax && threadIdx.x < 2 * SYT) {
+        const int r = threadIdx.x & (SYT - 1);
+        const bool mirror = threadIdx.x >= SYT;
+        float m = 0.0f;
+        for (int c = 0; c < SYT; ++c) m = fmaxf(m, fabsf(mirror ? t[c][r] : t[r][c]));
+        const int64_t row = (mirror ? j0 : i0) + r;
+        if (row < K && m > 0.0f)
+            atomicMax(rowmax + row, (unsigned long long)__double_as_longlong((double)m));
     }
     if (bad) atomicOr(status, ST_NONFINITE);
 }
@@ -497,9 +536,10 @@ hipError_t launch_set_identity_f64(double *X, int64_t K, hipStream_t s)
 }
 
 hipError_t launch_sym_lower_to_f64(double *D, const float *H, int64_t K, unsigned *status,
-                                   hipStream_t s)
+                                   hipStream_t s, unsigned long long *rowmax)
 {
-    hipLaunchKernelGGL(sym_lower_kernel, dim3((unsigned)K), dim3(NT), 0, s, D, H, K, status);
+    const int64_t ct = (K + SYT - 1) / SYT;
+    hipLaunchKernelGGL(sym_lower_kernel, dim3((unsigned)(ct * (ct + 1) / 2)), dim3(NT), 0, s, D, H, K, status, rowmax);
     return hipGetLastError();
 }
 

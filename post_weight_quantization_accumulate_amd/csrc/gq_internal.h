@@ -157,12 +157,15 @@ const OzConst &oz_const();
 int oz_beta(int64_t K);
 int64_t oz_padded(int64_t K);
 size_t oz_planes_bytes(int64_t K);
-hipError_t oz_split(const double *Z, int64_t K, int beta, int8_t *planes, int *rowexp, hipStream_t s);
+// rowmax, if set, holds each row's largest magnitude (fp64 bits), which the
+// split then does not recompute.
+hipError_t oz_split(const double *Z, int64_t K, int beta, int8_t *planes, int *rowexp, hipStream_t s,
+                    const unsigned long long *rowmax = nullptr);
 hipError_t oz_product(const GemmDesc &d, const OzOperand &A, const OzOperand &B, int beta, uint8_t *Cres,
                       bool out_f32, const OzOut &o, unsigned *status, hipStream_t s, hipEvent_t after_gemm = nullptr);
-// Zeroes n bytes at p (n a multiple of 16, p 16-byte aligned) with a kernel,
-// so that it can sit inside captured graphs.
-hipError_t launch_zero_bytes(void *p, size_t n, hipStream_t s);
+// Zeroes the padding of a split form that oz_product's CRT leaves unwritten
+// (nothing when K is a multiple of 256).
+hipError_t oz_clear_padding(int8_t *planes, int64_t K, hipStream_t s);
 
 // bf16 Gram: H_lower += X^T X, X T x K bf16 row-major.
 hipError_t launch_gram_bf16(float *H, const uint16_t *X, int64_t T, int64_t K, hipStream_t s);
@@ -190,8 +193,10 @@ hipError_t launch_fill_f64(double *p, int64_t n, double v, hipStream_t s);
 hipError_t launch_fill_u32(unsigned *p, int64_t n, unsigned v, hipStream_t s);
 hipError_t launch_set_identity_f64(double *X, int64_t K, hipStream_t s);
 // D = sym(lower(H)) in fp64; status |= NONFINITE on a non-finite lower entry.
+// rowmax, if set (K entries, zeroed beforehand), receives each row's largest
+// magnitude as the bits of an fp64.
 hipError_t launch_sym_lower_to_f64(double *D, const float *H, int64_t K, unsigned *status,
-                                   hipStream_t s);
+                                   hipStream_t s, unsigned long long *rowmax = nullptr);
 // out[0] = sqrt(sum of squares of a[0..n)), deterministic two-stage tree;
 // partials holds kFrobParts doubles.
 constexpr int64_t kFrobParts = 1024;

@@ -151,7 +151,8 @@ __device__ inline int64_t poff(int64_t row, int64_t k, int64_t Kp);
 
 __global__ __launch_bounds__(SPL_NT) void oz_split_kernel(const double *__restrict__ Z, int64_t K, int64_t Kp,
                                                           int beta, int8_t *__restrict__ planes,
-                                                          int *__restrict__ rowexp)
+                                                          int *__restrict__ rowexp,
+                                                          const unsigned long long *__restrict__ rowmax)
 {
     __shared__ double red[SPL_NT / 64];
     __shared__ int e_sh;
@@ -166,14 +167,17 @@ __global__ __launch_bounds__(SPL_NT) void oz_split_kernel(const double *__restri
         return;
     }
     const double *zr = Z + i * K;
-    double mx = 0.0;
-    for (int64_t k = tid; k < K; k += SPL_NT) mx = fmax(mx, fabs(zr[k]));
-    for (int o = 32; o > 0; o >>= 1) mx = fmax(mx, __shfl_xor(mx, o, 64));
-    if ((tid & 63) == 0) red[tid >> 6] = mx;
+    if (!rowmax) {
+        double mx = 0.0;
+        for (int64_t k = tid; k < K; k += SPL_NT) mx = fmax(mx, fabs(zr[k]));
+        for (int o = 32; o > 0; o >>= 1) mx = fmax(mx, __shfl_xor(mx, o, 64));
+        if ((tid & 63) == 0) red[tid >> 6] = mx;
+    }
     __syncthreads();
     if (tid == 0) {
-        double m = red[0];
-        for (int w = 1; w < SPL_NT / 64; ++w) m = fmax(m, red[w]);
+        double m = rowmax ? __longlong_as_double((long long)rowmax[i]) : red[0];
+        if (!rowmax)
+            for (int w = 1; w < SPL_NT / 64; ++w) m = fmax(m, red[w]);
         int e = 0;
         if (m > 0.0) frexp(m, &e);      // m = f 2^e, f in [1/2, 1): |z| <= 2^e
         e_sh = e;
@@ -449,8 +453,12 @@ __global__ __launch_bounds__(CNT) void oz_crt_kernel(GemmDesc d, const uint8_t *
     const int64_t K = d.M;
     int64_t ti = 0, tj = 0;
     {
-        // tile index -> (ti >= tj) in row order
-        const int64_t id = blockIdx.x;
+        // tile index -> (ti >= tj) in row order.  A tile row of one residue plane
+        // is 64 bytes, half a cache line: the tile beside it reads the other
+        // half.  Workgroups are dealt to the XCDs in turn, so the index is taken
+        // through xcd_order, which gives each XCD a contiguous run of tiles: the
+        // two tiles of a line then run together on one XCD and share its L2.
+        const int64_t id = xcd_order(blockIdx.x, gridDim.x);
         int64_t t = (int64_t)((sqrt(8.0 * (double)id + 1.0) - 1.0) * 0.5);
         while (t * (t + 1) / 2 > id) --t;
         while ((t + 1) * (t + 2) / 2 <= id) ++t;
@@ -604,10 +612,28 @@ __global__ __launch_bounds__(CNT) void oz_crt_kernel(GemmDesc d, const uint8_t *
     }
 }
 
-__global__ void zero16_kernel(uint4 *p, int64_t n16)
+// The bytes of a split form that oz_crt_kernel never writes: rows K .. Kp - 1,
+// and in rows below K the 64-byte row segments from column ceil(K / 64) 64 on
+// (the CRT's tiles end there).  One 16-byte chunk per thread and step.
+__global__ void oz_pad_kernel(int8_t *__restrict__ planes, int64_t K, int64_t Kp, int64_t per_plane)
 {
+    const int64_t kseg = Kp >> 6, c0 = (K + 63) >> 6;
+    const int64_t low = K * (kseg - c0);                // padding segments in rows below K
+    const int64_t total = per_plane * kOzMods * 4;
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride) p[i] = make_uint4(0u, 0u, 0u, 0u);
+    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total; e += stride) {
+        const int64_t sg = e >> 2, r = sg / per_plane;
+        int64_t rem = sg - r * per_plane, row, seg;
+        if (rem < low) {
+            row = rem / (kseg - c0);
+            seg = c0 + (rem - row * (kseg - c0));
+        } else {
+            rem -= low;
+            row = K + rem / kseg;
+            seg = rem - (row - K) * kseg;
+        }
+        *(uint4 *)(planes + r * Kp * Kp + poff(row, 64 * seg + 16 * (e & 3), Kp)) = make_uint4(0u, 0u, 0u, 0u);
+    }
 }
 
 }  // namespace
@@ -648,10 +674,12 @@ size_t oz_planes_bytes(int64_t K)
     return (size_t)kOzMods * (size_t)Kp * (size_t)Kp;
 }
 
-hipError_t oz_split(const double *Z, int64_t K, int beta, int8_t *planes, int *rowexp, hipStream_t s)
+hipError_t oz_split(const double *Z, int64_t K, int beta, int8_t *planes, int *rowexp, hipStream_t s,
+                    const unsigned long long *rowmax)
 {
     const int64_t Kp = oz_padded(K);
-    hipLaunchKernelGGL(oz_split_kernel, dim3((unsigned)Kp), dim3(SPL_NT), 0, s, Z, K, Kp, beta, planes, rowexp);
+    hipLaunchKernelGGL(oz_split_kernel, dim3((unsigned)Kp), dim3(SPL_NT), 0, s, Z, K, Kp, beta, planes, rowexp,
+                       rowmax);
     return hipGetLastError();
 }
 
@@ -689,13 +717,14 @@ hipError_t oz_product(const GemmDesc &d, const OzOperand &A, const OzOperand &B,
     return hipGetLastError();
 }
 
-hipError_t launch_zero_bytes(void *p, size_t n, hipStream_t s)
+hipError_t oz_clear_padding(int8_t *planes, int64_t K, hipStream_t s)
 {
-    if (n == 0) return hipSuccess;
-    if ((n & 15) || ((uintptr_t)p & 15)) return hipErrorInvalidValue;
-    const int64_t n16 = (int64_t)(n / 16);
-    const int64_t blocks = (n16 + 255) / 256 < 4096 ? (n16 + 255) / 256 : 4096;
-    hipLaunchKernelGGL(zero16_kernel, dim3((unsigned)blocks), dim3(256), 0, s, (uint4 *)p, n16);
+    const int64_t Kp = oz_padded(K), kseg = Kp / 64, c0 = (K + 63) / 64;
+    const int64_t per_plane = K * (kseg - c0) + (Kp - K) * kseg;
+    if (per_plane == 0) return hipSuccess;
+    const int64_t n = per_plane * kOzMods * 4;
+    const int64_t blocks = (n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096;
+    hipLaunchKernelGGL(oz_pad_kernel, dim3((unsigned)blocks), dim3(256), 0, s, planes, K, Kp, per_plane);
     return hipGetLastError();
 }
 
