@@ -334,12 +334,12 @@ int run_factor(float *U, const float *H, int64_t K, float damp, FactorWs &w, hip
     GQ_HIP(hipEventRecord(la->to_inv, s), "record");
     GQ_HIP(hipStreamWaitEvent(la->inv, la->to_inv, 0), "wait");
     GQ_HIP(launch_set_identity_f64(w.X, K, la->inv), "identity");
+    // (the caller has recorded to_inv on s once panel p is solved)
     auto inverse_rows = [&](int64_t p) -> hipError_t {
         const int64_t q0 = p * kPanel;
         const int nbq = (int)((K - q0) < kPanel ? (K - q0) : kPanel);
         const int64_t q1 = q0 + nbq;
-        hipError_t e = hipEventRecord(la->to_inv, s);
-        if (e == hipSuccess) e = hipStreamWaitEvent(la->inv, la->to_inv, 0);
+        hipError_t e = hipStreamWaitEvent(la->inv, la->to_inv, 0);
         if (e != hipSuccess) return e;
         // X_p = L_pp^-1 X_p = R_pp^-T X_p, in place, over the columns < q1
         e = launch_trsm_rt(w.M, K, q0, nbq, w.rinv + p * kRinvPerPanel, w.X + q0 * K, K, w.X + q0 * K, K, nullptr, 0, q1,
@@ -367,6 +367,7 @@ int run_factor(float *U, const float *H, int64_t K, float damp, FactorWs &w, hip
         const int nbp = (int)((K - p0) < kPanel ? (K - p0) : kPanel);
         const int64_t p1 = p0 + nbp;
         if (p1 >= K) {
+            GQ_HIP(hipEventRecord(la->to_inv, s), "record");
             GQ_HIP(inverse_rows(p), "inverse rows");
             break;
         }
@@ -374,7 +375,6 @@ int run_factor(float *U, const float *H, int64_t K, float damp, FactorWs &w, hip
         GQ_HIP(launch_trsm_rt(w.M, K, p0, nbp, w.rinv + p * kRinvPerPanel, w.M + p0 * K + p1, K, w.M + p0 * K + p1, K,
                               w.M + p1 * K + p0, K, K - p1, s),
                "trsm");
-        GQ_HIP(inverse_rows(p), "inverse rows");
         // trailing update of the upper triangle, A_rest -= R_{p,rest}^T R_{p,rest}:
         // first the block row of panel p+1 (which has panel p-1's update once the
         // side stream's last product is done) ...
@@ -387,11 +387,13 @@ int run_factor(float *U, const float *H, int64_t K, float damp, FactorWs &w, hip
         un.beta = 1.0;
         un.tri = 2;
         GQ_HIP(gemm_tn_f64(un, s), "syrk next row");
-        // ... then the rest on the side stream ...
+        // ... then the rest on the side stream, and the inverse's rows of panel
+        // p on the third, both behind one event: each event operation on s
+        // lengthens the chain of dependent launches ...
+        GQ_HIP(hipEventRecord(la->to_inv, s), "record");
         side_pending = p2 < K;
         if (side_pending) {
-            GQ_HIP(hipEventRecord(la->to_side, s), "record");
-            GQ_HIP(hipStreamWaitEvent(la->side, la->to_side, 0), "wait block row");
+            GQ_HIP(hipStreamWaitEvent(la->side, la->to_inv, 0), "wait block row");
             GemmDesc u = gemm(w.M + p0 * K + p2, K, w.M + p0 * K + p2, K, K - p2, K - p2, nbp,
                               w.M + p2 * K + p2, K);
             u.cin = w.M + p2 * K + p2;
@@ -402,6 +404,7 @@ int run_factor(float *U, const float *H, int64_t K, float damp, FactorWs &w, hip
             GQ_HIP(gemm_tn_f64(u, la->side), "syrk");
             GQ_HIP(hipEventRecord(la->to_main, la->side), "record");
         }
+        GQ_HIP(inverse_rows(p), "inverse rows");
         // ... while the diagonal block of panel p+1 is factored here
         GQ_HIP(launch_potrf_diag(w.M, K, p1, nbn, w.rinv + (p + 1) * kRinvPerPanel, w.sc.status, s), "potrf diag");
     }

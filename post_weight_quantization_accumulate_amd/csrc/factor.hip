@@ -1,8 +1,8 @@
 // factor.hip -- element-wise and small kernels around the blocked fp64
 // factorisation: damping in units of mean(diag H) (hipfire-calib-data, "The
 // fix"), the order reversal that turns a lower-first Cholesky into the
-// H_d = R R^T (R upper) factor whose inverse is the GPTQ factor U, the in-LDS
-// factorisation and inversion of one diagonal block, and the fp64 reductions
+// H_d = R R^T (R upper) factor whose inverse is the GPTQ factor U, the
+// factorisation of one diagonal block and the panel solves, and the fp64 reductions
 // (deterministic single-workgroup trees, no atomics on floating point).
 #include "gq_internal.h"
 
@@ -175,213 +175,151 @@ __global__ __launch_bounds__(NT) void damp_reverse_kernel(double *__restrict__ M
     }
 }
 
-// Upper Cholesky (A = R^T R) of one nb x nb diagonal block (nb <= 128), blocked
-// by 32 so that the sequential part runs in one wave without workgroup barriers:
-//   - one wave factors each 32 x 32 diagonal sub-block D in its
-//     registers (each lane a 4 x 4 tile), publishing the pivot row (column) of
-//     each step through LDS;
-//   - then the strip solve R[D, rest] = R_DD^-T A[D, rest] by substitution, one
-//     column per thread, and the trailing update A[rest, rest] -= R[D, rest]^T
-//     R[D, rest] by all 8 waves.
-// The block lives in LDS (R in the upper triangle).  Writes R (upper) and R^T
-// (lower) back into M, and 1 / R_kk for k < 128 to rinv (1 on padded rows), for
-// the block substitutions that use the panel.  Rows and columns beyond nb are
-// padded with the identity, which decouples them.
+// Upper Cholesky (A = R^T R) of one nb x nb diagonal block (nb <= 128) in one
+// workgroup, column by column, with the block in registers: thread t owns one
+// 4 x 4 tile (tr, tc), tr <= tc, of the upper triangle (528 tiles, t = tc (tc +
+// 1) / 2 + tr).  Step j subtracts a_j[r] a_j[c] / a_jj from every entry r > j,
+// c >= r, where a_j is row j as it stands after steps 0 .. j-1; the owners of
+// row j + 1 then publish it through LDS (two buffers, one barrier per step),
+// and the owner of its diagonal entry forms 1 / sqrt of the pivot for the
+// next step.  Each row is scaled by that value at the end (R_jc = a_jc /
+// sqrt(a_jj)).  Writes R (upper) and R^T (lower) back into M, and 1 / R_kk for
+// k < 128 to rinv (1 on padded rows), for the block substitutions that use the
+// panel.  Rows and columns beyond nb are padded with the identity, which
+// decouples them.
 constexpr int NBMAX = kPanel;
 constexpr int SB = 32;
-constexpr int PNT = 512;
+constexpr int PTE = 4;                                   // tile edge
+constexpr int PTN = NBMAX / PTE;                         // tiles per block row
+constexpr int PTILES = PTN * (PTN + 1) / 2;              // 528
+constexpr int PNT = (PTILES + 63) / 64 * 64;             // 576 threads, 9 waves
+static_assert(NBMAX % PTE == 0, "whole tiles");
+constexpr size_t kPotrfReserveLds = 128 * 1024;
 
-// fp64 lane exchanges: the value of lane `lane` (compile-time), and of lane
-// addr / 4 for each lane (ds_bpermute)
-__device__ inline double readlane_f64(double v, int lane)
+// 1 / sqrt(p) for p > 0: the hardware estimate and two Newton steps y <- y +
+// y (1/2 - (p/2) y^2), each doubling the correct bits, to full double precision
+__device__ inline double rsqrt_f64(double p)
 {
-    const int2 w = __builtin_bit_cast(int2, v);
-    return __builtin_bit_cast(double, make_int2(__builtin_amdgcn_readlane(w.x, lane), __builtin_amdgcn_readlane(w.y, lane)));
-}
-__device__ inline double bpermute_f64(int addr, double v)
-{
-    const int2 w = __builtin_bit_cast(int2, v);
-    return __builtin_bit_cast(double, make_int2(__builtin_amdgcn_ds_bpermute(addr, w.x), __builtin_amdgcn_ds_bpermute(addr, w.y)));
-}
-
-// One wave: Cholesky of the 32 x 32 block at (o, o) of A.  Lane l owns rows
-// 4 (l / 8) + i and columns 4 (l % 8) + k in registers.  Step j takes the pivot
-// from the lane holding (j, j) (readlane) and the pivot row from the 8 lanes
-// holding row j (one permute per value, issued while the pivot's inverse square
-// root is computed).  Writes R (upper) into A and 1 / R_jj into rinv[o + j].
-// Returns true if a pivot of a real (not padded) row was not positive.
-__device__ __attribute__((noinline)) bool wave_factor32(double (*A)[NBMAX + 1], double *rinv, int o, int nb,
-                                                        int lane)
-{
-    const int br = lane >> 3, bc = lane & 7;
-    double a[4][4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const int r = 4 * br + i, c = 4 * bc + k;
-            a[i][k] = (c >= r) ? A[o + r][o + c] : 0.0;
-        }
-    bool badp = false;
-    static_for<SB>([&](auto J) {
-        constexpr int j = decltype(J)::value;
-        constexpr int g = j >> 2, e = j & 3;             // row j: lanes 8 g + bc, register row e
-        const double piv0 = readlane_f64(a[e][e], 9 * g);   // (j, j): lane 8 g + g
-        // row j of the current matrix: columns 4 br + i (for the row factors) and
-        // 4 bc + k (for the column factors)
-        double vr[4], vc[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) vr[i] = bpermute_f64(4 * (8 * g + br), a[e][i]);
-#pragma unroll
-        for (int k = 0; k < 4; ++k) vc[k] = bpermute_f64(4 * (8 * g + bc), a[e][k]);
-        badp |= !(piv0 > 0.0) & (o + j < nb);
-        const double piv = piv0 > 0.0 ? piv0 : 1.0;
-        // 1/sqrt(piv) from the hardware estimate and two Newton steps
-        // y <- y + y (1/2 - (piv/2) y^2) (quadratic convergence to full double
-        // precision), then sqrt(piv) = piv y: a short dependent chain in place of
-        // a square root and a division
-        double inv = __builtin_amdgcn_rsq(piv);
-        const double hp = 0.5 * piv;
-        inv = fma(inv, fma(-hp * inv, inv, 0.5), inv);
-        inv = fma(inv, fma(-hp * inv, inv, 0.5), inv);
-        const double rjj = piv * inv;
-        if (lane == 0) rinv[o + j] = inv;
-        // A[r][c] -= R_jr R_jc = (A_jr / piv) A_jc for r > j, c >= r: the row
-        // factor is 0 for r <= j, so every lane updates its whole tile with plain
-        // fmas (entries below the diagonal are never read back)
-        const double inv2 = inv * inv;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) vr[i] = (4 * br + i > j) ? vr[i] * inv2 : 0.0;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int k = 0; k < 4; ++k) a[i][k] = fma(-vr[i], vc[k], a[i][k]);
-        // row j of R: R_jj = sqrt(piv), R_jc = A_jc / sqrt(piv) for c > j
-        if (br == g) {
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const int c = 4 * bc + k;
-                const double v = a[e][k];
-                a[e][k] = (c == j) ? rjj : ((c > j) ? v * inv : v);
-            }
-        }
-    });
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const int r = 4 * br + i, c = 4 * bc + k;
-            if (c >= r) A[o + r][o + c] = a[i][k];
-        }
-    return badp;
-}
-
-// In one thread: b <- R^-T b for the 32 x 32 upper block R at (o, o) of A (its
-// 1 / R_kk in rinv[o + k]), b in registers; forward substitution, R read by
-// broadcast.
-__device__ inline void solve32(const double (*R)[NBMAX + 1], const double *rinv, int o, double (&b)[SB])
-{
-    static_for<SB>([&](auto KK) {
-        constexpr int k = decltype(KK)::value;
-        b[k] *= rinv[o + k];
-        static_for<SB - 1 - k>([&](auto JJ) {
-            constexpr int j = k + 1 + decltype(JJ)::value;
-            b[j] = fma(-R[o + k][o + j], b[k], b[j]);
-        });
-    });
+    double y = __builtin_amdgcn_rsq(p);
+    const double hp = 0.5 * p;
+    y = fma(y, fma(-hp * y, y, 0.5), y);
+    y = fma(y, fma(-hp * y, y, 0.5), y);
+    return y;
 }
 
 __global__ __launch_bounds__(PNT) void potrf_diag_kernel(double *__restrict__ M, int64_t K, int64_t p0,
                                                         int nb, double *__restrict__ rinv_out, unsigned *status)
 {
-    __shared__ double A[NBMAX][NBMAX + 1];
+    __shared__ double row[2][NBMAX];         // a_j by step parity
+    __shared__ double inv2[2];               // 1 / a_jj by step parity
     __shared__ double rinv[NBMAX];
     __shared__ int bad;
-    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-
+    const int t = threadIdx.x;
+    const bool active = t < PTILES;
+    int tc = (int)((sqrtf(8.0f * (float)t + 1.0f) - 1.0f) * 0.5f);
+    while (tc * (tc + 1) / 2 > t) --tc;
+    while ((tc + 1) * (tc + 2) / 2 <= t) ++tc;
+    const int tr = active ? t - tc * (tc + 1) / 2 : PTN;        // inactive: no rows
+    const int r0 = PTE * tr, c0 = PTE * tc;
+    double a[PTE][PTE];
     {
-        // every thread's loads are issued before any LDS store (clamped
-        // addresses, selects after), so they overlap instead of round-tripping
-        constexpr int PER = NBMAX * NBMAX / PNT;
-        double v[PER];
+        // all 16 loads issued before any is used (clamped addresses, selects after)
+        double v[PTE][PTE];
 #pragma unroll
-        for (int m = 0; m < PER; ++m) {
-            const int e = t + PNT * m, r = e >> 7, c = e & 127;
-            const bool in = r < nb && c < nb && c >= r;
-            v[m] = M[in ? (p0 + r) * K + p0 + c : p0 * K + p0];
-        }
+        for (int i = 0; i < PTE; ++i)
 #pragma unroll
-        for (int m = 0; m < PER; ++m) {
-            const int e = t + PNT * m, r = e >> 7, c = e & 127;
-            const bool in = r < nb && c < nb && c >= r;
-            A[r][c] = in ? v[m] : ((r == c) ? 1.0 : 0.0);
-        }
+            for (int k = 0; k < PTE; ++k) {
+                const int r = r0 + i, c = c0 + k;
+                const bool in = active && r < nb && c < nb && c >= r;
+                v[i][k] = M[in ? (p0 + r) * K + p0 + c : p0 * K + p0];
+            }
+#pragma unroll
+        for (int i = 0; i < PTE; ++i)
+#pragma unroll
+            for (int k = 0; k < PTE; ++k) {
+                const int r = r0 + i, c = c0 + k;
+                const bool in = active && r < nb && c < nb && c >= r;
+                a[i][k] = in ? v[i][k] : ((r == c) ? 1.0 : 0.0);
+            }
     }
+    // the pivot a_jj of the owner of (j, j): 1 / sqrt of it into rinv[j], its
+    // inverse into inv2[buf]; a pivot of a real row that is not positive is
+    // replaced by 1 and flagged
+    bool badp = false;
+    auto pivot = [&](double pv0, int j, int buf) {
+        badp |= !(pv0 > 0.0) & (j < nb);
+        const double pv = pv0 > 0.0 ? pv0 : 1.0;
+        const double y = rsqrt_f64(pv);
+        rinv[j] = y;
+        inv2[buf] = y * y;
+    };
     if (t == 0) bad = 0;
+    // row 0
+    if (tr == 0) {
+#pragma unroll
+        for (int k = 0; k < PTE; ++k) row[0][c0 + k] = a[0][k];
+        if (tc == 0) pivot(a[0][0], 0, 0);
+    }
     __syncthreads();
-
-    const int ty = t >> 5, tx = t & 31;              // trailing mapping: 16 x 32 grid
 #pragma unroll 1
-    for (int s = 0; s < NBMAX / SB; ++s) {
-        const int o = s * SB;
-        if (wave == 0) {
-            const bool b = wave_factor32(A, rinv, o, nb, lane);
-            if (b && lane == 0) bad = 1;
-        }
-        __syncthreads();
-        if (o + SB >= NBMAX) break;
-        // strip: R[o.., c] = R_DD^-T A[o.., c], one column per thread
-        if (t < NBMAX - o - SB) {
-            const int c = o + SB + t;
-            double b[SB];
+    for (int jb = 0; jb < PTN; ++jb) {
+        static_for<PTE>([&](auto E) {
+            constexpr int e = decltype(E)::value;           // j = 4 jb + e
+            const int j = PTE * jb + e, buf = j & 1;
+            // rows of this tile past j take the step's update (rows at or
+            // before j are final); columns c >= r0 >= 4 jb, all published
+            if (active && r0 + PTE - 1 > j) {
+                const double q = inv2[buf];
+                double f[PTE], ac[PTE];
 #pragma unroll
-            for (int k = 0; k < SB; ++k) b[k] = A[o + k][c];
-            solve32(A, rinv, o, b);
+                for (int i = 0; i < PTE; ++i) f[i] = (r0 + i > j) ? row[buf][r0 + i] * q : 0.0;
 #pragma unroll
-            for (int k = 0; k < SB; ++k) A[o + k][c] = b[k];
-        }
-        __syncthreads();
-        // trailing: A[r][c] -= sum_k R[o+k][r] R[o+k][c], r <= c in [o+32, 128)
-        const int base = o + SB;
-        double acc[6][3];
+                for (int k = 0; k < PTE; ++k) ac[k] = row[buf][c0 + k];
 #pragma unroll
-        for (int i = 0; i < 6; ++i)
+                for (int i = 0; i < PTE; ++i)
 #pragma unroll
-            for (int kk = 0; kk < 3; ++kk) acc[i][kk] = 0.0;
-#pragma unroll 2
-        for (int k = 0; k < SB; ++k) {
-            double vr[6], vc[3];
-#pragma unroll
-            for (int i = 0; i < 6; ++i) {
-                const int r = base + ty + 16 * i;
-                vr[i] = A[o + k][r < NBMAX ? r : NBMAX - 1];
+                    for (int k = 0; k < PTE; ++k) a[i][k] = fma(-f[i], ac[k], a[i][k]);
             }
+            // publish row j + 1 (register row (e + 1) % 4 of tile row jb or jb + 1)
+            if (j + 1 < NBMAX) {
+                constexpr int en = (e + 1) & (PTE - 1);
+                const int trn = jb + (e + 1) / PTE;
+                if (tr == trn) {
 #pragma unroll
-            for (int kk = 0; kk < 3; ++kk) {
-                const int c2 = base + tx + 32 * kk;
-                vc[kk] = A[o + k][c2 < NBMAX ? c2 : NBMAX - 1];
+                    for (int k = 0; k < PTE; ++k) row[buf ^ 1][c0 + k] = a[en][k];
+                    if (tc == trn) pivot(a[en][en], j + 1, buf ^ 1);
+                }
             }
-#pragma unroll
-            for (int i = 0; i < 6; ++i)
-#pragma unroll
-                for (int kk = 0; kk < 3; ++kk) acc[i][kk] += vr[i] * vc[kk];
-        }
-#pragma unroll
-        for (int i = 0; i < 6; ++i)
-#pragma unroll
-            for (int kk = 0; kk < 3; ++kk) {
-                const int r = base + ty + 16 * i, c2 = base + tx + 32 * kk;
-                if (r < NBMAX && c2 < NBMAX && r <= c2) A[r][c2] -= acc[i][kk];
-            }
-        __syncthreads();
+            __syncthreads();
+        });
     }
-
-    // R is final: write it (upper) and R^T (lower) back, and 1 / R_kk
+    // R_rc = a_rc / sqrt(a_rr) (the pivot as used: 1 for a flagged one)
+    if (active) {
+#pragma unroll
+        for (int i = 0; i < PTE; ++i) {
+            const int r = r0 + i;
+            const double y = rinv[r];
+#pragma unroll
+            for (int k = 0; k < PTE; ++k) {
+                const int c = c0 + k;
+                const double v = a[i][k];
+                a[i][k] = (c == r) ? (v > 0.0 ? v : 1.0) * y : v * y;
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < PTE; ++i)
+#pragma unroll
+            for (int k = 0; k < PTE; ++k) {
+                const int r = r0 + i, c = c0 + k;
+                if (r < nb && c < nb && c >= r) {
+                    M[(p0 + r) * K + p0 + c] = a[i][k];
+                    M[(p0 + c) * K + p0 + r] = a[i][k];
+                }
+            }
+    }
     if (t < NBMAX) rinv_out[t] = rinv[t];
-    for (int e = t; e < NBMAX * NBMAX; e += PNT) {
-        const int r = e >> 7, c = e & 127;
-        if (r < nb && c < nb) M[(p0 + r) * K + p0 + c] = (c >= r) ? A[r][c] : A[c][r];
-    }
+    if (badp) atomicOr(&bad, 1);
+    __syncthreads();
     if (t == 0 && bad) atomicOr(status, ST_NOT_PD);
 }
 
@@ -578,7 +516,14 @@ hipError_t launch_potrf_diag(double *M, int64_t K, int64_t p0, int nb, double *r
                              hipStream_t s)
 {
     if (nb < 1 || nb > NBMAX) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(potrf_diag_kernel, dim3(1), dim3(PNT), 0, s, M, K, p0, nb, rinv, status);
+    // The workgroup reserves most of a CU's LDS, which it does not use, so that
+    // no workgroup of the concurrent trailing update shares its CU: the chain of
+    // 128 barrier-separated steps runs at the speed of an idle CU.
+    static const bool lds_ok = hipFuncSetAttribute((const void *)potrf_diag_kernel,
+                                                   hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                   (int)kPotrfReserveLds) == hipSuccess;
+    if (!lds_ok) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(potrf_diag_kernel, dim3(1), dim3(PNT), kPotrfReserveLds, s, M, K, p0, nb, rinv, status);
     return hipGetLastError();
 }
 
