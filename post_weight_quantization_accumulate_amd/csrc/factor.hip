@@ -176,17 +176,21 @@ __global__ __launch_bounds__(NT) void damp_reverse_kernel(double *__restrict__ M
 }
 
 // Upper Cholesky (A = R^T R) of one nb x nb diagonal block (nb <= 128) in one
-// workgroup, column by column, with the block in registers: thread t owns one
-// 4 x 4 tile (tr, tc), tr <= tc, of the upper triangle (528 tiles, t = tc (tc +
-// 1) / 2 + tr).  Step j subtracts a_j[r] a_j[c] / a_jj from every entry r > j,
-// c >= r, where a_j is row j as it stands after steps 0 .. j-1; the owners of
-// row j + 1 then publish it through LDS (two buffers, one barrier per step),
-// and the owner of its diagonal entry forms 1 / sqrt of the pivot for the
-// next step.  Each row is scaled by that value at the end (R_jc = a_jc /
-// sqrt(a_jj)).  Writes R (upper) and R^T (lower) back into M, and 1 / R_kk for
-// k < 128 to rinv (1 on padded rows), for the block substitutions that use the
-// panel.  Rows and columns beyond nb are padded with the identity, which
-// decouples them.
+// workgroup, four columns per step, with the block in registers: thread t owns
+// one 4 x 4 tile (tr, tc), tr <= tc, of the upper triangle (528 tiles, in row
+// order).  Step jb takes the block row J = 4 jb .. 4 jb + 3 as
+// it stands after steps 0 .. jb-1, published through LDS by its owners (two
+// buffers, one barrier per step).  Every thread eliminates the 4 x 4 diagonal
+// block D = A[J][J] in its registers, pivot by pivot: pivot e gives the
+// multipliers l[e2][e] = D_e,e2 / D_ee (D as updated by the pivots before e),
+// and the block row's rows become w_e = a_e - sum_{e' < e} l[e][e'] w_e'.  A
+// tile below the block row then takes A[r][c] -= sum_e w_e[r] w_e[c] / D_ee,
+// which is the four column steps of the unblocked algorithm, and the tile
+// owners of the block row turn w_e into R's rows, R_e,c = w_e[c] / sqrt(D_ee).
+// Writes R (upper) and R^T (lower) back into M, and 1 / R_kk for k < 128 to
+// rinv (1 on padded rows), for the block substitutions that use the panel.
+// Rows and columns beyond nb are padded with the identity, which decouples
+// them.
 constexpr int NBMAX = kPanel;
 constexpr int SB = 32;
 constexpr int PTE = 4;                                   // tile edge
@@ -196,8 +200,9 @@ constexpr int PNT = (PTILES + 63) / 64 * 64;             // 576 threads, 9 waves
 static_assert(NBMAX % PTE == 0, "whole tiles");
 constexpr size_t kPotrfReserveLds = 128 * 1024;
 
-// 1 / sqrt(p) for p > 0: the hardware estimate and two Newton steps y <- y +
-// y (1/2 - (p/2) y^2), each doubling the correct bits, to full double precision
+// 1 / sqrt(p) and 1 / p for p > 0: the hardware estimates and two Newton steps
+// each (y <- y + y (1/2 - (p/2) y^2), y <- y + y (1 - p y)), each step doubling
+// the correct bits, to full double precision
 __device__ inline double rsqrt_f64(double p)
 {
     double y = __builtin_amdgcn_rsq(p);
@@ -206,20 +211,28 @@ __device__ inline double rsqrt_f64(double p)
     y = fma(y, fma(-hp * y, y, 0.5), y);
     return y;
 }
+__device__ inline double rcp_f64(double p)
+{
+    double y = __builtin_amdgcn_rcp(p);
+    y = fma(y, fma(-p, y, 1.0), y);
+    y = fma(y, fma(-p, y, 1.0), y);
+    return y;
+}
 
 __global__ __launch_bounds__(PNT) void potrf_diag_kernel(double *__restrict__ M, int64_t K, int64_t p0,
                                                         int nb, double *__restrict__ rinv_out, unsigned *status)
 {
-    __shared__ double row[2][NBMAX];         // a_j by step parity
-    __shared__ double inv2[2];               // 1 / a_jj by step parity
+    __shared__ double rowb[2][PTE][NBMAX];   // the block row by step parity
     __shared__ double rinv[NBMAX];
     __shared__ int bad;
     const int t = threadIdx.x;
     const bool active = t < PTILES;
-    int tc = (int)((sqrtf(8.0f * (float)t + 1.0f) - 1.0f) * 0.5f);
-    while (tc * (tc + 1) / 2 > t) --tc;
-    while ((tc + 1) * (tc + 2) / 2 <= t) ++tc;
-    const int tr = active ? t - tc * (tc + 1) / 2 : PTN;        // inactive: no rows
+    // tiles in row order, so that a wave's tiles lie in a few neighbouring tile
+    // rows and the wave has no work left once the steps have passed them
+    int tr = 0, rs = 0;                                 // rs: index of tile (tr, tr)
+    while (tr < PTN - 1 && rs + (PTN - tr) <= t) rs += PTN - tr++;
+    const int tc = active ? tr + (t - rs) : PTN;
+    if (!active) tr = PTN;                              // inactive: no rows
     const int r0 = PTE * tr, c0 = PTE * tc;
     double a[PTE][PTE];
     {
@@ -242,70 +255,94 @@ __global__ __launch_bounds__(PNT) void potrf_diag_kernel(double *__restrict__ M,
                 a[i][k] = in ? v[i][k] : ((r == c) ? 1.0 : 0.0);
             }
     }
-    // the pivot a_jj of the owner of (j, j): 1 / sqrt of it into rinv[j], its
-    // inverse into inv2[buf]; a pivot of a real row that is not positive is
-    // replaced by 1 and flagged
-    bool badp = false;
-    auto pivot = [&](double pv0, int j, int buf) {
-        badp |= !(pv0 > 0.0) & (j < nb);
-        const double pv = pv0 > 0.0 ? pv0 : 1.0;
-        const double y = rsqrt_f64(pv);
-        rinv[j] = y;
-        inv2[buf] = y * y;
-    };
     if (t == 0) bad = 0;
-    // row 0
     if (tr == 0) {
 #pragma unroll
-        for (int k = 0; k < PTE; ++k) row[0][c0 + k] = a[0][k];
-        if (tc == 0) pivot(a[0][0], 0, 0);
+        for (int i = 0; i < PTE; ++i)
+#pragma unroll
+            for (int k = 0; k < PTE; ++k) rowb[0][i][c0 + k] = a[i][k];
     }
     __syncthreads();
+    bool badp = false;
 #pragma unroll 1
     for (int jb = 0; jb < PTN; ++jb) {
-        static_for<PTE>([&](auto E) {
-            constexpr int e = decltype(E)::value;           // j = 4 jb + e
-            const int j = PTE * jb + e, buf = j & 1;
-            // rows of this tile past j take the step's update (rows at or
-            // before j are final); columns c >= r0 >= 4 jb, all published
-            if (active && r0 + PTE - 1 > j) {
-                const double q = inv2[buf];
-                double f[PTE], ac[PTE];
+        const int buf = jb & 1, j0 = PTE * jb;
+        if (active && tr >= jb) {
+            // D eliminated pivot by pivot (a pivot of a real row that is not
+            // positive is replaced by 1 and flagged by the block row's owner)
+            double d[PTE][PTE], q[PTE], pv[PTE], l[PTE][PTE];
 #pragma unroll
-                for (int i = 0; i < PTE; ++i) f[i] = (r0 + i > j) ? row[buf][r0 + i] * q : 0.0;
+            for (int e = 0; e < PTE; ++e)
 #pragma unroll
-                for (int k = 0; k < PTE; ++k) ac[k] = row[buf][c0 + k];
+                for (int c = 0; c < PTE; ++c) d[e][c] = rowb[buf][e][j0 + c];
 #pragma unroll
-                for (int i = 0; i < PTE; ++i)
+            for (int e = 0; e < PTE; ++e) {
+                if (tr == jb) badp |= !(d[e][e] > 0.0) & (j0 + e < nb);
+                pv[e] = d[e][e] > 0.0 ? d[e][e] : 1.0;
+                q[e] = rcp_f64(pv[e]);
 #pragma unroll
-                    for (int k = 0; k < PTE; ++k) a[i][k] = fma(-f[i], ac[k], a[i][k]);
-            }
-            // publish row j + 1 (register row (e + 1) % 4 of tile row jb or jb + 1)
-            if (j + 1 < NBMAX) {
-                constexpr int en = (e + 1) & (PTE - 1);
-                const int trn = jb + (e + 1) / PTE;
-                if (tr == trn) {
+                for (int e2 = e + 1; e2 < PTE; ++e2) {
+                    l[e2][e] = d[e][e2] * q[e];
 #pragma unroll
-                    for (int k = 0; k < PTE; ++k) row[buf ^ 1][c0 + k] = a[en][k];
-                    if (tc == trn) pivot(a[en][en], j + 1, buf ^ 1);
+                    for (int c = e2; c < PTE; ++c) d[e2][c] = fma(-l[e2][e], d[e][c], d[e2][c]);
                 }
             }
-            __syncthreads();
-        });
-    }
-    // R_rc = a_rc / sqrt(a_rr) (the pivot as used: 1 for a flagged one)
-    if (active) {
+            if (tr > jb) {
+                // the block row at this tile's rows (wr) and columns (wc), as w_e
+                double wr[PTE][PTE], wc[PTE][PTE];
 #pragma unroll
-        for (int i = 0; i < PTE; ++i) {
-            const int r = r0 + i;
-            const double y = rinv[r];
+                for (int e = 0; e < PTE; ++e)
 #pragma unroll
-            for (int k = 0; k < PTE; ++k) {
-                const int c = c0 + k;
-                const double v = a[i][k];
-                a[i][k] = (c == r) ? (v > 0.0 ? v : 1.0) * y : v * y;
+                    for (int i = 0; i < PTE; ++i) {
+                        wr[e][i] = rowb[buf][e][r0 + i];
+                        wc[e][i] = rowb[buf][e][c0 + i];
+                    }
+#pragma unroll
+                for (int e = 1; e < PTE; ++e)
+#pragma unroll
+                    for (int e1 = 0; e1 < e; ++e1)
+#pragma unroll
+                        for (int i = 0; i < PTE; ++i) {
+                            wr[e][i] = fma(-l[e][e1], wr[e1][i], wr[e][i]);
+                            wc[e][i] = fma(-l[e][e1], wc[e1][i], wc[e][i]);
+                        }
+#pragma unroll
+                for (int e = 0; e < PTE; ++e)
+#pragma unroll
+                    for (int i = 0; i < PTE; ++i) {
+                        const double f = wr[e][i] * q[e];
+#pragma unroll
+                        for (int k = 0; k < PTE; ++k) a[i][k] = fma(-f, wc[e][k], a[i][k]);
+                    }
+            } else {
+                // this tile's rows are the block row: w_e from its own (published)
+                // values, then R's rows; on the diagonal tile the entries left of
+                // the diagonal are never read
+#pragma unroll
+                for (int e = 1; e < PTE; ++e)
+#pragma unroll
+                    for (int e1 = 0; e1 < e; ++e1)
+#pragma unroll
+                        for (int k = 0; k < PTE; ++k) a[e][k] = fma(-l[e][e1], a[e1][k], a[e][k]);
+#pragma unroll
+                for (int e = 0; e < PTE; ++e) {
+                    const double y = rsqrt_f64(pv[e]);
+#pragma unroll
+                    for (int k = 0; k < PTE; ++k) a[e][k] = (c0 + k == j0 + e) ? pv[e] * y : a[e][k] * y;
+                    if (tc == jb) rinv[j0 + e] = y;
+                }
             }
         }
+        // publish the next block row
+        if (active && tr == jb + 1) {
+#pragma unroll
+            for (int i = 0; i < PTE; ++i)
+#pragma unroll
+                for (int k = 0; k < PTE; ++k) rowb[buf ^ 1][i][c0 + k] = a[i][k];
+        }
+        __syncthreads();
+    }
+    if (active) {
 #pragma unroll
         for (int i = 0; i < PTE; ++i)
 #pragma unroll
