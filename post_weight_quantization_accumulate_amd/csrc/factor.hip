@@ -360,113 +360,117 @@ __global__ __launch_bounds__(PNT) void potrf_diag_kernel(double *__restrict__ M,
     if (t == 0 && bad) atomicOr(status, ST_NOT_PD);
 }
 
-// Y = R^-T B for the nb x nb upper block R at (p0, p0) of M (nb <= 128), by block
-// forward substitution over its 32 x 32 diagonal sub-blocks:
-//     Y_s = R_ss^-T (B_s - sum_{t < s} R_ts^T Y_t),
-// the update as small products (thread (a, g): row a of the block, columns
-// 8 g .. 8 g + 7), the diagonal solve by substitution in one thread per
-// column with 1 / R_kk from rinv (which the diagonal kernel wrote).  One
-// workgroup per 64 columns of B (nb x ncols, ld ldb), held in LDS.  Y goes to
-// out (ld ldo; out may be B: each workgroup reads its columns before it writes
-// them) and, with out_t set, transposed to out_t (out_t[c ldt + a] = Y[a][c]).
-// Memory is read in batches, every load of a batch issued before any of its
-// values is stored (clamped addresses, selects after): B's block once, and for
-// each s the column strip R[0 .. 32 s + 31][32 s .. 32 s + 31] it needs, so a
-// workgroup waits on memory five times rather than once per element it reads.
+// Y = R^-T B for the nb x nb upper block R at (p0, p0) of M (nb <= 128): block
+// forward substitution by four rows, Y_J = R_JJ^-T (B_J - sum_{J' < J} R_J'J^T
+// Y_J'), with 1 / R_kk from rinv (which the diagonal kernel wrote).  One
+// workgroup per 64 columns of B (nb x ncols, ld ldb); thread t owns the 4 x 4
+// tile (t / 16, t % 16) of the workgroup's 128 x 64 block of B in registers.
+// R's upper triangle is staged in LDS, packed by rows.  Step jb: the tile row
+// jb, which has every earlier step's update, solves its 4 x 4 diagonal system
+// and publishes Y_J through LDS (two buffers, one barrier per step); every
+// tile row below subtracts R_J,rows^T Y_J.  Y goes to out (ld ldo; out may be
+// B: each workgroup reads its columns before it writes them) and, with out_t
+// set, transposed to out_t (out_t[c ldt + a] = Y[a][c]).  Rows and columns
+// beyond nb are padded with the identity.
 constexpr int TSC = 64;
-constexpr int TST = 256;
+constexpr int TST = 512;
+constexpr int TTC = TSC / PTE;                           // tile columns: 16
+static_assert(TST == PTN * TTC, "one 4 x 4 tile per thread");
+__device__ constexpr int rpack(int r) { return r * NBMAX - r * (r - 1) / 2; }   // entry (r, r)
 __global__ __launch_bounds__(TST) void trsm_rt_kernel(const double *__restrict__ M, int64_t K, int64_t p0, int nb,
                                                       const double *__restrict__ rinv_in, const double *B,
                                                       int64_t ldb,
                                                       double *out, int64_t ldo, double *out_t, int64_t ldt,
                                                       int64_t ncols)
 {
-    __shared__ double Ys[NBMAX][TSC + 1];
-    __shared__ double Rs[NBMAX][SB + 1];          // R[0 .. 32 s + 31][32 s .. 32 s + 31]
+    __shared__ double Rp[NBMAX * (NBMAX + 1) / 2];
+    __shared__ double Yp[2][PTE][TSC];
     __shared__ double rinv[NBMAX];
-    const int t = threadIdx.x, a = t & 31, cg = t >> 5;
-    const int64_t c0 = (int64_t)blockIdx.x * TSC;
-    const int nsb = (nb + SB - 1) / SB;
+    const int t = threadIdx.x, tr = t / TTC, tcl = t % TTC;
+    const int r0 = PTE * tr, c0 = PTE * tcl;
+    const int64_t cb = (int64_t)blockIdx.x * TSC;
+    double b[PTE][PTE];
     {
-        constexpr int PER = NBMAX * TSC / TST;
-        double v[PER];
+        // every load (R's block, this tile of B) issued before any is used
+        // (clamped addresses, selects after)
+        constexpr int PER = NBMAX * NBMAX / TST;
+        double v[PER], w[PTE][PTE];
 #pragma unroll
         for (int m = 0; m < PER; ++m) {
-            const int e = t + TST * m, r = e / TSC, c = e % TSC;
-            const bool in = r < nb && c0 + c < ncols;
-            v[m] = B[in ? r * ldb + c0 + c : 0];
+            const int e = t + TST * m, r = e / NBMAX, c = e % NBMAX;
+            const bool in = r < nb && c < nb && c >= r;
+            v[m] = M[in ? (p0 + r) * K + p0 + c : p0 * K + p0];
         }
 #pragma unroll
+        for (int i = 0; i < PTE; ++i)
+#pragma unroll
+            for (int k = 0; k < PTE; ++k) {
+                const bool in = r0 + i < nb && cb + c0 + k < ncols;
+                w[i][k] = B[in ? (r0 + i) * ldb + cb + c0 + k : 0];
+            }
+#pragma unroll
         for (int m = 0; m < PER; ++m) {
-            const int e = t + TST * m, r = e / TSC, c = e % TSC;
-            const bool in = r < nb && c0 + c < ncols;
-            Ys[r][c] = in ? v[m] : 0.0;
+            const int e = t + TST * m, r = e / NBMAX, c = e % NBMAX;
+            if (c >= r) Rp[rpack(r) + c - r] = (r < nb && c < nb) ? v[m] : (r == c ? 1.0 : 0.0);
         }
+#pragma unroll
+        for (int i = 0; i < PTE; ++i)
+#pragma unroll
+            for (int k = 0; k < PTE; ++k) b[i][k] = (r0 + i < nb && cb + c0 + k < ncols) ? w[i][k] : 0.0;
     }
     if (t < NBMAX) rinv[t] = rinv_in[t];
+    __syncthreads();
 #pragma unroll 1
-    for (int s = 0; s < nsb; ++s) {
-        // the strip of R this block row needs: rows 0 .. 32 s + 31 of its 32
-        // columns (the identity past nb); element (rr, aa) is m-th of thread t
-        // for rr * SB + aa = t + TST m
-        {
-            constexpr int PER = NBMAX * SB / TST;
-            const int rows = SB * (s + 1);
-            double v[PER];
+    for (int jb = 0; jb < PTN; ++jb) {
+        const int buf = jb & 1, j0 = PTE * jb;
+        if (tr == jb) {
+            // y_e = (b_e - sum_{e1 < e} R[j0 + e1][j0 + e] y_e1) / R_ee, in place
 #pragma unroll
-            for (int m = 0; m < PER; ++m) {
-                const int e = t + TST * m, rr = e / SB, cc = SB * s + e % SB;
-                const bool in = rr < rows && rr < nb && cc < nb;
-                v[m] = M[in ? (p0 + rr) * K + p0 + cc : p0 * K + p0];
+            for (int e = 0; e < PTE; ++e) {
+#pragma unroll
+                for (int e1 = 0; e1 < e; ++e1) {
+                    const double rr = Rp[rpack(j0 + e1) + e - e1];
+#pragma unroll
+                    for (int k = 0; k < PTE; ++k) b[e][k] = fma(-rr, b[e1][k], b[e][k]);
+                }
+                const double ri = rinv[j0 + e];
+#pragma unroll
+                for (int k = 0; k < PTE; ++k) b[e][k] *= ri;
             }
 #pragma unroll
-            for (int m = 0; m < PER; ++m) {
-                const int e = t + TST * m, rr = e / SB, cc = SB * s + e % SB;
-                if (rr < rows) Rs[rr][e % SB] = (rr < nb && cc < nb) ? v[m] : (rr == cc ? 1.0 : 0.0);
+            for (int e = 0; e < PTE; ++e)
+#pragma unroll
+                for (int k = 0; k < PTE; ++k) Yp[buf][e][c0 + k] = b[e][k];
+        }
+        __syncthreads();
+        if (tr > jb) {
+            double y[PTE][PTE], rr[PTE][PTE];
+#pragma unroll
+            for (int e = 0; e < PTE; ++e)
+#pragma unroll
+                for (int k = 0; k < PTE; ++k) {
+                    y[e][k] = Yp[buf][e][c0 + k];
+                    rr[e][k] = Rp[rpack(j0 + e) + r0 + k - (j0 + e)];
+                }
+#pragma unroll
+            for (int i = 0; i < PTE; ++i)
+#pragma unroll
+                for (int e = 0; e < PTE; ++e)
+#pragma unroll
+                    for (int k = 0; k < PTE; ++k) b[i][k] = fma(-rr[e][i], y[e][k], b[i][k]);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < PTE; ++i)
+#pragma unroll
+        for (int k = 0; k < PTE; ++k) {
+            const int r = r0 + i;
+            const int64_t c = cb + c0 + k;
+            if (r < nb && c < ncols) {
+                out[r * ldo + c] = b[i][k];
+                if (out_t) out_t[c * ldt + r] = b[i][k];
             }
         }
-        __syncthreads();
-        double acc[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) acc[j] = Ys[SB * s + a][8 * cg + j];
-#pragma unroll 4
-        for (int k = 0; k < SB * s; ++k) {
-            const double r = Rs[k][a];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) acc[j] = fma(-r, Ys[k][8 * cg + j], acc[j]);
-        }
-        // (the update reads rows of Ys before block s only)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) Ys[SB * s + a][8 * cg + j] = acc[j];
-        __syncthreads();
-        if (t < TSC) {
-            // b <- R_ss^-T b, R_ss = Rs[32 s + k][j]
-            double b[SB];
-#pragma unroll
-            for (int k = 0; k < SB; ++k) b[k] = Ys[SB * s + k][t];
-            static_for<SB>([&](auto KK) {
-                constexpr int k = decltype(KK)::value;
-                b[k] *= rinv[SB * s + k];
-                static_for<SB - 1 - k>([&](auto JJ) {
-                    constexpr int j = k + 1 + decltype(JJ)::value;
-                    b[j] = fma(-Rs[SB * s + k][j], b[k], b[j]);
-                });
-            });
-#pragma unroll
-            for (int k = 0; k < SB; ++k) Ys[SB * s + k][t] = b[k];
-        }
-        __syncthreads();
-    }
-    for (int e = t; e < NBMAX * TSC; e += TST) {
-        const int r = e / TSC, c = e % TSC;
-        if (r < nb && c0 + c < ncols) out[r * ldo + c0 + c] = Ys[r][c];
-    }
-    if (out_t) {
-        for (int e = t; e < NBMAX * TSC; e += TST) {
-            const int c = e / NBMAX, r = e % NBMAX;
-            if (r < nb && c0 + c < ncols) out_t[(c0 + c) * ldt + r] = Ys[r][c];
-        }
-    }
 }
 
 // U[i][j] = X[K-1-i][K-1-j] (as fp32) for i <= j, 0 below: the lower triangular
