@@ -627,8 +627,10 @@ __global__ __launch_bounds__(QNT) void qerr_kernel(double *__restrict__ partials
 
 // The same sums for K a multiple of 8 with W (and imp) 16-byte and the codes
 // 4-byte aligned: a thread takes 8 consecutive columns of a row at a time (two
-// 16-byte loads of W, one 4-byte word of codes), the grid strides over the rows'
-// 8-column chunks, and each workgroup folds its sums in the fixed-order tree.
+// 16-byte loads of W, one 4-byte word of codes), the grid strides over the flat
+// index of the rows' 8-column chunks, and each workgroup folds its sums in the
+// fixed-order tree.  The next pass's loads are issued before this pass's
+// arithmetic, so that two passes' loads are in flight.
 template <bool NF4>
 __global__ __launch_bounds__(QNT) void qerr8_kernel(double *__restrict__ partials, const float *__restrict__ W,
                                                    const uint8_t *__restrict__ codes,
@@ -641,54 +643,69 @@ __global__ __launch_bounds__(QNT) void qerr8_kernel(double *__restrict__ partial
     __syncthreads();
     const int64_t chunks = K / 8, ng = K / G;
     const int lg = __builtin_ctzll((unsigned long long)G);   // G is a power of two
+    const int64_t total = N * chunks;
+    const int64_t S = (int64_t)gridDim.x * QNT;
+    const int64_t dq2 = 2 * S / chunks, dr2 = 2 * S - dq2 * chunks;
     double num = 0.0, den = 0.0;
-    // rows by workgroup, a row's 8-column chunks by thread; QU chunks per pass
-    // with their loads issued together, so that enough bytes are in flight
-    constexpr int QU = 2;
-    for (int64_t row = blockIdx.x; row < N; row += gridDim.x) {
-      const float *wrow = W + row * K;
-      const uint8_t *crow = codes + row * (K / 2);
-      const float *srow = scales + row * ng;
-      for (int64_t cb = threadIdx.x; cb < chunks; cb += QU * QNT) {
-        // every load of the pass (weights, codes, importance, the group's scale)
-        // is issued before any arithmetic, so that one memory round trip covers it
-        float4 av[QU], bv[QU], iav[QU], ibv[QU];
-        unsigned cwv[QU];
-        float s8v[QU];
-#pragma unroll
-        for (int q = 0; q < QU; ++q) {
-          const int64_t c = cb + q * QNT < chunks ? cb + q * QNT : cb;
-          av[q] = *(const float4 *)(wrow + 8 * c);
-          bv[q] = *(const float4 *)(wrow + 8 * c + 4);
-          cwv[q] = *(const unsigned *)(crow + 4 * c);
-          if (imp) {
-            iav[q] = *(const float4 *)(imp + 8 * c);
-            ibv[q] = *(const float4 *)(imp + 8 * c + 4);
-          } else {
-            iav[q] = ibv[q] = make_float4(1.0f, 1.0f, 1.0f, 1.0f);
-          }
-          s8v[q] = G >= 8 ? srow[(8 * c) >> lg] : 0.0f;        // one group holds all 8 columns
+    // two chunks per pass, the grid's stride apart, and the next pass's loads
+    // issued before this pass's arithmetic: four chunks' loads in flight
+    float4 a0, b0, ia0, ib0, a1, b1, ia1, ib1;
+    unsigned cw0, cw1;
+    float s0, s1;
+    auto load = [&](int64_t row, int64_t c, bool ok, float4 &a, float4 &b, float4 &ia, float4 &ib, unsigned &cw,
+                    float &s8) __attribute__((always_inline)) {
+        const int64_t r = ok ? row : 0, c8 = ok ? c : 0;
+        a = *(const float4 *)(W + r * K + 8 * c8);
+        b = *(const float4 *)(W + r * K + 8 * c8 + 4);
+        cw = *(const unsigned *)(codes + r * (K / 2) + 4 * c8);
+        if (imp) {
+            ia = *(const float4 *)(imp + 8 * c8);
+            ib = *(const float4 *)(imp + 8 * c8 + 4);
+        } else {
+            ia = ib = make_float4(1.0f, 1.0f, 1.0f, 1.0f);
         }
-#pragma unroll
-        for (int q = 0; q < QU; ++q) {
-          const int64_t c = cb + q * QNT;
-          if (c >= chunks) break;
-          const float4 a = av[q], b = bv[q];
-          const float w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-          const unsigned cw = cwv[q];
-          const float iw[8] = {iav[q].x, iav[q].y, iav[q].z, iav[q].w, ibv[q].x, ibv[q].y, ibv[q].z, ibv[q].w};
-          const float s8 = s8v[q];
-#pragma unroll
-          for (int t = 0; t < 8; ++t) {
-              const unsigned nib = (cw >> (4 * t)) & 0xFu;
-              const float cv = NF4 ? lev[nib] : (float)((int)nib - ((nib & 8u) ? 16 : 0));
-              const float sc = G >= 8 ? s8 : srow[(8 * c + t) >> lg];
-              const double d = (double)w[t] - (double)cv * (double)sc;
-              num += (double)iw[t] * d * d;
-              den += (double)iw[t] * (double)w[t] * (double)w[t];
-          }
+        s8 = G >= 8 ? scales[r * ng + ((8 * c8) >> lg)] : 0.0f;   // one group holds all 8 columns
+    };
+    auto advance = [&](int64_t &rw, int64_t &cl) __attribute__((always_inline)) {
+        rw += dq2;
+        cl += dr2;
+        if (cl >= chunks) {
+            cl -= chunks;
+            ++rw;
         }
-      }
+    };
+    auto accumulate = [&](float4 a, float4 b, float4 ia, float4 ib, unsigned cw, float s8, int64_t prow,
+                          int64_t c) __attribute__((always_inline)) {
+        const float w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+        const float iw[8] = {ia.x, ia.y, ia.z, ia.w, ib.x, ib.y, ib.z, ib.w};
+        const float *srow = scales + prow * ng;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            const unsigned nib = (cw >> (4 * t)) & 0xFu;
+            const float cv = NF4 ? lev[nib] : (float)((int)nib - ((nib & 8u) ? 16 : 0));
+            const float sc = G >= 8 ? s8 : srow[(8 * c + t) >> lg];
+            const double d = (double)w[t] - (double)cv * (double)sc;
+            num += (double)iw[t] * d * d;
+            den += (double)iw[t] * (double)w[t] * (double)w[t];
+        }
+    };
+    int64_t g0 = (int64_t)blockIdx.x * QNT + threadIdx.x;
+    int64_t r0 = g0 / chunks, c0 = g0 - r0 * chunks;
+    int64_t r1 = (g0 + S) / chunks, c1 = g0 + S - r1 * chunks;
+    load(r0, c0, g0 < total, a0, b0, ia0, ib0, cw0, s0);
+    load(r1, c1, g0 + S < total, a1, b1, ia1, ib1, cw1, s1);
+    for (; g0 < total; g0 += 2 * S) {
+        const float4 pa0 = a0, pb0 = b0, pia0 = ia0, pib0 = ib0, pa1 = a1, pb1 = b1, pia1 = ia1, pib1 = ib1;
+        const unsigned pcw0 = cw0, pcw1 = cw1;
+        const float ps0 = s0, ps1 = s1;
+        const int64_t pr0 = r0, pc0 = c0, pr1 = r1, pc1 = c1;
+        advance(r0, c0);
+        advance(r1, c1);
+        // the next pass (clamped to chunk 0 past the end: in bounds, unused)
+        load(r0, c0, g0 + 2 * S < total, a0, b0, ia0, ib0, cw0, s0);
+        load(r1, c1, g0 + 3 * S < total, a1, b1, ia1, ib1, cw1, s1);
+        accumulate(pa0, pb0, pia0, pib0, pcw0, ps0, pr0, pc0);
+        if (g0 + S < total) accumulate(pa1, pb1, pia1, pib1, pcw1, ps1, pr1, pc1);
     }
     block_sum2(num, den, sh);
     if (threadIdx.x == 0) {
@@ -786,37 +803,47 @@ __global__ __launch_bounds__(RTN_NT) void rtn8_kernel(const float *__restrict__ 
     const int lg = __builtin_ctz((unsigned)G);               // G is a power of two
     double num = 0.0, den = 0.0;
     bool bad = false;
-    // Passes: rows by workgroup, a row's 8-column chunks 256 at a time (every
-    // lane takes part in each pass, those past the row with a dummy chunk; a
-    // group of G/8 lanes is wholly in or out, since 256 and the row's chunk
-    // count are multiples of G/8).  The next pass's weights are loaded before
-    // this pass's arithmetic, so that two passes' loads are in flight.
-    auto wload = [&](int64_t row, int64_t cbase, float4 &a, float4 &b, float4 &ia, float4 &ib) {
-        const int64_t cc = cbase + threadIdx.x < chunks ? cbase + threadIdx.x : 0;
-        a = *(const float4 *)(W + row * K + 8 * cc);
-        b = *(const float4 *)(W + row * K + 8 * cc + 4);
+    // Passes over the flat index of the 8-column chunks (row-major, N x K/8 of
+    // them): the workgroup's 256 consecutive chunks, then the grid's stride on.
+    // Every lane takes part in each pass, those past the end with a dummy
+    // chunk; a group of G/8 lanes is wholly in or out, since the stride and the
+    // row's chunk count are multiples of G/8.  The next pass's weights are
+    // loaded before this pass's arithmetic, so that two passes' loads are in
+    // flight.
+    const int64_t total = N * chunks;
+    const int64_t stride = (int64_t)gridDim.x * RTN_NT;
+    const int64_t dq = stride / chunks, dr = stride - dq * chunks;
+    auto wload = [&](int64_t row, int64_t cc, bool ok, float4 &a, float4 &b, float4 &ia, float4 &ib) {
+        const int64_t r = ok ? row : 0, c8 = ok ? cc : 0;
+        a = *(const float4 *)(W + r * K + 8 * c8);
+        b = *(const float4 *)(W + r * K + 8 * c8 + 4);
         if (partials && imp) {                       // 16-byte aligned (checked at launch)
-            ia = *(const float4 *)(imp + 8 * cc);
-            ib = *(const float4 *)(imp + 8 * cc + 4);
+            ia = *(const float4 *)(imp + 8 * c8);
+            ib = *(const float4 *)(imp + 8 * c8 + 4);
         } else {
             ia = ib = make_float4(1.0f, 1.0f, 1.0f, 1.0f);
         }
     };
     float4 na, nbv, nia, nib;
-    int64_t row = blockIdx.x, cbase = 0;
-    if (row < N) wload(row, cbase, na, nbv, nia, nib);
-    for (; row < N;) {
-        const int64_t cb = cbase + threadIdx.x;
-        const bool valid = cb < chunks;
-        const int64_t c = valid ? cb : 0;
+    int64_t base = (int64_t)blockIdx.x * RTN_NT;     // the workgroup's first chunk of the pass
+    int64_t gi = base + threadIdx.x;
+    int64_t row = gi / chunks, cn = gi - row * chunks;
+    bool nvalid = gi < total;
+    if (base < total) wload(row, cn, nvalid, na, nbv, nia, nib);
+    for (; base < total;) {
+        const bool valid = nvalid;
+        const int64_t c = valid ? cn : 0, prow = valid ? row : 0;
         const float4 a = na, b = nbv, i0 = nia, i1 = nib;
-        const int64_t prow = row;
-        cbase += RTN_NT;
-        if (cbase >= chunks) {
-            cbase = 0;
-            row += gridDim.x;
+        base += stride;
+        gi += stride;
+        row += dq;
+        cn += dr;
+        if (cn >= chunks) {
+            cn -= chunks;
+            ++row;
         }
-        if (row < N) wload(row, cbase, na, nbv, nia, nib);
+        nvalid = gi < total;
+        if (base < total) wload(row, cn, nvalid, na, nbv, nia, nib);
         const float w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
 #pragma unroll
         for (int t = 0; t < 8; ++t) bad = bad || (valid && !isfinite(w[t]));
