@@ -36,7 +36,7 @@ METRIC = "GPTQ int4 weights quantized/sec at K=5120/17408; Hessian TFLOP/s vs MF
 # MI355X published peaks (dense): HBM 8 TB/s; bf16 2.5 PFLOP/s; int8 5.0 POP/s; fp32 157.3;
 # fp64 78.6 TFLOP/s
 PEAK_TFLOPS = {"bf16": 2516.6, "i8": 5000.0, "f32": 157.3, "f64": 78.6}
-OZ_MODULI = 14             # residue products per emulated fp64 product (psd_project, K < 65536)
+OZ_MODULI = 13             # residue products per emulated fp64 product (psd_project, K < 65536)
 PEAK_HBM_GBS = 8000.0
 SWEEP_BLOCK = 128          # lazy-batch width of gptq_sweep (include/gq.h)
 
@@ -287,8 +287,8 @@ def main():
         "vs_baseline": None,
         "dtype": "f64",
         "dtype_by_stage": {"accumulate": "bf16 products, f32 accumulate",
-                           "psd": ("f64-class products: operands rounded to 47-48-bit integers per row, exact "
-                                   "int8 residue products mod 14 moduli, 128-bit CRT, f64 epilogue"
+                           "psd": ("f64-class products: operands rounded to 43-44-bit integers per row, exact "
+                                   "int8 residue products mod 13 moduli, 128-bit CRT, f64 epilogue"
                                    if emulated else "f64"),
                            "factor": "f64", "sweep": "f32", "storage": "u16/u32 bits"},
         "data": "synthetic",

@@ -169,7 +169,7 @@ int psd_project_products(void);
  * within about 67 times the mean diagonal, a few more when it is larger (three
  * at a thousand times).  For K < 65536 its symmetric products are
  * computed exactly in integers on the int8 matrix cores from operands rounded
- * to 47-48-bit integers (one power-of-two scale per row; residues modulo 14
+ * to 43-44-bit integers (one power-of-two scale per row; residues modulo 13
  * moduli, Chinese remainder reconstruction, one rounding to fp64); above that,
  * fp64 matrix core products.
  *   H   K x K fp32; the lower triangle is read, the full symmetric result is

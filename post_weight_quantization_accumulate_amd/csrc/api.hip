@@ -889,7 +889,7 @@ int psd_project(float *H, int64_t K, void *ws, size_t ws_bytes, hipStream_t stre
         }
         tm.launches = launched;
         tm.ms = total;
-        tm.kernel = psd_emulated(K) ? "oz_gemm_kernel (int8 residue products, 14 moduli)"
+        tm.kernel = psd_emulated(K) ? "oz_gemm_kernel (int8 residue products, 13 moduli)"
                                     : "gemm_tn_streamk_kernel<double,double> (fp64 products)";
         tm.valid = true;
     }

@@ -137,7 +137,7 @@ hipError_t gemm_tn_f64_out_f32_streamk(const GemmDesc &d, void *partials, unsign
 // zero), and ORs ST_RANGE into *status if an entry reaches 2^o.exp.  Cres is
 // oz_planes_bytes(K) bytes of scratch; beta is oz_beta(K) for every operand.
 // after_gemm, if set, is recorded on s right after the int8 product kernel.
-constexpr int kOzMods = 14;
+constexpr int kOzMods = 13;
 struct OzConst {
     int m[kOzMods];
     double inv_m[kOzMods];

@@ -20,8 +20,8 @@
 //      residues, since |sum| <= K 2^(2 beta) < M / 2, M = prod m_r; it is then
 //      scaled back and rounded to fp64 once.
 // The only rounding is the truncation of step 1 (relative 2^-beta per entry of
-// the row's scale) and the final conversion; with 14 moduli (M ~ 2^110.2) beta
-// is 48 at K = 5120 and 47 at K = 17408.  The 14 int8 products run at the int8
+// the row's scale) and the final conversion; with 13 moduli (M ~ 2^102.5) beta
+// is 44 at K = 5120 and 43 at K = 17408.  The 13 int8 products run at the int8
 // matrix rate, 64 times the fp64 one.
 #include "gq_internal.h"
 
@@ -29,14 +29,14 @@ namespace gq {
 
 namespace {
 
-constexpr int kMods[kOzMods] = {256, 255, 253, 251, 247, 241, 239, 233, 229, 227, 223, 217, 211, 199};
+constexpr int kMods[kOzMods] = {256, 255, 253, 251, 247, 241, 239, 233, 229, 227, 223, 217, 211};
 
 typedef unsigned __int128 u128;
 typedef __int128 i128;
 
 // The reconstruction's constants, at compile time: M = prod m_r and the weights
 // W_r = (M / m_r) ((M / m_r)^-1 mod m_r) (so that sum_r c_r W_r = x mod M for
-// the residues c_r of x), each as limbs of 16 bits (7 for M ~ 2^110.2), which
+// the residues c_r of x), each as limbs of 16 bits (7 for M ~ 2^102.5), which
 // keeps every limb product c_r w below 2^24 (a full-rate 24-bit multiply).
 constexpr u128 oz_modulus()
 {
@@ -88,14 +88,18 @@ static_assert(kLimbs >= 3, "quotient estimate from the top three limbs");
 constexpr double kOzInvMTop = kOzLimbs.invM * (double)((u128)1 << (16 * (kLimbs - 3)));
 // The weight limbs of moduli 2j and 2j+1 side by side (u16 pairs), for
 // v_dot2_u32_u16: one instruction adds both moduli's products into a limb sum.
-static_assert(kOzMods % 2 == 0, "moduli in pairs");
-struct OzPairs { unsigned w[kOzMods / 2][kLimbs]; };
+// With an odd number of moduli the last pair's second half is a residue of 0
+// with a weight of 0.
+constexpr int kOzPairN = (kOzMods + 1) / 2;
+constexpr int kOzRes = 2 * kOzPairN;          // residues per output, the pad included
+struct OzPairs { unsigned w[kOzPairN][kLimbs]; };
 constexpr OzPairs oz_pairs()
 {
     OzPairs P{};
-    for (int j = 0; j < kOzMods / 2; ++j)
+    for (int j = 0; j < kOzPairN; ++j)
         for (int k = 0; k < kLimbs; ++k)
-            P.w[j][k] = (unsigned)kOzLimbs.w[2 * j][k] | ((unsigned)kOzLimbs.w[2 * j + 1][k] << 16);
+            P.w[j][k] = (unsigned)kOzLimbs.w[2 * j][k] |
+                        (2 * j + 1 < kOzMods ? ((unsigned)kOzLimbs.w[2 * j + 1][k] << 16) : 0u);
     return P;
 }
 constexpr OzPairs kOzPairs = oz_pairs();
@@ -478,13 +482,15 @@ __global__ __launch_bounds__(CNT) void oz_crt_kernel(GemmDesc d, const uint8_t *
     bool range_bad = false;
     // residues of 4 consecutive outputs of row li = 16 rr + lr: one dword per
     // plane (Kp is a multiple of 256, j0 + c4 of 4: aligned)
-    auto load_row = [&](unsigned (&rs)[kOzMods], int rr) {
+    auto load_row = [&](unsigned (&rs)[kOzRes], int rr) {
         const int64_t gi = i0 + rr * 16 + lr;
         const uint8_t *p = Cres + (gi < K ? gi : 0) * Kp + j0 + c4;
 #pragma unroll
         for (int r = 0; r < kOzMods; ++r) rs[r] = *(const unsigned *)(p + r * plane);
+#pragma unroll
+        for (int r = kOzMods; r < kOzRes; ++r) rs[r] = 0u;
     };
-    auto do_row = [&](const unsigned (&rs)[kOzMods], int rr) {
+    auto do_row = [&](const unsigned (&rs)[kOzRes], int rr) {
         const int li = rr * 16 + lr;
         const int64_t gi = i0 + li;
         const bool row_in = gi < K;
@@ -494,19 +500,19 @@ __global__ __launch_bounds__(CNT) void oz_crt_kernel(GemmDesc d, const uint8_t *
             double v = 0.0;
             if (row_in && gj < K && gi >= gj) {
                 // S = sum_r c_r W_r by 16-bit limbs of W_r: each limb sum is below
-                // 14 * 255 * 2^16 < 2^28.  The residues of moduli 2j, 2j+1 (byte t
-                // of rs[2j], rs[2j+1]) are put side by side as u16s by one byte
+                // kOzMods * 255 * 2^16 < 2^28.  The residues of moduli 2j, 2j+1 (byte
+                // t of rs[2j], rs[2j+1]) are put side by side as u16s by one byte
                 // permute, and each limb takes one dot2 per pair.
-                u16x2 cp[kOzMods / 2];
+                u16x2 cp[kOzPairN];
 #pragma unroll
-                for (int j = 0; j < kOzMods / 2; ++j)
+                for (int j = 0; j < kOzPairN; ++j)
                     cp[j] = __builtin_bit_cast(u16x2, __builtin_amdgcn_perm(rs[2 * j + 1], rs[2 * j],
                                                                             0x0C000C00u | ((4u + t) << 16) | (unsigned)t));
                 unsigned L[kLimbs] = {};
 #pragma unroll
                 for (int k = 0; k < kLimbs; ++k)
 #pragma unroll
-                    for (int j = 0; j < kOzMods / 2; ++j)
+                    for (int j = 0; j < kOzPairN; ++j)
                         L[k] = __builtin_amdgcn_udot2(cp[j], __builtin_bit_cast(u16x2, kOzPairs.w[j][k]), L[k], false);
                 // The centred value is x = S - q M with q the integer nearest S / M:
                 // |x| <= K 2^(2 beta) < 0.497 M (the choice of beta).  S / M < 2^12 is
@@ -532,7 +538,7 @@ __global__ __launch_bounds__(CNT) void oz_crt_kernel(GemmDesc d, const uint8_t *
     };
     // two rows in flight: each row's residues are loaded while the one before is
     // reconstructed (the last load repeats row 3, in bounds and unused)
-    unsigned ra[kOzMods], rb[kOzMods];
+    unsigned ra[kOzRes], rb[kOzRes];
     load_row(ra, 0);
 #pragma unroll 1
     for (int rr = 0; rr < CT / 16; rr += 2) {
@@ -575,14 +581,14 @@ __global__ __launch_bounds__(CNT) void oz_crt_kernel(GemmDesc d, const uint8_t *
             z[rr][t] = rint(v * sc);
         }
     constexpr int kBatch = 7;
-    static_assert(kOzMods % kBatch == 0, "whole batches");
     static_assert(sizeof(unsigned) * kBatch * CT * (CT / 4 + 1) <= sizeof(double) * CT * (CT + 1), "LDS reuse");
     unsigned (*rt)[CT][CT / 4 + 1] = reinterpret_cast<unsigned (*)[CT][CT / 4 + 1]>(&tile[0][0]);
     __syncthreads();                    // the fp64 tile is no longer read
 #pragma unroll 1
-    for (int batch = 0; batch < kOzMods / kBatch; ++batch) {
+    for (int batch = 0; batch < (kOzMods + kBatch - 1) / kBatch; ++batch) {
+        const int nq = kOzMods - kBatch * batch < kBatch ? kOzMods - kBatch * batch : kBatch;
 #pragma unroll 1
-        for (int q = 0; q < kBatch; ++q) {
+        for (int q = 0; q < nq; ++q) {
             const int r = kBatch * batch + q;
             int8_t *pl = planes + r * plane;
 #pragma unroll
@@ -597,7 +603,7 @@ __global__ __launch_bounds__(CNT) void oz_crt_kernel(GemmDesc d, const uint8_t *
         __syncthreads();
         // mirror rows j0 + li: bytes (i0 + c4 + t) come from rt[q][c4 + t][li]
 #pragma unroll 1
-        for (int q = 0; q < kBatch; ++q) {
+        for (int q = 0; q < nq; ++q) {
             int8_t *pl = planes + (kBatch * batch + q) * plane;
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) {
@@ -658,7 +664,7 @@ int oz_beta(int64_t K)
     // largest beta with K 2^(2 beta) <= 0.497 M, i.e. 2 beta <= log2 M - 1.01 - log2 K
     // (the reconstruction rounds S / M to the nearest integer and needs the
     // centred sum to stay clear of M / 2), and at most 48, where residue_word's
-    // quotient is exact (48 from K = 4100 up to 8192, 47 to 17408)
+    // quotient is exact (44 at K = 5120, 43 at K = 17408)
     const OzConst &c = oz_const();
     const double log2M = std::log2(ldexp((double)c.M_hi, 64) + (double)c.M_lo);
     const double room = log2M - 1.01 - std::log2((double)(K > 1 ? K : 1));
