@@ -24,6 +24,7 @@ from __future__ import annotations
 
 import argparse
 import json
+import re
 import math
 import os
 import sys
@@ -36,7 +37,6 @@ METRIC = "GPTQ int4 weights quantized/sec at K=5120/17408; Hessian TFLOP/s vs MF
 # MI355X published peaks (dense): HBM 8 TB/s; bf16 2.5 PFLOP/s; int8 5.0 POP/s; fp32 157.3;
 # fp64 78.6 TFLOP/s
 PEAK_TFLOPS = {"bf16": 2516.6, "i8": 5000.0, "f32": 157.3, "f64": 78.6}
-OZ_MODULI = 13             # residue products per emulated fp64 product (psd_project, K < 65536)
 PEAK_HBM_GBS = 8000.0
 SWEEP_BLOCK = 128          # lazy-batch width of gptq_sweep (include/gq.h)
 
@@ -200,11 +200,18 @@ def update_flops(N, K):
                for b0 in range(0, K, SWEEP_BLOCK))
 
 
+def moduli_of(kernel_name):
+    """Residue products per emulated fp64 product, as psd_project names its
+    product kernel ("... N moduli"); 1 for the fp64 products."""
+    m = re.search(r"(\d+) moduli", kernel_name)
+    return int(m.group(1)) if m else 1
+
+
 def product_roofline(K, r, steps):
     """The sign iteration's product kernel: its ops per launch and live rate."""
     prod = r["prod"]
     emulated = prod["kernel"].startswith("oz_gemm")
-    per_launch = K * K * (K + 1) * (OZ_MODULI if emulated else 1)
+    per_launch = K * K * (K + 1) * (moduli_of(prod["kernel"]) if emulated else 1)
     prod_ms = prod["ms"] / prod["launches"]
     tops = per_launch / (prod_ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS["i8" if emulated else "f64"]
@@ -287,8 +294,9 @@ def main():
         "vs_baseline": None,
         "dtype": "f64",
         "dtype_by_stage": {"accumulate": "bf16 products, f32 accumulate",
-                           "psd": ("f64-class products: operands rounded to 43-44-bit integers per row, exact "
-                                   "int8 residue products mod 13 moduli, 128-bit CRT, f64 epilogue"
+                           "psd": ("f64-class products: operands rounded per row to integers of 40 bits (12 "
+                                   "moduli, K <= 8192) or 43-44 bits (13 moduli), exact int8 residue products, "
+                                   "128-bit CRT, f64 epilogue"
                                    if emulated else "f64"),
                            "factor": "f64", "sweep": "f32", "storage": "u16/u32 bits"},
         "data": "synthetic",
@@ -312,7 +320,8 @@ def main():
             "traffic": traffic,
             "traffic_detail": traffic_detail,
             "algorithmic_bytes_per_launch": (
-                {"read_residue_planes_A_B": 2 * OZ_MODULI * K * K, "write_residues_lower": OZ_MODULI * K * (K + 1) // 2}
+                {"read_residue_planes_A_B": 2 * moduli_of(r["prod"]["kernel"]) * K * K,
+                 "write_residues_lower": moduli_of(r["prod"]["kernel"]) * K * (K + 1) // 2}
                 if emulated else
                 {"read_AB": 2 * K * K * 8, "read_cin_step_products": K * K * 8, "write_lower_and_mirror": K * K * 8}),
             "per_launch_ops": per_launch,

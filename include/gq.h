@@ -169,8 +169,9 @@ int psd_project_products(void);
  * within about 67 times the mean diagonal, a few more when it is larger (three
  * at a thousand times).  For K < 65536 its symmetric products are
  * computed exactly in integers on the int8 matrix cores from operands rounded
- * to 43-44-bit integers (one power-of-two scale per row; residues modulo 13
- * moduli, Chinese remainder reconstruction, one rounding to fp64); above that,
+ * to 40-bit integers up to K = 8192 and 43-44-bit integers above (one
+ * power-of-two scale per row; residues modulo 12 or 13 moduli, Chinese
+ * remainder reconstruction, one rounding to fp64); from K = 65536 on,
  * fp64 matrix core products.
  *   H   K x K fp32; the lower triangle is read, the full symmetric result is
  *       written in place.

@@ -889,8 +889,9 @@ int psd_project(float *H, int64_t K, void *ws, size_t ws_bytes, hipStream_t stre
         }
         tm.launches = launched;
         tm.ms = total;
-        tm.kernel = psd_emulated(K) ? "oz_gemm_kernel (int8 residue products, 13 moduli)"
-                                    : "gemm_tn_streamk_kernel<double,double> (fp64 products)";
+        tm.kernel = !psd_emulated(K) ? "gemm_tn_streamk_kernel<double,double> (fp64 products)"
+                    : oz_mods(K) == 12 ? "oz_gemm_kernel (int8 residue products, 12 moduli)"
+                                       : "oz_gemm_kernel (int8 residue products, 13 moduli)";
         tm.valid = true;
     }
     if (st & ST_RANGE) return fail(GQ_ERR_INTERNAL, "an iterate of the sign iteration left the range [-2, 2]");

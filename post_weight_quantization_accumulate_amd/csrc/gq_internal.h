@@ -123,8 +123,8 @@ hipError_t gemm_tn_f64_out_f32_streamk(const GemmDesc &d, void *partials, unsign
 
 // Products of symmetric fp64 matrices by modular integer emulation on the int8
 // matrix cores (ozaki.hip).  The split form of a K x K symmetric matrix Z holds
-// the residues, modulo each of kOzMods moduli, of its row-scaled integer form
-// rint(Z_ik 2^(beta - e_i)) (oz_planes_bytes(K) bytes: kOzMods planes of
+// the residues, modulo each of oz_mods(K) moduli, of its row-scaled integer form
+// rint(Z_ik 2^(beta - e_i)) (oz_planes_bytes(K) bytes: oz_mods(K) planes of
 // Kp x Kp int8 in blocks of 256 rows x 64 k, zero padded), with e_i either per
 // row (rowexp) or one exponent
 // for every row (entries below 2^exp in magnitude).  oz_split writes it with
@@ -137,10 +137,14 @@ hipError_t gemm_tn_f64_out_f32_streamk(const GemmDesc &d, void *partials, unsign
 // zero), and ORs ST_RANGE into *status if an entry reaches 2^o.exp.  Cres is
 // oz_planes_bytes(K) bytes of scratch; beta is oz_beta(K) for every operand.
 // after_gemm, if set, is recorded on s right after the int8 product kernel.
-constexpr int kOzMods = 13;
+// A product of order K uses the first oz_mods(K) of kOzMaxMods moduli: 12 up to
+// K = kOzFewModsMaxK (operands of 40 bits), 13 above (43-44 bits).
+constexpr int kOzMaxMods = 13;
+constexpr int64_t kOzFewModsMaxK = 8192;
 struct OzConst {
-    int m[kOzMods];
-    double inv_m[kOzMods];
+    int nm;                                            // moduli in use
+    int m[kOzMaxMods];
+    double inv_m[kOzMaxMods];
     unsigned long long M_lo, M_hi;                     // M = prod m_r
 };
 struct OzOperand {
@@ -153,7 +157,8 @@ struct OzOut {
     int exp;
     double diag_shift;
 };
-const OzConst &oz_const();
+int oz_mods(int64_t K);
+const OzConst &oz_const(int nm);
 int oz_beta(int64_t K);
 int64_t oz_padded(int64_t K);
 size_t oz_planes_bytes(int64_t K);

@@ -12,7 +12,7 @@
 //      are symmetric, C_ij = 2^(e_i + e_j - 2 beta) sum_k a_ik b_jk: the integer
 //      operands are read row by row, k contiguous, which is the layout the int8
 //      matrix instruction wants for both of its operands.
-//   2. each integer matrix is stored as its residues modulo kOzMods pairwise
+//   2. each integer matrix is stored as its residues modulo oz_mods(K) pairwise
 //      coprime moduli m_r <= 256, each residue centred to fit int8;
 //   3. per modulus, one int8 GEMM with exact int32 accumulation gives
 //      sum_k a_ik b_jk mod m_r (|sum| < K 128^2 < 2^31 for K < 2^17);
@@ -20,8 +20,9 @@
 //      residues, since |sum| <= K 2^(2 beta) < M / 2, M = prod m_r; it is then
 //      scaled back and rounded to fp64 once.
 // The only rounding is the truncation of step 1 (relative 2^-beta per entry of
-// the row's scale) and the final conversion; with 13 moduli (M ~ 2^102.5) beta
-// is 44 at K = 5120 and 43 at K = 17408.  The 13 int8 products run at the int8
+// the row's scale) and the final conversion.  Up to K = 8192 a product uses 12
+// moduli (M ~ 2^94.8, beta = 40 at K = 5120), above that 13 (M ~ 2^102.5, beta =
+// 43 at K = 17408).  The int8 products, one per modulus, run at the int8
 // matrix rate, 64 times the fp64 one.
 #include "gq_internal.h"
 
@@ -29,93 +30,99 @@ namespace gq {
 
 namespace {
 
-constexpr int kMods[kOzMods] = {256, 255, 253, 251, 247, 241, 239, 233, 229, 227, 223, 217, 211};
+// The moduli: the largest pairwise coprime values whose residues, centred,
+// fit int8.  A product uses the first oz_mods(K) of them.
+constexpr int kMods[kOzMaxMods] = {256, 255, 253, 251, 247, 241, 239, 233, 229, 227, 223, 217, 211};
 
 typedef unsigned __int128 u128;
 typedef __int128 i128;
 
-// The reconstruction's constants, at compile time: M = prod m_r and the weights
-// W_r = (M / m_r) ((M / m_r)^-1 mod m_r) (so that sum_r c_r W_r = x mod M for
-// the residues c_r of x), each as limbs of 16 bits (7 for M ~ 2^102.5), which
-// keeps every limb product c_r w below 2^24 (a full-rate 24-bit multiply).
-constexpr u128 oz_modulus()
+// The reconstruction's constants for the first NM moduli, at compile time:
+// M = prod m_r and the weights W_r = (M / m_r) ((M / m_r)^-1 mod m_r) (so that
+// sum_r c_r W_r = x mod M for the residues c_r of x), each as limbs of 16 bits
+// (6 for 12 moduli, M ~ 2^94.8; 7 for 13, M ~ 2^102.5), which keeps every limb
+// product c_r w below 2^24 (a full-rate 24-bit multiply).
+template <int NM> constexpr u128 oz_modulus()
 {
     u128 M = 1;
-    for (int r = 0; r < kOzMods; ++r) M *= (u128)kMods[r];
+    for (int r = 0; r < NM; ++r) M *= (u128)kMods[r];
     return M;
 }
-constexpr int oz_limb_count()
+template <int NM> constexpr int oz_limb_count()
 {
     int bits = 0;
-    for (u128 m = oz_modulus(); m; m >>= 1) ++bits;
+    for (u128 m = oz_modulus<NM>(); m; m >>= 1) ++bits;
     return (bits + 16) / 16;                  // one spare bit: signed limbs of values up to M
 }
-constexpr int kLimbs = oz_limb_count();
-struct OzLimbs {
-    unsigned short w[kOzMods][kLimbs];
-    unsigned short M[kLimbs];
+template <int NM> struct OzLimbs {
+    static constexpr int L = oz_limb_count<NM>();
+    unsigned short w[NM][L];
+    unsigned short M[L];
     double invM;
 };
-constexpr OzLimbs oz_limbs()
+template <int NM> constexpr OzLimbs<NM> oz_limbs()
 {
-    OzLimbs L{};
-    const u128 M = oz_modulus();
-    for (int r = 0; r < kOzMods; ++r) {
+    OzLimbs<NM> L{};
+    const u128 M = oz_modulus<NM>();
+    for (int r = 0; r < NM; ++r) {
         const u128 Mr = M / (u128)kMods[r];
         const int t = (int)(Mr % (u128)kMods[r]);
         int y = 1;
         while ((t * y) % kMods[r] != 1) ++y;
         const u128 W = Mr * (u128)y;                    // y < m_r, so W < M
-        for (int k = 0; k < kLimbs; ++k) L.w[r][k] = (unsigned short)(W >> (16 * k));
+        for (int k = 0; k < OzLimbs<NM>::L; ++k) L.w[r][k] = (unsigned short)(W >> (16 * k));
     }
-    for (int k = 0; k < kLimbs; ++k) L.M[k] = (unsigned short)(M >> (16 * k));
+    for (int k = 0; k < OzLimbs<NM>::L; ++k) L.M[k] = (unsigned short)(M >> (16 * k));
     L.invM = 1.0 / ((double)(unsigned long long)(M >> 64) * 18446744073709551616.0 +
                     (double)(unsigned long long)M);
     return L;
 }
-constexpr u128 kOzM = oz_modulus();
-struct OzInv { double v[kOzMods]; };
+template <int NM> constexpr OzLimbs<NM> kOzLimbs = oz_limbs<NM>();
+struct OzInv { double v[kOzMaxMods]; };
 constexpr OzInv oz_inverses()
 {
     OzInv t{};
-    for (int r = 0; r < kOzMods; ++r) t.v[r] = 1.0 / (double)kMods[r];
+    for (int r = 0; r < kOzMaxMods; ++r) t.v[r] = 1.0 / (double)kMods[r];
     return t;
 }
 constexpr OzInv kOzInv = oz_inverses();
-constexpr OzLimbs kOzLimbs = oz_limbs();
-static_assert(kLimbs >= 3, "quotient estimate from the top three limbs");
-// 1/M scaled by the weight of limb kLimbs - 3 (a power of two: exact)
-constexpr double kOzInvMTop = kOzLimbs.invM * (double)((u128)1 << (16 * (kLimbs - 3)));
+// 1/M scaled by the weight of limb L - 3 (a power of two: exact)
+template <int NM>
+constexpr double kOzInvMTop = kOzLimbs<NM>.invM * (double)((u128)1 << (16 * (OzLimbs<NM>::L - 3)));
 // The weight limbs of moduli 2j and 2j+1 side by side (u16 pairs), for
 // v_dot2_u32_u16: one instruction adds both moduli's products into a limb sum.
 // With an odd number of moduli the last pair's second half is a residue of 0
 // with a weight of 0.
-constexpr int kOzPairN = (kOzMods + 1) / 2;
-constexpr int kOzRes = 2 * kOzPairN;          // residues per output, the pad included
-struct OzPairs { unsigned w[kOzPairN][kLimbs]; };
-constexpr OzPairs oz_pairs()
+template <int NM> struct OzPairs {
+    static constexpr int N = (NM + 1) / 2;
+    static constexpr int RES = 2 * N;               // residues per output, the pad included
+    unsigned w[N][OzLimbs<NM>::L];
+};
+template <int NM> constexpr OzPairs<NM> oz_pairs()
 {
-    OzPairs P{};
-    for (int j = 0; j < kOzPairN; ++j)
-        for (int k = 0; k < kLimbs; ++k)
-            P.w[j][k] = (unsigned)kOzLimbs.w[2 * j][k] |
-                        (2 * j + 1 < kOzMods ? ((unsigned)kOzLimbs.w[2 * j + 1][k] << 16) : 0u);
+    OzPairs<NM> P{};
+    for (int j = 0; j < OzPairs<NM>::N; ++j)
+        for (int k = 0; k < OzLimbs<NM>::L; ++k)
+            P.w[j][k] = (unsigned)kOzLimbs<NM>.w[2 * j][k] |
+                        (2 * j + 1 < NM ? ((unsigned)kOzLimbs<NM>.w[2 * j + 1][k] << 16) : 0u);
     return P;
 }
-constexpr OzPairs kOzPairs = oz_pairs();
+template <int NM> constexpr OzPairs<NM> kOzPairs = oz_pairs<NM>();
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
-static_assert((kOzM >> (16 * kLimbs - 1)) == 0, "M fits the limbs");
+static_assert(OzLimbs<12>::L >= 3 && OzLimbs<13>::L >= 3, "quotient estimate from the top three limbs");
+static_assert((oz_modulus<12>() >> (16 * OzLimbs<12>::L - 1)) == 0, "M fits the limbs");
+static_assert((oz_modulus<13>() >> (16 * OzLimbs<13>::L - 1)) == 0, "M fits the limbs");
 
 // sum_k D[k] 2^(16 k) for signed limbs |D[k]| < 2^31
-__device__ inline i128 from_signed_limbs(const int (&D)[kLimbs])
+template <int L> __device__ inline i128 from_signed_limbs(const int (&D)[L])
 {
     // two's complement sums in unsigned arithmetic (wrapping, shifts defined),
     // limbs paired into 64-bit words first
     u128 x = 0;
-    static_for<(kLimbs + 1) / 2>([&](auto P) {
+    static_for<(L + 1) / 2>([&](auto P) {
         constexpr int k = 2 * decltype(P)::value;
         unsigned long long pk = (unsigned long long)(long long)D[k];
-        if constexpr (k + 1 < kLimbs) pk += (unsigned long long)(long long)D[k + 1] << 16;
+        if constexpr (k + 1 < L) pk += (unsigned long long)(long long)D[k + 1] << 16;
         x += (u128)(i128)(long long)pk << (16 * k);
     });
     return (i128)x;
@@ -153,6 +160,7 @@ constexpr int SPL_NT = 256;
 
 __device__ inline int64_t poff(int64_t row, int64_t k, int64_t Kp);
 
+template <int NM>
 __global__ __launch_bounds__(SPL_NT) void oz_split_kernel(const double *__restrict__ Z, int64_t K, int64_t Kp,
                                                           int beta, int8_t *__restrict__ planes,
                                                           int *__restrict__ rowexp,
@@ -166,7 +174,7 @@ __global__ __launch_bounds__(SPL_NT) void oz_split_kernel(const double *__restri
     if (i >= K) {                       // padding rows: zero in every plane
         for (int64_t k = 8 * tid; k < Kp; k += 8 * SPL_NT)
 #pragma unroll
-            for (int r = 0; r < kOzMods; ++r) *(uint2 *)(planes + r * plane + poff(i, k, Kp)) = make_uint2(0u, 0u);
+            for (int r = 0; r < NM; ++r) *(uint2 *)(planes + r * plane + poff(i, k, Kp)) = make_uint2(0u, 0u);
         if (tid == 0) rowexp[i] = 0;
         return;
     }
@@ -195,7 +203,7 @@ __global__ __launch_bounds__(SPL_NT) void oz_split_kernel(const double *__restri
         for (int t = 0; t < 8; ++t) z[t] = (k0 + t < K) ? rint(zr[k0 + t] * sc) : 0.0;   // exact integers
         const double z0[4] = {z[0], z[1], z[2], z[3]}, z1[4] = {z[4], z[5], z[6], z[7]};
 #pragma unroll
-        for (int r = 0; r < kOzMods; ++r)
+        for (int r = 0; r < NM; ++r)
             *(uint2 *)(planes + r * plane + poff(i, k0, Kp)) = make_uint2(residue_word(z0, r), residue_word(z1, r));
     }
 }
@@ -444,7 +452,7 @@ static_assert(kOzGemmLds >= (size_t)OBM * kOzEpiRow, "output tile");
 constexpr int CT = 64, CNT = 256;
 
 
-template <typename OutT>
+template <int NM, typename OutT>
 __global__ __launch_bounds__(CNT) void oz_crt_kernel(GemmDesc d, const uint8_t *__restrict__ Cres, int64_t Kp,
                                                     OzOperand A, OzOperand B, int twobeta, OzOut o,
                                                     int beta, unsigned *status)
@@ -482,13 +490,14 @@ __global__ __launch_bounds__(CNT) void oz_crt_kernel(GemmDesc d, const uint8_t *
     bool range_bad = false;
     // residues of 4 consecutive outputs of row li = 16 rr + lr: one dword per
     // plane (Kp is a multiple of 256, j0 + c4 of 4: aligned)
+    constexpr int kLimbs = OzLimbs<NM>::L, kOzPairN = OzPairs<NM>::N, kOzRes = OzPairs<NM>::RES;
     auto load_row = [&](unsigned (&rs)[kOzRes], int rr) {
         const int64_t gi = i0 + rr * 16 + lr;
         const uint8_t *p = Cres + (gi < K ? gi : 0) * Kp + j0 + c4;
 #pragma unroll
-        for (int r = 0; r < kOzMods; ++r) rs[r] = *(const unsigned *)(p + r * plane);
+        for (int r = 0; r < NM; ++r) rs[r] = *(const unsigned *)(p + r * plane);
 #pragma unroll
-        for (int r = kOzMods; r < kOzRes; ++r) rs[r] = 0u;
+        for (int r = NM; r < kOzRes; ++r) rs[r] = 0u;
     };
     auto do_row = [&](const unsigned (&rs)[kOzRes], int rr) {
         const int li = rr * 16 + lr;
@@ -500,7 +509,7 @@ __global__ __launch_bounds__(CNT) void oz_crt_kernel(GemmDesc d, const uint8_t *
             double v = 0.0;
             if (row_in && gj < K && gi >= gj) {
                 // S = sum_r c_r W_r by 16-bit limbs of W_r: each limb sum is below
-                // kOzMods * 255 * 2^16 < 2^28.  The residues of moduli 2j, 2j+1 (byte
+                // NM * 255 * 2^16 < 2^28.  The residues of moduli 2j, 2j+1 (byte
                 // t of rs[2j], rs[2j+1]) are put side by side as u16s by one byte
                 // permute, and each limb takes one dot2 per pair.
                 u16x2 cp[kOzPairN];
@@ -513,7 +522,7 @@ __global__ __launch_bounds__(CNT) void oz_crt_kernel(GemmDesc d, const uint8_t *
                 for (int k = 0; k < kLimbs; ++k)
 #pragma unroll
                     for (int j = 0; j < kOzPairN; ++j)
-                        L[k] = __builtin_amdgcn_udot2(cp[j], __builtin_bit_cast(u16x2, kOzPairs.w[j][k]), L[k], false);
+                        L[k] = __builtin_amdgcn_udot2(cp[j], __builtin_bit_cast(u16x2, kOzPairs<NM>.w[j][k]), L[k], false);
                 // The centred value is x = S - q M with q the integer nearest S / M:
                 // |x| <= K 2^(2 beta) < 0.497 M (the choice of beta).  S / M < 2^12 is
                 // estimated from the top three limbs (the rest adds below 2^-19 to
@@ -521,10 +530,10 @@ __global__ __launch_bounds__(CNT) void oz_crt_kernel(GemmDesc d, const uint8_t *
                 // limbs L[k] - q M[k] (q M[k] < 2^28), one carry pass in 128 bits.
                 const double St = fma(fma((double)L[kLimbs - 1], 65536.0, (double)L[kLimbs - 2]), 65536.0,
                                       (double)L[kLimbs - 3]);
-                const int nq = -(int)rint(St * kOzInvMTop);
+                const int nq = -(int)rint(St * kOzInvMTop<NM>);
                 int D[kLimbs];
 #pragma unroll
-                for (int k = 0; k < kLimbs; ++k) D[k] = __mul24(nq, (int)kOzLimbs.M[k]) + (int)L[k];
+                for (int k = 0; k < kLimbs; ++k) D[k] = __mul24(nq, (int)kOzLimbs<NM>.M[k]) + (int)L[k];
                 const i128 x = from_signed_limbs(D);
                 const double xd = ldexp((double)(long long)(x >> 64), 64) + (double)(unsigned long long)x;
                 const int e = (ea ? ea[gi] : A.exp) + (eb ? eb[gj] : B.exp);
@@ -585,8 +594,8 @@ __global__ __launch_bounds__(CNT) void oz_crt_kernel(GemmDesc d, const uint8_t *
     unsigned (*rt)[CT][CT / 4 + 1] = reinterpret_cast<unsigned (*)[CT][CT / 4 + 1]>(&tile[0][0]);
     __syncthreads();                    // the fp64 tile is no longer read
 #pragma unroll 1
-    for (int batch = 0; batch < (kOzMods + kBatch - 1) / kBatch; ++batch) {
-        const int nq = kOzMods - kBatch * batch < kBatch ? kOzMods - kBatch * batch : kBatch;
+    for (int batch = 0; batch < (NM + kBatch - 1) / kBatch; ++batch) {
+        const int nq = NM - kBatch * batch < kBatch ? NM - kBatch * batch : kBatch;
 #pragma unroll 1
         for (int q = 0; q < nq; ++q) {
             const int r = kBatch * batch + q;
@@ -621,11 +630,11 @@ __global__ __launch_bounds__(CNT) void oz_crt_kernel(GemmDesc d, const uint8_t *
 // The bytes of a split form that oz_crt_kernel never writes: rows K .. Kp - 1,
 // and in rows below K the 64-byte row segments from column ceil(K / 64) 64 on
 // (the CRT's tiles end there).  One 16-byte chunk per thread and step.
-__global__ void oz_pad_kernel(int8_t *__restrict__ planes, int64_t K, int64_t Kp, int64_t per_plane)
+__global__ void oz_pad_kernel(int8_t *__restrict__ planes, int64_t K, int64_t Kp, int64_t per_plane, int nm)
 {
     const int64_t kseg = Kp >> 6, c0 = (K + 63) >> 6;
     const int64_t low = K * (kseg - c0);                // padding segments in rows below K
-    const int64_t total = per_plane * kOzMods * 4;
+    const int64_t total = per_plane * nm * 4;
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total; e += stride) {
         const int64_t sg = e >> 2, r = sg / per_plane;
@@ -644,19 +653,24 @@ __global__ void oz_pad_kernel(int8_t *__restrict__ planes, int64_t K, int64_t Kp
 
 }  // namespace
 
-const OzConst &oz_const()
+int oz_mods(int64_t K) { return K <= kOzFewModsMaxK ? 12 : 13; }
+
+const OzConst &oz_const(int nm)
 {
-    static OzConst c = [] {
+    auto make = [](int n) {
         OzConst k{};
-        for (int r = 0; r < kOzMods; ++r) {
+        k.nm = n;
+        for (int r = 0; r < n; ++r) {
             k.m[r] = kMods[r];
             k.inv_m[r] = 1.0 / (double)kMods[r];
         }
-        k.M_lo = (unsigned long long)kOzM;
-        k.M_hi = (unsigned long long)(kOzM >> 64);
+        const u128 M = n == 12 ? oz_modulus<12>() : oz_modulus<13>();
+        k.M_lo = (unsigned long long)M;
+        k.M_hi = (unsigned long long)(M >> 64);
         return k;
-    }();
-    return c;
+    };
+    static const OzConst c12 = make(12), c13 = make(13);
+    return nm == 12 ? c12 : c13;
 }
 
 int oz_beta(int64_t K)
@@ -664,8 +678,8 @@ int oz_beta(int64_t K)
     // largest beta with K 2^(2 beta) <= 0.497 M, i.e. 2 beta <= log2 M - 1.01 - log2 K
     // (the reconstruction rounds S / M to the nearest integer and needs the
     // centred sum to stay clear of M / 2), and at most 48, where residue_word's
-    // quotient is exact (44 at K = 5120, 43 at K = 17408)
-    const OzConst &c = oz_const();
+    // quotient is exact (40 at K = 5120 with 12 moduli, 43 at K = 17408 with 13)
+    const OzConst &c = oz_const(oz_mods(K));
     const double log2M = std::log2(ldexp((double)c.M_hi, 64) + (double)c.M_lo);
     const double room = log2M - 1.01 - std::log2((double)(K > 1 ? K : 1));
     const int b = (int)std::floor(room / 2.0);
@@ -677,15 +691,19 @@ int64_t oz_padded(int64_t K) { return (K + OBM - 1) / OBM * OBM; }
 size_t oz_planes_bytes(int64_t K)
 {
     const int64_t Kp = oz_padded(K);
-    return (size_t)kOzMods * (size_t)Kp * (size_t)Kp;
+    return (size_t)oz_mods(K) * (size_t)Kp * (size_t)Kp;
 }
 
 hipError_t oz_split(const double *Z, int64_t K, int beta, int8_t *planes, int *rowexp, hipStream_t s,
                     const unsigned long long *rowmax)
 {
     const int64_t Kp = oz_padded(K);
-    hipLaunchKernelGGL(oz_split_kernel, dim3((unsigned)Kp), dim3(SPL_NT), 0, s, Z, K, Kp, beta, planes, rowexp,
-                       rowmax);
+    if (oz_mods(K) == 12)
+        hipLaunchKernelGGL(oz_split_kernel<12>, dim3((unsigned)Kp), dim3(SPL_NT), 0, s, Z, K, Kp, beta, planes, rowexp,
+                           rowmax);
+    else
+        hipLaunchKernelGGL(oz_split_kernel<13>, dim3((unsigned)Kp), dim3(SPL_NT), 0, s, Z, K, Kp, beta, planes, rowexp,
+                           rowmax);
     return hipGetLastError();
 }
 
@@ -702,24 +720,34 @@ hipError_t oz_product(const GemmDesc &d, const OzOperand &A, const OzOperand &B,
                          hipFuncSetAttribute((const void *)oz_gemm_kernel<true>,
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)kOzGemmLds) == hipSuccess;
     if (!lds_ok) return hipErrorInvalidConfiguration;
+    const int nm = oz_mods(K);
     // residues centred in [-128, 128): |P| <= Kp 2^14, within 2^29 up to Kp = 32768
     if (Kp <= 32768)
-        hipLaunchKernelGGL(oz_gemm_kernel<false>, dim3((unsigned)(nt * (nt + 1) / 2), kOzMods), dim3(ONT), kOzGemmLds,
-                           s, A.planes, B.planes, Kp, Cres, oz_const());
+        hipLaunchKernelGGL(oz_gemm_kernel<false>, dim3((unsigned)(nt * (nt + 1) / 2), (unsigned)nm), dim3(ONT),
+                           kOzGemmLds, s, A.planes, B.planes, Kp, Cres, oz_const(nm));
     else
-        hipLaunchKernelGGL(oz_gemm_kernel<true>, dim3((unsigned)(nt * (nt + 1) / 2), kOzMods), dim3(ONT), kOzGemmLds,
-                           s, A.planes, B.planes, Kp, Cres, oz_const());
+        hipLaunchKernelGGL(oz_gemm_kernel<true>, dim3((unsigned)(nt * (nt + 1) / 2), (unsigned)nm), dim3(ONT),
+                           kOzGemmLds, s, A.planes, B.planes, Kp, Cres, oz_const(nm));
     if (after_gemm) {
         const hipError_t e = hipEventRecord(after_gemm, s);
         if (e != hipSuccess) return e;
     }
-    const int64_t ct = (K + CT - 1) / CT;
-    if (out_f32)
-        hipLaunchKernelGGL(oz_crt_kernel<float>, dim3((unsigned)(ct * (ct + 1) / 2)), dim3(CNT), 0, s, d, Cres, Kp,
-                           A, B, 2 * beta, o, beta, status);
-    else
-        hipLaunchKernelGGL(oz_crt_kernel<double>, dim3((unsigned)(ct * (ct + 1) / 2)), dim3(CNT), 0, s, d, Cres, Kp,
-                           A, B, 2 * beta, o, beta, status);
+    const dim3 cg((unsigned)(((K + CT - 1) / CT) * ((K + CT - 1) / CT + 1) / 2));
+    if (nm == 12) {
+        if (out_f32)
+            hipLaunchKernelGGL((oz_crt_kernel<12, float>), cg, dim3(CNT), 0, s, d, Cres, Kp, A, B, 2 * beta, o, beta,
+                               status);
+        else
+            hipLaunchKernelGGL((oz_crt_kernel<12, double>), cg, dim3(CNT), 0, s, d, Cres, Kp, A, B, 2 * beta, o, beta,
+                               status);
+    } else {
+        if (out_f32)
+            hipLaunchKernelGGL((oz_crt_kernel<13, float>), cg, dim3(CNT), 0, s, d, Cres, Kp, A, B, 2 * beta, o, beta,
+                               status);
+        else
+            hipLaunchKernelGGL((oz_crt_kernel<13, double>), cg, dim3(CNT), 0, s, d, Cres, Kp, A, B, 2 * beta, o, beta,
+                               status);
+    }
     return hipGetLastError();
 }
 
@@ -728,9 +756,10 @@ hipError_t oz_clear_padding(int8_t *planes, int64_t K, hipStream_t s)
     const int64_t Kp = oz_padded(K), kseg = Kp / 64, c0 = (K + 63) / 64;
     const int64_t per_plane = K * (kseg - c0) + (Kp - K) * kseg;
     if (per_plane == 0) return hipSuccess;
-    const int64_t n = per_plane * kOzMods * 4;
+    const int nm = oz_mods(K);
+    const int64_t n = per_plane * nm * 4;
     const int64_t blocks = (n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096;
-    hipLaunchKernelGGL(oz_pad_kernel, dim3((unsigned)blocks), dim3(256), 0, s, planes, K, Kp, per_plane);
+    hipLaunchKernelGGL(oz_pad_kernel, dim3((unsigned)blocks), dim3(256), 0, s, planes, K, Kp, per_plane, nm);
     return hipGetLastError();
 }
 
