@@ -241,6 +241,13 @@ size_t gptq_quantize_workspace_size(int64_t N, int64_t K, int64_t group);
  * gptq_quantize -- damping, blocked Cholesky, U, and the lazy-batch sweep in one
  * call: gptq_factor into the workspace, then gptq_sweep.  Arguments as above;
  * H is K x K fp32 (lower triangle read), damp the damping fraction (0.01).
+ * Above K = 8192 the sweep keeps U (the same fp64 factor gptq_factor rounds to
+ * fp32), the working weights and the errors in fp64, with its block updates on
+ * the fp64 matrix cores: over rows that long an fp32 state drifts far enough
+ * from an fp64 one to decide measurably many rounding ties the other way.  The
+ * rounding decisions themselves are fp32 in both (the code of fl32(w) / s).
+ * The workspace (gptq_quantize_workspace_size) includes the N x K doubles this
+ * needs at every K.
  * Synchronises `stream`.
  */
 int gptq_quantize(uint8_t *codes, float *scales, double *qerr_out, const float *W,
@@ -443,6 +450,16 @@ int psd_project_last_timing(int *launches, double *product_ms, const char **kern
  * any other value (the setting is then unchanged). */
 enum { GQ_PSD_AUTO = 0, GQ_PSD_F64 = 1 };
 int gq_set_psd_products(int kind);
+
+/* State of gptq_quantize's sweep for the plain grid (flags 0), for tests and
+ * comparisons.  GQ_SWEEP_AUTO (default): fp64 above K = 8192, fp32 up to it.
+ * GQ_SWEEP_F32 / GQ_SWEEP_F64: that state at every K.  The variants (any flag
+ * set) and gptq_sweep always sweep in fp32.  Applies to later gptq_quantize and
+ * gptq_quantize_ex calls on this host thread; the workspace size covers both.
+ * Returns GQ_ERR_INVALID_ARG for any other value (the setting is then
+ * unchanged). */
+enum { GQ_SWEEP_AUTO = 0, GQ_SWEEP_F32 = 1, GQ_SWEEP_F64 = 2 };
+int gq_set_sweep_state(int kind);
 
 #ifdef __cplusplus
 }

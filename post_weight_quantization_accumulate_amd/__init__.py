@@ -24,11 +24,13 @@ GQ_HFQM_F32, GQ_HFQM_HESSIAN = 0, 130
 GQ_STATIC_GROUPS, GQ_NF4, GQ_ACT_ORDER = 1, 2, 4
 GQ_F32, GQ_BF16 = 0, 1
 GQ_PSD_AUTO, GQ_PSD_F64 = 0, 1
+GQ_SWEEP_AUTO, GQ_SWEEP_F32, GQ_SWEEP_F64 = 0, 1, 2
 
 EXPORTS = (
     "gq_abi_version", "gq_last_error", "hessian_accumulate", "hessian_tril_bytes",
     "hessian_pack_tril", "hessian_unpack_tril", "psd_project_workspace_size", "psd_project",
     "psd_project_flops", "psd_project_products", "gq_set_timing", "psd_project_last_timing", "gq_set_psd_products",
+    "gq_set_sweep_state",
     "gptq_factor_workspace_size", "gptq_factor", "gptq_sweep_workspace_size", "gptq_sweep",
     "gptq_quantize_workspace_size", "gptq_quantize", "rtn_quantize_workspace_size", "rtn_quantize",
     "gptq_sweep_ex", "gptq_quantize_ex", "rtn_quantize_ex", "gq_nf4_levels", "gptq_quantize_ex_workspace_size",
@@ -73,6 +75,7 @@ def lib() -> ctypes.CDLL:
             "psd_project_products": (I, []),
             "gq_set_timing": (None, [I]),
             "gq_set_psd_products": (I, [I]),
+            "gq_set_sweep_state": (I, [I]),
             "psd_project_last_timing": (I, [ctypes.POINTER(I), ctypes.POINTER(D), ctypes.POINTER(ctypes.c_char_p)]),
             "gptq_factor_workspace_size": (SZ, [I64]),
             "gptq_factor": (I, [P, P, I64, F, P, SZ, P]),
@@ -218,6 +221,12 @@ def gq_set_psd_products(kind: int) -> None:
     """GQ_PSD_AUTO or GQ_PSD_F64: kind of the products of later psd_project calls
     on this thread."""
     _check(lib().gq_set_psd_products(int(kind)), "gq_set_psd_products")
+
+
+def gq_set_sweep_state(kind: int) -> None:
+    """GQ_SWEEP_AUTO, GQ_SWEEP_F32 or GQ_SWEEP_F64: state of gptq_quantize's plain
+    sweep in later calls on this thread."""
+    _check(lib().gq_set_sweep_state(int(kind)), "gq_set_sweep_state")
 
 
 def psd_project_last_timing():

@@ -181,6 +181,8 @@ std::vector<double> sign_schedule(double l0 = kSignL0)
 constexpr int64_t kOzMaxK = 65536;
 // Product kind chosen by gq_set_psd_products on this thread (GQ_PSD_*).
 thread_local int g_psd_kind = GQ_PSD_AUTO;
+// Sweep state chosen by gq_set_sweep_state on this thread (GQ_SWEEP_*).
+thread_local int g_sweep_kind = GQ_SWEEP_AUTO;
 bool psd_emulated(int64_t K) { return K < kOzMaxK && g_psd_kind != GQ_PSD_F64; }
 
 struct PsdWs {
@@ -514,6 +516,65 @@ int run_sweep(uint8_t *codes, float *scales, double *qerr_out, const float *W, c
     return GQ_OK;
 }
 
+// gptq_quantize's sweep with U, the working weights and the errors in fp64
+// (sweep64.hip), for the plain grid: the same column order and lazy blocks as
+// run_sweep, every block and group update an fp64 product, all on the
+// caller's stream.  U64 is the upper factor in fp64, W64 N x K doubles of
+// scratch; the errors of one group (kSweepSuper x N doubles) reuse w.ET.
+int run_sweep64(uint8_t *codes, float *scales, double *qerr_out, const float *W, const double *U64,
+                const float *imp, int64_t N, int64_t K, int64_t G, SweepWs &w, double *W64, hipStream_t s)
+{
+    GQ_HIP(launch_fill_u32(w.sc.status, 4, 0u, s), "fill");
+    GQ_HIP(launch_w64(W64, W, N * K, w.sc.status, s), "copy W");
+    if (imp) GQ_HIP(launch_check_finite(imp, K, w.sc.status, s), "check imp");
+    double *const ET = (double *)w.ET;
+    auto update = [&](const double *Eb, int64_t k0, int64_t k1, int64_t c0, int64_t c1) -> hipError_t {
+        // W64[:, c0:c1] -= E[k0:k1]^T U[k0:k1, c0:c1], E's rows k0.. at Eb
+        GemmDesc d = gemm(Eb, N, U64 + k0 * K + c0, K, N, c1 - c0, k1 - k0, W64 + c0, K);
+        d.cin = W64 + c0;
+        d.alpha = -1.0;
+        d.beta = 1.0;
+        return gemm_tn_f64(d, s);
+    };
+    for (int64_t g0 = 0; g0 < K; g0 += kSweepSuper) {
+        const int64_t g1 = (K - g0) < kSweepSuper ? K : g0 + kSweepSuper;
+        for (int64_t b0 = g0; b0 < g1; b0 += kSweepBlock) {
+            const int64_t bw = (g1 - b0) < kSweepBlock ? (g1 - b0) : kSweepBlock;
+            double *ETb = ET + (b0 - g0) * N;
+            GQ_HIP(launch_sweep64_block(W64, ETb, codes, scales, U64, N, K, G, b0, s), "sweep block");
+            if (b0 + bw < g1) GQ_HIP(update(ETb, b0, b0 + bw, b0 + bw, g1), "block update");
+        }
+        if (g1 < K) GQ_HIP(update(ET, g0, g1, g1, K), "group update");
+    }
+    if (qerr_out) {
+        int64_t nparts = 0;
+        GQ_HIP(launch_qerr(w.sc.partials, W, codes, scales, imp, N, K, G, 0, s, &nparts), "qerr");
+        GQ_HIP(launch_qerr_reduce(w.sc.d, w.sc.partials, nparts, s), "qerr reduce");
+    }
+    unsigned st = 0;
+    int rc = read_status(w.sc.status, s, &st);
+    if (rc) return rc;
+    rc = status_to_code(st);
+    if (rc) return rc;
+    if (qerr_out) {
+        double nd[2] = {0.0, 0.0};
+        GQ_HIP(hipMemcpyAsync(nd, w.sc.d, sizeof(nd), hipMemcpyDeviceToHost, s), "qerr readback");
+        GQ_HIP(hipStreamSynchronize(s), "stream synchronize");
+        *qerr_out = nd[1] > 0.0 ? std::sqrt(nd[0] / nd[1]) : 0.0;
+    }
+    return GQ_OK;
+}
+
+// Whether gptq_quantize's sweep keeps its state in fp64: by default for the
+// plain grid above K = 8192, where the fp32 state's drift decides measurably
+// many rounding ties the other way from an fp64 sweep.
+constexpr int64_t kSweep64MinK = 8193;
+bool sweep64_applies(int64_t K, uint32_t flags)
+{
+    if (flags != 0u || g_sweep_kind == GQ_SWEEP_F32) return false;
+    return g_sweep_kind == GQ_SWEEP_F64 || K >= kSweep64MinK;
+}
+
 }  // namespace
 
 // The message gq_last_error returns, set by the other translation units (hfqm.hip).
@@ -534,6 +595,15 @@ int gq_set_psd_products(int kind)
     g_last_error.clear();
     if (kind != GQ_PSD_AUTO && kind != GQ_PSD_F64) return fail(GQ_ERR_INVALID_ARG, "unknown product kind");
     g_psd_kind = kind;
+    return GQ_OK;
+}
+
+int gq_set_sweep_state(int kind)
+{
+    g_last_error.clear();
+    if (kind != GQ_SWEEP_AUTO && kind != GQ_SWEEP_F32 && kind != GQ_SWEEP_F64)
+        return fail(GQ_ERR_INVALID_ARG, "unknown sweep state");
+    g_sweep_kind = kind;
     return GQ_OK;
 }
 
@@ -1124,7 +1194,10 @@ size_t gptq_quantize_workspace_size(int64_t N, int64_t K, int64_t group)
 {
     (void)group;
     if (N < 1 || K < 1) return 0;
-    return factor_bytes(K) + align_up((size_t)K * (size_t)K * sizeof(float)) + sweep_bytes(N, K);
+    // factor, U, sweep, and the fp64 sweep's working weights (present whatever
+    // the sweep's state, so that the size does not depend on gq_set_sweep_state)
+    return factor_bytes(K) + align_up((size_t)K * (size_t)K * sizeof(float)) + sweep_bytes(N, K) +
+           align_up((size_t)N * (size_t)K * sizeof(double));
 }
 
 // Workspace of gptq_quantize_ex: gptq_quantize's, plus for act order the
@@ -1164,7 +1237,7 @@ int gptq_quantize_ex(uint8_t *codes, float *scales, double *qerr_out, const floa
         const size_t fb = factor_bytes(K), ub = align_up((size_t)K * (size_t)K * sizeof(float));
         float *U = (float *)(base + fb);
         char *sweep_ws = base + fb + ub;
-        Carver cv(sweep_ws + sweep_bytes(N, K));
+        Carver cv(sweep_ws + sweep_bytes(N, K) + align_up((size_t)N * (size_t)K * sizeof(double)));
         float *Hp = cv.take<float>((size_t)K * (size_t)K);
         ActOrder act;
         act.perm = cv.take<int>((size_t)K);
@@ -1188,6 +1261,17 @@ int gptq_quantize_ex(uint8_t *codes, float *scales, double *qerr_out, const floa
     void *sweep_ws = base + fb + align_up((size_t)K * (size_t)K * sizeof(float));
     rc = gptq_factor(U, H, K, damp, base, fb, stream);
     if (rc) return rc;
+    if (sweep64_applies(K, flags)) {
+        // U in fp64 into the factor's M (free once the factor has returned),
+        // from the same L^-1 the fp32 U was rounded from
+        Carver fc(base);
+        FactorWs fw = carve_factor(fc, K);
+        GQ_HIP(launch_flip64(fw.M, fw.X, K, stream), "flip");
+        Carver sc(sweep_ws);
+        SweepWs w = carve_sweep(sc, N, K);
+        double *W64 = (double *)((char *)sweep_ws + sweep_bytes(N, K));
+        return run_sweep64(codes, scales, qerr_out, W, fw.M, imp, N, K, group, w, W64, stream);
+    }
     return gptq_sweep_ex(codes, scales, qerr_out, W, U, imp, N, K, group, flags, sweep_ws, sweep_bytes(N, K),
                          stream);
 }

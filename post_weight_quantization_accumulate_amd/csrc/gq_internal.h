@@ -262,6 +262,14 @@ enum : int { MODE_STATIC = 1, MODE_NF4 = 2 };
 hipError_t launch_sweep_block(float *Wk, float *ET, uint8_t *codes, float *scales,
                               const float *U, int64_t N, int64_t K, int64_t G, int64_t b0, int mode,
                               const int *gidx, hipStream_t s);
+// The sweep with its state in fp64 (sweep64.hip), plain int4 grid, dynamic
+// groups: W64 = W (with the finite check); U64 = the flip of the factor's
+// L^-1 (upper triangle, zeros below); one lazy block of the sweep at column b0
+// over W64 (K x N errors of the block written k-major to ET, N apart).
+hipError_t launch_w64(double *dst, const float *src, int64_t n, unsigned *status, hipStream_t s);
+hipError_t launch_flip64(double *U, const double *X, int64_t K, hipStream_t s);
+hipError_t launch_sweep64_block(double *Wk, double *ET, uint8_t *codes, float *scales, const double *U, int64_t N,
+                                int64_t K, int64_t G, int64_t b0, hipStream_t s);
 // Act order: perm[a] = the column with the a-th largest diagonal entry of H (ties
 // in column order), inv its inverse, gidx[a] = perm[a] / G; Hp = H permuted on
 // both sides (from H's lower triangle); Wk = W's columns permuted (with the finite
