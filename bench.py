@@ -118,14 +118,24 @@ def progress(msg):
     print(f"bench: {msg}", file=sys.stderr, flush=True)
 
 
+SWEEP64_MIN_K = 8193       # gptq_quantize sweeps with its state in fp64 from here on (include/gq.h)
+
+
 def run_path(gq, torch, wl, chunks, Ws, dev, steps, warmup):
     """Time whole steps of the path: zero H, accumulate every chunk (one
     hessian_accumulate_chunks call when there are several), pack, unpack,
     project, factor once, sweep every weight tensor under that U (qerr with the
     stored diagonal as importance).  Stage times come from torch events on the
     current stream; psd_project's product launches are timed by the library
-    with HIP events on the same stream."""
+    with HIP events on the same stream.
+
+    From K = 8193 on, gptq_quantize sweeps with its state in fp64 (U, working
+    weights and errors), which the split gptq_factor + gptq_sweep (fp32 U) does
+    not: there each tensor takes one gptq_quantize call in the step, and the
+    factor alone is timed after the steps to split that stage into factor and
+    sweep."""
     K, G, damp = wl.K, wl.group, wl.damp
+    fused = K >= SWEEP64_MIN_K
     H = torch.empty(K, K, dtype=torch.float32, device=dev)
     blob = torch.empty(gq.hessian_tril_bytes(K), dtype=torch.uint8, device=dev)
     Hs = torch.empty(K, K, dtype=torch.float32, device=dev)
@@ -134,7 +144,8 @@ def run_path(gq, torch, wl, chunks, Ws, dev, steps, warmup):
              torch.empty(W.shape[0], K // G, dtype=torch.float32, device=dev)) for W in Ws]
     ws_psd = gq.workspace(gq.psd_project_workspace_size(K), dev)
     ws_fac = gq.workspace(gq.gptq_factor_workspace_size(K), dev)
-    ws_swp = gq.workspace(max(gq.gptq_sweep_workspace_size(W.shape[0], K, G) for W in Ws), dev)
+    ws_swp = (gq.workspace(max(gq.gptq_quantize_workspace_size(W.shape[0], K, G) for W in Ws), dev) if fused
+              else gq.workspace(max(gq.gptq_sweep_workspace_size(W.shape[0], K, G) for W in Ws), dev))
     imp = blob[: 4 * K].view(torch.float32)          # stored exact diagonal of H
     ev = {s: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for s in STAGES}
     acc = {s: 0.0 for s in STAGES}
@@ -143,6 +154,10 @@ def run_path(gq, torch, wl, chunks, Ws, dev, steps, warmup):
     def sweeps():
         for t, (W, (c, sc)) in enumerate(zip(Ws, outs)):
             qerr[t] = gq.gptq_sweep(c, sc, W, U, imp, G, ws_swp)
+
+    def quantizes():
+        for t, (W, (c, sc)) in enumerate(zip(Ws, outs)):
+            qerr[t] = gq.gptq_quantize(c, sc, W, Hs, imp, G, damp, ws_swp)
 
     ws_acc = (gq.workspace(max(gq.hessian_accumulate_chunks_workspace_size(K, len(chunks)), 1), dev)
               if len(chunks) > 1 else None)
@@ -165,12 +180,16 @@ def run_path(gq, torch, wl, chunks, Ws, dev, steps, warmup):
         run("pack", lambda: gq.hessian_pack_tril(blob, H))
         run("unpack", lambda: gq.hessian_unpack_tril(Hs, blob))
         run("psd", lambda: gq.psd_project(Hs, ws_psd))
-        run("factor", lambda: gq.gptq_factor(U, Hs, damp, ws_fac))
-        run("sweep", sweeps)
+        if fused:
+            run("sweep", quantizes)
+        else:
+            run("factor", lambda: gq.gptq_factor(U, Hs, damp, ws_fac))
+            run("sweep", sweeps)
         if record:
             torch.cuda.synchronize()
             for s in STAGES:
-                acc[s] += ev[s][0].elapsed_time(ev[s][1])
+                if not (fused and s == "factor"):      # the factor ran inside gptq_quantize
+                    acc[s] += ev[s][0].elapsed_time(ev[s][1])
 
     for _ in range(warmup):
         step(False)
@@ -189,8 +208,24 @@ def run_path(gq, torch, wl, chunks, Ws, dev, steps, warmup):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     gq.gq_set_timing(False)
-    return {"ms_step": wall * 1e3 / steps, "stage_ms": {s: acc[s] / steps for s in STAGES}, "prod": prod,
-            "qerr": qerr, "H": H, "Hs": Hs, "U": U, "blob": blob, "imp": imp}
+    stage_ms = {s: acc[s] / steps for s in STAGES}
+    if fused:
+        # the "sweep" stage held whole gptq_quantize calls: time the factor alone
+        # on the same input and give the rest to the sweep
+        fe = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+        fac = 0.0
+        for _ in range(steps):
+            fe[0].record()
+            gq.gptq_factor(U, Hs, damp, ws_fac)
+            fe[1].record()
+            torch.cuda.synchronize()
+            fac += fe[0].elapsed_time(fe[1])
+        fac /= steps
+        stage_ms["gptq_quantize"] = stage_ms["sweep"]
+        stage_ms["factor"] = fac * len(Ws)
+        stage_ms["sweep"] = stage_ms["gptq_quantize"] - fac * len(Ws)
+    return {"ms_step": wall * 1e3 / steps, "stage_ms": stage_ms, "prod": prod,
+            "qerr": qerr, "H": H, "Hs": Hs, "U": U, "blob": blob, "imp": imp, "sweep_state": "f64" if fused else "f32"}
 
 
 def update_flops(N, K):
@@ -238,6 +273,7 @@ def block_summary(wl, r, steps):
         "gptq_weights_per_s": weights / ((st["factor"] + st["sweep"]) * 1e-3),
         "hessian_tflops": gram_tflops,
         "hessian_frac_of_bf16_peak": gram_tflops / PEAK_TFLOPS["bf16"],
+        "sweep_state": r["sweep_state"],
         "sweep_update_tflops": sum(update_flops(N, K) for N in Ns) / (st["sweep"] * 1e-3) / 1e12,
         "psd_products_per_call": r["prod"]["launches"] / steps,
         "psd_product_kernel": {"kernel": r["prod"]["kernel"], "avg_launch_ms": prod_ms, "per_launch_ops": per_launch,
