@@ -439,7 +439,7 @@ def mlp_gptq(gq, mlp, mlp_w):
 def test_mlp_gptq_projected_matches_oracle(gq, orc, mlp, mlp_w, mlp_gptq):
     """GPTQ on the projected K=17408 Hessian at damp 0.01 against the oracle:
     its U of the same projected matrix (the literal route, one LAPACK primitive
-    per step, fp64), its sweep and replay of 256 sampled rows (4.5 M decisions).
+    per step, fp64), its sweep and replay of 1024 sampled rows (17.8 M decisions).
     No decision may be inadmissible and every flip must sit at a rounding tie
     (within 1e-4 of a step of it), scales agree to 1e-5, raw code identity is
     at least 99.9%, and the sampled rows' qerr of the device's codes is within
@@ -449,15 +449,15 @@ def test_mlp_gptq_projected_matches_oracle(gq, orc, mlp, mlp_w, mlp_gptq):
     At this K gptq_quantize sweeps with its state in fp64 (U, working weights,
     errors), as the oracle does; an fp32 state decided about one tie in 37 rows
     the other way here, and each such flip changed a few thousand later codes of
-    its row (99.39% raw identity over these rows).  The fp64 sweep measured
-    100% with no flip."""
+    its row (99.39% raw identity over 256 of these rows).  The fp64 sweep
+    measured 100% with no flip."""
     wl, X, H, blob, Hs, P = mlp
     K, N, G = wl.K, wl.N[0], wl.group
     codes, scales, q, impn = mlp_gptq
     st, U, mu = orc.gptq_U_lapack(P.cpu().numpy(), wl.damp)
     assert st == orc.OK
     Wn = mlp_w.numpy()
-    rows = np.sort(np.random.default_rng(17408).choice(N, 256, replace=False))
+    rows = np.sort(np.random.default_rng(17408).choice(N, 1024, replace=False))
     cg = orc.unpack_codes(codes[rows], K)
     sg = scales[rows]
     rep = orc.gptq_replay(cg, sg, Wn, U, G, rows=rows)
