@@ -130,12 +130,10 @@ def run_path(gq, torch, wl, chunks, Ws, dev, steps, warmup):
     with HIP events on the same stream.
 
     From K = 8193 on, gptq_quantize sweeps with its state in fp64 (U, working
-    weights and errors), which the split gptq_factor + gptq_sweep (fp32 U) does
-    not: there each tensor takes one gptq_quantize call in the step, and the
-    factor alone is timed after the steps to split that stage into factor and
-    sweep."""
+    weights and errors): there the step runs its two halves with that state,
+    gptq_factor_f64 and gptq_sweep_f64."""
     K, G, damp = wl.K, wl.group, wl.damp
-    fused = K >= SWEEP64_MIN_K
+    f64 = K >= SWEEP64_MIN_K
     H = torch.empty(K, K, dtype=torch.float32, device=dev)
     blob = torch.empty(gq.hessian_tril_bytes(K), dtype=torch.uint8, device=dev)
     Hs = torch.empty(K, K, dtype=torch.float32, device=dev)
@@ -144,8 +142,9 @@ def run_path(gq, torch, wl, chunks, Ws, dev, steps, warmup):
              torch.empty(W.shape[0], K // G, dtype=torch.float32, device=dev)) for W in Ws]
     ws_psd = gq.workspace(gq.psd_project_workspace_size(K), dev)
     ws_fac = gq.workspace(gq.gptq_factor_workspace_size(K), dev)
-    ws_swp = (gq.workspace(max(gq.gptq_quantize_workspace_size(W.shape[0], K, G) for W in Ws), dev) if fused
+    ws_swp = (gq.workspace(max(gq.gptq_sweep_f64_workspace_size(W.shape[0], K, G) for W in Ws), dev) if f64
               else gq.workspace(max(gq.gptq_sweep_workspace_size(W.shape[0], K, G) for W in Ws), dev))
+    U64 = torch.empty(K, K, dtype=torch.float64, device=dev) if f64 else None
     imp = blob[: 4 * K].view(torch.float32)          # stored exact diagonal of H
     ev = {s: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for s in STAGES}
     acc = {s: 0.0 for s in STAGES}
@@ -155,9 +154,9 @@ def run_path(gq, torch, wl, chunks, Ws, dev, steps, warmup):
         for t, (W, (c, sc)) in enumerate(zip(Ws, outs)):
             qerr[t] = gq.gptq_sweep(c, sc, W, U, imp, G, ws_swp)
 
-    def quantizes():
+    def sweeps64():
         for t, (W, (c, sc)) in enumerate(zip(Ws, outs)):
-            qerr[t] = gq.gptq_quantize(c, sc, W, Hs, imp, G, damp, ws_swp)
+            qerr[t] = gq.gptq_sweep_f64(c, sc, W, U64, imp, G, ws_swp)
 
     ws_acc = (gq.workspace(max(gq.hessian_accumulate_chunks_workspace_size(K, len(chunks)), 1), dev)
               if len(chunks) > 1 else None)
@@ -180,16 +179,16 @@ def run_path(gq, torch, wl, chunks, Ws, dev, steps, warmup):
         run("pack", lambda: gq.hessian_pack_tril(blob, H))
         run("unpack", lambda: gq.hessian_unpack_tril(Hs, blob))
         run("psd", lambda: gq.psd_project(Hs, ws_psd))
-        if fused:
-            run("sweep", quantizes)
+        if f64:
+            run("factor", lambda: gq.gptq_factor_f64(U64, Hs, damp, ws_fac))
+            run("sweep", sweeps64)
         else:
             run("factor", lambda: gq.gptq_factor(U, Hs, damp, ws_fac))
             run("sweep", sweeps)
         if record:
             torch.cuda.synchronize()
             for s in STAGES:
-                if not (fused and s == "factor"):      # the factor ran inside gptq_quantize
-                    acc[s] += ev[s][0].elapsed_time(ev[s][1])
+                acc[s] += ev[s][0].elapsed_time(ev[s][1])
 
     for _ in range(warmup):
         step(False)
@@ -209,23 +208,10 @@ def run_path(gq, torch, wl, chunks, Ws, dev, steps, warmup):
     wall = time.perf_counter() - t0
     gq.gq_set_timing(False)
     stage_ms = {s: acc[s] / steps for s in STAGES}
-    if fused:
-        # the "sweep" stage held whole gptq_quantize calls: time the factor alone
-        # on the same input and give the rest to the sweep
-        fe = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-        fac = 0.0
-        for _ in range(steps):
-            fe[0].record()
-            gq.gptq_factor(U, Hs, damp, ws_fac)
-            fe[1].record()
-            torch.cuda.synchronize()
-            fac += fe[0].elapsed_time(fe[1])
-        fac /= steps
-        stage_ms["gptq_quantize"] = stage_ms["sweep"]
-        stage_ms["factor"] = fac * len(Ws)
-        stage_ms["sweep"] = stage_ms["gptq_quantize"] - fac * len(Ws)
+    if f64:
+        gq.gptq_factor(U, Hs, damp, ws_fac)          # the fp32 U the variants' sweeps take (untimed)
     return {"ms_step": wall * 1e3 / steps, "stage_ms": stage_ms, "prod": prod,
-            "qerr": qerr, "H": H, "Hs": Hs, "U": U, "blob": blob, "imp": imp, "sweep_state": "f64" if fused else "f32"}
+            "qerr": qerr, "H": H, "Hs": Hs, "U": U, "blob": blob, "imp": imp, "sweep_state": "f64" if f64 else "f32"}
 
 
 def update_flops(N, K):

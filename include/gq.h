@@ -234,6 +234,38 @@ int gptq_sweep(uint8_t *codes, float *scales, double *qerr_out, const float *W, 
                const float *imp, int64_t N, int64_t K, int64_t group, void *ws, size_t ws_bytes,
                hipStream_t stream);
 
+/*
+ * gptq_factor_f64 -- gptq_factor with U written in fp64: the same damping,
+ * Cholesky and inverse (computed in fp64), without the rounding to fp32.
+ *   U   K x K fp64 row-major, written (zeros below the diagonal).
+ * Other arguments, workspace (gptq_factor_workspace_size), synchronisation and
+ * errors as gptq_factor.  For tensors that share one Hessian at large K (for
+ * callers sharing a Hessian across weights, ork-driver wiki, "Exp 2026-08-18
+ * GPTQ Int4": the factor is per Hessian, the sweep per weight), with
+ * gptq_sweep_f64.
+ */
+int gptq_factor_f64(double *U, const float *H, int64_t K, float damp, void *ws, size_t ws_bytes,
+                    hipStream_t stream);
+
+/* Workspace bytes gptq_sweep_f64 needs (gptq_sweep's, plus N x K doubles). */
+size_t gptq_sweep_f64_workspace_size(int64_t N, int64_t K, int64_t group);
+
+/*
+ * gptq_sweep_f64 -- gptq_sweep with its state in fp64: U (from
+ * gptq_factor_f64), the working weights and the errors are fp64 and the block
+ * updates run on the fp64 matrix cores; the rounding decisions are those of
+ * gptq_sweep (the code of fl32(w) / s, ties to even).  This is the sweep
+ * gptq_quantize runs above K = 8192, where an fp32 state drifts far enough from
+ * an fp64 one to decide measurably many rounding ties the other way.  The
+ * uniform grid with dynamic groups only.
+ *   U   K x K fp64 from gptq_factor_f64 (upper triangle read).
+ * Other arguments, synchronisation and errors as gptq_sweep; ws at least
+ * gptq_sweep_f64_workspace_size(N, K, group) bytes.
+ */
+int gptq_sweep_f64(uint8_t *codes, float *scales, double *qerr_out, const float *W, const double *U,
+                   const float *imp, int64_t N, int64_t K, int64_t group, void *ws, size_t ws_bytes,
+                   hipStream_t stream);
+
 /* Workspace bytes gptq_quantize needs. */
 size_t gptq_quantize_workspace_size(int64_t N, int64_t K, int64_t group);
 

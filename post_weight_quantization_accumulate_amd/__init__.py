@@ -32,6 +32,7 @@ EXPORTS = (
     "psd_project_flops", "psd_project_products", "gq_set_timing", "psd_project_last_timing", "gq_set_psd_products",
     "gq_set_sweep_state",
     "gptq_factor_workspace_size", "gptq_factor", "gptq_sweep_workspace_size", "gptq_sweep",
+    "gptq_factor_f64", "gptq_sweep_f64_workspace_size", "gptq_sweep_f64",
     "gptq_quantize_workspace_size", "gptq_quantize", "rtn_quantize_workspace_size", "rtn_quantize",
     "gptq_sweep_ex", "gptq_quantize_ex", "rtn_quantize_ex", "gq_nf4_levels", "gptq_quantize_ex_workspace_size",
     "hfqm_write", "hfqm_read_header", "hfqm_read_entry", "hfqm_read_payload",
@@ -81,6 +82,9 @@ def lib() -> ctypes.CDLL:
             "gptq_factor": (I, [P, P, I64, F, P, SZ, P]),
             "gptq_sweep_workspace_size": (SZ, [I64, I64, I64]),
             "gptq_sweep": (I, [P, P, P, P, P, P, I64, I64, I64, P, SZ, P]),
+            "gptq_factor_f64": (I, [P, P, I64, F, P, SZ, P]),
+            "gptq_sweep_f64_workspace_size": (SZ, [I64, I64, I64]),
+            "gptq_sweep_f64": (I, [P, P, P, P, P, P, I64, I64, I64, P, SZ, P]),
             "gptq_quantize_workspace_size": (SZ, [I64, I64, I64]),
             "gptq_quantize": (I, [P, P, P, P, P, P, I64, I64, I64, F, P, SZ, P]),
             "rtn_quantize_workspace_size": (SZ, [I64, I64, I64]),
@@ -284,6 +288,32 @@ def gptq_sweep(codes, scales, W, U, imp, group: int, ws, want_qerr: bool = True)
     _check(lib().gptq_sweep(_ptr(codes), _ptr(scales), ctypes.byref(q) if want_qerr else None,
                             _ptr(W), _ptr(U), _ptr(imp), N, K, group, _ptr(ws), ws.numel(),
                             _stream(W)), "gptq_sweep")
+    return q.value if want_qerr else None
+
+
+def gptq_factor_f64(U: torch.Tensor, H: torch.Tensor, damp: float, ws: torch.Tensor) -> None:
+    """gptq_factor with U (K x K float64) kept in fp64."""
+    K = H.shape[0]
+    _need(U, "U", torch.float64, K * K)
+    _need(H, "H", torch.float32, K * K)
+    _need(ws, "ws", torch.uint8)
+    _check(lib().gptq_factor_f64(_ptr(U), _ptr(H), K, float(damp), _ptr(ws), ws.numel(), _stream(H)),
+           "gptq_factor_f64")
+
+
+def gptq_sweep_f64_workspace_size(N: int, K: int, group: int) -> int:
+    return int(lib().gptq_sweep_f64_workspace_size(N, K, group))
+
+
+def gptq_sweep_f64(codes, scales, W, U, imp, group: int, ws, want_qerr: bool = True):
+    """gptq_sweep with its state in fp64 under a float64 U from gptq_factor_f64;
+    returns qerr (or None)."""
+    N, K = _quant_args(codes, scales, W, None, imp, group, ws, "U")
+    _need(U, "U", torch.float64, K * K)
+    q = ctypes.c_double(0.0)
+    _check(lib().gptq_sweep_f64(_ptr(codes), _ptr(scales), ctypes.byref(q) if want_qerr else None,
+                                _ptr(W), _ptr(U), _ptr(imp), N, K, group, _ptr(ws), ws.numel(),
+                                _stream(W)), "gptq_sweep_f64")
     return q.value if want_qerr else None
 
 

@@ -414,7 +414,7 @@ int run_factor(float *U, const float *H, int64_t K, float damp, FactorWs &w, hip
     GQ_HIP(hipEventRecord(la->inv_done, la->inv), "record");
     GQ_HIP(hipStreamWaitEvent(s, la->inv_done, 0), "wait inverse");
     // U = J R^-T J = J L^-1 J: U[i][j] = X[K-1-i][K-1-j]
-    GQ_HIP(launch_flip(U, w.X, K, s), "flip");
+    if (U) GQ_HIP(launch_flip(U, w.X, K, s), "flip");
     return GQ_OK;
 }
 
@@ -573,6 +573,13 @@ bool sweep64_applies(int64_t K, uint32_t flags)
 {
     if (flags != 0u || g_sweep_kind == GQ_SWEEP_F32) return false;
     return g_sweep_kind == GQ_SWEEP_F64 || K >= kSweep64MinK;
+}
+
+// Workspace of gptq_sweep_f64: the sweep's (scalars, and errors of two fp32
+// groups, i.e. one fp64 group), then the N x K fp64 working weights.
+size_t sweep64_bytes(int64_t N, int64_t K)
+{
+    return sweep_bytes(N, K) + align_up((size_t)N * (size_t)K * sizeof(double));
 }
 
 }  // namespace
@@ -1188,6 +1195,46 @@ int rtn_quantize_noalloc(uint8_t *codes, float *scales, double *qerr_out, const 
     Carver cv(ws);
     const RtnWs w = carve_rtn(cv, N, K);
     return run_rtn(codes, scales, qerr_out, W, imp, N, K, group, flags, w, stream);
+}
+
+int gptq_factor_f64(double *U, const float *H, int64_t K, float damp, void *ws, size_t ws_bytes, hipStream_t stream)
+{
+    g_last_error.clear();
+    if (!U || !H || !ws) return fail(GQ_ERR_INVALID_ARG, "null required pointer");
+    if (K < 1) return fail(GQ_ERR_INVALID_ARG, "K must be >= 1");
+    if (!(damp >= 0.0f) || !std::isfinite(damp)) return fail(GQ_ERR_INVALID_ARG, "damp must be finite and >= 0");
+    if (ws_bytes < factor_bytes(K)) return fail(GQ_ERR_INVALID_ARG, "workspace too small");
+    Carver cv(ws);
+    FactorWs w = carve_factor(cv, K);
+    int rc = run_factor(nullptr, H, K, damp, w, stream);
+    if (rc) return rc;
+    GQ_HIP(launch_flip64(U, w.X, K, stream), "flip");
+    unsigned st = 0;
+    rc = read_status(w.sc.status, stream, &st);
+    if (rc) return rc;
+    return status_to_code(st);
+}
+
+size_t gptq_sweep_f64_workspace_size(int64_t N, int64_t K, int64_t group)
+{
+    (void)group;
+    if (N < 1 || K < 1) return 0;
+    return sweep64_bytes(N, K);
+}
+
+int gptq_sweep_f64(uint8_t *codes, float *scales, double *qerr_out, const float *W, const double *U,
+                   const float *imp, int64_t N, int64_t K, int64_t group, void *ws, size_t ws_bytes,
+                   hipStream_t stream)
+{
+    g_last_error.clear();
+    int rc = check_sweep_args(codes, scales, W, U, N, K, group);
+    if (rc) return rc;
+    if (!ws) return fail(GQ_ERR_INVALID_ARG, "null workspace");
+    if (ws_bytes < sweep64_bytes(N, K)) return fail(GQ_ERR_INVALID_ARG, "workspace too small");
+    Carver cv(ws);
+    SweepWs w = carve_sweep(cv, N, K);
+    double *W64 = (double *)((char *)ws + sweep_bytes(N, K));
+    return run_sweep64(codes, scales, qerr_out, W, U, imp, N, K, group, w, W64, stream);
 }
 
 size_t gptq_quantize_workspace_size(int64_t N, int64_t K, int64_t group)

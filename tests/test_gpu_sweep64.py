@@ -157,3 +157,55 @@ def test_sweep_state_setting(gq):
     with pytest.raises(gq.GQError) as e:
         gq.gq_set_sweep_state(7)
     assert e.value.status == gq.GQ_ERR_INVALID_ARG
+
+
+def _sym_case(N, K, seed):
+    X = g.normal_matrix(seed, g.S_X, 2 * K, K).numpy()
+    mix = g.normal_matrix(seed, g.S_A, K, K, 1.0 / np.sqrt(K)).numpy()
+    X = (X @ (np.eye(K) + mix)).astype(np.float32)
+    return g.uniform_weights(seed, N, K).numpy(), X
+
+
+@pytest.mark.parametrize("N,K,G", [(200, 256, 32), (40, 640, 64), (33, 384, 128)])
+def test_split_f64_is_quantize(gq, orc, N, K, G):
+    """gptq_factor_f64 + gptq_sweep_f64 are gptq_quantize's fp64 path in two
+    halves: the same codes, scales and qerr, bit for bit.  The fp64 U rounds to
+    gptq_factor's fp32 U exactly, and matches the oracle's fp64 U (the literal
+    route) to 1e-7 relative Frobenius (measured 7e-9: the two routes' fp64
+    roundings through H_d's conditioning; fp32's own rounding of U is 3e-8)."""
+    W, X = _sym_case(N, K, N + K)
+    H = orc.gram(X).astype(np.float32)
+    imp = np.diag(H).copy()
+    codes, scales, q = _gptq(gq, W, H, G, 0.01, imp)
+    Ht = torch.from_numpy(H).to(DEV)
+    U64 = torch.empty(K, K, dtype=torch.float64, device=DEV)
+    gq.gptq_factor_f64(U64, Ht, 0.01, gq.workspace(gq.gptq_factor_workspace_size(K), DEV))
+    U32 = torch.empty(K, K, dtype=torch.float32, device=DEV)
+    gq.gptq_factor(U32, Ht, 0.01, gq.workspace(gq.gptq_factor_workspace_size(K), DEV))
+    assert torch.equal(U64.to(torch.float32), U32)
+    st, Uo, _ = orc.gptq_U(H, 0.01)
+    assert st == orc.OK
+    Un = U64.cpu().numpy()
+    assert np.linalg.norm(Un - Uo) / np.linalg.norm(Uo) < 1e-7
+    c2 = torch.empty(N, K // 2, dtype=torch.uint8, device=DEV)
+    s2 = torch.empty(N, K // G, dtype=torch.float32, device=DEV)
+    q2 = gq.gptq_sweep_f64(c2, s2, torch.from_numpy(W).to(DEV), U64, torch.from_numpy(imp).to(DEV), G,
+                           gq.workspace(gq.gptq_sweep_f64_workspace_size(N, K, G), DEV))
+    assert np.array_equal(c2.cpu().numpy(), codes) and np.array_equal(s2.cpu().numpy(), scales)
+    assert q2 == q
+
+
+def test_split_f64_argument_errors(gq):
+    N, K, G = 8, 64, 32
+    W = torch.zeros(N, K, device=DEV)
+    U = torch.eye(K, dtype=torch.float64, device=DEV)
+    c = torch.empty(N, K // 2, dtype=torch.uint8, device=DEV)
+    s = torch.empty(N, K // G, dtype=torch.float32, device=DEV)
+    small = gq.workspace(gq.gptq_sweep_f64_workspace_size(N, K, G) - 1024, DEV)
+    with pytest.raises(gq.GQError) as e:
+        gq.gptq_sweep_f64(c, s, W, U, None, G, small)
+    assert e.value.status == gq.GQ_ERR_INVALID_ARG
+    s3 = torch.empty(N, K // 3, dtype=torch.float32, device=DEV)        # a group size that is not a power of two
+    with pytest.raises(gq.GQError) as e:
+        gq.gptq_sweep_f64(c, s3, W, U, None, 3, gq.workspace(gq.gptq_sweep_f64_workspace_size(N, K, G), DEV))
+    assert e.value.status == gq.GQ_ERR_INVALID_ARG
