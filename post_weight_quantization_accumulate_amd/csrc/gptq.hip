@@ -776,8 +776,12 @@ __device__ inline int nf4_index(float x, const float *mid)
 // pair (sum imp (w - c s)^2, sum imp w^2) in fp64, as qerr_kernel defines them,
 // to partials[2 blockIdx.x ..] (a fixed-order tree, so the sums are
 // deterministic): no second pass over W.
+// The kernel takes 91 VGPRs (five waves per SIMD, five 256-lane workgroups per
+// CU), and the grid is at most one such round of the 256 CUs: every workgroup
+// is resident from the start and takes the same number of passes, so no second
+// round runs on a partly idle chip.
 constexpr int RTN_NT = QNT;
-constexpr int RTN_MAX_WG = 2048;
+constexpr int RTN_MAX_WG = 5 * 256;
 __device__ inline float rtn_quot_y(float w, float s, float y)
 {
     const float q0 = w * y;
