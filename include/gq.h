@@ -393,7 +393,7 @@ int rtn_quantize_ex(uint8_t *codes, float *scales, double *qerr_out, const float
  * GQ_NOALLOC_SCRATCH_BYTES inside the library, one per device, held from its
  * first use on that device until the process ends; the call allocates nothing
  * and otherwise does exactly what rtn_quantize_ex does (same kernels, codes,
- * scales and qerr).  rtn_quantize_workspace_size is at most 49 KiB for any
+ * scales and qerr).  rtn_quantize_workspace_size is at most 36.5 KiB for any
  * N, K and group, so every size rtn_quantize_ex takes fits; a size that would
  * not is refused with GQ_ERR_INVALID_ARG.  Calls on one device share its
  * scratch: calls that overlap on the same device (other streams or threads)
