@@ -137,12 +137,15 @@ template <typename T> struct Tile {
     static constexpr int V = 16 / (int)sizeof(T);       // elements per 16-byte vector
     static constexpr int LDP = BM + V;                   // padded LDS row (elements)
     static constexpr int VPR = BM / V;                   // vectors per tile row
-    static constexpr int NV = BK * VPR / NT;             // vectors per thread per operand
+    // k rows per stage: 32 for fp32 (half the barriers per matrix instruction;
+    // two workgroups still share a CU's LDS), 16 for fp64 (the DMA ring's layout)
+    static constexpr int KB = sizeof(T) == 4 ? 2 * BK : BK;
+    static constexpr int NV = KB * VPR / NT;             // vectors per thread per operand
     typedef T vec_t __attribute__((ext_vector_type(V)));
     typedef typename MF::acc_t acc_t;
     struct Smem {
-        T As[2][BK][LDP];
-        T Bs[2][BK][LDP];
+        T As[2][KB][LDP];
+        T Bs[2][KB][LDP];
     };
 
     // acc = sum over k stages [s0, s1) of A[k][i0 + i] * B[k][j0 + j].
@@ -172,7 +175,7 @@ template <typename T> struct Tile {
         constexpr int D = sizeof(T) == 4 ? 2 : 1;
         vec_t ra[D][NV], rb[D][NV];
         auto gload = [&](int64_t kb, int sl) {
-            const bool full_k = kb + BK <= d.Kd;
+            const bool full_k = kb + KB <= d.Kd;
             if (full_i && full_k) {
 #pragma unroll
                 for (int v = 0; v < NV; ++v) {
@@ -228,7 +231,7 @@ template <typename T> struct Tile {
         auto compute = [&](int buf) {
             const int m = lane % MF::LPK;
 #pragma unroll
-            for (int kk = 0; kk < BK; kk += MF::KSTEP) {
+            for (int kk = 0; kk < KB; kk += MF::KSTEP) {
                 const int kr = kk + lane / MF::LPK;
                 T a[MF::NB], b[MF::NB];
 #pragma unroll
@@ -242,10 +245,10 @@ template <typename T> struct Tile {
             }
         };
 
-        gload(s0 * BK, 0);
+        gload(s0 * KB, 0);
         sstore(0, 0);
         if constexpr (D == 2) {
-            if (s0 + 1 < s1) gload((s0 + 1) * BK, 1);
+            if (s0 + 1 < s1) gload((s0 + 1) * KB, 1);
         }
         __syncthreads();
         if constexpr (D == 2) {
@@ -254,7 +257,7 @@ template <typename T> struct Tile {
             int64_t kt = s0;
             auto iter = [&](auto SL) {
                 constexpr int sl = decltype(SL)::value;        // (kt - s0) & 1
-                if (kt + 2 < s1) gload((kt + 2) * BK, sl);
+                if (kt + 2 < s1) gload((kt + 2) * KB, sl);
                 compute(sl);
                 if (kt + 1 < s1) sstore(sl ^ 1, sl ^ 1);
                 __syncthreads();
@@ -268,7 +271,7 @@ template <typename T> struct Tile {
         } else {
             for (int64_t kt = s0; kt < s1; ++kt) {
                 const int buf = (int)((kt - s0) & 1);
-                if (kt + 1 < s1) gload((kt + 1) * BK, 0);
+                if (kt + 1 < s1) gload((kt + 1) * KB, 0);
                 compute(buf);
                 if (kt + 1 < s1) sstore(buf ^ 1, 0);
                 __syncthreads();
@@ -446,7 +449,7 @@ __global__ __launch_bounds__(NT, 2) void gemm_tn_kernel(GemmDesc d, int64_t tile
     int64_t i0, j0;
     tile_coords(d, xcd_logical(blockIdx.x, gridDim.x), tiles_m, tiles_n, i0, j0);
     typename TL::acc_t acc[TL::MF::NB][TL::MF::NB];
-    TL::mainloop(d, i0, j0, 0, (d.Kd + BK - 1) / BK, vecA, vecB, sm, acc);
+    TL::mainloop(d, i0, j0, 0, (d.Kd + TL::KB - 1) / TL::KB, vecA, vecB, sm, acc);
     TL::template epilogue<OutT>(d, i0, j0, acc);
 }
 
