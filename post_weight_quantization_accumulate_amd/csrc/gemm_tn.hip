@@ -152,6 +152,7 @@ template <typename T> struct Tile {
     // Interior stages load whole 16-byte vectors unconditionally; edge stages
     // load element by element from clamped (always valid) addresses and zero the
     // out-of-range elements with a select, so no lane ever branches.
+    template <int DP = (sizeof(T) == 4 ? 2 : 1)>
     __device__ static void mainloop(const GemmDesc &d, int64_t i0, int64_t j0, int64_t s0, int64_t s1,
                                     int vecA, int vecB, Smem &sm, acc_t (&acc)[MF::NB][MF::NB])
     {
@@ -172,7 +173,7 @@ template <typename T> struct Tile {
         // Global loads go through registers: fp32 keeps two stages in flight
         // (a stage of its 64-cycle instructions is shorter than a load under
         // load), fp64 one.
-        constexpr int D = sizeof(T) == 4 ? 2 : 1;
+        constexpr int D = DP;
         vec_t ra[D][NV], rb[D][NV];
         auto gload = [&](int64_t kb, int sl) {
             const bool full_k = kb + KB <= d.Kd;
@@ -453,6 +454,25 @@ __global__ __launch_bounds__(NT, 2) void gemm_tn_kernel(GemmDesc d, int64_t tile
     TL::template epilogue<OutT>(d, i0, j0, acc);
 }
 
+// fp64 grids of at most kSmallTiles tiles (the factor's block-row updates, which
+// lie on its critical chain, and the smallest trailing and inverse updates):
+// occupancy is moot there, so one wave per SIMD with the loads two stages ahead,
+// as the fp32 ones are, and each stage's load latency hides behind two stages
+// of matrix work.  Larger grids keep two waves per SIMD.
+constexpr int64_t kSmallTiles = 64;
+template <typename OutT>
+__global__ __launch_bounds__(NT, 1) void gemm_tn_small_f64_kernel(GemmDesc d, int64_t tiles_m, int64_t tiles_n,
+                                                                  int vecA, int vecB)
+{
+    using TL = Tile<double>;
+    __shared__ __attribute__((aligned(16))) typename TL::Smem sm;
+    int64_t i0, j0;
+    tile_coords(d, xcd_logical(blockIdx.x, gridDim.x), tiles_m, tiles_n, i0, j0);
+    typename TL::acc_t acc[TL::MF::NB][TL::MF::NB];
+    TL::template mainloop<2>(d, i0, j0, 0, (d.Kd + TL::KB - 1) / TL::KB, vecA, vecB, sm, acc);
+    TL::template epilogue<OutT>(d, i0, j0, acc);
+}
+
 // Stream-K with a data-parallel head: a persistent grid of exactly the
 // resident workgroups.  The first dp_tiles tiles (whole waves) go one per
 // worker per round in the grouped order, so the workgroups resident on one XCD
@@ -578,6 +598,13 @@ hipError_t launch(const GemmDesc &d, hipStream_t s)
     }
     const int vecA = (d.lda % V == 0) && (((uintptr_t)d.A & 15) == 0);
     const int vecB = (d.ldb % V == 0) && (((uintptr_t)d.B & 15) == 0);
+    if constexpr (sizeof(T) == 8) {
+        if (ntiles <= kSmallTiles) {
+            hipLaunchKernelGGL((gemm_tn_small_f64_kernel<OutT>), dim3((unsigned)ntiles), dim3(NT), 0, s, d, tm, tn,
+                               vecA, vecB);
+            return hipGetLastError();
+        }
+    }
     hipLaunchKernelGGL((gemm_tn_kernel<T, OutT>), dim3((unsigned)ntiles), dim3(NT), 0, s, d, tm, tn,
                        vecA, vecB);
     return hipGetLastError();
